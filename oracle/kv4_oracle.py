@@ -1,0 +1,347 @@
+"""CPU oracle for the INT4 per-token-head RHT KV cache (write + paged attention).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The GPU product path never calls it,
+and it shares no code, tables or constants with the HIP sources.
+
+Sources (cited by title and section):
+  [PR40835]  vLLM PR #40835, "[Feature] Triton INT4 per-token-head KV cache
+             quantization" -- review thread (scale-cache shapes, uint8 cache,
+             slot mapping, query_start_loc / seq_lens metadata).
+  [PR56198]  runguoli.com, "vLLM -- Attention Kernels & KV Cache Quantization",
+             section "PR #56198 -- Support int4_per_token_head on
+             non-power-of-two head sizes" (block-diagonal H_b, b = largest
+             power-of-two divisor, compensation by b, fp64 reference errors).
+  [PR62881]  vLLM PR #62881, "[Bugfix][Test] Rotate KV into RHT domain in the
+             INT4 unified attn test" -- Details: Root cause (K_s = H.D.k,
+             q' = H.D.q with softmax_scale / d, output D.H(.)/d), Fix (rotation
+             rounded through bf16 before quantizing), Tolerance.
+
+Two tiers:
+  * spec tier  -- the exact float32 / bf16 operation order the write path is
+                  defined with (radix-2 butterflies in ascending stride order,
+                  one round-to-nearest-even to bf16, IEEE float32 division).
+                  Used for bit-exact comparison of codes and scales.
+  * math tier  -- fp64: explicit dense block-diagonal Hadamard matrix,
+                  scalar quantization, unpaged attention.
+
+Readings where the pages are silent (each listed in the design doc):
+  D: sign i is -1 iff bit 63 of the (i+1)-th SplitMix64 output seeded with
+     sign_seed is set; one D of length head_size shared by K, V, Q, all heads
+     and tokens.  H_b: Sylvester order, entry (r, c) = (-1)^popcount(r & c),
+     unnormalized.  Blocks are contiguous chunks [j*b, (j+1)*b).  The int4 rule
+     is absmax / 7, round-half-to-even of the float32 quotient, clamp [-8, 7],
+     two's-complement nibbles, element 2j in the low nibble of byte j.  amax == 0
+     stores scale 0 and codes 0.  slot < 0 skips the token.  Query i of a
+     sequence with query_len q and seq_len L sits at position L - q + i and
+     attends to keys 0..L-q+i.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_M64 = (1 << 64) - 1
+_GOLDEN_GAMMA = 0x9E3779B97F4A7C15
+
+
+# ---------------------------------------------------------------------------
+# Randomized signs D and the block-diagonal Hadamard H  ([PR56198], [PR62881])
+# ---------------------------------------------------------------------------
+
+def splitmix64(seed: int, n: int) -> list:
+    """First n outputs of SplitMix64 (Steele, Lea & Flood 2014, as published in
+    Vigna's public-domain splitmix64.c) started from state `seed`. Plain Python
+    integers, one output at a time."""
+    x = seed & _M64
+    out = []
+    for _ in range(n):
+        x = (x + _GOLDEN_GAMMA) & _M64
+        z = x
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+        out.append(z ^ (z >> 31))
+    return out
+
+
+def rht_signs(sign_seed: int, head_size: int) -> np.ndarray:
+    """Diagonal of D (float64 +-1): D.D = I ([PR62881] Root cause)."""
+    return np.array([-1.0 if (z >> 63) else 1.0 for z in splitmix64(sign_seed, head_size)])
+
+
+def largest_pow2_divisor(n: int) -> int:
+    """b: the largest power of two dividing head_size ([PR56198])."""
+    if n <= 0:
+        raise ValueError("head_size must be positive")
+    b = 1
+    while n % (2 * b) == 0:
+        b *= 2
+    return b
+
+
+def hadamard(b: int) -> np.ndarray:
+    """Unnormalized Sylvester Hadamard H_b, entries (-1)^popcount(r & c)."""
+    if b <= 0 or (b & (b - 1)):
+        raise ValueError("b must be a power of two")
+    H = np.empty((b, b), dtype=np.float64)
+    for r in range(b):
+        for c in range(b):
+            H[r, c] = -1.0 if bin(r & c).count("1") % 2 else 1.0
+    return H
+
+
+def block_diag_hadamard(head_size: int) -> np.ndarray:
+    """H for head_size d = b * n: H_b repeated n times on the diagonal
+    ([PR56198]: H @ H.T = b * I, no padding)."""
+    b = largest_pow2_divisor(head_size)
+    Hb = hadamard(b)
+    H = np.zeros((head_size, head_size), dtype=np.float64)
+    for j in range(head_size // b):
+        H[j * b:(j + 1) * b, j * b:(j + 1) * b] = Hb
+    return H
+
+
+def rotate_math(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """fp64 H . D . x along the last axis ([PR62881] Root cause: K_s = H.D.k)."""
+    H = block_diag_hadamard(x.shape[-1])
+    return (np.asarray(x, dtype=np.float64) * signs) @ H.T
+
+
+def unrotate_math(y: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """fp64 D . H . y / b along the last axis: the inverse of rotate_math
+    ([PR62881] Root cause, output compensation; divisor b per [PR56198])."""
+    d = y.shape[-1]
+    H = block_diag_hadamard(d)
+    return (np.asarray(y, dtype=np.float64) @ H.T) * signs / largest_pow2_divisor(d)
+
+
+# ---------------------------------------------------------------------------
+# Spec tier of the write path (float32 / bf16, fixed operation order)
+# ---------------------------------------------------------------------------
+
+def fwht_spec_f32(x: np.ndarray, b: int) -> np.ndarray:
+    """Radix-2 fast Walsh-Hadamard transform of every contiguous b-chunk of the
+    last axis, in float32: for stride h = 1, 2, 4, ..., b/2 and every index i
+    with (i & h) == 0 inside a chunk, (x_i, x_{i+h}) <- (x_i + x_{i+h},
+    x_i - x_{i+h}), each one IEEE float32 operation. Same matrix as hadamard(b)
+    (Sylvester order)."""
+    y = np.array(x, dtype=np.float32, copy=True)
+    d = y.shape[-1]
+    if d % b:
+        raise ValueError("b must divide the last axis")
+    v = y.reshape(y.shape[:-1] + (d // b, b))
+    h = 1
+    while h < b:
+        w = v.reshape(v.shape[:-1] + (b // (2 * h), 2, h))
+        lo = w[..., 0, :].copy()
+        hi = w[..., 1, :].copy()
+        w[..., 0, :] = lo + hi
+        w[..., 1, :] = lo - hi
+        h *= 2
+    return v.reshape(y.shape)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even), returned as the
+    exact float32 value of that bf16. Inputs must be finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def rotate_spec(x_bf16: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """The stored rotation of one head vector: sign flip (exact), float32
+    block butterflies, one bf16 rounding ([PR62881] Fix: rotation rounded
+    through bf16 before quantizing)."""
+    d = x_bf16.shape[-1]
+    xs = np.asarray(x_bf16, dtype=np.float32) * signs.astype(np.float32)
+    return bf16_round(fwht_spec_f32(xs, largest_pow2_divisor(d)))
+
+
+def quantize_int4(y: np.ndarray):
+    """Per-(token, head) symmetric int4: scale = float32(absmax) / 7 (IEEE
+    float32 division), code = clamp(rint_half_even(float32(y / scale)), -8, 7).
+    amax == 0 gives scale 0 and all-zero codes. One fp32 scale per vector
+    ([PR40835] review: scale caches are float32 per (token, kv head))."""
+    y = np.asarray(y, dtype=np.float32)
+    amax = np.max(np.abs(y), axis=-1)
+    scale = (amax / np.float32(7.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = (y / safe[..., None]).astype(np.float32)
+    codes = np.clip(np.rint(q), -8, 7).astype(np.int8)
+    codes = np.where(scale[..., None] > 0, codes, np.int8(0)).astype(np.int8)
+    return codes, scale
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Two's-complement nibbles, element 2j in the low nibble of byte j."""
+    c = np.asarray(codes, dtype=np.int16) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    lo = (p & 0xF).astype(np.int16)
+    hi = (p >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Paged cache (write, gather, dequant)
+# ---------------------------------------------------------------------------
+
+def new_cache(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int):
+    """Zeroed uint8 [nb, bs, nkv, hs/2] codes and float32 [nb, bs, nkv] scales
+    ([PR40835] review: uint8 int4 cache, float32 scale caches)."""
+    codes = np.zeros((num_blocks, block_size, num_kv_heads, head_size // 2), dtype=np.uint8)
+    scales = np.zeros((num_blocks, block_size, num_kv_heads), dtype=np.float32)
+    return codes, scales
+
+
+def rht_write(x_bf16: np.ndarray, cache: np.ndarray, scale_cache: np.ndarray,
+              slot_mapping: np.ndarray, sign_seed: int, chunk: int = 16384) -> None:
+    """Write path for one of K or V: rotate, round through bf16, quantize and
+    pack each (token, kv head) vector into its slot (blk = slot // bs,
+    off = slot % bs; [PR40835] review round-trip loop). slot < 0 skips.
+    Every vector is independent; tokens are processed a chunk at a time."""
+    x = np.asarray(x_bf16, dtype=np.float32)
+    T, nkv, hs = x.shape
+    bs = cache.shape[1]
+    signs = rht_signs(sign_seed, hs)
+    sl = np.asarray(slot_mapping, dtype=np.int64)
+    for t0 in range(0, T, chunk):
+        s = sl[t0:t0 + chunk]
+        keep = s >= 0
+        if not keep.any():
+            continue
+        y = rotate_spec(x[t0:t0 + chunk][keep], signs)      # [t, nkv, hs]
+        codes, scale = quantize_int4(y)
+        s = s[keep]
+        cache[s // bs, s % bs] = pack_int4(codes)
+        scale_cache[s // bs, s % bs] = scale
+
+
+def write_kv(key, value, slot_mapping, num_blocks, block_size, sign_seed):
+    """Convenience: fresh caches with every token of key/value written."""
+    T, nkv, hs = np.asarray(key).shape
+    kc, ks = new_cache(num_blocks, block_size, nkv, hs)
+    vc, vs = new_cache(num_blocks, block_size, nkv, hs)
+    rht_write(key, kc, ks, slot_mapping, sign_seed)
+    rht_write(value, vc, vs, slot_mapping, sign_seed)
+    return kc, vc, ks, vs
+
+
+def dequant(cache: np.ndarray, scale_cache: np.ndarray, slot_mapping: np.ndarray,
+            sign_seed: int, inverse_rotate: bool) -> np.ndarray:
+    """Gather slots and dequantize: code * scale as one float32 product; with
+    inverse_rotate, D.H(.)/b in fp64 back to the original domain."""
+    bs = cache.shape[1]
+    sl = np.asarray(slot_mapping, dtype=np.int64)
+    codes = unpack_int4(cache[sl // bs, sl % bs]).astype(np.float32)
+    sc = scale_cache[sl // bs, sl % bs].astype(np.float32)
+    y = (codes * sc[..., None]).astype(np.float32)
+    if not inverse_rotate:
+        return y
+    signs = rht_signs(sign_seed, cache.shape[-1] * 2)
+    return unrotate_math(y.astype(np.float64), signs)
+
+
+def gather_seq(cache: np.ndarray, scale_cache: np.ndarray, block_table_row: np.ndarray,
+               seq_len: int) -> np.ndarray:
+    """fp64 dequantized [seq_len, nkv, hs] of one sequence, read through its
+    page table (rotated domain)."""
+    bs = cache.shape[1]
+    pos = np.arange(seq_len)
+    blk = np.asarray(block_table_row, dtype=np.int64)[pos // bs]
+    off = pos % bs
+    codes = unpack_int4(cache[blk, off]).astype(np.float64)
+    return codes * scale_cache[blk, off].astype(np.float64)[..., None]
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def _causal_softmax_attend(logits: np.ndarray, vals: np.ndarray, L: int) -> np.ndarray:
+    """logits [ql, ..., L]: row i (query i of ql) may see keys 0 .. L - ql + i;
+    returns softmax(logits) @ vals with vals [L, hs]."""
+    ql = logits.shape[0]
+    pos = L - ql + np.arange(ql)
+    mask = np.arange(L)[None, :] > pos[:, None]                  # [ql, L]
+    mask = mask.reshape((ql,) + (1,) * (logits.ndim - 2) + (L,))
+    lg = np.where(mask, -np.inf, logits)
+    m = lg.max(axis=-1, keepdims=True)
+    p = np.exp(lg - m)
+    p /= p.sum(axis=-1, keepdims=True)
+    return p @ vals
+
+
+def paged_attention(query, key_cache, value_cache, k_scale_cache, v_scale_cache,
+                    block_table, seq_lens, query_start_loc, softmax_scale: float,
+                    sign_seed: int, seqs=None) -> np.ndarray:
+    """fp64 attention over the int4 RHT cache in the rotated domain
+    ([PR62881] Root cause; divisor b per [PR56198]):
+        q' = H.D.q,  logit_j = (q' . K_s_j) * softmax_scale / b,
+        o' = softmax(logit) @ V_s,  o = D.H.o' / b.
+    K_s, V_s are the dequantized cache values gathered through block_table.
+    Causal: query i of sequence s (query_len q, seq_len L) sees keys
+    0 .. L - q + i. GQA: q head h reads kv head h // (nq / nkv).
+    Returns fp64 [num_q_tokens, nq, hs]; rows of sequences not in `seqs`
+    are NaN."""
+    q = np.asarray(query, dtype=np.float64)
+    Tq, nq, hs = q.shape
+    nkv = key_cache.shape[2]
+    group = nq // nkv
+    b = largest_pow2_divisor(hs)
+    signs = rht_signs(sign_seed, hs)
+    out = np.full((Tq, nq, hs), np.nan)
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    if seqs is None:
+        seqs = range(len(seq_lens))
+    for s in seqs:
+        L = int(seq_lens[s])
+        q0, q1 = int(qsl[s]), int(qsl[s + 1])
+        if q1 == q0:
+            continue
+        Ks = gather_seq(key_cache, k_scale_cache, block_table[s], L)     # [L, nkv, hs]
+        Vs = gather_seq(value_cache, v_scale_cache, block_table[s], L)
+        qr = rotate_math(q[q0:q1], signs)                                 # [ql, nq, hs]
+        for g in range(nkv):
+            qg = qr[:, g * group:(g + 1) * group, :]                      # [ql, group, hs]
+            logits = (qg @ Ks[:, g, :].T) * softmax_scale / b            # [ql, group, L]
+            o_rot = _causal_softmax_attend(logits, Vs[:, g, :], L)       # [ql, group, hs]
+            out[q0:q1, g * group:(g + 1) * group] = unrotate_math(o_rot, signs)
+    return out
+
+
+def attention_dense(query, key, value, query_start_loc, seq_lens, softmax_scale: float,
+                    kv_start, seqs=None) -> np.ndarray:
+    """Plain fp64 causal attention in the original domain:
+    softmax(q . k * softmax_scale) @ v per sequence, GQA head h -> h // group.
+    Rows of sequence s in `key`/`value` are kv_start[s] .. kv_start[s] + L_s.
+    Used on unquantized K/V and on dequantized, inverse-rotated K/V."""
+    q = np.asarray(query, dtype=np.float64)
+    Tq, nq, hs = q.shape
+    nkv = np.asarray(key).shape[1]
+    group = nq // nkv
+    out = np.full((Tq, nq, hs), np.nan)
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    if seqs is None:
+        seqs = range(len(seq_lens))
+    for s in seqs:
+        L = int(seq_lens[s])
+        q0, q1 = int(qsl[s]), int(qsl[s + 1])
+        if q1 == q0:
+            continue
+        k0 = int(kv_start[s])
+        k = np.asarray(key[k0:k0 + L], dtype=np.float64)
+        v = np.asarray(value[k0:k0 + L], dtype=np.float64)
+        for g in range(nkv):
+            qg = q[q0:q1, g * group:(g + 1) * group, :]
+            logits = (qg @ k[:, g, :].T) * softmax_scale
+            out[q0:q1, g * group:(g + 1) * group] = _causal_softmax_attend(logits, v[:, g, :], L)
+    return out
