@@ -1,0 +1,262 @@
+"""Benchmark of the INT4 per-token-head RHT KV-cache hot path on one MI355X.
+
+One step = one serving step of the hot path over a resident batch: the step's
+new K/V tokens go through kv4_rht_write (rotate, round through bf16,
+quantize, pack, scatter) and then kv4_paged_attention runs over the whole
+batch (query rotation, paged int4 KV stream with on-the-fly dequant, online
+softmax with softmax_scale / b, split merge, inverse rotation of the output).
+Inputs are synthetic and seeded (workloads/), already in HBM when the timed
+region starts; the context of every sequence is written before timing with
+the same write kernel (that bulk write is timed separately and reported as
+write tokens/s).
+
+Prints ONE JSON line. `value` is decode-attention KV GB/s: algorithmic bytes
+the step's attention must read (int4 codes + fp32 scales of every visible
+(KV token, kv head), page-table entries, query and output) divided by the
+step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+CSRC = os.path.join(ROOT, "paged_decode_attention_reshape_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def attention_bytes(w) -> int:
+    """Algorithmic bytes one attention pass must move: for every sequence,
+    every visible (KV token, kv head): hs/2 + hs/2 code bytes + 2 fp32 scales;
+    plus block-table entries, bf16 query in and bf16 output out."""
+    kv = sum(w.seq_lens) * w.num_kv_heads * (w.head_size + 8)
+    bt = sum(-(-L // w.block_size) for L in w.seq_lens) * 4
+    qo = w.num_q_tokens * w.num_q_heads * w.head_size * 2 * 2
+    return int(kv + bt + qo)
+
+
+def kv_bytes(w) -> int:
+    return int(sum(w.seq_lens) * w.num_kv_heads * (w.head_size + 8))
+
+
+def write_bytes_per_token(w) -> int:
+    """Read bf16 K and V, write int4 codes and two fp32 scales per kv head,
+    read one int64 slot."""
+    return w.num_kv_heads * (4 * w.head_size + w.head_size + 8) + 8
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama8b_long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the write path and attention shard by kv head or sequence with no exchange; "
+              "see DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_decode_attention_reshape_amd as kv4
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.ALL[args.config]()
+    lay = W.make_layout(w)
+    print(f"# config {w.name}: seqs={w.num_seqs} nq={w.num_q_heads} nkv={w.num_kv_heads} hs={w.head_size} "
+          f"kv_tokens={w.total_kv_tokens} q_tokens={w.num_q_tokens}", file=sys.stderr, flush=True)
+    t = W.make_tensors(w, lay, device=dev)
+    slots_all = W.all_slots(lay, w)
+    new_rows = W.new_token_rows(lay, w)
+    ctx_mask = np.ones(slots_all.shape[0], dtype=bool)
+    ctx_mask[new_rows] = False
+    ctx_rows = np.nonzero(ctx_mask)[0]
+
+    nb, bs, nkv, hs = lay.num_blocks, w.block_size, w.num_kv_heads, w.head_size
+    kc = torch.zeros((nb, bs, nkv, hs // 2), dtype=torch.uint8, device=dev)
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros((nb, bs, nkv), dtype=torch.float32, device=dev)
+    vs = torch.zeros_like(ks)
+    stream = torch.cuda.Stream()
+
+    # ---- bulk write of every context token (timed on its own)
+    ctx_idx = torch.from_numpy(ctx_rows).to(dev)
+    k_ctx = t.key.index_select(0, ctx_idx)
+    v_ctx = t.value.index_select(0, ctx_idx)
+    s_ctx = torch.from_numpy(slots_all[ctx_rows]).to(dev)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    wr_ms = []
+    with torch.cuda.stream(stream):
+        for rep in range(3):
+            ev[0].record(stream)
+            kv4.kv4_rht_write(k_ctx, v_ctx, kc, vc, ks, vs, s_ctx, sign_seed=w.sign_seed, stream=stream)
+            ev[1].record(stream)
+            stream.synchronize()
+            wr_ms.append(ev[0].elapsed_time(ev[1]))
+    del k_ctx, v_ctx
+    n_ctx = int(ctx_rows.shape[0])
+    write_ms = float(np.median(wr_ms))
+    write_tps = n_ctx / (write_ms * 1e-3) if n_ctx else 0.0
+    write_gbs = n_ctx * write_bytes_per_token(w) / (write_ms * 1e-3) / 1e9 if n_ctx else 0.0
+
+    # ---- step inputs
+    new_idx = torch.from_numpy(new_rows).to(dev)
+    k_new = t.key.index_select(0, new_idx).contiguous()
+    v_new = t.value.index_select(0, new_idx).contiguous()
+    s_new = torch.from_numpy(slots_all[new_rows]).to(dev)
+    q = t.query
+    bt = torch.from_numpy(lay.block_table).to(dev)
+    slens = torch.from_numpy(lay.seq_lens).to(dev)
+    qsl = torch.from_numpy(lay.query_start_loc).to(dev)
+    out = torch.empty((w.num_q_tokens, w.num_q_heads, hs), dtype=torch.bfloat16, device=dev)
+    need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, w.num_q_heads, nkv, hs,
+                                                  w.max_query_len, w.max_seq_len)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+    def step(e_a=None, e_b=None):
+        kv4.kv4_rht_write(k_new, v_new, kc, vc, ks, vs, s_new, sign_seed=w.sign_seed, stream=stream)
+        if e_a is not None:
+            e_a.record(stream)
+        kv4.kv4_paged_attention(q, kc, vc, ks, vs, bt, slens, qsl, max_query_len=w.max_query_len,
+                                max_seq_len=w.max_seq_len, sign_seed=w.sign_seed, out=out, workspace=ws,
+                                stream=stream)
+        if e_b is not None:
+            e_b.record(stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            step(ev_a[i], ev_b[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(args.steps)]
+    ms_per_step = wall * 1e3 / args.steps
+    attn_avg_ms = float(np.mean(attn_ms))
+
+    a_bytes = attention_bytes(w)
+    value = a_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = a_bytes / (attn_avg_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(PROFILE_COUNTERS):
+        try:
+            pc = json.load(open(PROFILE_COUNTERS))
+            ent = pc.get("workloads", {}).get(w.name)
+            if ent and pc.get("kernel_source_hash") == kernel_source_hash():
+                traffic = ent.get("traffic_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    line = {
+        "metric": "INT4 paged decode attn: KV GB/s & % HBM peak; cache-write tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes / fp32 accumulate (bf16 in/out)",
+        "data": "synthetic seeded N(0,1) bf16, 1% outlier channels x20",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": nkv, "head_size": hs, "block_size": bs,
+                   "total_kv_tokens": w.total_kv_tokens, "max_seq_len": w.max_seq_len,
+                   "q_tokens_per_step": w.num_q_tokens, "new_kv_tokens_per_step": int(new_rows.shape[0]),
+                   "parallelism": "single GPU"},
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "attn_ms": round(attn_avg_ms, 4),
+        "attn_query_tokens_per_s": round(w.num_q_tokens / (attn_avg_ms * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes(w),
+        "write_tokens_per_s": round(write_tps, 1),
+        "write_GBps": round(write_gbs, 2),
+        "write_bulk_tokens": n_ctx,
+        "roofline": {"bound": "hbm", "kernel": "kv4_paged_attention (split-KV attention + merge)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": a_bytes},
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, lay, t, kc, vc, ks, vs, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float):
+    """The CPU oracle (fp64 numpy) on a bounded sample of the same workload:
+    whole sequences of this batch, read from the GPU-written cache, until
+    about `budget_s` seconds of CPU work; reported as KV GB/s like `value`."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from oracle import kv4_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    order = np.random.default_rng(0).permutation(w.num_seqs)
+    q = W.bf16_as_f32_numpy(t.query)
+    done_bytes, done_seqs, spent = 0, 0, 0.0
+    dev = kc.device
+    for s in order:
+        n = -(-w.seq_lens[s] // w.block_size)
+        pages = torch.from_numpy(lay.block_table[s, :n].astype(np.int64)).to(dev)
+        kcs, vcs = kc.index_select(0, pages).cpu().numpy(), vc.index_select(0, pages).cpu().numpy()
+        kss, vss = ks.index_select(0, pages).cpu().numpy(), vs.index_select(0, pages).cpu().numpy()
+        bt = np.zeros_like(lay.block_table)
+        bt[s, :n] = np.arange(n)
+        t0 = time.perf_counter()
+        O.paged_attention(q, kcs, vcs, kss, vss, bt, lay.seq_lens, lay.query_start_loc,
+                          w.head_size ** -0.5, w.sign_seed, seqs=[int(s)])
+        spent += time.perf_counter() - t0
+        done_bytes += int(w.seq_lens[s]) * w.num_kv_heads * (w.head_size + 8)
+        done_seqs += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "host_cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{done_seqs} of {w.num_seqs} sequences of {w.name} (fp64 numpy oracle reading the "
+                      f"GPU-written cache), {spent:.1f} s of CPU time"}
+
+
+if __name__ == "__main__":
+    main()

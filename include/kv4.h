@@ -1,0 +1,191 @@
+/*
+ * kv4.h -- C ABI of libkv4: INT4 per-token-head KV cache with a randomized
+ * Hadamard rotation, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [PR40835] vLLM PR #40835, "[Feature] Triton INT4 per-token-head KV cache
+ *             quantization" -- review thread: float32 scale caches of shape
+ *             [num_blocks, block_size, num_kv_heads], uint8 int4 cache,
+ *             slot_mapping [num_tokens], query_start_loc / seq_lens metadata,
+ *             prefill and decode served by one unified attention entry point.
+ *   [PR56198] runguoli.com, "vLLM -- Attention Kernels & KV Cache
+ *             Quantization", section "PR #56198 -- Support int4_per_token_head
+ *             on non-power-of-two head sizes": head_size d = b * n with b the
+ *             largest power-of-two divisor; H_b applied block-diagonally; the
+ *             read path compensates by b; every head size is accepted.
+ *   [PR62881] vLLM PR #62881, "[Bugfix][Test] Rotate KV into RHT domain in the
+ *             INT4 unified attn test", Details / Root cause and Fix: the write
+ *             path stores K_s = H.D.k (rounded through bf16); the read path
+ *             rotates q' = H.D.q, scales logits by softmax_scale / b and maps
+ *             the output back with D.H(.)/b.
+ *
+ * Numerics fixed where the pages are silent:
+ *   D      sign i (0 <= i < head_size) is -1 iff bit 63 of the (i+1)-th
+ *          SplitMix64 output from state sign_seed is set; one D shared by K,
+ *          V, Q, every head and token.
+ *   H_b    unnormalized Sylvester-order Walsh-Hadamard matrix, applied to the
+ *          contiguous chunks [j*b, (j+1)*b) of each head vector.
+ *   write  x (bf16) -> sign flip -> radix-2 butterflies in float32 with strides
+ *          1, 2, ..., b/2 in that order -> one round-to-nearest-even to bf16 ->
+ *          scale = absmax / 7 (IEEE float32 division) -> code =
+ *          clamp(rint_half_even(y / scale), -8, 7) -> two's-complement nibbles,
+ *          element 2j in the low nibble of byte j. absmax == 0 stores scale 0
+ *          and zero codes.
+ *   read   query i of a sequence with query_len q and seq_len L is at position
+ *          L - q + i and attends to keys 0 .. L - q + i (causal). GQA: query
+ *          head h reads kv head h / (num_q_heads / num_kv_heads).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are caller-owned device buffers (hipMalloc / torch); the
+ *     library never allocates, frees or synchronizes.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the legacy default
+ *     stream) and is asynchronous: a KV4_OK return means the arguments were
+ *     valid and the launches were queued.
+ *   - Arguments are validated on the host before any launch. On failure the
+ *     function returns a nonzero kv4_status, launches nothing, and
+ *     kv4_last_error() (thread-local) describes the problem.
+ *   - Device data that the host cannot see (slot ids, block ids, lengths) is
+ *     range-checked inside the kernels: an out-of-range slot is skipped, an
+ *     out-of-range page id contributes nothing, lengths are clamped to the
+ *     page-table capacity. Kernels never read or write outside the buffers
+ *     whose sizes the arguments describe.
+ *   - Pointers must be 16-byte aligned (the cache rows are read with 16-byte
+ *     vector loads; vLLM PR #62113 aligned per-token-head KV slots to 16 bytes
+ *     for the same reason).
+ *   - head_size: a multiple of 8 in [8, 256]; b must equal the largest power
+ *     of two dividing head_size ([PR56198]); anything else is KV4_EINVAL.
+ */
+#ifndef KV4_H_
+#define KV4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KV4_OK = 0,
+  KV4_EINVAL = 1,        /* invalid argument (shape, pointer, alignment)      */
+  KV4_EUNSUPPORTED = 2,  /* valid but not supported by this build             */
+  KV4_EHIP = 3,          /* a HIP runtime call or kernel launch failed        */
+  KV4_EWORKSPACE = 4     /* workspace missing or smaller than required        */
+} kv4_status;
+
+/*
+ * kv4_rht_write -- the write path, reshape_and_cache_int4 ([PR62881] Root
+ * cause; block-diagonal H_b per [PR56198]; scale cache shapes per [PR40835]).
+ *
+ * For every token t with slot s = slot_mapping[t] in [0, num_blocks*block_size)
+ * and every kv head h, rotates key[t, h, :] and value[t, h, :] (K_s = H.D.k),
+ * rounds through bf16, quantizes to int4 with one float32 scale, and stores
+ *   key_cache  [s / block_size, s % block_size, h, :]  (head_size/2 bytes)
+ *   k_scale_cache[s / block_size, s % block_size, h]   (float32)
+ * and likewise for value. Slots < 0 or >= num_blocks*block_size are skipped.
+ * Duplicate slots in one call race (the stored bytes are then unspecified).
+ *
+ *   key, value          bf16 [num_tokens, num_kv_heads, head_size]; rows of
+ *                       consecutive tokens are key_token_stride /
+ *                       value_token_stride elements apart (>= nkv*head_size,
+ *                       multiple of 8); heads are contiguous within a row.
+ *   key_cache,
+ *   value_cache         uint8 [num_blocks, block_size, num_kv_heads, head_size/2]
+ *   k_scale_cache,
+ *   v_scale_cache       float32 [num_blocks, block_size, num_kv_heads]
+ *   slot_mapping        int64 [num_tokens]
+ *   sign_seed           seed of D (see above)
+ * num_tokens == 0 is a valid no-op.
+ */
+int kv4_rht_write(const void* key, const void* value,
+                  int64_t key_token_stride, int64_t value_token_stride,
+                  void* key_cache, void* value_cache,
+                  float* k_scale_cache, float* v_scale_cache,
+                  const int64_t* slot_mapping, int64_t num_tokens,
+                  int32_t num_kv_heads, int32_t head_size, int32_t b,
+                  int32_t block_size, int64_t num_blocks,
+                  uint64_t sign_seed, void* stream);
+
+/*
+ * kv4_paged_attention_workspace_size -- bytes of device workspace that
+ * kv4_paged_attention needs for these sizes (split-KV partial results and
+ * their merge). Depends only on the host-known sizes listed. Returns 0 for
+ * invalid sizes (kv4_last_error() then says why) -- callers should treat 0
+ * with num_q_tokens > 0 as an error.
+ */
+size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_size, int32_t max_query_len,
+                                          int32_t max_seq_len);
+
+/*
+ * kv4_paged_attention -- the read path, unified_attention_int4 ([PR62881]
+ * Root cause; compensation by b per [PR56198]; metadata per [PR40835]).
+ * Prefill, decode and mixed batches in one call, causal.
+ *
+ * For sequence s with query rows query_start_loc[s] .. query_start_loc[s+1]
+ * and total KV length seq_lens[s] (including the new tokens, already written
+ * with kv4_rht_write), computes for each query head
+ *   q' = H.D.q,  logit_j = k_scale_j * (q' . code_K_j) * softmax_scale / b,
+ *   o' = sum_j softmax(logit)_j * v_scale_j * code_V_j,  out = D.H.o' / b,
+ * reading K/V pages through block_table, and writes out as bf16 (one
+ * round-to-nearest-even of the float32 result).
+ *
+ *   query               bf16 [num_q_tokens, num_q_heads, head_size], token
+ *                       rows query_token_stride elements apart (multiple of 8)
+ *   key_cache, ...      as written by kv4_rht_write; num_blocks pages
+ *   block_table         int32 [num_seqs, max_blocks_per_seq], page ids
+ *   seq_lens            int32 [num_seqs]        (device)
+ *   query_start_loc     int32 [num_seqs + 1]    (device), non-decreasing,
+ *                       query_start_loc[num_seqs] == num_q_tokens
+ *   max_query_len,
+ *   max_seq_len         host-side upper bounds of the device lengths; rows and
+ *                       keys beyond them are not computed
+ *   softmax_scale       the model's scale (e.g. head_size^-0.5); the kernels
+ *                       multiply logits by softmax_scale / b
+ *   out                 bf16 [num_q_tokens, num_q_heads, head_size], contiguous
+ *   workspace           device buffer of at least
+ *                       kv4_paged_attention_workspace_size(...) bytes; its
+ *                       contents need no initialization and are clobbered.
+ *                       Two calls in flight must not share a workspace.
+ * A query row whose causal window is empty (seq_len < query_len) gets zeros.
+ */
+int kv4_paged_attention(const void* query, int64_t query_token_stride,
+                        const void* key_cache, const void* value_cache,
+                        const float* k_scale_cache, const float* v_scale_cache,
+                        int64_t num_blocks,
+                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, const int32_t* query_start_loc,
+                        int32_t num_seqs, int64_t num_q_tokens,
+                        int32_t max_query_len, int32_t max_seq_len,
+                        int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_size, int32_t b, int32_t block_size,
+                        uint64_t sign_seed, float softmax_scale,
+                        void* out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * kv4_dequant -- gather and dequantize cache slots (for tests and debugging;
+ * the round-trip check of [PR62881] Fix).
+ *   out[t, h, i] = code * scale  (one float32 product), and with
+ *   inverse_rotate != 0 additionally D.H(.)/b applied per head vector in
+ *   float32, mapping back to the original domain.
+ *   cache               uint8 [num_blocks, block_size, num_kv_heads, head_size/2]
+ *   scale_cache         float32 [num_blocks, block_size, num_kv_heads]
+ *   slot_mapping        int64 [num_tokens]; out-of-range slots give zeros
+ *   out                 float32 [num_tokens, num_kv_heads, head_size]
+ */
+int kv4_dequant(const void* cache, const float* scale_cache, int64_t num_blocks,
+                const int64_t* slot_mapping, int64_t num_tokens,
+                int32_t num_kv_heads, int32_t head_size, int32_t b,
+                int32_t block_size, uint64_t sign_seed, int32_t inverse_rotate,
+                float* out, void* stream);
+
+/* Thread-local description of the last failure ("" if none). Never NULL. */
+const char* kv4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KV4_H_ */

@@ -1,0 +1,235 @@
+"""Python binding of libkv4 (INT4 per-token-head RHT KV cache on MI355X).
+
+Argument marshalling only: every step of the write path, the paged attention
+and the dequant helper runs in the HIP kernels of libkv4.so (see
+include/kv4.h for the C contracts). torch supplies device memory and the
+current HIP stream. The functions keep the C names.
+
+The library must have been built (``python -m
+paged_decode_attention_reshape_amd.build`` or ``__graft_entry__.build()``);
+importing the functions without it raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkv4.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kv4.h")
+
+KV4_OK, KV4_EINVAL, KV4_EUNSUPPORTED, KV4_EHIP, KV4_EWORKSPACE = 0, 1, 2, 3, 4
+DEFAULT_SIGN_SEED = 42
+
+_c_int32, _c_int64, _c_uint64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+_SIGNATURES = {
+    "kv4_rht_write": (ctypes.c_int, [_vp, _vp, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp, _c_int64,
+                                     _c_int32, _c_int32, _c_int32, _c_int32, _c_int64, _c_uint64, _vp]),
+    "kv4_paged_attention_workspace_size": (ctypes.c_size_t, [_c_int64, _c_int32, _c_int32, _c_int32,
+                                                             _c_int32, _c_int32, _c_int32]),
+    "kv4_paged_attention": (ctypes.c_int, [_vp, _c_int64, _vp, _vp, _vp, _vp, _c_int64, _vp, _c_int32,
+                                           _vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32, _c_int32,
+                                           _c_int32, _c_int32, _c_int32, _c_int32, _c_uint64,
+                                           ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
+    "kv4_dequant": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _c_int64, _c_int32, _c_int32, _c_int32,
+                                   _c_int32, _c_uint64, _c_int32, _vp, _vp]),
+    "kv4_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class Kv4Error(RuntimeError):
+    def __init__(self, func: str, code: int, msg: str):
+        super().__init__(f"{func} failed with status {code}: {msg}")
+        self.code = code
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions declared in include/kv4.h."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv4_[a-z0-9_]+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkv4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libkv4.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def kv4_last_error() -> str:
+    return lib().kv4_last_error().decode()
+
+
+def _check(func: str, rc: int):
+    if rc != KV4_OK:
+        raise Kv4Error(func, rc, kv4_last_error())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _contig(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def kv4_rht_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                  value_cache: torch.Tensor, k_scale_cache: torch.Tensor, v_scale_cache: torch.Tensor,
+                  slot_mapping: torch.Tensor, sign_seed: int = DEFAULT_SIGN_SEED,
+                  b: Optional[int] = None, stream=None) -> None:
+    """Rotate, quantize and scatter key/value [T, nkv, hs] (bf16) into the
+    int4 caches [nb, bs, nkv, hs/2] (uint8) and scale caches [nb, bs, nkv]
+    (float32) at slot_mapping [T] (int64). Asynchronous on `stream`."""
+    _need(key, "key", torch.bfloat16, 3)
+    _need(value, "value", torch.bfloat16, 3)
+    _need(key_cache, "key_cache", torch.uint8, 4)
+    _need(value_cache, "value_cache", torch.uint8, 4)
+    _need(k_scale_cache, "k_scale_cache", torch.float32, 3)
+    _need(v_scale_cache, "v_scale_cache", torch.float32, 3)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache"), (k_scale_cache, "k_scale_cache"),
+                 (v_scale_cache, "v_scale_cache"), (slot_mapping, "slot_mapping")):
+        _contig(t, n)
+    T, nkv, hs = key.shape
+    nb, bs = key_cache.shape[0], key_cache.shape[1]
+    if value.shape != key.shape or slot_mapping.shape[0] != T:
+        raise ValueError("key/value/slot_mapping shapes disagree")
+    if key_cache.shape != (nb, bs, nkv, hs // 2) or value_cache.shape != key_cache.shape:
+        raise ValueError(f"caches must be [num_blocks, block_size, {nkv}, {hs // 2}]")
+    if k_scale_cache.shape != (nb, bs, nkv) or v_scale_cache.shape != k_scale_cache.shape:
+        raise ValueError(f"scale caches must be [num_blocks, block_size, {nkv}]")
+    for t, n in ((key, "key"), (value, "value")):
+        if t.stride(2) != 1 or t.stride(1) != hs:
+            raise ValueError(f"{n} must have contiguous heads (stride (*, {hs}, 1))")
+    rc = lib().kv4_rht_write(key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0),
+                             key_cache.data_ptr(), value_cache.data_ptr(), k_scale_cache.data_ptr(),
+                             v_scale_cache.data_ptr(), slot_mapping.data_ptr(), T, nkv, hs,
+                             hs & -hs if b is None else b, bs, nb, sign_seed & (2 ** 64 - 1), _stream(stream))
+    _check("kv4_rht_write", rc)
+
+
+def kv4_paged_attention_workspace_size(num_q_tokens: int, num_seqs: int, num_q_heads: int,
+                                       num_kv_heads: int, head_size: int, max_query_len: int,
+                                       max_seq_len: int) -> int:
+    n = lib().kv4_paged_attention_workspace_size(num_q_tokens, num_seqs, num_q_heads, num_kv_heads,
+                                                 head_size, max_query_len, max_seq_len)
+    err = kv4_last_error()
+    if n == 0 and err:
+        raise Kv4Error("kv4_paged_attention_workspace_size", KV4_EINVAL, err)
+    return int(n)
+
+
+def kv4_paged_attention(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                        k_scale_cache: torch.Tensor, v_scale_cache: torch.Tensor,
+                        block_table: torch.Tensor, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                        max_query_len: int, max_seq_len: int, softmax_scale: Optional[float] = None,
+                        sign_seed: int = DEFAULT_SIGN_SEED, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, b: Optional[int] = None,
+                        stream=None) -> torch.Tensor:
+    """Paged causal attention over the int4 RHT cache. query [Tq, nq, hs] bf16,
+    block_table [S, max_blocks] int32, seq_lens [S] int32, query_start_loc
+    [S+1] int32 (device), max_query_len / max_seq_len host ints. Returns out
+    [Tq, nq, hs] bf16. Asynchronous on `stream`."""
+    _need(query, "query", torch.bfloat16, 3)
+    _need(key_cache, "key_cache", torch.uint8, 4)
+    _need(value_cache, "value_cache", torch.uint8, 4)
+    _need(k_scale_cache, "k_scale_cache", torch.float32, 3)
+    _need(v_scale_cache, "v_scale_cache", torch.float32, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache"), (k_scale_cache, "k_scale_cache"),
+                 (v_scale_cache, "v_scale_cache"), (block_table, "block_table"), (seq_lens, "seq_lens"),
+                 (query_start_loc, "query_start_loc")):
+        _contig(t, n)
+    Tq, nq, hs = query.shape
+    nb, bs, nkv = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]
+    S = seq_lens.shape[0]
+    if key_cache.shape[3] != hs // 2 or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shapes disagree with query head_size")
+    if k_scale_cache.shape != (nb, bs, nkv) or v_scale_cache.shape != k_scale_cache.shape:
+        raise ValueError("scale cache shapes disagree with the caches")
+    if query_start_loc.shape[0] != S + 1 or block_table.shape[0] != S:
+        raise ValueError("query_start_loc must be [num_seqs + 1] and block_table [num_seqs, *]")
+    if query.stride(2) != 1 or query.stride(1) != hs:
+        raise ValueError("query must have contiguous heads")
+    if out is None:
+        out = torch.empty((Tq, nq, hs), dtype=torch.bfloat16, device=query.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _contig(out, "out")
+    if out.shape != (Tq, nq, hs):
+        raise ValueError("out must be [num_q_tokens, num_q_heads, head_size]")
+    need = kv4_paged_attention_workspace_size(Tq, S, nq, nkv, hs, max_query_len, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if softmax_scale is None:
+        softmax_scale = hs ** -0.5
+    rc = lib().kv4_paged_attention(
+        query.data_ptr(), query.stride(0), key_cache.data_ptr(), value_cache.data_ptr(),
+        k_scale_cache.data_ptr(), v_scale_cache.data_ptr(), nb, block_table.data_ptr(),
+        block_table.shape[1], seq_lens.data_ptr(), query_start_loc.data_ptr(), S, Tq,
+        int(max_query_len), int(max_seq_len), nq, nkv, hs, hs & -hs if b is None else b, bs,
+        sign_seed & (2 ** 64 - 1), float(softmax_scale), out.data_ptr(), ws_ptr, ws_bytes, _stream(stream))
+    _check("kv4_paged_attention", rc)
+    return out
+
+
+def kv4_dequant(cache: torch.Tensor, scale_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                inverse_rotate: bool = False, sign_seed: int = DEFAULT_SIGN_SEED,
+                out: Optional[torch.Tensor] = None, b: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Gather slots from an int4 cache and dequantize to float32 [T, nkv, hs];
+    with inverse_rotate, map back to the original domain (D.H(.)/b)."""
+    _need(cache, "cache", torch.uint8, 4)
+    _need(scale_cache, "scale_cache", torch.float32, 3)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    for t, n in ((cache, "cache"), (scale_cache, "scale_cache"), (slot_mapping, "slot_mapping")):
+        _contig(t, n)
+    nb, bs, nkv, half = cache.shape
+    hs = 2 * half
+    T = slot_mapping.shape[0]
+    if out is None:
+        out = torch.empty((T, nkv, hs), dtype=torch.float32, device=cache.device)
+    _need(out, "out", torch.float32, 3)
+    _contig(out, "out")
+    rc = lib().kv4_dequant(cache.data_ptr(), scale_cache.data_ptr(), nb, slot_mapping.data_ptr(), T, nkv,
+                           hs, hs & -hs if b is None else b, bs, sign_seed & (2 ** 64 - 1),
+                           1 if inverse_rotate else 0, out.data_ptr(), _stream(stream))
+    _check("kv4_dequant", rc)
+    return out
+
+
+__all__ = ["kv4_rht_write", "kv4_paged_attention", "kv4_paged_attention_workspace_size", "kv4_dequant",
+           "kv4_last_error", "Kv4Error", "lib", "header_functions", "LIB_PATH"]

@@ -1,0 +1,301 @@
+// libkv4 C ABI: argument validation, work planning and kernel launches.
+// The declarations and their contracts are in include/kv4.h.
+#include "kv4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "kv4_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return KV4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_head(int32_t head_size, int32_t b) {
+  if (head_size < 8 || head_size > 256 || head_size % 8 != 0)
+    return fail(KV4_EINVAL, "head_size must be a multiple of 8 in [8, 256], got %d", head_size);
+  const int32_t want = head_size & -head_size;
+  if (b != want)
+    return fail(KV4_EINVAL,
+                "b must be the largest power of two dividing head_size (%d for head_size %d), got %d",
+                want, head_size, b);
+  return KV4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KV4_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+long env_long(const char* name, long dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  char* end = nullptr;
+  const long x = std::strtol(v, &end, 10);
+  return (end && *end == 0) ? x : dflt;
+}
+
+constexpr int kRowsMax = 8;          // query rows per VALU wave
+constexpr int64_t kTargetUnits = 2048;
+constexpr int kMinSplit = 256;
+
+// Host planner: depends only on host-known sizes (and the KV4_SPLIT_TOKENS
+// override used by tests), so the workspace size and the launch agree.
+int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t max_query_len,
+              int32_t max_seq_len, kv4::AttnPlan& p) {
+  std::memset(&p, 0, sizeof(p));
+  const int G = nq / nkv;
+  p.path = 0;
+  p.gh = G < kRowsMax ? G : kRowsMax;
+  if (max_query_len <= 1) {
+    p.tq = 1;
+    p.rows = kv4::host_next_pow2(p.gh);
+  } else {
+    p.tq = kRowsMax / p.gh;
+    if (p.tq < 1) p.tq = 1;
+    p.rows = kRowsMax;
+  }
+  p.n_head_tiles = (G + p.gh - 1) / p.gh;
+  const int mql = max_query_len < 1 ? 1 : max_query_len;
+  p.tiles_per_seq = (mql + p.tq - 1) / p.tq;
+  const int64_t uniform = (int64_t)num_seqs * p.tiles_per_seq;
+  const int64_t packed = num_q_tokens / p.tq + num_seqs;
+  if (uniform <= packed) {
+    p.packed_tiles = 0;
+    p.n_qtiles = uniform;
+  } else {
+    p.packed_tiles = 1;
+    p.n_qtiles = packed;
+  }
+  const int64_t units = p.n_qtiles * p.n_head_tiles * nkv;
+  if (units * p.n_head_tiles > INT32_MAX) return fail(KV4_EUNSUPPORTED, "too many query tiles");
+  const int msl = max_seq_len < 1 ? 1 : max_seq_len;
+  long split = env_long("KV4_SPLIT_TOKENS", 0);
+  if (split <= 0) {
+    int64_t ns = (kTargetUnits + units - 1) / (units > 0 ? units : 1);
+    if (ns < 1) ns = 1;
+    split = (msl + ns - 1) / ns;
+    split = (split + 63) / 64 * 64;
+    if (split < kMinSplit) split = kMinSplit;
+  }
+  if (split > msl) split = msl;
+  p.split_tokens = (int)split;
+  p.num_splits = (int)((msl + split - 1) / split);
+  if (p.num_splits > 65535) return fail(KV4_EUNSUPPORTED, "too many KV splits (%d)", p.num_splits);
+  return KV4_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t o_off, ml_off, total;
+};
+
+WsLayout ws_layout(const kv4::AttnPlan& p, int64_t num_q_tokens, int32_t nq, int32_t hs) {
+  WsLayout w{0, 0, 0};
+  if (p.num_splits <= 1 || num_q_tokens == 0) return w;
+  const size_t rows = (size_t)p.num_splits * (size_t)num_q_tokens * (size_t)nq;
+  w.o_off = 0;
+  w.ml_off = align_up(rows * (size_t)hs * sizeof(float), 256);
+  w.total = align_up(w.ml_off + rows * 2 * sizeof(float), 256);
+  return w;
+}
+
+int check_attn_sizes(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
+                     int32_t max_query_len, int32_t max_seq_len) {
+  if (num_q_tokens < 0 || num_q_tokens > INT32_MAX)
+    return fail(KV4_EINVAL, "num_q_tokens out of range: %lld", (long long)num_q_tokens);
+  if (num_seqs < 0) return fail(KV4_EINVAL, "num_seqs must be >= 0, got %d", num_seqs);
+  if (num_q_tokens > 0 && num_seqs == 0) return fail(KV4_EINVAL, "num_q_tokens > 0 needs num_seqs >= 1");
+  if (nkv < 1 || nkv > 65535) return fail(KV4_EINVAL, "num_kv_heads must be in [1, 65535], got %d", nkv);
+  if (nq < 1 || nq % nkv != 0)
+    return fail(KV4_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", nq, nkv);
+  if (max_query_len < 0 || max_seq_len < 0) return fail(KV4_EINVAL, "max lengths must be >= 0");
+  if (hs < 8 || hs > 256 || hs % 8) return fail(KV4_EINVAL, "head_size must be a multiple of 8 in [8, 256]");
+  return KV4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kv4_last_error(void) { return g_last_error.c_str(); }
+
+int kv4_rht_write(const void* key, const void* value, int64_t key_token_stride,
+                  int64_t value_token_stride, void* key_cache, void* value_cache,
+                  float* k_scale_cache, float* v_scale_cache, const int64_t* slot_mapping,
+                  int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b,
+                  int32_t block_size, int64_t num_blocks, uint64_t sign_seed, void* stream) {
+  if (int e = check_head(head_size, b)) return e;
+  if (num_tokens < 0) return fail(KV4_EINVAL, "num_tokens must be >= 0");
+  if (num_kv_heads < 1) return fail(KV4_EINVAL, "num_kv_heads must be >= 1");
+  if (block_size < 1 || block_size > 4096) return fail(KV4_EINVAL, "block_size must be in [1, 4096]");
+  if (num_blocks < 0) return fail(KV4_EINVAL, "num_blocks must be >= 0");
+  if (num_blocks > INT64_MAX / block_size / num_kv_heads / head_size)
+    return fail(KV4_EINVAL, "cache too large");
+  if (num_tokens == 0) return ok();
+  if (num_tokens > INT64_MAX / 2 / num_kv_heads) return fail(KV4_EINVAL, "num_tokens too large");
+  const int64_t row = (int64_t)num_kv_heads * head_size;
+  if (key_token_stride < row || value_token_stride < row || key_token_stride % 8 || value_token_stride % 8)
+    return fail(KV4_EINVAL, "token strides must be >= num_kv_heads*head_size (%lld) and multiples of 8",
+                (long long)row);
+  if (!key || !value || !key_cache || !value_cache || !k_scale_cache || !v_scale_cache || !slot_mapping)
+    return fail(KV4_EINVAL, "null pointer argument");
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
+      !aligned(k_scale_cache, 4) || !aligned(v_scale_cache, 4) || !aligned(slot_mapping, 8))
+    return fail(KV4_EINVAL, "misaligned pointer (K/V and caches need 16 bytes)");
+  kv4::WriteArgs a;
+  a.key = static_cast<const uint16_t*>(key);
+  a.value = static_cast<const uint16_t*>(value);
+  a.key_stride = key_token_stride;
+  a.value_stride = value_token_stride;
+  a.key_cache = static_cast<uint8_t*>(key_cache);
+  a.value_cache = static_cast<uint8_t*>(value_cache);
+  a.k_scale = k_scale_cache;
+  a.v_scale = v_scale_cache;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_slots = num_blocks * block_size;
+  a.nkv = num_kv_heads;
+  a.hs = head_size;
+  a.b = b;
+  a.seed = sign_seed;
+  return hip_status(kv4::launch_write(a, static_cast<hipStream_t>(stream)), "kv4_rht_write launch");
+}
+
+size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_size, int32_t max_query_len,
+                                          int32_t max_seq_len) {
+  if (check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
+                       max_seq_len))
+    return 0;
+  kv4::AttnPlan p;
+  if (make_plan(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, max_query_len, max_seq_len, p)) return 0;
+  g_last_error.clear();
+  return ws_layout(p, num_q_tokens, num_q_heads, head_size).total;
+}
+
+int kv4_paged_attention(const void* query, int64_t query_token_stride, const void* key_cache,
+                        const void* value_cache, const float* k_scale_cache, const float* v_scale_cache,
+                        int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                        int64_t num_q_tokens, int32_t max_query_len, int32_t max_seq_len,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size, int32_t b,
+                        int32_t block_size, uint64_t sign_seed, float softmax_scale, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (int e = check_head(head_size, b)) return e;
+  if (int e = check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
+                               max_seq_len))
+    return e;
+  if (block_size < 1 || block_size > 4096) return fail(KV4_EINVAL, "block_size must be in [1, 4096]");
+  if (num_blocks < 0 || num_blocks > INT32_MAX) return fail(KV4_EINVAL, "num_blocks out of range");
+  if (!std::isfinite(softmax_scale)) return fail(KV4_EINVAL, "softmax_scale must be finite");
+  if (num_q_tokens == 0) return ok();
+  if (max_blocks_per_seq < 1) return fail(KV4_EINVAL, "max_blocks_per_seq must be >= 1");
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return fail(KV4_EINVAL, "page table too long");
+  if (query_token_stride < (int64_t)num_q_heads * head_size || query_token_stride % 8)
+    return fail(KV4_EINVAL, "query_token_stride must be >= num_q_heads*head_size and a multiple of 8");
+  if (!query || !key_cache || !value_cache || !k_scale_cache || !v_scale_cache || !block_table || !seq_lens ||
+      !query_start_loc || !out)
+    return fail(KV4_EINVAL, "null pointer argument");
+  if (!aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(out, 16) ||
+      !aligned(k_scale_cache, 4) || !aligned(v_scale_cache, 4) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4) || !aligned(query_start_loc, 4))
+    return fail(KV4_EINVAL, "misaligned pointer (query, caches and out need 16 bytes)");
+
+  kv4::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  if (int e = make_plan(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, max_query_len, max_seq_len, a.plan))
+    return e;
+  const WsLayout ws = ws_layout(a.plan, num_q_tokens, num_q_heads, head_size);
+  if (ws.total > 0) {
+    if (!workspace || workspace_bytes < ws.total)
+      return fail(KV4_EWORKSPACE, "workspace of %zu bytes required, got %zu", ws.total,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(KV4_EINVAL, "workspace must be 16-byte aligned");
+    a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.o_off);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_off);
+  }
+  a.query = static_cast<const uint16_t*>(query);
+  a.q_stride = query_token_stride;
+  a.key_cache = static_cast<const uint8_t*>(key_cache);
+  a.value_cache = static_cast<const uint8_t*>(value_cache);
+  a.k_scale = k_scale_cache;
+  a.v_scale = v_scale_cache;
+  a.num_blocks = num_blocks;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.qsl = query_start_loc;
+  a.num_seqs = num_seqs;
+  a.num_q_tokens = num_q_tokens;
+  a.max_query_len = max_query_len;
+  a.max_seq_len = max_seq_len;
+  a.nq = num_q_heads;
+  a.nkv = num_kv_heads;
+  a.hs = head_size;
+  a.b = b;
+  a.bs = block_size;
+  a.seed = sign_seed;
+  a.scale_log2 = softmax_scale / (float)b * 1.4426950408889634f;
+  a.out = static_cast<uint16_t*>(out);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (int e = hip_status(kv4::launch_attn_valu(a, st), "kv4_paged_attention launch")) return e;
+  if (a.plan.num_splits > 1)
+    return hip_status(kv4::launch_attn_reduce(a, st), "kv4_paged_attention merge launch");
+  return ok();
+}
+
+int kv4_dequant(const void* cache, const float* scale_cache, int64_t num_blocks, const int64_t* slot_mapping,
+                int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size,
+                uint64_t sign_seed, int32_t inverse_rotate, float* out, void* stream) {
+  if (int e = check_head(head_size, b)) return e;
+  if (num_tokens < 0) return fail(KV4_EINVAL, "num_tokens must be >= 0");
+  if (num_kv_heads < 1) return fail(KV4_EINVAL, "num_kv_heads must be >= 1");
+  if (block_size < 1 || block_size > 4096) return fail(KV4_EINVAL, "block_size must be in [1, 4096]");
+  if (num_blocks < 0 || num_blocks > INT64_MAX / block_size / num_kv_heads / head_size)
+    return fail(KV4_EINVAL, "num_blocks out of range");
+  if (num_tokens == 0) return ok();
+  if (!cache || !scale_cache || !slot_mapping || !out) return fail(KV4_EINVAL, "null pointer argument");
+  if (!aligned(cache, 16) || !aligned(out, 16) || !aligned(scale_cache, 4) || !aligned(slot_mapping, 8))
+    return fail(KV4_EINVAL, "misaligned pointer");
+  kv4::DequantArgs a;
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.scale = scale_cache;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_slots = num_blocks * block_size;
+  a.nkv = num_kv_heads;
+  a.hs = head_size;
+  a.b = b;
+  a.seed = sign_seed;
+  a.inverse_rotate = inverse_rotate ? 1 : 0;
+  a.out = out;
+  return hip_status(kv4::launch_dequant(a, static_cast<hipStream_t>(stream)), "kv4_dequant launch");
+}
+
+}  // extern "C"

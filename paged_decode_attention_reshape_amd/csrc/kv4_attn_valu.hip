@@ -1,0 +1,374 @@
+// Read path (unified_attention_int4), vector-ALU split-KV kernel of libkv4,
+// plus the cross-split log-sum-exp merge and output epilogue.
+//
+// Computes, per query row (query token, query head) and its kv head g:
+//   q' = H.D.q (float32, never rounded), logit_j = k_scale_j (q' . code_j) *
+//   softmax_scale / b, online softmax over the row's causal window, o' =
+//   sum_j p_j v_scale_j code_V_j, out = D.H.o' / b rounded once to bf16 --
+//   vLLM PR #62881 "[Bugfix][Test] Rotate KV into RHT domain in the INT4
+//   unified attn test", Details / Root cause; divisor b per runguoli.com
+//   "vLLM -- Attention Kernels & KV Cache Quantization", section "PR #56198";
+//   metadata (block table, seq_lens, query_start_loc) per vLLM PR #40835
+//   "[Feature] Triton INT4 per-token-head KV cache quantization", review
+//   thread; the 2D / 3D (split along KV) launch choice mirrors the
+//   seq_threshold_3D cases named in PR #62881, Validation.
+//
+// Mapping: one wave per (query tile, kv head, KV split). A KV token is handled
+// by LPT = next_pow2(hs/8) lanes, each owning 8 elements (one 4-byte load of
+// packed codes); a wave covers 64/LPT tokens per step. q' lives in registers
+// in the same chunk layout, so dot products need only an LPT-lane reduction.
+// Codes enter the arithmetic as u = code + 8 (an exact small integer taken
+// from the nibble by masking and a byte-to-float conversion); the constant
+// offset is removed once per dot product with the sum of q', and once per
+// output element with the running sum of p * v_scale. Softmax runs in base 2
+// with softmax_scale / b * log2(e) folded into q'.
+#include "kv4_device.hpp"
+#include "kv4_launch.hpp"
+
+namespace kv4 {
+
+struct Tile {
+  int s;        // sequence
+  int i0;       // first query index of the tile inside the sequence
+  int qbeg;     // first query row of the sequence
+  int qlen;     // query_len of the sequence
+  int L;        // seq_len, clamped to the page-table capacity
+};
+
+// Maps a query-tile index to (sequence, first query). With packed tiles,
+// sequence s owns tiles qsl[s]/tq + s .. qsl[s+1]/tq + s (some may be empty).
+__device__ __forceinline__ bool locate_tile(const AttnArgs& a, int64_t qt, Tile& t) {
+  const int tq = a.plan.tq;
+  int s;
+  int64_t lt;
+  if (a.plan.packed_tiles) {
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      const int64_t v = (int64_t)a.qsl[mid] / tq + mid;
+      if (v <= qt) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
+    lt = qt - ((int64_t)a.qsl[s] / tq + s);
+    if (lt < 0) return false;
+  } else {
+    s = (int)(qt / a.plan.tiles_per_seq);
+    lt = qt - (int64_t)s * a.plan.tiles_per_seq;
+  }
+  if (s < 0 || s >= a.num_seqs) return false;
+  int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
+  qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
+  qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
+  const int qlen = (int)(qe - qb);
+  if (lt * tq >= qlen) return false;
+  int64_t L = a.seq_lens[s];
+  const int64_t cap = (int64_t)a.max_blocks * a.bs;
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  t.s = s;
+  t.i0 = (int)(lt * tq);
+  t.qbeg = (int)qb;
+  t.qlen = qlen;
+  t.L = (int)L;
+  return true;
+}
+
+// 8 packed int4 codes -> u = code + 8 as floats (exact).
+__device__ __forceinline__ void codes_to_u(uint32_t w, float (&u)[8]) {
+  const uint32_t x = w ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
+  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+  // (float)(byte k) lowers to v_cvt_f32_ubyte{k}
+  u[0] = (float)(lo & 0xFFu);
+  u[1] = (float)(hi & 0xFFu);
+  u[2] = (float)((lo >> 8) & 0xFFu);
+  u[3] = (float)((hi >> 8) & 0xFFu);
+  u[4] = (float)((lo >> 16) & 0xFFu);
+  u[5] = (float)((hi >> 16) & 0xFFu);
+  u[6] = (float)(lo >> 24);
+  u[7] = (float)(hi >> 24);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Inverse rotation and store of one output row chunk: o = D.H.o'/b, bf16.
+__device__ __forceinline__ void store_out_row(float (&o)[8], int b, int jj, uint32_t sbits,
+                                              float inv_b, uint16_t* dst, bool do_store) {
+  fwht_b(o, b, jj);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = apply_sign(o[e] * inv_b, sbits, e);
+  if (do_store) {
+    uint4 w;
+    w.x = pack_bf16x2(o[0], o[1]);
+    w.y = pack_bf16x2(o[2], o[3]);
+    w.z = pack_bf16x2(o[4], o[5]);
+    w.w = pack_bf16x2(o[6], o[7]);
+    *reinterpret_cast<uint4*>(dst) = w;
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
+  const int lane = threadIdx.x;
+  const int hs = a.hs;
+  const int LPT = next_pow2(hs >> 3);
+  const int TPI = kWave / LPT;
+  const int jj = lane & (LPT - 1);
+  const int tg = lane / LPT;
+  const bool lane_on = jj < (hs >> 3);
+
+  const int G = a.nq / a.nkv;
+  const int64_t qt = blockIdx.x / a.plan.n_head_tiles;
+  const int ht = blockIdx.x - (int)qt * a.plan.n_head_tiles;
+  const int g = blockIdx.y;
+  const int sp = blockIdx.z;
+
+  Tile t;
+  if (!locate_tile(a, qt, t)) return;
+  const int gh = a.plan.gh;
+  const int h0 = g * G + ht * gh;
+  const int nh = min(gh, G - ht * gh);
+  const int ntok = min(a.plan.tq, t.qlen - t.i0);
+  const int pos0 = t.L - t.qlen + t.i0;               // position of the tile's first query
+  const int kend = pos0 + ntok;                       // keys [0, kend) are visible to some row
+  const int k0 = sp * a.plan.split_tokens;
+  const int k1 = min(k0 + a.plan.split_tokens, kend);
+  if (k0 >= k1 && a.plan.num_splits > 1) return;      // nothing here; the merge skips this split
+
+  const uint32_t sbits = lane_on ? sign_bits8(a.seed, jj) : 0u;
+  uint32_t sx[4];
+  sign_xor_bf16x8(sbits, sx);
+
+  // ---- q' = H.D.q * (softmax_scale / b * log2 e), rows r = ti * gh + hi
+  float qv[R][8];
+  float qsum[R];
+  int rpos[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int ti = r / gh, hi = r - (r / gh) * gh;
+    const bool rv = ti < ntok && hi < nh;
+    rpos[r] = rv ? pos0 + ti : -1;
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (rv && lane_on) {
+      const uint16_t* src = a.query + (int64_t)(t.qbeg + t.i0 + ti) * a.q_stride +
+                            (int64_t)(h0 + hi) * hs + 8 * jj;
+      w = *reinterpret_cast<const uint4*>(src);
+    }
+    const uint32_t wd[4] = {w.x ^ sx[0], w.y ^ sx[1], w.z ^ sx[2], w.w ^ sx[3]};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      qv[r][2 * k] = bf16_lo(wd[k]);
+      qv[r][2 * k + 1] = bf16_hi(wd[k]);
+    }
+    fwht_b(qv[r], a.b, jj);
+    float sum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[r][e] *= a.scale_log2;
+      sum += qv[r][e];
+    }
+    qsum[r] = sum;
+  }
+
+  float acc[R][8];
+  float m[R], l[R], psum[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.0f;
+    psum[r] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] = 0.0f;
+  }
+
+  const int32_t* bt = a.block_table + (int64_t)t.s * a.max_blocks;
+  const int half_row = hs >> 1;
+  const int nkv = a.nkv;
+
+  for (int base = k0; base < k1; base += TPI) {
+    const int tok = base + tg;
+    bool valid = tok < k1;
+    int64_t row = 0;
+    if (valid) {
+      const int page = bt[tok / a.bs];
+      valid = page >= 0 && page < a.num_blocks;
+      row = ((int64_t)page * a.bs + (tok % a.bs)) * nkv + g;
+    }
+    uint32_t kw = 0u, vw = 0u;
+    float ks = 0.0f, vs = 0.0f;
+    if (valid) {
+      ks = a.k_scale[row];
+      vs = a.v_scale[row];
+      if (lane_on) {
+        kw = *reinterpret_cast<const uint32_t*>(a.key_cache + row * half_row + 4 * jj);
+        vw = *reinterpret_cast<const uint32_t*>(a.value_cache + row * half_row + 4 * jj);
+      }
+    }
+    float u[8];
+    codes_to_u(kw, u);
+    float logit[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float d = -8.0f * qsum[r];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(qv[r][e], u[e], d);
+      d = lane_on ? d : 0.0f;
+      logit[r] = group_sum(d, LPT) * ks;
+      if (!valid || tok > rpos[r]) logit[r] = -INFINITY;
+    }
+    codes_to_u(vw, u);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float mx = logit[r];
+      for (int dd = LPT; dd < kWave; dd <<= 1) mx = fmaxf(mx, xor_lane_rt(mx, dd));
+      const float m_new = fmaxf(m[r], mx);
+      if (m_new == -INFINITY) continue;                      // wave-uniform
+      const float p = fast_exp2(logit[r] - m_new);
+      const float pv = p * vs;
+      if (m_new != m[r]) {                                    // wave-uniform
+        const float alpha = fast_exp2(m[r] - m_new);
+        l[r] *= alpha;
+        psum[r] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+        m[r] = m_new;
+      }
+      l[r] += p;
+      psum[r] += pv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pv, u[e], acc[r][e]);
+    }
+  }
+
+  // ---- combine the token groups of the wave
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    for (int dd = LPT; dd < kWave; dd <<= 1) {
+      l[r] += xor_lane_rt(l[r], dd);
+      psum[r] += xor_lane_rt(psum[r], dd);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][e] += xor_lane_rt(acc[r][e], dd);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(-8.0f, psum[r], acc[r][e]);
+  }
+
+  const float inv_b = 1.0f / (float)a.b;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int ti = r / gh, hi = r - (r / gh) * gh;
+    const bool rv = ti < ntok && hi < nh;
+    const int64_t qrow = (int64_t)(t.qbeg + t.i0 + ti);
+    const int h = h0 + hi;
+    if (a.plan.num_splits == 1) {
+      const float inv_l = l[r] > 0.0f ? 1.0f / l[r] : 0.0f;
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = acc[r][e] * inv_l;
+      store_out_row(o, a.b, jj, sbits, inv_b, a.out + (qrow * a.nq + h) * hs + 8 * jj,
+                    rv && lane_on && tg == 0);
+    } else if (rv && tg == 0) {
+      const int64_t prow = ((int64_t)sp * a.num_q_tokens + qrow) * a.nq + h;
+      if (lane_on) {
+        float4* dst = reinterpret_cast<float4*>(a.ws_o + prow * hs + 8 * jj);
+        dst[0] = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+        dst[1] = make_float4(acc[r][4], acc[r][5], acc[r][6], acc[r][7]);
+      }
+      if (jj == 0) {
+        a.ws_ml[2 * prow] = m[r];
+        a.ws_ml[2 * prow + 1] = l[r];
+      }
+    }
+  }
+}
+
+// Merge of the split partials (log-sum-exp in base 2) and the output
+// epilogue D.H(.)/b. One lane group of LP = next_pow2(hs/8) lanes per output
+// row (query token, query head).
+__global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
+  const int hs = a.hs;
+  const int LP = next_pow2(hs >> 3);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int jj = lane & (LP - 1);
+  const int grp = lane / LP;
+  const bool lane_on = jj < (hs >> 3);
+  const int rows_per_wave = kWave / LP;
+  const int64_t n_rows = a.num_q_tokens * a.nq;
+  const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  const int64_t row = wave_id * rows_per_wave + grp;
+  const bool in = row < n_rows;
+  const uint32_t sbits = lane_on ? sign_bits8(a.seed, jj) : 0u;
+  const float inv_b = 1.0f / (float)a.b;
+
+  int nsp = 0;
+  int64_t qtok = 0;
+  if (in) {
+    qtok = row / a.nq;
+    // sequence of this query row: largest s with qsl[s] <= qtok
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.qsl[mid] <= qtok) lo = mid; else hi = mid - 1;
+    }
+    const int s = lo;
+    int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
+    int64_t L = a.seq_lens[s];
+    const int64_t cap = (int64_t)a.max_blocks * a.bs;
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    if (qtok >= qb && qtok < qe) {
+      const int64_t pos = L - (qe - qb) + (qtok - qb);
+      if (pos >= 0) {
+        const int64_t n = (pos + a.plan.split_tokens) / a.plan.split_tokens;   // ceil((pos+1)/split)
+        nsp = (int)(n < a.plan.num_splits ? n : a.plan.num_splits);
+      }
+    }
+  }
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, a.ws_ml[2 * ((int64_t)sp * n_rows + row)]);
+  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float Ls = 0.0f;
+  if (M != -INFINITY) {
+    for (int sp = 0; sp < nsp; ++sp) {
+      const int64_t prow = (int64_t)sp * n_rows + row;
+      const float msp = a.ws_ml[2 * prow];
+      if (msp == -INFINITY) continue;
+      const float w = fast_exp2(msp - M);
+      Ls = fmaf(a.ws_ml[2 * prow + 1], w, Ls);
+      if (lane_on) {
+        const float4* src = reinterpret_cast<const float4*>(a.ws_o + prow * hs + 8 * jj);
+        const float4 x0 = src[0], x1 = src[1];
+        o[0] = fmaf(x0.x, w, o[0]); o[1] = fmaf(x0.y, w, o[1]);
+        o[2] = fmaf(x0.z, w, o[2]); o[3] = fmaf(x0.w, w, o[3]);
+        o[4] = fmaf(x1.x, w, o[4]); o[5] = fmaf(x1.y, w, o[5]);
+        o[6] = fmaf(x1.z, w, o[6]); o[7] = fmaf(x1.w, w, o[7]);
+      }
+    }
+  }
+  const float inv_l = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] *= inv_l;
+  store_out_row(o, a.b, jj, sbits, inv_b, a.out + row * hs + 8 * jj, in && lane_on);
+}
+
+hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream) {
+  const int64_t gx = a.plan.n_qtiles * a.plan.n_head_tiles;
+  dim3 grid((unsigned)gx, (unsigned)a.nkv, (unsigned)a.plan.num_splits), block(64);
+  switch (a.plan.rows) {
+    case 1: hipLaunchKernelGGL(attn_valu_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(attn_valu_kernel<2>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(attn_valu_kernel<4>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(attn_valu_kernel<8>, grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream) {
+  const int LP = host_next_pow2(a.hs / 8);
+  const int64_t rows = a.num_q_tokens * a.nq;
+  const int64_t waves = (rows + (kWave / LP) - 1) / (kWave / LP);
+  const int64_t blocks = (waves + 3) / 4;
+  dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
+  hipLaunchKernelGGL(attn_reduce_kernel, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace kv4

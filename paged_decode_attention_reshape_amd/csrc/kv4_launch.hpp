@@ -1,0 +1,99 @@
+// Host-side launch interface between the C ABI (kv4_api.cpp) and the HIP
+// kernel translation units of libkv4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace kv4 {
+
+inline int host_next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+struct WriteArgs {
+  const uint16_t* key;
+  const uint16_t* value;
+  int64_t key_stride;    // elements between token rows
+  int64_t value_stride;
+  uint8_t* key_cache;
+  uint8_t* value_cache;
+  float* k_scale;
+  float* v_scale;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int64_t num_slots;     // num_blocks * block_size
+  int nkv;
+  int hs;
+  int b;
+  uint64_t seed;
+};
+
+struct DequantArgs {
+  const uint8_t* cache;
+  const float* scale;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int64_t num_slots;
+  int nkv;
+  int hs;
+  int b;
+  uint64_t seed;
+  int inverse_rotate;
+  float* out;
+};
+
+// Work decomposition of one attention call (chosen on the host from host-known
+// sizes only; no device data is read).
+struct AttnPlan {
+  int path;            // 0 = VALU split-KV kernel, 1 = MFMA kernel
+  int tq;              // query tokens per tile
+  int gh;              // query heads (of one kv head's group) per tile
+  int rows;            // tq * gh rounded up to the kernel's row count
+  int n_head_tiles;    // ceil(group / gh)
+  int packed_tiles;    // 1: tiles found by search over query_start_loc
+  int64_t n_qtiles;    // tiles of query tokens (grid, before head tiles)
+  int tiles_per_seq;   // uniform mode: tiles per sequence
+  int split_tokens;    // KV tokens per split
+  int num_splits;      // splits in the grid (1 = no partials)
+};
+
+struct AttnArgs {
+  const uint16_t* query;
+  int64_t q_stride;
+  const uint8_t* key_cache;
+  const uint8_t* value_cache;
+  const float* k_scale;
+  const float* v_scale;
+  int64_t num_blocks;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  int num_seqs;
+  int64_t num_q_tokens;
+  int max_query_len;
+  int max_seq_len;
+  int nq;
+  int nkv;
+  int hs;
+  int b;
+  int bs;
+  uint64_t seed;
+  float scale_log2;    // softmax_scale / b * log2(e)
+  uint16_t* out;
+  float* ws_o;         // [num_splits][num_q_tokens][nq][hs]   (split only)
+  float* ws_ml;        // [num_splits][num_q_tokens][nq][2]    (split only)
+  AttnPlan plan;
+};
+
+hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
+hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace kv4

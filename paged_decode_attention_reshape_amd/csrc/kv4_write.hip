@@ -1,0 +1,187 @@
+// Write path (reshape_and_cache_int4) and the dequant helper of libkv4.
+//
+// The write path stores K_s = H.D.k per (token, kv head) -- vLLM PR #62881
+// "[Bugfix][Test] Rotate KV into RHT domain in the INT4 unified attn test",
+// Details / Root cause -- with H block-diagonal H_b (runguoli.com "vLLM --
+// Attention Kernels & KV Cache Quantization", section "PR #56198"), rounded
+// through bf16 (PR #62881, Fix), one float32 scale per (token, kv head) and
+// two int4 codes per uint8 byte (vLLM PR #40835 "[Feature] Triton INT4
+// per-token-head KV cache quantization", review thread).
+//
+// Mapping on gfx950: one vector = one (token, kind, kv head) head vector of
+// head_size bf16. Each lane owns 8 consecutive elements (one 16-byte load,
+// one 4-byte store of packed codes); a vector spans LP = next_pow2(hs/8)
+// consecutive lanes, a wave handles 64/LP vectors, ordered so that one wave's
+// loads cover consecutive heads of one token row and its stores land in one
+// contiguous cache row. Butterflies with stride < 8 stay in registers; larger
+// strides exchange across lanes with DPP / ds_swizzle. Lanes past hs/8 carry
+// zeros and never store.
+#include "kv4_device.hpp"
+#include "kv4_launch.hpp"
+
+namespace kv4 {
+
+// Quantize one float32 value of a rotated head vector with the vector's scale:
+// rint_half_even(y / scale) clamped to [-8, 7] (IEEE float32 division).
+__device__ __forceinline__ int quant_code(float y, float scale) {
+  float q = __builtin_rintf(y / scale);
+  q = fminf(fmaxf(q, -8.0f), 7.0f);
+  return (int)q;
+}
+
+template <int LP>
+__global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
+  constexpr int VPW = kWave / LP;                      // vectors per wave
+  const int lane = threadIdx.x & (kWave - 1);
+  const int jj = lane & (LP - 1);                      // chunk index in the vector
+  const int grp = lane / LP;
+  const int nchunk = a.hs >> 3;
+  const bool lane_on = jj < nchunk;
+
+  uint32_t sx[4];
+  sign_xor_bf16x8(lane_on ? sign_bits8(a.seed, jj) : 0u, sx);
+
+  const int64_t n_items = a.num_tokens * 2 * a.nkv;
+  const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  const int half_row = a.hs >> 1;
+
+  for (int64_t base = wave_id * VPW; base < n_items; base += n_waves * VPW) {
+    const int64_t item = base + grp;
+    bool ok = item < n_items;
+    int64_t t = 0;
+    int kind = 0, h = 0;
+    int64_t slot = -1;
+    if (ok) {
+      t = item / (2 * a.nkv);
+      const int rem = (int)(item - t * 2 * a.nkv);
+      kind = rem / a.nkv;
+      h = rem - kind * a.nkv;
+      slot = a.slot_mapping[t];
+      ok = slot >= 0 && slot < a.num_slots;
+    }
+    // load 8 bf16 (16 bytes)
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (ok && lane_on) {
+      const uint16_t* src = kind ? (a.value + t * a.value_stride) : (a.key + t * a.key_stride);
+      w = *reinterpret_cast<const uint4*>(src + (int64_t)h * a.hs + 8 * jj);
+    }
+    const uint32_t wd[4] = {w.x ^ sx[0], w.y ^ sx[1], w.z ^ sx[2], w.w ^ sx[3]};
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = bf16_lo(wd[k]);
+      v[2 * k + 1] = bf16_hi(wd[k]);
+    }
+    fwht_b(v, a.b, jj);
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = round_bf16(v[e]);
+      amax = fmaxf(amax, fabsf(v[e]));
+    }
+    amax = group_max(amax, LP);
+    const float scale = amax / 7.0f;
+    uint32_t packed = 0;
+    if (scale > 0.0f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) packed |= ((uint32_t)quant_code(v[e], scale) & 0xFu) << (4 * e);
+    }
+    if (ok && lane_on) {
+      uint8_t* cache = kind ? a.value_cache : a.key_cache;
+      const int64_t row = slot * a.nkv + h;
+      *reinterpret_cast<uint32_t*>(cache + row * half_row + 4 * jj) = packed;
+      if (jj == 0) (kind ? a.v_scale : a.k_scale)[row] = scale;
+    }
+  }
+}
+
+template <int LP>
+__global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
+  constexpr int VPW = kWave / LP;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int jj = lane & (LP - 1);
+  const int grp = lane / LP;
+  const int nchunk = a.hs >> 3;
+  const bool lane_on = jj < nchunk;
+  const uint32_t sbits = lane_on ? sign_bits8(a.seed, jj) : 0u;
+  const float inv_b = 1.0f / (float)a.b;   // exact: b is a power of two
+  const int64_t n_items = a.num_tokens * a.nkv;
+  const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  const int half_row = a.hs >> 1;
+
+  for (int64_t base = wave_id * VPW; base < n_items; base += n_waves * VPW) {
+    const int64_t item = base + grp;
+    const bool in = item < n_items;
+    int64_t t = 0, slot = -1;
+    int h = 0;
+    if (in) {
+      t = item / a.nkv;
+      h = (int)(item - t * a.nkv);
+      slot = a.slot_mapping[t];
+    }
+    const bool ok = in && slot >= 0 && slot < a.num_slots;
+    uint32_t codes = 0;
+    float sc = 0.0f;
+    if (ok && lane_on) {
+      const int64_t row = slot * a.nkv + h;
+      codes = *reinterpret_cast<const uint32_t*>(a.cache + row * half_row + 4 * jj);
+      sc = a.scale[row];
+    }
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = ((int)(codes << (28 - 4 * e))) >> 28;   // sign-extend nibble e
+      v[e] = (float)c * sc;
+    }
+    if (a.inverse_rotate) {
+      fwht_b(v, a.b, jj);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = apply_sign(v[e] * inv_b, sbits, e);
+    }
+    if (in && lane_on) {
+      float4* dst = reinterpret_cast<float4*>(a.out + item * a.hs + 8 * jj);
+      dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+      dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+static int lanes_per_vector(int hs) { return host_next_pow2(hs / 8); }
+
+hipError_t launch_write(const WriteArgs& a, hipStream_t stream) {
+  const int LP = lanes_per_vector(a.hs);
+  const int64_t items = a.num_tokens * 2 * a.nkv;
+  const int64_t waves = (items + (kWave / LP) - 1) / (kWave / LP);
+  const int64_t blocks = std::min<int64_t>((waves + 3) / 4, 256 * 64);
+  dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
+  switch (LP) {
+    case 1: hipLaunchKernelGGL(write_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(write_kernel<2>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(write_kernel<4>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(write_kernel<8>, grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(write_kernel<16>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(write_kernel<32>, grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream) {
+  const int LP = lanes_per_vector(a.hs);
+  const int64_t items = a.num_tokens * a.nkv;
+  const int64_t waves = (items + (kWave / LP) - 1) / (kWave / LP);
+  const int64_t blocks = std::min<int64_t>((waves + 3) / 4, 256 * 64);
+  dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
+  switch (LP) {
+    case 1: hipLaunchKernelGGL(dequant_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(dequant_kernel<2>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(dequant_kernel<4>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(dequant_kernel<8>, grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(dequant_kernel<16>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(dequant_kernel<32>, grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kv4

@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kv4.h declares, and rejects invalid arguments on the host before any
+HIP call (no kernel is launched by anything here)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import paged_decode_attention_reshape_amd as kv4
+from paged_decode_attention_reshape_amd.build import build_library
+
+EINVAL, EWORKSPACE = kv4.KV4_EINVAL, kv4.KV4_EWORKSPACE
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kv4.LIB_PATH):
+        build_library()
+    return kv4.lib()
+
+
+def test_header_declares_the_boundary():
+    assert kv4.header_functions() == sorted([
+        "kv4_dequant", "kv4_last_error", "kv4_paged_attention",
+        "kv4_paged_attention_workspace_size", "kv4_rht_write"])
+
+
+def test_every_declared_symbol_is_exported(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", kv4.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in kv4.header_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_binding_names_match_c_names():
+    for name in kv4.header_functions():
+        assert callable(getattr(kv4, name)), name
+
+
+def _write(L, **over):
+    args = dict(key=16, value=16, ks=192, vs=192, kc=16, vc=16, ksc=16, vsc=16, slots=16, T=4, nkv=2, hs=96,
+                b=32, bs=16, nb=4, seed=42)
+    args.update(over)
+    a = args
+    return L.kv4_rht_write(a["key"], a["value"], a["ks"], a["vs"], a["kc"], a["vc"], a["ksc"], a["vsc"],
+                           a["slots"], a["T"], a["nkv"], a["hs"], a["b"], a["bs"], a["nb"], a["seed"], None)
+
+
+@pytest.mark.parametrize("over,needle", [
+    (dict(hs=100, b=4), "multiple of 8"),
+    (dict(hs=264, b=8), "multiple of 8"),
+    (dict(hs=96, b=96), "largest power of two"),
+    (dict(hs=96, b=16), "largest power of two"),
+    (dict(hs=128, b=64), "largest power of two"),
+    (dict(nkv=0), "num_kv_heads"),
+    (dict(bs=0), "block_size"),
+    (dict(T=-1), "num_tokens"),
+    (dict(ks=100), "stride"),
+    (dict(ks=194), "stride"),
+    (dict(key=0), "null"),
+    (dict(slots=0), "null"),
+    (dict(kc=8), "misaligned"),
+    (dict(key=24), "misaligned"),
+])
+def test_write_validation(L, over, needle):
+    assert _write(L, **over) == EINVAL
+    assert needle in kv4.kv4_last_error()
+
+
+def test_write_accepts_non_power_of_two_heads_noop(L):
+    """Every head size that is a multiple of 8 is accepted (the pages' abort
+    on head_size 96 is the failure this guards against); num_tokens == 0 is a
+    valid no-op that launches nothing."""
+    for hs in range(8, 257, 8):
+        assert _write(L, hs=hs, b=hs & -hs, ks=2 * hs, vs=2 * hs, T=0) == 0, kv4.kv4_last_error()
+    assert kv4.kv4_last_error() == ""
+
+
+def _attn(L, **over):
+    a = dict(q=16, qs=8 * 96, kc=16, vc=16, ksc=16, vsc=16, nb=10, bt=16, maxb=4, sl=16, qsl=16, S=2, Tq=2,
+             mql=1, msl=64, nq=8, nkv=2, hs=96, b=32, bs=16, seed=42, scale=0.1, out=16, ws=0, wsb=0)
+    a.update(over)
+    return L.kv4_paged_attention(a["q"], a["qs"], a["kc"], a["vc"], a["ksc"], a["vsc"], a["nb"], a["bt"],
+                                 a["maxb"], a["sl"], a["qsl"], a["S"], a["Tq"], a["mql"], a["msl"], a["nq"],
+                                 a["nkv"], a["hs"], a["b"], a["bs"], a["seed"], a["scale"], a["out"], a["ws"],
+                                 a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,needle", [
+    (dict(hs=97), "multiple of 8"),
+    (dict(b=96), "largest power of two"),
+    (dict(nq=7), "multiple of num_kv_heads"),
+    (dict(nkv=0), "num_kv_heads"),
+    (dict(S=0), "num_seqs"),
+    (dict(Tq=-3), "num_q_tokens"),
+    (dict(maxb=0), "max_blocks_per_seq"),
+    (dict(qs=8), "query_token_stride"),
+    (dict(scale=float("inf")), "softmax_scale"),
+    (dict(q=0), "null"),
+    (dict(out=8), "misaligned"),
+    (dict(mql=-1), "max lengths"),
+])
+def test_attention_validation(L, over, needle):
+    assert _attn(L, **over) == EINVAL
+    assert needle in kv4.kv4_last_error()
+
+
+def test_attention_workspace_required(L):
+    need = L.kv4_paged_attention_workspace_size(2, 2, 8, 2, 96, 1, 100000)
+    assert need > 0
+    assert _attn(L, msl=100000, ws=0, wsb=0) == EWORKSPACE
+    assert "workspace" in kv4.kv4_last_error()
+    assert _attn(L, msl=100000, ws=256, wsb=need - 1) == EWORKSPACE
+
+
+def test_workspace_size(L):
+    # no query tokens -> no workspace; decode over short contexts -> no split
+    assert L.kv4_paged_attention_workspace_size(0, 0, 8, 2, 96, 0, 0) == 0
+    assert L.kv4_paged_attention_workspace_size(4096, 4096, 8, 8, 128, 1, 200) == 0
+    # long contexts are split: partial rows of hs + 2 floats per split
+    n = L.kv4_paged_attention_workspace_size(128, 128, 32, 8, 128, 1, 32768)
+    assert n >= 2 * 128 * 32 * 130 * 4
+    # invalid sizes give 0 and a message
+    assert L.kv4_paged_attention_workspace_size(4, 1, 7, 2, 96, 1, 10) == 0
+    assert "multiple" in kv4.kv4_last_error()
+
+
+def test_dequant_validation(L):
+    rc = L.kv4_dequant(16, 16, 4, 16, 3, 2, 96, 64, 16, 42, 1, 16, None)
+    assert rc == EINVAL and "largest power of two" in kv4.kv4_last_error()
+    rc = L.kv4_dequant(16, 16, 4, 16, 0, 2, 96, 32, 16, 42, 1, 16, None)
+    assert rc == 0
+    rc = L.kv4_dequant(0, 16, 4, 16, 3, 2, 96, 32, 16, 42, 1, 16, None)
+    assert rc == EINVAL and "null" in kv4.kv4_last_error()
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros((2, 2, 96), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kv4.kv4_rht_write(x, x, torch.zeros((1, 16, 2, 48), dtype=torch.uint8),
+                          torch.zeros((1, 16, 2, 48), dtype=torch.uint8),
+                          torch.zeros((1, 16, 2)), torch.zeros((1, 16, 2)), torch.zeros(2, dtype=torch.int64))

@@ -1,0 +1,240 @@
+"""Read path parity for kv4_paged_attention.
+
+Gates (tolerances are written here, in the tests):
+  G2  vs the fp64 oracle reading the cache the GPU wrote: atol = rtol = 1e-2.
+  G3  vs the pages-style reference (the oracle rotates, rounds through bf16,
+      quantizes, dequantizes, inverse-rotates, then plain fp64 attention in
+      the original domain): the pages' atol = rtol = 5e-2.
+  G4  vs unquantized fp64 attention: atol = rtol = 5e-2 only where the int4
+      method itself meets it (long contexts); otherwise the error and the
+      correlation are reported.
+Writes are also compared bit-exactly (G1) in every case.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (DEV, O, W, allclose_report, corr, host, kv4, oracle_attention_on_gpu_cache,
+                         oracle_caches, run_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+G2 = dict(atol=1e-2, rtol=1e-2)
+G3 = dict(atol=5e-2, rtol=5e-2)
+
+
+def _g1(r):
+    okc, ovc, oks, ovs = oracle_caches(r)
+    np.testing.assert_array_equal(host(r.kc), okc)
+    np.testing.assert_array_equal(host(r.vc), ovc)
+    np.testing.assert_array_equal(host(r.ks).view(np.uint32), oks.view(np.uint32))
+    np.testing.assert_array_equal(host(r.vs).view(np.uint32), ovs.view(np.uint32))
+
+
+def _g2(r, **kw):
+    ref = oracle_attention_on_gpu_cache(r, **kw)
+    got = host(r.out.float())
+    nbad, mx = allclose_report(got, ref, **G2)
+    say(f"    G2 max abs err {mx:.3e}, violations {nbad}")
+    assert nbad == 0, f"G2: {nbad} elements outside atol=rtol=1e-2 (max err {mx})"
+    return got, ref
+
+
+def _g3(r, got):
+    w = r.w
+    key, value, query = (W.bf16_as_f32_numpy(x) for x in (r.t.key, r.t.value, r.t.query))
+    kc, vc, ks, vs = O.write_kv(key, value, r.slots, r.lay.num_blocks, w.block_size, w.sign_seed)
+    kh = O.dequant(kc, ks, r.slots, w.sign_seed, inverse_rotate=True)
+    vh = O.dequant(vc, vs, r.slots, w.sign_seed, inverse_rotate=True)
+    ref = O.attention_dense(query, kh, vh, r.lay.query_start_loc, w.seq_lens, w.head_size ** -0.5,
+                            r.lay.kv_start)
+    nbad, mx = allclose_report(got, ref, **G3)
+    assert nbad == 0, f"G3: {nbad} elements outside 5e-2 (max err {mx})"
+    return ref
+
+
+CASES = [
+    # name, nq, nkv, hs, query_lens, seq_lens, block_size
+    ("tiny_L32", 4, 4, 128, [1], [32], 16),
+    ("tiny_L64", 4, 4, 128, [1], [64], 16),
+    ("tiny_L128", 4, 4, 128, [1], [128], 16),
+    ("partial_page_q4_L128_L97", 4, 4, 128, [4, 4], [128, 97], 16),
+    ("phi3_like_hs96", 8, 8, 96, [1] * 5, [1024, 17, 300, 33, 512], 16),
+    ("gqa4_hs64", 8, 2, 64, [1] * 6, [1000, 1, 16, 17, 2049, 160], 16),
+    ("gqa6_hs128_mixed", 12, 2, 128, [1, 37, 1, 5, 1], [90, 300, 2000, 5, 64], 16),
+    ("hs192_b64", 8, 2, 192, [1, 3], [700, 129], 16),
+    ("hs80_b16", 4, 1, 80, [1, 2], [333, 50], 16),
+    ("hs256", 4, 2, 256, [1, 1], [100, 257], 16),
+    ("hs8", 2, 1, 8, [1, 3], [40, 9], 16),
+    ("bs8_gqa8", 16, 2, 64, [1, 1], [200, 95], 8),
+    ("bs32", 4, 4, 128, [1, 2], [300, 31], 32),
+    ("bs1", 2, 2, 64, [1], [37], 1),
+    ("group3_prefill", 6, 2, 64, [20, 1], [20, 60], 16),
+    ("group16", 32, 2, 64, [1, 4], [300, 64], 16),
+    ("empty_query_seq", 4, 2, 64, [0, 1, 0, 3], [10, 20, 30, 40], 16),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_attention_parity(case):
+    name, nq, nkv, hs, ql, sl, bs = case
+    w = W.custom(name, nq, nkv, hs, ql, sl, block_size=bs)
+    r = run_gpu(w)
+    _g1(r)
+    got, _ = _g2(r)
+    _g3(r, got)
+
+
+@pytest.mark.parametrize("split", ["64", "100", "1000"])
+def test_attention_forced_splits_match(split, monkeypatch):
+    """The split-KV launch (partials + log-sum-exp merge) against the oracle,
+    with small forced split sizes that give many splits and ragged tails."""
+    monkeypatch.setenv("KV4_SPLIT_TOKENS", split)
+    w = W.custom("split", 8, 2, 96, [1, 1, 7, 1], [1500, 63, 700, 1], block_size=16)
+    r = run_gpu(w)
+    _g2(r)
+
+
+def test_query_longer_than_context_gives_zero_rows():
+    """seq_len < query_len: rows whose causal window is empty come out as 0;
+    the others attend normally."""
+    w = W.custom("empty_window", 4, 2, 64, [5, 1], [3, 10], block_size=16)
+    r = run_gpu(w)
+    got = host(r.out.float())
+    ref = oracle_attention_on_gpu_cache(r)
+    # rows 0, 1 of sequence 0 sit at positions -2, -1: empty window
+    assert not got[0:2].any()
+    ref[0:2] = 0.0
+    nbad, mx = allclose_report(got, ref, **G2)
+    assert nbad == 0, mx
+
+
+def test_seed_sweep_tiny():
+    """200 seeds of the tiny shape (1 sequence, 4/4 heads, hs 128, kv_len 32
+    and 64, one decode query): G2 on every seed, and the pages' G3 check with
+    corr(out, ref) ~ 1 (the pages report 1.0000 and 0/200 failing)."""
+    worst2, worst3, fails3, corrs = 0.0, 0.0, 0, []
+    for seed in range(200):
+        for L in (32, 64):
+            w = W.custom(f"tiny{seed}", 4, 4, 128, [1], [L], block_size=16, shuffle_pages=False, seed=seed)
+            r = run_gpu(w) if seed % 50 == 0 else _quiet_run(w)
+            got = host(r.out.float())
+            ref2 = oracle_attention_on_gpu_cache(r)
+            n2, m2 = allclose_report(got, ref2, **G2)
+            assert n2 == 0, (seed, L, m2)
+            worst2 = max(worst2, m2)
+            ref3 = _g3_ref(r)
+            n3, m3 = allclose_report(got, ref3, **G3)
+            fails3 += n3 > 0
+            worst3 = max(worst3, m3)
+            corrs.append(corr(got, ref3))
+    say(f"    seed sweep: worst G2 {worst2:.3e}, worst G3 {worst3:.3e}, G3 fails {fails3}/400, "
+        f"min corr {min(corrs):.5f}")
+    assert fails3 == 0
+    assert min(corrs) > 0.999
+
+
+def _quiet_run(w):
+    import gpu_helpers
+    old = gpu_helpers.say
+    gpu_helpers.say = lambda *_: None
+    try:
+        return run_gpu(w)
+    finally:
+        gpu_helpers.say = old
+
+
+def _g3_ref(r):
+    w = r.w
+    key, value, query = (W.bf16_as_f32_numpy(x) for x in (r.t.key, r.t.value, r.t.query))
+    kc, vc, ks, vs = O.write_kv(key, value, r.slots, r.lay.num_blocks, w.block_size, w.sign_seed)
+    kh = O.dequant(kc, ks, r.slots, w.sign_seed, inverse_rotate=True)
+    vh = O.dequant(vc, vs, r.slots, w.sign_seed, inverse_rotate=True)
+    return O.attention_dense(query, kh, vh, r.lay.query_start_loc, w.seq_lens, w.head_size ** -0.5,
+                             r.lay.kv_start)
+
+
+def test_g4_unquantized_long_context():
+    """Against unquantized fp64 attention the int4 method meets the pages'
+    5e-2 at long contexts (hs 64, 2560 keys); the GPU must too."""
+    w = W.custom("g4", 8, 2, 64, [1, 1], [2560, 2400], block_size=16)
+    r = run_gpu(w)
+    key, value, query = (W.bf16_as_f32_numpy(x) for x in (r.t.key, r.t.value, r.t.query))
+    ref = O.attention_dense(query, key, value, r.lay.query_start_loc, w.seq_lens, 64 ** -0.5, r.lay.kv_start)
+    got = host(r.out.float())
+    nbad, mx = allclose_report(got, ref, atol=5e-2, rtol=5e-2)
+    say(f"    G4 max abs err {mx:.3e}, corr {corr(got, ref):.5f}")
+    assert nbad == 0
+
+
+def test_g4_reported_at_tiny_sizes():
+    """At kv_len 32..128 the int4 error alone exceeds 5e-2 against unquantized
+    attention for any implementation; report it and require the GPU error to
+    match the oracle's own int4 error closely."""
+    for L in (32, 64, 128):
+        w = W.custom(f"g4t{L}", 4, 4, 128, [1], [L], block_size=16, shuffle_pages=False)
+        r = run_gpu(w)
+        key, value, query = (W.bf16_as_f32_numpy(x) for x in (r.t.key, r.t.value, r.t.query))
+        ref = O.attention_dense(query, key, value, r.lay.query_start_loc, w.seq_lens, 128 ** -0.5,
+                                r.lay.kv_start)
+        got = host(r.out.float())
+        orc = oracle_attention_on_gpu_cache(r)
+        e_gpu, e_orc = np.abs(got - ref).max(), np.abs(orc - ref).max()
+        say(f"    L={L}: int4 vs unquantized max err gpu {e_gpu:.3e} oracle {e_orc:.3e}, "
+            f"corr {corr(got, ref):.4f}")
+        assert abs(e_gpu - e_orc) < 1e-2 + 0.05 * e_orc
+
+
+def test_negative_control_unrotated_cache_is_detected():
+    """A cache filled with unrotated K/V (quantized without H.D, built by the
+    oracle and uploaded) gives an output ~0, uncorrelated with the reference,
+    and fails G3 -- the tests can see a missing rotation."""
+    hs, L = 128, 64
+    w = W.custom("neg", 4, 4, hs, [1], [L], block_size=16, shuffle_pages=False)
+    lay = W.make_layout(w)
+    t = W.make_tensors(w, lay)
+    key, value, query = (W.bf16_as_f32_numpy(x) for x in (t.key, t.value, t.query))
+    caches = []
+    for x in (key, value):
+        codes, scale = O.quantize_int4(x)
+        c, s = O.new_cache(lay.num_blocks, 16, 4, hs)
+        sl = W.all_slots(lay, w)
+        c[sl // 16, sl % 16] = O.pack_int4(codes)
+        s[sl // 16, sl % 16] = scale
+        caches += [torch.from_numpy(c).to(DEV), torch.from_numpy(s).to(DEV)]
+    kc, ks, vc, vs = caches
+    out = kv4.kv4_paged_attention(t.query.to(DEV), kc, vc, ks, vs, torch.from_numpy(lay.block_table).to(DEV),
+                                  torch.from_numpy(lay.seq_lens).to(DEV),
+                                  torch.from_numpy(lay.query_start_loc).to(DEV), max_query_len=1,
+                                  max_seq_len=L)
+    torch.cuda.synchronize()
+    got = host(out.float())
+    ref = O.attention_dense(query, key, value, lay.query_start_loc, w.seq_lens, hs ** -0.5, lay.kv_start)
+    c = corr(got, ref)
+    say(f"    unrotated cache: corr {c:+.3f}, out std {got.std():.4f} vs ref std {ref.std():.4f}")
+    assert abs(c) < 0.3
+    assert got.std() < 0.2 * ref.std()
+    nbad, _ = allclose_report(got, ref, **G3)
+    assert nbad > 0
+
+
+def test_stream_and_out_buffer_reuse():
+    """Launch on a side stream into a caller-provided output and workspace."""
+    w = W.custom("stream", 8, 2, 128, [1, 1], [3000, 40], block_size=16)
+    lay = W.make_layout(w)
+    r = run_gpu(w, attention=False)
+    s = torch.cuda.Stream()
+    out = torch.full((w.num_q_tokens, 8, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, 8, 2, 128, 1, w.max_seq_len)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
+    q = r.t.query.to(DEV)
+    bt, slens, qsl = (torch.from_numpy(x).to(DEV) for x in (lay.block_table, lay.seq_lens, lay.query_start_loc))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        kv4.kv4_paged_attention(q, r.kc, r.vc, r.ks, r.vs, bt, slens, qsl, max_query_len=1,
+                                max_seq_len=w.max_seq_len, out=out, workspace=ws, stream=s)
+    s.synchronize()
+    r.out = out
+    _g2(r)
