@@ -32,7 +32,8 @@ Readings where the pages are silent (each listed in the design doc):
      unnormalized.  Blocks are contiguous chunks [j*b, (j+1)*b).  The int4 rule
      is absmax / 7, round-half-to-even of the float32 quotient, clamp [-8, 7],
      two's-complement nibbles, element 2j in the low nibble of byte j.  amax == 0
-     stores scale 0 and codes 0.  slot < 0 skips the token.  Query i of a
+     stores scale 0 and codes 0.  A slot outside [0, num_blocks * block_size)
+     skips the token.  Query i of a
      sequence with query_len q and seq_len L sits at position L - q + i and
      attends to keys 0..L-q+i.
 """
@@ -206,8 +207,9 @@ def rht_write(x_bf16: np.ndarray, cache: np.ndarray, scale_cache: np.ndarray,
               slot_mapping: np.ndarray, sign_seed: int, chunk: int = 16384) -> None:
     """Write path for one of K or V: rotate, round through bf16, quantize and
     pack each (token, kv head) vector into its slot (blk = slot // bs,
-    off = slot % bs; [PR40835] review round-trip loop). slot < 0 skips.
-    Every vector is independent; tokens are processed a chunk at a time."""
+    off = slot % bs; [PR40835] review round-trip loop). Slots outside
+    [0, num_blocks * bs) name no cache row and are skipped. Every vector is
+    independent; tokens are processed a chunk at a time."""
     x = np.asarray(x_bf16, dtype=np.float32)
     T, nkv, hs = x.shape
     bs = cache.shape[1]
@@ -215,7 +217,7 @@ def rht_write(x_bf16: np.ndarray, cache: np.ndarray, scale_cache: np.ndarray,
     sl = np.asarray(slot_mapping, dtype=np.int64)
     for t0 in range(0, T, chunk):
         s = sl[t0:t0 + chunk]
-        keep = s >= 0
+        keep = (s >= 0) & (s < cache.shape[0] * bs)
         if not keep.any():
             continue
         y = rotate_spec(x[t0:t0 + chunk][keep], signs)      # [t, nkv, hs]
