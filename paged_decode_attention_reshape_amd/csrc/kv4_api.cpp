@@ -59,25 +59,39 @@ long env_long(const char* name, long dflt) {
   return (end && *end == 0) ? x : dflt;
 }
 
-constexpr int kRowsMax = 8;          // query rows per VALU wave
-constexpr int64_t kTargetUnits = 2048;
+constexpr int kRowsMax = 8;             // query rows per VALU wave
+constexpr int kMfmaRows = 16;           // query rows per MFMA tile
+constexpr int64_t kTargetUnitsValu = 2048;
+constexpr int64_t kTargetUnitsMfma = 32768;
 constexpr int kMinSplit = 256;
 
-// Host planner: depends only on host-known sizes (and the KV4_SPLIT_TOKENS
-// override used by tests), so the workspace size and the launch agree.
-int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t max_query_len,
-              int32_t max_seq_len, kv4::AttnPlan& p) {
+bool mfma_head_size(int hs) { return hs == 64 || hs == 96 || hs == 128 || hs == 192; }
+
+// Host planner: depends only on host-known sizes (and the KV4_SPLIT_TOKENS /
+// KV4_FORCE_PATH overrides used by tests), so the workspace size and the
+// launch agree. Path 1 (matrix cores) is used where the query block is dense
+// (GQA group > 1 or query_len > 1), the head size is a multiple of 32 the
+// kernel is built for, and pages hold a multiple of 16 tokens.
+int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
+              int32_t max_query_len, int32_t max_seq_len, int32_t block_size, kv4::AttnPlan& p) {
   std::memset(&p, 0, sizeof(p));
   const int G = nq / nkv;
-  p.path = 0;
-  p.gh = G < kRowsMax ? G : kRowsMax;
+  const bool mfma_ok = mfma_head_size(hs) && block_size % 16 == 0;
+  bool mfma = mfma_ok && (G > 1 || max_query_len > 1);
+  if (const char* f = std::getenv("KV4_FORCE_PATH")) {
+    if (!std::strcmp(f, "valu")) mfma = false;
+    if (!std::strcmp(f, "mfma")) mfma = mfma_ok;
+  }
+  p.path = mfma ? 1 : 0;
+  const int rmax = mfma ? kMfmaRows : kRowsMax;
+  p.gh = G < rmax ? G : rmax;
   if (max_query_len <= 1) {
     p.tq = 1;
-    p.rows = kv4::host_next_pow2(p.gh);
+    p.rows = mfma ? kMfmaRows : kv4::host_next_pow2(p.gh);
   } else {
-    p.tq = kRowsMax / p.gh;
+    p.tq = rmax / p.gh;
     if (p.tq < 1) p.tq = 1;
-    p.rows = kRowsMax;
+    p.rows = rmax;
   }
   p.n_head_tiles = (G + p.gh - 1) / p.gh;
   const int mql = max_query_len < 1 ? 1 : max_query_len;
@@ -92,36 +106,54 @@ int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, i
     p.n_qtiles = packed;
   }
   const int64_t units = p.n_qtiles * p.n_head_tiles * nkv;
-  if (units * p.n_head_tiles > INT32_MAX) return fail(KV4_EUNSUPPORTED, "too many query tiles");
+  if (units > INT32_MAX / 2) return fail(KV4_EUNSUPPORTED, "too many query tiles");
   const int msl = max_seq_len < 1 ? 1 : max_seq_len;
   long split = env_long("KV4_SPLIT_TOKENS", 0);
   if (split <= 0) {
-    int64_t ns = (kTargetUnits + units - 1) / (units > 0 ? units : 1);
-    if (ns < 1) ns = 1;
-    split = (msl + ns - 1) / ns;
-    split = (split + 63) / 64 * 64;
-    if (split < kMinSplit) split = kMinSplit;
+    if (mfma) {
+      if (max_query_len > 1 && units >= 2048) {
+        split = msl;                        // prefill tiles already fill the machine
+      } else {
+        split = (long)((int64_t)msl * units / kTargetUnitsMfma);
+        if (split < kMinSplit) split = kMinSplit;
+      }
+    } else {
+      int64_t ns = (kTargetUnitsValu + units - 1) / (units > 0 ? units : 1);
+      if (ns < 1) ns = 1;
+      split = (msl + ns - 1) / ns;
+      if (split < kMinSplit) split = kMinSplit;
+    }
   }
-  if (split > msl) split = msl;
+  if (mfma) split = (split + 31) / 32 * 32;   // the MFMA kernel walks 32-token steps
+  if (split >= msl) split = mfma ? (msl + 31) / 32 * 32 : msl;
   p.split_tokens = (int)split;
   p.num_splits = (int)((msl + split - 1) / split);
   if (p.num_splits > 65535) return fail(KV4_EUNSUPPORTED, "too many KV splits (%d)", p.num_splits);
+  if (units * p.num_splits > INT32_MAX / 2) return fail(KV4_EUNSUPPORTED, "too many work units");
   return KV4_OK;
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t o_off, ml_off, total;
+  size_t prefix_off, o_off, ml_off, total;
 };
 
-WsLayout ws_layout(const kv4::AttnPlan& p, int64_t num_q_tokens, int32_t nq, int32_t hs) {
-  WsLayout w{0, 0, 0};
-  if (p.num_splits <= 1 || num_q_tokens == 0) return w;
-  const size_t rows = (size_t)p.num_splits * (size_t)num_q_tokens * (size_t)nq;
-  w.o_off = 0;
-  w.ml_off = align_up(rows * (size_t)hs * sizeof(float), 256);
-  w.total = align_up(w.ml_off + rows * 2 * sizeof(float), 256);
+WsLayout ws_layout(const kv4::AttnPlan& p, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t hs) {
+  WsLayout w{0, 0, 0, 0};
+  if (num_q_tokens == 0) return w;
+  size_t off = 0;
+  if (p.path == 1) {
+    w.prefix_off = 0;
+    off = align_up((size_t)(num_seqs + 1) * sizeof(int32_t), 256);
+  }
+  if (p.num_splits > 1) {
+    const size_t rows = (size_t)p.num_splits * (size_t)num_q_tokens * (size_t)nq;
+    w.o_off = off;
+    w.ml_off = align_up(off + rows * (size_t)hs * sizeof(float), 256);
+    off = align_up(w.ml_off + rows * 2 * sizeof(float), 256);
+  }
+  w.total = off;
   return w;
 }
 
@@ -193,10 +225,18 @@ size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs
   if (check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
                        max_seq_len))
     return 0;
-  kv4::AttnPlan p;
-  if (make_plan(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, max_query_len, max_seq_len, p)) return 0;
+  // block_size is not an argument here: size for the larger of the two paths
+  size_t need = 0;
+  for (int32_t bs : {16, 1}) {
+    kv4::AttnPlan p;
+    if (make_plan(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len, max_seq_len,
+                  bs, p))
+      return 0;
+    const size_t n = ws_layout(p, num_q_tokens, num_seqs, num_q_heads, head_size).total;
+    need = n > need ? n : need;
+  }
   g_last_error.clear();
-  return ws_layout(p, num_q_tokens, num_q_heads, head_size).total;
+  return need;
 }
 
 int kv4_paged_attention(const void* query, int64_t query_token_stride, const void* key_cache,
@@ -229,16 +269,22 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride, const voi
 
   kv4::AttnArgs a;
   std::memset(&a, 0, sizeof(a));
-  if (int e = make_plan(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, max_query_len, max_seq_len, a.plan))
+  if (num_blocks < 1) return fail(KV4_EINVAL, "num_blocks must be >= 1 when there are query tokens");
+  if (int e = make_plan(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
+                       max_seq_len, block_size, a.plan))
     return e;
-  const WsLayout ws = ws_layout(a.plan, num_q_tokens, num_q_heads, head_size);
+  const WsLayout ws = ws_layout(a.plan, num_q_tokens, num_seqs, num_q_heads, head_size);
+  int32_t* prefix = nullptr;
   if (ws.total > 0) {
     if (!workspace || workspace_bytes < ws.total)
       return fail(KV4_EWORKSPACE, "workspace of %zu bytes required, got %zu", ws.total,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(KV4_EINVAL, "workspace must be 16-byte aligned");
-    a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.o_off);
-    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_off);
+    if (a.plan.path == 1) prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ws.prefix_off);
+    if (a.plan.num_splits > 1) {
+      a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.o_off);
+      a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_off);
+    }
   }
   a.query = static_cast<const uint16_t*>(query);
   a.q_stride = query_token_stride;
@@ -264,7 +310,13 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride, const voi
   a.scale_log2 = softmax_scale / (float)b * 1.4426950408889634f;
   a.out = static_cast<uint16_t*>(out);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (int e = hip_status(kv4::launch_attn_valu(a, st), "kv4_paged_attention launch")) return e;
+  if (a.plan.path == 1) {
+    const int64_t max_units = a.plan.n_qtiles * a.plan.n_head_tiles * num_kv_heads * a.plan.num_splits;
+    if (int e = hip_status(kv4::launch_attn_mfma(a, prefix, max_units, st), "kv4_paged_attention launch"))
+      return e;
+  } else {
+    if (int e = hip_status(kv4::launch_attn_valu(a, st), "kv4_paged_attention launch")) return e;
+  }
   if (a.plan.num_splits > 1)
     return hip_status(kv4::launch_attn_reduce(a, st), "kv4_paged_attention merge launch");
   return ok();

@@ -1,0 +1,555 @@
+// Read path (unified_attention_int4) on the matrix cores: paged attention
+// over the int4 RHT cache where the query block is dense -- the query heads
+// of one GQA group and/or several query tokens of a prefill chunk share every
+// K/V element they read.
+//
+// Math per query row, as in the vector-ALU kernel (vLLM PR #62881 "[Bugfix]
+// [Test] Rotate KV into RHT domain in the INT4 unified attn test", Details /
+// Root cause; divisor b per runguoli.com "vLLM -- Attention Kernels & KV
+// Cache Quantization", section "PR #56198"): q' = H.D.q, logit_j = k_scale_j
+// (q' . code_j) softmax_scale / b, online softmax, o' = sum p_j v_scale_j
+// code_V_j, out = D.H.o'/b.
+//
+// gfx950 mapping. One wave = one work unit (sequence, query tile of up to 16
+// rows, kv head, KV split); a workgroup of 4 waves takes 4 consecutive units
+// (consecutive kv heads of the same pages when num_kv_heads >= 4, so their
+// 16-byte code rows share cache lines inside one CU). The KV range is walked
+// 32 tokens (two 16-token half tiles) per step:
+//   * S^T = K . Q'^T on v_mfma_f32_16x16x32_bf16: A = K codes (16 tokens x 32
+//     head elements), B = q' rows (bf16). The head dimension is permuted so
+//     that a lane's 16 / 12 / 8 ... code bytes of one token are one vector
+//     load and feed all k-steps; q' is permuted the same way.
+//   * q' and p * v_scale enter as bf16 hi + lo pairs (two MFMAs each), so
+//     the products carry ~16 significant bits: sharp softmax rows (large
+//     k_scale from outlier channels) stay within 1e-2 of the fp64 result.
+//   * Codes become bf16 operands exactly, two per VALU op: (u & 0xF) |
+//     0x4300 is the bf16 of 128 + u with u = code + 8 (nibble xor 8). The
+//     constant 136 is removed after the product with the sum of q' (QK) and
+//     with the sum of p*v_scale (PV, obtained from one extra MFMA against a
+//     ones operand, so it sees exactly the rounded operands).
+//   * The S^T accumulator leaves each lane with 8 logits of ONE query row,
+//     which is exactly the B-operand layout P^T needs for O'^T = V^T P^T, so
+//     softmax runs in registers with no transpose; the V^T operand is built
+//     from 8 tokens' code words per lane (byte permutes + masks).
+//   * k_scale / v_scale of the 32 tokens are loaded once per step (one lane
+//     per token) and redistributed through a 256-byte LDS slot per wave.
+// Pages are looked up once per 16-token half tile (block_size % 16 == 0).
+#include "kv4_device.hpp"
+#include "kv4_launch.hpp"
+
+namespace kv4 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 8 codes of one token (one 32-bit word) -> A operand of one k-step: bf16 of
+// 128 + u in k-order of element offsets [0, 4, 1, 5, 2, 6, 3, 7].
+__device__ __forceinline__ uint4 k_operand(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  uint4 r;
+  r.x = (x & 0x000F000Fu) | 0x43004300u;
+  r.y = ((x >> 4) & 0x000F000Fu) | 0x43004300u;
+  r.z = ((x >> 8) & 0x000F000Fu) | 0x43004300u;
+  r.w = ((x >> 12) & 0x000F000Fu) | 0x43004300u;
+  return r;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats as a bf16 pair hi (round to nearest even, v_cvt_pk_bf16_f32)
+// plus the bf16 pair of the remainders lo: hi + lo carries ~16 significant
+// bits, which keeps sharp softmax rows (large k_scale) accurate.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+  const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xFFFF0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a - ha, b - hb}, bf16x2_t));
+}
+
+// bytes jb of two words -> [a.jb, 0, b.jb, 0]
+__device__ __forceinline__ uint32_t pair_byte(uint32_t a, uint32_t b, int jb) {
+  const uint32_t sel = (uint32_t)jb | (0x0Cu << 8) | ((uint32_t)(4 + jb) << 16) | (0x0Cu << 24);
+  return __builtin_amdgcn_perm(b, a, sel);
+}
+
+template <int HS>
+struct Geo {
+  static constexpr int NK = HS / 32;            // QK k-steps; code words per lane per half tile
+  static constexpr int NS = HS / 16;            // PV n-steps
+  static constexpr int RDW = HS / 128;          // V column regions: 32-bit words (8 columns / lane)
+  static constexpr int RUS = (HS % 128) / 64;   //                   16-bit words (4 columns / lane)
+  static constexpr int RBY = (HS % 64) / 32;    //                   bytes        (2 columns / lane)
+  static constexpr int NVR = RDW + RUS + RBY;   // V words per token per lane
+};
+
+// V region r of head size HS: columns per lane (w), first column (cb).
+template <int HS>
+__device__ __forceinline__ void v_region(int r, int& w, int& cb) {
+  constexpr int RDW = Geo<HS>::RDW, RUS = Geo<HS>::RUS;
+  if (r < RDW) { w = 8; cb = 128 * r; }
+  else if (r < RDW + RUS) { w = 4; cb = 128 * RDW; }
+  else { w = 2; cb = 128 * RDW + 64 * RUS; }
+}
+
+template <int HS>
+__device__ __forceinline__ void load_k_words(const uint8_t* p, uint32_t (&w)[Geo<HS>::NK]) {
+  constexpr int NK = Geo<HS>::NK;
+  if constexpr (NK == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    w[0] = x.x; w[1] = x.y;
+  } else if constexpr (NK == 3) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    w[0] = q[0]; w[1] = q[1]; w[2] = q[2];
+  } else if constexpr (NK == 4) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+  } else if constexpr (NK == 8) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    const uint4 y = *reinterpret_cast<const uint4*>(p + 16);
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+    w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NK; i += 2) {
+      const uint2 x = *reinterpret_cast<const uint2*>(p + 4 * i);
+      w[i] = x.x; w[i + 1] = x.y;
+    }
+  }
+}
+
+// The code word(s) of V column chunk m of one token row.
+template <int HS>
+__device__ __forceinline__ void load_v_words(const uint8_t* row, int m, uint32_t (&w)[Geo<HS>::NVR]) {
+  constexpr int RDW = Geo<HS>::RDW, RUS = Geo<HS>::RUS, RBY = Geo<HS>::RBY;
+#pragma unroll
+  for (int r = 0; r < RDW; ++r) w[r] = *reinterpret_cast<const uint32_t*>(row + 64 * r + 4 * m);
+  if constexpr (RUS) w[RDW] = *reinterpret_cast<const uint16_t*>(row + 64 * RDW + 2 * m);
+  if constexpr (RBY) w[RDW + RUS] = row[64 * RDW + 32 * RUS + m];
+}
+
+struct Unit {
+  int s, i0, qbeg, qlen, L, g, ht, sp;
+};
+
+// Dense unit index -> (sequence, tile, head tile, kv head, split). prefix[s]
+// is the first unit of sequence s; unit order inside a sequence is kv head
+// fastest, then head tile, then split, then query tile.
+__device__ __forceinline__ bool decode_unit(const AttnArgs& a, const int32_t* prefix, int u, Unit& un) {
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo;
+  int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
+  qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
+  qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
+  int64_t L = a.seq_lens[s];
+  const int64_t cap = (int64_t)a.max_blocks * a.bs;
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const int split = a.plan.split_tokens;
+  int nsp = (int)((L + split - 1) / split);
+  nsp = nsp < 1 ? 1 : (nsp > a.plan.num_splits ? a.plan.num_splits : nsp);
+  int v = u - prefix[s];
+  un.g = v % a.nkv;
+  v /= a.nkv;
+  un.ht = v % a.plan.n_head_tiles;
+  v /= a.plan.n_head_tiles;
+  un.sp = v % nsp;
+  const int tile = v / nsp;
+  un.s = s;
+  un.qbeg = (int)qb;
+  un.qlen = (int)(qe - qb);
+  un.i0 = tile * a.plan.tq;
+  un.L = (int)L;
+  return un.i0 < un.qlen;
+}
+
+// Work units per sequence and their exclusive prefix (one workgroup).
+__global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* prefix) {
+  __shared__ int32_t wave_tot[16];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  const int split = a.plan.split_tokens;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 1024) {
+    const int s = c0 + tid;
+    int units = 0;
+    if (s < a.num_seqs) {
+      int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
+      qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
+      qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
+      int64_t L = a.seq_lens[s];
+      const int64_t cap = (int64_t)a.max_blocks * a.bs;
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+      int nsp = (int)((L + split - 1) / split);
+      nsp = nsp < 1 ? 1 : (nsp > a.plan.num_splits ? a.plan.num_splits : nsp);
+      const int ntile = (int)((qe - qb + a.plan.tq - 1) / a.plan.tq);
+      units = ntile * nsp * a.plan.n_head_tiles * a.nkv;
+    }
+    // inclusive scan inside the wave
+    int x = units;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wave_tot[wv] = x;
+    __syncthreads();
+    int before = carry;
+    for (int i = 0; i < wv; ++i) before += wave_tot[i];
+    if (s < a.num_seqs) prefix[s] = before + x - units;
+    __syncthreads();
+    if (tid == 1023) carry = before + x;
+    __syncthreads();
+  }
+  if (tid == 0) prefix[a.num_seqs] = carry;
+}
+
+template <int HS>
+struct MfmaSmem {
+  float buf[16 * HS];       // q' staging (bf16 pairs) and the output epilogue (fp32)
+  float qsum[16];
+  float scl[64];
+};
+
+template <int HS>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_t* prefix) {
+  using GG = Geo<HS>;
+  constexpr int NK = GG::NK, NS = GG::NS, NVR = GG::NVR;
+  constexpr int LP = (HS / 8) <= 8 ? 8 : ((HS / 8) <= 16 ? 16 : 32);   // lanes per row, chunk mapping
+  constexpr int RPP = kWave / LP;                                       // rows per pass
+  __shared__ MfmaSmem<HS> smem_all[4];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  MfmaSmem<HS>& sm = smem_all[wv];
+  const int n = lane & 15;          // MFMA column: query row of this lane
+  const int q4 = lane >> 4;         // 0..3
+  const int G = a.nq / a.nkv;
+  const int gh = a.plan.gh;
+  const int split = a.plan.split_tokens;
+  const int half_row = HS / 2;
+  const int total = prefix[a.num_seqs];
+  const int bsz = a.bs;
+  const float inv_b = 1.0f / (float)a.b;
+
+  // lane constants of the chunk mapping (q setup and epilogue)
+  const int cj = lane & (LP - 1);
+  const bool c_on = cj < HS / 8;
+  const uint32_t sbits = c_on ? sign_bits8(a.seed, cj) : 0u;
+  uint32_t sx[4];
+  sign_xor_bf16x8(sbits, sx);
+
+  for (int u0 = blockIdx.x * 4; u0 < total; u0 += gridDim.x * 4) {
+    const int u = u0 + wv;
+    Unit un;
+    if (u >= total || !decode_unit(a, prefix, u, un)) continue;
+    const int h0 = un.g * G + un.ht * gh;
+    const int nh = min(gh, G - un.ht * gh);
+    const int ntok = min(a.plan.tq, un.qlen - un.i0);
+    const int pos0 = un.L - un.qlen + un.i0;
+    const int kend = pos0 + ntok;
+    const int k0 = un.sp * split;
+    const int k1 = min(k0 + split, kend);
+    if (k0 >= k1 && un.sp > 0) continue;   // no keys for this tile in this split (merge skips it)
+
+    // ---- q' rows -> LDS (bf16, k-permuted) and their sums
+#pragma unroll
+    for (int ps = 0; ps < 16 / RPP; ++ps) {
+      const int r = ps * RPP + lane / LP;
+      const int ti = r / gh, hi = r - (r / gh) * gh;
+      const bool rv = ti < ntok && hi < nh;
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (rv && c_on)
+        w = *reinterpret_cast<const uint4*>(a.query + (int64_t)(un.qbeg + un.i0 + ti) * a.q_stride +
+                                           (int64_t)(h0 + hi) * HS + 8 * cj);
+      const uint32_t wd[4] = {w.x ^ sx[0], w.y ^ sx[1], w.z ^ sx[2], w.w ^ sx[3]};
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = bf16_lo(wd[k]);
+        v[2 * k + 1] = bf16_hi(wd[k]);
+      }
+      fwht_b(v, a.b, cj);
+      float sum = 0.0f;
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // k-order of element offsets [0, 4, 1, 5, 2, 6, 3, 7]
+        const float x0 = v[k] * a.scale_log2, x1 = v[k + 4] * a.scale_log2;
+        split_bf16x2(x0, x1, hw[k], lw[k]);
+        sum += (__uint_as_float(hw[k] << 16) + __uint_as_float(lw[k] << 16)) +
+               (__uint_as_float(hw[k] & 0xFFFF0000u) + __uint_as_float(lw[k] & 0xFFFF0000u));
+      }
+      sum = group_sum(c_on ? sum : 0.0f, LP);
+      if (c_on) {
+        reinterpret_cast<uint4*>(sm.buf)[(r * HS + 8 * cj) / 8] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        reinterpret_cast<uint4*>(sm.buf)[(16 * HS + r * HS + 8 * cj) / 8] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      }
+      if (cj == 0) sm.qsum[r] = sum;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    uint4 qb[NK], ql[NK];
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      qb[s] = reinterpret_cast<const uint4*>(sm.buf)[(n * HS + q4 * (HS / 4) + 8 * s) / 8];
+      ql[s] = reinterpret_cast<const uint4*>(sm.buf)[(16 * HS + n * HS + q4 * (HS / 4) + 8 * s) / 8];
+    }
+    const float qbias = 136.0f * sm.qsum[n];
+    const int ti_n = n / gh, hi_n = n - (n / gh) * gh;
+    const bool row_ok = ti_n < ntok && hi_n < nh;
+    const int rpos = row_ok ? pos0 + ti_n : -1;
+
+    f32x4_t acc[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t pacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    const int32_t* bt = a.block_table + (int64_t)un.s * a.max_blocks;
+    const int64_t nkv = a.nkv;
+
+    for (int base = k0; base < k1; base += 32) {
+      // pages of the two half tiles (wave-uniform)
+      int pa = bt[base / bsz];
+      const bool pa_ok = pa >= 0 && pa < a.num_blocks;
+      pa = pa_ok ? pa : 0;
+      int pb = pa;
+      bool pb_ok = pa_ok;
+      if (base + 16 < k1) {
+        pb = bt[(base + 16) / bsz];
+        pb_ok = pb >= 0 && pb < a.num_blocks;
+        pb = pb_ok ? pb : 0;
+      }
+      const int offa = base % bsz, offb = (base + 16) % bsz;
+      const int64_t rowa = ((int64_t)pa * bsz + offa) * nkv + un.g;
+      const int64_t rowb = ((int64_t)pb * bsz + offb) * nkv + un.g;
+
+      // K words: token n of each half tile, chunk q4
+      uint32_t kwa[NK], kwb[NK];
+      load_k_words<HS>(a.key_cache + (rowa + (int64_t)n * nkv) * half_row + q4 * (HS / 8), kwa);
+      load_k_words<HS>(a.key_cache + (rowb + (int64_t)n * nkv) * half_row + q4 * (HS / 8), kwb);
+      // V words: tokens 4*q4 + i of each half tile, column chunk n
+      uint32_t vw[8][NVR];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        load_v_words<HS>(a.value_cache + (rowa + (int64_t)(4 * q4 + i) * nkv) * half_row, n, vw[i]);
+        load_v_words<HS>(a.value_cache + (rowb + (int64_t)(4 * q4 + i) * nkv) * half_row, n, vw[4 + i]);
+      }
+      // scales: lane t < 32 -> k_scale of token t, lane t >= 32 -> v_scale of token t - 32
+      {
+        const int t = lane & 31;
+        const int64_t row = (t < 16 ? rowa + (int64_t)t * nkv : rowb + (int64_t)(t - 16) * nkv);
+        sm.scl[lane] = lane < 32 ? a.k_scale[row] : a.v_scale[row];
+      }
+
+      // S^T for both half tiles
+      f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        const uint4 ka = k_operand(kwa[s]), kb = k_operand(kwb[s]);
+        sa = mfma_bf16(ka, qb[s], sa);
+        sb = mfma_bf16(kb, qb[s], sb);
+        sa = mfma_bf16(ka, ql[s], sa);
+        sb = mfma_bf16(kb, ql[s], sb);
+      }
+      __builtin_amdgcn_wave_barrier();
+      const float4 ksa = *reinterpret_cast<const float4*>(&sm.scl[4 * q4]);
+      const float4 ksb = *reinterpret_cast<const float4*>(&sm.scl[16 + 4 * q4]);
+      const float4 vsa = *reinterpret_cast<const float4*>(&sm.scl[32 + 4 * q4]);
+      const float4 vsb = *reinterpret_cast<const float4*>(&sm.scl[48 + 4 * q4]);
+      const float ks8[8] = {ksa.x, ksa.y, ksa.z, ksa.w, ksb.x, ksb.y, ksb.z, ksb.w};
+      const float vs8[8] = {vsa.x, vsa.y, vsa.z, vsa.w, vsb.x, vsb.y, vsb.z, vsb.w};
+      const float s8[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+      float lg[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int tok = base + (i < 4 ? 4 * q4 + i : 16 + 4 * q4 + (i - 4));
+        const bool ok = tok < k1 && tok <= rpos && (i < 4 ? pa_ok : pb_ok);
+        lg[i] = ok ? (s8[i] - qbias) * ks8[i] : -INFINITY;
+        mx = fmaxf(mx, lg[i]);
+      }
+      mx = fmaxf(mx, xor_lane<16>(mx));
+      mx = fmaxf(mx, xor_lane<32>(mx));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      // a row that has seen no key yet has nothing to rescale
+      const float alpha = m_run == -INFINITY ? 1.0f : fast_exp2(m_run - m_use);
+      float psum_l = 0.0f;
+      uint32_t pw[4], pl[4];
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const float p0 = fast_exp2(lg[i] - m_use), p1 = fast_exp2(lg[i + 1] - m_use);
+        psum_l += p0 + p1;
+        split_bf16x2(p0 * vs8[i], p1 * vs8[i + 1], pw[i / 2], pl[i / 2]);
+      }
+      const uint4 pb4 = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      const uint4 pl4 = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) acc[i] *= alpha;
+        pacc *= alpha;
+      }
+      l_run = l_run * alpha + psum_l;
+      m_run = m_new;
+
+      // O'^T += V^T P^T, one n-step per V column of this lane's chunks
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < NVR; ++r) vw[i][r] ^= 0x88888888u;
+      int ns = 0;
+#pragma unroll
+      for (int r = 0; r < NVR; ++r) {
+        int w, cb;
+        v_region<HS>(r, w, cb);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          if (2 * jb >= w) break;
+          const uint32_t t01 = pair_byte(vw[0][r], vw[1][r], jb);
+          const uint32_t t23 = pair_byte(vw[2][r], vw[3][r], jb);
+          const uint32_t t45 = pair_byte(vw[4][r], vw[5][r], jb);
+          const uint32_t t67 = pair_byte(vw[6][r], vw[7][r], jb);
+          uint4 lo, hi;
+          lo.x = (t01 & 0x000F000Fu) | 0x43004300u;
+          lo.y = (t23 & 0x000F000Fu) | 0x43004300u;
+          lo.z = (t45 & 0x000F000Fu) | 0x43004300u;
+          lo.w = (t67 & 0x000F000Fu) | 0x43004300u;
+          hi.x = ((t01 >> 4) & 0x000F000Fu) | 0x43004300u;
+          hi.y = ((t23 >> 4) & 0x000F000Fu) | 0x43004300u;
+          hi.z = ((t45 >> 4) & 0x000F000Fu) | 0x43004300u;
+          hi.w = ((t67 >> 4) & 0x000F000Fu) | 0x43004300u;
+          acc[ns] = mfma_bf16(lo, pb4, acc[ns]);
+          acc[ns + 1] = mfma_bf16(hi, pb4, acc[ns + 1]);
+          acc[ns] = mfma_bf16(lo, pl4, acc[ns]);
+          acc[ns + 1] = mfma_bf16(hi, pl4, acc[ns + 1]);
+          ns += 2;
+        }
+      }
+      const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+      pacc = mfma_bf16(ones, pb4, pacc);
+      pacc = mfma_bf16(ones, pl4, pacc);
+    }
+
+    // ---- finish: l over the four lane quarters, remove the +136 offset
+    l_run += xor_lane<16>(l_run);
+    l_run += xor_lane<32>(l_run);
+    const float pbias = 136.0f * pacc[0];
+    const int qrow = un.qbeg + un.i0 + ti_n;
+    const int h = h0 + hi_n;
+    if (a.plan.num_splits > 1) {
+      if (row_ok) {
+        const int64_t prow = ((int64_t)un.sp * a.num_q_tokens + qrow) * a.nq + h;
+        float* dst = a.ws_o + prow * HS;
+        int ns = 0;
+#pragma unroll
+        for (int r = 0; r < NVR; ++r) {
+          int w, cb;
+          v_region<HS>(r, w, cb);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int c0 = cb + w * (4 * q4 + rr);
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+              if (t < w) dst[c0 + t] = acc[ns + t][rr] - pbias;
+          }
+          ns += w;
+        }
+        if (q4 == 0) {
+          a.ws_ml[2 * prow] = m_run;
+          a.ws_ml[2 * prow + 1] = l_run;
+        }
+      }
+      continue;
+    }
+    // single split: normalize, stage the row in LDS, inverse rotation, store
+    const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    __builtin_amdgcn_wave_barrier();
+    {
+      int ns = 0;
+#pragma unroll
+      for (int r = 0; r < NVR; ++r) {
+        int w, cb;
+        v_region<HS>(r, w, cb);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int c0 = cb + w * (4 * q4 + rr);
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (t < w) sm.buf[n * HS + c0 + t] = (acc[ns + t][rr] - pbias) * inv_l;
+        }
+        ns += w;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int ps = 0; ps < 16 / RPP; ++ps) {
+      const int r = ps * RPP + lane / LP;
+      const int ti = r / gh, hi = r - (r / gh) * gh;
+      const bool rv = ti < ntok && hi < nh;
+      float o[8];
+      if (c_on) {
+        const float4 x0 = reinterpret_cast<const float4*>(sm.buf)[(r * HS + 8 * cj) / 4];
+        const float4 x1 = reinterpret_cast<const float4*>(sm.buf)[(r * HS + 8 * cj) / 4 + 1];
+        o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
+        o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+      }
+      fwht_b(o, a.b, cj);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = apply_sign(o[e] * inv_b, sbits, e);
+      if (rv && c_on) {
+        uint4 wo;
+        wo.x = pack_bf16x2(o[0], o[1]);
+        wo.y = pack_bf16x2(o[2], o[3]);
+        wo.z = pack_bf16x2(o[4], o[5]);
+        wo.w = pack_bf16x2(o[6], o[7]);
+        *reinterpret_cast<uint4*>(a.out + ((int64_t)(un.qbeg + un.i0 + ti) * a.nq + h0 + hi) * HS + 8 * cj) = wo;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+static int g_num_cus = 0;
+
+hipError_t launch_attn_mfma(const AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a, prefix);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (g_num_cus == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      g_num_cus = cus;
+    else
+      g_num_cus = 256;
+  }
+  int64_t wgs = (max_units + 3) / 4;
+  const int64_t cap = (int64_t)g_num_cus * 8;
+  if (wgs > cap) wgs = cap;
+  if (wgs < 1) wgs = 1;
+  dim3 grid((unsigned)wgs), block(256);
+  switch (a.hs) {
+    case 64: hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, block, 0, stream, a, prefix); break;
+    case 96: hipLaunchKernelGGL(attn_mfma_kernel<96>, grid, block, 0, stream, a, prefix); break;
+    case 128: hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, block, 0, stream, a, prefix); break;
+    case 192: hipLaunchKernelGGL(attn_mfma_kernel<192>, grid, block, 0, stream, a, prefix); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kv4

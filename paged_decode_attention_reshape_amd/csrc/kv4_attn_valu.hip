@@ -88,8 +88,6 @@ __device__ __forceinline__ void codes_to_u(uint32_t w, float (&u)[8]) {
   u[7] = (float)(hi >> 24);
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // Inverse rotation and store of one output row chunk: o = D.H.o'/b, bf16.
 __device__ __forceinline__ void store_out_row(float (&o)[8], int b, int jj, uint32_t sbits,
                                               float inv_b, uint16_t* dst, bool do_store) {

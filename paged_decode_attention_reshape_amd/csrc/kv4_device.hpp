@@ -152,6 +152,9 @@ __device__ __forceinline__ float group_sum(float v, int width) {
   return v;
 }
 
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ int next_pow2(int x) {
   int p = 1;
   while (p < x) p <<= 1;

@@ -95,5 +95,8 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream);
+// Device plan (work units per sequence, exclusive prefix into `prefix`,
+// num_seqs + 1 ints) followed by the matrix-core attention kernel.
+hipError_t launch_attn_mfma(const AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream);
 
 }  // namespace kv4

@@ -77,8 +77,14 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", ["auto", "valu", "mfma"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_attention_parity(case):
+def test_attention_parity(case, path, monkeypatch):
+    """Every case on the planner's choice and on each path forced (the matrix
+    core path only runs where its head size / page size allow; elsewhere the
+    forced run falls back to the vector path)."""
+    if path != "auto":
+        monkeypatch.setenv("KV4_FORCE_PATH", path)
     name, nq, nkv, hs, ql, sl, bs = case
     w = W.custom(name, nq, nkv, hs, ql, sl, block_size=bs)
     r = run_gpu(w)
@@ -87,11 +93,13 @@ def test_attention_parity(case):
     _g3(r, got)
 
 
+@pytest.mark.parametrize("path", ["valu", "mfma"])
 @pytest.mark.parametrize("split", ["64", "100", "1000"])
-def test_attention_forced_splits_match(split, monkeypatch):
+def test_attention_forced_splits_match(split, path, monkeypatch):
     """The split-KV launch (partials + log-sum-exp merge) against the oracle,
     with small forced split sizes that give many splits and ragged tails."""
     monkeypatch.setenv("KV4_SPLIT_TOKENS", split)
+    monkeypatch.setenv("KV4_FORCE_PATH", path)
     w = W.custom("split", 8, 2, 96, [1, 1, 7, 1], [1500, 63, 700, 1], block_size=16)
     r = run_gpu(w)
     _g2(r)
