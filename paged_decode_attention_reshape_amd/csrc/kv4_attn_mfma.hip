@@ -212,31 +212,97 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* pr
   if (tid == 0) prefix[a.num_seqs] = carry;
 }
 
+// LDS layout of one 32-token step (per wave), filled by direct global->LDS
+// loads. A load of `size` bytes puts lane l's bytes at region + l * stride
+// with stride = 4 for 1-, 2- and 4-byte loads (sub-dword data zero-extended),
+// 16 for 12- and 16-byte loads.
+//   K  half h, load j : token (l & 15) of the half tile, code bytes of chunk
+//                       l >> 4, words [j * KSZ/4, (j + 1) * KSZ/4)
+//   V  token i, region r: token 4 * (l >> 4) + (i & 3) of half tile i >> 2,
+//                       column chunk (l & 15) of region r (one dword slot)
+//   S  lane l: k_scale (l < 32) / v_scale (l >= 32) of token (l & 15) of half
+//                       tile (l >> 4) & 1
+template <int HS>
+struct StageGeo {
+  static constexpr int NK = HS / 32;
+  static constexpr int NKL = NK == 2 ? 2 : (NK == 3 ? 1 : (NK == 4 ? 1 : 2));    // K loads per half
+  static constexpr int KSZ = NK == 2 ? 4 : (NK == 4 || NK == 8 ? 16 : 12);       // bytes per load
+  static constexpr int KSTR = KSZ == 4 ? 4 : 16;                                  // LDS bytes per lane
+  static constexpr int KREG = 64 * KSTR;                                          // one K load region
+  static constexpr int KHALF = NKL * KREG;                                        // K bytes per half tile
+  static constexpr int VBYTES_TOK = 256 * Geo<HS>::NVR;
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 2 * KHALF;
+  static constexpr int S_OFF = V_OFF + 8 * VBYTES_TOK;
+  static constexpr int BYTES = S_OFF + 256;
+  static constexpr int LOADS = 2 * NKL + 8 * Geo<HS>::NVR + 1;   // VMEM instructions per step
+};
+
+constexpr int kStages = 3;
+
 template <int HS>
 struct MfmaSmem {
-  float buf[16 * HS];       // q' staging (bf16 pairs) and the output epilogue (fp32)
+  static constexpr int STAGE = StageGeo<HS>::BYTES;
+  static constexpr int BUFB = 16 * HS * 4;                 // q' staging / epilogue (fp32 rows)
+  static constexpr int MAINB = kStages * STAGE > BUFB ? kStages * STAGE : BUFB;
+  alignas(16) unsigned char main[MAINB];                   // stages overlay the q / epilogue buffer
   float qsum[16];
-  float scl[64];
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma(const void* g, void* l, int size) {
+  switch (size) {
+    case 1: __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 1, 0, 0); break;
+    case 2: __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 2, 0, 0); break;
+    case 4: __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 4, 0, 0); break;
+    case 12: __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 12, 0, 0); break;
+    default: __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0); break;
+  }
+}
+
+// Buffer-resource variant: uniform base in SGPRs, 32-bit per-lane offset;
+// reads past num_records return 0 (never fault).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+template <int SIZE>
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* l) {
+  if constexpr (SIZE == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 1, voff, 0, 0, 0);
+  else if constexpr (SIZE == 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 2, voff, 0, 0, 0);
+  else if constexpr (SIZE == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 4, voff, 0, 0, 0);
+  else if constexpr (SIZE == 12) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 12, voff, 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 template <int HS>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_t* prefix) {
   using GG = Geo<HS>;
+  using SG = StageGeo<HS>;
   constexpr int NK = GG::NK, NS = GG::NS, NVR = GG::NVR;
   constexpr int LP = (HS / 8) <= 8 ? 8 : ((HS / 8) <= 16 ? 16 : 32);   // lanes per row, chunk mapping
   constexpr int RPP = kWave / LP;                                       // rows per pass
+  constexpr int HALF = HS / 2;
   __shared__ MfmaSmem<HS> smem_all[4];
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   MfmaSmem<HS>& sm = smem_all[wv];
+  float* buf = reinterpret_cast<float*>(sm.main);
   const int n = lane & 15;          // MFMA column: query row of this lane
   const int q4 = lane >> 4;         // 0..3
-  const int G = a.nq / a.nkv;
+  const int nkv = a.nkv;
+  const int G = a.nq / nkv;
   const int gh = a.plan.gh;
   const int split = a.plan.split_tokens;
-  const int half_row = HS / 2;
-  const int total = prefix[a.num_seqs];
+  const int total = uniform(prefix[a.num_seqs]);
   const int bsz = a.bs;
   const float inv_b = 1.0f / (float)a.b;
 
@@ -247,20 +313,36 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
   uint32_t sx[4];
   sign_xor_bf16x8(sbits, sx);
 
+  // lane byte offsets inside one half tile (relative to its first token row)
+  const uint32_t tok_stride = (uint32_t)nkv * HALF;         // bytes between token rows of a page
+  const uint32_t half_bytes = 16u * tok_stride;             // one half tile of a page
+  const uint32_t koff = (uint32_t)n * tok_stride + (uint32_t)q4 * (HS / 8);
+  uint32_t vo[4];                                           // token 4*q4 + i, 32-bit column chunk n
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vo[i] = (uint32_t)(4 * q4 + i) * tok_stride + 4u * (uint32_t)n;
+  const uint32_t soff = (uint32_t)(lane & 15) * (uint32_t)nkv;   // scale elements
+  const float* sc_base = lane < 32 ? a.k_scale : a.v_scale;
+  const bool sc_half_b = (lane & 16) != 0;
+
   for (int u0 = blockIdx.x * 4; u0 < total; u0 += gridDim.x * 4) {
     const int u = u0 + wv;
+    if (u >= total) continue;
     Unit un;
-    if (u >= total || !decode_unit(a, prefix, u, un)) continue;
-    const int h0 = un.g * G + un.ht * gh;
-    const int nh = min(gh, G - un.ht * gh);
-    const int ntok = min(a.plan.tq, un.qlen - un.i0);
-    const int pos0 = un.L - un.qlen + un.i0;
+    if (!decode_unit(a, prefix, u, un)) continue;
+    // the unit is the same for every lane of the wave
+    const int us = uniform(un.s), ui0 = uniform(un.i0), uqbeg = uniform(un.qbeg);
+    const int uqlen = uniform(un.qlen), uL = uniform(un.L), ug = uniform(un.g);
+    const int uht = uniform(un.ht), usp = uniform(un.sp);
+    const int h0 = ug * G + uht * gh;
+    const int nh = min(gh, G - uht * gh);
+    const int ntok = min(a.plan.tq, uqlen - ui0);
+    const int pos0 = uL - uqlen + ui0;
     const int kend = pos0 + ntok;
-    const int k0 = un.sp * split;
+    const int k0 = usp * split;
     const int k1 = min(k0 + split, kend);
-    if (k0 >= k1 && un.sp > 0) continue;   // no keys for this tile in this split (merge skips it)
+    if (k0 >= k1 && usp > 0) continue;   // no keys for this tile in this split (the merge skips it)
 
-    // ---- q' rows -> LDS (bf16, k-permuted) and their sums
+    // ---- q' rows -> LDS (bf16 hi / lo, k-permuted) and their sums
 #pragma unroll
     for (int ps = 0; ps < 16 / RPP; ++ps) {
       const int r = ps * RPP + lane / LP;
@@ -268,7 +350,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
       const bool rv = ti < ntok && hi < nh;
       uint4 w = make_uint4(0u, 0u, 0u, 0u);
       if (rv && c_on)
-        w = *reinterpret_cast<const uint4*>(a.query + (int64_t)(un.qbeg + un.i0 + ti) * a.q_stride +
+        w = *reinterpret_cast<const uint4*>(a.query + (int64_t)(uqbeg + ui0 + ti) * a.q_stride +
                                            (int64_t)(h0 + hi) * HS + 8 * cj);
       const uint32_t wd[4] = {w.x ^ sx[0], w.y ^ sx[1], w.z ^ sx[2], w.w ^ sx[3]};
       float v[8];
@@ -277,36 +359,38 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
         v[2 * k] = bf16_lo(wd[k]);
         v[2 * k + 1] = bf16_hi(wd[k]);
       }
-      fwht_b(v, a.b, cj);
+      fwht_b_ct<LP>(v, a.b, cj);
       float sum = 0.0f;
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         // k-order of element offsets [0, 4, 1, 5, 2, 6, 3, 7]
-        const float x0 = v[k] * a.scale_log2, x1 = v[k + 4] * a.scale_log2;
-        split_bf16x2(x0, x1, hw[k], lw[k]);
+        split_bf16x2(v[k] * a.scale_log2, v[k + 4] * a.scale_log2, hw[k], lw[k]);
         sum += (__uint_as_float(hw[k] << 16) + __uint_as_float(lw[k] << 16)) +
                (__uint_as_float(hw[k] & 0xFFFF0000u) + __uint_as_float(lw[k] & 0xFFFF0000u));
       }
-      sum = group_sum(c_on ? sum : 0.0f, LP);
+      sum = group_sum_ct<LP>(c_on ? sum : 0.0f);
       if (c_on) {
-        reinterpret_cast<uint4*>(sm.buf)[(r * HS + 8 * cj) / 8] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        reinterpret_cast<uint4*>(sm.buf)[(16 * HS + r * HS + 8 * cj) / 8] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        reinterpret_cast<uint4*>(buf)[(r * HS + 8 * cj) / 8] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        reinterpret_cast<uint4*>(buf)[(16 * HS + r * HS + 8 * cj) / 8] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
       if (cj == 0) sm.qsum[r] = sum;
     }
-    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
-    uint4 qb[NK], ql[NK];
+    uint4 qh[NK], ql[NK];
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
-      qb[s] = reinterpret_cast<const uint4*>(sm.buf)[(n * HS + q4 * (HS / 4) + 8 * s) / 8];
-      ql[s] = reinterpret_cast<const uint4*>(sm.buf)[(16 * HS + n * HS + q4 * (HS / 4) + 8 * s) / 8];
+      qh[s] = reinterpret_cast<const uint4*>(buf)[(n * HS + q4 * (HS / 4) + 8 * s) / 8];
+      ql[s] = reinterpret_cast<const uint4*>(buf)[(16 * HS + n * HS + q4 * (HS / 4) + 8 * s) / 8];
     }
     const float qbias = 136.0f * sm.qsum[n];
     const int ti_n = n / gh, hi_n = n - (n / gh) * gh;
     const bool row_ok = ti_n < ntok && hi_n < nh;
     const int rpos = row_ok ? pos0 + ti_n : -1;
+    const float row_add = row_ok ? 0.0f : -INFINITY;    // invalid rows never get weight
+    // the staged q' has been read into registers before the stages overwrite it
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
 
     f32x4_t acc[NS];
 #pragma unroll
@@ -314,70 +398,142 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
     f32x4_t pacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    const int32_t* bt = a.block_table + (int64_t)un.s * a.max_blocks;
-    const int64_t nkv = a.nkv;
-
-    for (int base = k0; base < k1; base += 32) {
-      // pages of the two half tiles (wave-uniform)
-      int pa = bt[base / bsz];
-      const bool pa_ok = pa >= 0 && pa < a.num_blocks;
-      pa = pa_ok ? pa : 0;
-      int pb = pa;
-      bool pb_ok = pa_ok;
-      if (base + 16 < k1) {
-        pb = bt[(base + 16) / bsz];
-        pb_ok = pb >= 0 && pb < a.num_blocks;
-        pb = pb_ok ? pb : 0;
+    // page ids of this unit, one per lane, 64 pages at a time
+    const int32_t* bt = a.block_table + (int64_t)us * a.max_blocks;
+    const int npages = k1 > 0 ? (k1 - 1) / bsz + 1 : 0;
+    int pg0 = k0 / bsz;
+    int pg_lane = -1;
+    auto load_pages = [&](int first) {
+      pg0 = first;
+      const int idx = first + lane;
+      int p = -1;
+      if (idx < npages) {
+        p = bt[idx];
+        p = (p >= 0 && p < a.num_blocks) ? p : -1;
       }
-      const int offa = base % bsz, offb = (base + 16) % bsz;
-      const int64_t rowa = ((int64_t)pa * bsz + offa) * nkv + un.g;
-      const int64_t rowb = ((int64_t)pb * bsz + offb) * nkv + un.g;
+      pg_lane = p;
+    };
+    const int nsteps = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
+    if (nsteps > 0) load_pages(pg0);
+    int okmask = 0;   // bit 2*slot: half A page valid, bit 2*slot+1: half B (wave-uniform)
 
-      // K words: token n of each half tile, chunk q4
-      uint32_t kwa[NK], kwb[NK];
-      load_k_words<HS>(a.key_cache + (rowa + (int64_t)n * nkv) * half_row + q4 * (HS / 8), kwa);
-      load_k_words<HS>(a.key_cache + (rowb + (int64_t)n * nkv) * half_row + q4 * (HS / 8), kwb);
-      // V words: tokens 4*q4 + i of each half tile, column chunk n
-      uint32_t vw[8][NVR];
+    // issue the loads of step `it` into stage slot `it % kStages`; steps past
+    // the end reload the first step's rows (in bounds, never read)
+    auto issue = [&](unsigned char* __restrict__ st, int it) {
+      const int slot = it % kStages;
+      const int base = k0 + 32 * (it < nsteps ? it : 0);
+      const int b_in = base + 16 < k1;
+      int ia = base / bsz - pg0;
+      int ib = (b_in ? (base + 16) / bsz : base / bsz) - pg0;
+      if (ia < 0 || ib >= 64) {             // another chunk of the page table (rare)
+        wait_vm<0>();
+        load_pages(base / bsz);
+        ia = 0;
+        ib = (b_in ? (base + 16) / bsz : base / bsz) - pg0;
+      }
+      int pa = __builtin_amdgcn_readlane(pg_lane, ia);
+      int pb = __builtin_amdgcn_readlane(pg_lane, ib);
+      const int oka = pa >= 0, okb = pb >= 0 && b_in;
+      okmask = (okmask & ~(3 << (2 * slot))) | ((oka | (okb << 1)) << (2 * slot));
+      pa = pa < 0 ? 0 : pa;
+      pb = pb < 0 ? 0 : pb;
+      const int offa = base % bsz;
+      const int offb = b_in ? (base + 16) % bsz : offa;
+      const int64_t rowa = ((int64_t)pa * bsz + offa) * nkv + ug;
+      const int64_t rowb = ((int64_t)pb * bsz + offb) * nkv + ug;
+      const __amdgpu_buffer_rsrc_t rk[2] = {rsrc(a.key_cache + rowa * HALF, half_bytes),
+                                            rsrc(a.key_cache + rowb * HALF, half_bytes)};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        load_v_words<HS>(a.value_cache + (rowa + (int64_t)(4 * q4 + i) * nkv) * half_row, n, vw[i]);
-        load_v_words<HS>(a.value_cache + (rowb + (int64_t)(4 * q4 + i) * nkv) * half_row, n, vw[4 + i]);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < SG::NKL; ++j) {
+          unsigned char* dst = st + SG::K_OFF + h * SG::KHALF + j * SG::KREG;
+          if constexpr (SG::KSZ == 16) dma_buf<16>(rk[h], koff + j * SG::KSZ, dst);
+          else if constexpr (SG::KSZ == 12) dma_buf<12>(rk[h], koff + j * SG::KSZ, dst);
+          else dma_buf<4>(rk[h], koff + j * SG::KSZ, dst);
+        }
+      const __amdgpu_buffer_rsrc_t rv[2] = {rsrc(a.value_cache + rowa * HALF, half_bytes),
+                                            rsrc(a.value_cache + rowb * HALF, half_bytes)};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        unsigned char* dst = st + SG::V_OFF + i * SG::VBYTES_TOK;
+        const uint32_t o = vo[i & 3];
+#pragma unroll
+        for (int r = 0; r < GG::RDW; ++r) dma_buf<4>(rv[i >> 2], o + 64 * r, dst + r * 256);
+        if constexpr (GG::RUS) dma_buf<2>(rv[i >> 2], o - 2u * n + 64 * GG::RDW, dst + GG::RDW * 256);
+        if constexpr (GG::RBY)
+          dma_buf<1>(rv[i >> 2], o - 3u * n + 64 * GG::RDW + 32 * GG::RUS, dst + (GG::RDW + GG::RUS) * 256);
       }
-      // scales: lane t < 32 -> k_scale of token t, lane t >= 32 -> v_scale of token t - 32
-      {
-        const int t = lane & 31;
-        const int64_t row = (t < 16 ? rowa + (int64_t)t * nkv : rowb + (int64_t)(t - 16) * nkv);
-        sm.scl[lane] = lane < 32 ? a.k_scale[row] : a.v_scale[row];
-      }
+      dma(sc_base + (sc_half_b ? rowb : rowa) + soff, st + SG::S_OFF, 4);
+    };
 
-      // S^T for both half tiles
+    if (nsteps > 0) {
+      issue(sm.main, 0);
+      issue(sm.main + SG::BYTES, 1);
+    }
+    // `st` (read) and `wr` (filled for step it + 2) are distinct stage slots;
+    // the restrict qualifiers let the compiler keep the lookahead loads in
+    // flight across the reads of the current step.
+    auto step = [&](const unsigned char* __restrict__ st, unsigned char* __restrict__ wr, int it) {
+      const int slot = it % kStages;
+      const int base = k0 + 32 * it;
+      wait_vm<SG::LOADS>();                  // step `it` landed; step `it + 1` may be in flight
+      __builtin_amdgcn_sched_barrier(0);
+      const bool oka = (okmask >> (2 * slot)) & 1, okb = (okmask >> (2 * slot + 1)) & 1;
+
+      // K code words of this lane: token n, chunk q4, both half tiles
+      uint32_t kw[2][NK];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned char* kr = st + SG::K_OFF + h * SG::KHALF;
+        if constexpr (NK == 4) {
+          const uint4 x = *reinterpret_cast<const uint4*>(kr + 16 * lane);
+          kw[h][0] = x.x; kw[h][1] = x.y; kw[h][2] = x.z; kw[h][3] = x.w;
+        } else if constexpr (NK == 3 || NK == 6) {
+#pragma unroll
+          for (int j = 0; j < NK / 3; ++j) {
+            const uint32_t* x = reinterpret_cast<const uint32_t*>(kr + j * SG::KREG + 16 * lane);
+            kw[h][3 * j] = x[0]; kw[h][3 * j + 1] = x[1]; kw[h][3 * j + 2] = x[2];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NK; ++j) kw[h][j] = reinterpret_cast<const uint32_t*>(kr + j * 256)[lane];
+        }
+      }
+      // S^T for both half tiles (q' as hi + lo)
       f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
-        const uint4 ka = k_operand(kwa[s]), kb = k_operand(kwb[s]);
-        sa = mfma_bf16(ka, qb[s], sa);
-        sb = mfma_bf16(kb, qb[s], sb);
+        const uint4 ka = k_operand(kw[0][s]), kb = k_operand(kw[1][s]);
+        sa = mfma_bf16(ka, qh[s], sa);
+        sb = mfma_bf16(kb, qh[s], sb);
         sa = mfma_bf16(ka, ql[s], sa);
         sb = mfma_bf16(kb, ql[s], sb);
+        __builtin_amdgcn_sched_barrier(0);   // keep one k-step's operands live at a time
       }
-      __builtin_amdgcn_wave_barrier();
-      const float4 ksa = *reinterpret_cast<const float4*>(&sm.scl[4 * q4]);
-      const float4 ksb = *reinterpret_cast<const float4*>(&sm.scl[16 + 4 * q4]);
-      const float4 vsa = *reinterpret_cast<const float4*>(&sm.scl[32 + 4 * q4]);
-      const float4 vsb = *reinterpret_cast<const float4*>(&sm.scl[48 + 4 * q4]);
+      const float* scl = reinterpret_cast<const float*>(st + SG::S_OFF);
+      const float4 ksa = *reinterpret_cast<const float4*>(&scl[4 * q4]);
+      const float4 ksb = *reinterpret_cast<const float4*>(&scl[16 + 4 * q4]);
+      const float4 vsa = *reinterpret_cast<const float4*>(&scl[32 + 4 * q4]);
+      const float4 vsb = *reinterpret_cast<const float4*>(&scl[48 + 4 * q4]);
       const float ks8[8] = {ksa.x, ksa.y, ksa.z, ksa.w, ksb.x, ksb.y, ksb.z, ksb.w};
       const float vs8[8] = {vsa.x, vsa.y, vsa.z, vsa.w, vsb.x, vsb.y, vsb.z, vsb.w};
       const float s8[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
       float lg[8];
-      float mx = -INFINITY;
+      const bool full = base + 32 <= k1 && base + 31 <= pos0 && oka && okb;   // wave-uniform
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = base + (i < 4 ? 4 * q4 + i : 16 + 4 * q4 + (i - 4));
-        const bool ok = tok < k1 && tok <= rpos && (i < 4 ? pa_ok : pb_ok);
-        lg[i] = ok ? (s8[i] - qbias) * ks8[i] : -INFINITY;
-        mx = fmaxf(mx, lg[i]);
+        for (int i = 0; i < 8; ++i) lg[i] = fmaf(s8[i] - qbias, ks8[i], row_add);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int tok = base + (i < 4 ? 4 * q4 + i : 16 + 4 * q4 + (i - 4));
+          const bool ok = tok < k1 && tok <= rpos && (i < 4 ? oka : okb);
+          lg[i] = ok ? (s8[i] - qbias) * ks8[i] : -INFINITY;
+        }
       }
+      float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),
+                       fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
       mx = fmaxf(mx, xor_lane<16>(mx));
       mx = fmaxf(mx, xor_lane<32>(mx));
       const float m_new = fmaxf(m_run, mx);
@@ -392,7 +548,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
         psum_l += p0 + p1;
         split_bf16x2(p0 * vs8[i], p1 * vs8[i + 1], pw[i / 2], pl[i / 2]);
       }
-      const uint4 pb4 = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      const uint4 ph4 = make_uint4(pw[0], pw[1], pw[2], pw[3]);
       const uint4 pl4 = make_uint4(pl[0], pl[1], pl[2], pl[3]);
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
@@ -403,22 +559,26 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
       m_run = m_new;
 
       // O'^T += V^T P^T, one n-step per V column of this lane's chunks
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int r = 0; r < NVR; ++r) vw[i][r] ^= 0x88888888u;
       int ns = 0;
 #pragma unroll
       for (int r = 0; r < NVR; ++r) {
         int w, cb;
         v_region<HS>(r, w, cb);
+        uint32_t x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const unsigned char* src = st + SG::V_OFF + i * SG::VBYTES_TOK;
+          // sub-dword regions hold zero-extended words; their unused
+          // nibbles are never selected below
+          x[i] = reinterpret_cast<const uint32_t*>(src + r * 256)[lane] ^ 0x88888888u;
+        }
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
           if (2 * jb >= w) break;
-          const uint32_t t01 = pair_byte(vw[0][r], vw[1][r], jb);
-          const uint32_t t23 = pair_byte(vw[2][r], vw[3][r], jb);
-          const uint32_t t45 = pair_byte(vw[4][r], vw[5][r], jb);
-          const uint32_t t67 = pair_byte(vw[6][r], vw[7][r], jb);
+          const uint32_t t01 = pair_byte(x[0], x[1], jb);
+          const uint32_t t23 = pair_byte(x[2], x[3], jb);
+          const uint32_t t45 = pair_byte(x[4], x[5], jb);
+          const uint32_t t67 = pair_byte(x[6], x[7], jb);
           uint4 lo, hi;
           lo.x = (t01 & 0x000F000Fu) | 0x43004300u;
           lo.y = (t23 & 0x000F000Fu) | 0x43004300u;
@@ -428,27 +588,34 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
           hi.y = ((t23 >> 4) & 0x000F000Fu) | 0x43004300u;
           hi.z = ((t45 >> 4) & 0x000F000Fu) | 0x43004300u;
           hi.w = ((t67 >> 4) & 0x000F000Fu) | 0x43004300u;
-          acc[ns] = mfma_bf16(lo, pb4, acc[ns]);
-          acc[ns + 1] = mfma_bf16(hi, pb4, acc[ns + 1]);
+          acc[ns] = mfma_bf16(lo, ph4, acc[ns]);
+          acc[ns + 1] = mfma_bf16(hi, ph4, acc[ns + 1]);
           acc[ns] = mfma_bf16(lo, pl4, acc[ns]);
           acc[ns + 1] = mfma_bf16(hi, pl4, acc[ns + 1]);
           ns += 2;
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-      pacc = mfma_bf16(ones, pb4, pacc);
+      pacc = mfma_bf16(ones, ph4, pacc);
       pacc = mfma_bf16(ones, pl4, pacc);
-    }
+      __builtin_amdgcn_sched_barrier(0);
+      issue(wr, it + 2);                      // into the slot step it - 1 used
+    };
+    for (int it = 0; it < nsteps; ++it)
+      step(sm.main + (it % kStages) * SG::BYTES, sm.main + ((it + 2) % kStages) * SG::BYTES, it);
+    wait_vm<0>();                             // no load may land in LDS after this point
+    __builtin_amdgcn_wave_barrier();
 
     // ---- finish: l over the four lane quarters, remove the +136 offset
     l_run += xor_lane<16>(l_run);
     l_run += xor_lane<32>(l_run);
     const float pbias = 136.0f * pacc[0];
-    const int qrow = un.qbeg + un.i0 + ti_n;
+    const int qrow = uqbeg + ui0 + ti_n;
     const int h = h0 + hi_n;
     if (a.plan.num_splits > 1) {
       if (row_ok) {
-        const int64_t prow = ((int64_t)un.sp * a.num_q_tokens + qrow) * a.nq + h;
+        const int64_t prow = ((int64_t)usp * a.num_q_tokens + qrow) * a.nq + h;
         float* dst = a.ws_o + prow * HS;
         int ns = 0;
 #pragma unroll
@@ -485,12 +652,11 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
           const int c0 = cb + w * (4 * q4 + rr);
 #pragma unroll
           for (int t = 0; t < 8; ++t)
-            if (t < w) sm.buf[n * HS + c0 + t] = (acc[ns + t][rr] - pbias) * inv_l;
+            if (t < w) buf[n * HS + c0 + t] = (acc[ns + t][rr] - pbias) * inv_l;
         }
         ns += w;
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int ps = 0; ps < 16 / RPP; ++ps) {
@@ -499,15 +665,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
       const bool rv = ti < ntok && hi < nh;
       float o[8];
       if (c_on) {
-        const float4 x0 = reinterpret_cast<const float4*>(sm.buf)[(r * HS + 8 * cj) / 4];
-        const float4 x1 = reinterpret_cast<const float4*>(sm.buf)[(r * HS + 8 * cj) / 4 + 1];
+        const float4 x0 = reinterpret_cast<const float4*>(buf)[(r * HS + 8 * cj) / 4];
+        const float4 x1 = reinterpret_cast<const float4*>(buf)[(r * HS + 8 * cj) / 4 + 1];
         o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
         o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = 0.0f;
       }
-      fwht_b(o, a.b, cj);
+      fwht_b_ct<LP>(o, a.b, cj);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = apply_sign(o[e] * inv_b, sbits, e);
       if (rv && c_on) {
@@ -516,7 +682,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
         wo.y = pack_bf16x2(o[2], o[3]);
         wo.z = pack_bf16x2(o[4], o[5]);
         wo.w = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<uint4*>(a.out + ((int64_t)(un.qbeg + un.i0 + ti) * a.nq + h0 + hi) * HS + 8 * cj) = wo;
+        *reinterpret_cast<uint4*>(a.out + ((int64_t)(uqbeg + ui0 + ti) * a.nq + h0 + hi) * HS + 8 * cj) = wo;
       }
     }
     __builtin_amdgcn_wave_barrier();

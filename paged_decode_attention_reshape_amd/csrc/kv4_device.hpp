@@ -84,7 +84,7 @@ __device__ __forceinline__ float xor_lane(float v) {
   } else if constexpr (D == 2) {
     x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
   } else if constexpr (D == 32) {
-    x = __builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32u) << 2), x);
+    x = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32u) << 2), x);
   } else {
     static_assert(D == 4 || D == 8 || D == 16, "xor distance");
     x = __builtin_amdgcn_ds_swizzle(x, (D << 10) | 0x1F);
@@ -141,6 +141,38 @@ __device__ __forceinline__ void fwht_b(float (&v)[8], int b, int jj) {
   fwht8_inlane(v);
   for (int d = 1; 8 * d < b; d <<= 1) fwht8_xlane(v, d, (jj & d) != 0);
 }
+
+// Compile-time variants for at most LPMAX lanes per vector (no runtime
+// dispatch on the lane distance).
+template <int D>
+__device__ __forceinline__ void fwht8_xlane_ct(float (&v)[8], bool upper) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = xor_lane<D>(v[e]);
+    v[e] = upper ? (p - v[e]) : (v[e] + p);
+  }
+}
+template <int LPMAX>
+__device__ __forceinline__ void fwht_b_ct(float (&v)[8], int b, int jj) {
+  fwht8_inlane(v);
+  if constexpr (LPMAX > 1) { if (b > 8) fwht8_xlane_ct<1>(v, (jj & 1) != 0); }
+  if constexpr (LPMAX > 2) { if (b > 16) fwht8_xlane_ct<2>(v, (jj & 2) != 0); }
+  if constexpr (LPMAX > 4) { if (b > 32) fwht8_xlane_ct<4>(v, (jj & 4) != 0); }
+  if constexpr (LPMAX > 8) { if (b > 64) fwht8_xlane_ct<8>(v, (jj & 8) != 0); }
+  if constexpr (LPMAX > 16) { if (b > 128) fwht8_xlane_ct<16>(v, (jj & 16) != 0); }
+}
+template <int W>
+__device__ __forceinline__ float group_sum_ct(float v) {
+  if constexpr (W > 1) v += xor_lane<1>(v);
+  if constexpr (W > 2) v += xor_lane<2>(v);
+  if constexpr (W > 4) v += xor_lane<4>(v);
+  if constexpr (W > 8) v += xor_lane<8>(v);
+  if constexpr (W > 16) v += xor_lane<16>(v);
+  if constexpr (W > 32) v += xor_lane<32>(v);
+  return v;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // max-reduce over the `width` lanes (power of two) of an aligned lane group.
 __device__ __forceinline__ float group_max(float v, int width) {
