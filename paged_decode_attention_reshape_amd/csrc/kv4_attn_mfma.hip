@@ -47,16 +47,17 @@ __device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// 8 codes of one token (one 32-bit word) -> A operand of one k-step: bf16 of
-// 128 + u in k-order of element offsets [0, 4, 1, 5, 2, 6, 3, 7].
+// Nibble pair -> bf16 pair: for the nibbles at bits 0-3 and 16-19 of x,
+// (nibble ^ 8) | 0x4300, i.e. the bf16 of 128 + u with u = code + 8; every
+// other bit comes from the constant. One v_bitop3 (out = m ? x ^ k : k).
+__device__ __forceinline__ uint32_t nib2bf(uint32_t x) {
+  return __builtin_amdgcn_bitop3_b32(x, 0x43084308u, 0x000F000Fu, 0x6C);
+}
+
+// 8 codes of one token (one 32-bit word) -> A operand of one k-step, in
+// k-order of element offsets [0, 4, 1, 5, 2, 6, 3, 7].
 __device__ __forceinline__ uint4 k_operand(uint32_t w) {
-  const uint32_t x = w ^ 0x88888888u;
-  uint4 r;
-  r.x = (x & 0x000F000Fu) | 0x43004300u;
-  r.y = ((x >> 4) & 0x000F000Fu) | 0x43004300u;
-  r.z = ((x >> 8) & 0x000F000Fu) | 0x43004300u;
-  r.w = ((x >> 12) & 0x000F000Fu) | 0x43004300u;
-  return r;
+  return make_uint4(nib2bf(w), nib2bf(w >> 4), nib2bf(w >> 8), nib2bf(w >> 12));
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -238,13 +239,16 @@ struct StageGeo {
   static constexpr int LOADS = 2 * NKL + 8 * Geo<HS>::NVR + 1;   // VMEM instructions per step
 };
 
-constexpr int kStages = 3;
+// stage slots per wave: loads run kStages - 1 steps ahead of the compute
+template <int HS>
+constexpr int stages_for() { return HS <= 128 ? 4 : 3; }
 
 template <int HS>
 struct MfmaSmem {
   static constexpr int STAGE = StageGeo<HS>::BYTES;
   static constexpr int BUFB = 16 * HS * 4;                 // q' staging / epilogue (fp32 rows)
-  static constexpr int MAINB = kStages * STAGE > BUFB ? kStages * STAGE : BUFB;
+  static constexpr int NST = stages_for<HS>();
+  static constexpr int MAINB = NST * STAGE > BUFB ? NST * STAGE : BUFB;
   alignas(16) unsigned char main[MAINB];                   // stages overlay the q / epilogue buffer
   float qsum[16];
 };
@@ -290,6 +294,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
   constexpr int LP = (HS / 8) <= 8 ? 8 : ((HS / 8) <= 16 ? 16 : 32);   // lanes per row, chunk mapping
   constexpr int RPP = kWave / LP;                                       // rows per pass
   constexpr int HALF = HS / 2;
+  constexpr int kStages = stages_for<HS>();
   __shared__ MfmaSmem<HS> smem_all[4];
 
   const int lane = threadIdx.x & 63;
@@ -468,8 +473,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
     };
 
     if (nsteps > 0) {
-      issue(sm.main, 0);
-      issue(sm.main + SG::BYTES, 1);
+#pragma unroll
+      for (int i = 0; i < kStages - 1; ++i) issue(sm.main + i * SG::BYTES, i);
     }
     // `st` (read) and `wr` (filled for step it + 2) are distinct stage slots;
     // the restrict qualifiers let the compiler keep the lookahead loads in
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
     auto step = [&](const unsigned char* __restrict__ st, unsigned char* __restrict__ wr, int it) {
       const int slot = it % kStages;
       const int base = k0 + 32 * it;
-      wait_vm<SG::LOADS>();                  // step `it` landed; step `it + 1` may be in flight
+      wait_vm<(kStages - 2) * SG::LOADS>();   // step `it` landed; later steps may be in flight
       __builtin_amdgcn_sched_barrier(0);
       const bool oka = (okmask >> (2 * slot)) & 1, okb = (okmask >> (2 * slot + 1)) & 1;
 
@@ -570,7 +575,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
           const unsigned char* src = st + SG::V_OFF + i * SG::VBYTES_TOK;
           // sub-dword regions hold zero-extended words; their unused
           // nibbles are never selected below
-          x[i] = reinterpret_cast<const uint32_t*>(src + r * 256)[lane] ^ 0x88888888u;
+          x[i] = reinterpret_cast<const uint32_t*>(src + r * 256)[lane];
         }
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
@@ -579,15 +584,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
           const uint32_t t23 = pair_byte(x[2], x[3], jb);
           const uint32_t t45 = pair_byte(x[4], x[5], jb);
           const uint32_t t67 = pair_byte(x[6], x[7], jb);
-          uint4 lo, hi;
-          lo.x = (t01 & 0x000F000Fu) | 0x43004300u;
-          lo.y = (t23 & 0x000F000Fu) | 0x43004300u;
-          lo.z = (t45 & 0x000F000Fu) | 0x43004300u;
-          lo.w = (t67 & 0x000F000Fu) | 0x43004300u;
-          hi.x = ((t01 >> 4) & 0x000F000Fu) | 0x43004300u;
-          hi.y = ((t23 >> 4) & 0x000F000Fu) | 0x43004300u;
-          hi.z = ((t45 >> 4) & 0x000F000Fu) | 0x43004300u;
-          hi.w = ((t67 >> 4) & 0x000F000Fu) | 0x43004300u;
+          const uint4 lo = make_uint4(nib2bf(t01), nib2bf(t23), nib2bf(t45), nib2bf(t67));
+          const uint4 hi = make_uint4(nib2bf(t01 >> 4), nib2bf(t23 >> 4), nib2bf(t45 >> 4), nib2bf(t67 >> 4));
           acc[ns] = mfma_bf16(lo, ph4, acc[ns]);
           acc[ns + 1] = mfma_bf16(hi, ph4, acc[ns + 1]);
           acc[ns] = mfma_bf16(lo, pl4, acc[ns]);
@@ -600,10 +598,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
       pacc = mfma_bf16(ones, ph4, pacc);
       pacc = mfma_bf16(ones, pl4, pacc);
       __builtin_amdgcn_sched_barrier(0);
-      issue(wr, it + 2);                      // into the slot step it - 1 used
+      issue(wr, it + kStages - 1);            // into the slot step it - 1 used
     };
     for (int it = 0; it < nsteps; ++it)
-      step(sm.main + (it % kStages) * SG::BYTES, sm.main + ((it + 2) % kStages) * SG::BYTES, it);
+      step(sm.main + (it % kStages) * SG::BYTES, sm.main + ((it + kStages - 1) % kStages) * SG::BYTES, it);
     wait_vm<0>();                             // no load may land in LDS after this point
     __builtin_amdgcn_wave_barrier();
 
@@ -624,10 +622,18 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
           v_region<HS>(r, w, cb);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            const int c0 = cb + w * (4 * q4 + rr);
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-              if (t < w) dst[c0 + t] = acc[ns + t][rr] - pbias;
+            float* d = dst + cb + w * (4 * q4 + rr);
+            if (w == 8) {
+              reinterpret_cast<float4*>(d)[0] = make_float4(acc[ns][rr] - pbias, acc[ns + 1][rr] - pbias,
+                                                            acc[ns + 2][rr] - pbias, acc[ns + 3][rr] - pbias);
+              reinterpret_cast<float4*>(d)[1] = make_float4(acc[ns + 4][rr] - pbias, acc[ns + 5][rr] - pbias,
+                                                            acc[ns + 6][rr] - pbias, acc[ns + 7][rr] - pbias);
+            } else if (w == 4) {
+              reinterpret_cast<float4*>(d)[0] = make_float4(acc[ns][rr] - pbias, acc[ns + 1][rr] - pbias,
+                                                            acc[ns + 2][rr] - pbias, acc[ns + 3][rr] - pbias);
+            } else {
+              reinterpret_cast<float2*>(d)[0] = make_float2(acc[ns][rr] - pbias, acc[ns + 1][rr] - pbias);
+            }
           }
           ns += w;
         }

@@ -320,25 +320,42 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
       }
     }
   }
-  float M = -INFINITY;
-  for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, a.ws_ml[2 * ((int64_t)sp * n_rows + row)]);
+  // one pass over the splits with a running maximum, four splits' loads in
+  // flight at a time
+  float M = -INFINITY, Ls = 0.0f;
   float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float Ls = 0.0f;
-  if (M != -INFINITY) {
-    for (int sp = 0; sp < nsp; ++sp) {
-      const int64_t prow = (int64_t)sp * n_rows + row;
-      const float msp = a.ws_ml[2 * prow];
-      if (msp == -INFINITY) continue;
-      const float w = fast_exp2(msp - M);
-      Ls = fmaf(a.ws_ml[2 * prow + 1], w, Ls);
-      if (lane_on) {
-        const float4* src = reinterpret_cast<const float4*>(a.ws_o + prow * hs + 8 * jj);
-        const float4 x0 = src[0], x1 = src[1];
-        o[0] = fmaf(x0.x, w, o[0]); o[1] = fmaf(x0.y, w, o[1]);
-        o[2] = fmaf(x0.z, w, o[2]); o[3] = fmaf(x0.w, w, o[3]);
-        o[4] = fmaf(x1.x, w, o[4]); o[5] = fmaf(x1.y, w, o[5]);
-        o[6] = fmaf(x1.z, w, o[6]); o[7] = fmaf(x1.w, w, o[7]);
+  for (int sp0 = 0; sp0 < nsp; sp0 += 4) {
+    float mm[4], ll[4];
+    float4 x0[4], x1[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int sp = sp0 + k;
+      mm[k] = -INFINITY;
+      ll[k] = 0.0f;
+      x0[k] = x1[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (sp < nsp) {
+        const int64_t prow = (int64_t)sp * n_rows + row;
+        mm[k] = a.ws_ml[2 * prow];
+        ll[k] = a.ws_ml[2 * prow + 1];
+        if (lane_on) {
+          const float4* src = reinterpret_cast<const float4*>(a.ws_o + prow * hs + 8 * jj);
+          x0[k] = src[0];
+          x1[k] = src[1];
+        }
       }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (mm[k] == -INFINITY) continue;
+      const float Mn = fmaxf(M, mm[k]);
+      const float so = fast_exp2(M - Mn);          // 0 while M is -inf
+      const float sn = fast_exp2(mm[k] - Mn);
+      Ls = Ls * so + ll[k] * sn;
+      o[0] = o[0] * so + x0[k].x * sn; o[1] = o[1] * so + x0[k].y * sn;
+      o[2] = o[2] * so + x0[k].z * sn; o[3] = o[3] * so + x0[k].w * sn;
+      o[4] = o[4] * so + x1[k].x * sn; o[5] = o[5] * so + x1[k].y * sn;
+      o[6] = o[6] * so + x1[k].z * sn; o[7] = o[7] * so + x1[k].w * sn;
+      M = Mn;
     }
   }
   const float inv_l = Ls > 0.0f ? 1.0f / Ls : 0.0f;
