@@ -70,6 +70,9 @@ def main():
     ap.add_argument("--config", default="llama8b_long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times) -- the reference "
+                         "kernel of known size for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -87,6 +90,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "repeats": 5}))
+        return
     w = W.ALL[args.config]()
     lay = W.make_layout(w)
     print(f"# config {w.name}: seqs={w.num_seqs} nq={w.num_q_heads} nkv={w.num_kv_heads} hs={w.head_size} "

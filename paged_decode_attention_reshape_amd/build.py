@@ -28,9 +28,20 @@ COMMON = [
 SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
+# The attention kernels use +-inf but never NaN: let max/min skip NaN quieting.
+# (The write path stays on default IEEE semantics: its results are compared
+# bit for bit.)
+# Matrix-core accumulators stay in ordinary VGPRs (the softmax rescale and
+# the epilogue touch them with VALU ops; AGPR copies would cost both).
+PER_FILE = {
+    "kv4_attn_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "kv4_attn_valu.hip": ["-fno-honor-nans"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:

@@ -241,7 +241,7 @@ struct StageGeo {
 
 // stage slots per wave: loads run kStages - 1 steps ahead of the compute
 template <int HS>
-constexpr int stages_for() { return HS <= 128 ? 4 : 3; }
+constexpr int stages_for() { return 3; }
 
 template <int HS>
 struct MfmaSmem {
@@ -287,7 +287,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 template <int HS>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_t* prefix) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_mfma_kernel(AttnArgs a, const int32_t* prefix) {
   using GG = Geo<HS>;
   using SG = StageGeo<HS>;
   constexpr int NK = GG::NK, NS = GG::NS, NVR = GG::NVR;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
   __shared__ MfmaSmem<HS> smem_all[4];
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = uniform(threadIdx.x >> 6);           // wave index (uniform: LDS bases in SGPRs)
   MfmaSmem<HS>& sm = smem_all[wv];
   float* buf = reinterpret_cast<float*>(sm.main);
   const int n = lane & 15;          // MFMA column: query row of this lane
@@ -321,6 +321,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
   // lane byte offsets inside one half tile (relative to its first token row)
   const uint32_t tok_stride = (uint32_t)nkv * HALF;         // bytes between token rows of a page
   const uint32_t half_bytes = 16u * tok_stride;             // one half tile of a page
+  const int64_t page_bytes = (int64_t)bsz * tok_stride;     // one page of one cache
+  const int64_t page_rows = (int64_t)bsz * nkv;             // scale entries per page
   const uint32_t koff = (uint32_t)n * tok_stride + (uint32_t)q4 * (HS / 8);
   uint32_t vo[4];                                           // token 4*q4 + i, 32-bit column chunk n
 #pragma unroll
@@ -444,10 +446,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
       pb = pb < 0 ? 0 : pb;
       const int offa = base % bsz;
       const int offb = b_in ? (base + 16) % bsz : offa;
-      const int64_t rowa = ((int64_t)pa * bsz + offa) * nkv + ug;
-      const int64_t rowb = ((int64_t)pb * bsz + offb) * nkv + ug;
-      const __amdgpu_buffer_rsrc_t rk[2] = {rsrc(a.key_cache + rowa * HALF, half_bytes),
-                                            rsrc(a.key_cache + rowb * HALF, half_bytes)};
+      // byte offset of the first token row of each half tile inside a cache,
+      // and the scale index of that row (kv head ug)
+      const int64_t bya = (int64_t)pa * page_bytes + (int64_t)(offa * nkv + ug) * HALF;
+      const int64_t byb = (int64_t)pb * page_bytes + (int64_t)(offb * nkv + ug) * HALF;
+      const int64_t rowa = (int64_t)pa * page_rows + offa * nkv + ug;
+      const int64_t rowb = (int64_t)pb * page_rows + offb * nkv + ug;
+      const __amdgpu_buffer_rsrc_t rk[2] = {rsrc(a.key_cache + bya, half_bytes),
+                                            rsrc(a.key_cache + byb, half_bytes)};
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -457,8 +463,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, const int32_
           else if constexpr (SG::KSZ == 12) dma_buf<12>(rk[h], koff + j * SG::KSZ, dst);
           else dma_buf<4>(rk[h], koff + j * SG::KSZ, dst);
         }
-      const __amdgpu_buffer_rsrc_t rv[2] = {rsrc(a.value_cache + rowa * HALF, half_bytes),
-                                            rsrc(a.value_cache + rowb * HALF, half_bytes)};
+      const __amdgpu_buffer_rsrc_t rv[2] = {rsrc(a.value_cache + bya, half_bytes),
+                                            rsrc(a.value_cache + byb, half_bytes)};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         unsigned char* dst = st + SG::V_OFF + i * SG::VBYTES_TOK;
