@@ -96,6 +96,10 @@ def main():
         dst = torch.empty_like(src)
         for _ in range(5):
             dst.copy_(src)
+        # a read-only pass over the same bytes (float32 sum: reads n bytes, writes one value)
+        f = src.view(torch.float32)
+        for _ in range(5):
+            f.sum()
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "repeats": 5}))
         return

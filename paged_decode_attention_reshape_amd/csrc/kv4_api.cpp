@@ -71,12 +71,12 @@ bool mfma_head_size(int hs) { return hs == 64 || hs == 96 || hs == 128 || hs == 
 // KV4_FORCE_PATH overrides used by tests), so the workspace size and the
 // launch agree. Path 1 (matrix cores) is used where the query block is dense
 // (GQA group > 1 or query_len > 1), the head size is a multiple of 32 the
-// kernel is built for, and pages hold a multiple of 16 tokens.
+// kernel is built for, and pages hold a power-of-two number (>= 16) of tokens.
 int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
               int32_t max_query_len, int32_t max_seq_len, int32_t block_size, kv4::AttnPlan& p) {
   std::memset(&p, 0, sizeof(p));
   const int G = nq / nkv;
-  const bool mfma_ok = mfma_head_size(hs) && block_size % 16 == 0;
+  const bool mfma_ok = mfma_head_size(hs) && block_size % 16 == 0 && (block_size & (block_size - 1)) == 0;
   bool mfma = mfma_ok && (G > 1 || max_query_len > 1);
   if (const char* f = std::getenv("KV4_FORCE_PATH")) {
     if (!std::strcmp(f, "valu")) mfma = false;

@@ -309,6 +309,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   const int split = a.plan.split_tokens;
   const int total = uniform(prefix[a.num_seqs]);
   const int bsz = a.bs;
+  const int bs_log2 = __builtin_ctz((unsigned)bsz);      // the planner sends only power-of-two pages here
+  const int bs_mask = bsz - 1;
   const float inv_b = 1.0f / (float)a.b;
 
   // lane constants of the chunk mapping (q setup and epilogue)
@@ -407,8 +409,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 
     // page ids of this unit, one per lane, 64 pages at a time
     const int32_t* bt = a.block_table + (int64_t)us * a.max_blocks;
-    const int npages = k1 > 0 ? (k1 - 1) / bsz + 1 : 0;
-    int pg0 = k0 / bsz;
+    const int npages = k1 > 0 ? ((k1 - 1) >> bs_log2) + 1 : 0;
+    int pg0 = k0 >> bs_log2;
     int pg_lane = -1;
     auto load_pages = [&](int first) {
       pg0 = first;
@@ -430,13 +432,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       const int slot = it % kStages;
       const int base = k0 + 32 * (it < nsteps ? it : 0);
       const int b_in = base + 16 < k1;
-      int ia = base / bsz - pg0;
-      int ib = (b_in ? (base + 16) / bsz : base / bsz) - pg0;
+      const int pga = base >> bs_log2;
+      const int pgb = b_in ? (base + 16) >> bs_log2 : pga;
+      int ia = pga - pg0;
+      int ib = pgb - pg0;
       if (ia < 0 || ib >= 64) {             // another chunk of the page table (rare)
         wait_vm<0>();
-        load_pages(base / bsz);
+        load_pages(pga);
         ia = 0;
-        ib = (b_in ? (base + 16) / bsz : base / bsz) - pg0;
+        ib = pgb - pg0;
       }
       int pa = __builtin_amdgcn_readlane(pg_lane, ia);
       int pb = __builtin_amdgcn_readlane(pg_lane, ib);
@@ -444,8 +448,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       okmask = (okmask & ~(3 << (2 * slot))) | ((oka | (okb << 1)) << (2 * slot));
       pa = pa < 0 ? 0 : pa;
       pb = pb < 0 ? 0 : pb;
-      const int offa = base % bsz;
-      const int offb = b_in ? (base + 16) % bsz : offa;
+      const int offa = base & bs_mask;
+      const int offb = b_in ? (base + 16) & bs_mask : offa;
       // byte offset of the first token row of each half tile inside a cache,
       // and the scale index of that row (kv head ug)
       const int64_t bya = (int64_t)pa * page_bytes + (int64_t)(offa * nkv + ug) * HALF;
@@ -490,6 +494,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       const int base = k0 + 32 * it;
       wait_vm<(kStages - 2) * SG::LOADS>();   // step `it` landed; later steps may be in flight
       __builtin_amdgcn_sched_barrier(0);
+      issue(wr, it + kStages - 1);            // into the slot step it - 1 used
       const bool oka = (okmask >> (2 * slot)) & 1, okb = (okmask >> (2 * slot + 1)) & 1;
 
       // K code words of this lane: token n, chunk q4, both half tiles
@@ -545,8 +550,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       }
       float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),
                        fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
-      mx = fmaxf(mx, xor_lane<16>(mx));
-      mx = fmaxf(mx, xor_lane<32>(mx));
+      mx = max_x16_x32(mx);
       const float m_new = fmaxf(m_run, mx);
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;
       // a row that has seen no key yet has nothing to rescale
@@ -603,8 +607,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
       pacc = mfma_bf16(ones, ph4, pacc);
       pacc = mfma_bf16(ones, pl4, pacc);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(wr, it + kStages - 1);            // into the slot step it - 1 used
     };
     for (int it = 0; it < nsteps; ++it)
       step(sm.main + (it % kStages) * SG::BYTES, sm.main + ((it + kStages - 1) % kStages) * SG::BYTES, it);
@@ -612,8 +614,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     __builtin_amdgcn_wave_barrier();
 
     // ---- finish: l over the four lane quarters, remove the +136 offset
-    l_run += xor_lane<16>(l_run);
-    l_run += xor_lane<32>(l_run);
+    l_run = sum_x16_x32(l_run);
     const float pbias = 136.0f * pacc[0];
     const int qrow = uqbeg + ui0 + ti_n;
     const int h = h0 + hi_n;

@@ -174,6 +174,26 @@ __device__ __forceinline__ float group_sum_ct(float v) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Reductions over lanes l, l ^ 16 and l ^ 32 with the gfx950 permlane swaps
+// (full-rate VALU, no LDS round trip). With both operands equal, the swap
+// returns the value of lane l ^ 16 (resp. l ^ 32) in one of its two results.
+__device__ __forceinline__ float max_x16_x32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_x16_x32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // max-reduce over the `width` lanes (power of two) of an aligned lane group.
 __device__ __forceinline__ float group_max(float v, int width) {
   for (int d = 1; d < width; d <<= 1) v = fmaxf(v, xor_lane_rt(v, d));
