@@ -137,16 +137,12 @@ struct Unit {
   int s, i0, qbeg, qlen, L, g, ht, sp;
 };
 
-// Dense unit index -> (sequence, tile, head tile, kv head, split). prefix[s]
-// is the first unit of sequence s; unit order inside a sequence is kv head
+// Dense unit index -> (sequence, tile, head tile, kv head, split); called by
+// all lanes of a wave with a wave-uniform u. prefix[s] is the first unit of
+// sequence s; unit order inside a sequence is kv head
 // fastest, then head tile, then split, then query tile.
 __device__ __forceinline__ bool decode_unit(const AttnArgs& a, const int32_t* prefix, int u, Unit& un) {
-  int lo = 0, hi = a.num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= u) lo = mid; else hi = mid - 1;
-  }
-  const int s = lo;
+  const int s = wave_search_le(prefix, a.num_seqs, u);
   int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
   qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
   qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
@@ -240,8 +236,12 @@ struct StageGeo {
 };
 
 // stage slots per wave: loads run kStages - 1 steps ahead of the compute
+// Stage slots per wave: the loads of step it + 1 run during step it. More
+// slots keep more bytes in flight, but then the L2 evicts 128-byte lines
+// before the wave of the neighbouring kv head (which reads the other half of
+// the line) gets to them; two slots measured best.
 template <int HS>
-constexpr int stages_for() { return 3; }
+constexpr int stages_for() { return 2; }
 
 template <int HS>
 struct MfmaSmem {
@@ -312,6 +312,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   const int bs_log2 = __builtin_ctz((unsigned)bsz);      // the planner sends only power-of-two pages here
   const int bs_mask = bsz - 1;
   const float inv_b = 1.0f / (float)a.b;
+  // With num_kv_heads % 4 == 0 the 4 units of a workgroup are 4 kv heads of
+  // one (sequence, query tile, head tile, split): the waves take the same
+  // branches and run the same number of steps. A workgroup barrier per step
+  // then keeps the waves of neighbouring kv heads (two per 128-byte line)
+  // together, so each line comes from HBM once.
+  const bool wg_sync = (nkv & 3) == 0;
 
   // lane constants of the chunk mapping (q setup and epilogue)
   const int cj = lane & (LP - 1);
@@ -333,7 +339,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   const float* sc_base = lane < 32 ? a.k_scale : a.v_scale;
   const bool sc_half_b = (lane & 16) != 0;
 
-  for (int u0 = blockIdx.x * 4; u0 < total; u0 += gridDim.x * 4) {
+  // Workgroups are dealt to the 8 XCDs round-robin (block b on XCD b % 8).
+  // Unit quads 2k and 2k + 1 (kv heads 0-3 and 4-7 of one sequence split,
+  // whose scale rows share 128-byte lines) go to blocks b and b + 8, which
+  // share an XCD and its L2.
+  const int nbk = gridDim.x, bk = blockIdx.x;
+  const int pbk = bk < (nbk & ~15) ? ((bk & ~15) | ((bk & 7) << 1) | ((bk >> 3) & 1)) : bk;
+  for (int u0 = pbk * 4; u0 < total; u0 += gridDim.x * 4) {
     const int u = u0 + wv;
     if (u >= total) continue;
     Unit un;
@@ -350,6 +362,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     const int k0 = usp * split;
     const int k1 = min(k0 + split, kend);
     if (k0 >= k1 && usp > 0) continue;   // no keys for this tile in this split (the merge skips it)
+
+    // page ids of this unit, one per lane, 64 pages at a time (loaded first:
+    // the q' setup below hides their latency)
+    const int32_t* bt = a.block_table + (int64_t)us * a.max_blocks;
+    const int npages = k1 > 0 ? ((k1 - 1) >> bs_log2) + 1 : 0;
+    int pg0 = k0 >> bs_log2;
+    int pg_lane = -1;
+    auto load_pages = [&](int first) {
+      pg0 = first;
+      const int idx = first + lane;
+      int p = -1;
+      if (idx < npages) {
+        p = bt[idx];
+        p = (p >= 0 && p < a.num_blocks) ? p : -1;
+      }
+      pg_lane = p;
+    };
+    const int nsteps = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
+    if (nsteps > 0) load_pages(pg0);
 
     // ---- q' rows -> LDS (bf16 hi / lo, k-permuted) and their sums
 #pragma unroll
@@ -407,29 +438,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     f32x4_t pacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    // page ids of this unit, one per lane, 64 pages at a time
-    const int32_t* bt = a.block_table + (int64_t)us * a.max_blocks;
-    const int npages = k1 > 0 ? ((k1 - 1) >> bs_log2) + 1 : 0;
-    int pg0 = k0 >> bs_log2;
-    int pg_lane = -1;
-    auto load_pages = [&](int first) {
-      pg0 = first;
-      const int idx = first + lane;
-      int p = -1;
-      if (idx < npages) {
-        p = bt[idx];
-        p = (p >= 0 && p < a.num_blocks) ? p : -1;
-      }
-      pg_lane = p;
-    };
-    const int nsteps = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
-    if (nsteps > 0) load_pages(pg0);
     int okmask = 0;   // bit 2*slot: half A page valid, bit 2*slot+1: half B (wave-uniform)
 
     // issue the loads of step `it` into stage slot `it % kStages`; steps past
-    // the end reload the first step's rows (in bounds, never read)
+    // the end issue loads with an empty buffer range (they fetch nothing and
+    // fill the slot with zeros, which is never read)
     auto issue = [&](unsigned char* __restrict__ st, int it) {
       const int slot = it % kStages;
+      const bool dummy = it >= nsteps;
       const int base = k0 + 32 * (it < nsteps ? it : 0);
       const int b_in = base + 16 < k1;
       const int pga = base >> bs_log2;
@@ -454,10 +470,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       // and the scale index of that row (kv head ug)
       const int64_t bya = (int64_t)pa * page_bytes + (int64_t)(offa * nkv + ug) * HALF;
       const int64_t byb = (int64_t)pb * page_bytes + (int64_t)(offb * nkv + ug) * HALF;
-      const int64_t rowa = (int64_t)pa * page_rows + offa * nkv + ug;
-      const int64_t rowb = (int64_t)pb * page_rows + offb * nkv + ug;
-      const __amdgpu_buffer_rsrc_t rk[2] = {rsrc(a.key_cache + bya, half_bytes),
-                                            rsrc(a.key_cache + byb, half_bytes)};
+      int64_t rowa = (int64_t)pa * page_rows + offa * nkv + ug;
+      int64_t rowb = (int64_t)pb * page_rows + offb * nkv + ug;
+      const uint32_t nrec = dummy ? 0u : half_bytes;
+      if (dummy) { rowa = 0; rowb = 0; }   // scale rows 0..15 of page 0: lines every wave keeps hot
+      const __amdgpu_buffer_rsrc_t rk[2] = {rsrc(a.key_cache + bya, nrec),
+                                            rsrc(a.key_cache + byb, nrec)};
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -467,8 +485,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
           else if constexpr (SG::KSZ == 12) dma_buf<12>(rk[h], koff + j * SG::KSZ, dst);
           else dma_buf<4>(rk[h], koff + j * SG::KSZ, dst);
         }
-      const __amdgpu_buffer_rsrc_t rv[2] = {rsrc(a.value_cache + bya, half_bytes),
-                                            rsrc(a.value_cache + byb, half_bytes)};
+      const __amdgpu_buffer_rsrc_t rv[2] = {rsrc(a.value_cache + bya, nrec),
+                                            rsrc(a.value_cache + byb, nrec)};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         unsigned char* dst = st + SG::V_OFF + i * SG::VBYTES_TOK;
@@ -482,17 +500,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       dma(sc_base + (sc_half_b ? rowb : rowa) + soff, st + SG::S_OFF, 4);
     };
 
+    if (wg_sync) __builtin_amdgcn_s_barrier();
     if (nsteps > 0) {
 #pragma unroll
       for (int i = 0; i < kStages - 1; ++i) issue(sm.main + i * SG::BYTES, i);
     }
-    // `st` (read) and `wr` (filled for step it + 2) are distinct stage slots;
+    // `st` (read) and `wr` (filled for step it + kStages - 1) are distinct slots;
     // the restrict qualifiers let the compiler keep the lookahead loads in
     // flight across the reads of the current step.
     auto step = [&](const unsigned char* __restrict__ st, unsigned char* __restrict__ wr, int it) {
       const int slot = it % kStages;
       const int base = k0 + 32 * it;
       wait_vm<(kStages - 2) * SG::LOADS>();   // step `it` landed; later steps may be in flight
+      if (wg_sync) __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       issue(wr, it + kStages - 1);            // into the slot step it - 1 used
       const bool oka = (okmask >> (2 * slot)) & 1, okb = (okmask >> (2 * slot + 1)) & 1;

@@ -280,88 +280,91 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 }
 
 // Merge of the split partials (log-sum-exp in base 2) and the output
-// epilogue D.H(.)/b. One lane group of LP = next_pow2(hs/8) lanes per output
-// row (query token, query head).
+// epilogue D.H(.)/b. One wave per output row (query token, query head): the
+// wave holds NG = 64 / LP copies of the row (LP = next_pow2(hs/8) lanes of 8
+// elements each); copy g folds splits g, g + NG, ... with four loads in flight,
+// then a butterfly over the copies combines them.
+template <int LP>
 __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
+  constexpr int NG = kWave / LP;
   const int hs = a.hs;
-  const int LP = next_pow2(hs >> 3);
   const int lane = threadIdx.x & (kWave - 1);
   const int jj = lane & (LP - 1);
   const int grp = lane / LP;
   const bool lane_on = jj < (hs >> 3);
-  const int rows_per_wave = kWave / LP;
   const int64_t n_rows = a.num_q_tokens * a.nq;
-  const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-  const int64_t row = wave_id * rows_per_wave + grp;
-  const bool in = row < n_rows;
   const uint32_t sbits = lane_on ? sign_bits8(a.seed, jj) : 0u;
   const float inv_b = 1.0f / (float)a.b;
-
-  int nsp = 0;
-  int64_t qtok = 0;
-  if (in) {
-    qtok = row / a.nq;
-    // sequence of this query row: largest s with qsl[s] <= qtok
-    int lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.qsl[mid] <= qtok) lo = mid; else hi = mid - 1;
-    }
-    const int s = lo;
-    int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
-    int64_t L = a.seq_lens[s];
-    const int64_t cap = (int64_t)a.max_blocks * a.bs;
-    L = L < 0 ? 0 : (L > cap ? cap : L);
-    if (qtok >= qb && qtok < qe) {
-      const int64_t pos = L - (qe - qb) + (qtok - qb);
-      if (pos >= 0) {
-        const int64_t n = (pos + a.plan.split_tokens) / a.plan.split_tokens;   // ceil((pos+1)/split)
-        nsp = (int)(n < a.plan.num_splits ? n : a.plan.num_splits);
-      }
-    }
-  }
-  // one pass over the splits with a running maximum, four splits' loads in
-  // flight at a time
-  float M = -INFINITY, Ls = 0.0f;
-  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int sp0 = 0; sp0 < nsp; sp0 += 4) {
-    float mm[4], ll[4];
-    float4 x0[4], x1[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int sp = sp0 + k;
-      mm[k] = -INFINITY;
-      ll[k] = 0.0f;
-      x0[k] = x1[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (sp < nsp) {
-        const int64_t prow = (int64_t)sp * n_rows + row;
-        mm[k] = a.ws_ml[2 * prow];
-        ll[k] = a.ws_ml[2 * prow + 1];
-        if (lane_on) {
-          const float4* src = reinterpret_cast<const float4*>(a.ws_o + prow * hs + 8 * jj);
-          x0[k] = src[0];
-          x1[k] = src[1];
+  const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t row = wave0; row < n_rows; row += n_waves) {
+    int nsp = 0;
+    {
+      const int64_t qtok = row / a.nq;
+      const int s = wave_search_le(a.qsl, a.num_seqs, qtok);   // sequence of this query row
+      const int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
+      int64_t L = a.seq_lens[s];
+      const int64_t cap = (int64_t)a.max_blocks * a.bs;
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+      if (qtok >= qb && qtok < qe) {
+        const int64_t pos = L - (qe - qb) + (qtok - qb);
+        if (pos >= 0) {
+          const int64_t n = (pos + a.plan.split_tokens) / a.plan.split_tokens;   // ceil((pos+1)/split)
+          nsp = (int)(n < a.plan.num_splits ? n : a.plan.num_splits);
         }
       }
     }
+    float M = -INFINITY, Ls = 0.0f;
+    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // fold one partial (m2, l2, y) into the running (M, Ls, o)
+    auto merge = [&](float m2, float l2, const float (&y)[8]) {
+      const float Mn = fmaxf(M, m2);
+      if (Mn == -INFINITY) return;                   // both empty
+      const float so = fast_exp2(M - Mn);            // 0 while M is -inf
+      const float sn = fast_exp2(m2 - Mn);
+      Ls = Ls * so + l2 * sn;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (mm[k] == -INFINITY) continue;
-      const float Mn = fmaxf(M, mm[k]);
-      const float so = fast_exp2(M - Mn);          // 0 while M is -inf
-      const float sn = fast_exp2(mm[k] - Mn);
-      Ls = Ls * so + ll[k] * sn;
-      o[0] = o[0] * so + x0[k].x * sn; o[1] = o[1] * so + x0[k].y * sn;
-      o[2] = o[2] * so + x0[k].z * sn; o[3] = o[3] * so + x0[k].w * sn;
-      o[4] = o[4] * so + x1[k].x * sn; o[5] = o[5] * so + x1[k].y * sn;
-      o[6] = o[6] * so + x1[k].z * sn; o[7] = o[7] * so + x1[k].w * sn;
+      for (int e = 0; e < 8; ++e) o[e] = o[e] * so + y[e] * sn;
       M = Mn;
-    }
-  }
-  const float inv_l = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    };
+    for (int sp0 = grp; sp0 < nsp; sp0 += 4 * NG) {
+      float mm[4], ll[4], y[4][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] *= inv_l;
-  store_out_row(o, a.b, jj, sbits, inv_b, a.out + row * hs + 8 * jj, in && lane_on);
+      for (int k = 0; k < 4; ++k) {
+        const int sp = sp0 + k * NG;
+        mm[k] = -INFINITY;
+        ll[k] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[k][e] = 0.0f;
+        if (sp < nsp) {
+          const int64_t prow = (int64_t)sp * n_rows + row;
+          mm[k] = a.ws_ml[2 * prow];
+          ll[k] = a.ws_ml[2 * prow + 1];
+          if (lane_on) {
+            const float4* src = reinterpret_cast<const float4*>(a.ws_o + prow * hs + 8 * jj);
+            const float4 x0 = src[0], x1 = src[1];
+            y[k][0] = x0.x; y[k][1] = x0.y; y[k][2] = x0.z; y[k][3] = x0.w;
+            y[k][4] = x1.x; y[k][5] = x1.y; y[k][6] = x1.z; y[k][7] = x1.w;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) merge(mm[k], ll[k], y[k]);
+    }
+    // combine the NG copies (every lane of the wave takes part)
+#pragma unroll
+    for (int d = LP; d < kWave; d <<= 1) {
+      const float m2 = xor_lane_rt(M, d), l2 = xor_lane_rt(Ls, d);
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = xor_lane_rt(o[e], d);
+      merge(m2, l2, y);
+    }
+    const float inv_l = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= inv_l;
+    store_out_row(o, a.b, jj, sbits, inv_b, a.out + row * hs + 8 * jj, lane_on && grp == 0);
+  }
 }
 
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream) {
@@ -378,11 +381,18 @@ hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream) {
   const int LP = host_next_pow2(a.hs / 8);
-  const int64_t rows = a.num_q_tokens * a.nq;
-  const int64_t waves = (rows + (kWave / LP) - 1) / (kWave / LP);
-  const int64_t blocks = (waves + 3) / 4;
+  const int64_t rows = a.num_q_tokens * a.nq;       // one wave per row (grid-stride beyond 2^22 rows)
+  const int64_t blocks = std::min<int64_t>((rows + 3) / 4, (int64_t)1 << 20);
   dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
-  hipLaunchKernelGGL(attn_reduce_kernel, grid, block, 0, stream, a);
+  switch (LP) {
+    case 1: hipLaunchKernelGGL(attn_reduce_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(attn_reduce_kernel<2>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(attn_reduce_kernel<4>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(attn_reduce_kernel<8>, grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(attn_reduce_kernel<16>, grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL(attn_reduce_kernel<32>, grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -174,6 +174,27 @@ __device__ __forceinline__ float group_sum_ct(float v) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Largest i in [0, n - 1] with arr[i] <= key (0 if there is none), for a
+// non-decreasing arr and a wave-uniform key; every lane of the wave takes
+// part. Each round probes 64 evenly spaced entries at once, so n entries
+// take ceil(log64 n) dependent loads instead of log2 n. The result is
+// wave-uniform and always in [0, n - 1], whatever arr holds.
+__device__ __forceinline__ int wave_search_le(const int32_t* arr, int n, int64_t key) {
+  const int lane = (int)__lane_id();
+  int lo = 0, len = n;
+  while (len > 1) {
+    const int step = (len + kWave - 1) / kWave;
+    const int idx = lo + lane * step;
+    const bool le = idx < lo + len && (int64_t)arr[idx] <= key;
+    int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(le));
+    cnt = cnt < 1 ? 1 : cnt;
+    const int end = lo + len;
+    lo += (cnt - 1) * step;
+    len = step < end - lo ? step : end - lo;
+  }
+  return uniform(lo);
+}
+
 // Reductions over lanes l, l ^ 16 and l ^ 32 with the gfx950 permlane swaps
 // (full-rate VALU, no LDS round trip). With both operands equal, the swap
 // returns the value of lane l ^ 16 (resp. l ^ 32) in one of its two results.
