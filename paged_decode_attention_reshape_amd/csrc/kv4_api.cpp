@@ -62,10 +62,16 @@ long env_long(const char* name, long dflt) {
 constexpr int kRowsMax = 8;             // query rows per VALU wave
 constexpr int kMfmaRows = 16;           // query rows per MFMA tile
 constexpr int64_t kTargetUnitsValu = 2048;
-constexpr int64_t kTargetUnitsMfma = 32768;
+constexpr int64_t kTargetUnitsMfma = 16384;
 constexpr int kMinSplit = 256;
 
 bool mfma_head_size(int hs) { return hs == 64 || hs == 96 || hs == 128 || hs == 192; }
+
+// Largest number of kv heads one matrix-core wave serves at a head size: each
+// head adds a 2-slot LDS stage (about 8.7 KB at head size 128), and larger
+// stages cut the waves a CU holds below what hides the load latency
+// (measured: 4 at 128, 2 at 64 and 96, 1 at 192).
+int mfma_hpw_max(int hs) { return hs == 128 ? 4 : (hs == 192 ? 1 : 2); }
 
 // Host planner: depends only on host-known sizes (and the KV4_SPLIT_TOKENS /
 // KV4_FORCE_PATH overrides used by tests), so the workspace size and the
@@ -77,7 +83,10 @@ int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, i
   std::memset(&p, 0, sizeof(p));
   const int G = nq / nkv;
   const bool mfma_ok = mfma_head_size(hs) && block_size % 16 == 0 && (block_size & (block_size - 1)) == 0;
-  bool mfma = mfma_ok && (G > 1 || max_query_len > 1);
+  // Single-query decode with one query head per kv head (G = 1) still fills
+  // the matrix-core rows when one wave serves several kv heads.
+  const bool g1_multi = nkv % 2 == 0 && mfma_hpw_max(hs) >= 2;
+  bool mfma = mfma_ok && (G > 1 || max_query_len > 1 || g1_multi);
   if (const char* f = std::getenv("KV4_FORCE_PATH")) {
     if (!std::strcmp(f, "valu")) mfma = false;
     if (!std::strcmp(f, "mfma")) mfma = mfma_ok;
@@ -94,6 +103,15 @@ int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, i
     p.rows = rmax;
   }
   p.n_head_tiles = (G + p.gh - 1) / p.gh;
+  // Single-token decode on the matrix cores: one wave serves hpw kv heads
+  // (hpw * G <= 16 MFMA rows), sharing its softmax and page walk.
+  p.hpw = 1;
+  if (mfma && max_query_len <= 1) {
+    long want = env_long("KV4_MFMA_HPW", 0);
+    if (want != 1 && want != 2 && want != 4) want = mfma_hpw_max(hs);
+    while (want > 1 && (want * G > kMfmaRows || nkv % want != 0)) want >>= 1;
+    p.hpw = (int)want;
+  }
   const int mql = max_query_len < 1 ? 1 : max_query_len;
   p.tiles_per_seq = (mql + p.tq - 1) / p.tq;
   const int64_t uniform = (int64_t)num_seqs * p.tiles_per_seq;
@@ -105,7 +123,7 @@ int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, i
     p.packed_tiles = 1;
     p.n_qtiles = packed;
   }
-  const int64_t units = p.n_qtiles * p.n_head_tiles * nkv;
+  const int64_t units = p.n_qtiles * p.n_head_tiles * (nkv / p.hpw);   // waves per split
   if (units > INT32_MAX / 2) return fail(KV4_EUNSUPPORTED, "too many query tiles");
   const int msl = max_seq_len < 1 ? 1 : max_seq_len;
   long split = env_long("KV4_SPLIT_TOKENS", 0);
@@ -114,7 +132,7 @@ int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, i
       if (max_query_len > 1 && units >= 2048) {
         split = msl;                        // prefill tiles already fill the machine
       } else {
-        split = (long)((int64_t)msl * units / kTargetUnitsMfma);
+        split = (long)((int64_t)msl * units * p.hpw / kTargetUnitsMfma);
         if (split < kMinSplit) split = kMinSplit;
       }
     } else {
@@ -311,7 +329,8 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride, const voi
   a.out = static_cast<uint16_t*>(out);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.plan.path == 1) {
-    const int64_t max_units = a.plan.n_qtiles * a.plan.n_head_tiles * num_kv_heads * a.plan.num_splits;
+    const int64_t max_units =
+        a.plan.n_qtiles * a.plan.n_head_tiles * (num_kv_heads / a.plan.hpw) * a.plan.num_splits;
     if (int e = hip_status(kv4::launch_attn_mfma(a, prefix, max_units, st), "kv4_paged_attention launch"))
       return e;
   } else {

@@ -11,28 +11,32 @@
 // code_V_j, out = D.H.o'/b.
 //
 // gfx950 mapping. One wave = one work unit (sequence, query tile of up to 16
-// rows, kv head, KV split); a workgroup of 4 waves takes 4 consecutive units
-// (consecutive kv heads of the same pages when num_kv_heads >= 4, so their
-// 16-byte code rows share cache lines inside one CU). The KV range is walked
-// 32 tokens (two 16-token half tiles) per step:
+// rows, group of hpw kv heads, KV split); a workgroup takes consecutive units
+// (neighbouring kv heads of the same pages, whose code rows share cache lines
+// inside one CU). The KV range is walked 32 tokens (two 16-token half tiles)
+// per step, with the loads of the next step in flight (direct buffer->LDS
+// loads into two stage slots):
 //   * S^T = K . Q'^T on v_mfma_f32_16x16x32_bf16: A = K codes (16 tokens x 32
 //     head elements), B = q' rows (bf16). The head dimension is permuted so
 //     that a lane's 16 / 12 / 8 ... code bytes of one token are one vector
-//     load and feed all k-steps; q' is permuted the same way.
-//   * q' and p * v_scale enter as bf16 hi + lo pairs (two MFMAs each), so
-//     the products carry ~16 significant bits: sharp softmax rows (large
-//     k_scale from outlier channels) stay within 1e-2 of the fp64 result.
-//   * Codes become bf16 operands exactly, two per VALU op: (u & 0xF) |
-//     0x4300 is the bf16 of 128 + u with u = code + 8 (nibble xor 8). The
-//     constant 136 is removed after the product with the sum of q' (QK) and
-//     with the sum of p*v_scale (PV, obtained from one extra MFMA against a
-//     ones operand, so it sees exactly the rounded operands).
+//     load and feed all k-steps; q' is permuted the same way. q' enters as a
+//     bf16 hi + lo pair (two MFMAs), ~16 significant bits: sharp softmax rows
+//     (large k_scale from outlier channels) stay within 1e-2 of the fp64
+//     result.
+//   * K codes become bf16 operands exactly, two per VALU op: (u & 0xF) |
+//     0x4300 is the bf16 of 128 + u with u = code + 8 (nibble xor 8); the
+//     constant 136 is removed after the product with the sum of q'.
 //   * The S^T accumulator leaves each lane with 8 logits of ONE query row,
 //     which is exactly the B-operand layout P^T needs for O'^T = V^T P^T, so
 //     softmax runs in registers with no transpose; the V^T operand is built
 //     from 8 tokens' code words per lane (byte permutes + masks).
+//   * O'^T = V^T P^T on v_mfma_f32_16x16x32_f16: V codes become the fp16 of
+//     64 + u exactly; p * v_scale is one fp16 (11 significant bits) under a
+//     per-step power-of-two scale that bounds it (see the softmax step). The
+//     constant 72 is removed with the sum of the rounded P, taken by one
+//     extra MFMA against a ones operand.
 //   * k_scale / v_scale of the 32 tokens are loaded once per step (one lane
-//     per token) and redistributed through a 256-byte LDS slot per wave.
+//     per token) and redistributed through a 256-byte LDS slot per head.
 // Pages are looked up once per 16-token half tile (block_size % 16 == 0).
 #include "kv4_device.hpp"
 #include "kv4_launch.hpp"
@@ -41,6 +45,7 @@ namespace kv4 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -60,8 +65,27 @@ __device__ __forceinline__ uint4 k_operand(uint32_t w) {
   return make_uint4(nib2bf(w), nib2bf(w >> 4), nib2bf(w >> 8), nib2bf(w >> 12));
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4_t mfma_f16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Nibble pair -> fp16 pair: for the nibbles at bits 4-7 and 20-23 of x,
+// (nibble ^ 8) becomes mantissa bits 4-7 under the exponent of 64, i.e. the
+// fp16 of 64 + u with u = code + 8. One v_bitop3 (out = m ? x ^ k : k).
+__device__ __forceinline__ uint32_t nib2h(uint32_t x) {
+  return __builtin_amdgcn_bitop3_b32(x, 0x54805480u, 0x00F000F0u, 0x6C);
+}
+
+// Two floats -> fp16 pair, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Two floats as a bf16 pair hi (round to nearest even, v_cvt_pk_bf16_f32)
 // plus the bf16 pair of the remainders lo: hi + lo carries ~16 significant
@@ -137,10 +161,10 @@ struct Unit {
   int s, i0, qbeg, qlen, L, g, ht, sp;
 };
 
-// Dense unit index -> (sequence, tile, head tile, kv head, split); called by
-// all lanes of a wave with a wave-uniform u. prefix[s] is the first unit of
-// sequence s; unit order inside a sequence is kv head
-// fastest, then head tile, then split, then query tile.
+// Dense unit index -> (sequence, tile, head tile, kv head group, split);
+// called by all lanes of a wave with a wave-uniform u. prefix[s] is the first
+// unit of sequence s; unit order inside a sequence is kv head group (plan.hpw
+// consecutive kv heads) fastest, then head tile, then split, then query tile.
 __device__ __forceinline__ bool decode_unit(const AttnArgs& a, const int32_t* prefix, int u, Unit& un) {
   const int s = wave_search_le(prefix, a.num_seqs, u);
   int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
@@ -152,9 +176,10 @@ __device__ __forceinline__ bool decode_unit(const AttnArgs& a, const int32_t* pr
   const int split = a.plan.split_tokens;
   int nsp = (int)((L + split - 1) / split);
   nsp = nsp < 1 ? 1 : (nsp > a.plan.num_splits ? a.plan.num_splits : nsp);
+  const int n_hg = a.nkv / a.plan.hpw;
   int v = u - prefix[s];
-  un.g = v % a.nkv;
-  v /= a.nkv;
+  un.g = v % n_hg;
+  v /= n_hg;
   un.ht = v % a.plan.n_head_tiles;
   v /= a.plan.n_head_tiles;
   un.sp = v % nsp;
@@ -188,7 +213,7 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* pr
       int nsp = (int)((L + split - 1) / split);
       nsp = nsp < 1 ? 1 : (nsp > a.plan.num_splits ? a.plan.num_splits : nsp);
       const int ntile = (int)((qe - qb + a.plan.tq - 1) / a.plan.tq);
-      units = ntile * nsp * a.plan.n_head_tiles * a.nkv;
+      units = ntile * nsp * a.plan.n_head_tiles * (a.nkv / a.plan.hpw);
     }
     // inclusive scan inside the wave
     int x = units;
@@ -243,13 +268,17 @@ struct StageGeo {
 template <int HS>
 constexpr int stages_for() { return 2; }
 
-template <int HS>
+// Per wave: kStages stage slots, each holding HPW per-head stages (one per kv
+// head the wave serves); the q' staging buffer and the epilogue buffer
+// overlay them.
+template <int HS, int HPW>
 struct MfmaSmem {
-  static constexpr int STAGE = StageGeo<HS>::BYTES;
+  static constexpr int STAGE_H = StageGeo<HS>::BYTES;       // one kv head
+  static constexpr int STAGE = HPW * STAGE_H;               // one slot
   static constexpr int BUFB = 16 * HS * 4;                 // q' staging / epilogue (fp32 rows)
   static constexpr int NST = stages_for<HS>();
   static constexpr int MAINB = NST * STAGE > BUFB ? NST * STAGE : BUFB;
-  alignas(16) unsigned char main[MAINB];                   // stages overlay the q / epilogue buffer
+  alignas(16) unsigned char main[MAINB];
   float qsum[16];
 };
 
@@ -286,38 +315,64 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int HS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_mfma_kernel(AttnArgs a, const int32_t* prefix) {
+// Waves per workgroup and the occupancy each HPW is built for: the LDS of
+// HPW per-head stages per wave bounds the waves a CU can hold. WPE is the
+// register target (waves per SIMD); head size 192 at one head per wave fits
+// two waves (256 registers), not three.
+template <int HPW> struct MfmaShape;
+template <> struct MfmaShape<1> { static constexpr int WPB = 4, WPE = 3; };
+template <> struct MfmaShape<2> { static constexpr int WPB = 4, WPE = 2; };
+template <> struct MfmaShape<4> { static constexpr int WPB = 2, WPE = 1; };
+template <int HS, int HPW>
+constexpr int mfma_wpe() { return HPW == 1 && HS >= 192 ? 2 : MfmaShape<HPW>::WPE; }
+
+// HPW = kv heads per wave. HPW = 1: the 16 MFMA rows are the query tile of one
+// kv head (tq tokens x gh query heads). HPW > 1 (single-token decode): rows
+// r = hl * G + i are query head i of kv head kv0 + hl; each head keeps its own
+// QK and PV matrix-core products (rows of the other heads are dropped from S
+// and zeroed in P), while the softmax, the page walk and the address work are
+// shared by the HPW heads.
+template <int HS, int HPW>
+__global__ __launch_bounds__(64 * MfmaShape<HPW>::WPB)
+__attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(AttnArgs a, const int32_t* prefix) {
   using GG = Geo<HS>;
   using SG = StageGeo<HS>;
+  using SM = MfmaSmem<HS, HPW>;
+  constexpr int WPB = MfmaShape<HPW>::WPB;
   constexpr int NK = GG::NK, NS = GG::NS, NVR = GG::NVR;
   constexpr int LP = (HS / 8) <= 8 ? 8 : ((HS / 8) <= 16 ? 16 : 32);   // lanes per row, chunk mapping
   constexpr int RPP = kWave / LP;                                       // rows per pass
   constexpr int HALF = HS / 2;
   constexpr int kStages = stages_for<HS>();
-  __shared__ MfmaSmem<HS> smem_all[4];
+  constexpr int STH = SM::STAGE_H;
+  __shared__ SM smem_all[WPB];
 
   const int lane = threadIdx.x & 63;
-  const int wv = uniform(threadIdx.x >> 6);           // wave index (uniform: LDS bases in SGPRs)
-  MfmaSmem<HS>& sm = smem_all[wv];
+  const int wv = WPB == 1 ? 0 : uniform(threadIdx.x >> 6);   // wave index (uniform: LDS bases in SGPRs)
+  SM& sm = smem_all[wv];
   float* buf = reinterpret_cast<float*>(sm.main);
   const int n = lane & 15;          // MFMA column: query row of this lane
   const int q4 = lane >> 4;         // 0..3
   const int nkv = a.nkv;
+  const int n_hg = nkv / HPW;       // kv head groups
   const int G = a.nq / nkv;
   const int gh = a.plan.gh;
+  const int rph = HPW == 1 ? 16 : a.plan.tq * gh;   // MFMA rows per kv head
   const int split = a.plan.split_tokens;
   const int total = uniform(prefix[a.num_seqs]);
   const int bsz = a.bs;
   const int bs_log2 = __builtin_ctz((unsigned)bsz);      // the planner sends only power-of-two pages here
   const int bs_mask = bsz - 1;
   const float inv_b = 1.0f / (float)a.b;
-  // With num_kv_heads % 4 == 0 the 4 units of a workgroup are 4 kv heads of
-  // one (sequence, query tile, head tile, split): the waves take the same
-  // branches and run the same number of steps. A workgroup barrier per step
-  // then keeps the waves of neighbouring kv heads (two per 128-byte line)
-  // together, so each line comes from HBM once.
-  const bool wg_sync = (nkv & 3) == 0;
+  // One kv head per wave reads half of each 128-byte code line (64-byte rows
+  // at head size 128); the neighbouring head's wave reads the other half.
+  // With n_hg % WPB == 0 the units of a workgroup are WPB kv heads of one
+  // (sequence, query tile, head tile, split): the waves take the same
+  // branches and run the same number of steps, and a workgroup barrier per
+  // step keeps the two halves of each line together, so each line comes from
+  // HBM once. With two or more heads per wave a wave reads whole lines and
+  // runs free.
+  const bool wg_sync = HPW == 1 && (n_hg % WPB) == 0;
 
   // lane constants of the chunk mapping (q setup and epilogue)
   const int cj = lane & (LP - 1);
@@ -339,13 +394,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   const float* sc_base = lane < 32 ? a.k_scale : a.v_scale;
   const bool sc_half_b = (lane & 16) != 0;
 
+  // this lane's MFMA row n: kv head (within the group) and place in the tile
+  const int hl_n = n / rph;
+  const int rr_n = n - hl_n * rph;
+  const int ti_n = rr_n / gh, hi_n = rr_n - (rr_n / gh) * gh;
+  const uint32_t hoff_n = (uint32_t)(hl_n < HPW ? hl_n : 0) * STH;   // its head's per-head stage
+
   // Workgroups are dealt to the 8 XCDs round-robin (block b on XCD b % 8).
-  // Unit quads 2k and 2k + 1 (kv heads 0-3 and 4-7 of one sequence split,
-  // whose scale rows share 128-byte lines) go to blocks b and b + 8, which
-  // share an XCD and its L2.
+  // Unit blocks 2k and 2k + 1 (e.g. kv heads 0-3 and 4-7 of one sequence
+  // split, whose scale rows share 128-byte lines) go to blocks b and b + 8,
+  // which share an XCD and its L2.
   const int nbk = gridDim.x, bk = blockIdx.x;
   const int pbk = bk < (nbk & ~15) ? ((bk & ~15) | ((bk & 7) << 1) | ((bk >> 3) & 1)) : bk;
-  for (int u0 = pbk * 4; u0 < total; u0 += gridDim.x * 4) {
+  for (int u0 = pbk * WPB; u0 < total; u0 += gridDim.x * WPB) {
     const int u = u0 + wv;
     if (u >= total) continue;
     Unit un;
@@ -354,8 +415,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     const int us = uniform(un.s), ui0 = uniform(un.i0), uqbeg = uniform(un.qbeg);
     const int uqlen = uniform(un.qlen), uL = uniform(un.L), ug = uniform(un.g);
     const int uht = uniform(un.ht), usp = uniform(un.sp);
-    const int h0 = ug * G + uht * gh;
-    const int nh = min(gh, G - uht * gh);
+    const int kv0 = ug * HPW;                      // first kv head of this unit
+    const int hq0 = uht * gh;                      // first query head of the tile within a group
+    const int nh = min(gh, G - hq0);
     const int ntok = min(a.plan.tq, uqlen - ui0);
     const int pos0 = uL - uqlen + ui0;
     const int kend = pos0 + ntok;
@@ -386,12 +448,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 #pragma unroll
     for (int ps = 0; ps < 16 / RPP; ++ps) {
       const int r = ps * RPP + lane / LP;
-      const int ti = r / gh, hi = r - (r / gh) * gh;
-      const bool rv = ti < ntok && hi < nh;
+      const int hl = r / rph, rr = r - (r / rph) * rph;
+      const int ti = rr / gh, hi = rr - (rr / gh) * gh;
+      const bool rv = hl < HPW && ti < ntok && hi < nh;
       uint4 w = make_uint4(0u, 0u, 0u, 0u);
       if (rv && c_on)
         w = *reinterpret_cast<const uint4*>(a.query + (int64_t)(uqbeg + ui0 + ti) * a.q_stride +
-                                           (int64_t)(h0 + hi) * HS + 8 * cj);
+                                           (int64_t)((kv0 + hl) * G + hq0 + hi) * HS + 8 * cj);
       const uint32_t wd[4] = {w.x ^ sx[0], w.y ^ sx[1], w.z ^ sx[2], w.w ^ sx[3]};
       float v[8];
 #pragma unroll
@@ -424,8 +487,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       ql[s] = reinterpret_cast<const uint4*>(buf)[(16 * HS + n * HS + q4 * (HS / 4) + 8 * s) / 8];
     }
     const float qbias = 136.0f * sm.qsum[n];
-    const int ti_n = n / gh, hi_n = n - (n / gh) * gh;
-    const bool row_ok = ti_n < ntok && hi_n < nh;
+    const bool row_ok = hl_n < HPW && ti_n < ntok && hi_n < nh;
     const int rpos = row_ok ? pos0 + ti_n : -1;
     const float row_add = row_ok ? 0.0f : -INFINITY;    // invalid rows never get weight
     // the staged q' has been read into registers before the stages overwrite it
@@ -437,6 +499,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     for (int i = 0; i < NS; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     f32x4_t pacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
+    float e_run = -100.0f;   // running v_scale exponent (see the softmax step)
 
     int okmask = 0;   // bit 2*slot: half A page valid, bit 2*slot+1: half B (wave-uniform)
 
@@ -467,43 +530,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       const int offa = base & bs_mask;
       const int offb = b_in ? (base + 16) & bs_mask : offa;
       // byte offset of the first token row of each half tile inside a cache,
-      // and the scale index of that row (kv head ug)
-      const int64_t bya = (int64_t)pa * page_bytes + (int64_t)(offa * nkv + ug) * HALF;
-      const int64_t byb = (int64_t)pb * page_bytes + (int64_t)(offb * nkv + ug) * HALF;
-      int64_t rowa = (int64_t)pa * page_rows + offa * nkv + ug;
-      int64_t rowb = (int64_t)pb * page_rows + offb * nkv + ug;
+      // and the scale index of that row (first kv head of the unit); head hl
+      // of the unit sits hl * HALF bytes (hl scale entries) further on
+      const int64_t bya = (int64_t)pa * page_bytes + (int64_t)(offa * nkv + kv0) * HALF;
+      const int64_t byb = (int64_t)pb * page_bytes + (int64_t)(offb * nkv + kv0) * HALF;
+      int64_t rowa = (int64_t)pa * page_rows + offa * nkv + kv0;
+      int64_t rowb = (int64_t)pb * page_rows + offb * nkv + kv0;
       const uint32_t nrec = dummy ? 0u : half_bytes;
       if (dummy) { rowa = 0; rowb = 0; }   // scale rows 0..15 of page 0: lines every wave keeps hot
       const __amdgpu_buffer_rsrc_t rk[2] = {rsrc(a.key_cache + bya, nrec),
                                             rsrc(a.key_cache + byb, nrec)};
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < SG::NKL; ++j) {
-          unsigned char* dst = st + SG::K_OFF + h * SG::KHALF + j * SG::KREG;
-          if constexpr (SG::KSZ == 16) dma_buf<16>(rk[h], koff + j * SG::KSZ, dst);
-          else if constexpr (SG::KSZ == 12) dma_buf<12>(rk[h], koff + j * SG::KSZ, dst);
-          else dma_buf<4>(rk[h], koff + j * SG::KSZ, dst);
-        }
       const __amdgpu_buffer_rsrc_t rv[2] = {rsrc(a.value_cache + bya, nrec),
                                             rsrc(a.value_cache + byb, nrec)};
+      const float* scp = sc_base + (sc_half_b ? rowb : rowa) + soff;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        unsigned char* dst = st + SG::V_OFF + i * SG::VBYTES_TOK;
-        const uint32_t o = vo[i & 3];
+      for (int hl = 0; hl < HPW; ++hl) {
+        unsigned char* sth = st + hl * STH;
 #pragma unroll
-        for (int r = 0; r < GG::RDW; ++r) dma_buf<4>(rv[i >> 2], o + 64 * r, dst + r * 256);
-        if constexpr (GG::RUS) dma_buf<2>(rv[i >> 2], o - 2u * n + 64 * GG::RDW, dst + GG::RDW * 256);
-        if constexpr (GG::RBY)
-          dma_buf<1>(rv[i >> 2], o - 3u * n + 64 * GG::RDW + 32 * GG::RUS, dst + (GG::RDW + GG::RUS) * 256);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < SG::NKL; ++j) {
+            unsigned char* dst = sth + SG::K_OFF + h * SG::KHALF + j * SG::KREG;
+            const uint32_t o = koff + j * SG::KSZ + hl * HALF;
+            if constexpr (SG::KSZ == 16) dma_buf<16>(rk[h], o, dst);
+            else if constexpr (SG::KSZ == 12) dma_buf<12>(rk[h], o, dst);
+            else dma_buf<4>(rk[h], o, dst);
+          }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          unsigned char* dst = sth + SG::V_OFF + i * SG::VBYTES_TOK;
+          const uint32_t o = vo[i & 3] + hl * HALF;
+#pragma unroll
+          for (int r = 0; r < GG::RDW; ++r) dma_buf<4>(rv[i >> 2], o + 64 * r, dst + r * 256);
+          if constexpr (GG::RUS) dma_buf<2>(rv[i >> 2], o - 2u * n + 64 * GG::RDW, dst + GG::RDW * 256);
+          if constexpr (GG::RBY)
+            dma_buf<1>(rv[i >> 2], o - 3u * n + 64 * GG::RDW + 32 * GG::RUS, dst + (GG::RDW + GG::RUS) * 256);
+        }
+        dma(scp + hl, sth + SG::S_OFF, 4);
       }
-      dma(sc_base + (sc_half_b ? rowb : rowa) + soff, st + SG::S_OFF, 4);
     };
 
     if (wg_sync) __builtin_amdgcn_s_barrier();
     if (nsteps > 0) {
 #pragma unroll
-      for (int i = 0; i < kStages - 1; ++i) issue(sm.main + i * SG::BYTES, i);
+      for (int i = 0; i < kStages - 1; ++i) issue(sm.main + i * SM::STAGE, i);
     }
     // `st` (read) and `wr` (filled for step it + kStages - 1) are distinct slots;
     // the restrict qualifiers let the compiler keep the lookahead loads in
@@ -511,50 +581,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     auto step = [&](const unsigned char* __restrict__ st, unsigned char* __restrict__ wr, int it) {
       const int slot = it % kStages;
       const int base = k0 + 32 * it;
-      wait_vm<(kStages - 2) * SG::LOADS>();   // step `it` landed; later steps may be in flight
+      wait_vm<0>();                           // step `it` landed (the loads of step it + 1 go out below)
       if (wg_sync) __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       issue(wr, it + kStages - 1);            // into the slot step it - 1 used
       const bool oka = (okmask >> (2 * slot)) & 1, okb = (okmask >> (2 * slot + 1)) & 1;
 
-      // K code words of this lane: token n, chunk q4, both half tiles
-      uint32_t kw[2][NK];
+      // S^T = K . Q'^T per kv head, both half tiles (q' as hi + lo); lane n
+      // keeps the logits of its own row's head
+      float s8[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const unsigned char* kr = st + SG::K_OFF + h * SG::KHALF;
-        if constexpr (NK == 4) {
-          const uint4 x = *reinterpret_cast<const uint4*>(kr + 16 * lane);
-          kw[h][0] = x.x; kw[h][1] = x.y; kw[h][2] = x.z; kw[h][3] = x.w;
-        } else if constexpr (NK == 3 || NK == 6) {
+      for (int hl = 0; hl < HPW; ++hl) {
+        // K code words of this lane: token n, chunk q4, both half tiles
+        uint32_t kw[2][NK];
 #pragma unroll
-          for (int j = 0; j < NK / 3; ++j) {
-            const uint32_t* x = reinterpret_cast<const uint32_t*>(kr + j * SG::KREG + 16 * lane);
-            kw[h][3 * j] = x[0]; kw[h][3 * j + 1] = x[1]; kw[h][3 * j + 2] = x[2];
+        for (int h = 0; h < 2; ++h) {
+          const unsigned char* kr = st + hl * STH + SG::K_OFF + h * SG::KHALF;
+          if constexpr (NK == 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(kr + 16 * lane);
+            kw[h][0] = x.x; kw[h][1] = x.y; kw[h][2] = x.z; kw[h][3] = x.w;
+          } else if constexpr (NK == 3 || NK == 6) {
+#pragma unroll
+            for (int j = 0; j < NK / 3; ++j) {
+              const uint32_t* x = reinterpret_cast<const uint32_t*>(kr + j * SG::KREG + 16 * lane);
+              kw[h][3 * j] = x[0]; kw[h][3 * j + 1] = x[1]; kw[h][3 * j + 2] = x[2];
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NK; ++j) kw[h][j] = reinterpret_cast<const uint32_t*>(kr + j * 256)[lane];
           }
-        } else {
+        }
+        f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < NK; ++j) kw[h][j] = reinterpret_cast<const uint32_t*>(kr + j * 256)[lane];
+        for (int s = 0; s < NK; ++s) {
+          const uint4 ka = k_operand(kw[0][s]), kb = k_operand(kw[1][s]);
+          sa = mfma_bf16(ka, qh[s], sa);
+          sb = mfma_bf16(kb, qh[s], sb);
+          sa = mfma_bf16(ka, ql[s], sa);
+          sb = mfma_bf16(kb, ql[s], sb);
+          if constexpr (HPW == 1) __builtin_amdgcn_sched_barrier(0);   // one k-step's operands live at a time
+        }
+        if (hl == 0 || hl == hl_n) {
+          s8[0] = sa[0]; s8[1] = sa[1]; s8[2] = sa[2]; s8[3] = sa[3];
+          s8[4] = sb[0]; s8[5] = sb[1]; s8[6] = sb[2]; s8[7] = sb[3];
         }
       }
-      // S^T for both half tiles (q' as hi + lo)
-      f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NK; ++s) {
-        const uint4 ka = k_operand(kw[0][s]), kb = k_operand(kw[1][s]);
-        sa = mfma_bf16(ka, qh[s], sa);
-        sb = mfma_bf16(kb, qh[s], sb);
-        sa = mfma_bf16(ka, ql[s], sa);
-        sb = mfma_bf16(kb, ql[s], sb);
-        __builtin_amdgcn_sched_barrier(0);   // keep one k-step's operands live at a time
-      }
-      const float* scl = reinterpret_cast<const float*>(st + SG::S_OFF);
+      const float* scl = reinterpret_cast<const float*>(st + hoff_n + SG::S_OFF);
       const float4 ksa = *reinterpret_cast<const float4*>(&scl[4 * q4]);
       const float4 ksb = *reinterpret_cast<const float4*>(&scl[16 + 4 * q4]);
       const float4 vsa = *reinterpret_cast<const float4*>(&scl[32 + 4 * q4]);
       const float4 vsb = *reinterpret_cast<const float4*>(&scl[48 + 4 * q4]);
       const float ks8[8] = {ksa.x, ksa.y, ksa.z, ksa.w, ksb.x, ksb.y, ksb.z, ksb.w};
       const float vs8[8] = {vsa.x, vsa.y, vsa.z, vsa.w, vsb.x, vsb.y, vsb.z, vsb.w};
-      const float s8[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
       float lg[8];
       const bool full = base + 32 <= k1 && base + 31 <= pos0 && oka && okb;   // wave-uniform
       if (full) {
@@ -571,20 +649,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),
                        fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
       mx = max_x16_x32(mx);
+      // p * v_scale enters the matrix cores as one fp16. A power of two 2^-e,
+      // e = (exponent of the step's largest v_scale) - 11 kept as a running
+      // maximum, holds it below 2^12 and clear of fp16 subnormals; acc, pacc
+      // and l all carry the scale 2^-(m + e), m the running logit maximum.
+      float vmx = fmaxf(fmaxf(fmaxf(vs8[0], vs8[1]), fmaxf(vs8[2], vs8[3])),
+                        fmaxf(fmaxf(vs8[4], vs8[5]), fmaxf(vs8[6], vs8[7])));
+      vmx = max_x16_x32(vmx);
+      const float e_step = fmaxf((float)((int)((__float_as_uint(vmx) >> 23) & 0xFFu) - 138), -100.0f);
+      const float e_new = fmaxf(e_run, e_step);
       const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float big_m = (m_new == -INFINITY ? 0.0f : m_new) + e_new;
       // a row that has seen no key yet has nothing to rescale
-      const float alpha = m_run == -INFINITY ? 1.0f : fast_exp2(m_run - m_use);
+      const float alpha = m_run == -INFINITY ? 1.0f : fast_exp2(m_run + e_run - big_m);
       float psum_l = 0.0f;
-      uint32_t pw[4], pl[4];
+      uint32_t pw[4];
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
-        const float p0 = fast_exp2(lg[i] - m_use), p1 = fast_exp2(lg[i + 1] - m_use);
+        const float p0 = fast_exp2(lg[i] - big_m), p1 = fast_exp2(lg[i + 1] - big_m);
         psum_l += p0 + p1;
-        split_bf16x2(p0 * vs8[i], p1 * vs8[i + 1], pw[i / 2], pl[i / 2]);
+        pw[i / 2] = pack_f16x2(p0 * vs8[i], p1 * vs8[i + 1]);
       }
       const uint4 ph4 = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-      const uint4 pl4 = make_uint4(pl[0], pl[1], pl[2], pl[3]);
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
         for (int i = 0; i < NS; ++i) acc[i] *= alpha;
@@ -592,52 +678,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       }
       l_run = l_run * alpha + psum_l;
       m_run = m_new;
+      e_run = e_new;
 
-      // O'^T += V^T P^T, one n-step per V column of this lane's chunks
-      int ns = 0;
+      // O'^T += V^T P^T per kv head, one n-step per V column of this lane's
+      // chunks; P^T is zero in the rows of the other heads
 #pragma unroll
-      for (int r = 0; r < NVR; ++r) {
-        int w, cb;
-        v_region<HS>(r, w, cb);
-        uint32_t x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const unsigned char* src = st + SG::V_OFF + i * SG::VBYTES_TOK;
-          // sub-dword regions hold zero-extended words; their unused
-          // nibbles are never selected below
-          x[i] = reinterpret_cast<const uint32_t*>(src + r * 256)[lane];
+      for (int hl = 0; hl < HPW; ++hl) {
+        uint4 phh = ph4;
+        if constexpr (HPW > 1) {
+          const bool mine = hl == hl_n;
+          phh = make_uint4(mine ? ph4.x : 0u, mine ? ph4.y : 0u, mine ? ph4.z : 0u, mine ? ph4.w : 0u);
         }
+        int ns = 0;
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-          if (2 * jb >= w) break;
-          const uint32_t t01 = pair_byte(x[0], x[1], jb);
-          const uint32_t t23 = pair_byte(x[2], x[3], jb);
-          const uint32_t t45 = pair_byte(x[4], x[5], jb);
-          const uint32_t t67 = pair_byte(x[6], x[7], jb);
-          const uint4 lo = make_uint4(nib2bf(t01), nib2bf(t23), nib2bf(t45), nib2bf(t67));
-          const uint4 hi = make_uint4(nib2bf(t01 >> 4), nib2bf(t23 >> 4), nib2bf(t45 >> 4), nib2bf(t67 >> 4));
-          acc[ns] = mfma_bf16(lo, ph4, acc[ns]);
-          acc[ns + 1] = mfma_bf16(hi, ph4, acc[ns + 1]);
-          acc[ns] = mfma_bf16(lo, pl4, acc[ns]);
-          acc[ns + 1] = mfma_bf16(hi, pl4, acc[ns + 1]);
-          ns += 2;
-          __builtin_amdgcn_sched_barrier(0);
+        for (int r = 0; r < NVR; ++r) {
+          int w, cb;
+          v_region<HS>(r, w, cb);
+          uint32_t x[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const unsigned char* src = st + hl * STH + SG::V_OFF + i * SG::VBYTES_TOK;
+            // sub-dword regions hold zero-extended words; their unused
+            // nibbles are never selected below
+            x[i] = reinterpret_cast<const uint32_t*>(src + r * 256)[lane];
+          }
+#pragma unroll
+          for (int jb = 0; jb < 4; ++jb) {
+            if (2 * jb >= w) break;
+            const uint32_t t01 = pair_byte(x[0], x[1], jb);
+            const uint32_t t23 = pair_byte(x[2], x[3], jb);
+            const uint32_t t45 = pair_byte(x[4], x[5], jb);
+            const uint32_t t67 = pair_byte(x[6], x[7], jb);
+            // low nibbles (column 2 jb) moved up to bits 4-7; high nibbles in place
+            const uint4 lo = make_uint4(nib2h(t01 << 4), nib2h(t23 << 4), nib2h(t45 << 4), nib2h(t67 << 4));
+            const uint4 hi = make_uint4(nib2h(t01), nib2h(t23), nib2h(t45), nib2h(t67));
+            acc[ns] = mfma_f16(lo, phh, acc[ns]);
+            acc[ns + 1] = mfma_f16(hi, phh, acc[ns + 1]);
+            ns += 2;
+            if constexpr (HPW == 1) __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
-      const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-      pacc = mfma_bf16(ones, ph4, pacc);
-      pacc = mfma_bf16(ones, pl4, pacc);
+      const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);   // fp16 1.0
+      pacc = mfma_f16(ones, ph4, pacc);
     };
     for (int it = 0; it < nsteps; ++it)
-      step(sm.main + (it % kStages) * SG::BYTES, sm.main + ((it + kStages - 1) % kStages) * SG::BYTES, it);
+      step(sm.main + (it % kStages) * SM::STAGE, sm.main + ((it + kStages - 1) % kStages) * SM::STAGE, it);
     wait_vm<0>();                             // no load may land in LDS after this point
     __builtin_amdgcn_wave_barrier();
 
-    // ---- finish: l over the four lane quarters, remove the +136 offset
+    // ---- finish: l over the four lane quarters, remove the +72 offset of the
+    // fp16 V operands (64 + u = 72 + code)
     l_run = sum_x16_x32(l_run);
-    const float pbias = 136.0f * pacc[0];
+    const float pbias = 72.0f * pacc[0];
     const int qrow = uqbeg + ui0 + ti_n;
-    const int h = h0 + hi_n;
+    const int h = (kv0 + hl_n) * G + hq0 + hi_n;
     if (a.plan.num_splits > 1) {
       if (row_ok) {
         const int64_t prow = ((int64_t)usp * a.num_q_tokens + qrow) * a.nq + h;
@@ -665,7 +760,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
           ns += w;
         }
         if (q4 == 0) {
-          a.ws_ml[2 * prow] = m_run;
+          a.ws_ml[2 * prow] = m_run + e_run;   // the scale exponent of this partial
           a.ws_ml[2 * prow + 1] = l_run;
         }
       }
@@ -694,8 +789,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 #pragma unroll
     for (int ps = 0; ps < 16 / RPP; ++ps) {
       const int r = ps * RPP + lane / LP;
-      const int ti = r / gh, hi = r - (r / gh) * gh;
-      const bool rv = ti < ntok && hi < nh;
+      const int hl = r / rph, rr = r - (r / rph) * rph;
+      const int ti = rr / gh, hi = rr - (rr / gh) * gh;
+      const bool rv = hl < HPW && ti < ntok && hi < nh;
       float o[8];
       if (c_on) {
         const float4 x0 = reinterpret_cast<const float4*>(buf)[(r * HS + 8 * cj) / 4];
@@ -715,7 +811,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         wo.y = pack_bf16x2(o[2], o[3]);
         wo.z = pack_bf16x2(o[4], o[5]);
         wo.w = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<uint4*>(a.out + ((int64_t)(uqbeg + ui0 + ti) * a.nq + h0 + hi) * HS + 8 * cj) = wo;
+        *reinterpret_cast<uint4*>(a.out + ((int64_t)(uqbeg + ui0 + ti) * a.nq + (kv0 + hl) * G + hq0 + hi) * HS +
+                                  8 * cj) = wo;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -723,6 +820,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 }
 
 static int g_num_cus = 0;
+
+template <int HS>
+static void launch_hs(const AttnArgs& a, const int32_t* prefix, int64_t max_units, hipStream_t stream) {
+  auto go = [&](auto kernel, int wpb) {
+    int64_t wgs = (max_units + wpb - 1) / wpb;
+    const int64_t cap = (int64_t)g_num_cus * 8;
+    if (wgs > cap) wgs = cap;
+    if (wgs < 1) wgs = 1;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(64 * wpb), 0, stream, a, prefix);
+  };
+  switch (a.plan.hpw) {
+    case 2: go(attn_mfma_kernel<HS, 2>, MfmaShape<2>::WPB); break;
+    case 4: go(attn_mfma_kernel<HS, 4>, MfmaShape<4>::WPB); break;
+    default: go(attn_mfma_kernel<HS, 1>, MfmaShape<1>::WPB); break;
+  }
+}
 
 hipError_t launch_attn_mfma(const AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream) {
   hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a, prefix);
@@ -736,16 +849,11 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int32_t* prefix, int64_t max_unit
     else
       g_num_cus = 256;
   }
-  int64_t wgs = (max_units + 3) / 4;
-  const int64_t cap = (int64_t)g_num_cus * 8;
-  if (wgs > cap) wgs = cap;
-  if (wgs < 1) wgs = 1;
-  dim3 grid((unsigned)wgs), block(256);
   switch (a.hs) {
-    case 64: hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, block, 0, stream, a, prefix); break;
-    case 96: hipLaunchKernelGGL(attn_mfma_kernel<96>, grid, block, 0, stream, a, prefix); break;
-    case 128: hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, block, 0, stream, a, prefix); break;
-    case 192: hipLaunchKernelGGL(attn_mfma_kernel<192>, grid, block, 0, stream, a, prefix); break;
+    case 64: launch_hs<64>(a, prefix, max_units, stream); break;
+    case 96: launch_hs<96>(a, prefix, max_units, stream); break;
+    case 128: launch_hs<128>(a, prefix, max_units, stream); break;
+    case 192: launch_hs<192>(a, prefix, max_units, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -60,6 +60,7 @@ struct AttnPlan {
   int tiles_per_seq;   // uniform mode: tiles per sequence
   int split_tokens;    // KV tokens per split
   int num_splits;      // splits in the grid (1 = no partials)
+  int hpw;             // MFMA path: kv heads per wave (1, 2 or 4; > 1 only for single-token decode)
 };
 
 struct AttnArgs {

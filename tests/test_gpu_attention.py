@@ -105,6 +105,34 @@ def test_attention_forced_splits_match(split, path, monkeypatch):
     _g2(r)
 
 
+HPW_CASES = [
+    # single-token decode shapes where one wave can serve several kv heads
+    ("g4_nkv8_hs128", 32, 8, 128, [1] * 5, [1000, 17, 300, 2049, 64], 16),
+    ("g2_nkv4_hs64", 8, 4, 64, [1] * 4, [513, 1, 64, 700], 16),
+    ("g1_nkv8_hs96", 8, 8, 96, [1] * 3, [96, 400, 33], 16),
+    ("g8_nkv2_hs128", 16, 2, 128, [1] * 3, [250, 16, 1100], 32),
+    ("g4_nkv4_hs192", 16, 4, 192, [1] * 2, [333, 640], 16),
+    ("g4_nkv8_empty_rows", 32, 8, 128, [0, 1, 0, 1], [10, 300, 5, 47], 16),
+]
+
+
+@pytest.mark.parametrize("split", ["auto", "64"])
+@pytest.mark.parametrize("hpw", ["1", "2", "4"])
+@pytest.mark.parametrize("case", HPW_CASES, ids=[c[0] for c in HPW_CASES])
+def test_attention_heads_per_wave(case, hpw, split, monkeypatch):
+    """The matrix-core kernel with 1, 2 and 4 kv heads per wave (the planner
+    lowers the request where G * hpw > 16 or hpw does not divide the kv
+    heads), with and without forced KV splits."""
+    monkeypatch.setenv("KV4_FORCE_PATH", "mfma")
+    monkeypatch.setenv("KV4_MFMA_HPW", hpw)
+    if split != "auto":
+        monkeypatch.setenv("KV4_SPLIT_TOKENS", split)
+    name, nq, nkv, hs, ql, sl, bs = case
+    w = W.custom(name, nq, nkv, hs, ql, sl, block_size=bs)
+    r = run_gpu(w)
+    _g2(r)
+
+
 def test_query_longer_than_context_gives_zero_rows():
     """seq_len < query_len: rows whose causal window is empty come out as 0;
     the others attend normally."""
