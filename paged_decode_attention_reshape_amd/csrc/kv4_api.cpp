@@ -67,11 +67,11 @@ constexpr int kMinSplit = 256;
 
 bool mfma_head_size(int hs) { return hs == 64 || hs == 96 || hs == 128 || hs == 192; }
 
-// Largest number of kv heads one matrix-core wave serves at a head size: each
-// head adds a 2-slot LDS stage (about 8.7 KB at head size 128), and larger
-// stages cut the waves a CU holds below what hides the load latency
-// (measured: 4 at 128, 2 at 64 and 96, 1 at 192).
-int mfma_hpw_max(int hs) { return hs == 128 ? 4 : (hs == 192 ? 1 : 2); }
+// Kv heads one matrix-core wave serves by default at a head size: each head
+// adds a 2-slot LDS stage (about 8.7 KB at head size 128), and larger stages
+// cut the waves a CU holds below what hides the load latency (measured best:
+// 2 at 64, 96 and 128; 1 at 192).
+int mfma_hpw_max(int hs) { return hs == 192 ? 1 : 2; }
 
 // Host planner: depends only on host-known sizes (and the KV4_SPLIT_TOKENS /
 // KV4_FORCE_PATH overrides used by tests), so the workspace size and the
@@ -109,6 +109,7 @@ int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, i
   if (mfma && max_query_len <= 1) {
     long want = env_long("KV4_MFMA_HPW", 0);
     if (want != 1 && want != 2 && want != 4) want = mfma_hpw_max(hs);
+    if (want > 2 && (hs == 96 || hs == 192)) want = 2;   // four heads' V loads would exceed the load counter
     while (want > 1 && (want * G > kMfmaRows || nkv % want != 0)) want >>= 1;
     p.hpw = (int)want;
   }

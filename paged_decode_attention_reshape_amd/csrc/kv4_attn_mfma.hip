@@ -257,7 +257,6 @@ struct StageGeo {
   static constexpr int V_OFF = 2 * KHALF;
   static constexpr int S_OFF = V_OFF + 8 * VBYTES_TOK;
   static constexpr int BYTES = S_OFF + 256;
-  static constexpr int LOADS = 2 * NKL + 8 * Geo<HS>::NVR + 1;   // VMEM instructions per step
 };
 
 // stage slots per wave: loads run kStages - 1 steps ahead of the compute
@@ -503,10 +502,17 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
 
     int okmask = 0;   // bit 2*slot: half A page valid, bit 2*slot+1: half B (wave-uniform)
 
-    // issue the loads of step `it` into stage slot `it % kStages`; steps past
-    // the end issue loads with an empty buffer range (they fetch nothing and
-    // fill the slot with zeros, which is never read)
-    auto issue = [&](unsigned char* __restrict__ st, int it) {
+    // Loads of step `it` into stage slot `it % kStages`, in two groups: K
+    // codes + both scales (issue_k, which also looks the pages up), then V
+    // codes (issue_v, from the bases issue_k left). Steps past the end issue
+    // loads with an empty buffer range (they fetch nothing and fill the slot
+    // with zeros, which is never read).
+    constexpr int NLK = HPW * (2 * SG::NKL + 1);   // loads per issue_k
+    constexpr int NLV = HPW * 8 * NVR;             // loads per issue_v
+    static_assert(NLK < 64 && NLV < 64, "vmcnt range");
+    int64_t v_bya = 0, v_byb = 0;
+    uint32_t v_nrec = 0;
+    auto issue_k = [&](unsigned char* __restrict__ st, int it) {
       const int slot = it % kStages;
       const bool dummy = it >= nsteps;
       const int base = k0 + 32 * (it < nsteps ? it : 0);
@@ -538,10 +544,11 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
       int64_t rowb = (int64_t)pb * page_rows + offb * nkv + kv0;
       const uint32_t nrec = dummy ? 0u : half_bytes;
       if (dummy) { rowa = 0; rowb = 0; }   // scale rows 0..15 of page 0: lines every wave keeps hot
+      v_bya = bya;
+      v_byb = byb;
+      v_nrec = nrec;
       const __amdgpu_buffer_rsrc_t rk[2] = {rsrc(a.key_cache + bya, nrec),
                                             rsrc(a.key_cache + byb, nrec)};
-      const __amdgpu_buffer_rsrc_t rv[2] = {rsrc(a.value_cache + bya, nrec),
-                                            rsrc(a.value_cache + byb, nrec)};
       const float* scp = sc_base + (sc_half_b ? rowb : rowa) + soff;
 #pragma unroll
       for (int hl = 0; hl < HPW; ++hl) {
@@ -556,6 +563,15 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
             else if constexpr (SG::KSZ == 12) dma_buf<12>(rk[h], o, dst);
             else dma_buf<4>(rk[h], o, dst);
           }
+        dma(scp + hl, sth + SG::S_OFF, 4);
+      }
+    };
+    auto issue_v = [&](unsigned char* __restrict__ st) {
+      const __amdgpu_buffer_rsrc_t rv[2] = {rsrc(a.value_cache + v_bya, v_nrec),
+                                            rsrc(a.value_cache + v_byb, v_nrec)};
+#pragma unroll
+      for (int hl = 0; hl < HPW; ++hl) {
+        unsigned char* sth = st + hl * STH;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           unsigned char* dst = sth + SG::V_OFF + i * SG::VBYTES_TOK;
@@ -566,25 +582,26 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
           if constexpr (GG::RBY)
             dma_buf<1>(rv[i >> 2], o - 3u * n + 64 * GG::RDW + 32 * GG::RUS, dst + (GG::RDW + GG::RUS) * 256);
         }
-        dma(scp + hl, sth + SG::S_OFF, 4);
       }
     };
 
     if (wg_sync) __builtin_amdgcn_s_barrier();
     if (nsteps > 0) {
-#pragma unroll
-      for (int i = 0; i < kStages - 1; ++i) issue(sm.main + i * SM::STAGE, i);
+      issue_k(sm.main, 0);
+      issue_v(sm.main);
     }
-    // `st` (read) and `wr` (filled for step it + kStages - 1) are distinct slots;
-    // the restrict qualifiers let the compiler keep the lookahead loads in
-    // flight across the reads of the current step.
+    static_assert(kStages == 2, "one step of lookahead");
+    // `st` (read) and `wr` (filled for step it + 1) are distinct slots; the
+    // restrict qualifiers let the compiler keep the lookahead loads in flight
+    // across the reads of the current step. Outstanding loads at the start of
+    // step it, oldest first: K(it), V(it).
     auto step = [&](const unsigned char* __restrict__ st, unsigned char* __restrict__ wr, int it) {
       const int slot = it % kStages;
       const int base = k0 + 32 * it;
-      wait_vm<0>();                           // step `it` landed (the loads of step it + 1 go out below)
+      wait_vm<NLV>();                         // K and scales of step it landed; V(it) may be in flight
       if (wg_sync) __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      issue(wr, it + kStages - 1);            // into the slot step it - 1 used
+      issue_k(wr, it + 1);                    // into the slot step it - 1 used
       const bool oka = (okmask >> (2 * slot)) & 1, okb = (okmask >> (2 * slot + 1)) & 1;
 
       // S^T = K . Q'^T per kv head, both half tiles (q' as hi + lo); lane n
@@ -680,6 +697,10 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
       m_run = m_new;
       e_run = e_new;
 
+      wait_vm<NLK>();                         // V(it) landed; K(it + 1) may be in flight
+      __builtin_amdgcn_sched_barrier(0);
+      issue_v(wr);
+
       // O'^T += V^T P^T per kv head, one n-step per V column of this lane's
       // chunks; P^T is zero in the rows of the other heads
 #pragma unroll
@@ -723,7 +744,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
       pacc = mfma_f16(ones, ph4, pacc);
     };
     for (int it = 0; it < nsteps; ++it)
-      step(sm.main + (it % kStages) * SM::STAGE, sm.main + ((it + kStages - 1) % kStages) * SM::STAGE, it);
+      step(sm.main + (it % kStages) * SM::STAGE, sm.main + ((it + 1) % kStages) * SM::STAGE, it);
     wait_vm<0>();                             // no load may land in LDS after this point
     __builtin_amdgcn_wave_barrier();
 
@@ -822,7 +843,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
 static int g_num_cus = 0;
 
 template <int HS>
-static void launch_hs(const AttnArgs& a, const int32_t* prefix, int64_t max_units, hipStream_t stream) {
+static hipError_t launch_hs(const AttnArgs& a, const int32_t* prefix, int64_t max_units, hipStream_t stream) {
+  if (a.plan.hpw == 4 && Geo<HS>::NVR != 1) return hipErrorInvalidValue;
   auto go = [&](auto kernel, int wpb) {
     int64_t wgs = (max_units + wpb - 1) / wpb;
     const int64_t cap = (int64_t)g_num_cus * 8;
@@ -832,9 +854,13 @@ static void launch_hs(const AttnArgs& a, const int32_t* prefix, int64_t max_unit
   };
   switch (a.plan.hpw) {
     case 2: go(attn_mfma_kernel<HS, 2>, MfmaShape<2>::WPB); break;
-    case 4: go(attn_mfma_kernel<HS, 4>, MfmaShape<4>::WPB); break;
+    case 4:
+      // four heads' V loads of a step must fit the 6-bit load counter
+      if constexpr (Geo<HS>::NVR == 1) go(attn_mfma_kernel<HS, 4>, MfmaShape<4>::WPB);
+      break;
     default: go(attn_mfma_kernel<HS, 1>, MfmaShape<1>::WPB); break;
   }
+  return hipSuccess;
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream) {
@@ -850,12 +876,13 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int32_t* prefix, int64_t max_unit
       g_num_cus = 256;
   }
   switch (a.hs) {
-    case 64: launch_hs<64>(a, prefix, max_units, stream); break;
-    case 96: launch_hs<96>(a, prefix, max_units, stream); break;
-    case 128: launch_hs<128>(a, prefix, max_units, stream); break;
-    case 192: launch_hs<192>(a, prefix, max_units, stream); break;
+    case 64: e = launch_hs<64>(a, prefix, max_units, stream); break;
+    case 96: e = launch_hs<96>(a, prefix, max_units, stream); break;
+    case 128: e = launch_hs<128>(a, prefix, max_units, stream); break;
+    case 192: e = launch_hs<192>(a, prefix, max_units, stream); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
