@@ -389,6 +389,25 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
   uint32_t vo[4];                                           // token 4*q4 + i, 32-bit column chunk n
 #pragma unroll
   for (int i = 0; i < 4; ++i) vo[i] = (uint32_t)(4 * q4 + i) * tok_stride + 4u * (uint32_t)n;
+  // Joint V layout (VJ): where the wave's heads make a 64- or 128-byte token
+  // row, V comes in with 16-byte lanes and lands token-major in LDS (row
+  // after row, RB bytes each, 1 KB per load). Lane l of a load fetches bytes
+  // [16 l % RB, +16) of token row 16 l / RB.
+  constexpr int RB = HPW * HALF;                            // V bytes per token row of the wave
+  constexpr bool VJ = RB == 64 || RB == 128;
+  constexpr int RPI = 1024 / RB;                            // token rows per 1 KB load (VJ)
+  const uint32_t vj_src = (uint32_t)((16 * lane) / RB) * tok_stride + (uint32_t)((16 * lane) % RB);
+  // ... and lane (n, q4) reads, for token 4 q4 + i of a half tile, its column
+  // chunk n of head hl at vj_rd[i] + hl * HALF: 4 bytes (8 columns, head
+  // size 128) or 2 bytes (4 columns, head size 64); each 16-lane quarter
+  // reads 64 (32) contiguous bytes of one row, so no two of its lanes share
+  // an LDS bank.
+  uint32_t vj_rd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 4 * q4 + i;
+    vj_rd[i] = (uint32_t)((t / RPI) * 1024 + (t % RPI) * RB) + (HS >= 128 ? 4u : 2u) * (uint32_t)n;
+  }
   const uint32_t soff = (uint32_t)(lane & 15) * (uint32_t)nkv;   // scale elements
   const float* sc_base = lane < 32 ? a.k_scale : a.v_scale;
   const bool sc_half_b = (lane & 16) != 0;
@@ -508,7 +527,10 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
     // loads with an empty buffer range (they fetch nothing and fill the slot
     // with zeros, which is never read).
     constexpr int NLK = HPW * (2 * SG::NKL + 1);   // loads per issue_k
-    constexpr int NLV = HPW * 8 * NVR;             // loads per issue_v
+    constexpr int NLV = VJ ? 2 * (16 / RPI) : HPW * 8 * NVR;   // loads per issue_v
+    // VJ: half tile hh of a slot (16 * RB bytes) sits in head hh's V region
+    // (2 KB; RB = 128, two or more heads per wave) or at V_OFF + hh KB (RB = 64)
+    auto vj_base = [&](auto* st, int hh) { return st + (RB == 128 ? hh * STH : hh * 1024) + SG::V_OFF; };
     static_assert(NLK < 64 && NLV < 64, "vmcnt range");
     int64_t v_bya = 0, v_byb = 0;
     uint32_t v_nrec = 0;
@@ -569,6 +591,14 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
     auto issue_v = [&](unsigned char* __restrict__ st) {
       const __amdgpu_buffer_rsrc_t rv[2] = {rsrc(a.value_cache + v_bya, v_nrec),
                                             rsrc(a.value_cache + v_byb, v_nrec)};
+      if constexpr (VJ) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int j = 0; j < 16 / RPI; ++j)
+            dma_buf<16>(rv[hh], vj_src + (uint32_t)(j * RPI) * tok_stride, vj_base(st, hh) + j * 1024);
+        return;
+      }
 #pragma unroll
       for (int hl = 0; hl < HPW; ++hl) {
         unsigned char* sth = st + hl * STH;
@@ -718,10 +748,16 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
           uint32_t x[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const unsigned char* src = st + hl * STH + SG::V_OFF + i * SG::VBYTES_TOK;
-            // sub-dword regions hold zero-extended words; their unused
-            // nibbles are never selected below
-            x[i] = reinterpret_cast<const uint32_t*>(src + r * 256)[lane];
+            if constexpr (VJ) {
+              const unsigned char* src = vj_base(st, i >> 2) + vj_rd[i & 3] + hl * HALF;
+              if constexpr (HS >= 128) x[i] = *reinterpret_cast<const uint32_t*>(src);
+              else x[i] = *reinterpret_cast<const uint16_t*>(src);
+            } else {
+              const unsigned char* src = st + hl * STH + SG::V_OFF + i * SG::VBYTES_TOK;
+              // sub-dword regions hold zero-extended words; their unused
+              // nibbles are never selected below
+              x[i] = reinterpret_cast<const uint32_t*>(src + r * 256)[lane];
+            }
           }
 #pragma unroll
           for (int jb = 0; jb < 4; ++jb) {
