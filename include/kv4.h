@@ -149,6 +149,15 @@ size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs
  *                       contents need no initialization and are clobbered.
  *                       Two calls in flight must not share a workspace.
  * A query row whose causal window is empty (seq_len < query_len) gets zeros.
+ *
+ * The launch plan (matrix-core or vector path, KV split size, kv heads per
+ * matrix-core wave) is chosen on the host from the sizes above. Three
+ * environment variables, read at each call, override it for testing and
+ * tuning: KV4_FORCE_PATH=valu|mfma, KV4_SPLIT_TOKENS=<tokens per split>,
+ * KV4_MFMA_HPW=1|2|4 (lowered where the shape does not allow it). Results
+ * agree within the rounding of the float32 accumulation order.
+ * kv4_paged_attention_workspace_size reads the same variables: query it with
+ * the same environment the call will see.
  */
 int kv4_paged_attention(const void* query, int64_t query_token_stride,
                         const void* key_cache, const void* value_cache,
