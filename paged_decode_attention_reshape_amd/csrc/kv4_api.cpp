@@ -64,6 +64,8 @@ constexpr int kMfmaRows = 16;           // query rows per MFMA tile
 constexpr int64_t kTargetUnitsValu = 2048;
 constexpr int64_t kTargetUnitsMfma = 16384;
 constexpr int kMinSplit = 256;
+constexpr int kSkMaxGrid = 2048;        // stream-K workgroups at most (8 per CU of a 256-CU GPU)
+constexpr int kSkMinSteps = 16;         // stream-K: KV steps per workgroup at least
 
 bool mfma_head_size(int hs) { return hs == 64 || hs == 96 || hs == 128 || hs == 192; }
 
@@ -112,6 +114,22 @@ int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, i
     if (want > 2 && (hs == 96 || hs == 192)) want = 2;   // four heads' V loads would exceed the load counter
     while (want > 1 && (want * G > kMfmaRows || nkv % want != 0)) want >>= 1;
     p.hpw = (int)want;
+  }
+  p.wpb = p.hpw == 4 ? 2 : 4;
+  // Single-token decode on the matrix cores, with whole workgroups of kv head
+  // groups: stream-K partition of the KV steps over the resident workgroups
+  // (no split size; every workgroup gets the same number of steps).
+  p.sk = 0;
+  if (mfma && max_query_len <= 1 && p.n_head_tiles == 1 && (nkv / p.hpw) % p.wpb == 0 &&
+      env_long("KV4_STREAMK", 1) != 0) {
+    p.sk = 1;
+    p.sk_quads = nkv / p.hpw / p.wpb;
+    const int64_t quads = p.sk_quads;
+    const int64_t max_steps = quads * num_seqs * (((int64_t)(max_seq_len < 1 ? 1 : max_seq_len) + 31) / 32);
+    int64_t cap = max_steps / kSkMinSteps;                      // at least kSkMinSteps steps per workgroup
+    const long forced = env_long("KV4_SK_GRID", 0);
+    if (forced > 0) cap = forced;
+    p.sk_pcap = (int)std::max<int64_t>(1, std::min<int64_t>(cap, kSkMaxGrid));
   }
   const int mql = max_query_len < 1 ? 1 : max_query_len;
   p.tiles_per_seq = (mql + p.tq - 1) / p.tq;
@@ -166,8 +184,11 @@ WsLayout ws_layout(const kv4::AttnPlan& p, int64_t num_q_tokens, int32_t num_seq
     w.prefix_off = 0;
     off = align_up((size_t)(num_seqs + 1) * sizeof(int32_t), 256);
   }
-  if (p.num_splits > 1) {
-    const size_t rows = (size_t)p.num_splits * (size_t)num_q_tokens * (size_t)nq;
+  if (p.sk || p.num_splits > 1) {
+    // split-KV: one row per (split, query token, q head); stream-K: one per
+    // (range piece, q head), at most workgroups + quads * sequences pieces
+    const size_t rows = p.sk ? ((size_t)p.sk_pcap + (size_t)p.sk_quads * (size_t)num_seqs) * (size_t)nq
+                             : (size_t)p.num_splits * (size_t)num_q_tokens * (size_t)nq;
     w.o_off = off;
     w.ml_off = align_up(off + rows * (size_t)hs * sizeof(float), 256);
     off = align_up(w.ml_off + rows * 2 * sizeof(float), 256);
@@ -300,7 +321,7 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride, const voi
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(KV4_EINVAL, "workspace must be 16-byte aligned");
     if (a.plan.path == 1) prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ws.prefix_off);
-    if (a.plan.num_splits > 1) {
+    if (a.plan.sk || a.plan.num_splits > 1) {
       a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.o_off);
       a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_off);
     }
@@ -328,6 +349,7 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride, const voi
   a.seed = sign_seed;
   a.scale_log2 = softmax_scale / (float)b * 1.4426950408889634f;
   a.out = static_cast<uint16_t*>(out);
+  a.prefix = prefix;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.plan.path == 1) {
     const int64_t max_units =
@@ -337,7 +359,7 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride, const voi
   } else {
     if (int e = hip_status(kv4::launch_attn_valu(a, st), "kv4_paged_attention launch")) return e;
   }
-  if (a.plan.num_splits > 1)
+  if (a.plan.sk || a.plan.num_splits > 1)
     return hip_status(kv4::launch_attn_reduce(a, st), "kv4_paged_attention merge launch");
   return ok();
 }

@@ -192,7 +192,8 @@ __device__ __forceinline__ bool decode_unit(const AttnArgs& a, const int32_t* pr
   return un.i0 < un.qlen;
 }
 
-// Work units per sequence and their exclusive prefix (one workgroup).
+// Work units per sequence and their exclusive prefix (one workgroup); in
+// stream-K decode, the 32-token KV steps per sequence instead.
 __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* prefix) {
   __shared__ int32_t wave_tot[16];
   __shared__ int32_t carry;
@@ -214,6 +215,7 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* pr
       nsp = nsp < 1 ? 1 : (nsp > a.plan.num_splits ? a.plan.num_splits : nsp);
       const int ntile = (int)((qe - qb + a.plan.tq - 1) / a.plan.tq);
       units = ntile * nsp * a.plan.n_head_tiles * (a.nkv / a.plan.hpw);
+      if (a.plan.sk) units = (qe > qb && L > 0) ? (int)((L + 31) / 32) : 0;   // KV steps of the sequence
     }
     // inclusive scan inside the wave
     int x = units;
@@ -418,30 +420,17 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
   const int ti_n = rr_n / gh, hi_n = rr_n - (rr_n / gh) * gh;
   const uint32_t hoff_n = (uint32_t)(hl_n < HPW ? hl_n : 0) * STH;   // its head's per-head stage
 
-  // Workgroups are dealt to the 8 XCDs round-robin (block b on XCD b % 8).
-  // Unit blocks 2k and 2k + 1 (e.g. kv heads 0-3 and 4-7 of one sequence
-  // split, whose scale rows share 128-byte lines) go to blocks b and b + 8,
-  // which share an XCD and its L2.
-  const int nbk = gridDim.x, bk = blockIdx.x;
-  const int pbk = bk < (nbk & ~15) ? ((bk & ~15) | ((bk & 7) << 1) | ((bk >> 3) & 1)) : bk;
-  for (int u0 = pbk * WPB; u0 < total; u0 += gridDim.x * WPB) {
-    const int u = u0 + wv;
-    if (u >= total) continue;
-    Unit un;
-    if (!decode_unit(a, prefix, u, un)) continue;
-    // the unit is the same for every lane of the wave
-    const int us = uniform(un.s), ui0 = uniform(un.i0), uqbeg = uniform(un.qbeg);
-    const int uqlen = uniform(un.qlen), uL = uniform(un.L), ug = uniform(un.g);
-    const int uht = uniform(un.ht), usp = uniform(un.sp);
+  // One work unit: the query tile starting at query ui0 of sequence us, kv
+  // head group ug, head tile uht, keys [k0, k1). With `partial` the
+  // unnormalized result goes to workspace row ptok (split-KV, or stream-K
+  // piece) for the merge; otherwise the output is written directly.
+  auto run_unit = [&](const int us, const int ui0, const int uqbeg, const int uqlen, const int uL, const int ug,
+                      const int uht, const int k0, const int k1, const int64_t ptok0, const bool partial) {
     const int kv0 = ug * HPW;                      // first kv head of this unit
     const int hq0 = uht * gh;                      // first query head of the tile within a group
     const int nh = min(gh, G - hq0);
     const int ntok = min(a.plan.tq, uqlen - ui0);
     const int pos0 = uL - uqlen + ui0;
-    const int kend = pos0 + ntok;
-    const int k0 = usp * split;
-    const int k1 = min(k0 + split, kend);
-    if (k0 >= k1 && usp > 0) continue;   // no keys for this tile in this split (the merge skips it)
 
     // page ids of this unit, one per lane, 64 pages at a time (loaded first:
     // the q' setup below hides their latency)
@@ -790,9 +779,11 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
     const float pbias = 72.0f * pacc[0];
     const int qrow = uqbeg + ui0 + ti_n;
     const int h = (kv0 + hl_n) * G + hq0 + hi_n;
-    if (a.plan.num_splits > 1) {
+    if (partial) {
       if (row_ok) {
-        const int64_t prow = ((int64_t)usp * a.num_q_tokens + qrow) * a.nq + h;
+        // split-KV: one row per (split, query token); stream-K: one per piece
+        const int64_t ptok = a.plan.sk ? ptok0 : ptok0 + qrow;
+        const int64_t prow = ptok * a.nq + h;
         float* dst = a.ws_o + prow * HS;
         int ns = 0;
 #pragma unroll
@@ -821,7 +812,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
           a.ws_ml[2 * prow + 1] = l_run;
         }
       }
-      continue;
+      return;
     }
     // single split: normalize, stage the row in LDS, inverse rotation, store
     const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
@@ -873,33 +864,112 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
       }
     }
     __builtin_amdgcn_wave_barrier();
+  };
+
+  if (a.plan.sk) {
+    // Single-token decode, stream-K: the KV steps (32 tokens) of every (kv
+    // head group quad, sequence) pair, concatenated quad-major, are cut into
+    // gridDim.x equal contiguous ranges; block w walks its range and runs one
+    // unit per sequence piece, its partial named w + quad * num_seqs + s.
+    // prefix[s] holds the first step of sequence s, prefix[num_seqs] the total.
+    const int nseq = a.num_seqs;
+    const int64_t S = total;
+    const int64_t W = (int64_t)a.plan.sk_quads * S;   // quads = n_hg / WPB
+    const int64_t P = gridDim.x;
+    const int64_t w = blockIdx.x;
+    int64_t x = w * W / P;
+    const int64_t x1 = (w + 1) * W / P;
+    while (x < x1) {
+      const int q = (int)(x / S);
+      const int64_t loc = x - (int64_t)q * S;
+      const int s_ = wave_search_le(prefix, nseq, loc);
+      const int64_t t0 = uniform(prefix[s_]), t1 = uniform(prefix[s_ + 1]);
+      const int64_t end = min(x1 - (int64_t)q * S, t1);
+      int64_t qb = a.qsl[s_], qe = a.qsl[s_ + 1];
+      qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
+      qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
+      int64_t L = a.seq_lens[s_];
+      const int64_t cap = (int64_t)a.max_blocks * a.bs;
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+      const int uqb = uniform((int)qb), uql = uniform((int)(qe - qb)), uL = uniform((int)L);
+      const int k0 = (int)(32 * (loc - t0));
+      const int k1 = (int)min((int64_t)32 * (end - t0), (int64_t)uL);
+      run_unit(s_, 0, uqb, uql, uL, q * WPB + wv, 0, k0, k1, w + (int64_t)q * nseq + s_, true);
+      x = (int64_t)q * S + end;
+    }
+    return;
+  }
+
+  // Workgroups are dealt to the 8 XCDs round-robin (block b on XCD b % 8).
+  // Unit blocks 2k and 2k + 1 (e.g. kv heads 0-3 and 4-7 of one sequence
+  // split, whose scale rows share 128-byte lines) go to blocks b and b + 8,
+  // which share an XCD and its L2.
+  const int nbk = gridDim.x, bk = blockIdx.x;
+  const int pbk = bk < (nbk & ~15) ? ((bk & ~15) | ((bk & 7) << 1) | ((bk >> 3) & 1)) : bk;
+  for (int u0 = pbk * WPB; u0 < total; u0 += gridDim.x * WPB) {
+    const int u = u0 + wv;
+    if (u >= total) continue;
+    Unit un;
+    if (!decode_unit(a, prefix, u, un)) continue;
+    // the unit is the same for every lane of the wave
+    const int us = uniform(un.s), ui0 = uniform(un.i0), uqbeg = uniform(un.qbeg);
+    const int uqlen = uniform(un.qlen), uL = uniform(un.L), ug = uniform(un.g);
+    const int uht = uniform(un.ht), usp = uniform(un.sp);
+    const int ntok = min(a.plan.tq, uqlen - ui0);
+    const int kend = uL - uqlen + ui0 + ntok;
+    const int k0 = usp * split;
+    const int k1 = min(k0 + split, kend);
+    if (k0 >= k1 && usp > 0) continue;   // no keys for this tile in this split (the merge skips it)
+    run_unit(us, ui0, uqbeg, uqlen, uL, ug, uht, k0, k1, (int64_t)usp * a.num_q_tokens, a.plan.num_splits > 1);
   }
 }
 
 static int g_num_cus = 0;
 
+template <int HS, int HPW>
+static int resident_blocks() {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW>),
+                                                     64 * MfmaShape<HPW>::WPB, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    per_cu = nb;
+  }
+  return per_cu * g_num_cus;
+}
+
 template <int HS>
-static hipError_t launch_hs(const AttnArgs& a, const int32_t* prefix, int64_t max_units, hipStream_t stream) {
+static hipError_t launch_hs(AttnArgs& a, const int32_t* prefix, int64_t max_units, hipStream_t stream) {
   if (a.plan.hpw == 4 && Geo<HS>::NVR != 1) return hipErrorInvalidValue;
-  auto go = [&](auto kernel, int wpb) {
-    int64_t wgs = (max_units + wpb - 1) / wpb;
-    const int64_t cap = (int64_t)g_num_cus * 8;
-    if (wgs > cap) wgs = cap;
-    if (wgs < 1) wgs = 1;
+  auto go = [&](auto kernel, int wpb, int resident) {
+    int64_t wgs;
+    if (a.plan.sk) {
+      // stream-K: exactly the workgroups the GPU holds at once (at most the
+      // planner's cap, which sized the workspace)
+      wgs = std::min<int64_t>(resident, a.plan.sk_pcap);
+      a.plan.sk_grid = (int)std::max<int64_t>(wgs, 1);
+      wgs = a.plan.sk_grid;
+    } else {
+      wgs = (max_units + wpb - 1) / wpb;
+      const int64_t cap = (int64_t)g_num_cus * 8;
+      if (wgs > cap) wgs = cap;
+      if (wgs < 1) wgs = 1;
+    }
     hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(64 * wpb), 0, stream, a, prefix);
   };
   switch (a.plan.hpw) {
-    case 2: go(attn_mfma_kernel<HS, 2>, MfmaShape<2>::WPB); break;
+    case 2: go(attn_mfma_kernel<HS, 2>, MfmaShape<2>::WPB, resident_blocks<HS, 2>()); break;
     case 4:
       // four heads' V loads of a step must fit the 6-bit load counter
-      if constexpr (Geo<HS>::NVR == 1) go(attn_mfma_kernel<HS, 4>, MfmaShape<4>::WPB);
+      if constexpr (Geo<HS>::NVR == 1) go(attn_mfma_kernel<HS, 4>, MfmaShape<4>::WPB, resident_blocks<HS, 4>());
       break;
-    default: go(attn_mfma_kernel<HS, 1>, MfmaShape<1>::WPB); break;
+    default: go(attn_mfma_kernel<HS, 1>, MfmaShape<1>::WPB, resident_blocks<HS, 1>()); break;
   }
   return hipSuccess;
 }
 
-hipError_t launch_attn_mfma(const AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream) {
+hipError_t launch_attn_mfma(AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream) {
   hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a, prefix);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

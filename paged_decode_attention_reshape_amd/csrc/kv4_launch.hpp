@@ -61,6 +61,11 @@ struct AttnPlan {
   int split_tokens;    // KV tokens per split
   int num_splits;      // splits in the grid (1 = no partials)
   int hpw;             // MFMA path: kv heads per wave (1, 2 or 4; > 1 only for single-token decode)
+  int wpb;             // MFMA path: waves per workgroup
+  int sk;              // MFMA single-token decode: stream-K partition instead of splits
+  int sk_quads;        // stream-K: kv head groups / waves per workgroup
+  int sk_pcap;         // stream-K: most workgroups (sizes the workspace)
+  int sk_grid;         // stream-K: workgroups launched (set at launch)
 };
 
 struct AttnArgs {
@@ -89,6 +94,8 @@ struct AttnArgs {
   uint16_t* out;
   float* ws_o;         // [num_splits][num_q_tokens][nq][hs]   (split only)
   float* ws_ml;        // [num_splits][num_q_tokens][nq][2]    (split only)
+                       // stream-K: [sk_pcap + quads * num_seqs][nq][hs] and [..][nq][2]
+  const int32_t* prefix;   // MFMA path: device plan output (stream-K: first KV step per sequence)
   AttnPlan plan;
 };
 
@@ -98,6 +105,7 @@ hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream);
 // Device plan (work units per sequence, exclusive prefix into `prefix`,
 // num_seqs + 1 ints) followed by the matrix-core attention kernel.
-hipError_t launch_attn_mfma(const AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream);
+// In stream-K mode it sets a.plan.sk_grid, which the merge needs.
+hipError_t launch_attn_mfma(AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream);
 
 }  // namespace kv4

@@ -116,17 +116,29 @@ HPW_CASES = [
 ]
 
 
-@pytest.mark.parametrize("split", ["auto", "64"])
+SCHED = {
+    # stream-K partition over the resident workgroups (the decode default)
+    "streamk": {},
+    # three workgroups: ranges straddle sequences, many pieces per row
+    "streamk_grid3": {"KV4_SK_GRID": "3"},
+    # more workgroups than KV steps: empty ranges that leave no piece
+    "streamk_grid2000": {"KV4_SK_GRID": "2000"},
+    # the split-KV scheme with small forced splits
+    "splits64": {"KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64"},
+}
+
+
+@pytest.mark.parametrize("sched", list(SCHED))
 @pytest.mark.parametrize("hpw", ["1", "2", "4"])
 @pytest.mark.parametrize("case", HPW_CASES, ids=[c[0] for c in HPW_CASES])
-def test_attention_heads_per_wave(case, hpw, split, monkeypatch):
+def test_attention_heads_per_wave(case, hpw, sched, monkeypatch):
     """The matrix-core kernel with 1, 2 and 4 kv heads per wave (the planner
     lowers the request where G * hpw > 16 or hpw does not divide the kv
-    heads), with and without forced KV splits."""
+    heads), under each decode work schedule."""
     monkeypatch.setenv("KV4_FORCE_PATH", "mfma")
     monkeypatch.setenv("KV4_MFMA_HPW", hpw)
-    if split != "auto":
-        monkeypatch.setenv("KV4_SPLIT_TOKENS", split)
+    for k, v in SCHED[sched].items():
+        monkeypatch.setenv(k, v)
     name, nq, nkv, hs, ql, sl, bs = case
     w = W.custom(name, nq, nkv, hs, ql, sl, block_size=bs)
     r = run_gpu(w)
