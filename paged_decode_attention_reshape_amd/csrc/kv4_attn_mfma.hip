@@ -869,16 +869,18 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
   if (a.plan.sk) {
     // Single-token decode, stream-K: the KV steps (32 tokens) of every (kv
     // head group quad, sequence) pair, concatenated quad-major, are cut into
-    // gridDim.x equal contiguous ranges; block w walks its range and runs one
+    // P = min(gridDim.x, steps) equal contiguous ranges; block w walks its range and runs one
     // unit per sequence piece, its partial named w + quad * num_seqs + s.
     // prefix[s] holds the first step of sequence s, prefix[num_seqs] the total.
     const int nseq = a.num_seqs;
     const int64_t S = total;
     const int64_t W = (int64_t)a.plan.sk_quads * S;   // quads = n_hg / WPB
-    const int64_t P = gridDim.x;
+    // no more ranges than steps, so none is empty (the merge relies on it)
+    const int64_t P = min((int64_t)gridDim.x, W);
     const int64_t w = blockIdx.x;
-    int64_t x = w * W / P;
-    const int64_t x1 = (w + 1) * W / P;
+    if (w >= P) return;
+    int64_t x = floor_div_small(w * W, P);
+    const int64_t x1 = floor_div_small((w + 1) * W, P);
     while (x < x1) {
       const int q = (int)(x / S);
       const int64_t loc = x - (int64_t)q * S;

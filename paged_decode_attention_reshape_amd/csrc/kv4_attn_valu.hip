@@ -299,10 +299,8 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
   for (int64_t row = wave0; row < n_rows; row += n_waves) {
     // partial k of this row sits at workspace row k * pstride + pbase
-    // (stream-K: unless workgroup sk_w0 + k had an empty range)
     int nsp = 0;
     int64_t pbase = row, pstride = n_rows;
-    int64_t sk_w0 = 0, sk_W = 0, sk_P = 1;
     {
       const int64_t qtok = row / a.nq;
       const int s = wave_search_le(a.qsl, a.num_seqs, qtok);   // sequence of this query row
@@ -317,16 +315,17 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
         const int h = (int)(row - qtok * a.nq);
         const int quad = h / (a.nq / a.nkv) / a.plan.hpw / a.plan.wpb;
         const int64_t S = a.prefix[a.num_seqs];
-        const int64_t W = (int64_t)a.plan.sk_quads * S, P = a.plan.sk_grid;
+        const int64_t W = (int64_t)a.plan.sk_quads * S;
+        const int64_t P = (int64_t)a.plan.sk_grid < W ? (int64_t)a.plan.sk_grid : W;   // ranges, none empty
         const int64_t xs = (int64_t)quad * S + a.prefix[s], xe = (int64_t)quad * S + a.prefix[s + 1];
         if (qtok >= qb && qtok < qe && xe > xs && W > 0) {
-          const int64_t w0 = ((xs + 1) * P - 1) / W, w1 = (xe * P - 1) / W;
+          // the range holding step x: the largest w with floor(w W / P) <= x
+          const int64_t w0 = floor_div_small((xs + 1) * P - 1, W);
+          const int64_t w1 = floor_div_small(xe * P - 1, W);
           nsp = (int)(w1 - w0 + 1);
           pbase = (w0 + (int64_t)quad * a.num_seqs + s) * a.nq + h;
           pstride = a.nq;
-          sk_w0 = w0;
-          sk_W = W;
-          sk_P = P;
+
         }
       } else if (qtok >= qb && qtok < qe) {
         const int64_t pos = L - (qe - qb) + (qtok - qb);
@@ -358,9 +357,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
         ll[k] = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[k][e] = 0.0f;
-        // a workgroup with an empty range (fewer steps than workgroups) left nothing
-        const bool live = !a.plan.sk || (sk_w0 + sp) * sk_W / sk_P != (sk_w0 + sp + 1) * sk_W / sk_P;
-        if (sp < nsp && live) {
+        if (sp < nsp) {
           const int64_t prow = (int64_t)sp * pstride + pbase;
           mm[k] = a.ws_ml[2 * prow];
           ll[k] = a.ws_ml[2 * prow + 1];

@@ -174,6 +174,16 @@ __device__ __forceinline__ float group_sum_ct(float v) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// floor(num / den) for 0 <= num < 2^53, den > 0: a correctly rounded double
+// quotient is within one of the floor, and one integer step fixes it (far
+// cheaper than a 64-bit integer division).
+__device__ __forceinline__ int64_t floor_div_small(int64_t num, int64_t den) {
+  int64_t q = (int64_t)((double)num / (double)den);
+  if (q * den > num) --q;
+  else if ((q + 1) * den <= num) ++q;
+  return q;
+}
+
 // Largest i in [0, n - 1] with arr[i] <= key (0 if there is none), for a
 // non-decreasing arr and a wave-uniform key; every lane of the wave takes
 // part. Each round probes 64 evenly spaced entries at once, so n entries
