@@ -295,6 +295,8 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride, const voi
   if (num_blocks < 0 || num_blocks > INT32_MAX) return fail(KV4_EINVAL, "num_blocks out of range");
   if (!std::isfinite(softmax_scale)) return fail(KV4_EINVAL, "softmax_scale must be finite");
   if (num_q_tokens == 0) return ok();
+  if (num_q_tokens * (int64_t)num_q_heads > INT32_MAX)
+    return fail(KV4_EUNSUPPORTED, "num_q_tokens * num_q_heads must be below 2^31");
   if (max_blocks_per_seq < 1) return fail(KV4_EINVAL, "max_blocks_per_seq must be >= 1");
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return fail(KV4_EINVAL, "page table too long");
   if (query_token_stride < (int64_t)num_q_heads * head_size || query_token_stride % 8)

@@ -89,9 +89,13 @@ __device__ __forceinline__ void codes_to_u(uint32_t w, float (&u)[8]) {
 }
 
 // Inverse rotation and store of one output row chunk: o = D.H.o'/b, bf16.
+// LPMAX > 0: at most LPMAX lanes per vector, with the lane distances fixed at
+// compile time (no dispatch on them); LPMAX = 0: any b.
+template <int LPMAX = 0>
 __device__ __forceinline__ void store_out_row(float (&o)[8], int b, int jj, uint32_t sbits,
                                               float inv_b, uint16_t* dst, bool do_store) {
-  fwht_b(o, b, jj);
+  if constexpr (LPMAX > 0) fwht_b_ct<LPMAX>(o, b, jj);
+  else fwht_b(o, b, jj);
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = apply_sign(o[e] * inv_b, sbits, e);
   if (do_store) {
@@ -302,10 +306,30 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
     int nsp = 0;
     int64_t pbase = row, pstride = n_rows;
     {
-      const int64_t qtok = row / a.nq;
-      const int s = wave_search_le(a.qsl, a.num_seqs, qtok);   // sequence of this query row
-      const int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
+      // rows number fewer than 2^31 (checked on the host): 32-bit division
+      const int64_t qtok = (uint32_t)row / (uint32_t)a.nq;
+      // sequence of this query row. In single-token decode token t is nearly
+      // always sequence t: its metadata is loaded with the check (one round
+      // trip), and the search runs only if the guess is wrong.
+      int s = (int)(qtok < a.num_seqs ? qtok : a.num_seqs - 1);
+      int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
       int64_t L = a.seq_lens[s];
+      int64_t pf0 = 0, pf1 = 0, pftot = 0;
+      if (a.plan.sk) {
+        pf0 = a.prefix[s];
+        pf1 = a.prefix[s + 1];
+        pftot = a.prefix[a.num_seqs];
+      }
+      if (!(qb <= qtok && qtok < qe)) {
+        s = wave_search_le(a.qsl, a.num_seqs, qtok);
+        qb = a.qsl[s];
+        qe = a.qsl[s + 1];
+        L = a.seq_lens[s];
+        if (a.plan.sk) {
+          pf0 = a.prefix[s];
+          pf1 = a.prefix[s + 1];
+        }
+      }
       const int64_t cap = (int64_t)a.max_blocks * a.bs;
       L = L < 0 ? 0 : (L > cap ? cap : L);
       if (a.plan.sk) {
@@ -314,10 +338,10 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
         // w + quad * num_seqs + s; workgroup w covers [w W / P, (w+1) W / P)
         const int h = (int)(row - qtok * a.nq);
         const int quad = h / (a.nq / a.nkv) / a.plan.hpw / a.plan.wpb;
-        const int64_t S = a.prefix[a.num_seqs];
+        const int64_t S = pftot;
         const int64_t W = (int64_t)a.plan.sk_quads * S;
         const int64_t P = (int64_t)a.plan.sk_grid < W ? (int64_t)a.plan.sk_grid : W;   // ranges, none empty
-        const int64_t xs = (int64_t)quad * S + a.prefix[s], xe = (int64_t)quad * S + a.prefix[s + 1];
+        const int64_t xs = (int64_t)quad * S + pf0, xe = (int64_t)quad * S + pf1;
         if (qtok >= qb && qtok < qe && xe > xs && W > 0) {
           // the range holding step x: the largest w with floor(w W / P) <= x
           const int64_t w0 = floor_div_small((xs + 1) * P - 1, W);
@@ -384,7 +408,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
     const float inv_l = Ls > 0.0f ? 1.0f / Ls : 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] *= inv_l;
-    store_out_row(o, a.b, jj, sbits, inv_b, a.out + row * hs + 8 * jj, lane_on && grp == 0);
+    store_out_row<LP>(o, a.b, jj, sbits, inv_b, a.out + row * hs + 8 * jj, lane_on && grp == 0);
   }
 }
 

@@ -108,6 +108,12 @@ def test_attention_validation(L, over, needle):
     assert needle in kv4.kv4_last_error()
 
 
+def test_attention_rejects_2_31_query_rows(L):
+    # the merge numbers (query token, query head) rows in 32 bits
+    assert _attn(L, Tq=1 << 28, nq=8, qs=8 * 96, qsl=16, mql=1) == kv4.KV4_EUNSUPPORTED
+    assert "2^31" in kv4.kv4_last_error()
+
+
 def test_attention_workspace_required(L):
     need = L.kv4_paged_attention_workspace_size(2, 2, 8, 2, 96, 1, 100000)
     assert need > 0
