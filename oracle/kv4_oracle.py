@@ -347,3 +347,165 @@ def attention_dense(query, key, value, query_start_loc, seq_lens, softmax_scale:
             logits = (qg @ k[:, g, :].T) * softmax_scale
             out[q0:q1, g * group:(g + 1) * group] = _causal_softmax_attend(logits, v[:, g, :], L)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Per-token-head INT8 / FP8 control modes (no rotation)
+# ---------------------------------------------------------------------------
+# The pages name int8_per_token_head and fp8_per_token_head as the control
+# modes of the same kernels ([PR56198]: they never use the transform; [PR40835]
+# review: int8 or FP8 cache dtype, float32 scale caches per (token, kv head)).
+# Readings (the pages are silent on the rule; listed in the design doc): symmetric
+# absmax per (token, kv head) vector, scale = float32(absmax) / qmax (IEEE
+# float32 division) with qmax = 127 (int8) or 448 (the largest finite OCP
+# e4m3fn value); int8 code = clamp(rint_half_even(float32(x / scale)), -128,
+# 127); fp8 code = float32(x / scale) rounded to nearest-even e4m3fn,
+# saturating at +-448; amax == 0 stores scale 0 and code 0. One code byte per
+# element: cache uint8 [nb, bs, nkv, hs].
+
+PTH_QMAX = {"int8": 127.0, "fp8": 448.0}
+
+
+def fp8_e4m3fn_decode(codes) -> np.ndarray:
+    """float64 value of OCP FP8 E4M3 (e4m3fn) bytes: sign bit 7, exponent bits
+    6..3 (bias 7), mantissa bits 2..0; exponent 0 is subnormal (m/8 * 2^-6);
+    S.1111.111 is NaN and there is no infinity."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_e4m3fn_encode(x) -> np.ndarray:
+    """Round float32 values to the nearest e4m3fn value (ties to even mantissa),
+    saturating magnitudes above 448 to 448; the sign bit follows the input's
+    (-0.0 -> 0x80)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)     # exact
+    neg = np.signbit(x)
+    a = np.abs(x)
+    # quantum of the binade holding a: 2^(e - 3) for normal e >= -6, 2^-9 below
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))                  # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)
+    quantum = np.exp2(e - 3.0)
+    mq = np.rint(a / quantum)                                   # half to even; exact division by 2^k
+    # mq in [0, 16]: 16 moves to the next binade (mantissa 0)
+    val = mq * quantum
+    code_mag = np.zeros(a.shape, dtype=np.int64)
+    sub = val < 2.0 ** -6
+    code_mag = np.where(sub, (val / 2.0 ** -9).astype(np.int64), code_mag)
+    _, ev = np.frexp(np.where(val > 0, val, 1.0))
+    ev = ev - 1
+    mant = np.where(val > 0, val / np.exp2(ev.astype(np.float64)) - 1.0, 0.0)   # exact, multiple of 1/8
+    normal_code = ((ev + 7) << 3) | np.rint(mant * 8.0).astype(np.int64)
+    code_mag = np.where(sub, code_mag, normal_code)
+    code_mag = np.where(val >= 448.0, 0x7E, code_mag)          # saturate (0x7F is NaN)
+    return (code_mag | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def quantize_pth(x: np.ndarray, mode: str):
+    """Per-(token, head) symmetric int8 / fp8 of float32 vectors along the last
+    axis: returns (uint8 codes, float32 scales). See the readings above."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = (amax / np.float32(PTH_QMAX[mode])).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = (x / safe[..., None]).astype(np.float32)
+    if mode == "int8":
+        codes = np.clip(np.rint(q), -128, 127).astype(np.int8).view(np.uint8)
+    else:
+        codes = fp8_e4m3fn_encode(q)
+    codes = np.where(scale[..., None] > 0, codes, np.uint8(0)).astype(np.uint8)
+    return codes, scale
+
+
+def decode_pth(codes, mode: str) -> np.ndarray:
+    """float64 values of stored int8 / fp8 code bytes."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if mode == "int8":
+        return c.view(np.int8).astype(np.float64)
+    return fp8_e4m3fn_decode(c)
+
+
+def pth_new_cache(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int):
+    """Zeroed uint8 [nb, bs, nkv, hs] codes and float32 [nb, bs, nkv] scales."""
+    codes = np.zeros((num_blocks, block_size, num_kv_heads, head_size), dtype=np.uint8)
+    scales = np.zeros((num_blocks, block_size, num_kv_heads), dtype=np.float32)
+    return codes, scales
+
+
+def pth_write(x_bf16: np.ndarray, cache: np.ndarray, scale_cache: np.ndarray,
+              slot_mapping: np.ndarray, mode: str) -> None:
+    """Write path of the int8 / fp8 modes for one of K or V: quantize each
+    (token, kv head) vector of the bf16 input (exactly float32) and store it
+    at its slot; slots outside [0, nb * bs) are skipped."""
+    x = np.asarray(x_bf16, dtype=np.float32)
+    bs = cache.shape[1]
+    s = np.asarray(slot_mapping, dtype=np.int64)
+    keep = (s >= 0) & (s < cache.shape[0] * bs)
+    if not keep.any():
+        return
+    codes, scale = quantize_pth(x[keep], mode)
+    s = s[keep]
+    cache[s // bs, s % bs] = codes
+    scale_cache[s // bs, s % bs] = scale
+
+
+def pth_write_kv(key, value, slot_mapping, num_blocks, block_size, mode: str):
+    """Convenience: fresh int8 / fp8 caches with every token written."""
+    T, nkv, hs = np.asarray(key).shape
+    kc, ks = pth_new_cache(num_blocks, block_size, nkv, hs)
+    vc, vs = pth_new_cache(num_blocks, block_size, nkv, hs)
+    pth_write(key, kc, ks, slot_mapping, mode)
+    pth_write(value, vc, vs, slot_mapping, mode)
+    return kc, vc, ks, vs
+
+
+def pth_dequant(cache: np.ndarray, scale_cache: np.ndarray, slot_mapping: np.ndarray,
+                mode: str) -> np.ndarray:
+    """Gather slots and dequantize: code value * scale as one float32 product."""
+    bs = cache.shape[1]
+    sl = np.asarray(slot_mapping, dtype=np.int64)
+    vals = decode_pth(cache[sl // bs, sl % bs], mode).astype(np.float32)
+    sc = scale_cache[sl // bs, sl % bs].astype(np.float32)
+    return (vals * sc[..., None]).astype(np.float32)
+
+
+def pth_gather_seq(cache, scale_cache, block_table_row, seq_len: int, mode: str) -> np.ndarray:
+    """fp64 dequantized [seq_len, nkv, hs] of one sequence through its page table."""
+    bs = cache.shape[1]
+    pos = np.arange(seq_len)
+    blk = np.asarray(block_table_row, dtype=np.int64)[pos // bs]
+    off = pos % bs
+    return decode_pth(cache[blk, off], mode) * scale_cache[blk, off].astype(np.float64)[..., None]
+
+
+def pth_paged_attention(query, key_cache, value_cache, k_scale_cache, v_scale_cache,
+                        block_table, seq_lens, query_start_loc, softmax_scale: float,
+                        mode: str, seqs=None) -> np.ndarray:
+    """fp64 causal paged attention over an int8 / fp8 per-token-head cache, in
+    the original domain: logit_j = (q . K_j) * softmax_scale with K_j, V_j the
+    dequantized cache rows; same causal rule and GQA mapping as
+    paged_attention. Rows of sequences not in `seqs` are NaN."""
+    q = np.asarray(query, dtype=np.float64)
+    Tq, nq, hs = q.shape
+    nkv = key_cache.shape[2]
+    group = nq // nkv
+    out = np.full((Tq, nq, hs), np.nan)
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    if seqs is None:
+        seqs = range(len(seq_lens))
+    for s in seqs:
+        L = int(seq_lens[s])
+        q0, q1 = int(qsl[s]), int(qsl[s + 1])
+        if q1 == q0:
+            continue
+        K = pth_gather_seq(key_cache, k_scale_cache, block_table[s], L, mode)
+        V = pth_gather_seq(value_cache, v_scale_cache, block_table[s], L, mode)
+        for g in range(nkv):
+            qg = q[q0:q1, g * group:(g + 1) * group, :]
+            logits = (qg @ K[:, g, :].T) * softmax_scale
+            out[q0:q1, g * group:(g + 1) * group] = _causal_softmax_attend(logits, V[:, g, :], L)
+    return out
