@@ -190,6 +190,51 @@ int kv4_dequant(const void* cache, const float* scale_cache, int64_t num_blocks,
                 int32_t block_size, uint64_t sign_seed, int32_t inverse_rotate,
                 float* out, void* stream);
 
+/*
+ * Per-token-head INT8 / FP8 control modes: the pages' int8_per_token_head
+ * and fp8_per_token_head ([PR56198]: controls that never use the transform;
+ * [PR40835] review: int8 or FP8 cache dtype, the same float32 scale caches).
+ * No rotation; one code byte per element. The rule is not on the pages and
+ * is fixed here as symmetric absmax per (token, kv head) vector:
+ *   KV4_MODE_INT8  scale = absmax / 127, code = clamp(rint_half_even(x /
+ *                  scale), -128, 127) as a two's-complement byte;
+ *   KV4_MODE_FP8   scale = absmax / 448, code = x / scale rounded to the
+ *                  nearest OCP FP8 E4M3 (e4m3fn) value, ties to the even
+ *                  mantissa, magnitudes >= 448 saturating to 448; the sign bit
+ *                  follows the quotient's.
+ * (IEEE float32 division; absmax == 0 stores scale 0 and code 0.) Caches:
+ * uint8 [num_blocks, block_size, num_kv_heads, head_size], scales float32
+ * [num_blocks, block_size, num_kv_heads].
+ */
+#define KV4_MODE_INT8 1
+#define KV4_MODE_FP8 2
+
+/*
+ * kv4_pth_write -- write path of the int8 / fp8 modes: quantize each (token,
+ * kv head) vector of key / value (bf16 [num_tokens, num_kv_heads, head_size],
+ * token rows key_token_stride / value_token_stride elements apart) and store
+ * it at slot_mapping[t] (slots outside [0, num_blocks * block_size) skip the
+ * token). Arguments otherwise as kv4_rht_write; KV4_EINVAL for another mode.
+ */
+int kv4_pth_write(int32_t kv_quant_mode, const void* key, const void* value,
+                  int64_t key_token_stride, int64_t value_token_stride,
+                  void* key_cache, void* value_cache,
+                  float* k_scale_cache, float* v_scale_cache,
+                  const int64_t* slot_mapping, int64_t num_tokens,
+                  int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                  int64_t num_blocks, void* stream);
+
+/*
+ * kv4_pth_dequant -- gather and dequantize int8 / fp8 cache slots (tests and
+ * debugging): out[t, h, i] = value(code) * scale as one float32 product;
+ * out-of-range slots give zeros. out float32 [num_tokens, num_kv_heads,
+ * head_size].
+ */
+int kv4_pth_dequant(int32_t kv_quant_mode, const void* cache, const float* scale_cache,
+                    int64_t num_blocks, const int64_t* slot_mapping, int64_t num_tokens,
+                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                    float* out, void* stream);
+
 /* Thread-local description of the last failure ("" if none). Never NULL. */
 const char* kv4_last_error(void);
 

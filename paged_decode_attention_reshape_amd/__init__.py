@@ -23,6 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libkv4.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kv4.h")
 
 KV4_OK, KV4_EINVAL, KV4_EUNSUPPORTED, KV4_EHIP, KV4_EWORKSPACE = 0, 1, 2, 3, 4
+KV4_MODE_INT8, KV4_MODE_FP8 = 1, 2
+_MODES = {"int8": KV4_MODE_INT8, "fp8": KV4_MODE_FP8, KV4_MODE_INT8: KV4_MODE_INT8, KV4_MODE_FP8: KV4_MODE_FP8}
 DEFAULT_SIGN_SEED = 42
 
 _c_int32, _c_int64, _c_uint64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
@@ -38,6 +40,10 @@ _SIGNATURES = {
     "kv4_dequant": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _c_int64, _c_int32, _c_int32, _c_int32,
                                    _c_int32, _c_uint64, _c_int32, _vp, _vp]),
     "kv4_last_error": (ctypes.c_char_p, []),
+    "kv4_pth_write": (ctypes.c_int, [_c_int32, _vp, _vp, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp,
+                                     _c_int64, _c_int32, _c_int32, _c_int32, _c_int64, _vp]),
+    "kv4_pth_dequant": (ctypes.c_int, [_c_int32, _vp, _vp, _c_int64, _vp, _c_int64, _c_int32, _c_int32,
+                                       _c_int32, _vp, _vp]),
 }
 
 _lib = None
@@ -233,3 +239,69 @@ def kv4_dequant(cache: torch.Tensor, scale_cache: torch.Tensor, slot_mapping: to
 
 __all__ = ["kv4_rht_write", "kv4_paged_attention", "kv4_paged_attention_workspace_size", "kv4_dequant",
            "kv4_last_error", "Kv4Error", "lib", "header_functions", "LIB_PATH"]
+
+
+def _mode(kv_quant_mode) -> int:
+    if kv_quant_mode not in _MODES:
+        raise ValueError(f"kv_quant_mode must be 'int8' or 'fp8', got {kv_quant_mode!r}")
+    return _MODES[kv_quant_mode]
+
+
+def kv4_pth_write(kv_quant_mode, key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                  value_cache: torch.Tensor, k_scale_cache: torch.Tensor, v_scale_cache: torch.Tensor,
+                  slot_mapping: torch.Tensor, stream=None) -> None:
+    """Quantize key/value [T, nkv, hs] (bf16) per (token, kv head) to int8 or
+    fp8 e4m3fn codes ('int8' / 'fp8'; no rotation) into the caches
+    [nb, bs, nkv, hs] (uint8) and scale caches [nb, bs, nkv] (float32) at
+    slot_mapping [T] (int64). Asynchronous on `stream`."""
+    m = _mode(kv_quant_mode)
+    _need(key, "key", torch.bfloat16, 3)
+    _need(value, "value", torch.bfloat16, 3)
+    _need(key_cache, "key_cache", torch.uint8, 4)
+    _need(value_cache, "value_cache", torch.uint8, 4)
+    _need(k_scale_cache, "k_scale_cache", torch.float32, 3)
+    _need(v_scale_cache, "v_scale_cache", torch.float32, 3)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache"), (k_scale_cache, "k_scale_cache"),
+                 (v_scale_cache, "v_scale_cache"), (slot_mapping, "slot_mapping")):
+        _contig(t, n)
+    T, nkv, hs = key.shape
+    nb, bs = key_cache.shape[0], key_cache.shape[1]
+    if value.shape != key.shape or slot_mapping.shape[0] != T:
+        raise ValueError("key/value/slot_mapping shapes disagree")
+    if key_cache.shape != (nb, bs, nkv, hs) or value_cache.shape != key_cache.shape:
+        raise ValueError(f"caches must be [num_blocks, block_size, {nkv}, {hs}]")
+    if k_scale_cache.shape != (nb, bs, nkv) or v_scale_cache.shape != k_scale_cache.shape:
+        raise ValueError(f"scale caches must be [num_blocks, block_size, {nkv}]")
+    for t, n in ((key, "key"), (value, "value")):
+        if t.stride(2) != 1 or t.stride(1) != hs:
+            raise ValueError(f"{n} must have contiguous heads (stride (*, {hs}, 1))")
+    rc = lib().kv4_pth_write(m, key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0),
+                             key_cache.data_ptr(), value_cache.data_ptr(), k_scale_cache.data_ptr(),
+                             v_scale_cache.data_ptr(), slot_mapping.data_ptr(), T, nkv, hs, bs, nb, _stream(stream))
+    _check("kv4_pth_write", rc)
+
+
+def kv4_pth_dequant(kv_quant_mode, cache: torch.Tensor, scale_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Gather slots from an int8 / fp8 cache and dequantize to float32 [T, nkv, hs]."""
+    m = _mode(kv_quant_mode)
+    _need(cache, "cache", torch.uint8, 4)
+    _need(scale_cache, "scale_cache", torch.float32, 3)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    for t, n in ((cache, "cache"), (scale_cache, "scale_cache"), (slot_mapping, "slot_mapping")):
+        _contig(t, n)
+    nb, bs, nkv, hs = cache.shape
+    if scale_cache.shape != (nb, bs, nkv):
+        raise ValueError("scale cache shape disagrees with the cache")
+    T = slot_mapping.shape[0]
+    if out is None:
+        out = torch.empty((T, nkv, hs), dtype=torch.float32, device=cache.device)
+    _need(out, "out", torch.float32, 3)
+    _contig(out, "out")
+    if out.shape != (T, nkv, hs):
+        raise ValueError("out must be [num_tokens, num_kv_heads, head_size]")
+    rc = lib().kv4_pth_dequant(m, cache.data_ptr(), scale_cache.data_ptr(), nb, slot_mapping.data_ptr(), T, nkv,
+                               hs, bs, out.data_ptr(), _stream(stream))
+    _check("kv4_pth_dequant", rc)
+    return out

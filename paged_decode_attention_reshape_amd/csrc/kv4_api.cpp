@@ -211,18 +211,23 @@ int check_attn_sizes(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t
   return KV4_OK;
 }
 
-}  // namespace
+int check_mode(int32_t mode) {
+  if (mode != 1 && mode != 2)
+    return fail(KV4_EINVAL, "kv_quant_mode must be 1 (int8) or 2 (fp8 e4m3fn), got %d", mode);
+  return KV4_OK;
+}
 
-extern "C" {
+int check_head_pth(int32_t head_size) {
+  if (head_size < 8 || head_size > 256 || head_size % 8 != 0)
+    return fail(KV4_EINVAL, "head_size must be a multiple of 8 in [8, 256], got %d", head_size);
+  return KV4_OK;
+}
 
-const char* kv4_last_error(void) { return g_last_error.c_str(); }
-
-int kv4_rht_write(const void* key, const void* value, int64_t key_token_stride,
-                  int64_t value_token_stride, void* key_cache, void* value_cache,
-                  float* k_scale_cache, float* v_scale_cache, const int64_t* slot_mapping,
-                  int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b,
-                  int32_t block_size, int64_t num_blocks, uint64_t sign_seed, void* stream) {
-  if (int e = check_head(head_size, b)) return e;
+int write_impl(int qm, const char* what, const void* key, const void* value, int64_t key_token_stride,
+               int64_t value_token_stride, void* key_cache, void* value_cache, float* k_scale_cache,
+               float* v_scale_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+               int32_t head_size, int32_t b, int32_t block_size, int64_t num_blocks, uint64_t sign_seed,
+               void* stream) {
   if (num_tokens < 0) return fail(KV4_EINVAL, "num_tokens must be >= 0");
   if (num_kv_heads < 1) return fail(KV4_EINVAL, "num_kv_heads must be >= 1");
   if (block_size < 1 || block_size > 4096) return fail(KV4_EINVAL, "block_size must be in [1, 4096]");
@@ -256,8 +261,67 @@ int kv4_rht_write(const void* key, const void* value, int64_t key_token_stride,
   a.hs = head_size;
   a.b = b;
   a.seed = sign_seed;
-  return hip_status(kv4::launch_write(a, static_cast<hipStream_t>(stream)), "kv4_rht_write launch");
+  a.qm = qm;
+  return hip_status(kv4::launch_write(a, static_cast<hipStream_t>(stream)), what);
 }
+
+int dequant_impl(int qm, const char* what, const void* cache, const float* scale_cache, int64_t num_blocks,
+                 const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                 int32_t b, int32_t block_size, uint64_t sign_seed, int32_t inverse_rotate, float* out,
+                 void* stream) {
+  if (num_tokens < 0) return fail(KV4_EINVAL, "num_tokens must be >= 0");
+  if (num_kv_heads < 1) return fail(KV4_EINVAL, "num_kv_heads must be >= 1");
+  if (block_size < 1 || block_size > 4096) return fail(KV4_EINVAL, "block_size must be in [1, 4096]");
+  if (num_blocks < 0 || num_blocks > INT64_MAX / block_size / num_kv_heads / head_size)
+    return fail(KV4_EINVAL, "num_blocks out of range");
+  if (num_tokens == 0) return ok();
+  if (!cache || !scale_cache || !slot_mapping || !out) return fail(KV4_EINVAL, "null pointer argument");
+  if (!aligned(cache, 16) || !aligned(out, 16) || !aligned(scale_cache, 4) || !aligned(slot_mapping, 8))
+    return fail(KV4_EINVAL, "misaligned pointer");
+  kv4::DequantArgs a;
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.scale = scale_cache;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_slots = num_blocks * block_size;
+  a.nkv = num_kv_heads;
+  a.hs = head_size;
+  a.b = b;
+  a.seed = sign_seed;
+  a.inverse_rotate = inverse_rotate ? 1 : 0;
+  a.out = out;
+  a.qm = qm;
+  return hip_status(kv4::launch_dequant(a, static_cast<hipStream_t>(stream)), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kv4_last_error(void) { return g_last_error.c_str(); }
+
+int kv4_rht_write(const void* key, const void* value, int64_t key_token_stride,
+                  int64_t value_token_stride, void* key_cache, void* value_cache,
+                  float* k_scale_cache, float* v_scale_cache, const int64_t* slot_mapping,
+                  int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b,
+                  int32_t block_size, int64_t num_blocks, uint64_t sign_seed, void* stream) {
+  if (int e = check_head(head_size, b)) return e;
+  return write_impl(0, "kv4_rht_write", key, value, key_token_stride, value_token_stride, key_cache,
+                    value_cache, k_scale_cache, v_scale_cache, slot_mapping, num_tokens, num_kv_heads,
+                    head_size, b, block_size, num_blocks, sign_seed, stream);
+}
+
+int kv4_pth_write(int32_t kv_quant_mode, const void* key, const void* value, int64_t key_token_stride,
+                  int64_t value_token_stride, void* key_cache, void* value_cache, float* k_scale_cache,
+                  float* v_scale_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                  int32_t head_size, int32_t block_size, int64_t num_blocks, void* stream) {
+  if (int e = check_mode(kv_quant_mode)) return e;
+  if (int e = check_head_pth(head_size)) return e;
+  return write_impl(kv_quant_mode, "kv4_pth_write", key, value, key_token_stride, value_token_stride,
+                    key_cache, value_cache, k_scale_cache, v_scale_cache, slot_mapping, num_tokens,
+                    num_kv_heads, head_size, 0, block_size, num_blocks, 0, stream);
+}
+
 
 size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t head_size, int32_t max_query_len,
@@ -370,28 +434,18 @@ int kv4_dequant(const void* cache, const float* scale_cache, int64_t num_blocks,
                 int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size,
                 uint64_t sign_seed, int32_t inverse_rotate, float* out, void* stream) {
   if (int e = check_head(head_size, b)) return e;
-  if (num_tokens < 0) return fail(KV4_EINVAL, "num_tokens must be >= 0");
-  if (num_kv_heads < 1) return fail(KV4_EINVAL, "num_kv_heads must be >= 1");
-  if (block_size < 1 || block_size > 4096) return fail(KV4_EINVAL, "block_size must be in [1, 4096]");
-  if (num_blocks < 0 || num_blocks > INT64_MAX / block_size / num_kv_heads / head_size)
-    return fail(KV4_EINVAL, "num_blocks out of range");
-  if (num_tokens == 0) return ok();
-  if (!cache || !scale_cache || !slot_mapping || !out) return fail(KV4_EINVAL, "null pointer argument");
-  if (!aligned(cache, 16) || !aligned(out, 16) || !aligned(scale_cache, 4) || !aligned(slot_mapping, 8))
-    return fail(KV4_EINVAL, "misaligned pointer");
-  kv4::DequantArgs a;
-  a.cache = static_cast<const uint8_t*>(cache);
-  a.scale = scale_cache;
-  a.slot_mapping = slot_mapping;
-  a.num_tokens = num_tokens;
-  a.num_slots = num_blocks * block_size;
-  a.nkv = num_kv_heads;
-  a.hs = head_size;
-  a.b = b;
-  a.seed = sign_seed;
-  a.inverse_rotate = inverse_rotate ? 1 : 0;
-  a.out = out;
-  return hip_status(kv4::launch_dequant(a, static_cast<hipStream_t>(stream)), "kv4_dequant launch");
+  return dequant_impl(0, "kv4_dequant", cache, scale_cache, num_blocks, slot_mapping, num_tokens, num_kv_heads,
+                      head_size, b, block_size, sign_seed, inverse_rotate, out, stream);
 }
+
+int kv4_pth_dequant(int32_t kv_quant_mode, const void* cache, const float* scale_cache, int64_t num_blocks,
+                    const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                    int32_t block_size, float* out, void* stream) {
+  if (int e = check_mode(kv_quant_mode)) return e;
+  if (int e = check_head_pth(head_size)) return e;
+  return dequant_impl(kv_quant_mode, "kv4_pth_dequant", cache, scale_cache, num_blocks, slot_mapping, num_tokens,
+                      num_kv_heads, head_size, 0, block_size, 0, 0, out, stream);
+}
+
 
 }  // extern "C"

@@ -14,6 +14,7 @@
 namespace kv4 {
 
 constexpr int kWave = 64;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // D: sign i is -1 iff bit 63 of the (i+1)-th SplitMix64 output from state

@@ -31,6 +31,7 @@ struct WriteArgs {
   int hs;
   int b;
   uint64_t seed;
+  int qm;                // 0: int4 RHT; 1: int8 per-token-head; 2: fp8 (e4m3fn) per-token-head
 };
 
 struct DequantArgs {
@@ -45,6 +46,7 @@ struct DequantArgs {
   uint64_t seed;
   int inverse_rotate;
   float* out;
+  int qm;                // as WriteArgs
 };
 
 // Work decomposition of one attention call (chosen on the host from host-known

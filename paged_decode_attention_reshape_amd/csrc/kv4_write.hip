@@ -29,7 +29,44 @@ __device__ __forceinline__ int quant_code(float y, float scale) {
   return (int)q;
 }
 
-template <int LP>
+// Per-token-head control modes (no rotation; the pages' int8_per_token_head
+// and fp8_per_token_head, vLLM PR #40835 review thread): one code byte per
+// element, scale = absmax / qmax.
+//   int8: rint_half_even(x / scale) clamped to [-128, 127];
+//   fp8:  x / scale rounded to the nearest OCP FP8 E4M3 (e4m3fn) value, ties to
+//         the even mantissa, magnitudes >= 448 saturating to 448; the sign bit
+//         follows the quotient's.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {                 // >= 448
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {           // < 2^-6: subnormal steps of 2^-9 (8 -> the first normal)
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {                                // keep 3 mantissa bits, round half to even
+    uint32_t bits = a >> 20;
+    const uint32_t rem = a & 0xFFFFFu;
+    bits += (rem > 0x80000u || (rem == 0x80000u && (bits & 1u))) ? 1u : 0u;
+    code = bits - (120u << 3);            // float32 exponent bias 127 -> e4m3 bias 7
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  return code | sign;
+}
+
+template <int QM>
+__device__ __forceinline__ uint32_t quant_byte(float x, float scale) {
+  if constexpr (QM == 1) {
+    float q = __builtin_rintf(x / scale);
+    q = fminf(fmaxf(q, -128.0f), 127.0f);
+    return (uint32_t)(int)q & 0xFFu;
+  } else {
+    return f32_to_e4m3(x / scale);
+  }
+}
+
+template <int LP, int QM>
 __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
   constexpr int VPW = kWave / LP;                      // vectors per wave
   const int lane = threadIdx.x & (kWave - 1);
@@ -38,8 +75,8 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
   const int nchunk = a.hs >> 3;
   const bool lane_on = jj < nchunk;
 
-  uint32_t sx[4];
-  sign_xor_bf16x8(lane_on ? sign_bits8(a.seed, jj) : 0u, sx);
+  uint32_t sx[4] = {0u, 0u, 0u, 0u};
+  if constexpr (QM == 0) sign_xor_bf16x8(lane_on ? sign_bits8(a.seed, jj) : 0u, sx);
 
   const int64_t n_items = a.num_tokens * 2 * a.nkv;
   const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
@@ -73,30 +110,48 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
       v[2 * k] = bf16_lo(wd[k]);
       v[2 * k + 1] = bf16_hi(wd[k]);
     }
-    fwht_b(v, a.b, jj);
+    if constexpr (QM == 0) fwht_b(v, a.b, jj);
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      v[e] = round_bf16(v[e]);
+      if constexpr (QM == 0) v[e] = round_bf16(v[e]);
       amax = fmaxf(amax, fabsf(v[e]));
     }
     amax = group_max(amax, LP);
-    const float scale = amax / 7.0f;
-    uint32_t packed = 0;
-    if (scale > 0.0f) {
+    if constexpr (QM == 0) {
+      const float scale = amax / 7.0f;
+      uint32_t packed = 0;
+      if (scale > 0.0f) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) packed |= ((uint32_t)quant_code(v[e], scale) & 0xFu) << (4 * e);
-    }
-    if (ok && lane_on) {
-      uint8_t* cache = kind ? a.value_cache : a.key_cache;
-      const int64_t row = slot * a.nkv + h;
-      *reinterpret_cast<uint32_t*>(cache + row * half_row + 4 * jj) = packed;
-      if (jj == 0) (kind ? a.v_scale : a.k_scale)[row] = scale;
+        for (int e = 0; e < 8; ++e) packed |= ((uint32_t)quant_code(v[e], scale) & 0xFu) << (4 * e);
+      }
+      if (ok && lane_on) {
+        uint8_t* cache = kind ? a.value_cache : a.key_cache;
+        const int64_t row = slot * a.nkv + h;
+        *reinterpret_cast<uint32_t*>(cache + row * half_row + 4 * jj) = packed;
+        if (jj == 0) (kind ? a.v_scale : a.k_scale)[row] = scale;
+      }
+    } else {
+      const float scale = amax / (QM == 1 ? 127.0f : 448.0f);
+      uint32_t lo = 0, hi = 0;
+      if (scale > 0.0f) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo |= quant_byte<QM>(v[e], scale) << (8 * e);
+          hi |= quant_byte<QM>(v[e + 4], scale) << (8 * e);
+        }
+      }
+      if (ok && lane_on) {
+        uint8_t* cache = kind ? a.value_cache : a.key_cache;
+        const int64_t row = slot * a.nkv + h;
+        *reinterpret_cast<uint2*>(cache + row * a.hs + 8 * jj) = make_uint2(lo, hi);
+        if (jj == 0) (kind ? a.v_scale : a.k_scale)[row] = scale;
+      }
     }
   }
 }
 
-template <int LP>
+template <int LP, int QM>
 __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   constexpr int VPW = kWave / LP;
   const int lane = threadIdx.x & (kWave - 1);
@@ -123,19 +178,37 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     }
     const bool ok = in && slot >= 0 && slot < a.num_slots;
     uint32_t codes = 0;
+    uint2 bytes = make_uint2(0u, 0u);
     float sc = 0.0f;
     if (ok && lane_on) {
       const int64_t row = slot * a.nkv + h;
-      codes = *reinterpret_cast<const uint32_t*>(a.cache + row * half_row + 4 * jj);
+      if constexpr (QM == 0) codes = *reinterpret_cast<const uint32_t*>(a.cache + row * half_row + 4 * jj);
+      else bytes = *reinterpret_cast<const uint2*>(a.cache + row * a.hs + 8 * jj);
       sc = a.scale[row];
     }
     float v[8];
+    if constexpr (QM == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = ((int)(codes << (28 - 4 * e))) >> 28;   // sign-extend nibble e
-      v[e] = (float)c * sc;
+      for (int e = 0; e < 8; ++e) {
+        const int c = ((int)(codes << (28 - 4 * e))) >> 28;   // sign-extend nibble e
+        v[e] = (float)c * sc;
+      }
+    } else if constexpr (QM == 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = (float)(int)(int8_t)(bytes.x >> (8 * e)) * sc;
+        v[e + 4] = (float)(int)(int8_t)(bytes.y >> (8 * e)) * sc;
+      }
+    } else {
+      // v_cvt_pk_f32_fp8: two e4m3fn bytes (word half lo / hi) -> exact floats
+      const f32x2_t p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)bytes.x, false);
+      const f32x2_t p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)bytes.x, true);
+      const f32x2_t p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)bytes.y, false);
+      const f32x2_t p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)bytes.y, true);
+      v[0] = p0.x * sc; v[1] = p0.y * sc; v[2] = p1.x * sc; v[3] = p1.y * sc;
+      v[4] = p2.x * sc; v[5] = p2.y * sc; v[6] = p3.x * sc; v[7] = p3.y * sc;
     }
-    if (a.inverse_rotate) {
+    if (QM == 0 && a.inverse_rotate) {
       fwht_b(v, a.b, jj);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = apply_sign(v[e] * inv_b, sbits, e);
@@ -150,21 +223,43 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 
 static int lanes_per_vector(int hs) { return host_next_pow2(hs / 8); }
 
+template <int QM>
+static void launch_write_qm(const WriteArgs& a, int LP, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (LP) {
+    case 1: hipLaunchKernelGGL((write_kernel<1, QM>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((write_kernel<2, QM>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((write_kernel<4, QM>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((write_kernel<8, QM>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((write_kernel<16, QM>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((write_kernel<32, QM>), grid, block, 0, stream, a); break;
+  }
+}
+
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream) {
   const int LP = lanes_per_vector(a.hs);
   const int64_t items = a.num_tokens * 2 * a.nkv;
   const int64_t waves = (items + (kWave / LP) - 1) / (kWave / LP);
   const int64_t blocks = std::min<int64_t>((waves + 3) / 4, 256 * 64);
   dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
-  switch (LP) {
-    case 1: hipLaunchKernelGGL(write_kernel<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(write_kernel<2>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(write_kernel<4>, grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(write_kernel<8>, grid, block, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL(write_kernel<16>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(write_kernel<32>, grid, block, 0, stream, a); break;
+  switch (a.qm) {
+    case 0: launch_write_qm<0>(a, LP, grid, block, stream); break;
+    case 1: launch_write_qm<1>(a, LP, grid, block, stream); break;
+    case 2: launch_write_qm<2>(a, LP, grid, block, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int QM>
+static void launch_dequant_qm(const DequantArgs& a, int LP, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (LP) {
+    case 1: hipLaunchKernelGGL((dequant_kernel<1, QM>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((dequant_kernel<2, QM>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((dequant_kernel<4, QM>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((dequant_kernel<8, QM>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((dequant_kernel<16, QM>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((dequant_kernel<32, QM>), grid, block, 0, stream, a); break;
+  }
 }
 
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream) {
@@ -173,13 +268,11 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream) {
   const int64_t waves = (items + (kWave / LP) - 1) / (kWave / LP);
   const int64_t blocks = std::min<int64_t>((waves + 3) / 4, 256 * 64);
   dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
-  switch (LP) {
-    case 1: hipLaunchKernelGGL(dequant_kernel<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(dequant_kernel<2>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(dequant_kernel<4>, grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(dequant_kernel<8>, grid, block, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL(dequant_kernel<16>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(dequant_kernel<32>, grid, block, 0, stream, a); break;
+  switch (a.qm) {
+    case 0: launch_dequant_qm<0>(a, LP, grid, block, stream); break;
+    case 1: launch_dequant_qm<1>(a, LP, grid, block, stream); break;
+    case 2: launch_dequant_qm<2>(a, LP, grid, block, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -23,7 +23,8 @@ def L():
 def test_header_declares_the_boundary():
     assert kv4.header_functions() == sorted([
         "kv4_dequant", "kv4_last_error", "kv4_paged_attention",
-        "kv4_paged_attention_workspace_size", "kv4_rht_write"])
+        "kv4_paged_attention_workspace_size", "kv4_rht_write",
+        "kv4_pth_write", "kv4_pth_dequant"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -154,3 +155,17 @@ def test_python_binding_rejects_cpu_tensors():
         kv4.kv4_rht_write(x, x, torch.zeros((1, 16, 2, 48), dtype=torch.uint8),
                           torch.zeros((1, 16, 2, 48), dtype=torch.uint8),
                           torch.zeros((1, 16, 2)), torch.zeros((1, 16, 2)), torch.zeros(2, dtype=torch.int64))
+
+
+def test_pth_mode_validation(L):
+    # kv_quant_mode must be 1 (int8) or 2 (fp8); checked before anything else
+    rc = L.kv4_pth_write(3, 16, 16, 64, 64, 16, 16, 16, 16, 16, 4, 1, 64, 16, 4, None)
+    assert rc == EINVAL and "kv_quant_mode" in kv4.kv4_last_error()
+    rc = L.kv4_pth_write(1, 16, 16, 64, 64, 16, 16, 16, 16, 16, 4, 1, 60, 16, 4, None)
+    assert rc == EINVAL and "multiple of 8" in kv4.kv4_last_error()
+    rc = L.kv4_pth_dequant(2, 16, 16, 4, 16, 0, 1, 64, 16, 16, None)
+    assert rc == 0
+    rc = L.kv4_pth_dequant(0, 16, 16, 4, 16, 3, 1, 64, 16, 16, None)
+    assert rc == EINVAL
+    with pytest.raises(ValueError):
+        kv4._mode("int4")
