@@ -225,6 +225,33 @@ int kv4_pth_write(int32_t kv_quant_mode, const void* key, const void* value,
                   int64_t num_blocks, void* stream);
 
 /*
+ * kv4_pth_attention_workspace_size / kv4_pth_attention -- the read path over
+ * an int8 / fp8 per-token-head cache: as kv4_paged_attention_workspace_size /
+ * kv4_paged_attention with no rotation, i.e. for each query head
+ *   logit_j = k_scale_j * (q . value(code_K_j)) * softmax_scale,
+ *   out = sum_j softmax(logit)_j * v_scale_j * value(code_V_j)  (bf16),
+ * the same causal rule, GQA mapping, metadata, workspace contract, planner
+ * overrides and error behaviour. Caches as written by kv4_pth_write with the
+ * same kv_quant_mode; KV4_EINVAL for another mode.
+ */
+size_t kv4_pth_attention_workspace_size(int32_t kv_quant_mode, int64_t num_q_tokens,
+                                        int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_size,
+                                        int32_t max_query_len, int32_t max_seq_len);
+int kv4_pth_attention(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
+                      const void* key_cache, const void* value_cache,
+                      const float* k_scale_cache, const float* v_scale_cache,
+                      int64_t num_blocks,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* seq_lens, const int32_t* query_start_loc,
+                      int32_t num_seqs, int64_t num_q_tokens,
+                      int32_t max_query_len, int32_t max_seq_len,
+                      int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_size, int32_t block_size, float softmax_scale,
+                      void* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * kv4_pth_dequant -- gather and dequantize int8 / fp8 cache slots (tests and
  * debugging): out[t, h, i] = value(code) * scale as one float32 product;
  * out-of-range slots give zeros. out float32 [num_tokens, num_kv_heads,

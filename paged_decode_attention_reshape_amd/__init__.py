@@ -44,6 +44,11 @@ _SIGNATURES = {
                                      _c_int64, _c_int32, _c_int32, _c_int32, _c_int64, _vp]),
     "kv4_pth_dequant": (ctypes.c_int, [_c_int32, _vp, _vp, _c_int64, _vp, _c_int64, _c_int32, _c_int32,
                                        _c_int32, _vp, _vp]),
+    "kv4_pth_attention_workspace_size": (ctypes.c_size_t, [_c_int32, _c_int64, _c_int32, _c_int32, _c_int32,
+                                                           _c_int32, _c_int32, _c_int32]),
+    "kv4_pth_attention": (ctypes.c_int, [_c_int32, _vp, _c_int64, _vp, _vp, _vp, _vp, _c_int64, _vp, _c_int32,
+                                         _vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32, _c_int32, _c_int32,
+                                         _c_int32, _c_int32, ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None
@@ -304,4 +309,68 @@ def kv4_pth_dequant(kv_quant_mode, cache: torch.Tensor, scale_cache: torch.Tenso
     rc = lib().kv4_pth_dequant(m, cache.data_ptr(), scale_cache.data_ptr(), nb, slot_mapping.data_ptr(), T, nkv,
                                hs, bs, out.data_ptr(), _stream(stream))
     _check("kv4_pth_dequant", rc)
+    return out
+
+
+def kv4_pth_attention_workspace_size(kv_quant_mode, num_q_tokens: int, num_seqs: int, num_q_heads: int,
+                                     num_kv_heads: int, head_size: int, max_query_len: int,
+                                     max_seq_len: int) -> int:
+    n = lib().kv4_pth_attention_workspace_size(_mode(kv_quant_mode), num_q_tokens, num_seqs, num_q_heads,
+                                               num_kv_heads, head_size, max_query_len, max_seq_len)
+    err = kv4_last_error()
+    if n == 0 and err:
+        raise Kv4Error("kv4_pth_attention_workspace_size", KV4_EINVAL, err)
+    return int(n)
+
+
+def kv4_pth_attention(kv_quant_mode, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                      k_scale_cache: torch.Tensor, v_scale_cache: torch.Tensor, block_table: torch.Tensor,
+                      seq_lens: torch.Tensor, query_start_loc: torch.Tensor, max_query_len: int,
+                      max_seq_len: int, softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Paged causal attention over an int8 / fp8 per-token-head cache
+    [nb, bs, nkv, hs] (no rotation); other arguments as kv4_paged_attention."""
+    m = _mode(kv_quant_mode)
+    _need(query, "query", torch.bfloat16, 3)
+    _need(key_cache, "key_cache", torch.uint8, 4)
+    _need(value_cache, "value_cache", torch.uint8, 4)
+    _need(k_scale_cache, "k_scale_cache", torch.float32, 3)
+    _need(v_scale_cache, "v_scale_cache", torch.float32, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache"), (k_scale_cache, "k_scale_cache"),
+                 (v_scale_cache, "v_scale_cache"), (block_table, "block_table"), (seq_lens, "seq_lens"),
+                 (query_start_loc, "query_start_loc")):
+        _contig(t, n)
+    Tq, nq, hs = query.shape
+    nb, bs, nkv = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]
+    S = seq_lens.shape[0]
+    if key_cache.shape[3] != hs or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shapes disagree with query head_size")
+    if k_scale_cache.shape != (nb, bs, nkv) or v_scale_cache.shape != k_scale_cache.shape:
+        raise ValueError("scale cache shapes disagree with the caches")
+    if query_start_loc.shape[0] != S + 1 or block_table.shape[0] != S:
+        raise ValueError("query_start_loc must be [num_seqs + 1] and block_table [num_seqs, *]")
+    if query.stride(2) != 1 or query.stride(1) != hs:
+        raise ValueError("query must have contiguous heads")
+    if out is None:
+        out = torch.empty((Tq, nq, hs), dtype=torch.bfloat16, device=query.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _contig(out, "out")
+    if out.shape != (Tq, nq, hs):
+        raise ValueError("out must be [num_q_tokens, num_q_heads, head_size]")
+    need = kv4_pth_attention_workspace_size(m, Tq, S, nq, nkv, hs, max_query_len, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if softmax_scale is None:
+        softmax_scale = hs ** -0.5
+    rc = lib().kv4_pth_attention(
+        m, query.data_ptr(), query.stride(0), key_cache.data_ptr(), value_cache.data_ptr(),
+        k_scale_cache.data_ptr(), v_scale_cache.data_ptr(), nb, block_table.data_ptr(), block_table.shape[1],
+        seq_lens.data_ptr(), query_start_loc.data_ptr(), S, Tq, int(max_query_len), int(max_seq_len), nq, nkv,
+        hs, bs, float(softmax_scale), out.data_ptr(), ws_ptr, ws_bytes, _stream(stream))
+    _check("kv4_pth_attention", rc)
     return out

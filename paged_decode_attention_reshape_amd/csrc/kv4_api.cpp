@@ -66,6 +66,7 @@ constexpr int64_t kTargetUnitsMfma = 16384;
 constexpr int kMinSplit = 256;
 constexpr int kSkMaxGrid = 2048;        // stream-K workgroups at most (8 per CU of a 256-CU GPU)
 constexpr int kSkMinSteps = 16;         // stream-K: KV steps per workgroup at least
+constexpr bool kPthMfma = false;        // matrix-core kernels for the int8 / fp8 caches
 
 bool mfma_head_size(int hs) { return hs == 64 || hs == 96 || hs == 128 || hs == 192; }
 
@@ -80,14 +81,17 @@ int mfma_hpw_max(int hs) { return hs == 192 ? 1 : 2; }
 // launch agree. Path 1 (matrix cores) is used where the query block is dense
 // (GQA group > 1 or query_len > 1), the head size is a multiple of 32 the
 // kernel is built for, and pages hold a power-of-two number (>= 16) of tokens.
-int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
+int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
               int32_t max_query_len, int32_t max_seq_len, int32_t block_size, kv4::AttnPlan& p) {
   std::memset(&p, 0, sizeof(p));
   const int G = nq / nkv;
-  const bool mfma_ok = mfma_head_size(hs) && block_size % 16 == 0 && (block_size & (block_size - 1)) == 0;
+  // int8 / fp8 caches (one byte per element) run on the matrix cores at head
+  // sizes 64 and 128 (64- and 128-byte token rows)
+  const bool hs_ok = qm == 0 ? mfma_head_size(hs) : (hs == 64 || hs == 128) && kPthMfma;
+  const bool mfma_ok = hs_ok && block_size % 16 == 0 && (block_size & (block_size - 1)) == 0;
   // Single-query decode with one query head per kv head (G = 1) still fills
   // the matrix-core rows when one wave serves several kv heads.
-  const bool g1_multi = nkv % 2 == 0 && mfma_hpw_max(hs) >= 2;
+  const bool g1_multi = qm == 0 && nkv % 2 == 0 && mfma_hpw_max(hs) >= 2;
   bool mfma = mfma_ok && (G > 1 || max_query_len > 1 || g1_multi);
   if (const char* f = std::getenv("KV4_FORCE_PATH")) {
     if (!std::strcmp(f, "valu")) mfma = false;
@@ -108,7 +112,7 @@ int make_plan(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, i
   // Single-token decode on the matrix cores: one wave serves hpw kv heads
   // (hpw * G <= 16 MFMA rows), sharing its softmax and page walk.
   p.hpw = 1;
-  if (mfma && max_query_len <= 1) {
+  if (mfma && max_query_len <= 1 && qm == 0) {
     long want = env_long("KV4_MFMA_HPW", 0);
     if (want != 1 && want != 2 && want != 4) want = mfma_hpw_max(hs);
     if (want > 2 && (hs == 96 || hs == 192)) want = 2;   // four heads' V loads would exceed the load counter
@@ -294,38 +298,8 @@ int dequant_impl(int qm, const char* what, const void* cache, const float* scale
   return hip_status(kv4::launch_dequant(a, static_cast<hipStream_t>(stream)), what);
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* kv4_last_error(void) { return g_last_error.c_str(); }
-
-int kv4_rht_write(const void* key, const void* value, int64_t key_token_stride,
-                  int64_t value_token_stride, void* key_cache, void* value_cache,
-                  float* k_scale_cache, float* v_scale_cache, const int64_t* slot_mapping,
-                  int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b,
-                  int32_t block_size, int64_t num_blocks, uint64_t sign_seed, void* stream) {
-  if (int e = check_head(head_size, b)) return e;
-  return write_impl(0, "kv4_rht_write", key, value, key_token_stride, value_token_stride, key_cache,
-                    value_cache, k_scale_cache, v_scale_cache, slot_mapping, num_tokens, num_kv_heads,
-                    head_size, b, block_size, num_blocks, sign_seed, stream);
-}
-
-int kv4_pth_write(int32_t kv_quant_mode, const void* key, const void* value, int64_t key_token_stride,
-                  int64_t value_token_stride, void* key_cache, void* value_cache, float* k_scale_cache,
-                  float* v_scale_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
-                  int32_t head_size, int32_t block_size, int64_t num_blocks, void* stream) {
-  if (int e = check_mode(kv_quant_mode)) return e;
-  if (int e = check_head_pth(head_size)) return e;
-  return write_impl(kv_quant_mode, "kv4_pth_write", key, value, key_token_stride, value_token_stride,
-                    key_cache, value_cache, k_scale_cache, v_scale_cache, slot_mapping, num_tokens,
-                    num_kv_heads, head_size, 0, block_size, num_blocks, 0, stream);
-}
-
-
-size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs, int32_t num_q_heads,
-                                          int32_t num_kv_heads, int32_t head_size, int32_t max_query_len,
-                                          int32_t max_seq_len) {
+size_t workspace_impl(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_size, int32_t max_query_len, int32_t max_seq_len) {
   if (check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
                        max_seq_len))
     return 0;
@@ -333,7 +307,7 @@ size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs
   size_t need = 0;
   for (int32_t bs : {16, 1}) {
     kv4::AttnPlan p;
-    if (make_plan(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len, max_seq_len,
+    if (make_plan(qm, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len, max_seq_len,
                   bs, p))
       return 0;
     const size_t n = ws_layout(p, num_q_tokens, num_seqs, num_q_heads, head_size).total;
@@ -343,15 +317,13 @@ size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs
   return need;
 }
 
-int kv4_paged_attention(const void* query, int64_t query_token_stride, const void* key_cache,
-                        const void* value_cache, const float* k_scale_cache, const float* v_scale_cache,
-                        int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
-                        const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
-                        int64_t num_q_tokens, int32_t max_query_len, int32_t max_seq_len,
-                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size, int32_t b,
-                        int32_t block_size, uint64_t sign_seed, float softmax_scale, void* out,
-                        void* workspace, size_t workspace_bytes, void* stream) {
-  if (int e = check_head(head_size, b)) return e;
+int attention_impl(int qm, const void* query, int64_t query_token_stride, const void* key_cache,
+                   const void* value_cache, const float* k_scale_cache, const float* v_scale_cache,
+                   int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                   const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                   int64_t num_q_tokens, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size, uint64_t sign_seed,
+                   float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (int e = check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
                                max_seq_len))
     return e;
@@ -376,7 +348,7 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride, const voi
   kv4::AttnArgs a;
   std::memset(&a, 0, sizeof(a));
   if (num_blocks < 1) return fail(KV4_EINVAL, "num_blocks must be >= 1 when there are query tokens");
-  if (int e = make_plan(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
+  if (int e = make_plan(qm, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
                        max_seq_len, block_size, a.plan))
     return e;
   const WsLayout ws = ws_layout(a.plan, num_q_tokens, num_seqs, num_q_heads, head_size);
@@ -413,6 +385,9 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride, const voi
   a.b = b;
   a.bs = block_size;
   a.seed = sign_seed;
+  a.qm = qm;
+  // int4: logits scale by softmax_scale / b; the per-token-head modes have no
+  // rotation and pass b = 1
   a.scale_log2 = softmax_scale / (float)b * 1.4426950408889634f;
   a.out = static_cast<uint16_t*>(out);
   a.prefix = prefix;
@@ -429,6 +404,82 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride, const voi
     return hip_status(kv4::launch_attn_reduce(a, st), "kv4_paged_attention merge launch");
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
+
+const char* kv4_last_error(void) { return g_last_error.c_str(); }
+
+int kv4_rht_write(const void* key, const void* value, int64_t key_token_stride,
+                  int64_t value_token_stride, void* key_cache, void* value_cache,
+                  float* k_scale_cache, float* v_scale_cache, const int64_t* slot_mapping,
+                  int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b,
+                  int32_t block_size, int64_t num_blocks, uint64_t sign_seed, void* stream) {
+  if (int e = check_head(head_size, b)) return e;
+  return write_impl(0, "kv4_rht_write", key, value, key_token_stride, value_token_stride, key_cache,
+                    value_cache, k_scale_cache, v_scale_cache, slot_mapping, num_tokens, num_kv_heads,
+                    head_size, b, block_size, num_blocks, sign_seed, stream);
+}
+
+int kv4_pth_write(int32_t kv_quant_mode, const void* key, const void* value, int64_t key_token_stride,
+                  int64_t value_token_stride, void* key_cache, void* value_cache, float* k_scale_cache,
+                  float* v_scale_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                  int32_t head_size, int32_t block_size, int64_t num_blocks, void* stream) {
+  if (int e = check_mode(kv_quant_mode)) return e;
+  if (int e = check_head_pth(head_size)) return e;
+  return write_impl(kv_quant_mode, "kv4_pth_write", key, value, key_token_stride, value_token_stride,
+                    key_cache, value_cache, k_scale_cache, v_scale_cache, slot_mapping, num_tokens,
+                    num_kv_heads, head_size, 0, block_size, num_blocks, 0, stream);
+}
+
+
+size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_size, int32_t max_query_len,
+                                          int32_t max_seq_len) {
+  return workspace_impl(0, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
+                        max_seq_len);
+}
+
+size_t kv4_pth_attention_workspace_size(int32_t kv_quant_mode, int64_t num_q_tokens, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                                        int32_t max_query_len, int32_t max_seq_len) {
+  if (check_mode(kv_quant_mode)) return 0;
+  return workspace_impl(kv_quant_mode, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size,
+                        max_query_len, max_seq_len);
+}
+
+
+int kv4_paged_attention(const void* query, int64_t query_token_stride, const void* key_cache,
+                        const void* value_cache, const float* k_scale_cache, const float* v_scale_cache,
+                        int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                        int64_t num_q_tokens, int32_t max_query_len, int32_t max_seq_len,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size, int32_t b,
+                        int32_t block_size, uint64_t sign_seed, float softmax_scale, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (int e = check_head(head_size, b)) return e;
+  return attention_impl(0, query, query_token_stride, key_cache, value_cache, k_scale_cache, v_scale_cache,
+                        num_blocks, block_table, max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                        num_q_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_size, b,
+                        block_size, sign_seed, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int kv4_pth_attention(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
+                      const void* key_cache, const void* value_cache, const float* k_scale_cache,
+                      const float* v_scale_cache, int64_t num_blocks, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, const int32_t* seq_lens, const int32_t* query_start_loc,
+                      int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len, int32_t max_seq_len,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                      float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int e = check_mode(kv_quant_mode)) return e;
+  if (int e = check_head_pth(head_size)) return e;
+  return attention_impl(kv_quant_mode, query, query_token_stride, key_cache, value_cache, k_scale_cache,
+                        v_scale_cache, num_blocks, block_table, max_blocks_per_seq, seq_lens, query_start_loc,
+                        num_seqs, num_q_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_size,
+                        1, block_size, 0, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
 
 int kv4_dequant(const void* cache, const float* scale_cache, int64_t num_blocks, const int64_t* slot_mapping,
                 int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size,

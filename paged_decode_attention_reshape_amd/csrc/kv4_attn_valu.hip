@@ -22,6 +22,8 @@
 // offset is removed once per dot product with the sum of q', and once per
 // output element with the running sum of p * v_scale. Softmax runs in base 2
 // with softmax_scale / b * log2(e) folded into q'.
+#include <type_traits>
+
 #include "kv4_device.hpp"
 #include "kv4_launch.hpp"
 
@@ -88,6 +90,38 @@ __device__ __forceinline__ void codes_to_u(uint32_t w, float (&u)[8]) {
   u[7] = (float)(hi >> 24);
 }
 
+// 8 code bytes of the per-token-head modes -> exact float values:
+// QM 1 two's-complement int8, QM 2 OCP e4m3fn (v_cvt_pk_f32_fp8).
+template <int QM>
+__device__ __forceinline__ void bytes_to_f(uint2 w, float (&u)[8]) {
+  if constexpr (QM == 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u[e] = (float)(int)(int8_t)(w.x >> (8 * e));
+      u[e + 4] = (float)(int)(int8_t)(w.y >> (8 * e));
+    }
+  } else {
+    const f32x2_t p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+    const f32x2_t p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+    const f32x2_t p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+    const f32x2_t p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+    u[0] = p0.x; u[1] = p0.y; u[2] = p1.x; u[3] = p1.y;
+    u[4] = p2.x; u[5] = p2.y; u[6] = p3.x; u[7] = p3.y;
+  }
+}
+
+// Store of one output row chunk without a rotation (per-token-head modes), bf16.
+__device__ __forceinline__ void store_out_plain(const float (&o)[8], uint16_t* dst, bool do_store) {
+  if (do_store) {
+    uint4 w;
+    w.x = pack_bf16x2(o[0], o[1]);
+    w.y = pack_bf16x2(o[2], o[3]);
+    w.z = pack_bf16x2(o[4], o[5]);
+    w.w = pack_bf16x2(o[6], o[7]);
+    *reinterpret_cast<uint4*>(dst) = w;
+  }
+}
+
 // Inverse rotation and store of one output row chunk: o = D.H.o'/b, bf16.
 // LPMAX > 0: at most LPMAX lanes per vector, with the lane distances fixed at
 // compile time (no dispatch on them); LPMAX = 0: any b.
@@ -108,7 +142,8 @@ __device__ __forceinline__ void store_out_row(float (&o)[8], int b, int jj, uint
   }
 }
 
-template <int R>
+// QM: 0 int4 RHT cache; 1 / 2 int8 / fp8 per-token-head cache (no rotation).
+template <int R, int QM>
 __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
   const int lane = threadIdx.x;
   const int hs = a.hs;
@@ -136,11 +171,12 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
   const int k1 = min(k0 + a.plan.split_tokens, kend);
   if (k0 >= k1 && a.plan.num_splits > 1) return;      // nothing here; the merge skips this split
 
-  const uint32_t sbits = lane_on ? sign_bits8(a.seed, jj) : 0u;
+  const uint32_t sbits = (QM == 0 && lane_on) ? sign_bits8(a.seed, jj) : 0u;
   uint32_t sx[4];
   sign_xor_bf16x8(sbits, sx);
 
   // ---- q' = H.D.q * (softmax_scale / b * log2 e), rows r = ti * gh + hi
+  // (per-token-head modes: q' = q * softmax_scale * log2 e)
   float qv[R][8];
   float qsum[R];
   int rpos[R];
@@ -161,7 +197,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
       qv[r][2 * k] = bf16_lo(wd[k]);
       qv[r][2 * k + 1] = bf16_hi(wd[k]);
     }
-    fwht_b(qv[r], a.b, jj);
+    if constexpr (QM == 0) fwht_b(qv[r], a.b, jj);
     float sum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -196,28 +232,36 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
       row = ((int64_t)page * a.bs + (tok % a.bs)) * nkv + g;
     }
     uint32_t kw = 0u, vw = 0u;
+    uint2 kb = make_uint2(0u, 0u), vb = make_uint2(0u, 0u);
     float ks = 0.0f, vs = 0.0f;
     if (valid) {
       ks = a.k_scale[row];
       vs = a.v_scale[row];
       if (lane_on) {
-        kw = *reinterpret_cast<const uint32_t*>(a.key_cache + row * half_row + 4 * jj);
-        vw = *reinterpret_cast<const uint32_t*>(a.value_cache + row * half_row + 4 * jj);
+        if constexpr (QM == 0) {
+          kw = *reinterpret_cast<const uint32_t*>(a.key_cache + row * half_row + 4 * jj);
+          vw = *reinterpret_cast<const uint32_t*>(a.value_cache + row * half_row + 4 * jj);
+        } else {
+          kb = *reinterpret_cast<const uint2*>(a.key_cache + row * hs + 8 * jj);
+          vb = *reinterpret_cast<const uint2*>(a.value_cache + row * hs + 8 * jj);
+        }
       }
     }
     float u[8];
-    codes_to_u(kw, u);
+    if constexpr (QM == 0) codes_to_u(kw, u);
+    else bytes_to_f<QM>(kb, u);
     float logit[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float d = -8.0f * qsum[r];
+      float d = QM == 0 ? -8.0f * qsum[r] : 0.0f;    // int4: u = code + 8
 #pragma unroll
       for (int e = 0; e < 8; ++e) d = fmaf(qv[r][e], u[e], d);
       d = lane_on ? d : 0.0f;
       logit[r] = group_sum(d, LPT) * ks;
       if (!valid || tok > rpos[r]) logit[r] = -INFINITY;
     }
-    codes_to_u(vw, u);
+    if constexpr (QM == 0) codes_to_u(vw, u);
+    else bytes_to_f<QM>(vb, u);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float mx = logit[r];
@@ -250,8 +294,10 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[r][e] += xor_lane_rt(acc[r][e], dd);
     }
+    if constexpr (QM == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(-8.0f, psum[r], acc[r][e]);
+      for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(-8.0f, psum[r], acc[r][e]);
+    }
   }
 
   const float inv_b = 1.0f / (float)a.b;
@@ -266,8 +312,11 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
       float o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = acc[r][e] * inv_l;
-      store_out_row(o, a.b, jj, sbits, inv_b, a.out + (qrow * a.nq + h) * hs + 8 * jj,
-                    rv && lane_on && tg == 0);
+      if constexpr (QM == 0)
+        store_out_row(o, a.b, jj, sbits, inv_b, a.out + (qrow * a.nq + h) * hs + 8 * jj,
+                      rv && lane_on && tg == 0);
+      else
+        store_out_plain(o, a.out + (qrow * a.nq + h) * hs + 8 * jj, rv && lane_on && tg == 0);
     } else if (rv && tg == 0) {
       const int64_t prow = ((int64_t)sp * a.num_q_tokens + qrow) * a.nq + h;
       if (lane_on) {
@@ -297,7 +346,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   const int grp = lane / LP;
   const bool lane_on = jj < (hs >> 3);
   const int64_t n_rows = a.num_q_tokens * a.nq;
-  const uint32_t sbits = lane_on ? sign_bits8(a.seed, jj) : 0u;
+  const uint32_t sbits = (a.qm == 0 && lane_on) ? sign_bits8(a.seed, jj) : 0u;
   const float inv_b = 1.0f / (float)a.b;
   const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
@@ -408,18 +457,28 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
     const float inv_l = Ls > 0.0f ? 1.0f / Ls : 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] *= inv_l;
-    store_out_row<LP>(o, a.b, jj, sbits, inv_b, a.out + row * hs + 8 * jj, lane_on && grp == 0);
+    if (a.qm == 0) store_out_row<LP>(o, a.b, jj, sbits, inv_b, a.out + row * hs + 8 * jj, lane_on && grp == 0);
+    else store_out_plain(o, a.out + row * hs + 8 * jj, lane_on && grp == 0);
   }
 }
 
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream) {
   const int64_t gx = a.plan.n_qtiles * a.plan.n_head_tiles;
   dim3 grid((unsigned)gx, (unsigned)a.nkv, (unsigned)a.plan.num_splits), block(64);
-  switch (a.plan.rows) {
-    case 1: hipLaunchKernelGGL(attn_valu_kernel<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(attn_valu_kernel<2>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(attn_valu_kernel<4>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(attn_valu_kernel<8>, grid, block, 0, stream, a); break;
+  auto go = [&](auto qm) {
+    constexpr int QM = decltype(qm)::value;
+    switch (a.plan.rows) {
+      case 1: hipLaunchKernelGGL((attn_valu_kernel<1, QM>), grid, block, 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((attn_valu_kernel<2, QM>), grid, block, 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((attn_valu_kernel<4, QM>), grid, block, 0, stream, a); break;
+      default: hipLaunchKernelGGL((attn_valu_kernel<8, QM>), grid, block, 0, stream, a); break;
+    }
+  };
+  switch (a.qm) {
+    case 0: go(std::integral_constant<int, 0>()); break;
+    case 1: go(std::integral_constant<int, 1>()); break;
+    case 2: go(std::integral_constant<int, 2>()); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -98,6 +98,7 @@ struct AttnArgs {
   float* ws_ml;        // [num_splits][num_q_tokens][nq][2]    (split only)
                        // stream-K: [sk_pcap + quads * num_seqs][nq][hs] and [..][nq][2]
   const int32_t* prefix;   // MFMA path: device plan output (stream-K: first KV step per sequence)
+  int qm;                  // 0: int4 RHT cache; 1 / 2: int8 / fp8 per-token-head cache (no rotation)
   AttnPlan plan;
 };
 

@@ -24,7 +24,7 @@ def test_header_declares_the_boundary():
     assert kv4.header_functions() == sorted([
         "kv4_dequant", "kv4_last_error", "kv4_paged_attention",
         "kv4_paged_attention_workspace_size", "kv4_rht_write",
-        "kv4_pth_write", "kv4_pth_dequant"])
+        "kv4_pth_write", "kv4_pth_dequant", "kv4_pth_attention", "kv4_pth_attention_workspace_size"])
 
 
 def test_every_declared_symbol_is_exported(L):
