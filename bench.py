@@ -42,24 +42,30 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def attention_bytes(w) -> int:
+def code_bytes(w, mode: str) -> int:
+    """Code bytes of one (token, kv head) row of one cache: int4 packs two
+    codes per byte; int8 / fp8 take one byte per element."""
+    return w.head_size // 2 if mode == "int4" else w.head_size
+
+
+def attention_bytes(w, mode: str = "int4") -> int:
     """Algorithmic bytes one attention pass must move: for every sequence,
-    every visible (KV token, kv head): hs/2 + hs/2 code bytes + 2 fp32 scales;
+    every visible (KV token, kv head): the K and V code rows + 2 fp32 scales;
     plus block-table entries, bf16 query in and bf16 output out."""
-    kv = sum(w.seq_lens) * w.num_kv_heads * (w.head_size + 8)
+    kv = kv_bytes(w, mode)
     bt = sum(-(-L // w.block_size) for L in w.seq_lens) * 4
     qo = w.num_q_tokens * w.num_q_heads * w.head_size * 2 * 2
     return int(kv + bt + qo)
 
 
-def kv_bytes(w) -> int:
-    return int(sum(w.seq_lens) * w.num_kv_heads * (w.head_size + 8))
+def kv_bytes(w, mode: str = "int4") -> int:
+    return int(sum(w.seq_lens) * w.num_kv_heads * (2 * code_bytes(w, mode) + 8))
 
 
-def write_bytes_per_token(w) -> int:
-    """Read bf16 K and V, write int4 codes and two fp32 scales per kv head,
+def write_bytes_per_token(w, mode: str = "int4") -> int:
+    """Read bf16 K and V, write the codes and two fp32 scales per kv head,
     read one int64 slot."""
-    return w.num_kv_heads * (4 * w.head_size + w.head_size + 8) + 8
+    return w.num_kv_heads * (4 * w.head_size + 2 * code_bytes(w, mode) + 8) + 8
 
 
 def main():
@@ -68,6 +74,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama8b_long")
+    ap.add_argument("--kv-mode", default="int4", choices=["int4", "int8", "fp8"],
+                    help="cache format: int4 RHT (the method) or the per-token-head int8 / fp8 controls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -115,11 +123,18 @@ def main():
     ctx_rows = np.nonzero(ctx_mask)[0]
 
     nb, bs, nkv, hs = lay.num_blocks, w.block_size, w.num_kv_heads, w.head_size
-    kc = torch.zeros((nb, bs, nkv, hs // 2), dtype=torch.uint8, device=dev)
+    mode = args.kv_mode
+    kc = torch.zeros((nb, bs, nkv, code_bytes(w, mode)), dtype=torch.uint8, device=dev)
     vc = torch.zeros_like(kc)
     ks = torch.zeros((nb, bs, nkv), dtype=torch.float32, device=dev)
     vs = torch.zeros_like(ks)
     stream = torch.cuda.Stream()
+
+    def write(k, v, slots):
+        if mode == "int4":
+            kv4.kv4_rht_write(k, v, kc, vc, ks, vs, slots, sign_seed=w.sign_seed, stream=stream)
+        else:
+            kv4.kv4_pth_write(mode, k, v, kc, vc, ks, vs, slots, stream=stream)
 
     # ---- bulk write of every context token (timed on its own)
     ctx_idx = torch.from_numpy(ctx_rows).to(dev)
@@ -132,7 +147,7 @@ def main():
     with torch.cuda.stream(stream):
         for rep in range(3):
             ev[0].record(stream)
-            kv4.kv4_rht_write(k_ctx, v_ctx, kc, vc, ks, vs, s_ctx, sign_seed=w.sign_seed, stream=stream)
+            write(k_ctx, v_ctx, s_ctx)
             ev[1].record(stream)
             stream.synchronize()
             wr_ms.append(ev[0].elapsed_time(ev[1]))
@@ -140,7 +155,7 @@ def main():
     n_ctx = int(ctx_rows.shape[0])
     write_ms = float(np.median(wr_ms))
     write_tps = n_ctx / (write_ms * 1e-3) if n_ctx else 0.0
-    write_gbs = n_ctx * write_bytes_per_token(w) / (write_ms * 1e-3) / 1e9 if n_ctx else 0.0
+    write_gbs = n_ctx * write_bytes_per_token(w, mode) / (write_ms * 1e-3) / 1e9 if n_ctx else 0.0
 
     # ---- step inputs
     new_idx = torch.from_numpy(new_rows).to(dev)
@@ -152,17 +167,25 @@ def main():
     slens = torch.from_numpy(lay.seq_lens).to(dev)
     qsl = torch.from_numpy(lay.query_start_loc).to(dev)
     out = torch.empty((w.num_q_tokens, w.num_q_heads, hs), dtype=torch.bfloat16, device=dev)
-    need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, w.num_q_heads, nkv, hs,
-                                                  w.max_query_len, w.max_seq_len)
+    if mode == "int4":
+        need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, w.num_q_heads, nkv, hs,
+                                                      w.max_query_len, w.max_seq_len)
+    else:
+        need = kv4.kv4_pth_attention_workspace_size(mode, w.num_q_tokens, w.num_seqs, w.num_q_heads, nkv, hs,
+                                                    w.max_query_len, w.max_seq_len)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
     def step(e_a=None, e_b=None):
-        kv4.kv4_rht_write(k_new, v_new, kc, vc, ks, vs, s_new, sign_seed=w.sign_seed, stream=stream)
+        write(k_new, v_new, s_new)
         if e_a is not None:
             e_a.record(stream)
-        kv4.kv4_paged_attention(q, kc, vc, ks, vs, bt, slens, qsl, max_query_len=w.max_query_len,
-                                max_seq_len=w.max_seq_len, sign_seed=w.sign_seed, out=out, workspace=ws,
-                                stream=stream)
+        if mode == "int4":
+            kv4.kv4_paged_attention(q, kc, vc, ks, vs, bt, slens, qsl, max_query_len=w.max_query_len,
+                                    max_seq_len=w.max_seq_len, sign_seed=w.sign_seed, out=out, workspace=ws,
+                                    stream=stream)
+        else:
+            kv4.kv4_pth_attention(mode, q, kc, vc, ks, vs, bt, slens, qsl, max_query_len=w.max_query_len,
+                                  max_seq_len=w.max_seq_len, out=out, workspace=ws, stream=stream)
         if e_b is not None:
             e_b.record(stream)
 
@@ -184,7 +207,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     attn_avg_ms = float(np.mean(attn_ms))
 
-    a_bytes = attention_bytes(w)
+    a_bytes = attention_bytes(w, mode)
     value = a_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = a_bytes / (attn_avg_ms * 1e-3) / 1e9
 
@@ -192,14 +215,15 @@ def main():
     if os.path.exists(PROFILE_COUNTERS):
         try:
             pc = json.load(open(PROFILE_COUNTERS))
-            ent = pc.get("workloads", {}).get(w.name)
+            ent = pc.get("workloads", {}).get(w.name if mode == "int4" else f"{w.name}_{mode}")
             if ent and pc.get("kernel_source_hash") == kernel_source_hash():
                 traffic = ent.get("traffic_bytes_per_launch")
         except Exception:
             traffic = None
 
     line = {
-        "metric": "INT4 paged decode attn: KV GB/s & % HBM peak; cache-write tokens/s",
+        "metric": "INT4 paged decode attn: KV GB/s & % HBM peak; cache-write tokens/s"
+                  + ("" if mode == "int4" else f" ({mode} per-token-head control cache)"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -209,9 +233,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes / fp32 accumulate (bf16 in/out)",
+        "dtype": f"{mode} codes / fp32 accumulate (bf16 in/out)",
         "data": "synthetic seeded N(0,1) bf16, 1% outlier channels x20",
-        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+        "config": {"workload": w.name, "kv_cache": mode, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": nkv, "head_size": hs, "block_size": bs,
                    "total_kv_tokens": w.total_kv_tokens, "max_seq_len": w.max_seq_len,
                    "q_tokens_per_step": w.num_q_tokens, "new_kv_tokens_per_step": int(new_rows.shape[0]),
@@ -219,22 +243,23 @@ def main():
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "attn_ms": round(attn_avg_ms, 4),
         "attn_query_tokens_per_s": round(w.num_q_tokens / (attn_avg_ms * 1e-3), 1),
-        "kv_bytes_per_step": kv_bytes(w),
+        "kv_bytes_per_step": kv_bytes(w, mode),
         "write_tokens_per_s": round(write_tps, 1),
         "write_GBps": round(write_gbs, 2),
         "write_bulk_tokens": n_ctx,
-        "roofline": {"bound": "hbm", "kernel": "kv4_paged_attention (split-KV attention + merge)",
+        "roofline": {"bound": "hbm", "kernel": ("kv4_paged_attention" if mode == "int4" else "kv4_pth_attention")
+                     + " (attention + merge)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": a_bytes},
     }
 
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, lay, t, kc, vc, ks, vs, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, lay, t, kc, vc, ks, vs, args.cpu_seconds, mode)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float):
+def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float, mode: str = "int4"):
     """The CPU oracle (fp64 numpy) on a bounded sample of the same workload:
     whole sequences of this batch, read from the GPU-written cache, until
     about `budget_s` seconds of CPU work; reported as KV GB/s like `value`."""
@@ -261,10 +286,14 @@ def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float):
         bt = np.zeros_like(lay.block_table)
         bt[s, :n] = np.arange(n)
         t0 = time.perf_counter()
-        O.paged_attention(q, kcs, vcs, kss, vss, bt, lay.seq_lens, lay.query_start_loc,
-                          w.head_size ** -0.5, w.sign_seed, seqs=[int(s)])
+        if mode == "int4":
+            O.paged_attention(q, kcs, vcs, kss, vss, bt, lay.seq_lens, lay.query_start_loc,
+                              w.head_size ** -0.5, w.sign_seed, seqs=[int(s)])
+        else:
+            O.pth_paged_attention(q, kcs, vcs, kss, vss, bt, lay.seq_lens, lay.query_start_loc,
+                                  w.head_size ** -0.5, mode, seqs=[int(s)])
         spent += time.perf_counter() - t0
-        done_bytes += int(w.seq_lens[s]) * w.num_kv_heads * (w.head_size + 8)
+        done_bytes += int(w.seq_lens[s]) * w.num_kv_heads * (2 * code_bytes(w, mode) + 8)
         done_seqs += 1
         if spent >= budget_s:
             break

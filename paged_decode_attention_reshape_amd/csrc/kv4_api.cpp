@@ -66,7 +66,7 @@ constexpr int64_t kTargetUnitsMfma = 16384;
 constexpr int kMinSplit = 256;
 constexpr int kSkMaxGrid = 2048;        // stream-K workgroups at most (8 per CU of a 256-CU GPU)
 constexpr int kSkMinSteps = 16;         // stream-K: KV steps per workgroup at least
-constexpr bool kPthMfma = false;        // matrix-core kernels for the int8 / fp8 caches
+constexpr bool kPthMfma = true;        // matrix-core kernels for the int8 / fp8 caches
 
 bool mfma_head_size(int hs) { return hs == 64 || hs == 96 || hs == 128 || hs == 192; }
 
@@ -85,14 +85,14 @@ int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_
               int32_t max_query_len, int32_t max_seq_len, int32_t block_size, kv4::AttnPlan& p) {
   std::memset(&p, 0, sizeof(p));
   const int G = nq / nkv;
-  // int8 / fp8 caches (one byte per element) run on the matrix cores at head
-  // sizes 64 and 128 (64- and 128-byte token rows)
-  const bool hs_ok = qm == 0 ? mfma_head_size(hs) : (hs == 64 || hs == 128) && kPthMfma;
+  const bool hs_ok = mfma_head_size(hs) && (qm == 0 || kPthMfma);
   const bool mfma_ok = hs_ok && block_size % 16 == 0 && (block_size & (block_size - 1)) == 0;
   // Single-query decode with one query head per kv head (G = 1) still fills
   // the matrix-core rows when one wave serves several kv heads.
   const bool g1_multi = qm == 0 && nkv % 2 == 0 && mfma_hpw_max(hs) >= 2;
-  bool mfma = mfma_ok && (G > 1 || max_query_len > 1 || g1_multi);
+  // (int8 / fp8: the matrix-core kernel's LDS pipeline streams the twice
+  // larger rows faster than the vector kernel even with one busy MFMA row)
+  bool mfma = mfma_ok && (G > 1 || max_query_len > 1 || g1_multi || qm != 0);
   if (const char* f = std::getenv("KV4_FORCE_PATH")) {
     if (!std::strcmp(f, "valu")) mfma = false;
     if (!std::strcmp(f, "mfma")) mfma = mfma_ok;
@@ -119,7 +119,9 @@ int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_
     while (want > 1 && (want * G > kMfmaRows || nkv % want != 0)) want >>= 1;
     p.hpw = (int)want;
   }
-  p.wpb = p.hpw == 4 ? 2 : 4;
+  // waves per workgroup, as the kernels are built: two at four heads per wave
+  // and for int8 / fp8 at head size 192, else four
+  p.wpb = (p.hpw == 4 || (qm != 0 && hs >= 192)) ? 2 : 4;
   // Single-token decode on the matrix cores, with whole workgroups of kv head
   // groups: stream-K partition of the KV steps over the resident workgroups
   // (no split size; every workgroup gets the same number of steps).

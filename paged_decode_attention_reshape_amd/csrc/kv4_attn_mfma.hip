@@ -101,6 +101,65 @@ __device__ __forceinline__ uint32_t pair_byte(uint32_t a, uint32_t b, int jb) {
   return __builtin_amdgcn_perm(b, a, sel);
 }
 
+// ---- one-byte codes of the per-token-head int8 / fp8 caches -> fp16 pairs
+// (exact). int8: the fp16 of 1024 + (code + 128) = 1152 + code, i.e. the
+// offset byte under the exponent of 1024; fp8 e4m3fn: v_cvt_scalef32_pk_f16_fp8
+// with unit scale (every finite e4m3 value, subnormals included, is an fp16).
+typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+// 8 consecutive codes (two words) of one token -> A operand of one k-step,
+// natural element order.
+template <int QM>
+__device__ __forceinline__ uint4 k_operand_q(uint32_t w0, uint32_t w1) {
+  if constexpr (QM == 1) {
+    const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+    const uint32_t c = 0x64646464u;
+    return make_uint4(__builtin_amdgcn_perm(c, x0, 0x04010400u), __builtin_amdgcn_perm(c, x0, 0x04030402u),
+                      __builtin_amdgcn_perm(c, x1, 0x04010400u), __builtin_amdgcn_perm(c, x1, 0x04030402u));
+  } else {
+    return make_uint4(fp8x2_to_f16x2<false>(w0), fp8x2_to_f16x2<true>(w0), fp8x2_to_f16x2<false>(w1),
+                      fp8x2_to_f16x2<true>(w1));
+  }
+}
+
+// V^T operands of columns jb and jb + 1 of a lane's 4-column word from 8
+// token words x[0..7] (token order = k order).
+template <int QM>
+__device__ __forceinline__ void v_operands_q(const uint32_t (&x)[8], int jb, uint4& c0, uint4& c1) {
+  if constexpr (QM == 1) {
+    c0 = make_uint4(pair_byte(x[0], x[1], jb) ^ 0x64806480u, pair_byte(x[2], x[3], jb) ^ 0x64806480u,
+                    pair_byte(x[4], x[5], jb) ^ 0x64806480u, pair_byte(x[6], x[7], jb) ^ 0x64806480u);
+    c1 = make_uint4(pair_byte(x[0], x[1], jb + 1) ^ 0x64806480u, pair_byte(x[2], x[3], jb + 1) ^ 0x64806480u,
+                    pair_byte(x[4], x[5], jb + 1) ^ 0x64806480u, pair_byte(x[6], x[7], jb + 1) ^ 0x64806480u);
+  } else {
+    // [a.jb, b.jb, a.jb+1, b.jb+1]: the low pair is column jb, the high pair jb + 1
+    const uint32_t sel = (uint32_t)jb | ((uint32_t)(4 + jb) << 8) | ((uint32_t)(jb + 1) << 16) |
+                         ((uint32_t)(5 + jb) << 24);
+    const uint32_t t01 = __builtin_amdgcn_perm(x[1], x[0], sel), t23 = __builtin_amdgcn_perm(x[3], x[2], sel);
+    const uint32_t t45 = __builtin_amdgcn_perm(x[5], x[4], sel), t67 = __builtin_amdgcn_perm(x[7], x[6], sel);
+    c0 = make_uint4(fp8x2_to_f16x2<false>(t01), fp8x2_to_f16x2<false>(t23), fp8x2_to_f16x2<false>(t45),
+                    fp8x2_to_f16x2<false>(t67));
+    c1 = make_uint4(fp8x2_to_f16x2<true>(t01), fp8x2_to_f16x2<true>(t23), fp8x2_to_f16x2<true>(t45),
+                    fp8x2_to_f16x2<true>(t67));
+  }
+}
+
+// Two floats as an fp16 pair hi (round to nearest even) plus the fp16 pair of
+// the remainders lo (~22 significant bits together).
+__device__ __forceinline__ void split_f16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_f16x2(a, b);
+  const f16x2v_t h = __builtin_bit_cast(f16x2v_t, hi);
+  lo = pack_f16x2(a - (float)h.x, b - (float)h.y);
+}
+__device__ __forceinline__ float f16x2_sum(uint32_t w) {
+  const f16x2v_t h = __builtin_bit_cast(f16x2v_t, w);
+  return (float)h.x + (float)h.y;
+}
+
 template <int HS>
 struct Geo {
   static constexpr int NK = HS / 32;            // QK k-steps; code words per lane per half tile
@@ -118,6 +177,18 @@ __device__ __forceinline__ void v_region(int r, int& w, int& cb) {
   if (r < RDW) { w = 8; cb = 128 * r; }
   else if (r < RDW + RUS) { w = 4; cb = 128 * RDW; }
   else { w = 2; cb = 128 * RDW + 64 * RUS; }
+}
+
+// ... and of the int8 / fp8 caches: 64-column regions with 4 columns per
+// lane (one code word), then a 32-column tail with 2 per lane (head size 96).
+template <int HS, int QM>
+__device__ __forceinline__ void v_region_any(int r, int& w, int& cb) {
+  if constexpr (QM != 0) {
+    w = r < HS / 64 ? 4 : 2;
+    cb = 64 * r;
+  } else {
+    v_region<HS>(r, w, cb);
+  }
 }
 
 template <int HS>
@@ -260,7 +331,32 @@ struct StageGeo {
   static constexpr int BYTES = S_OFF + 256;
 };
 
-// stage slots per wave: loads run kStages - 1 steps ahead of the compute
+// Per-token-head int8 / fp8 caches (one byte per element, token rows of HS
+// bytes):
+//   K  half h, load j : token (l & 15), bytes [HS/4 (l >> 4) + j KSZ, +KSZ)
+//                       of its row (HS/4 bytes per lane in 16- or 12-byte
+//                       loads, lane stride 16)
+//   V  half h         : the 16 token rows packed (row t at t * HS), filled
+//                       by 1 KB loads of 16-byte lanes (byte 16 l + 1024 j
+//                       of the half tile; lanes past its end fetch nothing)
+template <int HS>
+struct StageGeoQ {
+  static_assert(HS % 32 == 0, "head size");
+  static constexpr int KL = HS / 4;                         // K bytes per lane per half tile
+  static constexpr int KSZ = KL % 16 == 0 ? 16 : 12;
+  static constexpr int NKL = KL / KSZ;
+  static constexpr int KSTR = 16, KREG = 1024;
+  static constexpr int KHALF = NKL * KREG;
+  static constexpr int VL = (16 * HS + 1023) / 1024;      // V loads per half tile
+  static constexpr int VHALF = VL * 1024;
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 2 * KHALF;
+  static constexpr int S_OFF = V_OFF + 2 * VHALF;
+  static constexpr int BYTES = S_OFF + 256;
+};
+template <int HS, int QM> struct StageSel { using T = StageGeoQ<HS>; };
+template <int HS> struct StageSel<HS, 0> { using T = StageGeo<HS>; };
+
 // Stage slots per wave: the loads of step it + 1 run during step it. More
 // slots keep more bytes in flight, but then the L2 evicts 128-byte lines
 // before the wave of the neighbouring kv head (which reads the other half of
@@ -271,15 +367,16 @@ constexpr int stages_for() { return 2; }
 // Per wave: kStages stage slots, each holding HPW per-head stages (one per kv
 // head the wave serves); the q' staging buffer and the epilogue buffer
 // overlay them.
-template <int HS, int HPW>
+template <int HS, int HPW, int QM>
 struct MfmaSmem {
-  static constexpr int STAGE_H = StageGeo<HS>::BYTES;       // one kv head
+  static constexpr int STAGE_H = StageSel<HS, QM>::T::BYTES;   // one kv head
   static constexpr int STAGE = HPW * STAGE_H;               // one slot
   static constexpr int BUFB = 16 * HS * 4;                 // q' staging / epilogue (fp32 rows)
   static constexpr int NST = stages_for<HS>();
   static constexpr int MAINB = NST * STAGE > BUFB ? NST * STAGE : BUFB;
   alignas(16) unsigned char main[MAINB];
   float qsum[16];
+  float qrs[16];   // int8 / fp8: power of two that undoes the row scaling of q'
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -323,8 +420,14 @@ template <int HPW> struct MfmaShape;
 template <> struct MfmaShape<1> { static constexpr int WPB = 4, WPE = 3; };
 template <> struct MfmaShape<2> { static constexpr int WPB = 4, WPE = 2; };
 template <> struct MfmaShape<4> { static constexpr int WPB = 2, WPE = 1; };
-template <int HS, int HPW>
-constexpr int mfma_wpe() { return HPW == 1 && HS >= 192 ? 2 : MfmaShape<HPW>::WPE; }
+// int8 / fp8 at head size 192 (12 KB stages): two waves per workgroup, so
+// that three workgroups fit a CU's LDS.
+template <int HS, int HPW, int QM>
+constexpr int mfma_wpb() { return QM != 0 && HS >= 192 ? 2 : MfmaShape<HPW>::WPB; }
+template <int HS, int HPW, int QM>
+constexpr int mfma_wpe() {
+  return HPW == 1 && (HS >= 192 || (QM != 0 && HS >= 96)) ? 2 : MfmaShape<HPW>::WPE;
+}
 
 // HPW = kv heads per wave. HPW = 1: the 16 MFMA rows are the query tile of one
 // kv head (tq tokens x gh query heads). HPW > 1 (single-token decode): rows
@@ -332,17 +435,29 @@ constexpr int mfma_wpe() { return HPW == 1 && HS >= 192 ? 2 : MfmaShape<HPW>::WP
 // QK and PV matrix-core products (rows of the other heads are dropped from S
 // and zeroed in P), while the softmax, the page walk and the address work are
 // shared by the HPW heads.
-template <int HS, int HPW>
-__global__ __launch_bounds__(64 * MfmaShape<HPW>::WPB)
-__attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(AttnArgs a, const int32_t* prefix) {
+//
+// QM selects the cache: 0 the int4 RHT cache above; 1 / 2 the per-token-head
+// int8 / fp8 e4m3fn caches (one byte per element, no rotation; one kv head
+// per wave). For those, K and V codes become fp16 operands exactly (int8 with
+// the offset 1152 removed through the sums of q' and of P as for int4), QK
+// runs on v_mfma_f32_16x16x32_f16 with q' as an fp16 hi + lo pair, and each
+// q' row is first scaled by a power of two that puts its largest element in
+// [2^14, 2^15) (fp16 keeps its full precision whatever the query's range);
+// the logits take the inverse power back.
+template <int HS, int HPW, int QM>
+__global__ __launch_bounds__((64 * mfma_wpb<HS, HPW, QM>()))
+__attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_kernel(AttnArgs a,
+                                                                                  const int32_t* prefix) {
   using GG = Geo<HS>;
-  using SG = StageGeo<HS>;
-  using SM = MfmaSmem<HS, HPW>;
-  constexpr int WPB = MfmaShape<HPW>::WPB;
-  constexpr int NK = GG::NK, NS = GG::NS, NVR = GG::NVR;
+  using SG = typename StageSel<HS, QM>::T;
+  using SM = MfmaSmem<HS, HPW, QM>;
+  constexpr int WPB = mfma_wpb<HS, HPW, QM>();
+  constexpr int NK = GG::NK, NS = GG::NS;
+  constexpr int NVR = QM ? (HS + 63) / 64 : GG::NVR;   // V column regions
   constexpr int LP = (HS / 8) <= 8 ? 8 : ((HS / 8) <= 16 ? 16 : 32);   // lanes per row, chunk mapping
   constexpr int RPP = kWave / LP;                                       // rows per pass
-  constexpr int HALF = HS / 2;
+  constexpr int HALF = QM ? HS : HS / 2;        // code bytes per token row of one kv head
+  static_assert(QM == 0 || HPW == 1, "int8 / fp8: one kv head per wave");
   constexpr int kStages = stages_for<HS>();
   constexpr int STH = SM::STAGE_H;
   __shared__ SM smem_all[WPB];
@@ -372,12 +487,12 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
   // step keeps the two halves of each line together, so each line comes from
   // HBM once. With two or more heads per wave a wave reads whole lines and
   // runs free.
-  const bool wg_sync = HPW == 1 && (n_hg % WPB) == 0;
+  const bool wg_sync = HPW == 1 && HALF % 128 != 0 && (n_hg % WPB) == 0;
 
   // lane constants of the chunk mapping (q setup and epilogue)
   const int cj = lane & (LP - 1);
   const bool c_on = cj < HS / 8;
-  const uint32_t sbits = c_on ? sign_bits8(a.seed, cj) : 0u;
+  const uint32_t sbits = (QM == 0 && c_on) ? sign_bits8(a.seed, cj) : 0u;
   uint32_t sx[4];
   sign_xor_bf16x8(sbits, sx);
 
@@ -386,7 +501,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
   const uint32_t half_bytes = 16u * tok_stride;             // one half tile of a page
   const int64_t page_bytes = (int64_t)bsz * tok_stride;     // one page of one cache
   const int64_t page_rows = (int64_t)bsz * nkv;             // scale entries per page
-  const uint32_t koff = (uint32_t)n * tok_stride + (uint32_t)q4 * (HS / 8);
+  const uint32_t koff = (uint32_t)n * tok_stride + (uint32_t)q4 * (HALF / 4);
   uint32_t vo[4];                                           // token 4*q4 + i, 32-bit column chunk n
 #pragma unroll
   for (int i = 0; i < 4; ++i) vo[i] = (uint32_t)(4 * q4 + i) * tok_stride + 4u * (uint32_t)n;
@@ -395,14 +510,28 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
   // after row, RB bytes each, 1 KB per load). Lane l of a load fetches bytes
   // [16 l % RB, +16) of token row 16 l / RB.
   constexpr int RB = HPW * HALF;                            // V bytes per token row of the wave
-  constexpr bool VJ = RB == 64 || RB == 128;
+  constexpr bool VJ = QM == 0 && (RB == 64 || RB == 128);
   constexpr int RPI = 1024 / RB;                            // token rows per 1 KB load (VJ)
   const uint32_t vj_src = (uint32_t)((16 * lane) / RB) * tok_stride + (uint32_t)((16 * lane) % RB);
   // ... and lane (n, q4) reads, for token 4 q4 + i of a half tile, its column
   // chunk n of head hl at vj_rd[i] + hl * HALF: 4 bytes (8 columns, head
-  // size 128) or 2 bytes (4 columns, head size 64); each 16-lane quarter
-  // reads 64 (32) contiguous bytes of one row, so no two of its lanes share
-  // an LDS bank.
+  // size 128; int8 / fp8: 4 columns of each 64-column region) or 2 bytes (4
+  // columns, head size 64); each 16-lane quarter reads 64 (32) contiguous
+  // bytes of one row, so no two of its lanes share an LDS bank.
+  // int8 / fp8 (packed token rows, any head size): the source of lane l in V
+  // load j of a half tile, and the LDS read offset of lane (n, q4) for token
+  // 4 q4 + i (its word n of the row; the 32-column tail: its 16-bit word n)
+  uint32_t vq_src[QM ? StageGeoQ<HS>::VL : 1];
+  uint32_t vq_rd[4];
+  if constexpr (QM != 0) {
+#pragma unroll
+    for (int j = 0; j < StageGeoQ<HS>::VL; ++j) {
+      const int b = 1024 * j + 16 * lane, t = b / HS;
+      vq_src[j] = t < 16 ? (uint32_t)t * tok_stride + (uint32_t)(b % HS) : 0x80000000u;   // past the range: zeros
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vq_rd[i] = (uint32_t)((4 * q4 + i) * HS) + 4u * (uint32_t)n;
+  }
   uint32_t vj_rd[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -468,15 +597,38 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
         v[2 * k] = bf16_lo(wd[k]);
         v[2 * k + 1] = bf16_hi(wd[k]);
       }
-      fwht_b_ct<LP>(v, a.b, cj);
       float sum = 0.0f;
       uint32_t hw[4], lw[4];
+      if constexpr (QM == 0) {
+        fwht_b_ct<LP>(v, a.b, cj);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        // k-order of element offsets [0, 4, 1, 5, 2, 6, 3, 7]
-        split_bf16x2(v[k] * a.scale_log2, v[k + 4] * a.scale_log2, hw[k], lw[k]);
-        sum += (__uint_as_float(hw[k] << 16) + __uint_as_float(lw[k] << 16)) +
-               (__uint_as_float(hw[k] & 0xFFFF0000u) + __uint_as_float(lw[k] & 0xFFFF0000u));
+        for (int k = 0; k < 4; ++k) {
+          // k-order of element offsets [0, 4, 1, 5, 2, 6, 3, 7]
+          split_bf16x2(v[k] * a.scale_log2, v[k + 4] * a.scale_log2, hw[k], lw[k]);
+          sum += (__uint_as_float(hw[k] << 16) + __uint_as_float(lw[k] << 16)) +
+                 (__uint_as_float(hw[k] & 0xFFFF0000u) + __uint_as_float(lw[k] & 0xFFFF0000u));
+        }
+      } else {
+        float mx = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[e] *= a.scale_log2;
+          mx = fmaxf(mx, fabsf(v[e]));
+        }
+#pragma unroll
+        for (int d = 1; d < LP; d <<= 1) mx = fmaxf(mx, xor_lane_rt(mx, d));
+        // 2^sh puts the row maximum in [2^14, 2^15); sh is kept where both
+        // 2^sh and 2^-sh are normal floats
+        int sh = 141 - (int)((__float_as_uint(mx) >> 23) & 0xFFu);
+        sh = sh < -126 ? -126 : (sh > 126 ? 126 : sh);
+        const float f = __uint_as_float((uint32_t)(sh + 127) << 23);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // natural element order
+          split_f16x2(v[2 * k] * f, v[2 * k + 1] * f, hw[k], lw[k]);
+          sum += f16x2_sum(hw[k]) + f16x2_sum(lw[k]);
+        }
+        if (cj == 0) sm.qrs[r] = __uint_as_float((uint32_t)(127 - sh) << 23);
       }
       sum = group_sum_ct<LP>(c_on ? sum : 0.0f);
       if (c_on) {
@@ -492,7 +644,9 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
       qh[s] = reinterpret_cast<const uint4*>(buf)[(n * HS + q4 * (HS / 4) + 8 * s) / 8];
       ql[s] = reinterpret_cast<const uint4*>(buf)[(16 * HS + n * HS + q4 * (HS / 4) + 8 * s) / 8];
     }
-    const float qbias = 136.0f * sm.qsum[n];
+    // sum of q' times the operand offset of the K codes (int4 136, int8 1152)
+    const float qbias = (QM == 0 ? 136.0f : (QM == 1 ? 1152.0f : 0.0f)) * sm.qsum[n];
+    const float qrs_n = QM == 0 ? 1.0f : sm.qrs[n];
     const bool row_ok = hl_n < HPW && ti_n < ntok && hi_n < nh;
     const int rpos = row_ok ? pos0 + ti_n : -1;
     const float row_add = row_ok ? 0.0f : -INFINITY;    // invalid rows never get weight
@@ -515,7 +669,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
     // loads with an empty buffer range (they fetch nothing and fill the slot
     // with zeros, which is never read).
     constexpr int NLK = HPW * (2 * SG::NKL + 1);   // loads per issue_k
-    constexpr int NLV = VJ ? 2 * (16 / RPI) : HPW * 8 * NVR;   // loads per issue_v
+    constexpr int NLV = QM ? 2 * StageGeoQ<HS>::VL : (VJ ? 2 * (16 / RPI) : HPW * 8 * NVR);   // loads per issue_v
     // VJ: half tile hh of a slot (16 * RB bytes) sits in head hh's V region
     // (2 KB; RB = 128, two or more heads per wave) or at V_OFF + hh KB (RB = 64)
     auto vj_base = [&](auto* st, int hh) { return st + (RB == 128 ? hh * STH : hh * 1024) + SG::V_OFF; };
@@ -579,26 +733,33 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
     auto issue_v = [&](unsigned char* __restrict__ st) {
       const __amdgpu_buffer_rsrc_t rv[2] = {rsrc(a.value_cache + v_bya, v_nrec),
                                             rsrc(a.value_cache + v_byb, v_nrec)};
-      if constexpr (VJ) {
+      if constexpr (QM != 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int j = 0; j < StageGeoQ<HS>::VL; ++j)
+            dma_buf<16>(rv[hh], vq_src[j], st + SG::V_OFF + hh * StageGeoQ<HS>::VHALF + j * 1024);
+      } else if constexpr (VJ) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int j = 0; j < 16 / RPI; ++j)
             dma_buf<16>(rv[hh], vj_src + (uint32_t)(j * RPI) * tok_stride, vj_base(st, hh) + j * 1024);
-        return;
-      }
+      } else {
 #pragma unroll
-      for (int hl = 0; hl < HPW; ++hl) {
-        unsigned char* sth = st + hl * STH;
+        for (int hl = 0; hl < HPW; ++hl) {
+          unsigned char* sth = st + hl * STH;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          unsigned char* dst = sth + SG::V_OFF + i * SG::VBYTES_TOK;
-          const uint32_t o = vo[i & 3] + hl * HALF;
+          for (int i = 0; i < 8; ++i) {
+            unsigned char* dst = sth + SG::V_OFF + i * SG::VBYTES_TOK;
+            const uint32_t o = vo[i & 3] + hl * HALF;
 #pragma unroll
-          for (int r = 0; r < GG::RDW; ++r) dma_buf<4>(rv[i >> 2], o + 64 * r, dst + r * 256);
-          if constexpr (GG::RUS) dma_buf<2>(rv[i >> 2], o - 2u * n + 64 * GG::RDW, dst + GG::RDW * 256);
-          if constexpr (GG::RBY)
-            dma_buf<1>(rv[i >> 2], o - 3u * n + 64 * GG::RDW + 32 * GG::RUS, dst + (GG::RDW + GG::RUS) * 256);
+            for (int r = 0; r < GG::RDW; ++r) dma_buf<4>(rv[i >> 2], o + 64 * r, dst + r * 256);
+            if constexpr (GG::RUS) dma_buf<2>(rv[i >> 2], o - 2u * n + 64 * GG::RDW, dst + GG::RDW * 256);
+            if constexpr (GG::RBY)
+              dma_buf<1>(rv[i >> 2], o - 3u * n + 64 * GG::RDW + 32 * GG::RUS,
+                         dst + (GG::RDW + GG::RUS) * 256);
+          }
         }
       }
     };
@@ -625,6 +786,33 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
       // S^T = K . Q'^T per kv head, both half tiles (q' as hi + lo); lane n
       // keeps the logits of its own row's head
       float s8[8];
+      if constexpr (QM != 0) {
+        // K codes of this lane: token n, bytes [HS/4 q4, +HS/4), both half tiles
+        uint32_t kw[2][2 * NK];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const unsigned char* kr = st + SG::K_OFF + h * SG::KHALF;
+#pragma unroll
+          for (int j = 0; j < SG::NKL; ++j) {
+            const uint32_t* x = reinterpret_cast<const uint32_t*>(kr + j * SG::KREG + 16 * lane);
+#pragma unroll
+            for (int e = 0; e < SG::KSZ / 4; ++e) kw[h][j * (SG::KSZ / 4) + e] = x[e];
+          }
+        }
+        f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+          const uint4 ka = k_operand_q<QM>(kw[0][2 * s], kw[0][2 * s + 1]);
+          const uint4 kb = k_operand_q<QM>(kw[1][2 * s], kw[1][2 * s + 1]);
+          sa = mfma_f16(ka, qh[s], sa);
+          sb = mfma_f16(kb, qh[s], sb);
+          sa = mfma_f16(ka, ql[s], sa);
+          sb = mfma_f16(kb, ql[s], sb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        s8[0] = sa[0]; s8[1] = sa[1]; s8[2] = sa[2]; s8[3] = sa[3];
+        s8[4] = sb[0]; s8[5] = sb[1]; s8[6] = sb[2]; s8[7] = sb[3];
+      } else
 #pragma unroll
       for (int hl = 0; hl < HPW; ++hl) {
         // K code words of this lane: token n, chunk q4, both half tiles
@@ -670,15 +858,18 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
       const float vs8[8] = {vsa.x, vsa.y, vsa.z, vsa.w, vsb.x, vsb.y, vsb.z, vsb.w};
       float lg[8];
       const bool full = base + 32 <= k1 && base + 31 <= pos0 && oka && okb;   // wave-uniform
+      float dq[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dq[i] = QM == 0 ? s8[i] - qbias : (s8[i] - qbias) * qrs_n;
       if (full) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lg[i] = fmaf(s8[i] - qbias, ks8[i], row_add);
+        for (int i = 0; i < 8; ++i) lg[i] = fmaf(dq[i], ks8[i], row_add);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int tok = base + (i < 4 ? 4 * q4 + i : 16 + 4 * q4 + (i - 4));
           const bool ok = tok < k1 && tok <= rpos && (i < 4 ? oka : okb);
-          lg[i] = ok ? (s8[i] - qbias) * ks8[i] : -INFINITY;
+          lg[i] = ok ? dq[i] * ks8[i] : -INFINITY;
         }
       }
       float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),
@@ -721,6 +912,29 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
 
       // O'^T += V^T P^T per kv head, one n-step per V column of this lane's
       // chunks; P^T is zero in the rows of the other heads
+      if constexpr (QM != 0) {
+        // n-step 4 r + j: column 64 r + 4 m + j in MFMA row m (tail region:
+        // 64 r + 2 m + j)
+#pragma unroll
+        for (int r = 0; r < NVR; ++r) {
+          constexpr int R4 = HS / 64;
+          uint32_t x[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const unsigned char* src = st + SG::V_OFF + (i >> 2) * StageGeoQ<HS>::VHALF + vq_rd[i & 3];
+            if (r < R4) x[i] = *reinterpret_cast<const uint32_t*>(src + 64 * r);
+            else x[i] = *reinterpret_cast<const uint16_t*>(src - 2 * n + 64 * R4);
+          }
+#pragma unroll
+          for (int jb = 0; jb < (r < R4 ? 4 : 2); jb += 2) {
+            uint4 c0, c1;
+            v_operands_q<QM>(x, jb, c0, c1);
+            acc[4 * r + jb] = mfma_f16(c0, ph4, acc[4 * r + jb]);
+            acc[4 * r + jb + 1] = mfma_f16(c1, ph4, acc[4 * r + jb + 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      } else
 #pragma unroll
       for (int hl = 0; hl < HPW; ++hl) {
         uint4 phh = ph4;
@@ -764,18 +978,20 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
           }
         }
       }
-      const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);   // fp16 1.0
-      pacc = mfma_f16(ones, ph4, pacc);
+      if constexpr (QM != 2) {   // fp8 codes carry no offset
+        const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);   // fp16 1.0
+        pacc = mfma_f16(ones, ph4, pacc);
+      }
     };
     for (int it = 0; it < nsteps; ++it)
       step(sm.main + (it % kStages) * SM::STAGE, sm.main + ((it + 1) % kStages) * SM::STAGE, it);
     wait_vm<0>();                             // no load may land in LDS after this point
     __builtin_amdgcn_wave_barrier();
 
-    // ---- finish: l over the four lane quarters, remove the +72 offset of the
-    // fp16 V operands (64 + u = 72 + code)
+    // ---- finish: l over the four lane quarters, remove the offset of the
+    // fp16 V operands (int4: 64 + u = 72 + code; int8: 1152 + code)
     l_run = sum_x16_x32(l_run);
-    const float pbias = 72.0f * pacc[0];
+    const float pbias = (QM == 0 ? 72.0f : (QM == 1 ? 1152.0f : 0.0f)) * pacc[0];
     const int qrow = uqbeg + ui0 + ti_n;
     const int h = (kv0 + hl_n) * G + hq0 + hi_n;
     if (partial) {
@@ -788,7 +1004,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < NVR; ++r) {
           int w, cb;
-          v_region<HS>(r, w, cb);
+          v_region_any<HS, QM>(r, w, cb);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             float* d = dst + cb + w * (4 * q4 + rr);
@@ -821,7 +1037,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < NVR; ++r) {
         int w, cb;
-        v_region<HS>(r, w, cb);
+        v_region_any<HS, QM>(r, w, cb);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int c0 = cb + w * (4 * q4 + rr);
@@ -849,9 +1065,11 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = 0.0f;
       }
-      fwht_b_ct<LP>(o, a.b, cj);
+      if constexpr (QM == 0) {
+        fwht_b_ct<LP>(o, a.b, cj);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = apply_sign(o[e] * inv_b, sbits, e);
+        for (int e = 0; e < 8; ++e) o[e] = apply_sign(o[e] * inv_b, sbits, e);
+      }
       if (rv && c_on) {
         uint4 wo;
         wo.x = pack_bf16x2(o[0], o[1]);
@@ -927,22 +1145,24 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW>()))) void attn_mfma_kernel(
 
 static int g_num_cus = 0;
 
-template <int HS, int HPW>
+template <int HS, int HPW, int QM>
 static int resident_blocks() {
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW>),
-                                                     64 * MfmaShape<HPW>::WPB, 0) != hipSuccess || nb < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb,
+                                                     reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM>),
+                                                     64 * mfma_wpb<HS, HPW, QM>(), 0) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
   }
   return per_cu * g_num_cus;
 }
 
-template <int HS>
+template <int HS, int QM>
 static hipError_t launch_hs(AttnArgs& a, const int32_t* prefix, int64_t max_units, hipStream_t stream) {
   if (a.plan.hpw == 4 && Geo<HS>::NVR != 1) return hipErrorInvalidValue;
+  if (QM != 0 && (a.plan.hpw != 1 || a.plan.wpb != mfma_wpb<HS, 1, QM>())) return hipErrorInvalidValue;
   auto go = [&](auto kernel, int wpb, int resident) {
     int64_t wgs;
     if (a.plan.sk) {
@@ -959,13 +1179,18 @@ static hipError_t launch_hs(AttnArgs& a, const int32_t* prefix, int64_t max_unit
     }
     hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(64 * wpb), 0, stream, a, prefix);
   };
+  if constexpr (QM != 0) {
+    go(attn_mfma_kernel<HS, 1, QM>, mfma_wpb<HS, 1, QM>(), resident_blocks<HS, 1, QM>());
+    return hipSuccess;
+  }
   switch (a.plan.hpw) {
-    case 2: go(attn_mfma_kernel<HS, 2>, MfmaShape<2>::WPB, resident_blocks<HS, 2>()); break;
+    case 2: go(attn_mfma_kernel<HS, 2, 0>, MfmaShape<2>::WPB, resident_blocks<HS, 2, 0>()); break;
     case 4:
       // four heads' V loads of a step must fit the 6-bit load counter
-      if constexpr (Geo<HS>::NVR == 1) go(attn_mfma_kernel<HS, 4>, MfmaShape<4>::WPB, resident_blocks<HS, 4>());
+      if constexpr (Geo<HS>::NVR == 1)
+        go(attn_mfma_kernel<HS, 4, 0>, MfmaShape<4>::WPB, resident_blocks<HS, 4, 0>());
       break;
-    default: go(attn_mfma_kernel<HS, 1>, MfmaShape<1>::WPB, resident_blocks<HS, 1>()); break;
+    default: go(attn_mfma_kernel<HS, 1, 0>, MfmaShape<1>::WPB, resident_blocks<HS, 1, 0>()); break;
   }
   return hipSuccess;
 }
@@ -982,12 +1207,29 @@ hipError_t launch_attn_mfma(AttnArgs& a, int32_t* prefix, int64_t max_units, hip
     else
       g_num_cus = 256;
   }
-  switch (a.hs) {
-    case 64: e = launch_hs<64>(a, prefix, max_units, stream); break;
-    case 96: e = launch_hs<96>(a, prefix, max_units, stream); break;
-    case 128: e = launch_hs<128>(a, prefix, max_units, stream); break;
-    case 192: e = launch_hs<192>(a, prefix, max_units, stream); break;
-    default: return hipErrorInvalidValue;
+  if (a.qm == 0) {
+    switch (a.hs) {
+      case 64: e = launch_hs<64, 0>(a, prefix, max_units, stream); break;
+      case 96: e = launch_hs<96, 0>(a, prefix, max_units, stream); break;
+      case 128: e = launch_hs<128, 0>(a, prefix, max_units, stream); break;
+      case 192: e = launch_hs<192, 0>(a, prefix, max_units, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (a.qm == 1 || a.qm == 2) {
+    const bool q1 = a.qm == 1;
+    switch (a.hs) {
+      case 64: e = q1 ? launch_hs<64, 1>(a, prefix, max_units, stream) : launch_hs<64, 2>(a, prefix, max_units, stream); break;
+      case 96: e = q1 ? launch_hs<96, 1>(a, prefix, max_units, stream) : launch_hs<96, 2>(a, prefix, max_units, stream); break;
+      case 128:
+        e = q1 ? launch_hs<128, 1>(a, prefix, max_units, stream) : launch_hs<128, 2>(a, prefix, max_units, stream);
+        break;
+      case 192:
+        e = q1 ? launch_hs<192, 1>(a, prefix, max_units, stream) : launch_hs<192, 2>(a, prefix, max_units, stream);
+        break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
   return hipGetLastError();

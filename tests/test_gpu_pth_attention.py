@@ -20,7 +20,7 @@ G2 = dict(atol=1e-2, rtol=1e-2)
 G4 = dict(atol=5e-2, rtol=5e-2)
 
 
-def _run(w, mode, softmax_scale=None):
+def _run(w, mode, softmax_scale=None, q_gain=1.0):
     say(f"[gpu] pth attention {mode} case {w.name}: nq={w.num_q_heads} nkv={w.num_kv_heads} "
         f"hs={w.head_size} bs={w.block_size} seqs={w.num_seqs} q_tokens={w.num_q_tokens}")
     lay = W.make_layout(w)
@@ -31,6 +31,8 @@ def _run(w, mode, softmax_scale=None):
     vc = torch.zeros_like(kc)
     ks = torch.zeros((lay.num_blocks, bs, nkv), dtype=torch.float32, device=DEV)
     vs = torch.zeros_like(ks)
+    if q_gain != 1.0:
+        t.query = (t.query.float() * q_gain).to(torch.bfloat16)
     kv4.kv4_pth_write(mode, t.key.to(DEV), t.value.to(DEV), kc, vc, ks, vs, torch.from_numpy(slots).to(DEV))
     out = kv4.kv4_pth_attention(
         mode, t.query.to(DEV), kc, vc, ks, vs, torch.from_numpy(lay.block_table).to(DEV),
@@ -64,6 +66,8 @@ CASES = [
     ("gqa4_hs64", 8, 2, 64, [1] * 6, [1000, 1, 16, 17, 2049, 160], 16),
     ("gqa6_hs128_mixed", 12, 2, 128, [1, 37, 1, 5, 1], [90, 300, 2000, 5, 64], 16),
     ("hs192", 8, 2, 192, [1, 3], [700, 129], 16),
+    ("hs192_mha_odd_heads", 6, 6, 192, [1, 1], [333, 1030], 16),
+    ("hs96_prefill", 8, 4, 96, [17, 1], [40, 500], 32),
     ("hs80", 4, 1, 80, [1, 2], [333, 50], 16),
     ("hs256", 4, 2, 256, [1, 1], [100, 257], 16),
     ("hs8", 2, 1, 8, [1, 3], [40, 9], 16),
@@ -75,9 +79,15 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", ["auto", "valu", "mfma"])
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_pth_attention_parity(case, mode):
+def test_pth_attention_parity(case, mode, path, monkeypatch):
+    """Every case on the planner's choice and on each path forced (the matrix
+    core path takes head sizes 64 and 128 with pages a multiple of 16;
+    elsewhere the forced run falls back to the vector path)."""
+    if path != "auto":
+        monkeypatch.setenv("KV4_FORCE_PATH", path)
     name, nq, nkv, hs, ql, sl, bs = case
     _run(W.custom(name, nq, nkv, hs, ql, sl, block_size=bs), mode)
 
@@ -98,7 +108,11 @@ def test_pth_attention_schedules(mode, sched, monkeypatch):
     for k, v in SCHED[sched].items():
         monkeypatch.setenv(k, v)
     _run(W.custom("sched_decode", 32, 8, 128, [1] * 5, [1000, 17, 300, 2049, 64], block_size=16), mode)
-    _run(W.custom("sched_mixed", 8, 2, 96, [1, 1, 7, 1], [1500, 63, 700, 1], block_size=16), mode)
+    _run(W.custom("sched_decode64", 16, 4, 64, [1] * 4, [513, 1, 64, 700], block_size=32), mode)
+    _run(W.custom("sched_mixed", 8, 2, 128, [1, 1, 7, 1], [1500, 63, 700, 1], block_size=16), mode)
+    _run(W.custom("sched_mixed96", 8, 2, 96, [1, 1, 7, 1], [1500, 63, 700, 1], block_size=16), mode)
+    _run(W.custom("sched_decode192", 8, 4, 192, [1] * 3, [700, 33, 1200], block_size=16), mode)
+    _run(W.custom("sched_mha96", 8, 8, 96, [1] * 3, [900, 5, 260], block_size=32), mode)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -121,3 +135,15 @@ def test_pth_attention_vs_unquantized(mode):
     if mode == "int8":
         assert nbad == 0, f"G4: {nbad} elements outside 5e-2 (max err {mx})"
 
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("gain", [2.0 ** -30, 2.0 ** -8, 2.0 ** 6, 2.0 ** 40])
+@pytest.mark.parametrize("mode", MODES)
+def test_pth_attention_query_range(mode, gain, path, monkeypatch):
+    """Queries far from unit size: flat and one-hot softmax rows, and q' rows
+    whose power-of-two normalization (matrix-core path) moves them by up to
+    2^40."""
+    monkeypatch.setenv("KV4_FORCE_PATH", path)
+    w = W.custom("qrange", 8, 2, 128, [1, 3, 1], [600, 80, 17], block_size=16)
+    _run(w, mode, q_gain=gain)
