@@ -85,9 +85,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the write path and attention shard by kv head or sequence with no exchange; "
-              "see DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on one GPU only: there is no multi-GPU path here "
+              "(the write path and attention would shard by kv head or sequence with no exchange). "
+              "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

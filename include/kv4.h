@@ -68,7 +68,7 @@ extern "C" {
 typedef enum {
   KV4_OK = 0,
   KV4_EINVAL = 1,        /* invalid argument (shape, pointer, alignment)      */
-  KV4_EUNSUPPORTED = 2,  /* valid but not supported by this build             */
+  KV4_EUNSUPPORTED = 2,  /* valid but not supported by this library           */
   KV4_EHIP = 3,          /* a HIP runtime call or kernel launch failed        */
   KV4_EWORKSPACE = 4     /* workspace missing or smaller than required        */
 } kv4_status;

@@ -25,7 +25,7 @@ Two tiers:
   * math tier  -- fp64: explicit dense block-diagonal Hadamard matrix,
                   scalar quantization, unpaged attention.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   D: sign i is -1 iff bit 63 of the (i+1)-th SplitMix64 output seeded with
      sign_seed is set; one D of length head_size shared by K, V, Q, all heads
      and tokens.  H_b: Sylvester order, entry (r, c) = (-1)^popcount(r & c),
@@ -355,7 +355,7 @@ def attention_dense(query, key, value, query_start_loc, seq_lens, softmax_scale:
 # The pages name int8_per_token_head and fp8_per_token_head as the control
 # modes of the same kernels ([PR56198]: they never use the transform; [PR40835]
 # review: int8 or FP8 cache dtype, float32 scale caches per (token, kv head)).
-# Readings (the pages are silent on the rule; listed in the design doc): symmetric
+# Readings (the pages are silent on the rule): symmetric
 # absmax per (token, kv head) vector, scale = float32(absmax) / qmax (IEEE
 # float32 division) with qmax = 127 (int8) or 448 (the largest finite OCP
 # e4m3fn value); int8 code = clamp(rint_half_even(float32(x / scale)), -128,
