@@ -119,9 +119,7 @@ int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_
     while (want > 1 && (want * G > kMfmaRows || nkv % want != 0)) want >>= 1;
     p.hpw = (int)want;
   }
-  // waves per workgroup, as the kernels are built: two at four heads per wave
-  // and for int8 / fp8 at head size 192, else four
-  p.wpb = (p.hpw == 4 || (qm != 0 && hs >= 192)) ? 2 : 4;
+  p.wpb = kv4::mfma_waves_per_block(p.hpw, qm, hs);
   // Single-token decode on the matrix cores, with whole workgroups of kv head
   // groups: stream-K partition of the KV steps over the resident workgroups
   // (no split size; every workgroup gets the same number of steps).

@@ -412,18 +412,16 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Waves per workgroup and the occupancy each HPW is built for: the LDS of
-// HPW per-head stages per wave bounds the waves a CU can hold. WPE is the
-// register target (waves per SIMD); head size 192 at one head per wave fits
-// two waves (256 registers), not three.
+// The occupancy each HPW is built for: the LDS of HPW per-head stages per
+// wave bounds the waves a CU can hold. WPE is the register target (waves per
+// SIMD); head size 192 at one head per wave fits two waves (256 registers),
+// not three.
 template <int HPW> struct MfmaShape;
-template <> struct MfmaShape<1> { static constexpr int WPB = 4, WPE = 3; };
-template <> struct MfmaShape<2> { static constexpr int WPB = 4, WPE = 2; };
-template <> struct MfmaShape<4> { static constexpr int WPB = 2, WPE = 1; };
-// int8 / fp8 at head size 192 (12 KB stages): two waves per workgroup, so
-// that three workgroups fit a CU's LDS.
+template <> struct MfmaShape<1> { static constexpr int WPE = 3; };
+template <> struct MfmaShape<2> { static constexpr int WPE = 2; };
+template <> struct MfmaShape<4> { static constexpr int WPE = 1; };
 template <int HS, int HPW, int QM>
-constexpr int mfma_wpb() { return QM != 0 && HS >= 192 ? 2 : MfmaShape<HPW>::WPB; }
+constexpr int mfma_wpb() { return mfma_waves_per_block(HPW, QM, HS); }
 template <int HS, int HPW, int QM>
 constexpr int mfma_wpe() {
   return HPW == 1 && (HS >= 192 || (QM != 0 && HS >= 96)) ? 2 : MfmaShape<HPW>::WPE;
@@ -1184,13 +1182,13 @@ static hipError_t launch_hs(AttnArgs& a, const int32_t* prefix, int64_t max_unit
     return hipSuccess;
   }
   switch (a.plan.hpw) {
-    case 2: go(attn_mfma_kernel<HS, 2, 0>, MfmaShape<2>::WPB, resident_blocks<HS, 2, 0>()); break;
+    case 2: go(attn_mfma_kernel<HS, 2, 0>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0>()); break;
     case 4:
       // four heads' V loads of a step must fit the 6-bit load counter
       if constexpr (Geo<HS>::NVR == 1)
-        go(attn_mfma_kernel<HS, 4, 0>, MfmaShape<4>::WPB, resident_blocks<HS, 4, 0>());
+        go(attn_mfma_kernel<HS, 4, 0>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0>());
       break;
-    default: go(attn_mfma_kernel<HS, 1, 0>, MfmaShape<1>::WPB, resident_blocks<HS, 1, 0>()); break;
+    default: go(attn_mfma_kernel<HS, 1, 0>, mfma_wpb<HS, 1, 0>(), resident_blocks<HS, 1, 0>()); break;
   }
   return hipSuccess;
 }

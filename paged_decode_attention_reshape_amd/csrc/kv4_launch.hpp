@@ -49,6 +49,14 @@ struct DequantArgs {
   int qm;                // as WriteArgs
 };
 
+// Waves per workgroup of the matrix-core kernel at (kv heads per wave, cache
+// mode, head size), as the kernels are built; the planner's stream-K cut
+// uses the same value. Four heads per wave, and int8 / fp8 at head size 192
+// (12 KB stages), take two waves so that more workgroups fit a CU's LDS.
+constexpr int mfma_waves_per_block(int hpw, int qm, int hs) {
+  return (hpw == 4 || (qm != 0 && hs >= 192)) ? 2 : 4;
+}
+
 // Work decomposition of one attention call (chosen on the host from host-known
 // sizes only; no device data is read).
 struct AttnPlan {
