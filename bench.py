@@ -76,6 +76,9 @@ def main():
     ap.add_argument("--config", default="llama8b_long")
     ap.add_argument("--kv-mode", default="int4", choices=["int4", "int8", "fp8"],
                     help="cache format: int4 RHT (the method) or the per-token-head int8 / fp8 controls")
+    ap.add_argument("--layout", default="packed", choices=["packed", "inline"],
+                    help="cache layout: separate packed code and scale tensors, or one buffer with each "
+                         "row's scale inline and rows padded to 16 bytes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -124,14 +127,21 @@ def main():
 
     nb, bs, nkv, hs = lay.num_blocks, w.block_size, w.num_kv_heads, w.head_size
     mode = args.kv_mode
-    kc = torch.zeros((nb, bs, nkv, code_bytes(w, mode)), dtype=torch.uint8, device=dev)
-    vc = torch.zeros_like(kc)
-    ks = torch.zeros((nb, bs, nkv), dtype=torch.float32, device=dev)
-    vs = torch.zeros_like(ks)
+    inline = args.layout == "inline"
+    if inline:
+        lcache = kv4.LayoutCache.inline(mode, nb, bs, nkv, hs, device=dev)
+        kc = vc = ks = vs = None
+    else:
+        kc = torch.zeros((nb, bs, nkv, code_bytes(w, mode)), dtype=torch.uint8, device=dev)
+        vc = torch.zeros_like(kc)
+        ks = torch.zeros((nb, bs, nkv), dtype=torch.float32, device=dev)
+        vs = torch.zeros_like(ks)
     stream = torch.cuda.Stream()
 
     def write(k, v, slots):
-        if mode == "int4":
+        if inline:
+            kv4.kv4_write_layout(k, v, lcache, slots, sign_seed=w.sign_seed, stream=stream)
+        elif mode == "int4":
             kv4.kv4_rht_write(k, v, kc, vc, ks, vs, slots, sign_seed=w.sign_seed, stream=stream)
         else:
             kv4.kv4_pth_write(mode, k, v, kc, vc, ks, vs, slots, stream=stream)
@@ -167,7 +177,10 @@ def main():
     slens = torch.from_numpy(lay.seq_lens).to(dev)
     qsl = torch.from_numpy(lay.query_start_loc).to(dev)
     out = torch.empty((w.num_q_tokens, w.num_q_heads, hs), dtype=torch.bfloat16, device=dev)
-    if mode == "int4":
+    if inline:
+        need = kv4.kv4_attention_layout_workspace_size(lcache, w.num_q_tokens, w.num_seqs, w.num_q_heads,
+                                                       w.max_query_len, w.max_seq_len)
+    elif mode == "int4":
         need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, w.num_q_heads, nkv, hs,
                                                       w.max_query_len, w.max_seq_len)
     else:
@@ -179,7 +192,10 @@ def main():
         write(k_new, v_new, s_new)
         if e_a is not None:
             e_a.record(stream)
-        if mode == "int4":
+        if inline:
+            kv4.kv4_attention_layout(q, lcache, bt, slens, qsl, w.max_query_len, w.max_seq_len,
+                                     sign_seed=w.sign_seed, out=out, workspace=ws, stream=stream)
+        elif mode == "int4":
             kv4.kv4_paged_attention(q, kc, vc, ks, vs, bt, slens, qsl, max_query_len=w.max_query_len,
                                     max_seq_len=w.max_seq_len, sign_seed=w.sign_seed, out=out, workspace=ws,
                                     stream=stream)
@@ -215,7 +231,8 @@ def main():
     if os.path.exists(PROFILE_COUNTERS):
         try:
             pc = json.load(open(PROFILE_COUNTERS))
-            ent = pc.get("workloads", {}).get(w.name if mode == "int4" else f"{w.name}_{mode}")
+            key = w.name + ("" if mode == "int4" else f"_{mode}") + ("_inline" if inline else "")
+            ent = pc.get("workloads", {}).get(key)
             if ent and pc.get("kernel_source_hash") == kernel_source_hash():
                 traffic = ent.get("traffic_bytes_per_launch")
         except Exception:
@@ -223,7 +240,8 @@ def main():
 
     line = {
         "metric": "INT4 paged decode attn: KV GB/s & % HBM peak; cache-write tokens/s"
-                  + ("" if mode == "int4" else f" ({mode} per-token-head control cache)"),
+                  + ("" if mode == "int4" else f" ({mode} per-token-head control cache)")
+                  + (" (inline-scale padded-slot layout)" if inline else ""),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -235,7 +253,7 @@ def main():
         "vs_baseline": None,
         "dtype": f"{mode} codes / fp32 accumulate (bf16 in/out)",
         "data": "synthetic seeded N(0,1) bf16, 1% outlier channels x20",
-        "config": {"workload": w.name, "kv_cache": mode, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+        "config": {"workload": w.name, "kv_cache": mode, "cache_layout": args.layout, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": nkv, "head_size": hs, "block_size": bs,
                    "total_kv_tokens": w.total_kv_tokens, "max_seq_len": w.max_seq_len,
                    "q_tokens_per_step": w.num_q_tokens, "new_kv_tokens_per_step": int(new_rows.shape[0]),
@@ -255,11 +273,12 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, lay, t, kc, vc, ks, vs, args.cpu_seconds, mode)
+        line["cpu_baseline"] = cpu_baseline(w, lay, t, kc, vc, ks, vs, args.cpu_seconds, mode,
+                                            lcache if inline else None)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float, mode: str = "int4"):
+def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float, mode: str = "int4", lcache=None):
     """The CPU oracle (fp64 numpy) on a bounded sample of the same workload:
     whole sequences of this batch, read from the GPU-written cache, until
     about `budget_s` seconds of CPU work; reported as KV GB/s like `value`."""
@@ -277,12 +296,16 @@ def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float, mode: str = "int4")
     order = np.random.default_rng(0).permutation(w.num_seqs)
     q = W.bf16_as_f32_numpy(t.query)
     done_bytes, done_seqs, spent = 0, 0, 0.0
-    dev = kc.device
+    dev = (lcache.buffer if lcache is not None else kc).device
     for s in order:
         n = -(-w.seq_lens[s] // w.block_size)
         pages = torch.from_numpy(lay.block_table[s, :n].astype(np.int64)).to(dev)
-        kcs, vcs = kc.index_select(0, pages).cpu().numpy(), vc.index_select(0, pages).cpu().numpy()
-        kss, vss = ks.index_select(0, pages).cpu().numpy(), vs.index_select(0, pages).cpu().numpy()
+        if lcache is not None:     # the sequence's pages of the inline buffer, unpacked (not timed)
+            kcs, vcs, kss, vss = O.inline_unpack(lcache.buffer.index_select(0, pages).cpu().numpy(), mode,
+                                                 w.num_kv_heads, w.head_size, w.block_size)
+        else:
+            kcs, vcs = kc.index_select(0, pages).cpu().numpy(), vc.index_select(0, pages).cpu().numpy()
+            kss, vss = ks.index_select(0, pages).cpu().numpy(), vs.index_select(0, pages).cpu().numpy()
         bt = np.zeros_like(lay.block_table)
         bt[s, :n] = np.arange(n)
         t0 = time.perf_counter()

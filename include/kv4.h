@@ -263,6 +263,101 @@ int kv4_pth_dequant(int32_t kv_quant_mode, const void* cache, const float* scale
                     float* out, void* stream);
 
 /* Thread-local description of the last failure ("" if none). Never NULL. */
+/*
+ * Cache layouts. Every entry point above takes the packed layout: codes
+ * uint8 [num_blocks, block_size, num_kv_heads, C] (C = head_size / 2 for the
+ * int4 RHT mode, head_size for int8 / fp8) and scales float32 [num_blocks,
+ * block_size, num_kv_heads]. The *_layout entry points below take any
+ * layout described by strides instead, for all three modes
+ * (kv_quant_mode 0 = int4 RHT, KV4_MODE_INT8, KV4_MODE_FP8): the C code
+ * bytes of (page p, token slot t of the page, kv head h) start at
+ *   cache + p * block_stride + t * token_stride + h * head_stride
+ * and its scale is the float at
+ *   scale_cache + p * scale_block_stride + t * scale_token_stride
+ *               + h * scale_head_stride
+ * (the K and V caches share one layout). Code strides must be positive
+ * multiples of 4 bytes (int4) or 8 bytes (int8 / fp8), scale strides
+ * positive; the matrix-core kernels run where the code strides are also
+ * multiples of 16 bytes, and serve one kv head per wave unless the heads of a
+ * token slot are packed (head_stride == C, scale_head_stride == 1). Distinct
+ * (page, slot, head) rows and scales must not overlap each other; the
+ * library cannot check this, nor buffer sizes.
+ */
+typedef struct kv4_cache_layout {
+  int64_t block_stride;        /* bytes between pages of a code cache          */
+  int64_t token_stride;        /* bytes between token slots of a page          */
+  int64_t head_stride;         /* bytes between kv heads of a token slot        */
+  int64_t scale_block_stride;  /* floats between pages of a scale cache        */
+  int64_t scale_token_stride;  /* floats between token slots                   */
+  int64_t scale_head_stride;   /* floats between kv heads                      */
+} kv4_cache_layout;
+
+/* kv4_cache_layout_packed -- the packed layout of the other entry points. */
+int kv4_cache_layout_packed(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size,
+                            int32_t block_size, kv4_cache_layout* layout);
+
+/*
+ * kv4_cache_layout_inline -- the inline-scale padded-slot layout of the
+ * per-token-head caches (vLLM PR #40835 review of `_ensure_scale_caches`:
+ * float32 views of sizes full_block = 2 kv_half_bytes, slot = num_kv_heads
+ * padded rows, head = one padded row, scale offset = the code bytes of a row;
+ * K scales in half 0 and V scales kv_half_bytes further; rows padded to a
+ * 16-byte multiple, vLLM PR #62113 "16-byte-align per-token-head KV slots").
+ * One buffer of num_blocks * block_bytes bytes holds both caches: page p is
+ * the K half (block_size * num_kv_heads rows) then the V half; each row is C
+ * code bytes, its float32 scale, then zero padding up to the pitch
+ * P = round_up(C + 4, 16). Use key_cache = buffer, value_cache = buffer +
+ * value_offset, k_scale_cache = (float*)(buffer + scale_offset),
+ * v_scale_cache = (float*)(buffer + value_offset + scale_offset) with the
+ * returned layout. block_bytes / value_offset / scale_offset may be NULL.
+ */
+int kv4_cache_layout_inline(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size,
+                            int32_t block_size, kv4_cache_layout* layout, int64_t* block_bytes,
+                            int64_t* value_offset, int64_t* scale_offset);
+
+/*
+ * kv4_write_layout / kv4_attention_layout_workspace_size /
+ * kv4_attention_layout / kv4_dequant_layout -- kv4_rht_write,
+ * kv4_paged_attention_workspace_size, kv4_paged_attention and kv4_dequant
+ * (kv_quant_mode 0) or their kv4_pth_* counterparts (modes 1 / 2: b,
+ * sign_seed and inverse_rotate are ignored) over caches in `layout`. Same
+ * results, argument rules and errors, plus KV4_EINVAL for an invalid layout.
+ * The workspace size depends on the layout (it selects the plan).
+ */
+int kv4_write_layout(int32_t kv_quant_mode, const void* key, const void* value,
+                     int64_t key_token_stride, int64_t value_token_stride,
+                     void* key_cache, void* value_cache,
+                     float* k_scale_cache, float* v_scale_cache,
+                     const kv4_cache_layout* layout,
+                     const int64_t* slot_mapping, int64_t num_tokens,
+                     int32_t num_kv_heads, int32_t head_size, int32_t b,
+                     int32_t block_size, int64_t num_blocks,
+                     uint64_t sign_seed, void* stream);
+size_t kv4_attention_layout_workspace_size(int32_t kv_quant_mode, const kv4_cache_layout* layout,
+                                           int64_t num_q_tokens, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_size, int32_t max_query_len,
+                                           int32_t max_seq_len);
+int kv4_attention_layout(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
+                         const void* key_cache, const void* value_cache,
+                         const float* k_scale_cache, const float* v_scale_cache,
+                         const kv4_cache_layout* layout, int64_t num_blocks,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, const int32_t* query_start_loc,
+                         int32_t num_seqs, int64_t num_q_tokens,
+                         int32_t max_query_len, int32_t max_seq_len,
+                         int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_size, int32_t b, int32_t block_size,
+                         uint64_t sign_seed, float softmax_scale,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+int kv4_dequant_layout(int32_t kv_quant_mode, const void* cache, const float* scale_cache,
+                       const kv4_cache_layout* layout, int64_t num_blocks,
+                       const int64_t* slot_mapping, int64_t num_tokens,
+                       int32_t num_kv_heads, int32_t head_size, int32_t b,
+                       int32_t block_size, uint64_t sign_seed, int32_t inverse_rotate,
+                       float* out, void* stream);
+
 const char* kv4_last_error(void);
 
 #ifdef __cplusplus

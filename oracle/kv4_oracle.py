@@ -509,3 +509,91 @@ def pth_paged_attention(query, key_cache, value_cache, k_scale_cache, v_scale_ca
             logits = (qg @ K[:, g, :].T) * softmax_scale
             out[q0:q1, g * group:(g + 1) * group] = _causal_softmax_attend(logits, V[:, g, :], L)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Inline-scale padded-slot cache layout  ([PR40835] review of
+# `_ensure_scale_caches`; vLLM PR #62113 "16-byte-align per-token-head KV
+# slots so Triton vectorizes loads")
+# ---------------------------------------------------------------------------
+# The review shows float32 views into the cache with
+#   full_block_f32 = 2 * kv_half_bytes / 4,  slot_f32 = nkv * padded_hs * dtype_sz / 4,
+#   head_f32 = padded_hs * dtype_sz / 4,    scale_off_f32 = hs * dtype_sz / 4,
+# K scales in kv half 0 and V scales offset by kv_half_bytes. Reading (the
+# pages give no more): one buffer per layer, a page is the K half then the V
+# half, each half bs * nkv rows (slot-major, then head); a row is the C code
+# bytes (C = hs / 2 for int4, hs for int8 / fp8; "hs * dtype_sz" above), the
+# float32 scale right after them, then zero padding to a 16-byte pitch
+# (padded_hs * dtype_sz = round_up(C + 4, 16)).
+
+def inline_geometry(mode: str, nkv: int, hs: int, bs: int) -> dict:
+    """Byte and float32-view sizes of the inline layout (see above)."""
+    c = hs // 2 if mode == "int4" else hs
+    pitch = -(-(c + 4) // 16) * 16
+    kv_half = bs * nkv * pitch
+    return {"code_bytes": c, "pitch": pitch, "kv_half_bytes": kv_half, "block_bytes": 2 * kv_half,
+            "full_block_f32": 2 * kv_half // 4, "slot_f32": nkv * pitch // 4, "head_f32": pitch // 4,
+            "scale_off_f32": c // 4}
+
+
+def inline_row_offset(geo: dict, page: int, half: int, slot: int, head: int, nkv: int) -> int:
+    """Byte offset of the row of (page, kv half 0 = K / 1 = V, slot, kv head)."""
+    return page * geo["block_bytes"] + half * geo["kv_half_bytes"] + (slot * nkv + head) * geo["pitch"]
+
+
+def inline_pack(kc, vc, ks, vs, mode: str) -> np.ndarray:
+    """Packed caches (codes [nb, bs, nkv, C], float32 scales [nb, bs, nkv])
+    -> the inline buffer uint8 [nb, block_bytes], padding zero. Python loops:
+    small inputs only."""
+    nb, bs, nkv, c = kc.shape
+    hs = 2 * c if mode == "int4" else c
+    geo = inline_geometry(mode, nkv, hs, bs)
+    buf = np.zeros(nb * geo["block_bytes"], dtype=np.uint8)
+    for p in range(nb):
+        for half, (codes, sc) in enumerate(((kc, ks), (vc, vs))):
+            for t in range(bs):
+                for h in range(nkv):
+                    o = inline_row_offset(geo, p, half, t, h, nkv)
+                    buf[o:o + c] = codes[p, t, h]
+                    buf[o + c:o + c + 4] = np.frombuffer(np.float32(sc[p, t, h]).tobytes(), dtype=np.uint8)
+    return buf.reshape(nb, geo["block_bytes"])
+
+
+def inline_unpack(buf, mode: str, nkv: int, hs: int, bs: int):
+    """Inverse of inline_pack: (kc, vc, ks, vs) from the inline buffer."""
+    geo = inline_geometry(mode, nkv, hs, bs)
+    flat = np.asarray(buf, dtype=np.uint8).reshape(-1)
+    nb = flat.size // geo["block_bytes"]
+    c = geo["code_bytes"]
+    kc = np.zeros((nb, bs, nkv, c), dtype=np.uint8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros((nb, bs, nkv), dtype=np.float32)
+    vs = np.zeros_like(ks)
+    for p in range(nb):
+        for half, (codes, sc) in enumerate(((kc, ks), (vc, vs))):
+            for t in range(bs):
+                for h in range(nkv):
+                    o = inline_row_offset(geo, p, half, t, h, nkv)
+                    codes[p, t, h] = flat[o:o + c]
+                    sc[p, t, h] = flat[o + c:o + c + 4].view(np.float32)[0]
+    return kc, vc, ks, vs
+
+
+def inline_store_rows(buf, kc, vc, ks, vs, slot_mapping, mode: str) -> None:
+    """The inline layout's write: copy the rows of the given slots (from the
+    packed caches the write path computed) into an existing inline buffer;
+    padding and other rows keep their bytes. Slots outside the cache are
+    skipped."""
+    nb, bs, nkv, c = kc.shape
+    hs = 2 * c if mode == "int4" else c
+    geo = inline_geometry(mode, nkv, hs, bs)
+    flat = buf.reshape(-1)
+    for s in np.asarray(slot_mapping, dtype=np.int64):
+        if s < 0 or s >= nb * bs:
+            continue
+        p, t = int(s // bs), int(s % bs)
+        for half, (codes, sc) in enumerate(((kc, ks), (vc, vs))):
+            for h in range(nkv):
+                o = inline_row_offset(geo, p, half, t, h, nkv)
+                flat[o:o + c] = codes[p, t, h]
+                flat[o + c:o + c + 4] = np.frombuffer(np.float32(sc[p, t, h]).tobytes(), dtype=np.uint8)

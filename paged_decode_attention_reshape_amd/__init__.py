@@ -28,6 +28,19 @@ _MODES = {"int8": KV4_MODE_INT8, "fp8": KV4_MODE_FP8, KV4_MODE_INT8: KV4_MODE_IN
 DEFAULT_SIGN_SEED = 42
 
 _c_int32, _c_int64, _c_uint64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+
+
+class CacheLayout(ctypes.Structure):
+    """kv4_cache_layout: code strides in bytes, scale strides in floats."""
+    _fields_ = [("block_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64), ("scale_block_stride", ctypes.c_int64),
+                ("scale_token_stride", ctypes.c_int64), ("scale_head_stride", ctypes.c_int64)]
+
+    def as_tuple(self):
+        return tuple(getattr(self, f) for f, _ in self._fields_)
+
+
+_LP = ctypes.POINTER(CacheLayout)
 _SIGNATURES = {
     "kv4_rht_write": (ctypes.c_int, [_vp, _vp, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp, _c_int64,
                                      _c_int32, _c_int32, _c_int32, _c_int32, _c_int64, _c_uint64, _vp]),
@@ -49,6 +62,21 @@ _SIGNATURES = {
     "kv4_pth_attention": (ctypes.c_int, [_c_int32, _vp, _c_int64, _vp, _vp, _vp, _vp, _c_int64, _vp, _c_int32,
                                          _vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32, _c_int32, _c_int32,
                                          _c_int32, _c_int32, ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
+    "kv4_cache_layout_packed": (ctypes.c_int, [_c_int32, _c_int32, _c_int32, _c_int32, _LP]),
+    "kv4_cache_layout_inline": (ctypes.c_int, [_c_int32, _c_int32, _c_int32, _c_int32, _LP,
+                                               ctypes.POINTER(_c_int64), ctypes.POINTER(_c_int64),
+                                               ctypes.POINTER(_c_int64)]),
+    "kv4_write_layout": (ctypes.c_int, [_c_int32, _vp, _vp, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _LP, _vp,
+                                        _c_int64, _c_int32, _c_int32, _c_int32, _c_int32, _c_int64, _c_uint64,
+                                        _vp]),
+    "kv4_attention_layout_workspace_size": (ctypes.c_size_t, [_c_int32, _LP, _c_int64, _c_int32, _c_int32,
+                                                              _c_int32, _c_int32, _c_int32, _c_int32]),
+    "kv4_attention_layout": (ctypes.c_int, [_c_int32, _vp, _c_int64, _vp, _vp, _vp, _vp, _LP, _c_int64, _vp,
+                                            _c_int32, _vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32, _c_int32,
+                                            _c_int32, _c_int32, _c_int32, _c_int32, _c_uint64, ctypes.c_float,
+                                            _vp, _vp, ctypes.c_size_t, _vp]),
+    "kv4_dequant_layout": (ctypes.c_int, [_c_int32, _vp, _vp, _LP, _c_int64, _vp, _c_int64, _c_int32, _c_int32,
+                                          _c_int32, _c_int32, _c_uint64, _c_int32, _vp, _vp]),
 }
 
 _lib = None
@@ -373,4 +401,159 @@ def kv4_pth_attention(kv_quant_mode, query: torch.Tensor, key_cache: torch.Tenso
         seq_lens.data_ptr(), query_start_loc.data_ptr(), S, Tq, int(max_query_len), int(max_seq_len), nq, nkv,
         hs, bs, float(softmax_scale), out.data_ptr(), ws_ptr, ws_bytes, _stream(stream))
     _check("kv4_pth_attention", rc)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Caller-described cache layouts (all three modes; see include/kv4.h)
+# ---------------------------------------------------------------------------
+_ANY_MODES = {"int4": 0, 0: 0, "int8": KV4_MODE_INT8, "fp8": KV4_MODE_FP8, KV4_MODE_INT8: KV4_MODE_INT8,
+              KV4_MODE_FP8: KV4_MODE_FP8}
+
+
+def _any_mode(m) -> int:
+    if m not in _ANY_MODES:
+        raise ValueError(f"kv_quant_mode must be 'int4', 'int8' or 'fp8', got {m!r}")
+    return _ANY_MODES[m]
+
+
+def kv4_cache_layout_packed(kv_quant_mode, num_kv_heads: int, head_size: int, block_size: int) -> CacheLayout:
+    lay = CacheLayout()
+    _check("kv4_cache_layout_packed",
+           lib().kv4_cache_layout_packed(_any_mode(kv_quant_mode), num_kv_heads, head_size, block_size,
+                                         ctypes.byref(lay)))
+    return lay
+
+
+def kv4_cache_layout_inline(kv_quant_mode, num_kv_heads: int, head_size: int, block_size: int):
+    """(layout, block_bytes, value_offset, scale_offset) of the inline-scale
+    padded-slot layout."""
+    lay = CacheLayout()
+    bb, vo, so = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check("kv4_cache_layout_inline",
+           lib().kv4_cache_layout_inline(_any_mode(kv_quant_mode), num_kv_heads, head_size, block_size,
+                                         ctypes.byref(lay), ctypes.byref(bb), ctypes.byref(vo), ctypes.byref(so)))
+    return lay, bb.value, vo.value, so.value
+
+
+class LayoutCache:
+    """A K/V cache pair with its scales in a caller-described layout: device
+    pointers of the K codes, V codes, K scales and V scales, the layout, and
+    the tensor(s) that own the memory."""
+
+    def __init__(self, mode, layout: CacheLayout, num_blocks: int, block_size: int, num_kv_heads: int,
+                 head_size: int, key_ptr: int, value_ptr: int, k_scale_ptr: int, v_scale_ptr: int, owners=()):
+        self.mode = _any_mode(mode)
+        self.layout = layout
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.num_kv_heads, self.head_size = num_kv_heads, head_size
+        self.key_ptr, self.value_ptr, self.k_scale_ptr, self.v_scale_ptr = key_ptr, value_ptr, k_scale_ptr, v_scale_ptr
+        self.owners = tuple(owners)
+
+    @classmethod
+    def inline(cls, mode, num_blocks: int, block_size: int, num_kv_heads: int, head_size: int,
+               device="cuda", fill: int = 0):
+        """One uint8 buffer [num_blocks, block_bytes] in the inline-scale layout."""
+        lay, bb, vo, so = kv4_cache_layout_inline(mode, num_kv_heads, head_size, block_size)
+        buf = torch.full((num_blocks, bb), fill, dtype=torch.uint8, device=device)
+        p = buf.data_ptr()
+        c = cls(mode, lay, num_blocks, block_size, num_kv_heads, head_size, p, p + vo, p + so, p + vo + so, (buf,))
+        c.buffer, c.block_bytes, c.value_offset, c.scale_offset = buf, bb, vo, so
+        return c
+
+
+def kv4_write_layout(key: torch.Tensor, value: torch.Tensor, cache: LayoutCache, slot_mapping: torch.Tensor,
+                     sign_seed: int = DEFAULT_SIGN_SEED, b: Optional[int] = None, stream=None) -> None:
+    """Write path of the cache's mode into a LayoutCache (see kv4_rht_write /
+    kv4_pth_write)."""
+    _need(key, "key", torch.bfloat16, 3)
+    _need(value, "value", torch.bfloat16, 3)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    _contig(slot_mapping, "slot_mapping")
+    T, nkv, hs = key.shape
+    if value.shape != key.shape or slot_mapping.shape[0] != T:
+        raise ValueError("key/value/slot_mapping shapes disagree")
+    if (nkv, hs) != (cache.num_kv_heads, cache.head_size):
+        raise ValueError("key heads / head size disagree with the cache")
+    for t, n in ((key, "key"), (value, "value")):
+        if t.stride(2) != 1 or t.stride(1) != hs:
+            raise ValueError(f"{n} must have contiguous heads (stride (*, {hs}, 1))")
+    rc = lib().kv4_write_layout(cache.mode, key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0),
+                                cache.key_ptr, cache.value_ptr, cache.k_scale_ptr, cache.v_scale_ptr,
+                                ctypes.byref(cache.layout), slot_mapping.data_ptr(), T, nkv, hs,
+                                hs & -hs if b is None else b, cache.block_size, cache.num_blocks,
+                                sign_seed & (2 ** 64 - 1), _stream(stream))
+    _check("kv4_write_layout", rc)
+
+
+def kv4_attention_layout_workspace_size(cache: LayoutCache, num_q_tokens: int, num_seqs: int, num_q_heads: int,
+                                        max_query_len: int, max_seq_len: int) -> int:
+    n = lib().kv4_attention_layout_workspace_size(cache.mode, ctypes.byref(cache.layout), num_q_tokens, num_seqs,
+                                                  num_q_heads, cache.num_kv_heads, cache.head_size, max_query_len,
+                                                  max_seq_len)
+    err = kv4_last_error()
+    if n == 0 and err:
+        raise Kv4Error("kv4_attention_layout_workspace_size", KV4_EINVAL, err)
+    return int(n)
+
+
+def kv4_attention_layout(query: torch.Tensor, cache: LayoutCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                         query_start_loc: torch.Tensor, max_query_len: int, max_seq_len: int,
+                         sign_seed: int = DEFAULT_SIGN_SEED, softmax_scale: Optional[float] = None,
+                         b: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Paged causal attention over a LayoutCache (see kv4_paged_attention /
+    kv4_pth_attention)."""
+    _need(query, "query", torch.bfloat16, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    for t, n in ((block_table, "block_table"), (seq_lens, "seq_lens"), (query_start_loc, "query_start_loc")):
+        _contig(t, n)
+    Tq, nq, hs = query.shape
+    S = seq_lens.shape[0]
+    if hs != cache.head_size:
+        raise ValueError("query head size disagrees with the cache")
+    if query_start_loc.shape[0] != S + 1 or block_table.shape[0] != S:
+        raise ValueError("query_start_loc must be [num_seqs + 1] and block_table [num_seqs, *]")
+    if query.stride(2) != 1 or query.stride(1) != hs:
+        raise ValueError("query must have contiguous heads")
+    if out is None:
+        out = torch.empty((Tq, nq, hs), dtype=torch.bfloat16, device=query.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _contig(out, "out")
+    need = kv4_attention_layout_workspace_size(cache, Tq, S, nq, max_query_len, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if softmax_scale is None:
+        softmax_scale = hs ** -0.5
+    rc = lib().kv4_attention_layout(
+        cache.mode, query.data_ptr(), query.stride(0), cache.key_ptr, cache.value_ptr, cache.k_scale_ptr,
+        cache.v_scale_ptr, ctypes.byref(cache.layout), cache.num_blocks, block_table.data_ptr(),
+        block_table.shape[1], seq_lens.data_ptr(), query_start_loc.data_ptr(), S, Tq, int(max_query_len),
+        int(max_seq_len), nq, cache.num_kv_heads, hs, hs & -hs if b is None else b, cache.block_size,
+        sign_seed & (2 ** 64 - 1), float(softmax_scale), out.data_ptr(), ws_ptr, ws_bytes, _stream(stream))
+    _check("kv4_attention_layout", rc)
+    return out
+
+
+def kv4_dequant_layout(cache: LayoutCache, which: str, slot_mapping: torch.Tensor, inverse_rotate: bool = False,
+                       sign_seed: int = DEFAULT_SIGN_SEED, b: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Gather and dequantize K ('k') or V ('v') slots of a LayoutCache
+    (float32 [T, nkv, hs]; out-of-range slots give zeros)."""
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    _contig(slot_mapping, "slot_mapping")
+    if which not in ("k", "v"):
+        raise ValueError("which must be 'k' or 'v'")
+    T = slot_mapping.shape[0]
+    hs, nkv = cache.head_size, cache.num_kv_heads
+    out = torch.empty((T, nkv, hs), dtype=torch.float32, device=slot_mapping.device)
+    codes, scales = (cache.key_ptr, cache.k_scale_ptr) if which == "k" else (cache.value_ptr, cache.v_scale_ptr)
+    rc = lib().kv4_dequant_layout(cache.mode, codes, scales, ctypes.byref(cache.layout), cache.num_blocks,
+                                  slot_mapping.data_ptr(), T, nkv, hs, hs & -hs if b is None else b,
+                                  cache.block_size, sign_seed & (2 ** 64 - 1), 1 if inverse_rotate else 0,
+                                  out.data_ptr(), _stream(stream))
+    _check("kv4_dequant_layout", rc)
     return out

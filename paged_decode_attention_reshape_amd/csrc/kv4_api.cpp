@@ -82,17 +82,24 @@ int mfma_hpw_max(int hs) { return hs == 192 ? 1 : 2; }
 // (GQA group > 1 or query_len > 1), the head size is a multiple of 32 the
 // kernel is built for, and pages hold a power-of-two number (>= 16) of tokens.
 int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
-              int32_t max_query_len, int32_t max_seq_len, int32_t block_size, kv4::AttnPlan& p) {
+              int32_t max_query_len, int32_t max_seq_len, int32_t block_size, const kv4::CacheLayout& lay,
+              kv4::AttnPlan& p) {
   std::memset(&p, 0, sizeof(p));
   const int G = nq / nkv;
+  const int64_t code_bytes = qm ? hs : hs / 2;
+  // the matrix-core kernel moves 16-byte pieces with 32-bit offsets inside a
+  // 16-token half tile; heads of one token row side by side (and their
+  // scales) let one wave serve several kv heads
+  const bool lay_dma = lay.blk % 16 == 0 && lay.tok % 16 == 0 && lay.head % 16 == 0 &&
+                       lay.tok <= (INT32_MAX - 4096) / 16;
+  const bool lay_contig = lay.head == code_bytes && lay.shead == 1;
   const bool hs_ok = mfma_head_size(hs) && (qm == 0 || kPthMfma);
-  const bool mfma_ok = hs_ok && block_size % 16 == 0 && (block_size & (block_size - 1)) == 0;
-  // Single-query decode with one query head per kv head (G = 1) still fills
-  // the matrix-core rows when one wave serves several kv heads.
-  const bool g1_multi = qm == 0 && nkv % 2 == 0 && mfma_hpw_max(hs) >= 2;
-  // (int8 / fp8: the matrix-core kernel's LDS pipeline streams the twice
-  // larger rows faster than the vector kernel even with one busy MFMA row)
-  bool mfma = mfma_ok && (G > 1 || max_query_len > 1 || g1_multi || qm != 0);
+  const bool mfma_ok = hs_ok && lay_dma && block_size % 16 == 0 && (block_size & (block_size - 1)) == 0;
+  // The matrix-core kernel wherever the shape allows it: even single-query
+  // decode with one query head per kv head (one busy MFMA row of 16 unless a
+  // wave serves several kv heads) streams the cache about 4x faster through
+  // its LDS pipeline than the vector kernel.
+  bool mfma = mfma_ok;
   if (const char* f = std::getenv("KV4_FORCE_PATH")) {
     if (!std::strcmp(f, "valu")) mfma = false;
     if (!std::strcmp(f, "mfma")) mfma = mfma_ok;
@@ -112,7 +119,7 @@ int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_
   // Single-token decode on the matrix cores: one wave serves hpw kv heads
   // (hpw * G <= 16 MFMA rows), sharing its softmax and page walk.
   p.hpw = 1;
-  if (mfma && max_query_len <= 1 && qm == 0) {
+  if (mfma && max_query_len <= 1 && qm == 0 && lay_contig) {
     long want = env_long("KV4_MFMA_HPW", 0);
     if (want != 1 && want != 2 && want != 4) want = mfma_hpw_max(hs);
     if (want > 2 && (hs == 96 || hs == 192)) want = 2;   // four heads' V loads would exceed the load counter
@@ -227,11 +234,39 @@ int check_head_pth(int32_t head_size) {
   return KV4_OK;
 }
 
+int64_t code_row_bytes(int qm, int32_t head_size) { return qm ? head_size : head_size / 2; }
+
+int bs_shift_of(int32_t bs) { return (bs & (bs - 1)) == 0 ? __builtin_ctz((unsigned)bs) : -1; }
+
+// A caller-described layout: positive strides, code strides multiples of the
+// kernels' access width (4 bytes int4, 8 bytes int8 / fp8). Rows are not
+// checked for overlap (the caller's layout must keep them apart).
+int check_layout(int qm, const kv4::CacheLayout& l) {
+  const int64_t A = qm ? 8 : 4;
+  if (l.blk <= 0 || l.tok <= 0 || l.head <= 0 || l.sblk <= 0 || l.stok <= 0 || l.shead <= 0)
+    return fail(KV4_EINVAL, "layout strides must be positive");
+  if (l.blk % A || l.tok % A || l.head % A)
+    return fail(KV4_EINVAL, "layout code strides must be multiples of %lld bytes", (long long)A);
+  if (l.blk > (INT64_MAX >> 20) || l.sblk > (INT64_MAX >> 22)) return fail(KV4_EINVAL, "layout strides too large");
+  return KV4_OK;
+}
+
+kv4::CacheLayout to_layout(const kv4_cache_layout* l) {
+  kv4::CacheLayout c;
+  c.blk = l->block_stride;
+  c.tok = l->token_stride;
+  c.head = l->head_stride;
+  c.sblk = l->scale_block_stride;
+  c.stok = l->scale_token_stride;
+  c.shead = l->scale_head_stride;
+  return c;
+}
+
 int write_impl(int qm, const char* what, const void* key, const void* value, int64_t key_token_stride,
                int64_t value_token_stride, void* key_cache, void* value_cache, float* k_scale_cache,
                float* v_scale_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                int32_t head_size, int32_t b, int32_t block_size, int64_t num_blocks, uint64_t sign_seed,
-               void* stream) {
+               void* stream, const kv4::CacheLayout* layout = nullptr) {
   if (num_tokens < 0) return fail(KV4_EINVAL, "num_tokens must be >= 0");
   if (num_kv_heads < 1) return fail(KV4_EINVAL, "num_kv_heads must be >= 1");
   if (block_size < 1 || block_size > 4096) return fail(KV4_EINVAL, "block_size must be in [1, 4096]");
@@ -249,6 +284,9 @@ int write_impl(int qm, const char* what, const void* key, const void* value, int
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16) ||
       !aligned(k_scale_cache, 4) || !aligned(v_scale_cache, 4) || !aligned(slot_mapping, 8))
     return fail(KV4_EINVAL, "misaligned pointer (K/V and caches need 16 bytes)");
+  const kv4::CacheLayout lay =
+      layout ? *layout : kv4::packed_layout(num_kv_heads, (int)code_row_bytes(qm, head_size), block_size);
+  if (int e = check_layout(qm, lay)) return e;
   kv4::WriteArgs a;
   a.key = static_cast<const uint16_t*>(key);
   a.value = static_cast<const uint16_t*>(value);
@@ -266,13 +304,16 @@ int write_impl(int qm, const char* what, const void* key, const void* value, int
   a.b = b;
   a.seed = sign_seed;
   a.qm = qm;
+  a.bs = block_size;
+  a.bs_shift = bs_shift_of(block_size);
+  a.lay = lay;
   return hip_status(kv4::launch_write(a, static_cast<hipStream_t>(stream)), what);
 }
 
 int dequant_impl(int qm, const char* what, const void* cache, const float* scale_cache, int64_t num_blocks,
                  const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads, int32_t head_size,
                  int32_t b, int32_t block_size, uint64_t sign_seed, int32_t inverse_rotate, float* out,
-                 void* stream) {
+                 void* stream, const kv4::CacheLayout* layout = nullptr) {
   if (num_tokens < 0) return fail(KV4_EINVAL, "num_tokens must be >= 0");
   if (num_kv_heads < 1) return fail(KV4_EINVAL, "num_kv_heads must be >= 1");
   if (block_size < 1 || block_size > 4096) return fail(KV4_EINVAL, "block_size must be in [1, 4096]");
@@ -282,6 +323,9 @@ int dequant_impl(int qm, const char* what, const void* cache, const float* scale
   if (!cache || !scale_cache || !slot_mapping || !out) return fail(KV4_EINVAL, "null pointer argument");
   if (!aligned(cache, 16) || !aligned(out, 16) || !aligned(scale_cache, 4) || !aligned(slot_mapping, 8))
     return fail(KV4_EINVAL, "misaligned pointer");
+  const kv4::CacheLayout lay =
+      layout ? *layout : kv4::packed_layout(num_kv_heads, (int)code_row_bytes(qm, head_size), block_size);
+  if (int e = check_layout(qm, lay)) return e;
   kv4::DequantArgs a;
   a.cache = static_cast<const uint8_t*>(cache);
   a.scale = scale_cache;
@@ -295,20 +339,27 @@ int dequant_impl(int qm, const char* what, const void* cache, const float* scale
   a.inverse_rotate = inverse_rotate ? 1 : 0;
   a.out = out;
   a.qm = qm;
+  a.bs = block_size;
+  a.bs_shift = bs_shift_of(block_size);
+  a.lay = lay;
   return hip_status(kv4::launch_dequant(a, static_cast<hipStream_t>(stream)), what);
 }
 
 size_t workspace_impl(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                      int32_t head_size, int32_t max_query_len, int32_t max_seq_len) {
+                      int32_t head_size, int32_t max_query_len, int32_t max_seq_len,
+                      const kv4::CacheLayout* layout = nullptr) {
   if (check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
                        max_seq_len))
     return 0;
+  if (layout && check_layout(qm, *layout)) return 0;
   // block_size is not an argument here: size for the larger of the two paths
   size_t need = 0;
   for (int32_t bs : {16, 1}) {
     kv4::AttnPlan p;
+    const kv4::CacheLayout lay =
+        layout ? *layout : kv4::packed_layout(num_kv_heads, (int)code_row_bytes(qm, head_size), 16);
     if (make_plan(qm, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len, max_seq_len,
-                  bs, p))
+                  bs, lay, p))
       return 0;
     const size_t n = ws_layout(p, num_q_tokens, num_seqs, num_q_heads, head_size).total;
     need = n > need ? n : need;
@@ -323,7 +374,8 @@ int attention_impl(int qm, const void* query, int64_t query_token_stride, const 
                    const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
                    int64_t num_q_tokens, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size, uint64_t sign_seed,
-                   float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                   float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                   const kv4::CacheLayout* layout = nullptr) {
   if (int e = check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
                                max_seq_len))
     return e;
@@ -348,8 +400,10 @@ int attention_impl(int qm, const void* query, int64_t query_token_stride, const 
   kv4::AttnArgs a;
   std::memset(&a, 0, sizeof(a));
   if (num_blocks < 1) return fail(KV4_EINVAL, "num_blocks must be >= 1 when there are query tokens");
+  a.lay = layout ? *layout : kv4::packed_layout(num_kv_heads, (int)code_row_bytes(qm, head_size), block_size);
+  if (int e = check_layout(qm, a.lay)) return e;
   if (int e = make_plan(qm, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
-                       max_seq_len, block_size, a.plan))
+                       max_seq_len, block_size, a.lay, a.plan))
     return e;
   const WsLayout ws = ws_layout(a.plan, num_q_tokens, num_seqs, num_q_heads, head_size);
   int32_t* prefix = nullptr;
@@ -498,5 +552,99 @@ int kv4_pth_dequant(int32_t kv_quant_mode, const void* cache, const float* scale
                       num_kv_heads, head_size, 0, block_size, 0, 0, out, stream);
 }
 
+
+int kv4_cache_layout_packed(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                            kv4_cache_layout* layout) {
+  if (kv_quant_mode < 0 || kv_quant_mode > 2) return fail(KV4_EINVAL, "kv_quant_mode must be 0, 1 or 2");
+  if (num_kv_heads < 1 || head_size < 8 || head_size % 8 || block_size < 1 || !layout)
+    return fail(KV4_EINVAL, "invalid sizes or null layout");
+  const kv4::CacheLayout l = kv4::packed_layout(num_kv_heads, (int)code_row_bytes(kv_quant_mode, head_size),
+                                                block_size);
+  *layout = kv4_cache_layout{l.blk, l.tok, l.head, l.sblk, l.stok, l.shead};
+  return ok();
+}
+
+int kv4_cache_layout_inline(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                            kv4_cache_layout* layout, int64_t* block_bytes, int64_t* value_offset,
+                            int64_t* scale_offset) {
+  if (kv_quant_mode < 0 || kv_quant_mode > 2) return fail(KV4_EINVAL, "kv_quant_mode must be 0, 1 or 2");
+  if (num_kv_heads < 1 || head_size < 8 || head_size % 8 || block_size < 1 || block_size > 4096 || !layout)
+    return fail(KV4_EINVAL, "invalid sizes or null layout");
+  const int64_t c = code_row_bytes(kv_quant_mode, head_size);
+  const int64_t pitch = (c + 4 + 15) / 16 * 16;               // codes, fp32 scale, zero padding
+  const int64_t half = (int64_t)block_size * num_kv_heads * pitch;
+  *layout = kv4_cache_layout{2 * half, num_kv_heads * pitch, pitch, 2 * half / 4, num_kv_heads * pitch / 4,
+                             pitch / 4};
+  if (block_bytes) *block_bytes = 2 * half;
+  if (value_offset) *value_offset = half;
+  if (scale_offset) *scale_offset = c;
+  return ok();
+}
+
+namespace {
+int check_any_mode(int32_t mode, int32_t head_size, int32_t b) {
+  if (mode == 0) return check_head(head_size, b);
+  if (int e = check_mode(mode)) return e;
+  return check_head_pth(head_size);
+}
+}  // namespace
+
+int kv4_write_layout(int32_t kv_quant_mode, const void* key, const void* value, int64_t key_token_stride,
+                     int64_t value_token_stride, void* key_cache, void* value_cache, float* k_scale_cache,
+                     float* v_scale_cache, const kv4_cache_layout* layout, const int64_t* slot_mapping,
+                     int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size,
+                     int64_t num_blocks, uint64_t sign_seed, void* stream) {
+  if (int e = check_any_mode(kv_quant_mode, head_size, b)) return e;
+  if (!layout) return fail(KV4_EINVAL, "null layout");
+  const kv4::CacheLayout l = to_layout(layout);
+  return write_impl(kv_quant_mode, "kv4_write_layout", key, value, key_token_stride, value_token_stride,
+                    key_cache, value_cache, k_scale_cache, v_scale_cache, slot_mapping, num_tokens, num_kv_heads,
+                    head_size, kv_quant_mode ? 1 : b, block_size, num_blocks, kv_quant_mode ? 0 : sign_seed,
+                    stream, &l);
+}
+
+size_t kv4_attention_layout_workspace_size(int32_t kv_quant_mode, const kv4_cache_layout* layout,
+                                           int64_t num_q_tokens, int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_size, int32_t max_query_len,
+                                           int32_t max_seq_len) {
+  if (kv_quant_mode != 0 && check_mode(kv_quant_mode)) return 0;
+  if (!layout) {
+    fail(KV4_EINVAL, "null layout");
+    return 0;
+  }
+  const kv4::CacheLayout l = to_layout(layout);
+  return workspace_impl(kv_quant_mode, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
+                        max_seq_len, &l);
+}
+
+int kv4_attention_layout(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
+                         const void* key_cache, const void* value_cache, const float* k_scale_cache,
+                         const float* v_scale_cache, const kv4_cache_layout* layout, int64_t num_blocks,
+                         const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
+                         int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_size, int32_t b, int32_t block_size, uint64_t sign_seed, float softmax_scale,
+                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int e = check_any_mode(kv_quant_mode, head_size, b)) return e;
+  if (!layout) return fail(KV4_EINVAL, "null layout");
+  const kv4::CacheLayout l = to_layout(layout);
+  return attention_impl(kv_quant_mode, query, query_token_stride, key_cache, value_cache, k_scale_cache,
+                        v_scale_cache, num_blocks, block_table, max_blocks_per_seq, seq_lens, query_start_loc,
+                        num_seqs, num_q_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_size,
+                        kv_quant_mode ? 1 : b, block_size, kv_quant_mode ? 0 : sign_seed, softmax_scale, out,
+                        workspace, workspace_bytes, stream, &l);
+}
+
+int kv4_dequant_layout(int32_t kv_quant_mode, const void* cache, const float* scale_cache,
+                       const kv4_cache_layout* layout, int64_t num_blocks, const int64_t* slot_mapping,
+                       int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size,
+                       uint64_t sign_seed, int32_t inverse_rotate, float* out, void* stream) {
+  if (int e = check_any_mode(kv_quant_mode, head_size, b)) return e;
+  if (!layout) return fail(KV4_EINVAL, "null layout");
+  const kv4::CacheLayout l = to_layout(layout);
+  return dequant_impl(kv_quant_mode, "kv4_dequant_layout", cache, scale_cache, num_blocks, slot_mapping,
+                      num_tokens, num_kv_heads, head_size, kv_quant_mode ? 1 : b, block_size,
+                      kv_quant_mode ? 0 : sign_seed, kv_quant_mode ? 0 : inverse_rotate, out, stream, &l);
+}
 
 }  // extern "C"

@@ -495,10 +495,14 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
   sign_xor_bf16x8(sbits, sx);
 
   // lane byte offsets inside one half tile (relative to its first token row)
-  const uint32_t tok_stride = (uint32_t)nkv * HALF;         // bytes between token rows of a page
+  // cache addressing (packed: token rows of nkv * HALF bytes, heads HALF
+  // bytes apart; or any layout the caller describes, e.g. scales inline)
+  const uint32_t tok_stride = (uint32_t)a.lay.tok;          // bytes between token rows of a page
+  const uint32_t head_bytes = (uint32_t)a.lay.head;         // bytes between kv heads of a row
   const uint32_t half_bytes = 16u * tok_stride;             // one half tile of a page
-  const int64_t page_bytes = (int64_t)bsz * tok_stride;     // one page of one cache
-  const int64_t page_rows = (int64_t)bsz * nkv;             // scale entries per page
+  const int64_t page_bytes = a.lay.blk;                     // one page of one cache
+  const int64_t page_rows = a.lay.sblk;                     // scale floats per page
+  const int64_t s_tok = a.lay.stok, s_head = a.lay.shead;   // scale floats per token row / head
   const uint32_t koff = (uint32_t)n * tok_stride + (uint32_t)q4 * (HALF / 4);
   uint32_t vo[4];                                           // token 4*q4 + i, 32-bit column chunk n
 #pragma unroll
@@ -536,7 +540,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
     const int t = 4 * q4 + i;
     vj_rd[i] = (uint32_t)((t / RPI) * 1024 + (t % RPI) * RB) + (HS >= 128 ? 4u : 2u) * (uint32_t)n;
   }
-  const uint32_t soff = (uint32_t)(lane & 15) * (uint32_t)nkv;   // scale elements
+  const int64_t soff = (int64_t)(lane & 15) * s_tok;         // scale floats
   const float* sc_base = lane < 32 ? a.k_scale : a.v_scale;
   const bool sc_half_b = (lane & 16) != 0;
 
@@ -699,11 +703,11 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
       const int offb = b_in ? (base + 16) & bs_mask : offa;
       // byte offset of the first token row of each half tile inside a cache,
       // and the scale index of that row (first kv head of the unit); head hl
-      // of the unit sits hl * HALF bytes (hl scale entries) further on
-      const int64_t bya = (int64_t)pa * page_bytes + (int64_t)(offa * nkv + kv0) * HALF;
-      const int64_t byb = (int64_t)pb * page_bytes + (int64_t)(offb * nkv + kv0) * HALF;
-      int64_t rowa = (int64_t)pa * page_rows + offa * nkv + kv0;
-      int64_t rowb = (int64_t)pb * page_rows + offb * nkv + kv0;
+      // of the unit sits hl head strides further on
+      const int64_t bya = (int64_t)pa * page_bytes + (int64_t)offa * tok_stride + (int64_t)kv0 * head_bytes;
+      const int64_t byb = (int64_t)pb * page_bytes + (int64_t)offb * tok_stride + (int64_t)kv0 * head_bytes;
+      int64_t rowa = (int64_t)pa * page_rows + offa * s_tok + kv0 * s_head;
+      int64_t rowb = (int64_t)pb * page_rows + offb * s_tok + kv0 * s_head;
       const uint32_t nrec = dummy ? 0u : half_bytes;
       if (dummy) { rowa = 0; rowb = 0; }   // scale rows 0..15 of page 0: lines every wave keeps hot
       v_bya = bya;
@@ -720,12 +724,12 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 #pragma unroll
           for (int j = 0; j < SG::NKL; ++j) {
             unsigned char* dst = sth + SG::K_OFF + h * SG::KHALF + j * SG::KREG;
-            const uint32_t o = koff + j * SG::KSZ + hl * HALF;
+            const uint32_t o = koff + j * SG::KSZ + hl * head_bytes;
             if constexpr (SG::KSZ == 16) dma_buf<16>(rk[h], o, dst);
             else if constexpr (SG::KSZ == 12) dma_buf<12>(rk[h], o, dst);
             else dma_buf<4>(rk[h], o, dst);
           }
-        dma(scp + hl, sth + SG::S_OFF, 4);
+        dma(scp + hl * s_head, sth + SG::S_OFF, 4);
       }
     };
     auto issue_v = [&](unsigned char* __restrict__ st) {
@@ -750,7 +754,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             unsigned char* dst = sth + SG::V_OFF + i * SG::VBYTES_TOK;
-            const uint32_t o = vo[i & 3] + hl * HALF;
+            const uint32_t o = vo[i & 3] + hl * head_bytes;
 #pragma unroll
             for (int r = 0; r < GG::RDW; ++r) dma_buf<4>(rv[i >> 2], o + 64 * r, dst + r * 256);
             if constexpr (GG::RUS) dma_buf<2>(rv[i >> 2], o - 2u * n + 64 * GG::RDW, dst + GG::RDW * 256);

@@ -219,31 +219,30 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
   }
 
   const int32_t* bt = a.block_table + (int64_t)t.s * a.max_blocks;
-  const int half_row = hs >> 1;
-  const int nkv = a.nkv;
 
   for (int base = k0; base < k1; base += TPI) {
     const int tok = base + tg;
     bool valid = tok < k1;
-    int64_t row = 0;
+    int64_t coff = 0, soff = 0;
     if (valid) {
       const int page = bt[tok / a.bs];
       valid = page >= 0 && page < a.num_blocks;
-      row = ((int64_t)page * a.bs + (tok % a.bs)) * nkv + g;
+      coff = a.lay.code_off(page, tok % a.bs, g);
+      soff = a.lay.scale_off(page, tok % a.bs, g);
     }
     uint32_t kw = 0u, vw = 0u;
     uint2 kb = make_uint2(0u, 0u), vb = make_uint2(0u, 0u);
     float ks = 0.0f, vs = 0.0f;
     if (valid) {
-      ks = a.k_scale[row];
-      vs = a.v_scale[row];
+      ks = a.k_scale[soff];
+      vs = a.v_scale[soff];
       if (lane_on) {
         if constexpr (QM == 0) {
-          kw = *reinterpret_cast<const uint32_t*>(a.key_cache + row * half_row + 4 * jj);
-          vw = *reinterpret_cast<const uint32_t*>(a.value_cache + row * half_row + 4 * jj);
+          kw = *reinterpret_cast<const uint32_t*>(a.key_cache + coff + 4 * jj);
+          vw = *reinterpret_cast<const uint32_t*>(a.value_cache + coff + 4 * jj);
         } else {
-          kb = *reinterpret_cast<const uint2*>(a.key_cache + row * hs + 8 * jj);
-          vb = *reinterpret_cast<const uint2*>(a.value_cache + row * hs + 8 * jj);
+          kb = *reinterpret_cast<const uint2*>(a.key_cache + coff + 8 * jj);
+          vb = *reinterpret_cast<const uint2*>(a.value_cache + coff + 8 * jj);
         }
       }
     }

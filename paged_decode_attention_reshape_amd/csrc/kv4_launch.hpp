@@ -15,6 +15,33 @@ inline int host_next_pow2(int x) {
   return p;
 }
 
+// Addressing of a paged cache: the code bytes of (page p, token slot t of
+// the page, kv head h) start p * blk + t * tok + h * head bytes after the
+// cache base, and its scale sits p * sblk + t * stok + h * shead floats after
+// the scale base. The packed layout (C code bytes per row): blk = bs * nkv *
+// C, tok = nkv * C, head = C, sblk = bs * nkv, stok = nkv, shead = 1.
+struct CacheLayout {
+  int64_t blk, tok, head;
+  int64_t sblk, stok, shead;
+  __host__ __device__ int64_t code_off(int64_t page, int64_t t, int64_t h) const {
+    return page * blk + t * tok + h * head;
+  }
+  __host__ __device__ int64_t scale_off(int64_t page, int64_t t, int64_t h) const {
+    return page * sblk + t * stok + h * shead;
+  }
+};
+
+inline CacheLayout packed_layout(int nkv, int code_bytes, int bs) {
+  CacheLayout l;
+  l.head = code_bytes;
+  l.tok = (int64_t)nkv * code_bytes;
+  l.blk = (int64_t)bs * l.tok;
+  l.shead = 1;
+  l.stok = nkv;
+  l.sblk = (int64_t)bs * nkv;
+  return l;
+}
+
 struct WriteArgs {
   const uint16_t* key;
   const uint16_t* value;
@@ -32,6 +59,9 @@ struct WriteArgs {
   int b;
   uint64_t seed;
   int qm;                // 0: int4 RHT; 1: int8 per-token-head; 2: fp8 (e4m3fn) per-token-head
+  int bs;                // block size
+  int bs_shift;          // log2(bs) if bs is a power of two, else -1
+  CacheLayout lay;
 };
 
 struct DequantArgs {
@@ -47,6 +77,9 @@ struct DequantArgs {
   int inverse_rotate;
   float* out;
   int qm;                // as WriteArgs
+  int bs;
+  int bs_shift;
+  CacheLayout lay;
 };
 
 // Waves per workgroup of the matrix-core kernel at (kv heads per wave, cache
@@ -107,6 +140,7 @@ struct AttnArgs {
                        // stream-K: [sk_pcap + quads * num_seqs][nq][hs] and [..][nq][2]
   const int32_t* prefix;   // MFMA path: device plan output (stream-K: first KV step per sequence)
   int qm;                  // 0: int4 RHT cache; 1 / 2: int8 / fp8 per-token-head cache (no rotation)
+  CacheLayout lay;         // shared by the K and V caches and their scales
   AttnPlan plan;
 };
 

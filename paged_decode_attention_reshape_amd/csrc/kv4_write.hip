@@ -66,6 +66,12 @@ __device__ __forceinline__ uint32_t quant_byte(float x, float scale) {
   }
 }
 
+// Page of a slot (block size a power of two: a shift).
+template <typename Args>
+__device__ __forceinline__ int64_t slot_page(const Args& a, int64_t slot) {
+  return a.bs_shift >= 0 ? (slot >> a.bs_shift) : slot / a.bs;
+}
+
 template <int LP, int QM>
 __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
   constexpr int VPW = kWave / LP;                      // vectors per wave
@@ -81,7 +87,6 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
   const int64_t n_items = a.num_tokens * 2 * a.nkv;
   const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  const int half_row = a.hs >> 1;
 
   for (int64_t base = wave_id * VPW; base < n_items; base += n_waves * VPW) {
     const int64_t item = base + grp;
@@ -127,9 +132,9 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
       }
       if (ok && lane_on) {
         uint8_t* cache = kind ? a.value_cache : a.key_cache;
-        const int64_t row = slot * a.nkv + h;
-        *reinterpret_cast<uint32_t*>(cache + row * half_row + 4 * jj) = packed;
-        if (jj == 0) (kind ? a.v_scale : a.k_scale)[row] = scale;
+        const int64_t pg = slot_page(a, slot), tk = slot - pg * a.bs;
+        *reinterpret_cast<uint32_t*>(cache + a.lay.code_off(pg, tk, h) + 4 * jj) = packed;
+        if (jj == 0) (kind ? a.v_scale : a.k_scale)[a.lay.scale_off(pg, tk, h)] = scale;
       }
     } else {
       const float scale = amax / (QM == 1 ? 127.0f : 448.0f);
@@ -143,9 +148,9 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
       }
       if (ok && lane_on) {
         uint8_t* cache = kind ? a.value_cache : a.key_cache;
-        const int64_t row = slot * a.nkv + h;
-        *reinterpret_cast<uint2*>(cache + row * a.hs + 8 * jj) = make_uint2(lo, hi);
-        if (jj == 0) (kind ? a.v_scale : a.k_scale)[row] = scale;
+        const int64_t pg = slot_page(a, slot), tk = slot - pg * a.bs;
+        *reinterpret_cast<uint2*>(cache + a.lay.code_off(pg, tk, h) + 8 * jj) = make_uint2(lo, hi);
+        if (jj == 0) (kind ? a.v_scale : a.k_scale)[a.lay.scale_off(pg, tk, h)] = scale;
       }
     }
   }
@@ -164,7 +169,6 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   const int64_t n_items = a.num_tokens * a.nkv;
   const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  const int half_row = a.hs >> 1;
 
   for (int64_t base = wave_id * VPW; base < n_items; base += n_waves * VPW) {
     const int64_t item = base + grp;
@@ -181,10 +185,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     uint2 bytes = make_uint2(0u, 0u);
     float sc = 0.0f;
     if (ok && lane_on) {
-      const int64_t row = slot * a.nkv + h;
-      if constexpr (QM == 0) codes = *reinterpret_cast<const uint32_t*>(a.cache + row * half_row + 4 * jj);
-      else bytes = *reinterpret_cast<const uint2*>(a.cache + row * a.hs + 8 * jj);
-      sc = a.scale[row];
+      const int64_t pg = slot_page(a, slot), tk = slot - pg * a.bs;
+      const uint8_t* src = a.cache + a.lay.code_off(pg, tk, h);
+      if constexpr (QM == 0) codes = *reinterpret_cast<const uint32_t*>(src + 4 * jj);
+      else bytes = *reinterpret_cast<const uint2*>(src + 8 * jj);
+      sc = a.scale[a.lay.scale_off(pg, tk, h)];
     }
     float v[8];
     if constexpr (QM == 0) {

@@ -24,7 +24,9 @@ def test_header_declares_the_boundary():
     assert kv4.header_functions() == sorted([
         "kv4_dequant", "kv4_last_error", "kv4_paged_attention",
         "kv4_paged_attention_workspace_size", "kv4_rht_write",
-        "kv4_pth_write", "kv4_pth_dequant", "kv4_pth_attention", "kv4_pth_attention_workspace_size"])
+        "kv4_pth_write", "kv4_pth_dequant", "kv4_pth_attention", "kv4_pth_attention_workspace_size",
+        "kv4_cache_layout_packed", "kv4_cache_layout_inline", "kv4_write_layout",
+        "kv4_attention_layout_workspace_size", "kv4_attention_layout", "kv4_dequant_layout"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -169,3 +171,40 @@ def test_pth_mode_validation(L):
     assert rc == EINVAL
     with pytest.raises(ValueError):
         kv4._mode("int4")
+
+
+def test_cache_layouts_on_the_host():
+    """Packed and inline layouts (host-only helpers; no GPU needed)."""
+    p = kv4.kv4_cache_layout_packed("int4", 8, 128, 16).as_tuple()
+    assert p == (16 * 8 * 64, 8 * 64, 64, 16 * 8, 8, 1)
+    p = kv4.kv4_cache_layout_packed("fp8", 2, 96, 32).as_tuple()
+    assert p == (32 * 2 * 96, 2 * 96, 96, 32 * 2, 2, 1)
+    lay, bb, vo, so = kv4.kv4_cache_layout_inline("int4", 8, 128, 16)
+    # 64 code bytes + 4-byte scale -> 80-byte rows; K half then V half
+    assert (bb, vo, so) == (2 * 16 * 8 * 80, 16 * 8 * 80, 64)
+    assert lay.as_tuple() == (bb, 8 * 80, 80, bb // 4, 8 * 80 // 4, 80 // 4)
+    lay, bb, vo, so = kv4.kv4_cache_layout_inline("int8", 3, 8, 1)
+    assert (lay.head_stride, so, bb) == (16, 8, 2 * 3 * 16)
+    with pytest.raises(kv4.Kv4Error):
+        kv4.kv4_cache_layout_inline("int4", 0, 128, 16)
+    with pytest.raises(ValueError):
+        kv4.kv4_cache_layout_inline("int2", 8, 128, 16)
+
+
+def test_invalid_layouts_are_rejected_on_the_host():
+    good = kv4.kv4_cache_layout_inline("int8", 2, 64, 16)[0]
+
+    class C:   # a LayoutCache stand-in; only its sizes and layout are read
+        mode, num_kv_heads, head_size = 1, 2, 64
+
+    def ws(t):
+        c = C()
+        c.layout = kv4.CacheLayout(*t)
+        return kv4.kv4_attention_layout_workspace_size(c, 4, 2, 8, 1, 100)
+
+    assert ws(good.as_tuple()) >= 0
+    for bad in [(0, 128, 64, 10, 5, 1),            # zero stride
+                (4096, 132, 64, 10, 5, 1),         # int8 code stride not a multiple of 8
+                (4096, 128, 64, 10, 5, -1)]:       # negative scale stride
+        with pytest.raises(kv4.Kv4Error):
+            ws(bad)
