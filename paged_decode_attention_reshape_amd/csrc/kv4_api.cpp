@@ -119,7 +119,9 @@ int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_
   // Single-token decode on the matrix cores: one wave serves hpw kv heads
   // (hpw * G <= 16 MFMA rows), sharing its softmax and page walk.
   p.hpw = 1;
-  if (mfma && max_query_len <= 1 && qm == 0 && lay_contig) {
+  // several heads per wave need the heads of a token row side by side,
+  // except at head size 128 where V can be staged per head
+  if (mfma && max_query_len <= 1 && qm == 0 && (lay_contig || hs == 128)) {
     long want = env_long("KV4_MFMA_HPW", 0);
     if (want != 1 && want != 2 && want != 4) want = mfma_hpw_max(hs);
     if (want > 2 && (hs == 96 || hs == 192)) want = 2;   // four heads' V loads would exceed the load counter
@@ -127,6 +129,7 @@ int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_
     p.hpw = (int)want;
   }
   p.wpb = kv4::mfma_waves_per_block(p.hpw, qm, hs);
+  p.vjh = (p.hpw > 1 && !lay_contig) ? 1 : 0;
   // Single-token decode on the matrix cores, with whole workgroups of kv head
   // groups: stream-K partition of the KV steps over the resident workgroups
   // (no split size; every workgroup gets the same number of steps).

@@ -442,7 +442,11 @@ constexpr int mfma_wpe() {
 // q' row is first scaled by a power of two that puts its largest element in
 // [2^14, 2^15) (fp16 keeps its full precision whatever the query's range);
 // the logits take the inverse power back.
-template <int HS, int HPW, int QM>
+//
+// PH (head size 128, several heads per wave): V staged per head instead of as
+// joint token rows of the wave's heads, for layouts whose heads of a token
+// row are not adjacent (about 1 % slower than joint rows where they are).
+template <int HS, int HPW, int QM, bool PH>
 __global__ __launch_bounds__((64 * mfma_wpb<HS, HPW, QM>()))
 __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_kernel(AttnArgs a,
                                                                                   const int32_t* prefix) {
@@ -512,8 +516,14 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
   // after row, RB bytes each, 1 KB per load). Lane l of a load fetches bytes
   // [16 l % RB, +16) of token row 16 l / RB.
   constexpr int RB = HPW * HALF;                            // V bytes per token row of the wave
-  constexpr bool VJ = QM == 0 && (RB == 64 || RB == 128);
+  // Per-head variant (VJH, head size 128 with several heads per wave): each
+  // head's 64-byte rows land in its own stage, so the heads of a token row
+  // need not be adjacent in memory.
+  constexpr bool VJH = QM == 0 && HPW > 1 && HALF == 64 && PH;
+  static_assert(!PH || VJH, "per-head V staging: int4, head size 128, several heads per wave");
+  constexpr bool VJ = QM == 0 && !VJH && (RB == 64 || RB == 128);
   constexpr int RPI = 1024 / RB;                            // token rows per 1 KB load (VJ)
+  const uint32_t vjh_src = (uint32_t)(lane >> 2) * tok_stride + 16u * (uint32_t)(lane & 3);
   const uint32_t vj_src = (uint32_t)((16 * lane) / RB) * tok_stride + (uint32_t)((16 * lane) % RB);
   // ... and lane (n, q4) reads, for token 4 q4 + i of a half tile, its column
   // chunk n of head hl at vj_rd[i] + hl * HALF: 4 bytes (8 columns, head
@@ -538,7 +548,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = 4 * q4 + i;
-    vj_rd[i] = (uint32_t)((t / RPI) * 1024 + (t % RPI) * RB) + (HS >= 128 ? 4u : 2u) * (uint32_t)n;
+    vj_rd[i] = VJH ? (uint32_t)(t * 64) + 4u * (uint32_t)n
+                   : (uint32_t)((t / RPI) * 1024 + (t % RPI) * RB) + (HS >= 128 ? 4u : 2u) * (uint32_t)n;
   }
   const int64_t soff = (int64_t)(lane & 15) * s_tok;         // scale floats
   const float* sc_base = lane < 32 ? a.k_scale : a.v_scale;
@@ -671,7 +682,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
     // loads with an empty buffer range (they fetch nothing and fill the slot
     // with zeros, which is never read).
     constexpr int NLK = HPW * (2 * SG::NKL + 1);   // loads per issue_k
-    constexpr int NLV = QM ? 2 * StageGeoQ<HS>::VL : (VJ ? 2 * (16 / RPI) : HPW * 8 * NVR);   // loads per issue_v
+    constexpr int NLV = QM ? 2 * StageGeoQ<HS>::VL
+                           : (VJH ? 2 * HPW : (VJ ? 2 * (16 / RPI) : HPW * 8 * NVR));   // loads per issue_v
     // VJ: half tile hh of a slot (16 * RB bytes) sits in head hh's V region
     // (2 KB; RB = 128, two or more heads per wave) or at V_OFF + hh KB (RB = 64)
     auto vj_base = [&](auto* st, int hh) { return st + (RB == 128 ? hh * STH : hh * 1024) + SG::V_OFF; };
@@ -741,6 +753,12 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 #pragma unroll
           for (int j = 0; j < StageGeoQ<HS>::VL; ++j)
             dma_buf<16>(rv[hh], vq_src[j], st + SG::V_OFF + hh * StageGeoQ<HS>::VHALF + j * 1024);
+      } else if constexpr (VJH) {
+#pragma unroll
+        for (int hl = 0; hl < HPW; ++hl)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            dma_buf<16>(rv[hh], vjh_src + hl * head_bytes, st + hl * STH + SG::V_OFF + hh * 1024);
       } else if constexpr (VJ) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -952,7 +970,9 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
           uint32_t x[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            if constexpr (VJ) {
+            if constexpr (VJH) {
+              x[i] = *reinterpret_cast<const uint32_t*>(st + hl * STH + SG::V_OFF + (i >> 2) * 1024 + vj_rd[i & 3]);
+            } else if constexpr (VJ) {
               const unsigned char* src = vj_base(st, i >> 2) + vj_rd[i & 3] + hl * HALF;
               if constexpr (HS >= 128) x[i] = *reinterpret_cast<const uint32_t*>(src);
               else x[i] = *reinterpret_cast<const uint16_t*>(src);
@@ -1147,13 +1167,13 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 
 static int g_num_cus = 0;
 
-template <int HS, int HPW, int QM>
+template <int HS, int HPW, int QM, bool PH = false>
 static int resident_blocks() {
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb,
-                                                     reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM>),
+                                                     reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH>),
                                                      64 * mfma_wpb<HS, HPW, QM>(), 0) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
@@ -1182,17 +1202,30 @@ static hipError_t launch_hs(AttnArgs& a, const int32_t* prefix, int64_t max_unit
     hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(64 * wpb), 0, stream, a, prefix);
   };
   if constexpr (QM != 0) {
-    go(attn_mfma_kernel<HS, 1, QM>, mfma_wpb<HS, 1, QM>(), resident_blocks<HS, 1, QM>());
+    go(attn_mfma_kernel<HS, 1, QM, false>, mfma_wpb<HS, 1, QM>(), resident_blocks<HS, 1, QM>());
     return hipSuccess;
   }
+  if (a.plan.vjh) {
+    if constexpr (HS == 128) {
+      if (a.plan.hpw == 2) {
+        go(attn_mfma_kernel<HS, 2, 0, true>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0, true>());
+      } else if (a.plan.hpw == 4) {
+        go(attn_mfma_kernel<HS, 4, 0, true>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0, true>());
+      } else {
+        return hipErrorInvalidValue;
+      }
+      return hipSuccess;
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.plan.hpw) {
-    case 2: go(attn_mfma_kernel<HS, 2, 0>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0>()); break;
+    case 2: go(attn_mfma_kernel<HS, 2, 0, false>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0>()); break;
     case 4:
       // four heads' V loads of a step must fit the 6-bit load counter
       if constexpr (Geo<HS>::NVR == 1)
-        go(attn_mfma_kernel<HS, 4, 0>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0>());
+        go(attn_mfma_kernel<HS, 4, 0, false>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0>());
       break;
-    default: go(attn_mfma_kernel<HS, 1, 0>, mfma_wpb<HS, 1, 0>(), resident_blocks<HS, 1, 0>()); break;
+    default: go(attn_mfma_kernel<HS, 1, 0, false>, mfma_wpb<HS, 1, 0>(), resident_blocks<HS, 1, 0>()); break;
   }
   return hipSuccess;
 }

@@ -109,6 +109,7 @@ struct AttnPlan {
   int sk_quads;        // stream-K: kv head groups / waves per workgroup
   int sk_pcap;         // stream-K: most workgroups (sizes the workspace)
   int sk_grid;         // stream-K: workgroups launched (set at launch)
+  int vjh;             // MFMA, head size 128, hpw > 1: V staged per head (heads not adjacent)
 };
 
 struct AttnArgs {

@@ -92,6 +92,10 @@ SCHED = {
     "valu": {"KV4_FORCE_PATH": "valu"},
     "mfma_streamk": {"KV4_FORCE_PATH": "mfma"},
     "mfma_splits64": {"KV4_FORCE_PATH": "mfma", "KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64"},
+    # several kv heads per wave over rows whose heads are not adjacent (int4:
+    # V staged per head; int8 / fp8 keep one head per wave)
+    "mfma_hpw4": {"KV4_FORCE_PATH": "mfma", "KV4_MFMA_HPW": "4"},
+    "mfma_hpw1": {"KV4_FORCE_PATH": "mfma", "KV4_MFMA_HPW": "1"},
 }
 
 
