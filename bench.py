@@ -48,12 +48,21 @@ def code_bytes(w, mode: str) -> int:
     return w.head_size // 2 if mode == "int4" else w.head_size
 
 
-def attention_bytes(w, mode: str = "int4") -> int:
+def visible_keys(w, window: int = 0):
+    """Per sequence, the keys some query of it can see: all L, or with a
+    sliding window the last window + query_len - 1 of them."""
+    if window <= 0:
+        return list(w.seq_lens)
+    return [min(L, window + q - 1) if q > 0 else 0 for L, q in zip(w.seq_lens, w.query_lens)]
+
+
+def attention_bytes(w, mode: str = "int4", window: int = 0) -> int:
     """Algorithmic bytes one attention pass must move: for every sequence,
     every visible (KV token, kv head): the K and V code rows + 2 fp32 scales;
     plus block-table entries, bf16 query in and bf16 output out."""
-    kv = kv_bytes(w, mode)
-    bt = sum(-(-L // w.block_size) for L in w.seq_lens) * 4
+    vis = visible_keys(w, window)
+    kv = int(sum(vis) * w.num_kv_heads * (2 * code_bytes(w, mode) + 8))
+    bt = sum(-(-n // w.block_size) for n in vis) * 4
     qo = w.num_q_tokens * w.num_q_heads * w.head_size * 2 * 2
     return int(kv + bt + qo)
 
@@ -76,6 +85,8 @@ def main():
     ap.add_argument("--config", default="llama8b_long")
     ap.add_argument("--kv-mode", default="int4", choices=["int4", "int8", "fp8"],
                     help="cache format: int4 RHT (the method) or the per-token-head int8 / fp8 controls")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window (keys per query; 0 = full causal attention)")
     ap.add_argument("--layout", default="packed", choices=["packed", "inline"],
                     help="cache layout: separate packed code and scale tensors, or one buffer with each "
                          "row's scale inline and rows padded to 16 bytes")
@@ -127,8 +138,8 @@ def main():
 
     nb, bs, nkv, hs = lay.num_blocks, w.block_size, w.num_kv_heads, w.head_size
     mode = args.kv_mode
-    inline = args.layout == "inline"
-    if inline:
+    inline = args.layout == "inline" or args.window > 0
+    if args.layout == "inline":
         lcache = kv4.LayoutCache.inline(mode, nb, bs, nkv, hs, device=dev)
         kc = vc = ks = vs = None
     else:
@@ -136,6 +147,8 @@ def main():
         vc = torch.zeros_like(kc)
         ks = torch.zeros((nb, bs, nkv), dtype=torch.float32, device=dev)
         vs = torch.zeros_like(ks)
+        if inline:    # packed caches through the layout entry points (sliding window)
+            lcache = kv4.packed_layout_cache(mode, kc, vc, ks, vs)
     stream = torch.cuda.Stream()
 
     def write(k, v, slots):
@@ -194,7 +207,8 @@ def main():
             e_a.record(stream)
         if inline:
             kv4.kv4_attention_layout(q, lcache, bt, slens, qsl, w.max_query_len, w.max_seq_len,
-                                     sign_seed=w.sign_seed, out=out, workspace=ws, stream=stream)
+                                     sign_seed=w.sign_seed, out=out, workspace=ws, stream=stream,
+                                     sliding_window=args.window)
         elif mode == "int4":
             kv4.kv4_paged_attention(q, kc, vc, ks, vs, bt, slens, qsl, max_query_len=w.max_query_len,
                                     max_seq_len=w.max_seq_len, sign_seed=w.sign_seed, out=out, workspace=ws,
@@ -223,7 +237,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     attn_avg_ms = float(np.mean(attn_ms))
 
-    a_bytes = attention_bytes(w, mode)
+    a_bytes = attention_bytes(w, mode, args.window)
     value = a_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = a_bytes / (attn_avg_ms * 1e-3) / 1e9
 
@@ -231,7 +245,8 @@ def main():
     if os.path.exists(PROFILE_COUNTERS):
         try:
             pc = json.load(open(PROFILE_COUNTERS))
-            key = w.name + ("" if mode == "int4" else f"_{mode}") + ("_inline" if inline else "")
+            key = (w.name + ("" if mode == "int4" else f"_{mode}") + ("_inline" if args.layout == "inline" else "")
+                   + (f"_w{args.window}" if args.window > 0 else ""))
             ent = pc.get("workloads", {}).get(key)
             if ent and pc.get("kernel_source_hash") == kernel_source_hash():
                 traffic = ent.get("traffic_bytes_per_launch")
@@ -241,7 +256,8 @@ def main():
     line = {
         "metric": "INT4 paged decode attn: KV GB/s & % HBM peak; cache-write tokens/s"
                   + ("" if mode == "int4" else f" ({mode} per-token-head control cache)")
-                  + (" (inline-scale padded-slot layout)" if inline else ""),
+                  + (" (inline-scale padded-slot layout)" if args.layout == "inline" else "")
+                  + (f" (sliding window {args.window})" if args.window > 0 else ""),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -253,7 +269,8 @@ def main():
         "vs_baseline": None,
         "dtype": f"{mode} codes / fp32 accumulate (bf16 in/out)",
         "data": "synthetic seeded N(0,1) bf16, 1% outlier channels x20",
-        "config": {"workload": w.name, "kv_cache": mode, "cache_layout": args.layout, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+        "config": {"workload": w.name, "kv_cache": mode, "cache_layout": args.layout,
+                   "sliding_window": args.window, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": nkv, "head_size": hs, "block_size": bs,
                    "total_kv_tokens": w.total_kv_tokens, "max_seq_len": w.max_seq_len,
                    "q_tokens_per_step": w.num_q_tokens, "new_kv_tokens_per_step": int(new_rows.shape[0]),
@@ -261,7 +278,7 @@ def main():
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "attn_ms": round(attn_avg_ms, 4),
         "attn_query_tokens_per_s": round(w.num_q_tokens / (attn_avg_ms * 1e-3), 1),
-        "kv_bytes_per_step": kv_bytes(w, mode),
+        "kv_bytes_per_step": int(sum(visible_keys(w, args.window)) * w.num_kv_heads * (2 * code_bytes(w, mode) + 8)),
         "write_tokens_per_s": round(write_tps, 1),
         "write_GBps": round(write_gbs, 2),
         "write_bulk_tokens": n_ctx,
@@ -274,11 +291,11 @@ def main():
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, lay, t, kc, vc, ks, vs, args.cpu_seconds, mode,
-                                            lcache if inline else None)
+                                            lcache if args.layout == "inline" else None, args.window)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float, mode: str = "int4", lcache=None):
+def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float, mode: str = "int4", lcache=None, window: int = 0):
     """The CPU oracle (fp64 numpy) on a bounded sample of the same workload:
     whole sequences of this batch, read from the GPU-written cache, until
     about `budget_s` seconds of CPU work; reported as KV GB/s like `value`."""
@@ -311,12 +328,12 @@ def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float, mode: str = "int4",
         t0 = time.perf_counter()
         if mode == "int4":
             O.paged_attention(q, kcs, vcs, kss, vss, bt, lay.seq_lens, lay.query_start_loc,
-                              w.head_size ** -0.5, w.sign_seed, seqs=[int(s)])
+                              w.head_size ** -0.5, w.sign_seed, seqs=[int(s)], window=window)
         else:
             O.pth_paged_attention(q, kcs, vcs, kss, vss, bt, lay.seq_lens, lay.query_start_loc,
-                                  w.head_size ** -0.5, mode, seqs=[int(s)])
+                                  w.head_size ** -0.5, mode, seqs=[int(s)], window=window)
         spent += time.perf_counter() - t0
-        done_bytes += int(w.seq_lens[s]) * w.num_kv_heads * (2 * code_bytes(w, mode) + 8)
+        done_bytes += int(visible_keys(w, window)[s]) * w.num_kv_heads * (2 * code_bytes(w, mode) + 8)
         done_seqs += 1
         if spent >= budget_s:
             break

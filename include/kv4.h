@@ -323,6 +323,14 @@ int kv4_cache_layout_inline(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t
  * sign_seed and inverse_rotate are ignored) over caches in `layout`. Same
  * results, argument rules and errors, plus KV4_EINVAL for an invalid layout.
  * The workspace size depends on the layout (it selects the plan).
+ *
+ * kv4_attention_layout also takes sliding_window (0 = off): the query at
+ * position p then sees only keys j with p - sliding_window < j <= p, the
+ * window most recent keys of its causal range (the pages' "added window"
+ * commit of vLLM PR #40835 names the feature; this rule is the reading taken
+ * here). Keys below every row's window are not read. Negative values give
+ * KV4_EINVAL. Pass the packed layout (kv4_cache_layout_packed) for the caches
+ * of the other entry points.
  */
 int kv4_write_layout(int32_t kv_quant_mode, const void* key, const void* value,
                      int64_t key_token_stride, int64_t value_token_stride,
@@ -348,7 +356,7 @@ int kv4_attention_layout(int32_t kv_quant_mode, const void* query, int64_t query
                          int32_t max_query_len, int32_t max_seq_len,
                          int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_size, int32_t b, int32_t block_size,
-                         uint64_t sign_seed, float softmax_scale,
+                         uint64_t sign_seed, int32_t sliding_window, float softmax_scale,
                          void* out, void* workspace, size_t workspace_bytes,
                          void* stream);
 int kv4_dequant_layout(int32_t kv_quant_mode, const void* cache, const float* scale_cache,

@@ -268,12 +268,17 @@ def gather_seq(cache: np.ndarray, scale_cache: np.ndarray, block_table_row: np.n
 # Attention
 # ---------------------------------------------------------------------------
 
-def _causal_softmax_attend(logits: np.ndarray, vals: np.ndarray, L: int) -> np.ndarray:
-    """logits [ql, ..., L]: row i (query i of ql) may see keys 0 .. L - ql + i;
-    returns softmax(logits) @ vals with vals [L, hs]."""
+def _causal_softmax_attend(logits: np.ndarray, vals: np.ndarray, L: int, window: int = 0) -> np.ndarray:
+    """logits [ql, ..., L]: row i (query i of ql, position pos = L - ql + i)
+    may see keys 0 .. pos, and with a sliding window W > 0 only keys j with
+    pos - W < j <= pos (the W most recent); returns softmax(logits) @ vals
+    with vals [L, hs]."""
     ql = logits.shape[0]
     pos = L - ql + np.arange(ql)
-    mask = np.arange(L)[None, :] > pos[:, None]                  # [ql, L]
+    keys = np.arange(L)[None, :]
+    mask = keys > pos[:, None]                                    # [ql, L]
+    if window > 0:
+        mask |= keys <= pos[:, None] - window
     mask = mask.reshape((ql,) + (1,) * (logits.ndim - 2) + (L,))
     lg = np.where(mask, -np.inf, logits)
     m = lg.max(axis=-1, keepdims=True)
@@ -284,14 +289,17 @@ def _causal_softmax_attend(logits: np.ndarray, vals: np.ndarray, L: int) -> np.n
 
 def paged_attention(query, key_cache, value_cache, k_scale_cache, v_scale_cache,
                     block_table, seq_lens, query_start_loc, softmax_scale: float,
-                    sign_seed: int, seqs=None) -> np.ndarray:
+                    sign_seed: int, seqs=None, window: int = 0) -> np.ndarray:
     """fp64 attention over the int4 RHT cache in the rotated domain
     ([PR62881] Root cause; divisor b per [PR56198]):
         q' = H.D.q,  logit_j = (q' . K_s_j) * softmax_scale / b,
         o' = softmax(logit) @ V_s,  o = D.H.o' / b.
     K_s, V_s are the dequantized cache values gathered through block_table.
     Causal: query i of sequence s (query_len q, seq_len L) sees keys
-    0 .. L - q + i. GQA: q head h reads kv head h // (nq / nkv).
+    0 .. L - q + i; with window > 0 only the `window` most recent of them
+    (the pages' "added window" commit names the feature and nothing more;
+    reading: key j is visible iff pos - window < j <= pos). GQA: q head h
+    reads kv head h // (nq / nkv).
     Returns fp64 [num_q_tokens, nq, hs]; rows of sequences not in `seqs`
     are NaN."""
     q = np.asarray(query, dtype=np.float64)
@@ -315,13 +323,13 @@ def paged_attention(query, key_cache, value_cache, k_scale_cache, v_scale_cache,
         for g in range(nkv):
             qg = qr[:, g * group:(g + 1) * group, :]                      # [ql, group, hs]
             logits = (qg @ Ks[:, g, :].T) * softmax_scale / b            # [ql, group, L]
-            o_rot = _causal_softmax_attend(logits, Vs[:, g, :], L)       # [ql, group, hs]
+            o_rot = _causal_softmax_attend(logits, Vs[:, g, :], L, window)   # [ql, group, hs]
             out[q0:q1, g * group:(g + 1) * group] = unrotate_math(o_rot, signs)
     return out
 
 
 def attention_dense(query, key, value, query_start_loc, seq_lens, softmax_scale: float,
-                    kv_start, seqs=None) -> np.ndarray:
+                    kv_start, seqs=None, window: int = 0) -> np.ndarray:
     """Plain fp64 causal attention in the original domain:
     softmax(q . k * softmax_scale) @ v per sequence, GQA head h -> h // group.
     Rows of sequence s in `key`/`value` are kv_start[s] .. kv_start[s] + L_s.
@@ -345,7 +353,7 @@ def attention_dense(query, key, value, query_start_loc, seq_lens, softmax_scale:
         for g in range(nkv):
             qg = q[q0:q1, g * group:(g + 1) * group, :]
             logits = (qg @ k[:, g, :].T) * softmax_scale
-            out[q0:q1, g * group:(g + 1) * group] = _causal_softmax_attend(logits, v[:, g, :], L)
+            out[q0:q1, g * group:(g + 1) * group] = _causal_softmax_attend(logits, v[:, g, :], L, window)
     return out
 
 
@@ -484,7 +492,7 @@ def pth_gather_seq(cache, scale_cache, block_table_row, seq_len: int, mode: str)
 
 def pth_paged_attention(query, key_cache, value_cache, k_scale_cache, v_scale_cache,
                         block_table, seq_lens, query_start_loc, softmax_scale: float,
-                        mode: str, seqs=None) -> np.ndarray:
+                        mode: str, seqs=None, window: int = 0) -> np.ndarray:
     """fp64 causal paged attention over an int8 / fp8 per-token-head cache, in
     the original domain: logit_j = (q . K_j) * softmax_scale with K_j, V_j the
     dequantized cache rows; same causal rule and GQA mapping as
@@ -507,7 +515,7 @@ def pth_paged_attention(query, key_cache, value_cache, k_scale_cache, v_scale_ca
         for g in range(nkv):
             qg = q[q0:q1, g * group:(g + 1) * group, :]
             logits = (qg @ K[:, g, :].T) * softmax_scale
-            out[q0:q1, g * group:(g + 1) * group] = _causal_softmax_attend(logits, V[:, g, :], L)
+            out[q0:q1, g * group:(g + 1) * group] = _causal_softmax_attend(logits, V[:, g, :], L, window)
     return out
 
 

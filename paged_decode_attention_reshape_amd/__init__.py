@@ -73,8 +73,8 @@ _SIGNATURES = {
                                                               _c_int32, _c_int32, _c_int32, _c_int32]),
     "kv4_attention_layout": (ctypes.c_int, [_c_int32, _vp, _c_int64, _vp, _vp, _vp, _vp, _LP, _c_int64, _vp,
                                             _c_int32, _vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32, _c_int32,
-                                            _c_int32, _c_int32, _c_int32, _c_int32, _c_uint64, ctypes.c_float,
-                                            _vp, _vp, ctypes.c_size_t, _vp]),
+                                            _c_int32, _c_int32, _c_int32, _c_int32, _c_uint64, _c_int32,
+                                            ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
     "kv4_dequant_layout": (ctypes.c_int, [_c_int32, _vp, _vp, _LP, _c_int64, _vp, _c_int64, _c_int32, _c_int32,
                                           _c_int32, _c_int32, _c_uint64, _c_int32, _vp, _vp]),
 }
@@ -501,9 +501,11 @@ def kv4_attention_layout(query: torch.Tensor, cache: LayoutCache, block_table: t
                          query_start_loc: torch.Tensor, max_query_len: int, max_seq_len: int,
                          sign_seed: int = DEFAULT_SIGN_SEED, softmax_scale: Optional[float] = None,
                          b: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                         workspace: Optional[torch.Tensor] = None, stream=None,
+                         sliding_window: int = 0) -> torch.Tensor:
     """Paged causal attention over a LayoutCache (see kv4_paged_attention /
-    kv4_pth_attention)."""
+    kv4_pth_attention); sliding_window > 0 keeps the window most recent keys
+    of each query's causal range."""
     _need(query, "query", torch.bfloat16, 3)
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
@@ -534,7 +536,8 @@ def kv4_attention_layout(query: torch.Tensor, cache: LayoutCache, block_table: t
         cache.v_scale_ptr, ctypes.byref(cache.layout), cache.num_blocks, block_table.data_ptr(),
         block_table.shape[1], seq_lens.data_ptr(), query_start_loc.data_ptr(), S, Tq, int(max_query_len),
         int(max_seq_len), nq, cache.num_kv_heads, hs, hs & -hs if b is None else b, cache.block_size,
-        sign_seed & (2 ** 64 - 1), float(softmax_scale), out.data_ptr(), ws_ptr, ws_bytes, _stream(stream))
+        sign_seed & (2 ** 64 - 1), int(sliding_window), float(softmax_scale), out.data_ptr(), ws_ptr, ws_bytes,
+        _stream(stream))
     _check("kv4_attention_layout", rc)
     return out
 
@@ -557,3 +560,19 @@ def kv4_dequant_layout(cache: LayoutCache, which: str, slot_mapping: torch.Tenso
                                   out.data_ptr(), _stream(stream))
     _check("kv4_dequant_layout", rc)
     return out
+
+
+def packed_layout_cache(mode, key_cache: torch.Tensor, value_cache: torch.Tensor, k_scale_cache: torch.Tensor,
+                        v_scale_cache: torch.Tensor) -> LayoutCache:
+    """A LayoutCache view of packed caches ([nb, bs, nkv, C] codes, [nb, bs,
+    nkv] scales), for the *_layout entry points."""
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache"), (k_scale_cache, "k_scale_cache"),
+                 (v_scale_cache, "v_scale_cache")):
+        _contig(t, n)
+    m = _any_mode(mode)
+    nb, bs, nkv, c = key_cache.shape
+    hs = 2 * c if m == 0 else c
+    lay = kv4_cache_layout_packed(m, nkv, hs, bs)
+    return LayoutCache(m, lay, nb, bs, nkv, hs, key_cache.data_ptr(), value_cache.data_ptr(),
+                       k_scale_cache.data_ptr(), v_scale_cache.data_ptr(),
+                       (key_cache, value_cache, k_scale_cache, v_scale_cache))

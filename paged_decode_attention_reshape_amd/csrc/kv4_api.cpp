@@ -378,13 +378,14 @@ int attention_impl(int qm, const void* query, int64_t query_token_stride, const 
                    int64_t num_q_tokens, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size, uint64_t sign_seed,
                    float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                   const kv4::CacheLayout* layout = nullptr) {
+                   const kv4::CacheLayout* layout = nullptr, int32_t window = 0) {
   if (int e = check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
                                max_seq_len))
     return e;
   if (block_size < 1 || block_size > 4096) return fail(KV4_EINVAL, "block_size must be in [1, 4096]");
   if (num_blocks < 0 || num_blocks > INT32_MAX) return fail(KV4_EINVAL, "num_blocks out of range");
   if (!std::isfinite(softmax_scale)) return fail(KV4_EINVAL, "softmax_scale must be finite");
+  if (window < 0) return fail(KV4_EINVAL, "sliding_window must be >= 0 (0 = none), got %d", window);
   if (num_q_tokens == 0) return ok();
   if (num_q_tokens * (int64_t)num_q_heads > INT32_MAX)
     return fail(KV4_EUNSUPPORTED, "num_q_tokens * num_q_heads must be below 2^31");
@@ -448,6 +449,7 @@ int attention_impl(int qm, const void* query, int64_t query_token_stride, const 
   a.scale_log2 = softmax_scale / (float)b * 1.4426950408889634f;
   a.out = static_cast<uint16_t*>(out);
   a.prefix = prefix;
+  a.window = window;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.plan.path == 1) {
     const int64_t max_units =
@@ -626,8 +628,9 @@ int kv4_attention_layout(int32_t kv_quant_mode, const void* query, int64_t query
                          const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                          const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
                          int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
-                         int32_t head_size, int32_t b, int32_t block_size, uint64_t sign_seed, float softmax_scale,
-                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                         int32_t head_size, int32_t b, int32_t block_size, uint64_t sign_seed,
+                         int32_t sliding_window, float softmax_scale, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   if (int e = check_any_mode(kv_quant_mode, head_size, b)) return e;
   if (!layout) return fail(KV4_EINVAL, "null layout");
   const kv4::CacheLayout l = to_layout(layout);
@@ -635,7 +638,7 @@ int kv4_attention_layout(int32_t kv_quant_mode, const void* query, int64_t query
                         v_scale_cache, num_blocks, block_table, max_blocks_per_seq, seq_lens, query_start_loc,
                         num_seqs, num_q_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_size,
                         kv_quant_mode ? 1 : b, block_size, kv_quant_mode ? 0 : sign_seed, softmax_scale, out,
-                        workspace, workspace_bytes, stream, &l);
+                        workspace, workspace_bytes, stream, &l, sliding_window);
 }
 
 int kv4_dequant_layout(int32_t kv_quant_mode, const void* cache, const float* scale_cache,

@@ -264,6 +264,12 @@ __device__ __forceinline__ bool decode_unit(const AttnArgs& a, const int32_t* pr
 
 // Work units per sequence and their exclusive prefix (one workgroup); in
 // stream-K decode, the 32-token KV steps per sequence instead.
+// First 32-token KV step of a single-token decode row (position L - 1) under
+// a sliding window: keys L - window .. L - 1 are visible.
+__device__ __forceinline__ int sk_first_step(int window, int64_t L) {
+  return (window > 0 && L > window) ? (int)((L - window) >> 5) : 0;
+}
+
 __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* prefix) {
   __shared__ int32_t wave_tot[16];
   __shared__ int32_t carry;
@@ -285,7 +291,8 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* pr
       nsp = nsp < 1 ? 1 : (nsp > a.plan.num_splits ? a.plan.num_splits : nsp);
       const int ntile = (int)((qe - qb + a.plan.tq - 1) / a.plan.tq);
       units = ntile * nsp * a.plan.n_head_tiles * (a.nkv / a.plan.hpw);
-      if (a.plan.sk) units = (qe > qb && L > 0) ? (int)((L + 31) / 32) : 0;   // KV steps of the sequence
+      if (a.plan.sk)   // KV steps of the sequence (from the 32-token step holding its window start)
+        units = (qe > qb && L > 0) ? (int)((L + 31) / 32) - sk_first_step(a.window, L) : 0;
     }
     // inclusive scan inside the wave
     int x = units;
@@ -572,6 +579,10 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
     const int nh = min(gh, G - hq0);
     const int ntok = min(a.plan.tq, uqlen - ui0);
     const int pos0 = uL - uqlen + ui0;
+    // sliding window: row r sees keys (rpos - win, rpos]; a step starting at
+    // or after wlo lies in the window of every row of the tile
+    const int win = a.window > 0 ? a.window : INT_MAX;
+    const int wlo = a.window > 0 ? pos0 + ntok - a.window : INT_MIN;
 
     // page ids of this unit, one per lane, 64 pages at a time (loaded first:
     // the q' setup below hides their latency)
@@ -877,7 +888,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
       const float ks8[8] = {ksa.x, ksa.y, ksa.z, ksa.w, ksb.x, ksb.y, ksb.z, ksb.w};
       const float vs8[8] = {vsa.x, vsa.y, vsa.z, vsa.w, vsb.x, vsb.y, vsb.z, vsb.w};
       float lg[8];
-      const bool full = base + 32 <= k1 && base + 31 <= pos0 && oka && okb;   // wave-uniform
+      const bool full = base + 32 <= k1 && base + 31 <= pos0 && base >= wlo && oka && okb;   // wave-uniform
       float dq[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) dq[i] = QM == 0 ? s8[i] - qbias : (s8[i] - qbias) * qrs_n;
@@ -888,7 +899,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int tok = base + (i < 4 ? 4 * q4 + i : 16 + 4 * q4 + (i - 4));
-          const bool ok = tok < k1 && tok <= rpos && (i < 4 ? oka : okb);
+          const bool ok = tok < k1 && tok <= rpos && tok > rpos - win && (i < 4 ? oka : okb);
           lg[i] = ok ? dq[i] * ks8[i] : -INFINITY;
         }
       }
@@ -1133,8 +1144,9 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
       const int64_t cap = (int64_t)a.max_blocks * a.bs;
       L = L < 0 ? 0 : (L > cap ? cap : L);
       const int uqb = uniform((int)qb), uql = uniform((int)(qe - qb)), uL = uniform((int)L);
-      const int k0 = (int)(32 * (loc - t0));
-      const int k1 = (int)min((int64_t)32 * (end - t0), (int64_t)uL);
+      const int fs = sk_first_step(a.window, uL);
+      const int k0 = (int)(32 * (loc - t0 + fs));
+      const int k1 = (int)min((int64_t)32 * (end - t0 + fs), (int64_t)uL);
       run_unit(s_, 0, uqb, uql, uL, q * WPB + wv, 0, k0, k1, w + (int64_t)q * nseq + s_, true);
       x = (int64_t)q * S + end;
     }
@@ -1158,8 +1170,10 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
     const int uht = uniform(un.ht), usp = uniform(un.sp);
     const int ntok = min(a.plan.tq, uqlen - ui0);
     const int kend = uL - uqlen + ui0 + ntok;
-    const int k0 = usp * split;
-    const int k1 = min(k0 + split, kend);
+    // keys below the tile's first sliding window start (32-aligned) are not read
+    const int kwin = a.window > 0 ? (max(0, uL - uqlen + ui0 - a.window + 1) & ~31) : 0;
+    const int k0 = max(usp * split, kwin);
+    const int k1 = min(usp * split + split, kend);
     if (k0 >= k1 && usp > 0) continue;   // no keys for this tile in this split (the merge skips it)
     run_unit(us, ui0, uqbeg, uqlen, uL, ug, uht, k0, k1, (int64_t)usp * a.num_q_tokens, a.plan.num_splits > 1);
   }

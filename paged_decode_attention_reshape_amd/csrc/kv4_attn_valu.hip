@@ -167,8 +167,10 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
   const int ntok = min(a.plan.tq, t.qlen - t.i0);
   const int pos0 = t.L - t.qlen + t.i0;               // position of the tile's first query
   const int kend = pos0 + ntok;                       // keys [0, kend) are visible to some row
-  const int k0 = sp * a.plan.split_tokens;
-  const int k1 = min(k0 + a.plan.split_tokens, kend);
+  // keys below the first query's sliding window are visible to no row
+  const int kwin = a.window > 0 ? max(0, pos0 - a.window + 1) : 0;
+  const int k0 = max(sp * a.plan.split_tokens, kwin);
+  const int k1 = min(sp * a.plan.split_tokens + a.plan.split_tokens, kend);
   if (k0 >= k1 && a.plan.num_splits > 1) return;      // nothing here; the merge skips this split
 
   const uint32_t sbits = (QM == 0 && lane_on) ? sign_bits8(a.seed, jj) : 0u;
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
       for (int e = 0; e < 8; ++e) d = fmaf(qv[r][e], u[e], d);
       d = lane_on ? d : 0.0f;
       logit[r] = group_sum(d, LPT) * ks;
-      if (!valid || tok > rpos[r]) logit[r] = -INFINITY;
+      if (!valid || tok > rpos[r] || (a.window > 0 && tok <= rpos[r] - a.window)) logit[r] = -INFINITY;
     }
     if constexpr (QM == 0) codes_to_u(vw, u);
     else bytes_to_f<QM>(vb, u);
@@ -404,6 +406,13 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
         if (pos >= 0) {
           const int64_t n = (pos + a.plan.split_tokens) / a.plan.split_tokens;   // ceil((pos+1)/split)
           nsp = (int)(n < a.plan.num_splits ? n : a.plan.num_splits);
+          // sliding window: the splits before the one holding the row's first
+          // visible key hold nothing for it (and may not have been written)
+          if (a.window > 0 && pos - a.window + 1 > 0) {
+            const int first = (int)((pos - a.window + 1) / a.plan.split_tokens);
+            nsp -= first;
+            pbase += (int64_t)first * pstride;
+          }
         }
       }
     }

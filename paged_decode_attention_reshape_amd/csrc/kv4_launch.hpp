@@ -142,6 +142,7 @@ struct AttnArgs {
   const int32_t* prefix;   // MFMA path: device plan output (stream-K: first KV step per sequence)
   int qm;                  // 0: int4 RHT cache; 1 / 2: int8 / fp8 per-token-head cache (no rotation)
   CacheLayout lay;         // shared by the K and V caches and their scales
+  int window;              // sliding window: the query at position p sees keys (p - window, p]; 0 = none
   AttnPlan plan;
 };
 

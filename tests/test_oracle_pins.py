@@ -492,3 +492,94 @@ def test_planted_mistakes_are_caught(monkeypatch):
             m.setattr(O, name, fake)
             assert not _pins_pass(), f"planted mistake in {name} not caught"
     assert _pins_pass()
+
+
+# ---------------------------------------------------------------------------
+# Sliding window (a reading of the pages' "added window" commit: the query at
+# position p sees keys j with p - W < j <= p)
+# ---------------------------------------------------------------------------
+
+def _window_case(seed=0):
+    rng = np.random.default_rng(seed)
+    nq, nkv, hs = 4, 2, 16
+    slens, qlens = [37, 9, 20], [1, 3, 5]
+    q = rng.standard_normal((sum(qlens), nq, hs))
+    k = rng.standard_normal((sum(slens), nkv, hs))
+    v = rng.standard_normal((sum(slens), nkv, hs))
+    qsl = np.concatenate([[0], np.cumsum(qlens)])
+    kv_start = np.concatenate([[0], np.cumsum(slens)])
+    return q, k, v, qsl, np.array(slens), kv_start
+
+
+def test_window_degenerate_cases_reduce_to_causal_and_to_self():
+    q, k, v, qsl, sl, ks = _window_case()
+    causal = O.attention_dense(q, k, v, qsl, sl, 0.25, ks)
+    # a window at least as long as every sequence changes nothing
+    assert np.array_equal(O.attention_dense(q, k, v, qsl, sl, 0.25, ks, window=int(sl.max())), causal)
+    assert np.array_equal(O.attention_dense(q, k, v, qsl, sl, 0.25, ks, window=0), causal)
+    # window 1: every query sees only its own key, so the output is its own value row
+    w1 = O.attention_dense(q, k, v, qsl, sl, 0.25, ks, window=1)
+    group = q.shape[1] // k.shape[1]
+    for s in range(len(sl)):
+        L, q0, q1 = int(sl[s]), int(qsl[s]), int(qsl[s + 1])
+        for i in range(q1 - q0):
+            pos = L - (q1 - q0) + i
+            for h in range(q.shape[1]):
+                assert np.allclose(w1[q0 + i, h], v[ks[s] + pos, h // group], atol=1e-12)
+
+
+@pytest.mark.parametrize("W", [2, 5, 8, 19])
+def test_window_equals_causal_attention_on_the_truncated_history(W):
+    """Each row's windowed result equals plain causal attention of that row
+    over only its last W keys (slicing instead of masking)."""
+    q, k, v, qsl, sl, ks = _window_case(seed=W)
+    got = O.attention_dense(q, k, v, qsl, sl, 0.25, ks, window=W)
+    for s in range(len(sl)):
+        L, q0, q1 = int(sl[s]), int(qsl[s]), int(qsl[s + 1])
+        for i in range(q1 - q0):
+            pos = L - (q1 - q0) + i
+            lo = max(0, pos - W + 1)
+            n = pos + 1 - lo                       # keys lo .. pos, the row is the last query
+            ref = O.attention_dense(q[q0 + i:q0 + i + 1], k[ks[s] + lo:ks[s] + pos + 1],
+                                    v[ks[s] + lo:ks[s] + pos + 1], np.array([0, 1]), np.array([n]), 0.25,
+                                    np.array([0, n]))
+            assert np.allclose(got[q0 + i], ref[0], atol=1e-12)
+
+
+def test_window_paged_forms_agree_with_dense():
+    """The paged oracles (int4 rotated domain and int8) pass the window to the
+    same mask: their windowed results match dense windowed attention on the
+    dequantized values."""
+    rng = np.random.default_rng(4)
+    nq, nkv, hs, bs = 4, 2, 32, 4
+    slens, qlens = [23, 10], [1, 4]
+    T = sum(slens)
+    key = rng.standard_normal((T, nkv, hs)).astype(np.float32)
+    value = rng.standard_normal((T, nkv, hs)).astype(np.float32)
+    q = rng.standard_normal((sum(qlens), nq, hs))
+    nb = 16
+    bt = np.full((2, 8), -1, dtype=np.int32)
+    perm = rng.permutation(nb)
+    slots, kv_start, used = [], [0], 0
+    for s, L in enumerate(slens):
+        n = -(-L // bs)
+        bt[s, :n] = perm[used:used + n]
+        used += n
+        slots += [int(bt[s, p // bs]) * bs + p % bs for p in range(L)]
+        kv_start.append(kv_start[-1] + L)
+    slots = np.array(slots, dtype=np.int64)
+    qsl = np.array([0, 1, 5])
+    sl = np.array(slens)
+    kc, vc, ks, vs = O.pth_write_kv(key, value, slots, nb, bs, "int8")
+    kd = O.pth_dequant(kc, ks, slots, "int8").astype(np.float64)
+    vd = O.pth_dequant(vc, vs, slots, "int8").astype(np.float64)
+    for W in (1, 3, 7):
+        got = O.pth_paged_attention(q, kc, vc, ks, vs, bt, sl, qsl, 0.2, "int8", window=W)
+        ref = O.attention_dense(q, kd, vd, qsl, sl, 0.2, np.array(kv_start), window=W)
+        assert np.allclose(got, ref, atol=1e-6)
+        kc4, vc4, ks4, vs4 = O.write_kv(key, value, slots, nb, bs, 42)
+        got4 = O.paged_attention(q, kc4, vc4, ks4, vs4, bt, sl, qsl, 0.2, 42, window=W)
+        kh = O.dequant(kc4, ks4, slots, 42, inverse_rotate=True).astype(np.float64)
+        vh = O.dequant(vc4, vs4, slots, 42, inverse_rotate=True).astype(np.float64)
+        ref4 = O.attention_dense(q, kh, vh, qsl, sl, 0.2, np.array(kv_start), window=W)
+        assert np.allclose(got4, ref4, atol=1e-4)
