@@ -133,8 +133,10 @@ int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_
   // Single-token decode on the matrix cores, with whole workgroups of kv head
   // groups: stream-K partition of the KV steps over the resident workgroups
   // (no split size; every workgroup gets the same number of steps).
+  // (also multi-token decode where every sequence's queries fit one tile)
   p.sk = 0;
-  if (mfma && max_query_len <= 1 && p.n_head_tiles == 1 && (nkv / p.hpw) % p.wpb == 0 &&
+  const int mql1 = max_query_len < 1 ? 1 : max_query_len;
+  if (mfma && mql1 <= p.tq && p.n_head_tiles == 1 && (nkv / p.hpw) % p.wpb == 0 &&
       env_long("KV4_STREAMK", 1) != 0) {
     p.sk = 1;
     p.sk_quads = nkv / p.hpw / p.wpb;
@@ -162,7 +164,7 @@ int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_
   long split = env_long("KV4_SPLIT_TOKENS", 0);
   if (split <= 0) {
     if (mfma) {
-      if (max_query_len > 1 && units >= 2048) {
+      if (max_query_len > 1 && units >= kTargetUnitsMfma) {
         split = msl;                        // prefill tiles already fill the machine
       } else {
         split = (long)((int64_t)msl * units * p.hpw / kTargetUnitsMfma);
@@ -200,8 +202,10 @@ WsLayout ws_layout(const kv4::AttnPlan& p, int64_t num_q_tokens, int32_t num_seq
   }
   if (p.sk || p.num_splits > 1) {
     // split-KV: one row per (split, query token, q head); stream-K: one per
-    // (range piece, q head), at most workgroups + quads * sequences pieces
-    const size_t rows = p.sk ? ((size_t)p.sk_pcap + (size_t)p.sk_quads * (size_t)num_seqs) * (size_t)nq
+    // (range piece, query token of the tile, q head), at most workgroups +
+    // quads * sequences pieces
+    const size_t rows = p.sk ? ((size_t)p.sk_pcap + (size_t)p.sk_quads * (size_t)num_seqs) * (size_t)p.tq *
+                                   (size_t)nq
                              : (size_t)p.num_splits * (size_t)num_q_tokens * (size_t)nq;
     w.o_off = off;
     w.ml_off = align_up(off + rows * (size_t)hs * sizeof(float), 256);

@@ -38,6 +38,8 @@
 //   * k_scale / v_scale of the 32 tokens are loaded once per step (one lane
 //     per token) and redistributed through a 256-byte LDS slot per head.
 // Pages are looked up once per 16-token half tile (block_size % 16 == 0).
+#include <type_traits>
+
 #include "kv4_device.hpp"
 #include "kv4_launch.hpp"
 
@@ -264,10 +266,12 @@ __device__ __forceinline__ bool decode_unit(const AttnArgs& a, const int32_t* pr
 
 // Work units per sequence and their exclusive prefix (one workgroup); in
 // stream-K decode, the 32-token KV steps per sequence instead.
-// First 32-token KV step of a single-token decode row (position L - 1) under
-// a sliding window: keys L - window .. L - 1 are visible.
-__device__ __forceinline__ int sk_first_step(int window, int64_t L) {
-  return (window > 0 && L > window) ? (int)((L - window) >> 5) : 0;
+// First 32-token KV step of a one-tile query block (qlen rows at positions
+// L - qlen .. L - 1) under a sliding window: its first row sees keys from
+// L - qlen - window + 1 on.
+__device__ __forceinline__ int sk_first_step(int window, int64_t L, int64_t qlen) {
+  const int64_t k = L - qlen - window + 1;
+  return (window > 0 && k > 0) ? (int)(k >> 5) : 0;
 }
 
 __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* prefix) {
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* pr
       const int ntile = (int)((qe - qb + a.plan.tq - 1) / a.plan.tq);
       units = ntile * nsp * a.plan.n_head_tiles * (a.nkv / a.plan.hpw);
       if (a.plan.sk)   // KV steps of the sequence (from the 32-token step holding its window start)
-        units = (qe > qb && L > 0) ? (int)((L + 31) / 32) - sk_first_step(a.window, L) : 0;
+        units = (qe > qb && L > 0) ? (int)((L + 31) / 32) - sk_first_step(a.window, L, qe - qb) : 0;
     }
     // inclusive scan inside the wave
     int x = units;
@@ -453,7 +457,10 @@ constexpr int mfma_wpe() {
 // PH (head size 128, several heads per wave): V staged per head instead of as
 // joint token rows of the wave's heads, for layouts whose heads of a token
 // row are not adjacent (about 1 % slower than joint rows where they are).
-template <int HS, int HPW, int QM, bool PH>
+//
+// WIN: built with the sliding-window terms (calls without a window run the
+// kernel without them).
+template <int HS, int HPW, int QM, bool PH, bool WIN>
 __global__ __launch_bounds__((64 * mfma_wpb<HS, HPW, QM>()))
 __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_kernel(AttnArgs a,
                                                                                   const int32_t* prefix) {
@@ -581,8 +588,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
     const int pos0 = uL - uqlen + ui0;
     // sliding window: row r sees keys (rpos - win, rpos]; a step starting at
     // or after wlo lies in the window of every row of the tile
-    const int win = a.window > 0 ? a.window : INT_MAX;
-    const int wlo = a.window > 0 ? pos0 + ntok - a.window : INT_MIN;
+    const int win = WIN ? a.window : INT_MAX;
+    const int wlo = WIN ? pos0 + ntok - a.window : INT_MIN;
 
     // page ids of this unit, one per lane, 64 pages at a time (loaded first:
     // the q' setup below hides their latency)
@@ -888,7 +895,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
       const float ks8[8] = {ksa.x, ksa.y, ksa.z, ksa.w, ksb.x, ksb.y, ksb.z, ksb.w};
       const float vs8[8] = {vsa.x, vsa.y, vsa.z, vsa.w, vsb.x, vsb.y, vsb.z, vsb.w};
       float lg[8];
-      const bool full = base + 32 <= k1 && base + 31 <= pos0 && base >= wlo && oka && okb;   // wave-uniform
+      const bool full = base + 32 <= k1 && base + 31 <= pos0 && (!WIN || base >= wlo) && oka && okb;   // wave-uniform
       float dq[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) dq[i] = QM == 0 ? s8[i] - qbias : (s8[i] - qbias) * qrs_n;
@@ -899,7 +906,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int tok = base + (i < 4 ? 4 * q4 + i : 16 + 4 * q4 + (i - 4));
-          const bool ok = tok < k1 && tok <= rpos && tok > rpos - win && (i < 4 ? oka : okb);
+          const bool ok = tok < k1 && tok <= rpos && (!WIN || tok > rpos - win) && (i < 4 ? oka : okb);
           lg[i] = ok ? dq[i] * ks8[i] : -INFINITY;
         }
       }
@@ -1030,7 +1037,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
     if (partial) {
       if (row_ok) {
         // split-KV: one row per (split, query token); stream-K: one per piece
-        const int64_t ptok = a.plan.sk ? ptok0 : ptok0 + qrow;
+        // (stream-K: one row per (piece, query token of the tile, q head))
+        const int64_t ptok = a.plan.sk ? ptok0 * a.plan.tq + ti_n : ptok0 + qrow;
         const int64_t prow = ptok * a.nq + h;
         float* dst = a.ws_o + prow * HS;
         int ns = 0;
@@ -1144,7 +1152,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
       const int64_t cap = (int64_t)a.max_blocks * a.bs;
       L = L < 0 ? 0 : (L > cap ? cap : L);
       const int uqb = uniform((int)qb), uql = uniform((int)(qe - qb)), uL = uniform((int)L);
-      const int fs = sk_first_step(a.window, uL);
+      const int fs = WIN ? sk_first_step(a.window, uL, uql) : 0;
       const int k0 = (int)(32 * (loc - t0 + fs));
       const int k1 = (int)min((int64_t)32 * (end - t0 + fs), (int64_t)uL);
       run_unit(s_, 0, uqb, uql, uL, q * WPB + wv, 0, k0, k1, w + (int64_t)q * nseq + s_, true);
@@ -1171,7 +1179,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
     const int ntok = min(a.plan.tq, uqlen - ui0);
     const int kend = uL - uqlen + ui0 + ntok;
     // keys below the tile's first sliding window start (32-aligned) are not read
-    const int kwin = a.window > 0 ? (max(0, uL - uqlen + ui0 - a.window + 1) & ~31) : 0;
+    const int kwin = WIN ? (max(0, uL - uqlen + ui0 - a.window + 1) & ~31) : 0;
     const int k0 = max(usp * split, kwin);
     const int k1 = min(usp * split + split, kend);
     if (k0 >= k1 && usp > 0) continue;   // no keys for this tile in this split (the merge skips it)
@@ -1181,13 +1189,13 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 
 static int g_num_cus = 0;
 
-template <int HS, int HPW, int QM, bool PH = false>
+template <int HS, int HPW, int QM, bool PH, bool WIN>
 static int resident_blocks() {
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb,
-                                                     reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH>),
+                                                     reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH, WIN>),
                                                      64 * mfma_wpb<HS, HPW, QM>(), 0) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
@@ -1195,8 +1203,8 @@ static int resident_blocks() {
   return per_cu * g_num_cus;
 }
 
-template <int HS, int QM>
-static hipError_t launch_hs(AttnArgs& a, const int32_t* prefix, int64_t max_units, hipStream_t stream) {
+template <int HS, int QM, bool WIN>
+static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_units, hipStream_t stream) {
   if (a.plan.hpw == 4 && Geo<HS>::NVR != 1) return hipErrorInvalidValue;
   if (QM != 0 && (a.plan.hpw != 1 || a.plan.wpb != mfma_wpb<HS, 1, QM>())) return hipErrorInvalidValue;
   auto go = [&](auto kernel, int wpb, int resident) {
@@ -1216,15 +1224,15 @@ static hipError_t launch_hs(AttnArgs& a, const int32_t* prefix, int64_t max_unit
     hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(64 * wpb), 0, stream, a, prefix);
   };
   if constexpr (QM != 0) {
-    go(attn_mfma_kernel<HS, 1, QM, false>, mfma_wpb<HS, 1, QM>(), resident_blocks<HS, 1, QM>());
+    go(attn_mfma_kernel<HS, 1, QM, false, WIN>, mfma_wpb<HS, 1, QM>(), resident_blocks<HS, 1, QM, false, WIN>());
     return hipSuccess;
   }
   if (a.plan.vjh) {
     if constexpr (HS == 128) {
       if (a.plan.hpw == 2) {
-        go(attn_mfma_kernel<HS, 2, 0, true>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0, true>());
+        go(attn_mfma_kernel<HS, 2, 0, true, WIN>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0, true, WIN>());
       } else if (a.plan.hpw == 4) {
-        go(attn_mfma_kernel<HS, 4, 0, true>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0, true>());
+        go(attn_mfma_kernel<HS, 4, 0, true, WIN>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0, true, WIN>());
       } else {
         return hipErrorInvalidValue;
       }
@@ -1233,15 +1241,21 @@ static hipError_t launch_hs(AttnArgs& a, const int32_t* prefix, int64_t max_unit
     return hipErrorInvalidValue;
   }
   switch (a.plan.hpw) {
-    case 2: go(attn_mfma_kernel<HS, 2, 0, false>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0>()); break;
+    case 2: go(attn_mfma_kernel<HS, 2, 0, false, WIN>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0, false, WIN>()); break;
     case 4:
       // four heads' V loads of a step must fit the 6-bit load counter
       if constexpr (Geo<HS>::NVR == 1)
-        go(attn_mfma_kernel<HS, 4, 0, false>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0>());
+        go(attn_mfma_kernel<HS, 4, 0, false, WIN>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0, false, WIN>());
       break;
-    default: go(attn_mfma_kernel<HS, 1, 0, false>, mfma_wpb<HS, 1, 0>(), resident_blocks<HS, 1, 0>()); break;
+    default: go(attn_mfma_kernel<HS, 1, 0, false, WIN>, mfma_wpb<HS, 1, 0>(), resident_blocks<HS, 1, 0, false, WIN>()); break;
   }
   return hipSuccess;
+}
+
+template <int HS, int QM>
+static hipError_t launch_hs(AttnArgs& a, const int32_t* prefix, int64_t max_units, hipStream_t stream) {
+  if (a.window > 0) return launch_hs_w<HS, QM, true>(a, prefix, max_units, stream);
+  return launch_hs_w<HS, QM, false>(a, prefix, max_units, stream);
 }
 
 hipError_t launch_attn_mfma(AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream) {

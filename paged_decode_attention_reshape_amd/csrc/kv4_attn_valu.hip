@@ -397,8 +397,8 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
           const int64_t w0 = floor_div_small((xs + 1) * P - 1, W);
           const int64_t w1 = floor_div_small(xe * P - 1, W);
           nsp = (int)(w1 - w0 + 1);
-          pbase = (w0 + (int64_t)quad * a.num_seqs + s) * a.nq + h;
-          pstride = a.nq;
+          pbase = ((w0 + (int64_t)quad * a.num_seqs + s) * a.plan.tq + (qtok - qb)) * a.nq + h;
+          pstride = (int64_t)a.plan.tq * a.nq;
 
         }
       } else if (qtok >= qb && qtok < qe) {

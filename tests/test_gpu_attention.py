@@ -286,3 +286,24 @@ def test_stream_and_out_buffer_reuse():
     s.synchronize()
     r.out = out
     _g2(r)
+
+
+MTD_CASES = [
+    # multi-token decode: every sequence's queries fit one MFMA tile (stream-K)
+    ("gqa4_q2to4_hs128", 32, 8, 128, [2, 4, 3, 1, 4], [1000, 17, 300, 2049, 64], 16),
+    ("gqa2_q8_hs64", 8, 4, 64, [8, 5, 8], [513, 9, 700], 32),
+    ("mha_q16_hs96", 4, 4, 96, [16, 3], [400, 16], 16),
+    ("gqa4_q4_hs192", 16, 4, 192, [4, 2], [333, 640], 16),
+]
+
+
+@pytest.mark.parametrize("sched", list(SCHED))
+@pytest.mark.parametrize("case", MTD_CASES, ids=[c[0] for c in MTD_CASES])
+def test_multi_token_decode(case, sched, monkeypatch):
+    """Speculative-decode-like batches (2-16 new tokens per sequence) under
+    each decode work schedule."""
+    for k, v in SCHED[sched].items():
+        monkeypatch.setenv(k, v)
+    name, nq, nkv, hs, ql, sl, bs = case
+    r = run_gpu(W.custom(name, nq, nkv, hs, ql, sl, block_size=bs))
+    _g2(r)

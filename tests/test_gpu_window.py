@@ -60,6 +60,7 @@ CASES = [
     ("mixed_prefill", 12, 2, 128, [1, 37, 1, 5, 1], [90, 300, 2000, 5, 64], 16),
     ("prefill_hs64_bs32", 8, 2, 64, [40, 3], [100, 77], 32),
     ("vector_path_bs8", 4, 2, 80, [1, 6], [333, 50], 8),
+    ("multi_token_decode", 32, 8, 128, [3, 1, 4, 2], [700, 40, 1500, 5], 16),
 ]
 
 

@@ -135,6 +135,19 @@ def llama8b_long(seed: int = 0, batch: int = 128) -> Workload:
         seq_lens=tuple(int(x) for x in lens), outlier_frac=0.01, data_seed=seed)
 
 
+def llama8b_spec(seed: int = 0, batch: int = 128, qmin: int = 2, qmax: int = 8) -> Workload:
+    """Multi-token decode at the long-context Llama-3-8B shape: each sequence
+    scores qmin..qmax new tokens at once (speculative-decode-like), ctx
+    log-U[4096, 32768], 1 % outlier channels x20."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = _loguniform_ints(rng, 4096, 32768, batch)
+    qlens = rng.integers(qmin, qmax, size=batch, endpoint=True)
+    return Workload(
+        name=f"llama8b_hs128_b{batch}_q{qmin}-{qmax}_logU4k-32k", num_q_heads=32, num_kv_heads=8,
+        head_size=128, block_size=BLOCK_SIZE, query_lens=tuple(int(x) for x in qlens),
+        seq_lens=tuple(int(x) for x in lens), outlier_frac=0.01, data_seed=seed)
+
+
 def llama8b_hs192(seed: int = 0, batch: int = 32, ctx: int = 16384) -> Workload:
     """Secondary sweep of the long-context shape: head_size 192 (b = 64)."""
     return Workload(
@@ -281,4 +294,6 @@ ALL = {
     "qwen_mixed": qwen_mixed,
     "llama8b_long": llama8b_long,
     "llama8b_hs192": llama8b_hs192,
+    "llama8b_spec": llama8b_spec,
+    "llama8b_spec4": lambda: llama8b_spec(qmin=4, qmax=4),
 }
