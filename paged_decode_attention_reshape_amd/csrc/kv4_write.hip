@@ -16,17 +16,72 @@
 // contiguous cache row. Butterflies with stride < 8 stay in registers; larger
 // strides exchange across lanes with DPP / ds_swizzle. Lanes past hs/8 carry
 // zeros and never store.
+#include <type_traits>
+
 #include "kv4_device.hpp"
 #include "kv4_launch.hpp"
 
 namespace kv4 {
 
-// Quantize one float32 value of a rotated head vector with the vector's scale:
-// rint_half_even(y / scale) clamped to [-8, 7] (IEEE float32 division).
-__device__ __forceinline__ int quant_code(float y, float scale) {
-  float q = __builtin_rintf(y / scale);
-  q = fminf(fmaxf(q, -8.0f), 7.0f);
-  return (int)q;
+typedef __bf16 bf16x2_rt __attribute__((ext_vector_type(2)));
+
+// rint_half_even(fl(y / scale)) for the IEEE float32 quotient the write rule
+// uses, for all 8 values of a lane. The quotients are first taken as y * rcp
+// (rcp = v_rcp_f32(scale), within 1 ulp; with the product's rounding |t -
+// y/scale| < 2^-22 |t|, below 2^-19 for |t| < 8 and 2^-15 for |t| < 128) and
+// the lane redoes all 8 with the correctly rounded division only if one t lies
+// within `tie` of a half-integer -- the only place where the two can round to
+// different integers (t - rint(t) is exact). `fast` is false for scales
+// outside the normal range.
+template <int QMAX>
+__device__ __forceinline__ void rint_quotients(const float (&y)[8], float scale, bool fast, float (&q)[8]) {
+  constexpr float tie = QMAX <= 8 ? 0.5f - 0x1p-16f : 0.5f - 0x1p-12f;
+  bool redo = !fast;
+  if (fast) {
+    const float rcp = __builtin_amdgcn_rcpf(scale);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = y[e] * rcp;
+      q[e] = __builtin_rintf(t);
+      redo |= fabsf(t - q[e]) >= tie;
+    }
+  }
+  if (redo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = __builtin_rintf(y[e] / scale);
+  }
+}
+
+// The radix-2 Walsh-Hadamard butterflies of the write path with the sign of
+// each cross-lane stage carried instead of applied: at the stage pairing
+// lane j with lane j ^ d, both lanes have taken the same upper / lower roles
+// in every earlier cross-lane stage, so they hold their values with the same
+// carried sign s; the lower lane computes own + partner (= s * (x_i +
+// x_{i+h})) and the upper lane own - partner (= -s * (x_i - x_{i+h}), the
+// exact negation of partner - own), one v_fmac with the partner as its DPP /
+// swizzle source. Returns the lane's final carried sign (+1 / -1): the true
+// values are sign * v, each element rounded exactly as in fwht_b_ct.
+template <int D>
+__device__ __forceinline__ void fwht8_xlane_lazy(float (&v)[8], float sgn) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = fmaf(xor_lane<D>(v[e]), sgn, v[e]);
+}
+template <int LPMAX>
+__device__ __forceinline__ float fwht_b_lazy(float (&v)[8], int b, int jj) {
+  fwht8_inlane(v);
+  float sg = 1.0f;
+  auto stage = [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    const float s = (jj & D) ? -1.0f : 1.0f;
+    fwht8_xlane_lazy<D>(v, s);
+    sg *= s;
+  };
+  if constexpr (LPMAX > 1) { if (b > 8) stage(std::integral_constant<int, 1>()); }
+  if constexpr (LPMAX > 2) { if (b > 16) stage(std::integral_constant<int, 2>()); }
+  if constexpr (LPMAX > 4) { if (b > 32) stage(std::integral_constant<int, 4>()); }
+  if constexpr (LPMAX > 8) { if (b > 64) stage(std::integral_constant<int, 8>()); }
+  if constexpr (LPMAX > 16) { if (b > 128) stage(std::integral_constant<int, 16>()); }
+  return sg;
 }
 
 // Per-token-head control modes (no rotation; the pages' int8_per_token_head
@@ -55,15 +110,10 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
   return code | sign;
 }
 
-template <int QM>
-__device__ __forceinline__ uint32_t quant_byte(float x, float scale) {
-  if constexpr (QM == 1) {
-    float q = __builtin_rintf(x / scale);
-    q = fminf(fmaxf(q, -128.0f), 127.0f);
-    return (uint32_t)(int)q & 0xFFu;
-  } else {
-    return f32_to_e4m3(x / scale);
-  }
+// int8 code byte of an already rounded quotient q.
+__device__ __forceinline__ uint32_t int8_byte(float q) {
+  q = fminf(fmaxf(q, -128.0f), 127.0f);
+  return (uint32_t)(int)q & 0xFFu;
 }
 
 // Page of a slot (block size a power of two: a shift).
@@ -87,18 +137,34 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
   const int64_t n_items = a.num_tokens * 2 * a.nkv;
   const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  // item = token * 2 nkv + kind * nkv + head, advanced by a fixed stride per
+  // iteration: (token, rem) are stepped, not divided, in the loop
+  const int per_tok = 2 * a.nkv;
+  const int64_t stride = n_waves * VPW;
+  const int64_t st_t = stride / per_tok;
+  const int st_r = (int)(stride - st_t * per_tok);
+  int64_t t;
+  int rem;
+  {
+    const int64_t item0 = wave_id * VPW + grp;
+    t = item0 / per_tok;
+    rem = (int)(item0 - t * per_tok);
+  }
 
-  for (int64_t base = wave_id * VPW; base < n_items; base += n_waves * VPW) {
-    const int64_t item = base + grp;
-    bool ok = item < n_items;
-    int64_t t = 0;
-    int kind = 0, h = 0;
+  for (int64_t base = wave_id * VPW; base < n_items; base += stride) {
+    if (base != wave_id * VPW) {
+      t += st_t;
+      rem += st_r;
+      if (rem >= per_tok) {
+        rem -= per_tok;
+        ++t;
+      }
+    }
+    bool ok = t < a.num_tokens;
+    const int kind = rem >= a.nkv ? 1 : 0;
+    const int h = rem - kind * a.nkv;
     int64_t slot = -1;
     if (ok) {
-      t = item / (2 * a.nkv);
-      const int rem = (int)(item - t * 2 * a.nkv);
-      kind = rem / a.nkv;
-      h = rem - kind * a.nkv;
       slot = a.slot_mapping[t];
       ok = slot >= 0 && slot < a.num_slots;
     }
@@ -115,20 +181,37 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
       v[2 * k] = bf16_lo(wd[k]);
       v[2 * k + 1] = bf16_hi(wd[k]);
     }
-    if constexpr (QM == 0) fwht_b(v, a.b, jj);
+    // rotation (carried sign sg: the rotated values are sg * v) and one
+    // round-to-nearest-even to bf16 (v_cvt_pk_bf16_f32); rounding, absmax
+    // and the int4 rule are symmetric in the sign, so sg is applied to the
+    // codes only
+    float sg = 1.0f;
+    if constexpr (QM == 0) {
+      sg = fwht_b_lazy<LP>(v, a.b, jj);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[2 * k], v[2 * k + 1]},
+                                                                                  bf16x2_rt));
+        v[2 * k] = bf16_lo(w2);
+        v[2 * k + 1] = bf16_hi(w2);
+      }
+    }
     float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (QM == 0) v[e] = round_bf16(v[e]);
-      amax = fmaxf(amax, fabsf(v[e]));
-    }
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
     amax = group_max(amax, LP);
     if constexpr (QM == 0) {
       const float scale = amax / 7.0f;
+      const bool fast = scale >= 0x1p-126f && scale <= 0x1p126f;
       uint32_t packed = 0;
       if (scale > 0.0f) {
+        float q[8];
+        rint_quotients<8>(v, scale, fast, q);
+        // |q| <= 7 (the largest |y| is amax = 7 scale up to rounding): the
+        // clamp to [-8, 7] never acts, and -q codes -y
 #pragma unroll
-        for (int e = 0; e < 8; ++e) packed |= ((uint32_t)quant_code(v[e], scale) & 0xFu) << (4 * e);
+        for (int e = 0; e < 8; ++e)
+          packed |= ((uint32_t)(int)fminf(fmaxf(q[e] * sg, -8.0f), 7.0f) & 0xFu) << (4 * e);
       }
       if (ok && lane_on) {
         uint8_t* cache = kind ? a.value_cache : a.key_cache;
@@ -138,12 +221,23 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
       }
     } else {
       const float scale = amax / (QM == 1 ? 127.0f : 448.0f);
+      const bool fast = scale >= 0x1p-126f && scale <= 0x1p126f;
       uint32_t lo = 0, hi = 0;
       if (scale > 0.0f) {
+        if constexpr (QM == 1) {
+          float q[8];
+          rint_quotients<128>(v, scale, fast, q);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo |= quant_byte<QM>(v[e], scale) << (8 * e);
-          hi |= quant_byte<QM>(v[e + 4], scale) << (8 * e);
+          for (int e = 0; e < 4; ++e) {
+            lo |= int8_byte(q[e]) << (8 * e);
+            hi |= int8_byte(q[e + 4]) << (8 * e);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo |= f32_to_e4m3(v[e] / scale) << (8 * e);
+            hi |= f32_to_e4m3(v[e + 4] / scale) << (8 * e);
+          }
         }
       }
       if (ok && lane_on) {
