@@ -378,16 +378,16 @@ constexpr int stages_for() { return 2; }
 // Per wave: kStages stage slots, each holding HPW per-head stages (one per kv
 // head the wave serves); the q' staging buffer and the epilogue buffer
 // overlay them.
-template <int HS, int HPW, int QM>
+template <int HS, int HPW, int QM, int NRB>
 struct MfmaSmem {
   static constexpr int STAGE_H = StageSel<HS, QM>::T::BYTES;   // one kv head
   static constexpr int STAGE = HPW * STAGE_H;               // one slot
-  static constexpr int BUFB = 16 * HS * 4;                 // q' staging / epilogue (fp32 rows)
+  static constexpr int BUFB = 16 * NRB * HS * 4;            // q' staging / epilogue (fp32 rows)
   static constexpr int NST = stages_for<HS>();
   static constexpr int MAINB = NST * STAGE > BUFB ? NST * STAGE : BUFB;
   alignas(16) unsigned char main[MAINB];
-  float qsum[16];
-  float qrs[16];   // int8 / fp8: power of two that undoes the row scaling of q'
+  float qsum[16 * NRB];
+  float qrs[16 * NRB];   // int8 / fp8: power of two that undoes the row scaling of q'
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -433,9 +433,9 @@ template <> struct MfmaShape<2> { static constexpr int WPE = 2; };
 template <> struct MfmaShape<4> { static constexpr int WPE = 1; };
 template <int HS, int HPW, int QM>
 constexpr int mfma_wpb() { return mfma_waves_per_block(HPW, QM, HS); }
-template <int HS, int HPW, int QM>
+template <int HS, int HPW, int QM, int NRB = 1>
 constexpr int mfma_wpe() {
-  return HPW == 1 && (HS >= 192 || (QM != 0 && HS >= 96)) ? 2 : MfmaShape<HPW>::WPE;
+  return HPW == 1 && (NRB > 1 || HS >= 192 || (QM != 0 && HS >= 96)) ? 2 : MfmaShape<HPW>::WPE;
 }
 
 // HPW = kv heads per wave. HPW = 1: the 16 MFMA rows are the query tile of one
@@ -460,13 +460,22 @@ constexpr int mfma_wpe() {
 //
 // WIN: built with the sliding-window terms (calls without a window run the
 // kernel without them).
-template <int HS, int HPW, int QM, bool PH, bool WIN>
+//
+// NRB (int4, one kv head per wave): 16-row MFMA blocks per wave. With NRB = 2
+// one wave serves 32 query rows (a prefill tile, or a multi-token decode
+// block of up to 32 / G tokens); the K and V codes of a step become
+// operands once and feed both blocks' products, and each block keeps its own
+// softmax state (the v_scale exponent e is shared: it depends on the keys
+// only).
+template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB>
 __global__ __launch_bounds__((64 * mfma_wpb<HS, HPW, QM>()))
-__attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_kernel(AttnArgs a,
-                                                                                  const int32_t* prefix) {
+__attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfma_kernel(AttnArgs a,
+                                                                                      const int32_t* prefix) {
+  static_assert(NRB == 1 || (HPW == 1 && QM == 0), "two row blocks: int4, one kv head per wave");
   using GG = Geo<HS>;
   using SG = typename StageSel<HS, QM>::T;
-  using SM = MfmaSmem<HS, HPW, QM>;
+  using SM = MfmaSmem<HS, HPW, QM, NRB>;
+  constexpr int ROWS = 16 * NRB;
   constexpr int WPB = mfma_wpb<HS, HPW, QM>();
   constexpr int NK = GG::NK, NS = GG::NS;
   constexpr int NVR = QM ? (HS + 63) / 64 : GG::NVR;   // V column regions
@@ -488,7 +497,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
   const int n_hg = nkv / HPW;       // kv head groups
   const int G = a.nq / nkv;
   const int gh = a.plan.gh;
-  const int rph = HPW == 1 ? 16 : a.plan.tq * gh;   // MFMA rows per kv head
+  const int rph = HPW == 1 ? ROWS : a.plan.tq * gh;   // MFMA rows per kv head
   const int split = a.plan.split_tokens;
   const int total = uniform(prefix[a.num_seqs]);
   const int bsz = a.bs;
@@ -612,7 +621,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 
     // ---- q' rows -> LDS (bf16 hi / lo, k-permuted) and their sums
 #pragma unroll
-    for (int ps = 0; ps < 16 / RPP; ++ps) {
+    for (int ps = 0; ps < ROWS / RPP; ++ps) {
       const int r = ps * RPP + lane / LP;
       const int hl = r / rph, rr = r - (r / rph) * rph;
       const int ti = rr / gh, hi = rr - (rr / gh) * gh;
@@ -664,32 +673,49 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
       sum = group_sum_ct<LP>(c_on ? sum : 0.0f);
       if (c_on) {
         reinterpret_cast<uint4*>(buf)[(r * HS + 8 * cj) / 8] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        reinterpret_cast<uint4*>(buf)[(16 * HS + r * HS + 8 * cj) / 8] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        reinterpret_cast<uint4*>(buf)[(ROWS * HS + r * HS + 8 * cj) / 8] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
       if (cj == 0) sm.qsum[r] = sum;
     }
     __builtin_amdgcn_wave_barrier();
-    uint4 qh[NK], ql[NK];
+    uint4 qh[NRB][NK], ql[NRB][NK];
+    float qbias[NRB], qrs_n[NRB], row_add[NRB];
+    bool row_ok[NRB];
+    int rpos[NRB], ti_b[NRB], hi_b[NRB];
 #pragma unroll
-    for (int s = 0; s < NK; ++s) {
-      qh[s] = reinterpret_cast<const uint4*>(buf)[(n * HS + q4 * (HS / 4) + 8 * s) / 8];
-      ql[s] = reinterpret_cast<const uint4*>(buf)[(16 * HS + n * HS + q4 * (HS / 4) + 8 * s) / 8];
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int rn = 16 * rb + n;                      // this lane's row in block rb
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        qh[rb][s] = reinterpret_cast<const uint4*>(buf)[(rn * HS + q4 * (HS / 4) + 8 * s) / 8];
+        ql[rb][s] = reinterpret_cast<const uint4*>(buf)[(ROWS * HS + rn * HS + q4 * (HS / 4) + 8 * s) / 8];
+      }
+      // sum of q' times the operand offset of the K codes (int4 136, int8 1152)
+      qbias[rb] = (QM == 0 ? 136.0f : (QM == 1 ? 1152.0f : 0.0f)) * sm.qsum[rn];
+      qrs_n[rb] = QM == 0 ? 1.0f : sm.qrs[rn];
+      const int hl = NRB == 1 ? hl_n : 0;
+      const int rr = NRB == 1 ? rr_n : rn;
+      ti_b[rb] = NRB == 1 ? ti_n : rr / gh;
+      hi_b[rb] = NRB == 1 ? hi_n : rr - (rr / gh) * gh;
+      row_ok[rb] = hl < HPW && ti_b[rb] < ntok && hi_b[rb] < nh;
+      rpos[rb] = row_ok[rb] ? pos0 + ti_b[rb] : -1;
+      row_add[rb] = row_ok[rb] ? 0.0f : -INFINITY;     // invalid rows never get weight
     }
-    // sum of q' times the operand offset of the K codes (int4 136, int8 1152)
-    const float qbias = (QM == 0 ? 136.0f : (QM == 1 ? 1152.0f : 0.0f)) * sm.qsum[n];
-    const float qrs_n = QM == 0 ? 1.0f : sm.qrs[n];
-    const bool row_ok = hl_n < HPW && ti_n < ntok && hi_n < nh;
-    const int rpos = row_ok ? pos0 + ti_n : -1;
-    const float row_add = row_ok ? 0.0f : -INFINITY;    // invalid rows never get weight
     // the staged q' has been read into registers before the stages overwrite it
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
 
-    f32x4_t acc[NS];
+    f32x4_t acc[NRB][NS];
+    f32x4_t pacc[NRB];
+    float m_run[NRB], l_run[NRB];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    f32x4_t pacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
+    for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) acc[rb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      pacc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m_run[rb] = -INFINITY;
+      l_run[rb] = 0.0f;
+    }
     float e_run = -100.0f;   // running v_scale exponent (see the softmax step)
 
     int okmask = 0;   // bit 2*slot: half A page valid, bit 2*slot+1: half B (wave-uniform)
@@ -823,7 +849,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 
       // S^T = K . Q'^T per kv head, both half tiles (q' as hi + lo); lane n
       // keeps the logits of its own row's head
-      float s8[8];
+      float s8[NRB][8];
       if constexpr (QM != 0) {
         // K codes of this lane: token n, bytes [HS/4 q4, +HS/4), both half tiles
         uint32_t kw[2][2 * NK];
@@ -842,14 +868,14 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
         for (int s = 0; s < NK; ++s) {
           const uint4 ka = k_operand_q<QM>(kw[0][2 * s], kw[0][2 * s + 1]);
           const uint4 kb = k_operand_q<QM>(kw[1][2 * s], kw[1][2 * s + 1]);
-          sa = mfma_f16(ka, qh[s], sa);
-          sb = mfma_f16(kb, qh[s], sb);
-          sa = mfma_f16(ka, ql[s], sa);
-          sb = mfma_f16(kb, ql[s], sb);
+          sa = mfma_f16(ka, qh[0][s], sa);
+          sb = mfma_f16(kb, qh[0][s], sb);
+          sa = mfma_f16(ka, ql[0][s], sa);
+          sb = mfma_f16(kb, ql[0][s], sb);
           __builtin_amdgcn_sched_barrier(0);
         }
-        s8[0] = sa[0]; s8[1] = sa[1]; s8[2] = sa[2]; s8[3] = sa[3];
-        s8[4] = sb[0]; s8[5] = sb[1]; s8[6] = sb[2]; s8[7] = sb[3];
+        s8[0][0] = sa[0]; s8[0][1] = sa[1]; s8[0][2] = sa[2]; s8[0][3] = sa[3];
+        s8[0][4] = sb[0]; s8[0][5] = sb[1]; s8[0][6] = sb[2]; s8[0][7] = sb[3];
       } else
 #pragma unroll
       for (int hl = 0; hl < HPW; ++hl) {
@@ -872,19 +898,30 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
             for (int j = 0; j < NK; ++j) kw[h][j] = reinterpret_cast<const uint32_t*>(kr + j * 256)[lane];
           }
         }
-        f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t sa[NRB], sb[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          sa[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          sb[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int s = 0; s < NK; ++s) {
           const uint4 ka = k_operand(kw[0][s]), kb = k_operand(kw[1][s]);
-          sa = mfma_bf16(ka, qh[s], sa);
-          sb = mfma_bf16(kb, qh[s], sb);
-          sa = mfma_bf16(ka, ql[s], sa);
-          sb = mfma_bf16(kb, ql[s], sb);
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+            sa[rb] = mfma_bf16(ka, qh[rb][s], sa[rb]);
+            sb[rb] = mfma_bf16(kb, qh[rb][s], sb[rb]);
+            sa[rb] = mfma_bf16(ka, ql[rb][s], sa[rb]);
+            sb[rb] = mfma_bf16(kb, ql[rb][s], sb[rb]);
+          }
           if constexpr (HPW == 1) __builtin_amdgcn_sched_barrier(0);   // one k-step's operands live at a time
         }
         if (hl == 0 || hl == hl_n) {
-          s8[0] = sa[0]; s8[1] = sa[1]; s8[2] = sa[2]; s8[3] = sa[3];
-          s8[4] = sb[0]; s8[5] = sb[1]; s8[6] = sb[2]; s8[7] = sb[3];
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+            s8[rb][0] = sa[rb][0]; s8[rb][1] = sa[rb][1]; s8[rb][2] = sa[rb][2]; s8[rb][3] = sa[rb][3];
+            s8[rb][4] = sb[rb][0]; s8[rb][5] = sb[rb][1]; s8[rb][6] = sb[rb][2]; s8[rb][7] = sb[rb][3];
+          }
         }
       }
       const float* scl = reinterpret_cast<const float*>(st + hoff_n + SG::S_OFF);
@@ -894,25 +931,30 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
       const float4 vsb = *reinterpret_cast<const float4*>(&scl[48 + 4 * q4]);
       const float ks8[8] = {ksa.x, ksa.y, ksa.z, ksa.w, ksb.x, ksb.y, ksb.z, ksb.w};
       const float vs8[8] = {vsa.x, vsa.y, vsa.z, vsa.w, vsb.x, vsb.y, vsb.z, vsb.w};
-      float lg[8];
+      float lg[NRB][8];
       const bool full = base + 32 <= k1 && base + 31 <= pos0 && (!WIN || base >= wlo) && oka && okb;   // wave-uniform
-      float dq[8];
+      float mx[NRB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dq[i] = QM == 0 ? s8[i] - qbias : (s8[i] - qbias) * qrs_n;
-      if (full) {
+      for (int rb = 0; rb < NRB; ++rb) {
+        float dq[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lg[i] = fmaf(dq[i], ks8[i], row_add);
-      } else {
+        for (int i = 0; i < 8; ++i) dq[i] = QM == 0 ? s8[rb][i] - qbias[rb] : (s8[rb][i] - qbias[rb]) * qrs_n[rb];
+        if (full) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int tok = base + (i < 4 ? 4 * q4 + i : 16 + 4 * q4 + (i - 4));
-          const bool ok = tok < k1 && tok <= rpos && (!WIN || tok > rpos - win) && (i < 4 ? oka : okb);
-          lg[i] = ok ? dq[i] * ks8[i] : -INFINITY;
+          for (int i = 0; i < 8; ++i) lg[rb][i] = fmaf(dq[i], ks8[i], row_add[rb]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int tok = base + (i < 4 ? 4 * q4 + i : 16 + 4 * q4 + (i - 4));
+            const bool ok =
+                tok < k1 && tok <= rpos[rb] && (!WIN || tok > rpos[rb] - win) && (i < 4 ? oka : okb);
+            lg[rb][i] = ok ? dq[i] * ks8[i] : -INFINITY;
+          }
         }
+        mx[rb] = fmaxf(fmaxf(fmaxf(lg[rb][0], lg[rb][1]), fmaxf(lg[rb][2], lg[rb][3])),
+                       fmaxf(fmaxf(lg[rb][4], lg[rb][5]), fmaxf(lg[rb][6], lg[rb][7])));
+        mx[rb] = max_x16_x32(mx[rb]);
       }
-      float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),
-                       fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
-      mx = max_x16_x32(mx);
       // p * v_scale enters the matrix cores as one fp16. A power of two 2^-e,
       // e = (exponent of the step's largest v_scale) - 11 kept as a running
       // maximum, holds it below 2^12 and clear of fp16 subnormals; acc, pacc
@@ -922,26 +964,30 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
       vmx = max_x16_x32(vmx);
       const float e_step = fmaxf((float)((int)((__float_as_uint(vmx) >> 23) & 0xFFu) - 138), -100.0f);
       const float e_new = fmaxf(e_run, e_step);
-      const float m_new = fmaxf(m_run, mx);
-      const float big_m = (m_new == -INFINITY ? 0.0f : m_new) + e_new;
-      // a row that has seen no key yet has nothing to rescale
-      const float alpha = m_run == -INFINITY ? 1.0f : fast_exp2(m_run + e_run - big_m);
-      float psum_l = 0.0f;
-      uint32_t pw[4];
+      uint4 ph4[NRB];
 #pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const float p0 = fast_exp2(lg[i] - big_m), p1 = fast_exp2(lg[i + 1] - big_m);
-        psum_l += p0 + p1;
-        pw[i / 2] = pack_f16x2(p0 * vs8[i], p1 * vs8[i + 1]);
-      }
-      const uint4 ph4 = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+      for (int rb = 0; rb < NRB; ++rb) {
+        const float m_new = fmaxf(m_run[rb], mx[rb]);
+        const float big_m = (m_new == -INFINITY ? 0.0f : m_new) + e_new;
+        // a row that has seen no key yet has nothing to rescale
+        const float alpha = m_run[rb] == -INFINITY ? 1.0f : fast_exp2(m_run[rb] + e_run - big_m);
+        float psum_l = 0.0f;
+        uint32_t pw[4];
 #pragma unroll
-        for (int i = 0; i < NS; ++i) acc[i] *= alpha;
-        pacc *= alpha;
+        for (int i = 0; i < 8; i += 2) {
+          const float p0 = fast_exp2(lg[rb][i] - big_m), p1 = fast_exp2(lg[rb][i + 1] - big_m);
+          psum_l += p0 + p1;
+          pw[i / 2] = pack_f16x2(p0 * vs8[i], p1 * vs8[i + 1]);
+        }
+        ph4[rb] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+          for (int i = 0; i < NS; ++i) acc[rb][i] *= alpha;
+          pacc[rb] *= alpha;
+        }
+        l_run[rb] = l_run[rb] * alpha + psum_l;
+        m_run[rb] = m_new;
       }
-      l_run = l_run * alpha + psum_l;
-      m_run = m_new;
       e_run = e_new;
 
       wait_vm<NLK>();                         // V(it) landed; K(it + 1) may be in flight
@@ -967,18 +1013,20 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
           for (int jb = 0; jb < (r < R4 ? 4 : 2); jb += 2) {
             uint4 c0, c1;
             v_operands_q<QM>(x, jb, c0, c1);
-            acc[4 * r + jb] = mfma_f16(c0, ph4, acc[4 * r + jb]);
-            acc[4 * r + jb + 1] = mfma_f16(c1, ph4, acc[4 * r + jb + 1]);
+            acc[0][4 * r + jb] = mfma_f16(c0, ph4[0], acc[0][4 * r + jb]);
+            acc[0][4 * r + jb + 1] = mfma_f16(c1, ph4[0], acc[0][4 * r + jb + 1]);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
       } else
 #pragma unroll
       for (int hl = 0; hl < HPW; ++hl) {
-        uint4 phh = ph4;
+        uint4 phh[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) phh[rb] = ph4[rb];
         if constexpr (HPW > 1) {
           const bool mine = hl == hl_n;
-          phh = make_uint4(mine ? ph4.x : 0u, mine ? ph4.y : 0u, mine ? ph4.z : 0u, mine ? ph4.w : 0u);
+          phh[0] = make_uint4(mine ? ph4[0].x : 0u, mine ? ph4[0].y : 0u, mine ? ph4[0].z : 0u, mine ? ph4[0].w : 0u);
         }
         int ns = 0;
 #pragma unroll
@@ -1011,8 +1059,11 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
             // low nibbles (column 2 jb) moved up to bits 4-7; high nibbles in place
             const uint4 lo = make_uint4(nib2h(t01 << 4), nib2h(t23 << 4), nib2h(t45 << 4), nib2h(t67 << 4));
             const uint4 hi = make_uint4(nib2h(t01), nib2h(t23), nib2h(t45), nib2h(t67));
-            acc[ns] = mfma_f16(lo, phh, acc[ns]);
-            acc[ns + 1] = mfma_f16(hi, phh, acc[ns + 1]);
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+              acc[rb][ns] = mfma_f16(lo, phh[rb], acc[rb][ns]);
+              acc[rb][ns + 1] = mfma_f16(hi, phh[rb], acc[rb][ns + 1]);
+            }
             ns += 2;
             if constexpr (HPW == 1) __builtin_amdgcn_sched_barrier(0);
           }
@@ -1020,7 +1071,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
       }
       if constexpr (QM != 2) {   // fp8 codes carry no offset
         const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);   // fp16 1.0
-        pacc = mfma_f16(ones, ph4, pacc);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) pacc[rb] = mfma_f16(ones, ph4[rb], pacc[rb]);
       }
     };
     for (int it = 0; it < nsteps; ++it)
@@ -1030,15 +1082,21 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 
     // ---- finish: l over the four lane quarters, remove the offset of the
     // fp16 V operands (int4: 64 + u = 72 + code; int8: 1152 + code)
-    l_run = sum_x16_x32(l_run);
-    const float pbias = (QM == 0 ? 72.0f : (QM == 1 ? 1152.0f : 0.0f)) * pacc[0];
-    const int qrow = uqbeg + ui0 + ti_n;
-    const int h = (kv0 + hl_n) * G + hq0 + hi_n;
+    float pbias[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      l_run[rb] = sum_x16_x32(l_run[rb]);
+      pbias[rb] = (QM == 0 ? 72.0f : (QM == 1 ? 1152.0f : 0.0f)) * pacc[rb][0];
+    }
     if (partial) {
-      if (row_ok) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+      const int qrow = uqbeg + ui0 + ti_b[rb];
+      const int h = (kv0 + (NRB == 1 ? hl_n : 0)) * G + hq0 + hi_b[rb];
+      if (row_ok[rb]) {
         // split-KV: one row per (split, query token); stream-K: one per piece
         // (stream-K: one row per (piece, query token of the tile, q head))
-        const int64_t ptok = a.plan.sk ? ptok0 * a.plan.tq + ti_n : ptok0 + qrow;
+        const int64_t ptok = a.plan.sk ? ptok0 * a.plan.tq + ti_b[rb] : ptok0 + qrow;
         const int64_t prow = ptok * a.nq + h;
         float* dst = a.ws_o + prow * HS;
         int ns = 0;
@@ -1049,31 +1107,35 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             float* d = dst + cb + w * (4 * q4 + rr);
+            const f32x4_t* A = acc[rb];
+            const float pb = pbias[rb];
             if (w == 8) {
-              reinterpret_cast<float4*>(d)[0] = make_float4(acc[ns][rr] - pbias, acc[ns + 1][rr] - pbias,
-                                                            acc[ns + 2][rr] - pbias, acc[ns + 3][rr] - pbias);
-              reinterpret_cast<float4*>(d)[1] = make_float4(acc[ns + 4][rr] - pbias, acc[ns + 5][rr] - pbias,
-                                                            acc[ns + 6][rr] - pbias, acc[ns + 7][rr] - pbias);
+              reinterpret_cast<float4*>(d)[0] = make_float4(A[ns][rr] - pb, A[ns + 1][rr] - pb,
+                                                            A[ns + 2][rr] - pb, A[ns + 3][rr] - pb);
+              reinterpret_cast<float4*>(d)[1] = make_float4(A[ns + 4][rr] - pb, A[ns + 5][rr] - pb,
+                                                            A[ns + 6][rr] - pb, A[ns + 7][rr] - pb);
             } else if (w == 4) {
-              reinterpret_cast<float4*>(d)[0] = make_float4(acc[ns][rr] - pbias, acc[ns + 1][rr] - pbias,
-                                                            acc[ns + 2][rr] - pbias, acc[ns + 3][rr] - pbias);
+              reinterpret_cast<float4*>(d)[0] = make_float4(A[ns][rr] - pb, A[ns + 1][rr] - pb,
+                                                            A[ns + 2][rr] - pb, A[ns + 3][rr] - pb);
             } else {
-              reinterpret_cast<float2*>(d)[0] = make_float2(acc[ns][rr] - pbias, acc[ns + 1][rr] - pbias);
+              reinterpret_cast<float2*>(d)[0] = make_float2(A[ns][rr] - pb, A[ns + 1][rr] - pb);
             }
           }
           ns += w;
         }
         if (q4 == 0) {
-          a.ws_ml[2 * prow] = m_run + e_run;   // the scale exponent of this partial
-          a.ws_ml[2 * prow + 1] = l_run;
+          a.ws_ml[2 * prow] = m_run[rb] + e_run;   // the scale exponent of this partial
+          a.ws_ml[2 * prow + 1] = l_run[rb];
         }
+      }
       }
       return;
     }
-    // single split: normalize, stage the row in LDS, inverse rotation, store
-    const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    // single split: normalize, stage the rows in LDS, inverse rotation, store
     __builtin_amdgcn_wave_barrier();
-    {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float inv_l = l_run[rb] > 0.0f ? 1.0f / l_run[rb] : 0.0f;
       int ns = 0;
 #pragma unroll
       for (int r = 0; r < NVR; ++r) {
@@ -1084,14 +1146,14 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
           const int c0 = cb + w * (4 * q4 + rr);
 #pragma unroll
           for (int t = 0; t < 8; ++t)
-            if (t < w) buf[n * HS + c0 + t] = (acc[ns + t][rr] - pbias) * inv_l;
+            if (t < w) buf[(16 * rb + n) * HS + c0 + t] = (acc[rb][ns + t][rr] - pbias[rb]) * inv_l;
         }
         ns += w;
       }
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int ps = 0; ps < 16 / RPP; ++ps) {
+    for (int ps = 0; ps < ROWS / RPP; ++ps) {
       const int r = ps * RPP + lane / LP;
       const int hl = r / rph, rr = r - (r / rph) * rph;
       const int ti = rr / gh, hi = rr - (rr / gh) * gh;
@@ -1189,13 +1251,13 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM>()))) void attn_mfma_ker
 
 static int g_num_cus = 0;
 
-template <int HS, int HPW, int QM, bool PH, bool WIN>
+template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB = 1>
 static int resident_blocks() {
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb,
-                                                     reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH, WIN>),
+                                                     reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH, WIN, NRB>),
                                                      64 * mfma_wpb<HS, HPW, QM>(), 0) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
@@ -1224,15 +1286,15 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
     hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(64 * wpb), 0, stream, a, prefix);
   };
   if constexpr (QM != 0) {
-    go(attn_mfma_kernel<HS, 1, QM, false, WIN>, mfma_wpb<HS, 1, QM>(), resident_blocks<HS, 1, QM, false, WIN>());
+    go(attn_mfma_kernel<HS, 1, QM, false, WIN, 1>, mfma_wpb<HS, 1, QM>(), resident_blocks<HS, 1, QM, false, WIN>());
     return hipSuccess;
   }
   if (a.plan.vjh) {
     if constexpr (HS == 128) {
       if (a.plan.hpw == 2) {
-        go(attn_mfma_kernel<HS, 2, 0, true, WIN>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0, true, WIN>());
+        go(attn_mfma_kernel<HS, 2, 0, true, WIN, 1>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0, true, WIN>());
       } else if (a.plan.hpw == 4) {
-        go(attn_mfma_kernel<HS, 4, 0, true, WIN>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0, true, WIN>());
+        go(attn_mfma_kernel<HS, 4, 0, true, WIN, 1>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0, true, WIN>());
       } else {
         return hipErrorInvalidValue;
       }
@@ -1240,14 +1302,21 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
     }
     return hipErrorInvalidValue;
   }
+  if (a.plan.rb == 2) {
+    if constexpr (HS <= 128) {
+      go(attn_mfma_kernel<HS, 1, 0, false, WIN, 2>, mfma_wpb<HS, 1, 0>(), resident_blocks<HS, 1, 0, false, WIN, 2>());
+      return hipSuccess;
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.plan.hpw) {
-    case 2: go(attn_mfma_kernel<HS, 2, 0, false, WIN>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0, false, WIN>()); break;
+    case 2: go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0, false, WIN>()); break;
     case 4:
       // four heads' V loads of a step must fit the 6-bit load counter
       if constexpr (Geo<HS>::NVR == 1)
-        go(attn_mfma_kernel<HS, 4, 0, false, WIN>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0, false, WIN>());
+        go(attn_mfma_kernel<HS, 4, 0, false, WIN, 1>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0, false, WIN>());
       break;
-    default: go(attn_mfma_kernel<HS, 1, 0, false, WIN>, mfma_wpb<HS, 1, 0>(), resident_blocks<HS, 1, 0, false, WIN>()); break;
+    default: go(attn_mfma_kernel<HS, 1, 0, false, WIN, 1>, mfma_wpb<HS, 1, 0>(), resident_blocks<HS, 1, 0, false, WIN>()); break;
   }
   return hipSuccess;
 }

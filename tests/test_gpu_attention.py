@@ -307,3 +307,38 @@ def test_multi_token_decode(case, sched, monkeypatch):
     name, nq, nkv, hs, ql, sl, bs = case
     r = run_gpu(W.custom(name, nq, nkv, hs, ql, sl, block_size=bs))
     _g2(r)
+
+
+RB_CASES = [
+    # tiles of more than 16 dense rows: two 16-row MFMA blocks per wave
+    ("g6_prefill_hs128", 12, 2, 128, [37, 1, 5, 70], [300, 2000, 5, 70], 16),
+    ("g3_prefill_hs64", 6, 2, 64, [20, 1, 33], [20, 60, 100], 16),
+    ("g1_prefill_hs96", 4, 4, 96, [40, 7], [100, 7], 16),
+    ("g24_decode_hs64", 48, 2, 64, [1] * 3, [300, 17, 1000], 16),
+    ("g32_decode_q2_hs128", 32, 1, 128, [1, 2], [500, 64], 16),
+    ("g4_mtd_q8_hs128", 32, 8, 128, [8, 3, 1, 6], [700, 40, 129, 2049], 16),
+    ("g8_mtd_q4_hs64_bs32", 32, 4, 64, [4, 2, 4], [513, 9, 70], 32),
+]
+
+RB_SCHED = {
+    "rb2": {},
+    "rb2_grid3": {"KV4_SK_GRID": "3"},
+    "rb2_splits64": {"KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64"},
+    "rb1": {"KV4_MFMA_RB": "1"},
+}
+
+
+@pytest.mark.parametrize("sched", list(RB_SCHED))
+@pytest.mark.parametrize("case", RB_CASES, ids=[c[0] for c in RB_CASES])
+def test_row_blocks_per_wave(case, sched, monkeypatch):
+    """Prefill, multi-token decode and groups above 16 on the matrix cores
+    with one and two 16-row blocks per wave, under split-KV and stream-K
+    schedules (ragged tiles: rows of the 32 left unused by a group that does
+    not divide it)."""
+    monkeypatch.setenv("KV4_FORCE_PATH", "mfma")
+    for k, v in RB_SCHED[sched].items():
+        monkeypatch.setenv(k, v)
+    name, nq, nkv, hs, ql, sl, bs = case
+    r = run_gpu(W.custom(name, nq, nkv, hs, ql, sl, block_size=bs))
+    _g1(r)
+    _g2(r)
