@@ -333,11 +333,101 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
   }
 }
 
+// Sequence of query token qtok and its step prefix (wave-uniform qtok).
+struct RowSeq {
+  int s;
+  int64_t qb, qe, L, pf0, pf1, pftot;
+};
+
+__device__ __forceinline__ RowSeq row_sequence(const AttnArgs& a, int64_t qtok) {
+  RowSeq q;
+  // In single-token decode token t is nearly always sequence t: its
+  // metadata is loaded with the check (one round trip), and the search runs
+  // only if the guess is wrong.
+  q.s = (int)(qtok < a.num_seqs ? qtok : a.num_seqs - 1);
+  q.qb = a.qsl[q.s];
+  q.qe = a.qsl[q.s + 1];
+  q.L = a.seq_lens[q.s];
+  q.pf0 = q.pf1 = q.pftot = 0;
+  if (a.plan.sk) {
+    q.pf0 = a.prefix[q.s];
+    q.pf1 = a.prefix[q.s + 1];
+    q.pftot = a.prefix[a.num_seqs];
+  }
+  if (!(q.qb <= qtok && qtok < q.qe)) {
+    q.s = wave_search_le(a.qsl, a.num_seqs, qtok);
+    q.qb = a.qsl[q.s];
+    q.qe = a.qsl[q.s + 1];
+    q.L = a.seq_lens[q.s];
+    if (a.plan.sk) {
+      q.pf0 = a.prefix[q.s];
+      q.pf1 = a.prefix[q.s + 1];
+    }
+  }
+  const int64_t cap = (int64_t)a.max_blocks * a.bs;
+  q.L = q.L < 0 ? 0 : (q.L > cap ? cap : q.L);
+  return q;
+}
+
+// The partials of output row `row` (query token qtok, query head h): nsp of
+// them, partial k at workspace row k * pstride + pbase.
+__device__ __forceinline__ void row_pieces(const AttnArgs& a, const RowSeq& q, int64_t qtok, int h, int64_t row,
+                                           int& nsp, int64_t& pbase, int64_t& pstride) {
+  nsp = 0;
+  pbase = row;
+  pstride = a.num_q_tokens * a.nq;
+  if (a.plan.sk) {
+    // stream-K: the workgroups whose step ranges cover this row's
+    // (quad, sequence) steps [xs, xe) each left one piece, numbered
+    // w + quad * num_seqs + s; workgroup w covers [w W / P, (w+1) W / P)
+    const int quad = h / (a.nq / a.nkv) / a.plan.hpw / a.plan.wpb;
+    const int64_t S = q.pftot;
+    const int64_t W = (int64_t)a.plan.sk_quads * S;
+    const int64_t P = (int64_t)a.plan.sk_grid < W ? (int64_t)a.plan.sk_grid : W;   // ranges, none empty
+    const int64_t xs = (int64_t)quad * S + q.pf0, xe = (int64_t)quad * S + q.pf1;
+    if (qtok >= q.qb && qtok < q.qe && xe > xs && W > 0) {
+      // the range holding step x: the largest w with floor(w W / P) <= x
+      const int64_t w0 = floor_div_small((xs + 1) * P - 1, W);
+      const int64_t w1 = floor_div_small(xe * P - 1, W);
+      nsp = (int)(w1 - w0 + 1);
+      pbase = ((w0 + (int64_t)quad * a.num_seqs + q.s) * a.plan.tq + (qtok - q.qb)) * a.nq + h;
+      pstride = (int64_t)a.plan.tq * a.nq;
+    }
+  } else if (qtok >= q.qb && qtok < q.qe) {
+    const int64_t pos = q.L - (q.qe - q.qb) + (qtok - q.qb);
+    if (pos >= 0) {
+      const int64_t n = (pos + a.plan.split_tokens) / a.plan.split_tokens;   // ceil((pos+1)/split)
+      nsp = (int)(n < a.plan.num_splits ? n : a.plan.num_splits);
+      // sliding window: the splits before the one holding the row's first
+      // visible key hold nothing for it (and may not have been written)
+      if (a.window > 0 && pos - a.window + 1 > 0) {
+        const int first = (int)((pos - a.window + 1) / a.plan.split_tokens);
+        nsp -= first;
+        pbase += (int64_t)first * pstride;
+      }
+    }
+  }
+}
+
+// fold one partial (m2, l2, y) into the running (M, Ls, o)
+__device__ __forceinline__ void lse_fold(float& M, float& Ls, float (&o)[8], float m2, float l2,
+                                         const float (&y)[8]) {
+  const float Mn = fmaxf(M, m2);
+  if (Mn == -INFINITY) return;                   // both empty
+  const float so = fast_exp2(M - Mn);            // 0 while M is -inf
+  const float sn = fast_exp2(m2 - Mn);
+  Ls = Ls * so + l2 * sn;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = o[e] * so + y[e] * sn;
+  M = Mn;
+}
+
 // Merge of the split partials (log-sum-exp in base 2) and the output
 // epilogue D.H(.)/b. One wave per output row (query token, query head): the
 // wave holds NG = 64 / LP copies of the row (LP = next_pow2(hs/8) lanes of 8
 // elements each); copy g folds splits g, g + NG, ... with four loads in flight,
-// then a butterfly over the copies combines them.
+// then a butterfly over the copies combines them. For calls with few rows
+// (more waves share the latency-bound work).
 template <int LP>
 __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   constexpr int NG = kWave / LP;
@@ -352,83 +442,14 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
   for (int64_t row = wave0; row < n_rows; row += n_waves) {
-    // partial k of this row sits at workspace row k * pstride + pbase
-    int nsp = 0;
-    int64_t pbase = row, pstride = n_rows;
-    {
-      // rows number fewer than 2^31 (checked on the host): 32-bit division
-      const int64_t qtok = (uint32_t)row / (uint32_t)a.nq;
-      // sequence of this query row. In single-token decode token t is nearly
-      // always sequence t: its metadata is loaded with the check (one round
-      // trip), and the search runs only if the guess is wrong.
-      int s = (int)(qtok < a.num_seqs ? qtok : a.num_seqs - 1);
-      int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
-      int64_t L = a.seq_lens[s];
-      int64_t pf0 = 0, pf1 = 0, pftot = 0;
-      if (a.plan.sk) {
-        pf0 = a.prefix[s];
-        pf1 = a.prefix[s + 1];
-        pftot = a.prefix[a.num_seqs];
-      }
-      if (!(qb <= qtok && qtok < qe)) {
-        s = wave_search_le(a.qsl, a.num_seqs, qtok);
-        qb = a.qsl[s];
-        qe = a.qsl[s + 1];
-        L = a.seq_lens[s];
-        if (a.plan.sk) {
-          pf0 = a.prefix[s];
-          pf1 = a.prefix[s + 1];
-        }
-      }
-      const int64_t cap = (int64_t)a.max_blocks * a.bs;
-      L = L < 0 ? 0 : (L > cap ? cap : L);
-      if (a.plan.sk) {
-        // stream-K: the workgroups whose step ranges cover this row's
-        // (quad, sequence) steps [xs, xe) each left one piece, numbered
-        // w + quad * num_seqs + s; workgroup w covers [w W / P, (w+1) W / P)
-        const int h = (int)(row - qtok * a.nq);
-        const int quad = h / (a.nq / a.nkv) / a.plan.hpw / a.plan.wpb;
-        const int64_t S = pftot;
-        const int64_t W = (int64_t)a.plan.sk_quads * S;
-        const int64_t P = (int64_t)a.plan.sk_grid < W ? (int64_t)a.plan.sk_grid : W;   // ranges, none empty
-        const int64_t xs = (int64_t)quad * S + pf0, xe = (int64_t)quad * S + pf1;
-        if (qtok >= qb && qtok < qe && xe > xs && W > 0) {
-          // the range holding step x: the largest w with floor(w W / P) <= x
-          const int64_t w0 = floor_div_small((xs + 1) * P - 1, W);
-          const int64_t w1 = floor_div_small(xe * P - 1, W);
-          nsp = (int)(w1 - w0 + 1);
-          pbase = ((w0 + (int64_t)quad * a.num_seqs + s) * a.plan.tq + (qtok - qb)) * a.nq + h;
-          pstride = (int64_t)a.plan.tq * a.nq;
-
-        }
-      } else if (qtok >= qb && qtok < qe) {
-        const int64_t pos = L - (qe - qb) + (qtok - qb);
-        if (pos >= 0) {
-          const int64_t n = (pos + a.plan.split_tokens) / a.plan.split_tokens;   // ceil((pos+1)/split)
-          nsp = (int)(n < a.plan.num_splits ? n : a.plan.num_splits);
-          // sliding window: the splits before the one holding the row's first
-          // visible key hold nothing for it (and may not have been written)
-          if (a.window > 0 && pos - a.window + 1 > 0) {
-            const int first = (int)((pos - a.window + 1) / a.plan.split_tokens);
-            nsp -= first;
-            pbase += (int64_t)first * pstride;
-          }
-        }
-      }
-    }
+    // rows number fewer than 2^31 (checked on the host): 32-bit division
+    const int64_t qtok = (uint32_t)row / (uint32_t)a.nq;
+    const RowSeq q = row_sequence(a, qtok);
+    int nsp;
+    int64_t pbase, pstride;
+    row_pieces(a, q, qtok, (int)(row - qtok * a.nq), row, nsp, pbase, pstride);
     float M = -INFINITY, Ls = 0.0f;
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    // fold one partial (m2, l2, y) into the running (M, Ls, o)
-    auto merge = [&](float m2, float l2, const float (&y)[8]) {
-      const float Mn = fmaxf(M, m2);
-      if (Mn == -INFINITY) return;                   // both empty
-      const float so = fast_exp2(M - Mn);            // 0 while M is -inf
-      const float sn = fast_exp2(m2 - Mn);
-      Ls = Ls * so + l2 * sn;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = o[e] * so + y[e] * sn;
-      M = Mn;
-    };
     for (int sp0 = grp; sp0 < nsp; sp0 += 4 * NG) {
       float mm[4], ll[4], y[4][8];
 #pragma unroll
@@ -451,7 +472,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
         }
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) merge(mm[k], ll[k], y[k]);
+      for (int k = 0; k < 4; ++k) lse_fold(M, Ls, o, mm[k], ll[k], y[k]);
     }
     // combine the NG copies (every lane of the wave takes part)
 #pragma unroll
@@ -460,13 +481,75 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = xor_lane_rt(o[e], d);
-      merge(m2, l2, y);
+      lse_fold(M, Ls, o, m2, l2, y);
     }
     const float inv_l = Ls > 0.0f ? 1.0f / Ls : 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] *= inv_l;
     if (a.qm == 0) store_out_row<LP>(o, a.b, jj, sbits, inv_b, a.out + row * hs + 8 * jj, lane_on && grp == 0);
     else store_out_plain(o, a.out + row * hs + 8 * jj, lane_on && grp == 0);
+  }
+}
+
+// The same merge for calls with many rows: each LP-lane group of a wave
+// takes its own row, NG consecutive rows (one query token: num_q_heads is a
+// multiple of NG) per wave, and folds the row's partials four loads at a
+// time; no cross-group butterfly. A quarter of the waves (head size 128) of
+// the one-row-per-wave form for the same rows.
+template <int LP>
+__global__ __launch_bounds__(256) void attn_reduce_rows_kernel(AttnArgs a) {
+  constexpr int NG = kWave / LP;
+  const int hs = a.hs;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int jj = lane & (LP - 1);
+  const int grp = lane / LP;
+  const bool lane_on = jj < (hs >> 3);
+  const int64_t n_units = a.num_q_tokens * (a.nq / NG);
+  const uint32_t sbits = (a.qm == 0 && lane_on) ? sign_bits8(a.seed, jj) : 0u;
+  const float inv_b = 1.0f / (float)a.b;
+  const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t u = wave0; u < n_units; u += n_waves) {
+    const int64_t row0 = u * NG;                              // the wave's first row
+    const int64_t qtok = (uint32_t)row0 / (uint32_t)a.nq;     // one token for all NG rows
+    const RowSeq q = row_sequence(a, qtok);
+    const int h = (int)(row0 - qtok * a.nq) + grp;
+    const int64_t row = row0 + grp;
+    int nsp;
+    int64_t pbase, pstride;
+    row_pieces(a, q, qtok, h, row, nsp, pbase, pstride);
+    float M = -INFINITY, Ls = 0.0f;
+    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int sp0 = 0; sp0 < nsp; sp0 += 4) {
+      float mm[4], ll[4], y[4][8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int sp = sp0 + k;
+        mm[k] = -INFINITY;
+        ll[k] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[k][e] = 0.0f;
+        if (sp < nsp) {
+          const int64_t prow = (int64_t)sp * pstride + pbase;
+          mm[k] = a.ws_ml[2 * prow];
+          ll[k] = a.ws_ml[2 * prow + 1];
+          if (lane_on) {
+            const float4* src = reinterpret_cast<const float4*>(a.ws_o + prow * hs + 8 * jj);
+            const float4 x0 = src[0], x1 = src[1];
+            y[k][0] = x0.x; y[k][1] = x0.y; y[k][2] = x0.z; y[k][3] = x0.w;
+            y[k][4] = x1.x; y[k][5] = x1.y; y[k][6] = x1.z; y[k][7] = x1.w;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) lse_fold(M, Ls, o, mm[k], ll[k], y[k]);
+    }
+    const float inv_l = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= inv_l;
+    // the epilogue's lane exchanges stay inside each LP-lane group
+    if (a.qm == 0) store_out_row<LP>(o, a.b, jj, sbits, inv_b, a.out + row * hs + 8 * jj, lane_on);
+    else store_out_plain(o, a.out + row * hs + 8 * jj, lane_on);
   }
 }
 
@@ -493,8 +576,26 @@ hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream) {
   const int LP = host_next_pow2(a.hs / 8);
-  const int64_t rows = a.num_q_tokens * a.nq;       // one wave per row (grid-stride beyond 2^22 rows)
-  const int64_t blocks = std::min<int64_t>((rows + 3) / 4, (int64_t)1 << 20);
+  const int NG = kWave / LP;
+  const int64_t rows = a.num_q_tokens * a.nq;
+  // one row per lane group where the caller asks for it and a wave's NG rows
+  // share one query token
+  if (a.reduce_rows && a.nq % NG == 0) {
+    const int64_t units = rows / NG;                 // waves (grid-stride beyond 2^22)
+    const int64_t blocks = std::min<int64_t>((units + 3) / 4, (int64_t)1 << 20);
+    dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
+    switch (LP) {
+      case 1: hipLaunchKernelGGL(attn_reduce_rows_kernel<1>, grid, block, 0, stream, a); break;
+      case 2: hipLaunchKernelGGL(attn_reduce_rows_kernel<2>, grid, block, 0, stream, a); break;
+      case 4: hipLaunchKernelGGL(attn_reduce_rows_kernel<4>, grid, block, 0, stream, a); break;
+      case 8: hipLaunchKernelGGL(attn_reduce_rows_kernel<8>, grid, block, 0, stream, a); break;
+      case 16: hipLaunchKernelGGL(attn_reduce_rows_kernel<16>, grid, block, 0, stream, a); break;
+      case 32: hipLaunchKernelGGL(attn_reduce_rows_kernel<32>, grid, block, 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  const int64_t blocks = std::min<int64_t>((rows + 3) / 4, (int64_t)1 << 20);   // one wave per row
   dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
   switch (LP) {
     case 1: hipLaunchKernelGGL(attn_reduce_kernel<1>, grid, block, 0, stream, a); break;

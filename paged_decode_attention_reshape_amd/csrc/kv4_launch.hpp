@@ -144,6 +144,7 @@ struct AttnArgs {
   int qm;                  // 0: int4 RHT cache; 1 / 2: int8 / fp8 per-token-head cache (no rotation)
   CacheLayout lay;         // shared by the K and V caches and their scales
   int window;              // sliding window: the query at position p sees keys (p - window, p]; 0 = none
+  int reduce_rows;         // merge: one row per lane group (few partials per row) instead of per wave
   AttnPlan plan;
 };
 

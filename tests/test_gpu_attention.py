@@ -125,6 +125,10 @@ SCHED = {
     "streamk_grid2000": {"KV4_SK_GRID": "2000"},
     # the split-KV scheme with small forced splits
     "splits64": {"KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64"},
+    # the merge forms forced: one row per wave after stream-K, one row per
+    # lane group after many splits
+    "streamk_merge_per_wave": {"KV4_REDUCE_ROWS": "0"},
+    "splits64_merge_per_group": {"KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64", "KV4_REDUCE_ROWS": "1"},
 }
 
 
