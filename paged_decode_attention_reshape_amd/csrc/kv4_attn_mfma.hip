@@ -38,6 +38,7 @@
 //   * k_scale / v_scale of the 32 tokens are loaded once per step (one lane
 //     per token) and redistributed through a 256-byte LDS slot per head.
 // Pages are looked up once per 16-token half tile (block_size % 16 == 0).
+#include <cstdlib>
 #include <type_traits>
 
 #include "kv4_device.hpp"
@@ -274,30 +275,35 @@ __device__ __forceinline__ int sk_first_step(int window, int64_t L, int64_t qlen
   return (window > 0 && k > 0) ? (int)(k >> 5) : 0;
 }
 
-__global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* prefix) {
-  __shared__ int32_t wave_tot[16];
-  __shared__ int32_t carry;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  if (tid == 0) carry = 0;
-  __syncthreads();
+// Work units (stream-K: KV steps, from the 32-token step holding the window
+// start) of sequence s.
+__device__ __forceinline__ int seq_units(const AttnArgs& a, int s) {
+  int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
+  qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
+  qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
+  int64_t L = a.seq_lens[s];
+  const int64_t cap = (int64_t)a.max_blocks * a.bs;
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  if (a.plan.sk) return (qe > qb && L > 0) ? (int)((L + 31) / 32) - sk_first_step(a.window, L, qe - qb) : 0;
   const int split = a.plan.split_tokens;
-  for (int c0 = 0; c0 < a.num_seqs; c0 += 1024) {
+  int nsp = (int)((L + split - 1) / split);
+  nsp = nsp < 1 ? 1 : (nsp > a.plan.num_splits ? a.plan.num_splits : nsp);
+  const int ntile = (int)((qe - qb + a.plan.tq - 1) / a.plan.tq);
+  return ntile * nsp * a.plan.n_head_tiles * (a.nkv / a.plan.hpw);
+}
+
+// Exclusive prefix of seq_units over the sequences, by the NT threads of one
+// workgroup: into lds[0 .. num_seqs] (lds[num_seqs] = total; NT / 64 more
+// ints of lds hold the wave totals) and, when gout is set, into gout too.
+template <int NT>
+__device__ void block_prefix(const AttnArgs& a, int32_t* lds, int32_t* gout) {
+  constexpr int NW = NT / 64;
+  int32_t* wave_tot = lds + a.num_seqs + 1;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int carry = 0;                                  // the same in every thread
+  for (int c0 = 0; c0 < a.num_seqs; c0 += NT) {
     const int s = c0 + tid;
-    int units = 0;
-    if (s < a.num_seqs) {
-      int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
-      qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
-      qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
-      int64_t L = a.seq_lens[s];
-      const int64_t cap = (int64_t)a.max_blocks * a.bs;
-      L = L < 0 ? 0 : (L > cap ? cap : L);
-      int nsp = (int)((L + split - 1) / split);
-      nsp = nsp < 1 ? 1 : (nsp > a.plan.num_splits ? a.plan.num_splits : nsp);
-      const int ntile = (int)((qe - qb + a.plan.tq - 1) / a.plan.tq);
-      units = ntile * nsp * a.plan.n_head_tiles * (a.nkv / a.plan.hpw);
-      if (a.plan.sk)   // KV steps of the sequence (from the 32-token step holding its window start)
-        units = (qe > qb && L > 0) ? (int)((L + 31) / 32) - sk_first_step(a.window, L, qe - qb) : 0;
-    }
+    const int units = s < a.num_seqs ? seq_units(a, s) : 0;
     // inclusive scan inside the wave
     int x = units;
 #pragma unroll
@@ -307,14 +313,46 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* pr
     }
     if (lane == 63) wave_tot[wv] = x;
     __syncthreads();
-    int before = carry;
-    for (int i = 0; i < wv; ++i) before += wave_tot[i];
-    if (s < a.num_seqs) prefix[s] = before + x - units;
-    __syncthreads();
-    if (tid == 1023) carry = before + x;
-    __syncthreads();
+    int before = carry, all = carry;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      before += i < wv ? wave_tot[i] : 0;
+      all += wave_tot[i];
+    }
+    if (s < a.num_seqs) {
+      lds[s] = before + x - units;
+      if (gout) gout[s] = before + x - units;
+    }
+    carry = all;
+    __syncthreads();                              // wave_tot is rewritten next round
   }
-  if (tid == 0) prefix[a.num_seqs] = carry;
+  if (tid == 0) {
+    lds[a.num_seqs] = carry;
+    if (gout) gout[a.num_seqs] = carry;
+  }
+  __syncthreads();
+}
+
+// The prefix as its own one-workgroup kernel (calls whose sequences do not
+// fit the attention kernel's LDS).
+__global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a, int32_t* prefix) {
+  __shared__ int32_t lds[1024 + 1 + 16];
+  // chunks of 1024 sequences: prefix of the chunk in LDS, then offset by the
+  // running total into the global prefix
+  int base = 0;
+  const int nseq = a.num_seqs;
+  for (int c0 = 0; c0 < nseq || c0 == 0; c0 += 1024) {
+    AttnArgs c = a;
+    c.num_seqs = nseq - c0 < 1024 ? nseq - c0 : 1024;
+    c.qsl = a.qsl + c0;
+    c.seq_lens = a.seq_lens + c0;
+    block_prefix<1024>(c, lds, nullptr);
+    for (int i = threadIdx.x; i < c.num_seqs; i += 1024) prefix[c0 + i] = base + lds[i];
+    base += lds[c.num_seqs];
+    __syncthreads();
+    if (c0 + 1024 >= nseq) break;
+  }
+  if (threadIdx.x == 0) prefix[nseq] = base;
 }
 
 // LDS layout of one 32-token step (per wave), filled by direct global->LDS
@@ -486,6 +524,14 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
   constexpr int kStages = stages_for<HS>();
   constexpr int STH = SM::STAGE_H;
   __shared__ SM smem_all[WPB];
+  // fused plan: the sequences' prefix, computed by every workgroup
+  extern __shared__ int32_t plan_lds[];
+  const int32_t* pf = prefix;
+  if (a.plan.fused_plan) {
+    // the merge reads block 0's copy of the prefix
+    block_prefix<64 * WPB>(a, plan_lds, blockIdx.x == 0 ? const_cast<int32_t*>(prefix) : nullptr);
+    pf = plan_lds;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wv = WPB == 1 ? 0 : uniform(threadIdx.x >> 6);   // wave index (uniform: LDS bases in SGPRs)
@@ -499,7 +545,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
   const int gh = a.plan.gh;
   const int rph = HPW == 1 ? ROWS : a.plan.tq * gh;   // MFMA rows per kv head
   const int split = a.plan.split_tokens;
-  const int total = uniform(prefix[a.num_seqs]);
+  const int total = uniform(pf[a.num_seqs]);
   const int bsz = a.bs;
   const int bs_log2 = __builtin_ctz((unsigned)bsz);      // the planner sends only power-of-two pages here
   const int bs_mask = bsz - 1;
@@ -1204,8 +1250,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
     while (x < x1) {
       const int q = (int)(x / S);
       const int64_t loc = x - (int64_t)q * S;
-      const int s_ = wave_search_le(prefix, nseq, loc);
-      const int64_t t0 = uniform(prefix[s_]), t1 = uniform(prefix[s_ + 1]);
+      const int s_ = wave_search_le(pf, nseq, loc);
+      const int64_t t0 = uniform(pf[s_]), t1 = uniform(pf[s_ + 1]);
       const int64_t end = min(x1 - (int64_t)q * S, t1);
       int64_t qb = a.qsl[s_], qe = a.qsl[s_ + 1];
       qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
@@ -1233,7 +1279,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
     const int u = u0 + wv;
     if (u >= total) continue;
     Unit un;
-    if (!decode_unit(a, prefix, u, un)) continue;
+    if (!decode_unit(a, pf, u, un)) continue;
     // the unit is the same for every lane of the wave
     const int us = uniform(un.s), ui0 = uniform(un.i0), uqbeg = uniform(un.qbeg);
     const int uqlen = uniform(un.qlen), uL = uniform(un.L), ug = uniform(un.g);
@@ -1251,25 +1297,40 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
 
 static int g_num_cus = 0;
 
+// Sequences whose prefix the attention kernel computes itself (in LDS) when
+// that costs it no occupancy; longer batches run the plan kernel first.
+constexpr int kFusedPlanMaxSeqs = 1024;
+constexpr size_t kFusedPlanLds = (kFusedPlanMaxSeqs + 1 + 16) * sizeof(int32_t);
+
+// Workgroups of the kernel the GPU holds at once (fused: with the plan LDS).
 template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB = 1>
-static int resident_blocks() {
-  static int per_cu = 0;
-  if (per_cu == 0) {
+static int resident_blocks(bool fused) {
+  static int per_cu[2] = {0, 0};
+  int& pc = per_cu[fused ? 1 : 0];
+  if (pc == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb,
                                                      reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH, WIN, NRB>),
-                                                     64 * mfma_wpb<HS, HPW, QM>(), 0) != hipSuccess || nb < 1)
+                                                     64 * mfma_wpb<HS, HPW, QM>(), fused ? kFusedPlanLds : 0) != hipSuccess ||
+        nb < 1)
       nb = 1;
-    per_cu = nb;
+    pc = nb;
   }
-  return per_cu * g_num_cus;
+  return pc * g_num_cus;
 }
 
 template <int HS, int QM, bool WIN>
 static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_units, hipStream_t stream) {
   if (a.plan.hpw == 4 && Geo<HS>::NVR != 1) return hipErrorInvalidValue;
   if (QM != 0 && (a.plan.hpw != 1 || a.plan.wpb != mfma_wpb<HS, 1, QM>())) return hipErrorInvalidValue;
-  auto go = [&](auto kernel, int wpb, int resident) {
+  // resident(fused) -> workgroups the GPU holds at once
+  auto go = [&](auto kernel, int wpb, auto resident_of) {
+    const int plain = resident_of(false);
+    a.plan.fused_plan = (a.num_seqs <= kFusedPlanMaxSeqs && resident_of(true) == plain) ? 1 : 0;
+    if (const char* f = std::getenv("KV4_FUSED_PLAN")) a.plan.fused_plan = a.plan.fused_plan && std::atoi(f) != 0;
+    const int resident = plain;
+    if (!a.plan.fused_plan)
+      hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a, const_cast<int32_t*>(prefix));
     int64_t wgs;
     if (a.plan.sk) {
       // stream-K: exactly the workgroups the GPU holds at once (at most the
@@ -1283,18 +1344,19 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
       if (wgs > cap) wgs = cap;
       if (wgs < 1) wgs = 1;
     }
-    hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(64 * wpb), 0, stream, a, prefix);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(64 * wpb), a.plan.fused_plan ? kFusedPlanLds : 0, stream, a,
+                       prefix);
   };
   if constexpr (QM != 0) {
-    go(attn_mfma_kernel<HS, 1, QM, false, WIN, 1>, mfma_wpb<HS, 1, QM>(), resident_blocks<HS, 1, QM, false, WIN>());
+    go(attn_mfma_kernel<HS, 1, QM, false, WIN, 1>, mfma_wpb<HS, 1, QM>(), [](bool f) { return resident_blocks<HS, 1, QM, false, WIN>(f); });
     return hipSuccess;
   }
   if (a.plan.vjh) {
     if constexpr (HS == 128) {
       if (a.plan.hpw == 2) {
-        go(attn_mfma_kernel<HS, 2, 0, true, WIN, 1>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0, true, WIN>());
+        go(attn_mfma_kernel<HS, 2, 0, true, WIN, 1>, mfma_wpb<HS, 2, 0>(), [](bool f) { return resident_blocks<HS, 2, 0, true, WIN>(f); });
       } else if (a.plan.hpw == 4) {
-        go(attn_mfma_kernel<HS, 4, 0, true, WIN, 1>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0, true, WIN>());
+        go(attn_mfma_kernel<HS, 4, 0, true, WIN, 1>, mfma_wpb<HS, 4, 0>(), [](bool f) { return resident_blocks<HS, 4, 0, true, WIN>(f); });
       } else {
         return hipErrorInvalidValue;
       }
@@ -1304,19 +1366,19 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
   }
   if (a.plan.rb == 2) {
     if constexpr (HS <= 128) {
-      go(attn_mfma_kernel<HS, 1, 0, false, WIN, 2>, mfma_wpb<HS, 1, 0>(), resident_blocks<HS, 1, 0, false, WIN, 2>());
+      go(attn_mfma_kernel<HS, 1, 0, false, WIN, 2>, mfma_wpb<HS, 1, 0>(), [](bool f) { return resident_blocks<HS, 1, 0, false, WIN, 2>(f); });
       return hipSuccess;
     }
     return hipErrorInvalidValue;
   }
   switch (a.plan.hpw) {
-    case 2: go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1>, mfma_wpb<HS, 2, 0>(), resident_blocks<HS, 2, 0, false, WIN>()); break;
+    case 2: go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1>, mfma_wpb<HS, 2, 0>(), [](bool f) { return resident_blocks<HS, 2, 0, false, WIN>(f); }); break;
     case 4:
       // four heads' V loads of a step must fit the 6-bit load counter
       if constexpr (Geo<HS>::NVR == 1)
-        go(attn_mfma_kernel<HS, 4, 0, false, WIN, 1>, mfma_wpb<HS, 4, 0>(), resident_blocks<HS, 4, 0, false, WIN>());
+        go(attn_mfma_kernel<HS, 4, 0, false, WIN, 1>, mfma_wpb<HS, 4, 0>(), [](bool f) { return resident_blocks<HS, 4, 0, false, WIN>(f); });
       break;
-    default: go(attn_mfma_kernel<HS, 1, 0, false, WIN, 1>, mfma_wpb<HS, 1, 0>(), resident_blocks<HS, 1, 0, false, WIN>()); break;
+    default: go(attn_mfma_kernel<HS, 1, 0, false, WIN, 1>, mfma_wpb<HS, 1, 0>(), [](bool f) { return resident_blocks<HS, 1, 0, false, WIN>(f); }); break;
   }
   return hipSuccess;
 }
@@ -1328,9 +1390,7 @@ static hipError_t launch_hs(AttnArgs& a, const int32_t* prefix, int64_t max_unit
 }
 
 hipError_t launch_attn_mfma(AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a, prefix);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   if (g_num_cus == 0) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) == hipSuccess &&

@@ -111,6 +111,7 @@ struct AttnPlan {
   int sk_grid;         // stream-K: workgroups launched (set at launch)
   int vjh;             // MFMA, head size 128, hpw > 1: V staged per head (heads not adjacent)
   int rb;              // MFMA, int4, hpw 1: 16-row MFMA blocks per wave (1 or 2)
+  int fused_plan;      // MFMA: the kernel computes the sequences' prefix itself (set at launch)
 };
 
 struct AttnArgs {

@@ -129,6 +129,9 @@ SCHED = {
     # lane group after many splits
     "streamk_merge_per_wave": {"KV4_REDUCE_ROWS": "0"},
     "splits64_merge_per_group": {"KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64", "KV4_REDUCE_ROWS": "1"},
+    # the sequences' prefix from the separate plan kernel instead of in-kernel
+    "streamk_plan_kernel": {"KV4_FUSED_PLAN": "0"},
+    "splits64_plan_kernel": {"KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64", "KV4_FUSED_PLAN": "0"},
 }
 
 
@@ -345,4 +348,19 @@ def test_row_blocks_per_wave(case, sched, monkeypatch):
     name, nq, nkv, hs, ql, sl, bs = case
     r = run_gpu(W.custom(name, nq, nkv, hs, ql, sl, block_size=bs))
     _g1(r)
+    _g2(r)
+
+
+@pytest.mark.parametrize("sched", ["streamk", "splits64"])
+@pytest.mark.parametrize("qlen", [1, 3])
+def test_more_sequences_than_the_in_kernel_prefix_holds(qlen, sched, monkeypatch):
+    """1500 short sequences: beyond the 1024 whose prefix the attention kernel
+    builds itself, so the plan kernel runs first, in two chunks."""
+    monkeypatch.setenv("KV4_FORCE_PATH", "mfma")
+    if sched == "splits64":
+        monkeypatch.setenv("KV4_STREAMK", "0")
+        monkeypatch.setenv("KV4_SPLIT_TOKENS", "64")
+    rng = np.random.default_rng(7 + qlen)
+    sl = [int(x) for x in rng.integers(qlen, 90, 1500)]
+    r = run_gpu(W.custom("many_seqs", 8, 2, 64, [qlen] * 1500, sl, block_size=16))
     _g2(r)
