@@ -1302,6 +1302,26 @@ static int g_num_cus = 0;
 constexpr int kFusedPlanMaxSeqs = 1024;
 constexpr size_t kFusedPlanLds = (kFusedPlanMaxSeqs + 1 + 16) * sizeof(int32_t);
 
+// Whether the plan LDS leaves the kernel's resident workgroups per CU as
+// they are, counting LDS in 1 KB units: the occupancy query counts bytes,
+// and a kernel whose workgroups fill the CU to within a few hundred bytes
+// (head size 192, int8 / fp8: three of 50.4 KB) was measured to lose a
+// workgroup per CU with the plan LDS although the query said otherwise.
+static bool plan_lds_fits(const void* kernel, int resident) {
+  static int lds_per_cu = 0;
+  if (lds_per_cu == 0) {
+    int dev = 0, v = 0;
+    lds_per_cu = (hipGetDevice(&dev) == hipSuccess &&
+                  hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
+                  v > 0) ? v : 160 * 1024;
+  }
+  hipFuncAttributes fa;
+  if (hipFuncGetAttributes(&fa, kernel) != hipSuccess) return false;
+  const size_t per_wg = (fa.sharedSizeBytes + kFusedPlanLds + 1023) / 1024 * 1024;
+  const int per_cu = resident / (g_num_cus > 0 ? g_num_cus : 1);
+  return (size_t)per_cu * per_wg <= (size_t)lds_per_cu;
+}
+
 // Workgroups of the kernel the GPU holds at once (fused: with the plan LDS).
 template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB = 1>
 static int resident_blocks(bool fused) {
@@ -1326,7 +1346,8 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
   // resident(fused) -> workgroups the GPU holds at once
   auto go = [&](auto kernel, int wpb, auto resident_of) {
     const int plain = resident_of(false);
-    a.plan.fused_plan = (a.num_seqs <= kFusedPlanMaxSeqs && resident_of(true) == plain) ? 1 : 0;
+    a.plan.fused_plan = (a.num_seqs <= kFusedPlanMaxSeqs && resident_of(true) == plain &&
+                         plan_lds_fits(reinterpret_cast<const void*>(kernel), plain)) ? 1 : 0;
     if (const char* f = std::getenv("KV4_FUSED_PLAN")) a.plan.fused_plan = a.plan.fused_plan && std::atoi(f) != 0;
     const int resident = plain;
     if (!a.plan.fused_plan)
