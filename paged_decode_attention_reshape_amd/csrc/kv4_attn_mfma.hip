@@ -39,6 +39,8 @@
 //     per token) and redistributed through a 256-byte LDS slot per head.
 // Pages are looked up once per 16-token half tile (block_size % 16 == 0).
 #include <cstdlib>
+#include <mutex>
+#include <unordered_map>
 #include <type_traits>
 
 #include "kv4_device.hpp"
@@ -1315,9 +1317,21 @@ static bool plan_lds_fits(const void* kernel, int resident) {
                   hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
                   v > 0) ? v : 160 * 1024;
   }
-  hipFuncAttributes fa;
-  if (hipFuncGetAttributes(&fa, kernel) != hipSuccess) return false;
-  const size_t per_wg = (fa.sharedSizeBytes + kFusedPlanLds + 1023) / 1024 * 1024;
+  // static LDS of each kernel, looked up once
+  static std::mutex mu;
+  static std::unordered_map<const void*, size_t> static_lds;
+  size_t lds = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = static_lds.find(kernel);
+    if (it == static_lds.end()) {
+      hipFuncAttributes fa;
+      if (hipFuncGetAttributes(&fa, kernel) != hipSuccess) return false;
+      it = static_lds.emplace(kernel, fa.sharedSizeBytes).first;
+    }
+    lds = it->second;
+  }
+  const size_t per_wg = (lds + kFusedPlanLds + 1023) / 1024 * 1024;
   const int per_cu = resident / (g_num_cus > 0 ? g_num_cus : 1);
   return (size_t)per_cu * per_wg <= (size_t)lds_per_cu;
 }
