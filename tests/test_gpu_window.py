@@ -79,6 +79,13 @@ SCHED = {
     "mfma_split1000": {"KV4_FORCE_PATH": "mfma", "KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "1000"},
     "valu_split100": {"KV4_FORCE_PATH": "valu", "KV4_SPLIT_TOKENS": "100"},
     "streamk_grid3": {"KV4_SK_GRID": "3"},
+    # the other merge form (one row per lane group) over windowed splits, and
+    # the separate plan kernel with windowed stream-K steps
+    "mfma_split64_merge_per_group": {"KV4_FORCE_PATH": "mfma", "KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64",
+                                     "KV4_REDUCE_ROWS": "1"},
+    "streamk_plan_kernel": {"KV4_FUSED_PLAN": "0"},
+    # one 16-row block per wave for the 9-token sequence (two by default)
+    "mfma_one_row_block": {"KV4_FORCE_PATH": "mfma", "KV4_MFMA_RB": "1"},
 }
 
 
