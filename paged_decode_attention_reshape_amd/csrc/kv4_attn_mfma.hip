@@ -478,8 +478,8 @@ constexpr int mfma_wpe() {
   return HPW == 1 && (NRB > 1 || HS >= 192 || (QM != 0 && HS >= 96)) ? 2 : MfmaShape<HPW>::WPE;
 }
 
-// HPW = kv heads per wave. HPW = 1: the 16 MFMA rows are the query tile of one
-// kv head (tq tokens x gh query heads). HPW > 1 (single-token decode): rows
+// HPW = kv heads per wave. HPW = 1: the 16 MFMA rows (32 with NRB = 2) are
+// the query tile of one kv head (tq tokens x gh query heads). HPW > 1 (single-token decode): rows
 // r = hl * G + i are query head i of kv head kv0 + hl; each head keeps its own
 // QK and PV matrix-core products (rows of the other heads are dropped from S
 // and zeroed in P), while the softmax, the page walk and the address work are
