@@ -352,10 +352,11 @@ def test_row_blocks_per_wave(case, sched, monkeypatch):
 
 
 @pytest.mark.parametrize("sched", ["streamk", "splits64"])
-@pytest.mark.parametrize("qlen", [1, 3])
+@pytest.mark.parametrize("qlen", [1, 3, 5])
 def test_more_sequences_than_the_in_kernel_prefix_holds(qlen, sched, monkeypatch):
     """1500 short sequences: beyond the 1024 whose prefix the attention kernel
-    builds itself, so the plan kernel runs first, in two chunks."""
+    builds itself, so the plan kernel runs first, in two chunks (qlen 5 x
+    group 4: two row blocks per wave)."""
     monkeypatch.setenv("KV4_FORCE_PATH", "mfma")
     if sched == "splits64":
         monkeypatch.setenv("KV4_STREAMK", "0")
