@@ -1,0 +1,65 @@
+"""Seeded random shapes through the whole int4 path: head size, group, page
+size, query lengths (decode, multi-token, prefill chunks, empty), context
+lengths and work schedule are drawn per case, so that combinations no
+hand-written case lists (row blocks with ragged groups, stream-K pieces over
+short sequences, merges over few or many pieces) meet the oracle.
+
+Gates: codes and scales bit-exact (G1), attention atol = rtol = 1e-2 against
+the fp64 oracle reading the GPU-written cache (G2).
+"""
+import numpy as np
+import pytest
+
+from gpu_helpers import W, run_gpu
+from test_gpu_attention import _g1, _g2
+
+pytestmark = pytest.mark.gpu
+
+SCHEDULES = [
+    {},
+    {"KV4_FORCE_PATH": "mfma"},
+    {"KV4_FORCE_PATH": "mfma", "KV4_SK_GRID": "5"},
+    {"KV4_FORCE_PATH": "mfma", "KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "96"},
+    {"KV4_FORCE_PATH": "mfma", "KV4_REDUCE_ROWS": "1"},
+    {"KV4_FORCE_PATH": "mfma", "KV4_FUSED_PLAN": "0"},
+    {"KV4_FORCE_PATH": "mfma", "KV4_MFMA_RB": "1"},
+    {"KV4_FORCE_PATH": "valu"},
+]
+
+
+def _case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    hs = int(rng.choice([64, 96, 128, 192, 80]))
+    nkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 6, 8, 16, 24]))
+    bs = int(rng.choice([16, 32, 16, 8]))
+    nseq = int(rng.integers(1, 7))
+    kind = rng.choice(["decode", "multi", "prefill", "mixed"])
+    ql, sl = [], []
+    for _ in range(nseq):
+        if kind == "decode":
+            q = 1
+        elif kind == "multi":
+            q = int(rng.integers(1, 9))
+        elif kind == "prefill":
+            q = int(rng.integers(1, 60))
+        else:
+            q = int(rng.choice([0, 1, 1, 5, 33]))
+        ctx = int(rng.integers(0, 700))
+        ql.append(q)
+        sl.append(q + ctx)
+    if sum(ql) == 0:
+        ql[0], sl[0] = 1, max(sl[0], 1)
+    sched = SCHEDULES[seed % len(SCHEDULES)]
+    return hs, nkv, g, bs, ql, sl, sched
+
+
+@pytest.mark.parametrize("seed", range(120))
+def test_random_shape(seed, monkeypatch):
+    hs, nkv, g, bs, ql, sl, sched = _case(seed)
+    for k, v in sched.items():
+        monkeypatch.setenv(k, v)
+    w = W.custom(f"rand{seed}", nkv * g, nkv, hs, ql, sl, block_size=bs, seed=seed, outlier_frac=0.01)
+    r = run_gpu(w)
+    _g1(r)
+    _g2(r)
