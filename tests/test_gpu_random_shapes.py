@@ -63,3 +63,19 @@ def test_random_shape(seed, monkeypatch):
     r = run_gpu(w)
     _g1(r)
     _g2(r)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_shape_modes_layouts_windows(seed, monkeypatch):
+    """The same draws through the layout entry points: int4 / int8 / fp8
+    caches, packed or inline-scale rows, with or without a sliding window."""
+    from test_gpu_window import _run
+    hs, nkv, g, bs, ql, sl, sched = _case(500 + seed)
+    for k, v in sched.items():
+        monkeypatch.setenv(k, v)
+    rng = np.random.default_rng(7000 + seed)
+    mode = ["int4", "int8", "fp8"][seed % 3]
+    inline = bool(rng.integers(0, 2))
+    window = int(rng.choice([0, 0, 1, 9, 64, 300]))
+    w = W.custom(f"randl{seed}", nkv * g, nkv, hs, ql, sl, block_size=bs, seed=seed, outlier_frac=0.01)
+    _run(w, mode, window, inline=inline)
