@@ -79,3 +79,26 @@ def test_random_shape_modes_layouts_windows(seed, monkeypatch):
     window = int(rng.choice([0, 0, 1, 9, 64, 300]))
     w = W.custom(f"randl{seed}", nkv * g, nkv, hs, ql, sl, block_size=bs, seed=seed, outlier_frac=0.01)
     _run(w, mode, window, inline=inline)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_write(seed):
+    """kv4_rht_write on random head sizes (any multiple of 8 up to 256),
+    kv head counts, page sizes and slot maps (shuffled, repeated pages,
+    negative and past-the-end slots, which are skipped), against the oracle
+    bit for bit over the whole cache (untouched bytes keep the fill)."""
+    from test_gpu_write import _write_and_compare
+    rng = np.random.default_rng(9000 + seed)
+    hs = 8 * int(rng.integers(1, 33))
+    nkv = int(rng.integers(1, 9))
+    bs = int(rng.choice([1, 8, 16, 32]))
+    T = int(rng.integers(0, 400))
+    nb = max(1, (T + bs - 1) // bs + int(rng.integers(0, 3)))
+    slots = rng.permutation(nb * bs)[:T].astype(np.int64)
+    if T:
+        bad = rng.random(T) < 0.05
+        slots[bad] = rng.choice([-1, -7, nb * bs, nb * bs + 5], int(bad.sum()))
+    gain = np.where(rng.random((nkv, hs)) < 0.02, 20.0, 1.0).astype(np.float32)   # a few outlier channels
+    key = W.normal_bf16((T, nkv, hs), seed=seed, gain=gain)
+    value = W.normal_bf16((T, nkv, hs), seed=seed + 10 ** 6)
+    _write_and_compare(key, value, slots, nb, bs, seed=0x1234 + seed)
