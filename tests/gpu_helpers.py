@@ -47,9 +47,11 @@ def alloc_cache(w: W.Workload, num_blocks: int, fill: int = 0):
     return kc, vc, ks, vs
 
 
-def run_gpu(w: W.Workload, gen_device="cpu", attention=True, fill=0, softmax_scale=None) -> GpuRun:
+def run_gpu(w: W.Workload, gen_device="cpu", attention=True, fill=0, softmax_scale=None,
+            len_slack=(0, 0)) -> GpuRun:
     """Generate inputs, write every KV token with kv4_rht_write (one call),
-    run kv4_paged_attention over the batch."""
+    run kv4_paged_attention over the batch. len_slack adds to the host-side
+    max_query_len / max_seq_len bounds (upper bounds need not be tight)."""
     say(f"[gpu] case {w.name}: nq={w.num_q_heads} nkv={w.num_kv_heads} hs={w.head_size} "
         f"bs={w.block_size} seqs={w.num_seqs} q_tokens={w.num_q_tokens} kv_tokens={w.total_kv_tokens}")
     lay = W.make_layout(w)
@@ -63,8 +65,8 @@ def run_gpu(w: W.Workload, gen_device="cpu", attention=True, fill=0, softmax_sca
         r.out = kv4.kv4_paged_attention(
             t.query.to(DEV), kc, vc, ks, vs, torch.from_numpy(lay.block_table).to(DEV),
             torch.from_numpy(lay.seq_lens).to(DEV), torch.from_numpy(lay.query_start_loc).to(DEV),
-            max_query_len=w.max_query_len, max_seq_len=w.max_seq_len, sign_seed=w.sign_seed,
-            softmax_scale=softmax_scale)
+            max_query_len=w.max_query_len + len_slack[0], max_seq_len=w.max_seq_len + len_slack[1],
+            sign_seed=w.sign_seed, softmax_scale=softmax_scale)
     torch.cuda.synchronize()
     return r
 

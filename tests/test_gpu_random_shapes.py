@@ -60,7 +60,9 @@ def test_random_shape(seed, monkeypatch):
     for k, v in sched.items():
         monkeypatch.setenv(k, v)
     w = W.custom(f"rand{seed}", nkv * g, nkv, hs, ql, sl, block_size=bs, seed=seed, outlier_frac=0.01)
-    r = run_gpu(w)
+    # every third case passes loose host-side bounds (upper bounds, not maxima)
+    slack = (3, 2 * w.max_seq_len + 17) if seed % 3 == 2 else (0, 0)
+    r = run_gpu(w, len_slack=slack)
     _g1(r)
     _g2(r)
 
