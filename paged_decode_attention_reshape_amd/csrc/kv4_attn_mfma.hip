@@ -376,9 +376,11 @@ struct StageGeo {
   static constexpr int KREG = 64 * KSTR;                                          // one K load region
   static constexpr int KHALF = NKL * KREG;                                        // K bytes per half tile
   static constexpr int VBYTES_TOK = 256 * Geo<HS>::NVR;
+  // head size 96: packed token rows of the wave's heads, 2 KB per head
+  static constexpr int VREG = HS == 96 ? 2048 : 8 * VBYTES_TOK;
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = 2 * KHALF;
-  static constexpr int S_OFF = V_OFF + 8 * VBYTES_TOK;
+  static constexpr int S_OFF = V_OFF + VREG;
   static constexpr int BYTES = S_OFF + 256;
 };
 
@@ -622,6 +624,38 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
     vj_rd[i] = VJH ? (uint32_t)(t * 64) + 4u * (uint32_t)n
                    : (uint32_t)((t / RPI) * 1024 + (t % RPI) * RB) + (HS >= 128 ? 4u : 2u) * (uint32_t)n;
   }
+  // Packed joint V rows (VP, int4 head size 96): the wave's RB-byte token rows
+  // (48 or 96 bytes, six 16-byte pieces per head pair) land token-major in LDS
+  // through 16-byte lanes, VPL loads of 1 KB per half tile (lanes past its 16
+  // rows fetch nothing). Lane (n, q4) reads 4 bytes (8 columns) of token
+  // 4 q4 + i at offset 4 n of its head's 48 bytes, so PV runs as at head size
+  // 128: one region of 8 columns per lane, MFMA rows 12-15 (columns 96-127)
+  // carrying nothing that is stored.
+  constexpr bool VP = QM == 0 && !VJH && HS == 96;
+  constexpr int VPL = (16 * RB + 1023) / 1024;
+  uint32_t vp_src[VP ? VPL : 1];
+  uint32_t vp_rd[4];
+  if constexpr (VP) {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int b = 1024 * j + 16 * lane, t = b / RB;
+      vp_src[j] = t < 16 ? (uint32_t)t * tok_stride + (uint32_t)(b % RB) : 0x80000000u;   // past the range: zeros
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vp_rd[i] = (uint32_t)((4 * q4 + i) * RB) + 4u * (uint32_t)n;
+  }
+  // PV column regions (VP: one region of 8 columns per lane) and the V
+  // accumulators they need
+  constexpr int NVRV = VP ? 1 : NVR;
+  constexpr int NSV = VP ? 8 : NS;
+  auto vreg = [&](int r, int& w, int& cb) {
+    if constexpr (VP) {
+      w = 8;
+      cb = 0;
+    } else {
+      v_region_any<HS, QM>(r, w, cb);
+    }
+  };
   const int64_t soff = (int64_t)(lane & 15) * s_tok;         // scale floats
   const float* sc_base = lane < 32 ? a.k_scale : a.v_scale;
   const bool sc_half_b = (lane & 16) != 0;
@@ -753,13 +787,13 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
 
-    f32x4_t acc[NRB][NS];
+    f32x4_t acc[NRB][NSV];
     f32x4_t pacc[NRB];
     float m_run[NRB], l_run[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
-      for (int i = 0; i < NS; ++i) acc[rb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NSV; ++i) acc[rb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       pacc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       m_run[rb] = -INFINITY;
       l_run[rb] = 0.0f;
@@ -775,10 +809,12 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
     // with zeros, which is never read).
     constexpr int NLK = HPW * (2 * SG::NKL + 1);   // loads per issue_k
     constexpr int NLV = QM ? 2 * StageGeoQ<HS>::VL
-                           : (VJH ? 2 * HPW : (VJ ? 2 * (16 / RPI) : HPW * 8 * NVR));   // loads per issue_v
+                           : (VJH ? 2 * HPW : (VJ ? 2 * (16 / RPI) : (VP ? 2 * VPL : HPW * 8 * NVR)));   // loads per issue_v
     // VJ: half tile hh of a slot (16 * RB bytes) sits in head hh's V region
     // (2 KB; RB = 128, two or more heads per wave) or at V_OFF + hh KB (RB = 64)
     auto vj_base = [&](auto* st, int hh) { return st + (RB == 128 ? hh * STH : hh * 1024) + SG::V_OFF; };
+    // VP: half tile hh in head hh's V region (two heads) or at V_OFF + hh KB (one)
+    auto vp_base = [&](auto* st, int hh) { return st + (HPW == 1 ? hh * 1024 : hh * STH) + SG::V_OFF; };
     static_assert(NLK < 64 && NLV < 64, "vmcnt range");
     int64_t v_bya = 0, v_byb = 0;
     uint32_t v_nrec = 0;
@@ -851,6 +887,11 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
             dma_buf<16>(rv[hh], vjh_src + hl * head_bytes, st + hl * STH + SG::V_OFF + hh * 1024);
+      } else if constexpr (VP) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) dma_buf<16>(rv[hh], vp_src[j], vp_base(st, hh) + j * 1024);
       } else if constexpr (VJ) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -1030,7 +1071,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
         ph4[rb] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-          for (int i = 0; i < NS; ++i) acc[rb][i] *= alpha;
+          for (int i = 0; i < NSV; ++i) acc[rb][i] *= alpha;
           pacc[rb] *= alpha;
         }
         l_run[rb] = l_run[rb] * alpha + psum_l;
@@ -1078,13 +1119,15 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
         }
         int ns = 0;
 #pragma unroll
-        for (int r = 0; r < NVR; ++r) {
+        for (int r = 0; r < NVRV; ++r) {
           int w, cb;
-          v_region<HS>(r, w, cb);
+          vreg(r, w, cb);
           uint32_t x[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            if constexpr (VJH) {
+            if constexpr (VP) {
+              x[i] = *reinterpret_cast<const uint32_t*>(vp_base(st, i >> 2) + vp_rd[i & 3] + hl * HALF);
+            } else if constexpr (VJH) {
               x[i] = *reinterpret_cast<const uint32_t*>(st + hl * STH + SG::V_OFF + (i >> 2) * 1024 + vj_rd[i & 3]);
             } else if constexpr (VJ) {
               const unsigned char* src = vj_base(st, i >> 2) + vj_rd[i & 3] + hl * HALF;
@@ -1149,11 +1192,12 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
         float* dst = a.ws_o + prow * HS;
         int ns = 0;
 #pragma unroll
-        for (int r = 0; r < NVR; ++r) {
+        for (int r = 0; r < NVRV; ++r) {
           int w, cb;
-          v_region_any<HS, QM>(r, w, cb);
+          vreg(r, w, cb);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
+            if (VP && 4 * q4 + rr >= HS / 8) continue;   // MFMA rows past the head's columns
             float* d = dst + cb + w * (4 * q4 + rr);
             const f32x4_t* A = acc[rb];
             const float pb = pbias[rb];
@@ -1186,11 +1230,12 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
       const float inv_l = l_run[rb] > 0.0f ? 1.0f / l_run[rb] : 0.0f;
       int ns = 0;
 #pragma unroll
-      for (int r = 0; r < NVR; ++r) {
+      for (int r = 0; r < NVRV; ++r) {
         int w, cb;
-        v_region_any<HS, QM>(r, w, cb);
+        vreg(r, w, cb);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
+          if (VP && 4 * q4 + rr >= HS / 8) continue;   // MFMA rows past the head's columns
           const int c0 = cb + w * (4 * q4 + rr);
 #pragma unroll
           for (int t = 0; t < 8; ++t)
