@@ -11,7 +11,8 @@
 // code_V_j, out = D.H.o'/b.
 //
 // gfx950 mapping. One wave = one work unit (sequence, query tile of up to 16
-// rows, group of hpw kv heads, KV split); a workgroup takes consecutive units
+// rows -- 32 with two row blocks --, group of hpw kv heads, KV range: a split,
+// or a stream-K piece in decode); a workgroup takes consecutive units
 // (neighbouring kv heads of the same pages, whose code rows share cache lines
 // inside one CU). The KV range is walked 32 tokens (two 16-token half tiles)
 // per step, with the loads of the next step in flight (direct buffer->LDS
