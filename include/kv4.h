@@ -83,7 +83,11 @@ typedef enum {
  *   key_cache  [s / block_size, s % block_size, h, :]  (head_size/2 bytes)
  *   k_scale_cache[s / block_size, s % block_size, h]   (float32)
  * and likewise for value. Slots < 0 or >= num_blocks*block_size are skipped.
- * Duplicate slots in one call race (the stored bytes are then unspecified).
+ * Duplicate slots in one call race (the stored bytes are then unspecified);
+ * with the environment variable KV4_CHECK_SLOTS=1 every write entry point
+ * copies the slot map to the host first (the call then waits for the
+ * stream) and returns KV4_EINVAL, before any launch, if a slot in
+ * [0, num_blocks * block_size) appears twice.
  *
  *   key, value          bf16 [num_tokens, num_kv_heads, head_size]; rows of
  *                       consecutive tokens are key_token_stride /

@@ -9,6 +9,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <unordered_map>
+#include <vector>
 #include <string>
 
 #include "kv4_launch.hpp"
@@ -285,6 +287,29 @@ kv4::CacheLayout to_layout(const kv4_cache_layout* l) {
   return c;
 }
 
+// Debug check (KV4_CHECK_SLOTS=1): the slot map is copied to the host (the
+// call then waits for the stream) and every slot in [0, num_slots) must
+// appear at most once -- two tokens in one slot would race.
+int check_unique_slots(const char* what, const int64_t* slot_mapping, int64_t num_tokens, int64_t num_slots,
+                       hipStream_t stream) {
+  std::vector<int64_t> h((size_t)num_tokens);
+  if (int e = hip_status(hipMemcpyAsync(h.data(), slot_mapping, (size_t)num_tokens * sizeof(int64_t),
+                                        hipMemcpyDeviceToHost, stream), what))
+    return e;
+  if (int e = hip_status(hipStreamSynchronize(stream), what)) return e;
+  std::unordered_map<int64_t, int64_t> first;
+  first.reserve((size_t)num_tokens);
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const int64_t sl = h[(size_t)t];
+    if (sl < 0 || sl >= num_slots) continue;          // skipped by the kernel
+    auto ins = first.emplace(sl, t);
+    if (!ins.second)
+      return fail(KV4_EINVAL, "%s: slot %lld appears at tokens %lld and %lld", what, (long long)sl,
+                  (long long)ins.first->second, (long long)t);
+  }
+  return KV4_OK;
+}
+
 int write_impl(int qm, const char* what, const void* key, const void* value, int64_t key_token_stride,
                int64_t value_token_stride, void* key_cache, void* value_cache, float* k_scale_cache,
                float* v_scale_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
@@ -310,6 +335,11 @@ int write_impl(int qm, const char* what, const void* key, const void* value, int
   const kv4::CacheLayout lay =
       layout ? *layout : kv4::packed_layout(num_kv_heads, (int)code_row_bytes(qm, head_size), block_size);
   if (int e = check_layout(qm, lay)) return e;
+  if (env_long("KV4_CHECK_SLOTS", 0) != 0) {
+    if (int e = check_unique_slots(what, slot_mapping, num_tokens, num_blocks * block_size,
+                                   static_cast<hipStream_t>(stream)))
+      return e;
+  }
   kv4::WriteArgs a;
   a.key = static_cast<const uint16_t*>(key);
   a.value = static_cast<const uint16_t*>(value);

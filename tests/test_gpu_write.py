@@ -130,3 +130,30 @@ def test_dequant_matches_oracle(hs):
     x = key.float().numpy()[::3]
     bad = np.abs(back[:-2] - x) > 0.5 + 0.5 * np.abs(x)
     assert bad.mean() < 1e-3
+
+
+def test_duplicate_slots_debug_check(monkeypatch):
+    """KV4_CHECK_SLOTS=1: a slot map that names one slot twice is rejected
+    before any launch (the cache keeps its fill); without the variable the
+    call runs (duplicates race, by contract); a map without duplicates passes
+    the check and is written bit-exactly."""
+    T, nkv, hs, bs, nb = 40, 2, 64, 16, 4
+    key = W.normal_bf16((T, nkv, hs), seed=5)
+    value = W.normal_bf16((T, nkv, hs), seed=6)
+    dup = np.arange(T, dtype=np.int64)
+    dup[17] = dup[3]
+    dup[20] = -1                      # skipped slots are not duplicates
+    dup[21] = -1
+    w = W.custom("dup", nkv, nkv, hs, [1], [1], block_size=bs)
+    kc, vc, ks, vs = alloc_cache(w, nb, 0xA5)
+    monkeypatch.setenv("KV4_CHECK_SLOTS", "1")
+    with pytest.raises(kv4.Kv4Error, match="slot 3 appears at tokens 3 and 17"):
+        kv4.kv4_rht_write(key.to(DEV), value.to(DEV), kc, vc, ks, vs, torch.from_numpy(dup).to(DEV), sign_seed=1)
+    torch.cuda.synchronize()
+    assert (host(kc) == 0xA5).all() and (host(vc) == 0xA5).all()
+    uniq = np.random.default_rng(0).permutation(nb * bs)[:T].astype(np.int64)
+    uniq[5] = -1
+    _write_and_compare(key, value, uniq, nb, bs, seed=1)
+    monkeypatch.delenv("KV4_CHECK_SLOTS")
+    kv4.kv4_rht_write(key.to(DEV), value.to(DEV), kc, vc, ks, vs, torch.from_numpy(dup).to(DEV), sign_seed=1)
+    torch.cuda.synchronize()
