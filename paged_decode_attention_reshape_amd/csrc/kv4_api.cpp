@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -67,7 +68,8 @@ constexpr int64_t kTargetUnitsValu = 2048;
 constexpr int64_t kTargetUnitsMfma = 16384;
 constexpr int kMinSplit = 256;
 constexpr int kSkMaxGrid = 2048;        // stream-K workgroups at most (8 per CU of a 256-CU GPU)
-constexpr int kSkMinSteps = 16;         // stream-K: KV steps per workgroup at least
+constexpr int kSkMinSteps = 16;         // stream-K: KV steps per workgroup at least ...
+constexpr int kSkMinGrid = 512;         // ... unless that leaves fewer than 2 workgroups per CU (256 CUs)
 constexpr bool kPthMfma = true;        // matrix-core kernels for the int8 / fp8 caches
 constexpr int64_t kReduceRowsMinWaves = 2048;   // merge: one row per lane group from this many waves
 
@@ -154,7 +156,10 @@ int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_
     p.sk_quads = nkv / p.hpw / p.wpb;
     const int64_t quads = p.sk_quads;
     const int64_t max_steps = quads * num_seqs * (((int64_t)(max_seq_len < 1 ? 1 : max_seq_len) + 31) / 32);
-    int64_t cap = max_steps / kSkMinSteps;                      // at least kSkMinSteps steps per workgroup
+    // at least kSkMinSteps steps per workgroup, but two workgroups per CU
+    // where the LDS holds them (measured: Phi-3-shaped decode, 16 steps per
+    // workgroup on 256 workgroups 3 % slower than 8 on 512)
+    int64_t cap = std::max<int64_t>(max_steps / kSkMinSteps, std::min<int64_t>(kSkMinGrid, max_steps));
     const long forced = env_long("KV4_SK_GRID", 0);
     if (forced > 0) cap = forced;
     p.sk_pcap = (int)std::max<int64_t>(1, std::min<int64_t>(cap, kSkMaxGrid));
