@@ -450,13 +450,21 @@ __device__ __forceinline__ void dma(const void* g, void* l, int size) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
-template <int SIZE>
+// AUX is the load's cache-policy field: 0 = default, 2 = non-temporal (nt).
+template <int SIZE, int AUX = 0>
 __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* l) {
-  if constexpr (SIZE == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 1, voff, 0, 0, 0);
-  else if constexpr (SIZE == 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 2, voff, 0, 0, 0);
-  else if constexpr (SIZE == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 4, voff, 0, 0, 0);
-  else if constexpr (SIZE == 12) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 12, voff, 0, 0, 0);
-  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 16, voff, 0, 0, 0);
+  if constexpr (SIZE == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 1, voff, 0, 0, AUX);
+  else if constexpr (SIZE == 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 2, voff, 0, 0, AUX);
+  else if constexpr (SIZE == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 4, voff, 0, 0, AUX);
+  else if constexpr (SIZE == 12) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 12, voff, 0, 0, AUX);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 16, voff, 0, 0, AUX);
+}
+// K/V code loads: non-temporal where the host found that no other wave reads
+// the same cache lines (the flag is uniform, so this is a scalar branch).
+template <int SIZE>
+__device__ __forceinline__ void dma_code(bool nt, __amdgpu_buffer_rsrc_t r, uint32_t voff, void* l) {
+  if (nt) dma_buf<SIZE, 2>(r, voff, l);
+  else dma_buf<SIZE, 0>(r, voff, l);
 }
 
 // s_waitcnt with only the vector-memory counter (gfx9 encoding).
@@ -581,6 +589,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
   const int64_t page_bytes = a.lay.blk;                     // one page of one cache
   const int64_t page_rows = a.lay.sblk;                     // scale floats per page
   const int64_t s_tok = a.lay.stok, s_head = a.lay.shead;   // scale floats per token row / head
+  const bool code_nt = a.code_nt != 0;                      // K/V code loads non-temporal
   const uint32_t koff = (uint32_t)n * tok_stride + (uint32_t)q4 * (HALF / 4);
   uint32_t vo[4];                                           // token 4*q4 + i, 32-bit column chunk n
 #pragma unroll
@@ -866,9 +875,9 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
           for (int j = 0; j < SG::NKL; ++j) {
             unsigned char* dst = sth + SG::K_OFF + h * SG::KHALF + j * SG::KREG;
             const uint32_t o = koff + j * SG::KSZ + hl * head_bytes;
-            if constexpr (SG::KSZ == 16) dma_buf<16>(rk[h], o, dst);
-            else if constexpr (SG::KSZ == 12) dma_buf<12>(rk[h], o, dst);
-            else dma_buf<4>(rk[h], o, dst);
+            if constexpr (SG::KSZ == 16) dma_code<16>(code_nt, rk[h], o, dst);
+            else if constexpr (SG::KSZ == 12) dma_code<12>(code_nt, rk[h], o, dst);
+            else dma_code<4>(code_nt, rk[h], o, dst);
           }
         dma(scp + hl * s_head, sth + SG::S_OFF, 4);
       }
@@ -881,24 +890,24 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int j = 0; j < StageGeoQ<HS>::VL; ++j)
-            dma_buf<16>(rv[hh], vq_src[j], st + SG::V_OFF + hh * StageGeoQ<HS>::VHALF + j * 1024);
+            dma_code<16>(code_nt, rv[hh], vq_src[j], st + SG::V_OFF + hh * StageGeoQ<HS>::VHALF + j * 1024);
       } else if constexpr (VJH) {
 #pragma unroll
         for (int hl = 0; hl < HPW; ++hl)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
-            dma_buf<16>(rv[hh], vjh_src + hl * head_bytes, st + hl * STH + SG::V_OFF + hh * 1024);
+            dma_code<16>(code_nt, rv[hh], vjh_src + hl * head_bytes, st + hl * STH + SG::V_OFF + hh * 1024);
       } else if constexpr (VP) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int j = 0; j < VPL; ++j) dma_buf<16>(rv[hh], vp_src[j], vp_base(st, hh) + j * 1024);
+          for (int j = 0; j < VPL; ++j) dma_code<16>(code_nt, rv[hh], vp_src[j], vp_base(st, hh) + j * 1024);
       } else if constexpr (VJ) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int j = 0; j < 16 / RPI; ++j)
-            dma_buf<16>(rv[hh], vj_src + (uint32_t)(j * RPI) * tok_stride, vj_base(st, hh) + j * 1024);
+            dma_code<16>(code_nt, rv[hh], vj_src + (uint32_t)(j * RPI) * tok_stride, vj_base(st, hh) + j * 1024);
       } else {
 #pragma unroll
         for (int hl = 0; hl < HPW; ++hl) {
@@ -908,10 +917,10 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
             unsigned char* dst = sth + SG::V_OFF + i * SG::VBYTES_TOK;
             const uint32_t o = vo[i & 3] + hl * head_bytes;
 #pragma unroll
-            for (int r = 0; r < GG::RDW; ++r) dma_buf<4>(rv[i >> 2], o + 64 * r, dst + r * 256);
-            if constexpr (GG::RUS) dma_buf<2>(rv[i >> 2], o - 2u * n + 64 * GG::RDW, dst + GG::RDW * 256);
+            for (int r = 0; r < GG::RDW; ++r) dma_code<4>(code_nt, rv[i >> 2], o + 64 * r, dst + r * 256);
+            if constexpr (GG::RUS) dma_code<2>(code_nt, rv[i >> 2], o - 2u * n + 64 * GG::RDW, dst + GG::RDW * 256);
             if constexpr (GG::RBY)
-              dma_buf<1>(rv[i >> 2], o - 3u * n + 64 * GG::RDW + 32 * GG::RUS,
+              dma_code<1>(code_nt, rv[i >> 2], o - 3u * n + 64 * GG::RDW + 32 * GG::RUS,
                          dst + (GG::RDW + GG::RUS) * 256);
           }
         }

@@ -132,6 +132,11 @@ SCHED = {
     # the sequences' prefix from the separate plan kernel instead of in-kernel
     "streamk_plan_kernel": {"KV4_FUSED_PLAN": "0"},
     "splits64_plan_kernel": {"KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64", "KV4_FUSED_PLAN": "0"},
+    # K/V code loads with the non-temporal hint forced on and off (the host
+    # sets it only where a wave's lines are its own)
+    "streamk_nt_on": {"KV4_NT": "1"},
+    "splits64_nt_on": {"KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64", "KV4_NT": "1"},
+    "streamk_nt_off": {"KV4_NT": "0"},
 }
 
 
@@ -329,6 +334,7 @@ RB_CASES = [
 
 RB_SCHED = {
     "rb2": {},
+    "rb2_nt_on": {"KV4_NT": "1"},
     "rb2_grid3": {"KV4_SK_GRID": "3"},
     "rb2_splits64": {"KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64"},
     "rb1": {"KV4_MFMA_RB": "1"},
@@ -349,6 +355,35 @@ def test_row_blocks_per_wave(case, sched, monkeypatch):
     r = run_gpu(W.custom(name, nq, nkv, hs, ql, sl, block_size=bs))
     _g1(r)
     _g2(r)
+
+
+NT_CASES = [
+    # name, nq, nkv, hs, query_lens, seq_lens, block_size (int4)
+    ("g4_nkv8_hs128_hpw2", 32, 8, 128, [1] * 4, [1000, 17, 2049, 300], 16),
+    ("g8_nkv2_hs128", 16, 2, 128, [1] * 3, [250, 16, 1100], 32),
+    ("g4_nkv8_hs128_q3", 32, 8, 128, [3, 1, 2], [700, 40, 129], 16),
+    ("g4_nkv4_hs192", 16, 4, 192, [1] * 2, [333, 640], 16),
+    ("g4_nkv8_hs64", 32, 8, 64, [1] * 3, [513, 64, 700], 16),
+]
+
+
+@pytest.mark.parametrize("case", NT_CASES, ids=[c[0] for c in NT_CASES])
+def test_nontemporal_hint_leaves_results_unchanged(case, monkeypatch):
+    """The non-temporal hint on the K/V code loads is a cache policy only: the
+    output with it forced on is bit-identical to the output with it off, and
+    both meet the oracle."""
+    name, nq, nkv, hs, ql, sl, bs = case
+    w = W.custom(name, nq, nkv, hs, ql, sl, block_size=bs)
+    monkeypatch.setenv("KV4_NT", "0")
+    r = run_gpu(w)
+    _g2(r)
+    monkeypatch.setenv("KV4_NT", "1")
+    out_nt = kv4.kv4_paged_attention(
+        r.t.query.to(DEV), r.kc, r.vc, r.ks, r.vs, torch.from_numpy(r.lay.block_table).to(DEV),
+        torch.from_numpy(r.lay.seq_lens).to(DEV), torch.from_numpy(r.lay.query_start_loc).to(DEV),
+        max_query_len=w.max_query_len, max_seq_len=w.max_seq_len, sign_seed=w.sign_seed)
+    torch.cuda.synchronize()
+    assert torch.equal(out_nt.view(torch.int16), r.out.view(torch.int16))
 
 
 @pytest.mark.parametrize("sched", ["streamk", "splits64"])

@@ -97,6 +97,8 @@ SCHED = {
     "streamk_grid3": {"KV4_SK_GRID": "3"},
     "splits64": {"KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64"},
     "split100": {"KV4_SPLIT_TOKENS": "100"},
+    "streamk_nt_on": {"KV4_NT": "1"},
+    "streamk_nt_off": {"KV4_NT": "0"},
 }
 
 
