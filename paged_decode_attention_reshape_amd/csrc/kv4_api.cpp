@@ -276,9 +276,15 @@ int64_t code_row_bytes(int qm, int32_t head_size) { return qm ? head_size : head
 // are split between waves (int4 at head sizes 64, 96 and 192, or the
 // inline-scale layout) the hint measured 12-28 % slower, with up to 39 % more
 // bytes fetched from HBM, so it stays off there.
+// The kernels are built with the hint at head size 128 only: int4 with two or
+// four adjacent heads per wave, int8 / fp8 (one head of 128 bytes per wave).
+bool nt_kernel_built(int qm, int32_t head_size, const kv4::AttnPlan& p) {
+  return p.path == 1 && head_size == 128 && (qm != 0 || (p.hpw >= 2 && !p.vjh && p.rb == 1));
+}
+
 bool code_lines_private(int qm, int32_t head_size, const kv4::AttnPlan& p, const kv4::CacheLayout& lay,
                         const void* key_cache, const void* value_cache) {
-  if (p.path != 1 || p.n_head_tiles != 1 || p.tiles_per_seq != 1) return false;
+  if (!nt_kernel_built(qm, head_size, p) || p.n_head_tiles != 1 || p.tiles_per_seq != 1) return false;
   const int64_t cb = code_row_bytes(qm, head_size);
   const int64_t span = (p.hpw > 1 && lay.head == cb) ? p.hpw * cb : cb;   // bytes one wave reads per row
   const bool heads_ok = (p.hpw > 1 && lay.head == cb) ? true : lay.head % 128 == 0;
@@ -526,7 +532,8 @@ int attention_impl(int qm, const void* query, int64_t query_token_stride, const 
   a.prefix = prefix;
   a.window = window;
   a.code_nt = code_lines_private(qm, head_size, a.plan, a.lay, key_cache, value_cache) ? 1 : 0;
-  if (const long f = env_long("KV4_NT", -1); f == 0 || f == 1) a.code_nt = (int)f;
+  if (const long f = env_long("KV4_NT", -1); f == 0 || f == 1)
+    a.code_nt = (f == 1 && nt_kernel_built(qm, head_size, a.plan)) ? 1 : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.plan.path == 1) {
     const int64_t max_units =

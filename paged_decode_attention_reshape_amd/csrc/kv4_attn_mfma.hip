@@ -459,13 +459,6 @@ __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff,
   else if constexpr (SIZE == 12) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 12, voff, 0, 0, AUX);
   else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 16, voff, 0, 0, AUX);
 }
-// K/V code loads: non-temporal where the host found that no other wave reads
-// the same cache lines (the flag is uniform, so this is a scalar branch).
-template <int SIZE>
-__device__ __forceinline__ void dma_code(bool nt, __amdgpu_buffer_rsrc_t r, uint32_t voff, void* l) {
-  if (nt) dma_buf<SIZE, 2>(r, voff, l);
-  else dma_buf<SIZE, 0>(r, voff, l);
-}
 
 // s_waitcnt with only the vector-memory counter (gfx9 encoding).
 template <int N>
@@ -512,13 +505,18 @@ constexpr int mfma_wpe() {
 // WIN: built with the sliding-window terms (calls without a window run the
 // kernel without them).
 //
+// NT: the K and V code loads carry the non-temporal cache policy. The host
+// asks for it where every 128-byte line a wave loads is loaded by that wave
+// alone; built for head size 128 (int4 with two or four adjacent heads per
+// wave, int8 / fp8).
+//
 // NRB (int4, one kv head per wave): 16-row MFMA blocks per wave. With NRB = 2
 // one wave serves 32 query rows (a prefill tile, or a multi-token decode
 // block of up to 32 / G tokens); the K and V codes of a step become
 // operands once and feed both blocks' products, and each block keeps its own
 // softmax state (the v_scale exponent e is shared: it depends on the keys
 // only).
-template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB>
+template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB, bool NT = false>
 __global__ __launch_bounds__((64 * mfma_wpb<HS, HPW, QM>()))
 __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfma_kernel(AttnArgs a,
                                                                                       const int32_t* prefix) {
@@ -589,7 +587,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
   const int64_t page_bytes = a.lay.blk;                     // one page of one cache
   const int64_t page_rows = a.lay.sblk;                     // scale floats per page
   const int64_t s_tok = a.lay.stok, s_head = a.lay.shead;   // scale floats per token row / head
-  const bool code_nt = a.code_nt != 0;                      // K/V code loads non-temporal
+  constexpr int CA = NT ? 2 : 0;                            // cache policy of the K/V code loads
   const uint32_t koff = (uint32_t)n * tok_stride + (uint32_t)q4 * (HALF / 4);
   uint32_t vo[4];                                           // token 4*q4 + i, 32-bit column chunk n
 #pragma unroll
@@ -875,9 +873,9 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
           for (int j = 0; j < SG::NKL; ++j) {
             unsigned char* dst = sth + SG::K_OFF + h * SG::KHALF + j * SG::KREG;
             const uint32_t o = koff + j * SG::KSZ + hl * head_bytes;
-            if constexpr (SG::KSZ == 16) dma_code<16>(code_nt, rk[h], o, dst);
-            else if constexpr (SG::KSZ == 12) dma_code<12>(code_nt, rk[h], o, dst);
-            else dma_code<4>(code_nt, rk[h], o, dst);
+            if constexpr (SG::KSZ == 16) dma_buf<16, CA>(rk[h], o, dst);
+            else if constexpr (SG::KSZ == 12) dma_buf<12, CA>(rk[h], o, dst);
+            else dma_buf<4, CA>(rk[h], o, dst);
           }
         dma(scp + hl * s_head, sth + SG::S_OFF, 4);
       }
@@ -890,24 +888,24 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int j = 0; j < StageGeoQ<HS>::VL; ++j)
-            dma_code<16>(code_nt, rv[hh], vq_src[j], st + SG::V_OFF + hh * StageGeoQ<HS>::VHALF + j * 1024);
+            dma_buf<16, CA>(rv[hh], vq_src[j], st + SG::V_OFF + hh * StageGeoQ<HS>::VHALF + j * 1024);
       } else if constexpr (VJH) {
 #pragma unroll
         for (int hl = 0; hl < HPW; ++hl)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
-            dma_code<16>(code_nt, rv[hh], vjh_src + hl * head_bytes, st + hl * STH + SG::V_OFF + hh * 1024);
+            dma_buf<16, CA>(rv[hh], vjh_src + hl * head_bytes, st + hl * STH + SG::V_OFF + hh * 1024);
       } else if constexpr (VP) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int j = 0; j < VPL; ++j) dma_code<16>(code_nt, rv[hh], vp_src[j], vp_base(st, hh) + j * 1024);
+          for (int j = 0; j < VPL; ++j) dma_buf<16, CA>(rv[hh], vp_src[j], vp_base(st, hh) + j * 1024);
       } else if constexpr (VJ) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int j = 0; j < 16 / RPI; ++j)
-            dma_code<16>(code_nt, rv[hh], vj_src + (uint32_t)(j * RPI) * tok_stride, vj_base(st, hh) + j * 1024);
+            dma_buf<16, CA>(rv[hh], vj_src + (uint32_t)(j * RPI) * tok_stride, vj_base(st, hh) + j * 1024);
       } else {
 #pragma unroll
         for (int hl = 0; hl < HPW; ++hl) {
@@ -917,10 +915,10 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
             unsigned char* dst = sth + SG::V_OFF + i * SG::VBYTES_TOK;
             const uint32_t o = vo[i & 3] + hl * head_bytes;
 #pragma unroll
-            for (int r = 0; r < GG::RDW; ++r) dma_code<4>(code_nt, rv[i >> 2], o + 64 * r, dst + r * 256);
-            if constexpr (GG::RUS) dma_code<2>(code_nt, rv[i >> 2], o - 2u * n + 64 * GG::RDW, dst + GG::RDW * 256);
+            for (int r = 0; r < GG::RDW; ++r) dma_buf<4, CA>(rv[i >> 2], o + 64 * r, dst + r * 256);
+            if constexpr (GG::RUS) dma_buf<2, CA>(rv[i >> 2], o - 2u * n + 64 * GG::RDW, dst + GG::RDW * 256);
             if constexpr (GG::RBY)
-              dma_code<1>(code_nt, rv[i >> 2], o - 3u * n + 64 * GG::RDW + 32 * GG::RUS,
+              dma_buf<1, CA>(rv[i >> 2], o - 3u * n + 64 * GG::RDW + 32 * GG::RUS,
                          dst + (GG::RDW + GG::RUS) * 256);
           }
         }
@@ -1392,14 +1390,14 @@ static bool plan_lds_fits(const void* kernel, int resident) {
 }
 
 // Workgroups of the kernel the GPU holds at once (fused: with the plan LDS).
-template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB = 1>
+template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB = 1, bool NT = false>
 static int resident_blocks(bool fused) {
   static int per_cu[2] = {0, 0};
   int& pc = per_cu[fused ? 1 : 0];
   if (pc == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb,
-                                                     reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH, WIN, NRB>),
+                                                     reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH, WIN, NRB, NT>),
                                                      64 * mfma_wpb<HS, HPW, QM>(), fused ? kFusedPlanLds : 0) != hipSuccess ||
         nb < 1)
       nb = 1;
@@ -1438,6 +1436,13 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
                        prefix);
   };
   if constexpr (QM != 0) {
+    if constexpr (HS == 128) {
+      if (a.code_nt) {
+        go(attn_mfma_kernel<HS, 1, QM, false, WIN, 1, true>, mfma_wpb<HS, 1, QM>(),
+           [](bool f) { return resident_blocks<HS, 1, QM, false, WIN, 1, true>(f); });
+        return hipSuccess;
+      }
+    }
     go(attn_mfma_kernel<HS, 1, QM, false, WIN, 1>, mfma_wpb<HS, 1, QM>(), [](bool f) { return resident_blocks<HS, 1, QM, false, WIN>(f); });
     return hipSuccess;
   }
@@ -1460,6 +1465,18 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
       return hipSuccess;
     }
     return hipErrorInvalidValue;
+  }
+  if constexpr (HS == 128) {
+    if (a.code_nt && a.plan.hpw == 2) {
+      go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1, true>, mfma_wpb<HS, 2, 0>(),
+         [](bool f) { return resident_blocks<HS, 2, 0, false, WIN, 1, true>(f); });
+      return hipSuccess;
+    }
+    if (a.code_nt && a.plan.hpw == 4) {
+      go(attn_mfma_kernel<HS, 4, 0, false, WIN, 1, true>, mfma_wpb<HS, 4, 0>(),
+         [](bool f) { return resident_blocks<HS, 4, 0, false, WIN, 1, true>(f); });
+      return hipSuccess;
+    }
   }
   switch (a.plan.hpw) {
     case 2: go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1>, mfma_wpb<HS, 2, 0>(), [](bool f) { return resident_blocks<HS, 2, 0, false, WIN>(f); }); break;

@@ -146,7 +146,7 @@ struct AttnArgs {
   CacheLayout lay;         // shared by the K and V caches and their scales
   int window;              // sliding window: the query at position p sees keys (p - window, p]; 0 = none
   int reduce_rows;         // merge: one row per lane group (few partials per row) instead of per wave
-  int code_nt;             // MFMA path: K/V code loads carry the non-temporal hint
+  int code_nt;             // MFMA path: K/V code loads carry the non-temporal hint (head size 128 kernels)
   AttnPlan plan;
 };
 

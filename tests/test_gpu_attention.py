@@ -334,7 +334,6 @@ RB_CASES = [
 
 RB_SCHED = {
     "rb2": {},
-    "rb2_nt_on": {"KV4_NT": "1"},
     "rb2_grid3": {"KV4_SK_GRID": "3"},
     "rb2_splits64": {"KV4_STREAMK": "0", "KV4_SPLIT_TOKENS": "64"},
     "rb1": {"KV4_MFMA_RB": "1"},
@@ -358,22 +357,23 @@ def test_row_blocks_per_wave(case, sched, monkeypatch):
 
 
 NT_CASES = [
-    # name, nq, nkv, hs, query_lens, seq_lens, block_size (int4)
-    ("g4_nkv8_hs128_hpw2", 32, 8, 128, [1] * 4, [1000, 17, 2049, 300], 16),
-    ("g8_nkv2_hs128", 16, 2, 128, [1] * 3, [250, 16, 1100], 32),
-    ("g4_nkv8_hs128_q3", 32, 8, 128, [3, 1, 2], [700, 40, 129], 16),
-    ("g4_nkv4_hs192", 16, 4, 192, [1] * 2, [333, 640], 16),
-    ("g4_nkv8_hs64", 32, 8, 64, [1] * 3, [513, 64, 700], 16),
+    # name, nq, nkv, hs, query_lens, seq_lens, block_size, kv heads per wave (int4)
+    ("g4_nkv8_hs128_hpw2", 32, 8, 128, [1] * 4, [1000, 17, 2049, 300], 16, "2"),
+    ("g4_nkv8_hs128_hpw4", 32, 8, 128, [1] * 4, [1000, 17, 2049, 300], 16, "4"),
+    ("g8_nkv2_hs128_bs32", 16, 2, 128, [1] * 3, [250, 16, 1100], 32, "2"),
+    ("g2_nkv4_hs128_hpw4", 8, 4, 128, [1] * 5, [1, 64, 513, 31, 700], 16, "4"),
 ]
 
 
 @pytest.mark.parametrize("case", NT_CASES, ids=[c[0] for c in NT_CASES])
 def test_nontemporal_hint_leaves_results_unchanged(case, monkeypatch):
     """The non-temporal hint on the K/V code loads is a cache policy only: the
-    output with it forced on is bit-identical to the output with it off, and
-    both meet the oracle."""
-    name, nq, nkv, hs, ql, sl, bs = case
+    output of the kernel built with it is bit-identical to the output of the
+    kernel built without it, and both meet the oracle."""
+    name, nq, nkv, hs, ql, sl, bs, hpw = case
     w = W.custom(name, nq, nkv, hs, ql, sl, block_size=bs)
+    monkeypatch.setenv("KV4_FORCE_PATH", "mfma")
+    monkeypatch.setenv("KV4_MFMA_HPW", hpw)
     monkeypatch.setenv("KV4_NT", "0")
     r = run_gpu(w)
     _g2(r)
