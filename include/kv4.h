@@ -155,11 +155,16 @@ size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs
  * A query row whose causal window is empty (seq_len < query_len) gets zeros.
  *
  * The launch plan (matrix-core or vector path, KV split size, kv heads per
- * matrix-core wave) is chosen on the host from the sizes above. Three
- * environment variables, read at each call, override it for testing and
- * tuning: KV4_FORCE_PATH=valu|mfma, KV4_SPLIT_TOKENS=<tokens per split>,
- * KV4_MFMA_HPW=1|2|4 (lowered where the shape does not allow it). Results
- * agree within the rounding of the float32 accumulation order.
+ * matrix-core wave) is chosen on the host from the sizes above. Environment
+ * variables, read at each call, override it for testing and tuning:
+ * KV4_FORCE_PATH=valu|mfma, KV4_SPLIT_TOKENS=<tokens per split>,
+ * KV4_MFMA_HPW=1|2|4 (lowered where the shape does not allow it),
+ * KV4_STREAMK=0 (split-KV instead of the stream-K decode schedule),
+ * KV4_SK_GRID=<stream-K workgroups at most>, KV4_MFMA_RB=1 (one 16-row block
+ * per wave), KV4_REDUCE_ROWS=0|1 (merge form), KV4_FUSED_PLAN=0 (separate
+ * plan kernel), KV4_NT=0|1 (non-temporal K/V code loads, where a kernel is
+ * built with them). Results agree within the rounding of the float32
+ * accumulation order; KV4_NT and KV4_FUSED_PLAN leave them bit-identical.
  * kv4_paged_attention_workspace_size reads the same variables: query it with
  * the same environment the call will see.
  */
