@@ -52,6 +52,49 @@ __device__ __forceinline__ void rint_quotients(const float (&y)[8], float scale,
   }
 }
 
+// Packed int4 codes (element e in bits 4e..4e+3) of the quotients sg * v[e] /
+// scale, scale > 0, sg = +1 or -1 (rint is odd, so the sign goes on the
+// quotient). Fast path (normal scales): t = v * (sg * rcp(scale)); the sum t +
+// 1.5 * 2^23 is 1.5 * 2^23 + rint_half_even(t) exactly (|t| < 2^22, unit
+// spacing there), so for |t| <= 8 the low nibble of its bit pattern is the
+// two's-complement code. A normal scale keeps |t| <= 7 up to rounding, so the
+// clamp to [-8, 7] cannot act there. As in rint_quotients, a lane with a t
+// within 2^-16 of a half-integer redoes its 8 codes with the correctly rounded
+// division, clamped (a subnormal scale can give |y / scale| > 7.5).
+__device__ __forceinline__ uint32_t int4_codes(const float (&v)[8], float scale, float sg, bool fast) {
+  constexpr float kRound = 12582912.0f;   // 1.5 * 2^23
+  constexpr float tie = 0.5f - 0x1p-16f;
+  uint32_t packed = 0;
+  bool redo = !fast;
+  if (fast) {
+    const float r = __builtin_amdgcn_rcpf(scale) * sg;
+    uint32_t u[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = v[e] * r;
+      const float f = t + kRound;
+      redo |= fabsf(t - (f - kRound)) >= tie;
+      u[e] = __float_as_uint(f);
+    }
+    // byte 0 of the even elements' patterns into one word and of the odd
+    // ones into another (v_perm_b32: selector 0-3 picks a byte of the second
+    // operand, 4-7 of the first, 12 a zero byte), then each byte's low
+    // nibble from the even word and high nibble from the odd one
+    const uint32_t ev = __builtin_amdgcn_perm(u[2], u[0], 0x0C0C0400u) | __builtin_amdgcn_perm(u[6], u[4], 0x04000C0Cu);
+    const uint32_t od = __builtin_amdgcn_perm(u[3], u[1], 0x0C0C0400u) | __builtin_amdgcn_perm(u[7], u[5], 0x04000C0Cu);
+    packed = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+  }
+  if (redo) {
+    packed = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float q = fminf(fmaxf(__builtin_rintf(v[e] / scale) * sg, -8.0f), 7.0f);
+      packed |= ((uint32_t)(int)q & 0xFu) << (4 * e);
+    }
+  }
+  return packed;
+}
+
 // The radix-2 Walsh-Hadamard butterflies of the write path with the sign of
 // each cross-lane stage carried instead of applied: at the stage pairing
 // lane j with lane j ^ d, both lanes have taken the same upper / lower roles
@@ -63,8 +106,12 @@ __device__ __forceinline__ void rint_quotients(const float (&y)[8], float scale,
 // values are sign * v, each element rounded exactly as in fwht_b_ct.
 template <int D>
 __device__ __forceinline__ void fwht8_xlane_lazy(float (&v)[8], float sgn) {
+  float p[8];   // all 8 exchanges in flight before the first use
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = fmaf(xor_lane<D>(v[e]), sgn, v[e]);
+  for (int e = 0; e < 8; ++e) p[e] = xor_lane<D>(v[e]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = fmaf(p[e], sgn, v[e]);
 }
 template <int LPMAX>
 __device__ __forceinline__ float fwht_b_lazy(float (&v)[8], int b, int jj) {
@@ -203,16 +250,7 @@ __global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
     if constexpr (QM == 0) {
       const float scale = amax / 7.0f;
       const bool fast = scale >= 0x1p-126f && scale <= 0x1p126f;
-      uint32_t packed = 0;
-      if (scale > 0.0f) {
-        float q[8];
-        rint_quotients<8>(v, scale, fast, q);
-        // |q| <= 7 (the largest |y| is amax = 7 scale up to rounding): the
-        // clamp to [-8, 7] never acts, and -q codes -y
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          packed |= ((uint32_t)(int)fminf(fmaxf(q[e] * sg, -8.0f), 7.0f) & 0xFu) << (4 * e);
-      }
+      const uint32_t packed = scale > 0.0f ? int4_codes(v, scale, sg, fast) : 0u;
       if (ok && lane_on) {
         uint8_t* cache = kind ? a.value_cache : a.key_cache;
         const int64_t pg = slot_page(a, slot), tk = slot - pg * a.bs;

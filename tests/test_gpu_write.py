@@ -86,6 +86,36 @@ def test_write_zero_outlier_and_extreme_vectors():
     _write_and_compare(key, value, slots, T // bs, bs, seed=42)
 
 
+@pytest.mark.parametrize("hs", [128, 96])
+def test_write_exact_ties(hs):
+    """Vectors whose rotated values are 7 * 2^k on one element and half-integer
+    multiples of 2^k on three others (inputs from the oracle's exact inverse
+    rotation, exact in bf16): scale = 2^k exactly, so every nonzero quotient
+    y / scale is a whole or half integer and the codes of the halves are
+    decided by ties to even, for K and for -K (the negated vectors)."""
+    say(f"[gpu] write exact ties hs={hs}")
+    T, nkv, bs, seed = 48, 2, 16, 42
+    rng = np.random.default_rng(17 + hs)
+    y = np.zeros((T, nkv, hs))
+    for t in range(T):
+        for h in range(nkv):
+            idx = rng.choice(hs, 4, replace=False)
+            y[t, h, idx[0]] = 7.0 * rng.choice([-1.0, 1.0])
+            y[t, h, idx[1:]] = rng.integers(-14, 15, 3) / 2.0
+            y[t, h] *= 2.0 ** int(rng.integers(-20, 21))
+    x = O.unrotate_math(y, O.rht_signs(seed, hs)).astype(np.float32)
+    assert np.array_equal(O.bf16_round(x), x)             # exact inputs
+    yr = O.rotate_spec(x, O.rht_signs(seed, hs))
+    assert np.array_equal(yr, y.astype(np.float32))       # the rotation lands on y exactly
+    _, scale = O.quantize_int4(yr)
+    q = yr / scale[..., None]
+    assert (np.abs(q - np.floor(q)) == 0.5).sum() > T      # exact ties are present
+    key = torch.from_numpy(x).to(torch.bfloat16)
+    value = (-key.float()).to(torch.bfloat16)
+    slots = np.random.default_rng(5).permutation(T).astype(np.int64)
+    _write_and_compare(key, value, slots, T // bs, bs, seed=seed)
+
+
 def test_write_many_tokens():
     say("[gpu] write 40000 tokens")
     T, nkv, hs, bs = 40000, 8, 64, 16
