@@ -169,8 +169,9 @@ __device__ __forceinline__ int64_t slot_page(const Args& a, int64_t slot) {
   return a.bs_shift >= 0 ? (slot >> a.bs_shift) : slot / a.bs;
 }
 
+// At most 96 scalar registers: eight waves per SIMD (101 left it at seven).
 template <int LP, int QM>
-__global__ __launch_bounds__(256) void write_kernel(WriteArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96))) void write_kernel(WriteArgs a) {
   constexpr int VPW = kWave / LP;                      // vectors per wave
   const int lane = threadIdx.x & (kWave - 1);
   const int jj = lane & (LP - 1);                      // chunk index in the vector
