@@ -272,19 +272,29 @@ def _causal_softmax_attend(logits: np.ndarray, vals: np.ndarray, L: int, window:
     """logits [ql, ..., L]: row i (query i of ql, position pos = L - ql + i)
     may see keys 0 .. pos, and with a sliding window W > 0 only keys j with
     pos - W < j <= pos (the W most recent); returns softmax(logits) @ vals
-    with vals [L, hs]."""
+    with vals [L, hs]. A row that sees no key at all (pos < 0: the sequence
+    is shorter than its query block) is exactly 0 -- the reading taken for
+    an empty causal window, where the softmax has no terms."""
     ql = logits.shape[0]
+    hs = vals.shape[-1]
     pos = L - ql + np.arange(ql)
     keys = np.arange(L)[None, :]
     mask = keys > pos[:, None]                                    # [ql, L]
     if window > 0:
         mask |= keys <= pos[:, None] - window
+    empty = mask.all(axis=-1)                                     # [ql]; all True when L == 0
+    if empty.all():
+        return np.zeros(logits.shape[:-1] + (hs,))
     mask = mask.reshape((ql,) + (1,) * (logits.ndim - 2) + (L,))
+    # an empty row gets one unmasked key for the arithmetic and is zeroed below
+    mask = mask & ~empty.reshape((ql,) + (1,) * (logits.ndim - 1))
     lg = np.where(mask, -np.inf, logits)
     m = lg.max(axis=-1, keepdims=True)
     p = np.exp(lg - m)
     p /= p.sum(axis=-1, keepdims=True)
-    return p @ vals
+    out = p @ vals
+    out[empty] = 0.0
+    return out
 
 
 def paged_attention(query, key_cache, value_cache, k_scale_cache, v_scale_cache,

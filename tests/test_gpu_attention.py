@@ -164,9 +164,10 @@ def test_query_longer_than_context_gives_zero_rows():
     r = run_gpu(w)
     got = host(r.out.float())
     ref = oracle_attention_on_gpu_cache(r)
-    # rows 0, 1 of sequence 0 sit at positions -2, -1: empty window
+    # rows 0, 1 of sequence 0 sit at positions -2, -1: empty window; the
+    # oracle returns exactly 0 there
     assert not got[0:2].any()
-    ref[0:2] = 0.0
+    assert not ref[0:2].any() and np.isfinite(ref).all()
     nbad, mx = allclose_report(got, ref, **G2)
     assert nbad == 0, mx
 
@@ -296,6 +297,35 @@ def test_stream_and_out_buffer_reuse():
         kv4.kv4_paged_attention(q, r.kc, r.vc, r.ks, r.vs, bt, slens, qsl, max_query_len=1,
                                 max_seq_len=w.max_seq_len, out=out, workspace=ws, stream=s)
     s.synchronize()
+    r.out = out
+    _g2(r)
+
+
+def test_side_stream_binding_allocates_workspace():
+    """Launch on a busy side stream and let the binding allocate the output
+    and the workspace; then, before the side stream reaches the attention
+    kernels, allocate and fill buffers of the same sizes on the current
+    stream. Buffers the binding allocated on the current stream and dropped
+    would be handed to those fills and clobbered; allocated on the launch
+    stream, they are not."""
+    w = W.custom("stream_ws", 32, 8, 128, [1] * 6, [3000, 40, 777, 4100, 129, 2000], block_size=16)
+    lay = W.make_layout(w)
+    r = run_gpu(w, attention=False)
+    need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, 32, 8, 128, 1, w.max_seq_len)
+    assert need > 0
+    q = r.t.query.to(DEV)
+    bt, slens, qsl = (torch.from_numpy(x).to(DEV) for x in (lay.block_table, lay.seq_lens, lay.query_start_loc))
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(20_000_000)      # a bounded spin: the side stream is busy for a few ms
+    out = kv4.kv4_paged_attention(q, r.kc, r.vc, r.ks, r.vs, bt, slens, qsl, max_query_len=1,
+                                  max_seq_len=w.max_seq_len, stream=s)
+    fills = [torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV),
+             torch.full(tuple(out.shape), 3.0, dtype=torch.bfloat16, device=DEV)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert fills[0].eq(0xA5).all()
     r.out = out
     _g2(r)
 

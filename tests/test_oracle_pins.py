@@ -583,3 +583,52 @@ def test_window_paged_forms_agree_with_dense():
         vh = O.dequant(vc4, vs4, slots, 42, inverse_rotate=True).astype(np.float64)
         ref4 = O.attention_dense(q, kh, vh, qsl, sl, 0.2, np.array(kv_start), window=W)
         assert np.allclose(got4, ref4, atol=1e-4)
+
+
+def test_empty_causal_window_rows_are_zero():
+    """A sequence shorter than its query block leaves its first rows with no
+    visible key (position < 0): the oracle returns exactly 0 there, with no
+    NaN and no floating-point warning, and every other row equals causal
+    attention computed over the rows that do see keys. A sequence of length
+    0 gives all-zero rows. Same reading in the dense, int4 and int8 forms."""
+    import warnings
+    rng = np.random.default_rng(11)
+    nq, nkv, hs = 4, 2, 32
+    qlens, slens = [5, 2, 1], [3, 0, 6]
+    q = rng.standard_normal((sum(qlens), nq, hs))
+    k = rng.standard_normal((sum(slens), nkv, hs))
+    v = rng.standard_normal((sum(slens), nkv, hs))
+    qsl = np.concatenate([[0], np.cumsum(qlens)])
+    kvs = np.concatenate([[0], np.cumsum(slens)])
+    with warnings.catch_warnings():
+        warnings.simplefilter("error")
+        got = O.attention_dense(q, k, v, qsl, slens, 0.3, kvs)
+        gotw = O.attention_dense(q, k, v, qsl, slens, 0.3, kvs, window=2)
+    assert np.isfinite(got).all() and np.isfinite(gotw).all()
+    # sequence 0: rows at positions -2, -1 see nothing; rows 2..4 see keys 0..i-2
+    assert not got[0:2].any() and not gotw[0:2].any()
+    # sequence 1 (length 0): both rows are zero
+    assert not got[5:7].any()
+    # the rows with keys equal attention over a query block of the same positions
+    tail = O.attention_dense(q[2:5], k[0:3], v[0:3], np.array([0, 3]), [3], 0.3, np.array([0, 3]))
+    np.testing.assert_allclose(got[2:5], tail, rtol=0, atol=1e-14)
+    want = _sdpa_reference(q[2:5], k[0:3], v[0:3], [3], [3], np.array([0, 3]), 0.3)
+    np.testing.assert_allclose(got[2:5], want, rtol=1e-12, atol=1e-12)
+
+    # paged forms over caches written by the oracle
+    bs, nb = 4, 6
+    bt = np.zeros((3, 2), dtype=np.int32)
+    bt[0, 0] = 0
+    bt[2, :] = [1, 2]
+    slots = np.array([0, 1, 2] + [4, 5, 6, 7, 8, 9], dtype=np.int64)
+    key32, val32 = k.astype(np.float32), v.astype(np.float32)
+    with warnings.catch_warnings():
+        warnings.simplefilter("error")
+        kc, vc, ks, vs = O.write_kv(key32, val32, slots, nb, bs, 42)
+        p4 = O.paged_attention(q, kc, vc, ks, vs, bt, np.array(slens), qsl, 0.3, 42)
+        kc8, vc8, ks8, vs8 = O.pth_write_kv(key32, val32, slots, nb, bs, "int8")
+        p8 = O.pth_paged_attention(q, kc8, vc8, ks8, vs8, bt, np.array(slens), qsl, 0.3, "int8")
+    for p in (p4, p8):
+        assert np.isfinite(p).all()
+        assert not p[0:2].any() and not p[5:7].any()
+        assert np.abs(p[2:5]).max() > 0.05 and np.abs(p[7]).max() > 0.05
