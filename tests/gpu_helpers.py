@@ -97,3 +97,24 @@ def allclose_report(got: np.ndarray, ref: np.ndarray, atol: float, rtol: float):
 
 def corr(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.corrcoef(a.ravel(), b.ravel())[0, 1])
+
+
+def inline_rows(buf: np.ndarray, mode: str, nkv: int, hs: int, bs: int):
+    """Vectorized reader of an inline-scale buffer (uint8 [nb, block_bytes]):
+    (kc, vc, ks, vs) with the geometry the oracle defines (inline_geometry);
+    the same result as O.inline_unpack, without its per-row Python loops, and
+    the padding bytes of every row as a fifth value. Host logic only."""
+    geo = O.inline_geometry(mode, nkv, hs, bs)
+    c, pitch = geo["code_bytes"], geo["pitch"]
+    rows = np.ascontiguousarray(buf, dtype=np.uint8).reshape(-1, 2, bs, nkv, pitch)
+    codes = rows[..., :c]
+    scales = np.ascontiguousarray(rows[..., c:c + 4]).view(np.float32)[..., 0]
+    pad = rows[..., c + 4:]
+    return (np.ascontiguousarray(codes[:, 0]), np.ascontiguousarray(codes[:, 1]),
+            np.ascontiguousarray(scales[:, 0]), np.ascontiguousarray(scales[:, 1]), pad)
+
+
+def worker_count() -> int:
+    """CPU workers for oracle work: the host cores this process may use, at
+    most 16 (a GPU machine's share)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))

@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
         "kv4_paged_attention_workspace_size", "kv4_rht_write",
         "kv4_pth_write", "kv4_pth_dequant", "kv4_pth_attention", "kv4_pth_attention_workspace_size",
         "kv4_cache_layout_packed", "kv4_cache_layout_inline", "kv4_write_layout",
-        "kv4_attention_layout_workspace_size", "kv4_attention_layout", "kv4_dequant_layout"])
+        "kv4_attention_layout_workspace_size", "kv4_attention_layout", "kv4_dequant_layout",
+        "kv4_stream_read"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -80,6 +81,30 @@ def test_write_accepts_non_power_of_two_heads_noop(L):
     for hs in range(8, 257, 8):
         assert _write(L, hs=hs, b=hs & -hs, ks=2 * hs, vs=2 * hs, T=0) == 0, kv4.kv4_last_error()
     assert kv4.kv4_last_error() == ""
+
+
+def test_b_zero_derives_the_rule(L):
+    """b = 0 asks the library for the largest power of two dividing head_size:
+    accepted for every head size (checked before the no-op return), while a
+    wrong nonzero b is still rejected."""
+    for hs in range(8, 257, 8):
+        assert _write(L, hs=hs, b=0, ks=2 * hs, vs=2 * hs, T=0) == 0, kv4.kv4_last_error()
+        assert L.kv4_dequant(16, 16, 4, 16, 0, 2, hs, 0, 16, 42, 1, 16, None) == 0, kv4.kv4_last_error()
+    assert _write(L, hs=96, b=96, T=0) == EINVAL
+    assert _attn(L, b=0, Tq=0, S=0) == 0, kv4.kv4_last_error()
+    assert _attn(L, b=0, hs=100, Tq=0, S=0) == EINVAL
+
+
+def test_entry_points_return_kv4_status():
+    """The header declares every work entry point as returning kv4_status."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", open(kv4.HEADER_PATH).read(), flags=re.S)
+    for name in kv4.header_functions():
+        m = re.search(r"^([A-Za-z_0-9 ]+\**)\s*" + name + r"\(", text, flags=re.M)
+        assert m, name
+        want = {"kv4_last_error": "const char*"}.get(name, "size_t" if name.endswith("workspace_size")
+                                                    else "kv4_status")
+        assert m.group(1).strip() == want, (name, m.group(1))
 
 
 def _attn(L, **over):

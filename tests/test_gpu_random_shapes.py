@@ -104,3 +104,30 @@ def test_random_write(seed):
     key = W.normal_bf16((T, nkv, hs), seed=seed, gain=gain)
     value = W.normal_bf16((T, nkv, hs), seed=seed + 10 ** 6)
     _write_and_compare(key, value, slots, nb, bs, seed=0x1234 + seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shape_short_sequences_and_odd_pages(seed, monkeypatch):
+    """Draws in which some sequences are shorter than their query block (the
+    first rows of such a sequence see no key and must come out as exactly 0,
+    as the oracle returns them) and, every other case, a page size that is not
+    a power of two (12 or 24 tokens, served by the vector kernel). G1 and G2
+    over every row."""
+    hs, nkv, g, bs, ql, sl, sched = _case(3000 + seed)
+    rng = np.random.default_rng(5000 + seed)
+    for i, q in enumerate(ql):
+        if q > 1 and rng.random() < 0.6:
+            sl[i] = int(rng.integers(0, q))
+    if seed % 2:
+        bs = int(rng.choice([12, 24]))
+    for k, v in sched.items():
+        monkeypatch.setenv(k, v)
+    w = W.custom(f"rshort{seed}", nkv * g, nkv, hs, ql, sl, block_size=bs, seed=seed, outlier_frac=0.01)
+    r = run_gpu(w)
+    _g1(r)
+    got, ref = _g2(r)
+    qsl = r.lay.query_start_loc
+    for s, (q, L) in enumerate(zip(ql, sl)):
+        if q > L:
+            rows = slice(int(qsl[s]), int(qsl[s]) + q - L)
+            assert not got[rows].any() and not ref[rows].any()
