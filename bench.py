@@ -29,6 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 matrix peak (no sparsity)
+MALL_ROTATE_BELOW = 512 << 20  # working sets below this are rotated through copies (256 MB Infinity Cache)
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 CSRC = os.path.join(ROOT, "paged_decode_attention_reshape_amd", "csrc")
 
@@ -67,6 +69,24 @@ def attention_bytes(w, mode: str = "int4", window: int = 0) -> int:
     return int(kv + bt + qo)
 
 
+def attention_flops(w, window: int = 0) -> int:
+    """Algorithmic flops of one attention pass: 4 * head_size per (query
+    head, visible key) -- q.k and p.v, a multiply and an add each. Query i of a
+    sequence with query_len q and seq_len L sees the keys at positions up to
+    L - q + i (and with a window only the last `window` of them)."""
+    pairs = 0
+    for L, q in zip(w.seq_lens, w.query_lens):
+        for i in range(q):
+            vis = max(0, L - q + i + 1)
+            pairs += min(vis, window) if window > 0 else vis
+    return int(4 * w.head_size * w.num_q_heads * pairs)
+
+
+def percentile(xs, p: float) -> float:
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), p))
+
+
 def kv_bytes(w, mode: str = "int4") -> int:
     return int(sum(w.seq_lens) * w.num_kv_heads * (2 * code_bytes(w, mode) + 8))
 
@@ -90,10 +110,17 @@ def main():
     ap.add_argument("--layout", default="packed", choices=["packed", "inline"],
                     help="cache layout: separate packed code and scale tensors, or one buffer with each "
                          "row's scale inline and rows padded to 16 bytes")
+    ap.add_argument("--rotate", type=int, default=0, metavar="N",
+                    help="independent copies of the cache the steps cycle through, so that a working set "
+                         "smaller than the 256 MB Infinity Cache is not served from it by the previous step "
+                         "(as in a model, where the other layers' caches pass in between); 0 = 4 copies when "
+                         "the step's KV working set is below 512 MB, else 1")
     ap.add_argument("--prewarm-s", type=float, default=0.5,
                     help="seconds of back-to-back steps before the warmup steps, so that the GPU's clocks have "
                          "left their idle state (a serving GPU runs continuously); never timed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the measured HBM read ceiling (kv4_stream_read over 2 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) -- the reference "
@@ -121,10 +148,6 @@ def main():
         dst = torch.empty_like(src)
         for _ in range(5):
             dst.copy_(src)
-        # a read-only pass over the same bytes (float32 sum: reads n bytes, writes one value)
-        f = src.view(torch.float32)
-        for _ in range(5):
-            f.sum()
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "repeats": 5}))
         return
@@ -141,36 +164,42 @@ def main():
 
     nb, bs, nkv, hs = lay.num_blocks, w.block_size, w.num_kv_heads, w.head_size
     mode = args.kv_mode
-    inline = args.layout == "inline" or args.window > 0
-    if args.layout == "inline":
-        lcache = kv4.LayoutCache.inline(mode, nb, bs, nkv, hs, device=dev)
-        kc = vc = ks = vs = None
-    else:
+    use_layout = args.layout == "inline" or args.window > 0
+    kv_set = int(sum(visible_keys(w, args.window)) * nkv * (2 * code_bytes(w, mode) + 8))
+    n_copies = args.rotate if args.rotate > 0 else (4 if kv_set < MALL_ROTATE_BELOW else 1)
+
+    def new_cache():
+        """One cache set: (packed tensors or None, layout cache or None)."""
+        if args.layout == "inline":
+            return None, kv4.LayoutCache.inline(mode, nb, bs, nkv, hs, device=dev)
         kc = torch.zeros((nb, bs, nkv, code_bytes(w, mode)), dtype=torch.uint8, device=dev)
-        vc = torch.zeros_like(kc)
-        ks = torch.zeros((nb, bs, nkv), dtype=torch.float32, device=dev)
-        vs = torch.zeros_like(ks)
-        if inline:    # packed caches through the layout entry points (sliding window)
-            lcache = kv4.packed_layout_cache(mode, kc, vc, ks, vs)
+        packed = (kc, torch.zeros_like(kc), torch.zeros((nb, bs, nkv), dtype=torch.float32, device=dev),
+                  torch.zeros((nb, bs, nkv), dtype=torch.float32, device=dev))
+        # packed caches through the layout entry points (sliding window)
+        return packed, (kv4.packed_layout_cache(mode, *packed) if use_layout else None)
+
+    caches = [new_cache() for _ in range(n_copies)]
     stream = torch.cuda.Stream()
 
-    def write(k, v, slots):
-        if inline:
+    def write(c, k, v, slots):
+        packed, lcache = c
+        if lcache is not None:
             kv4.kv4_write_layout(k, v, lcache, slots, sign_seed=w.sign_seed, stream=stream)
         elif mode == "int4":
-            kv4.kv4_rht_write(k, v, kc, vc, ks, vs, slots, sign_seed=w.sign_seed, stream=stream)
+            kv4.kv4_rht_write(k, v, *packed, slots, sign_seed=w.sign_seed, stream=stream)
         else:
-            kv4.kv4_pth_write(mode, k, v, kc, vc, ks, vs, slots, stream=stream)
+            kv4.kv4_pth_write(mode, k, v, *packed, slots, stream=stream)
 
-    # ---- bulk write of every context token (here untimed; timed again after
-    # the pre-warm below)
+    # ---- bulk write of every context token into every copy (here untimed;
+    # timed again after the timed steps)
     ctx_idx = torch.from_numpy(ctx_rows).to(dev)
     k_ctx = t.key.index_select(0, ctx_idx)
     v_ctx = t.value.index_select(0, ctx_idx)
     s_ctx = torch.from_numpy(slots_all[ctx_rows]).to(dev)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        write(k_ctx, v_ctx, s_ctx)
+        for c in caches:
+            write(c, k_ctx, v_ctx, s_ctx)
     torch.cuda.synchronize()
     n_ctx = int(ctx_rows.shape[0])
 
@@ -184,8 +213,8 @@ def main():
     slens = torch.from_numpy(lay.seq_lens).to(dev)
     qsl = torch.from_numpy(lay.query_start_loc).to(dev)
     out = torch.empty((w.num_q_tokens, w.num_q_heads, hs), dtype=torch.bfloat16, device=dev)
-    if inline:
-        need = kv4.kv4_attention_layout_workspace_size(lcache, w.num_q_tokens, w.num_seqs, w.num_q_heads,
+    if use_layout:
+        need = kv4.kv4_attention_layout_workspace_size(caches[0][1], w.num_q_tokens, w.num_seqs, w.num_q_heads,
                                                        w.max_query_len, w.max_seq_len)
     elif mode == "int4":
         need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, w.num_q_heads, nkv, hs,
@@ -195,20 +224,24 @@ def main():
                                                     w.max_query_len, w.max_seq_len)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
+    step_no = [0]
+
     def step(e_a=None, e_b=None):
-        write(k_new, v_new, s_new)
+        packed, lcache = caches[step_no[0] % n_copies]
+        step_no[0] += 1
+        write((packed, lcache), k_new, v_new, s_new)
         if e_a is not None:
             e_a.record(stream)
-        if inline:
+        if lcache is not None:
             kv4.kv4_attention_layout(q, lcache, bt, slens, qsl, w.max_query_len, w.max_seq_len,
                                      sign_seed=w.sign_seed, out=out, workspace=ws, stream=stream,
                                      sliding_window=args.window)
         elif mode == "int4":
-            kv4.kv4_paged_attention(q, kc, vc, ks, vs, bt, slens, qsl, max_query_len=w.max_query_len,
+            kv4.kv4_paged_attention(q, *packed, bt, slens, qsl, max_query_len=w.max_query_len,
                                     max_seq_len=w.max_seq_len, sign_seed=w.sign_seed, out=out, workspace=ws,
                                     stream=stream)
         else:
-            kv4.kv4_pth_attention(mode, q, kc, vc, ks, vs, bt, slens, qsl, max_query_len=w.max_query_len,
+            kv4.kv4_pth_attention(mode, q, *packed, bt, slens, qsl, max_query_len=w.max_query_len,
                                   max_seq_len=w.max_seq_len, out=out, workspace=ws, stream=stream)
         if e_b is not None:
             e_b.record(stream)
@@ -252,7 +285,7 @@ def main():
     with torch.cuda.stream(stream):
         for rep in range(3):
             ev[0].record(stream)
-            write(k_ctx, v_ctx, s_ctx)
+            write(caches[rep % n_copies], k_ctx, v_ctx, s_ctx)
             ev[1].record(stream)
             stream.synchronize()
             wr_ms.append(ev[0].elapsed_time(ev[1]))
@@ -261,8 +294,22 @@ def main():
     write_tps = n_ctx / (write_ms * 1e-3) if n_ctx else 0.0
     write_gbs = n_ctx * write_bytes_per_token(w, mode) / (write_ms * 1e-3) / 1e9 if n_ctx else 0.0
     a_bytes = attention_bytes(w, mode, args.window)
+    a_flops = attention_flops(w, args.window)
     value = a_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = a_bytes / (attn_avg_ms * 1e-3) / 1e9
+
+    # Roofline of the attention call: the larger of its time at the HBM peak
+    # (algorithmic bytes) and at the matrix-core peak (algorithmic flops)
+    # decides the bound; achieved is taken over the mean HIP-event time of
+    # the call on its stream (what a kernel trace averages).
+    t_hbm = a_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = a_flops / (MFMA_PEAK_TFLOPS * 1e12)
+    gbs = a_bytes / (attn_avg_ms * 1e-3) / 1e9
+    tflops = a_flops / (attn_avg_ms * 1e-3) / 1e12
+    bound = "mfma" if t_mfma > t_hbm else "hbm"
+
+    read_ceiling = None
+    if not args.no_read_ceiling:
+        read_ceiling = measured_read_ceiling(torch, kv4, dev, stream)
 
     traffic = None
     if os.path.exists(PROFILE_COUNTERS):
@@ -275,6 +322,24 @@ def main():
                 traffic = ent.get("traffic_bytes_per_launch")
         except Exception:
             traffic = None
+
+    roof = {"bound": bound,
+            "kernel": ("kv4_paged_attention" if mode == "int4" and not use_layout else
+                       "kv4_attention_layout" if use_layout else "kv4_pth_attention") + " (attention + merge)",
+            "achieved": round(tflops if bound == "mfma" else gbs, 2),
+            "peak": MFMA_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+            "frac": round((tflops / MFMA_PEAK_TFLOPS) if bound == "mfma" else (gbs / HBM_PEAK_GBS), 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": a_bytes,
+            "algorithmic_flops_per_launch": a_flops,
+            "time_at_hbm_peak_us": round(t_hbm * 1e6, 2),
+            "time_at_mfma_peak_us": round(t_mfma * 1e6, 2),
+            "hbm_GBps": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "mfma_TFLOPs": round(tflops, 2), "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4)}
+    if read_ceiling:
+        roof["measured_read_GBps"] = read_ceiling["GBps"]
+        roof["hbm_frac_of_measured"] = round(gbs / read_ceiling["GBps"], 4)
 
     line = {
         "metric": "INT4 paged decode attn: KV GB/s & % HBM peak; cache-write tokens/s"
@@ -292,37 +357,77 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": f"{mode} codes / fp32 accumulate (bf16 in/out)",
-        "data": "synthetic seeded N(0,1) bf16, 1% outlier channels x20",
+        "data": "synthetic seeded N(0,1) bf16" + (", 1% outlier channels x20" if w.outlier_frac > 0 else ""),
         "config": {"workload": w.name, "kv_cache": mode, "cache_layout": args.layout,
                    "sliding_window": args.window, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": nkv, "head_size": hs, "block_size": bs,
                    "total_kv_tokens": w.total_kv_tokens, "max_seq_len": w.max_seq_len,
                    "q_tokens_per_step": w.num_q_tokens, "new_kv_tokens_per_step": int(new_rows.shape[0]),
-                   "parallelism": "single GPU"},
+                   "cache_copies_rotated": n_copies, "parallelism": "single GPU"},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "attn_ms": round(attn_avg_ms, 4),
+        "attn_ms_median": round(percentile(attn_ms, 50), 4),
+        "attn_ms_p10": round(percentile(attn_ms, 10), 4),
+        "attn_ms_p90": round(percentile(attn_ms, 90), 4),
+        "attn_GBps_median": round(a_bytes / (percentile(attn_ms, 50) * 1e-3) / 1e9, 2),
         "attn_query_tokens_per_s": round(w.num_q_tokens / (attn_avg_ms * 1e-3), 1),
-        "kv_bytes_per_step": int(sum(visible_keys(w, args.window)) * w.num_kv_heads * (2 * code_bytes(w, mode) + 8)),
+        "kv_bytes_per_step": kv_set,
         "write_tokens_per_s": round(write_tps, 1),
         "write_GBps": round(write_gbs, 2),
+        "write_hbm_frac": round(write_gbs / HBM_PEAK_GBS, 4),
         "write_bulk_tokens": n_ctx,
-        "roofline": {"bound": "hbm", "kernel": ("kv4_paged_attention" if mode == "int4" else "kv4_pth_attention")
-                     + " (attention + merge)",
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": a_bytes},
+        "roofline": roof,
     }
+    if read_ceiling:
+        line["read_ceiling"] = read_ceiling
 
     if not args.no_cpu_baseline:
+        packed0, lcache0 = caches[0]
+        kc, vc, ks, vs = packed0 if packed0 is not None else (None,) * 4
         line["cpu_baseline"] = cpu_baseline(w, lay, t, kc, vc, ks, vs, args.cpu_seconds, mode,
-                                            lcache if args.layout == "inline" else None, args.window)
+                                            lcache0 if args.layout == "inline" else None, args.window,
+                                            ctx_rows, slots_all)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float, mode: str = "int4", lcache=None, window: int = 0):
-    """The CPU oracle (fp64 numpy) on a bounded sample of the same workload:
-    whole sequences of this batch, read from the GPU-written cache, until
-    about `budget_s` seconds of CPU work; reported as KV GB/s like `value`."""
+def measured_read_ceiling(torch, kv4, dev, stream, nbytes: int = 2 << 30):
+    """Achievable HBM read rate on this GPU: kv4_stream_read over a 2 GiB
+    buffer (8x the Infinity Cache) at three grid sizes, 3 warm + 10 timed
+    passes each; the best median, with its spread."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best = None
+    for grid in (1024, 2048, 4096):
+        ms = []
+        with torch.cuda.stream(stream):
+            for rep in range(13):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                kv4.kv4_stream_read(buf, sink, grid=grid, stream=stream)
+                e1.record(stream)
+                stream.synchronize()
+                if rep >= 3:
+                    ms.append(e0.elapsed_time(e1))
+        med = percentile(ms, 50)
+        ent = {"GBps": round(nbytes / (med * 1e-3) / 1e9, 1), "grid": grid,
+               "GBps_p10_p90": [round(nbytes / (percentile(ms, 90) * 1e-3) / 1e9, 1),
+                                round(nbytes / (percentile(ms, 10) * 1e-3) / 1e9, 1)]}
+        if best is None or ent["GBps"] > best["GBps"]:
+            best = ent
+    del buf
+    best["kernel"] = "kv4_stream_read (16-byte non-temporal loads, 2 GiB, median of 10)"
+    return best
+
+
+def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float, mode: str = "int4", lcache=None, window: int = 0,
+                 ctx_rows=None, slots_all=None):
+    """The CPU oracle (numpy) on a bounded sample of the same workload:
+    attention over whole sequences of this batch, read from the GPU-written
+    cache, until about `budget_s` seconds of CPU work (reported as KV GB/s
+    like `value`, and as query tokens/s); and the write path (spec tier:
+    rotation, bf16 rounding, quantization, packing) on the first context
+    tokens for about a fifth of that (tokens/s)."""
     import numpy as np
     import torch
 
@@ -331,12 +436,15 @@ def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float, mode: str = "int4",
 
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = sorted({f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                       for i in info if i.get("user_api") == "blas"})
     except Exception:  # pragma: no cover
-        threads = 1
+        threads, blas = 1, []
     order = np.random.default_rng(0).permutation(w.num_seqs)
     q = W.bf16_as_f32_numpy(t.query)
-    done_bytes, done_seqs, spent = 0, 0, 0.0
+    done_bytes, done_seqs, done_q, spent = 0, 0, 0, 0.0
     dev = (lcache.buffer if lcache is not None else kc).device
     for s in order:
         n = -(-w.seq_lens[s] // w.block_size)
@@ -359,12 +467,38 @@ def cpu_baseline(w, lay, t, kc, vc, ks, vs, budget_s: float, mode: str = "int4",
         spent += time.perf_counter() - t0
         done_bytes += int(visible_keys(w, window)[s]) * w.num_kv_heads * (2 * code_bytes(w, mode) + 8)
         done_seqs += 1
+        done_q += int(w.query_lens[s])
         if spent >= budget_s:
             break
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "host_cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"{done_seqs} of {w.num_seqs} sequences of {w.name} (fp64 numpy oracle reading the "
-                      f"GPU-written cache), {spent:.1f} s of CPU time"}
+
+    # write path: chunks of 4096 context tokens (K and V) until the budget
+    wr_tok, wr_spent = 0, 0.0
+    if ctx_rows is not None and len(ctx_rows):
+        nb = lay.num_blocks
+        for r0 in range(0, len(ctx_rows), 4096):
+            rows = torch.from_numpy(ctx_rows[r0:r0 + 4096]).to(t.key.device)
+            key = W.bf16_as_f32_numpy(t.key.index_select(0, rows))
+            value = W.bf16_as_f32_numpy(t.value.index_select(0, rows))
+            sl = slots_all[ctx_rows[r0:r0 + 4096]]
+            t0 = time.perf_counter()
+            if mode == "int4":
+                O.write_kv(key, value, sl, nb, w.block_size, w.sign_seed)
+            else:
+                O.pth_write_kv(key, value, sl, nb, w.block_size, mode)
+            wr_spent += time.perf_counter() - t0
+            wr_tok += len(sl)
+            if wr_spent >= budget_s / 5:
+                break
+    res = {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+           "host_cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+           "sample": f"attention: {done_seqs} of {w.num_seqs} sequences of {w.name} (fp64 numpy oracle reading "
+                     f"the GPU-written cache), {spent:.1f} s of CPU time; write: {wr_tok} context tokens "
+                     f"(spec-tier numpy oracle, K and V), {wr_spent:.1f} s",
+           "attn_query_tokens_per_s": round(done_q / spent, 2),
+           "numpy": np.__version__, "blas": blas}
+    if wr_tok:
+        res["write_tokens_per_s"] = round(wr_tok / wr_spent, 1)
+    return res
 
 
 if __name__ == "__main__":

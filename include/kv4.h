@@ -53,7 +53,14 @@
  *     vector loads; vLLM PR #62113 aligned per-token-head KV slots to 16 bytes
  *     for the same reason).
  *   - head_size: a multiple of 8 in [8, 256]; b must equal the largest power
- *     of two dividing head_size ([PR56198]); anything else is KV4_EINVAL.
+ *     of two dividing head_size ([PR56198]), or be 0 to let the library take
+ *     that value; anything else is KV4_EINVAL.
+ *   - block_size (tokens per page) may be any value in [1, 4096]; the
+ *     matrix-core attention kernel serves powers of two >= 16 and the vector
+ *     kernel every other size, with the same results.
+ *   - Every entry point that does work returns a kv4_status; the
+ *     *_workspace_size queries return a byte count (0 with an error message
+ *     for invalid sizes).
  */
 #ifndef KV4_H_
 #define KV4_H_
@@ -101,14 +108,14 @@ typedef enum {
  *   sign_seed           seed of D (see above)
  * num_tokens == 0 is a valid no-op.
  */
-int kv4_rht_write(const void* key, const void* value,
-                  int64_t key_token_stride, int64_t value_token_stride,
-                  void* key_cache, void* value_cache,
-                  float* k_scale_cache, float* v_scale_cache,
-                  const int64_t* slot_mapping, int64_t num_tokens,
-                  int32_t num_kv_heads, int32_t head_size, int32_t b,
-                  int32_t block_size, int64_t num_blocks,
-                  uint64_t sign_seed, void* stream);
+kv4_status kv4_rht_write(const void* key, const void* value,
+                         int64_t key_token_stride, int64_t value_token_stride,
+                         void* key_cache, void* value_cache,
+                         float* k_scale_cache, float* v_scale_cache,
+                         const int64_t* slot_mapping, int64_t num_tokens,
+                         int32_t num_kv_heads, int32_t head_size, int32_t b,
+                         int32_t block_size, int64_t num_blocks,
+                         uint64_t sign_seed, void* stream);
 
 /*
  * kv4_paged_attention_workspace_size -- bytes of device workspace that
@@ -168,19 +175,19 @@ size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs
  * kv4_paged_attention_workspace_size reads the same variables: query it with
  * the same environment the call will see.
  */
-int kv4_paged_attention(const void* query, int64_t query_token_stride,
-                        const void* key_cache, const void* value_cache,
-                        const float* k_scale_cache, const float* v_scale_cache,
-                        int64_t num_blocks,
-                        const int32_t* block_table, int32_t max_blocks_per_seq,
-                        const int32_t* seq_lens, const int32_t* query_start_loc,
-                        int32_t num_seqs, int64_t num_q_tokens,
-                        int32_t max_query_len, int32_t max_seq_len,
-                        int32_t num_q_heads, int32_t num_kv_heads,
-                        int32_t head_size, int32_t b, int32_t block_size,
-                        uint64_t sign_seed, float softmax_scale,
-                        void* out, void* workspace, size_t workspace_bytes,
-                        void* stream);
+kv4_status kv4_paged_attention(const void* query, int64_t query_token_stride,
+                               const void* key_cache, const void* value_cache,
+                               const float* k_scale_cache, const float* v_scale_cache,
+                               int64_t num_blocks,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, const int32_t* query_start_loc,
+                               int32_t num_seqs, int64_t num_q_tokens,
+                               int32_t max_query_len, int32_t max_seq_len,
+                               int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_size, int32_t b, int32_t block_size,
+                               uint64_t sign_seed, float softmax_scale,
+                               void* out, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /*
  * kv4_dequant -- gather and dequantize cache slots (for tests and debugging;
@@ -193,11 +200,11 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride,
  *   slot_mapping        int64 [num_tokens]; out-of-range slots give zeros
  *   out                 float32 [num_tokens, num_kv_heads, head_size]
  */
-int kv4_dequant(const void* cache, const float* scale_cache, int64_t num_blocks,
-                const int64_t* slot_mapping, int64_t num_tokens,
-                int32_t num_kv_heads, int32_t head_size, int32_t b,
-                int32_t block_size, uint64_t sign_seed, int32_t inverse_rotate,
-                float* out, void* stream);
+kv4_status kv4_dequant(const void* cache, const float* scale_cache, int64_t num_blocks,
+                       const int64_t* slot_mapping, int64_t num_tokens,
+                       int32_t num_kv_heads, int32_t head_size, int32_t b,
+                       int32_t block_size, uint64_t sign_seed, int32_t inverse_rotate,
+                       float* out, void* stream);
 
 /*
  * Per-token-head INT8 / FP8 control modes: the pages' int8_per_token_head
@@ -225,13 +232,13 @@ int kv4_dequant(const void* cache, const float* scale_cache, int64_t num_blocks,
  * it at slot_mapping[t] (slots outside [0, num_blocks * block_size) skip the
  * token). Arguments otherwise as kv4_rht_write; KV4_EINVAL for another mode.
  */
-int kv4_pth_write(int32_t kv_quant_mode, const void* key, const void* value,
-                  int64_t key_token_stride, int64_t value_token_stride,
-                  void* key_cache, void* value_cache,
-                  float* k_scale_cache, float* v_scale_cache,
-                  const int64_t* slot_mapping, int64_t num_tokens,
-                  int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                  int64_t num_blocks, void* stream);
+kv4_status kv4_pth_write(int32_t kv_quant_mode, const void* key, const void* value,
+                         int64_t key_token_stride, int64_t value_token_stride,
+                         void* key_cache, void* value_cache,
+                         float* k_scale_cache, float* v_scale_cache,
+                         const int64_t* slot_mapping, int64_t num_tokens,
+                         int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                         int64_t num_blocks, void* stream);
 
 /*
  * kv4_pth_attention_workspace_size / kv4_pth_attention -- the read path over
@@ -247,18 +254,18 @@ size_t kv4_pth_attention_workspace_size(int32_t kv_quant_mode, int64_t num_q_tok
                                         int32_t num_seqs, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_size,
                                         int32_t max_query_len, int32_t max_seq_len);
-int kv4_pth_attention(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
-                      const void* key_cache, const void* value_cache,
-                      const float* k_scale_cache, const float* v_scale_cache,
-                      int64_t num_blocks,
-                      const int32_t* block_table, int32_t max_blocks_per_seq,
-                      const int32_t* seq_lens, const int32_t* query_start_loc,
-                      int32_t num_seqs, int64_t num_q_tokens,
-                      int32_t max_query_len, int32_t max_seq_len,
-                      int32_t num_q_heads, int32_t num_kv_heads,
-                      int32_t head_size, int32_t block_size, float softmax_scale,
-                      void* out, void* workspace, size_t workspace_bytes,
-                      void* stream);
+kv4_status kv4_pth_attention(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
+                             const void* key_cache, const void* value_cache,
+                             const float* k_scale_cache, const float* v_scale_cache,
+                             int64_t num_blocks,
+                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                             const int32_t* seq_lens, const int32_t* query_start_loc,
+                             int32_t num_seqs, int64_t num_q_tokens,
+                             int32_t max_query_len, int32_t max_seq_len,
+                             int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size, float softmax_scale,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * kv4_pth_dequant -- gather and dequantize int8 / fp8 cache slots (tests and
@@ -266,12 +273,11 @@ int kv4_pth_attention(int32_t kv_quant_mode, const void* query, int64_t query_to
  * out-of-range slots give zeros. out float32 [num_tokens, num_kv_heads,
  * head_size].
  */
-int kv4_pth_dequant(int32_t kv_quant_mode, const void* cache, const float* scale_cache,
-                    int64_t num_blocks, const int64_t* slot_mapping, int64_t num_tokens,
-                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                    float* out, void* stream);
+kv4_status kv4_pth_dequant(int32_t kv_quant_mode, const void* cache, const float* scale_cache,
+                           int64_t num_blocks, const int64_t* slot_mapping, int64_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                           float* out, void* stream);
 
-/* Thread-local description of the last failure ("" if none). Never NULL. */
 /*
  * Cache layouts. Every entry point above takes the packed layout: codes
  * uint8 [num_blocks, block_size, num_kv_heads, C] (C = head_size / 2 for the
@@ -302,8 +308,8 @@ typedef struct kv4_cache_layout {
 } kv4_cache_layout;
 
 /* kv4_cache_layout_packed -- the packed layout of the other entry points. */
-int kv4_cache_layout_packed(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size,
-                            int32_t block_size, kv4_cache_layout* layout);
+kv4_status kv4_cache_layout_packed(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size,
+                                   int32_t block_size, kv4_cache_layout* layout);
 
 /*
  * kv4_cache_layout_inline -- the inline-scale padded-slot layout of the
@@ -320,9 +326,9 @@ int kv4_cache_layout_packed(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t
  * v_scale_cache = (float*)(buffer + value_offset + scale_offset) with the
  * returned layout. block_bytes / value_offset / scale_offset may be NULL.
  */
-int kv4_cache_layout_inline(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size,
-                            int32_t block_size, kv4_cache_layout* layout, int64_t* block_bytes,
-                            int64_t* value_offset, int64_t* scale_offset);
+kv4_status kv4_cache_layout_inline(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size,
+                                   int32_t block_size, kv4_cache_layout* layout, int64_t* block_bytes,
+                                   int64_t* value_offset, int64_t* scale_offset);
 
 /*
  * kv4_write_layout / kv4_attention_layout_workspace_size /
@@ -341,40 +347,57 @@ int kv4_cache_layout_inline(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t
  * KV4_EINVAL. Pass the packed layout (kv4_cache_layout_packed) for the caches
  * of the other entry points.
  */
-int kv4_write_layout(int32_t kv_quant_mode, const void* key, const void* value,
-                     int64_t key_token_stride, int64_t value_token_stride,
-                     void* key_cache, void* value_cache,
-                     float* k_scale_cache, float* v_scale_cache,
-                     const kv4_cache_layout* layout,
-                     const int64_t* slot_mapping, int64_t num_tokens,
-                     int32_t num_kv_heads, int32_t head_size, int32_t b,
-                     int32_t block_size, int64_t num_blocks,
-                     uint64_t sign_seed, void* stream);
+kv4_status kv4_write_layout(int32_t kv_quant_mode, const void* key, const void* value,
+                            int64_t key_token_stride, int64_t value_token_stride,
+                            void* key_cache, void* value_cache,
+                            float* k_scale_cache, float* v_scale_cache,
+                            const kv4_cache_layout* layout,
+                            const int64_t* slot_mapping, int64_t num_tokens,
+                            int32_t num_kv_heads, int32_t head_size, int32_t b,
+                            int32_t block_size, int64_t num_blocks,
+                            uint64_t sign_seed, void* stream);
 size_t kv4_attention_layout_workspace_size(int32_t kv_quant_mode, const kv4_cache_layout* layout,
                                            int64_t num_q_tokens, int32_t num_seqs,
                                            int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_size, int32_t max_query_len,
                                            int32_t max_seq_len);
-int kv4_attention_layout(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
-                         const void* key_cache, const void* value_cache,
-                         const float* k_scale_cache, const float* v_scale_cache,
-                         const kv4_cache_layout* layout, int64_t num_blocks,
-                         const int32_t* block_table, int32_t max_blocks_per_seq,
-                         const int32_t* seq_lens, const int32_t* query_start_loc,
-                         int32_t num_seqs, int64_t num_q_tokens,
-                         int32_t max_query_len, int32_t max_seq_len,
-                         int32_t num_q_heads, int32_t num_kv_heads,
-                         int32_t head_size, int32_t b, int32_t block_size,
-                         uint64_t sign_seed, int32_t sliding_window, float softmax_scale,
-                         void* out, void* workspace, size_t workspace_bytes,
-                         void* stream);
-int kv4_dequant_layout(int32_t kv_quant_mode, const void* cache, const float* scale_cache,
-                       const kv4_cache_layout* layout, int64_t num_blocks,
-                       const int64_t* slot_mapping, int64_t num_tokens,
-                       int32_t num_kv_heads, int32_t head_size, int32_t b,
-                       int32_t block_size, uint64_t sign_seed, int32_t inverse_rotate,
-                       float* out, void* stream);
+kv4_status kv4_attention_layout(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
+                                const void* key_cache, const void* value_cache,
+                                const float* k_scale_cache, const float* v_scale_cache,
+                                const kv4_cache_layout* layout, int64_t num_blocks,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, const int32_t* query_start_loc,
+                                int32_t num_seqs, int64_t num_q_tokens,
+                                int32_t max_query_len, int32_t max_seq_len,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_size, int32_t b, int32_t block_size,
+                                uint64_t sign_seed, int32_t sliding_window, float softmax_scale,
+                                void* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+kv4_status kv4_dequant_layout(int32_t kv_quant_mode, const void* cache, const float* scale_cache,
+                              const kv4_cache_layout* layout, int64_t num_blocks,
+                              const int64_t* slot_mapping, int64_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_size, int32_t b,
+                              int32_t block_size, uint64_t sign_seed, int32_t inverse_rotate,
+                              float* out, void* stream);
 
+/*
+ * kv4_stream_read -- measurement aid, not a step of the method: reads `bytes`
+ * (a multiple of 16) of device memory at `buffer` (16-byte aligned) once,
+ * with 16-byte non-temporal vector loads from `grid` workgroups of 256
+ * lanes, four loads in flight per lane. Its duration gives the achievable
+ * HBM read rate that the attention kernels' bandwidth is compared with.
+ * `sink` (4 bytes, device) receives a value only if the XOR of everything
+ * read is 0x9E3779B9 (which keeps the loads from being optimized away).
+ */
+kv4_status kv4_stream_read(const void* buffer, int64_t bytes, uint32_t* sink, int32_t grid,
+                           void* stream);
+
+/*
+ * kv4_last_error -- thread-local description of the last failure of a call
+ * made on this thread ("" after a call that succeeded). Never NULL; the
+ * string stays valid until the next kv4_* call on the same thread.
+ */
 const char* kv4_last_error(void);
 
 #ifdef __cplusplus

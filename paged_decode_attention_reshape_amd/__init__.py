@@ -53,6 +53,7 @@ _SIGNATURES = {
     "kv4_dequant": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _c_int64, _c_int32, _c_int32, _c_int32,
                                    _c_int32, _c_uint64, _c_int32, _vp, _vp]),
     "kv4_last_error": (ctypes.c_char_p, []),
+    "kv4_stream_read": (ctypes.c_int, [_vp, _c_int64, _vp, _c_int32, _vp]),
     "kv4_pth_write": (ctypes.c_int, [_c_int32, _vp, _vp, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp,
                                      _c_int64, _c_int32, _c_int32, _c_int32, _c_int64, _vp]),
     "kv4_pth_dequant": (ctypes.c_int, [_c_int32, _vp, _vp, _c_int64, _vp, _c_int64, _c_int32, _c_int32,
@@ -119,12 +120,39 @@ def _check(func: str, rc: int):
         raise Kv4Error(func, rc, kv4_last_error())
 
 
+def _b(b: Optional[int]) -> int:
+    """b as the C calls take it: 0 lets the library derive the largest power
+    of two dividing head_size; any other value is passed on and validated
+    there."""
+    return 0 if b is None else int(b)
+
+
+def _torch_stream(stream):
+    """The torch stream object of the stream a call is queued on: the current
+    stream, a torch.cuda.Stream, or a raw hipStream_t handle."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def _empty_on(stream, shape, dtype, device) -> torch.Tensor:
+    """A buffer the binding allocates for a call (its output or workspace),
+    taken from the caching allocator's pool of the call's own stream: when
+    the binding drops it, the allocator hands it out again only for work
+    queued after this call on that stream, never while the call's kernels
+    may still write it."""
+    with torch.cuda.stream(_torch_stream(stream)):
+        return torch.empty(shape, dtype=dtype, device=device)
 
 
 def _need(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
@@ -174,7 +202,7 @@ def kv4_rht_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tenso
     rc = lib().kv4_rht_write(key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0),
                              key_cache.data_ptr(), value_cache.data_ptr(), k_scale_cache.data_ptr(),
                              v_scale_cache.data_ptr(), slot_mapping.data_ptr(), T, nkv, hs,
-                             hs & -hs if b is None else b, bs, nb, sign_seed & (2 ** 64 - 1), _stream(stream))
+                             _b(b), bs, nb, sign_seed & (2 ** 64 - 1), _stream(stream))
     _check("kv4_rht_write", rc)
 
 
@@ -224,14 +252,14 @@ def kv4_paged_attention(query: torch.Tensor, key_cache: torch.Tensor, value_cach
     if query.stride(2) != 1 or query.stride(1) != hs:
         raise ValueError("query must have contiguous heads")
     if out is None:
-        out = torch.empty((Tq, nq, hs), dtype=torch.bfloat16, device=query.device)
+        out = _empty_on(stream, (Tq, nq, hs), torch.bfloat16, query.device)
     _need(out, "out", torch.bfloat16, 3)
     _contig(out, "out")
     if out.shape != (Tq, nq, hs):
         raise ValueError("out must be [num_q_tokens, num_q_heads, head_size]")
     need = kv4_paged_attention_workspace_size(Tq, S, nq, nkv, hs, max_query_len, max_seq_len)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+        workspace = _empty_on(stream, (need,), torch.uint8, query.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if softmax_scale is None:
@@ -240,7 +268,7 @@ def kv4_paged_attention(query: torch.Tensor, key_cache: torch.Tensor, value_cach
         query.data_ptr(), query.stride(0), key_cache.data_ptr(), value_cache.data_ptr(),
         k_scale_cache.data_ptr(), v_scale_cache.data_ptr(), nb, block_table.data_ptr(),
         block_table.shape[1], seq_lens.data_ptr(), query_start_loc.data_ptr(), S, Tq,
-        int(max_query_len), int(max_seq_len), nq, nkv, hs, hs & -hs if b is None else b, bs,
+        int(max_query_len), int(max_seq_len), nq, nkv, hs, _b(b), bs,
         sign_seed & (2 ** 64 - 1), float(softmax_scale), out.data_ptr(), ws_ptr, ws_bytes, _stream(stream))
     _check("kv4_paged_attention", rc)
     return out
@@ -260,14 +288,25 @@ def kv4_dequant(cache: torch.Tensor, scale_cache: torch.Tensor, slot_mapping: to
     hs = 2 * half
     T = slot_mapping.shape[0]
     if out is None:
-        out = torch.empty((T, nkv, hs), dtype=torch.float32, device=cache.device)
+        out = _empty_on(stream, (T, nkv, hs), torch.float32, cache.device)
     _need(out, "out", torch.float32, 3)
     _contig(out, "out")
     rc = lib().kv4_dequant(cache.data_ptr(), scale_cache.data_ptr(), nb, slot_mapping.data_ptr(), T, nkv,
-                           hs, hs & -hs if b is None else b, bs, sign_seed & (2 ** 64 - 1),
+                           hs, _b(b), bs, sign_seed & (2 ** 64 - 1),
                            1 if inverse_rotate else 0, out.data_ptr(), _stream(stream))
     _check("kv4_dequant", rc)
     return out
+
+
+def kv4_stream_read(buffer: torch.Tensor, sink: torch.Tensor, grid: int = 2048, stream=None) -> None:
+    """Read every byte of `buffer` once (bandwidth calibration; see
+    include/kv4.h). `sink` is a 4-byte device tensor."""
+    _contig(buffer, "buffer")
+    if buffer.device.type != "cuda" or sink.device.type != "cuda" or sink.numel() * sink.element_size() < 4:
+        raise ValueError("buffer and a 4-byte sink must be GPU tensors")
+    nbytes = buffer.numel() * buffer.element_size()
+    _check("kv4_stream_read", lib().kv4_stream_read(buffer.data_ptr(), nbytes - nbytes % 16, sink.data_ptr(),
+                                                    int(grid), _stream(stream)))
 
 
 __all__ = ["kv4_rht_write", "kv4_paged_attention", "kv4_paged_attention_workspace_size", "kv4_dequant",
@@ -329,7 +368,7 @@ def kv4_pth_dequant(kv_quant_mode, cache: torch.Tensor, scale_cache: torch.Tenso
         raise ValueError("scale cache shape disagrees with the cache")
     T = slot_mapping.shape[0]
     if out is None:
-        out = torch.empty((T, nkv, hs), dtype=torch.float32, device=cache.device)
+        out = _empty_on(stream, (T, nkv, hs), torch.float32, cache.device)
     _need(out, "out", torch.float32, 3)
     _contig(out, "out")
     if out.shape != (T, nkv, hs):
@@ -383,14 +422,14 @@ def kv4_pth_attention(kv_quant_mode, query: torch.Tensor, key_cache: torch.Tenso
     if query.stride(2) != 1 or query.stride(1) != hs:
         raise ValueError("query must have contiguous heads")
     if out is None:
-        out = torch.empty((Tq, nq, hs), dtype=torch.bfloat16, device=query.device)
+        out = _empty_on(stream, (Tq, nq, hs), torch.bfloat16, query.device)
     _need(out, "out", torch.bfloat16, 3)
     _contig(out, "out")
     if out.shape != (Tq, nq, hs):
         raise ValueError("out must be [num_q_tokens, num_q_heads, head_size]")
     need = kv4_pth_attention_workspace_size(m, Tq, S, nq, nkv, hs, max_query_len, max_seq_len)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+        workspace = _empty_on(stream, (need,), torch.uint8, query.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if softmax_scale is None:
@@ -481,7 +520,7 @@ def kv4_write_layout(key: torch.Tensor, value: torch.Tensor, cache: LayoutCache,
     rc = lib().kv4_write_layout(cache.mode, key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0),
                                 cache.key_ptr, cache.value_ptr, cache.k_scale_ptr, cache.v_scale_ptr,
                                 ctypes.byref(cache.layout), slot_mapping.data_ptr(), T, nkv, hs,
-                                hs & -hs if b is None else b, cache.block_size, cache.num_blocks,
+                                _b(b), cache.block_size, cache.num_blocks,
                                 sign_seed & (2 ** 64 - 1), _stream(stream))
     _check("kv4_write_layout", rc)
 
@@ -521,12 +560,12 @@ def kv4_attention_layout(query: torch.Tensor, cache: LayoutCache, block_table: t
     if query.stride(2) != 1 or query.stride(1) != hs:
         raise ValueError("query must have contiguous heads")
     if out is None:
-        out = torch.empty((Tq, nq, hs), dtype=torch.bfloat16, device=query.device)
+        out = _empty_on(stream, (Tq, nq, hs), torch.bfloat16, query.device)
     _need(out, "out", torch.bfloat16, 3)
     _contig(out, "out")
     need = kv4_attention_layout_workspace_size(cache, Tq, S, nq, max_query_len, max_seq_len)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+        workspace = _empty_on(stream, (need,), torch.uint8, query.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if softmax_scale is None:
@@ -535,7 +574,7 @@ def kv4_attention_layout(query: torch.Tensor, cache: LayoutCache, block_table: t
         cache.mode, query.data_ptr(), query.stride(0), cache.key_ptr, cache.value_ptr, cache.k_scale_ptr,
         cache.v_scale_ptr, ctypes.byref(cache.layout), cache.num_blocks, block_table.data_ptr(),
         block_table.shape[1], seq_lens.data_ptr(), query_start_loc.data_ptr(), S, Tq, int(max_query_len),
-        int(max_seq_len), nq, cache.num_kv_heads, hs, hs & -hs if b is None else b, cache.block_size,
+        int(max_seq_len), nq, cache.num_kv_heads, hs, _b(b), cache.block_size,
         sign_seed & (2 ** 64 - 1), int(sliding_window), float(softmax_scale), out.data_ptr(), ws_ptr, ws_bytes,
         _stream(stream))
     _check("kv4_attention_layout", rc)
@@ -552,10 +591,10 @@ def kv4_dequant_layout(cache: LayoutCache, which: str, slot_mapping: torch.Tenso
         raise ValueError("which must be 'k' or 'v'")
     T = slot_mapping.shape[0]
     hs, nkv = cache.head_size, cache.num_kv_heads
-    out = torch.empty((T, nkv, hs), dtype=torch.float32, device=slot_mapping.device)
+    out = _empty_on(stream, (T, nkv, hs), torch.float32, slot_mapping.device)
     codes, scales = (cache.key_ptr, cache.k_scale_ptr) if which == "k" else (cache.value_ptr, cache.v_scale_ptr)
     rc = lib().kv4_dequant_layout(cache.mode, codes, scales, ctypes.byref(cache.layout), cache.num_blocks,
-                                  slot_mapping.data_ptr(), T, nkv, hs, hs & -hs if b is None else b,
+                                  slot_mapping.data_ptr(), T, nkv, hs, _b(b),
                                   cache.block_size, sign_seed & (2 ** 64 - 1), 1 if inverse_rotate else 0,
                                   out.data_ptr(), _stream(stream))
     _check("kv4_dequant_layout", rc)

@@ -20,8 +20,8 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
-int fail(int code, const char* fmt, ...) {
+kv4_status fail(kv4_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kv4_status fail(kv4_status code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -31,17 +31,19 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int ok() {
+kv4_status ok() {
   g_last_error.clear();
   return KV4_OK;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_head(int32_t head_size, int32_t b) {
+// b == 0 asks for the rule's value: the largest power of two dividing head_size.
+kv4_status check_head(int32_t head_size, int32_t& b) {
   if (head_size < 8 || head_size > 256 || head_size % 8 != 0)
     return fail(KV4_EINVAL, "head_size must be a multiple of 8 in [8, 256], got %d", head_size);
   const int32_t want = head_size & -head_size;
+  if (b == 0) b = want;
   if (b != want)
     return fail(KV4_EINVAL,
                 "b must be the largest power of two dividing head_size (%d for head_size %d), got %d",
@@ -49,7 +51,7 @@ int check_head(int32_t head_size, int32_t b) {
   return KV4_OK;
 }
 
-int hip_status(hipError_t e, const char* what) {
+kv4_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(KV4_EHIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
 }
@@ -86,7 +88,7 @@ int mfma_hpw_max(int hs) { return hs == 192 ? 1 : 2; }
 // launch agree. Path 1 (matrix cores) is used where the query block is dense
 // (GQA group > 1 or query_len > 1), the head size is a multiple of 32 the
 // kernel is built for, and pages hold a power-of-two number (>= 16) of tokens.
-int make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
+kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
               int32_t max_query_len, int32_t max_seq_len, int32_t block_size, const kv4::CacheLayout& lay,
               kv4::AttnPlan& p) {
   std::memset(&p, 0, sizeof(p));
@@ -238,7 +240,7 @@ WsLayout ws_layout(const kv4::AttnPlan& p, int64_t num_q_tokens, int32_t num_seq
   return w;
 }
 
-int check_attn_sizes(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
+kv4_status check_attn_sizes(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
                      int32_t max_query_len, int32_t max_seq_len) {
   if (num_q_tokens < 0 || num_q_tokens > INT32_MAX)
     return fail(KV4_EINVAL, "num_q_tokens out of range: %lld", (long long)num_q_tokens);
@@ -252,13 +254,13 @@ int check_attn_sizes(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t
   return KV4_OK;
 }
 
-int check_mode(int32_t mode) {
+kv4_status check_mode(int32_t mode) {
   if (mode != 1 && mode != 2)
     return fail(KV4_EINVAL, "kv_quant_mode must be 1 (int8) or 2 (fp8 e4m3fn), got %d", mode);
   return KV4_OK;
 }
 
-int check_head_pth(int32_t head_size) {
+kv4_status check_head_pth(int32_t head_size) {
   if (head_size < 8 || head_size > 256 || head_size % 8 != 0)
     return fail(KV4_EINVAL, "head_size must be a multiple of 8 in [8, 256], got %d", head_size);
   return KV4_OK;
@@ -297,7 +299,7 @@ int bs_shift_of(int32_t bs) { return (bs & (bs - 1)) == 0 ? __builtin_ctz((unsig
 // A caller-described layout: positive strides, code strides multiples of the
 // kernels' access width (4 bytes int4, 8 bytes int8 / fp8). Rows are not
 // checked for overlap (the caller's layout must keep them apart).
-int check_layout(int qm, const kv4::CacheLayout& l) {
+kv4_status check_layout(int qm, const kv4::CacheLayout& l) {
   const int64_t A = qm ? 8 : 4;
   if (l.blk <= 0 || l.tok <= 0 || l.head <= 0 || l.sblk <= 0 || l.stok <= 0 || l.shead <= 0)
     return fail(KV4_EINVAL, "layout strides must be positive");
@@ -321,13 +323,13 @@ kv4::CacheLayout to_layout(const kv4_cache_layout* l) {
 // Debug check (KV4_CHECK_SLOTS=1): the slot map is copied to the host (the
 // call then waits for the stream) and every slot in [0, num_slots) must
 // appear at most once -- two tokens in one slot would race.
-int check_unique_slots(const char* what, const int64_t* slot_mapping, int64_t num_tokens, int64_t num_slots,
+kv4_status check_unique_slots(const char* what, const int64_t* slot_mapping, int64_t num_tokens, int64_t num_slots,
                        hipStream_t stream) {
   std::vector<int64_t> h((size_t)num_tokens);
-  if (int e = hip_status(hipMemcpyAsync(h.data(), slot_mapping, (size_t)num_tokens * sizeof(int64_t),
+  if (kv4_status e = hip_status(hipMemcpyAsync(h.data(), slot_mapping, (size_t)num_tokens * sizeof(int64_t),
                                         hipMemcpyDeviceToHost, stream), what))
     return e;
-  if (int e = hip_status(hipStreamSynchronize(stream), what)) return e;
+  if (kv4_status e = hip_status(hipStreamSynchronize(stream), what)) return e;
   std::unordered_map<int64_t, int64_t> first;
   first.reserve((size_t)num_tokens);
   for (int64_t t = 0; t < num_tokens; ++t) {
@@ -341,7 +343,7 @@ int check_unique_slots(const char* what, const int64_t* slot_mapping, int64_t nu
   return KV4_OK;
 }
 
-int write_impl(int qm, const char* what, const void* key, const void* value, int64_t key_token_stride,
+kv4_status write_impl(int qm, const char* what, const void* key, const void* value, int64_t key_token_stride,
                int64_t value_token_stride, void* key_cache, void* value_cache, float* k_scale_cache,
                float* v_scale_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                int32_t head_size, int32_t b, int32_t block_size, int64_t num_blocks, uint64_t sign_seed,
@@ -365,9 +367,9 @@ int write_impl(int qm, const char* what, const void* key, const void* value, int
     return fail(KV4_EINVAL, "misaligned pointer (K/V and caches need 16 bytes)");
   const kv4::CacheLayout lay =
       layout ? *layout : kv4::packed_layout(num_kv_heads, (int)code_row_bytes(qm, head_size), block_size);
-  if (int e = check_layout(qm, lay)) return e;
+  if (kv4_status e = check_layout(qm, lay)) return e;
   if (env_long("KV4_CHECK_SLOTS", 0) != 0) {
-    if (int e = check_unique_slots(what, slot_mapping, num_tokens, num_blocks * block_size,
+    if (kv4_status e = check_unique_slots(what, slot_mapping, num_tokens, num_blocks * block_size,
                                    static_cast<hipStream_t>(stream)))
       return e;
   }
@@ -394,7 +396,7 @@ int write_impl(int qm, const char* what, const void* key, const void* value, int
   return hip_status(kv4::launch_write(a, static_cast<hipStream_t>(stream)), what);
 }
 
-int dequant_impl(int qm, const char* what, const void* cache, const float* scale_cache, int64_t num_blocks,
+kv4_status dequant_impl(int qm, const char* what, const void* cache, const float* scale_cache, int64_t num_blocks,
                  const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads, int32_t head_size,
                  int32_t b, int32_t block_size, uint64_t sign_seed, int32_t inverse_rotate, float* out,
                  void* stream, const kv4::CacheLayout* layout = nullptr) {
@@ -409,7 +411,7 @@ int dequant_impl(int qm, const char* what, const void* cache, const float* scale
     return fail(KV4_EINVAL, "misaligned pointer");
   const kv4::CacheLayout lay =
       layout ? *layout : kv4::packed_layout(num_kv_heads, (int)code_row_bytes(qm, head_size), block_size);
-  if (int e = check_layout(qm, lay)) return e;
+  if (kv4_status e = check_layout(qm, lay)) return e;
   kv4::DequantArgs a;
   a.cache = static_cast<const uint8_t*>(cache);
   a.scale = scale_cache;
@@ -452,7 +454,7 @@ size_t workspace_impl(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nu
   return need;
 }
 
-int attention_impl(int qm, const void* query, int64_t query_token_stride, const void* key_cache,
+kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride, const void* key_cache,
                    const void* value_cache, const float* k_scale_cache, const float* v_scale_cache,
                    int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
                    const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
@@ -460,7 +462,7 @@ int attention_impl(int qm, const void* query, int64_t query_token_stride, const 
                    int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size, uint64_t sign_seed,
                    float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
                    const kv4::CacheLayout* layout = nullptr, int32_t window = 0) {
-  if (int e = check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
+  if (kv4_status e = check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
                                max_seq_len))
     return e;
   if (block_size < 1 || block_size > 4096) return fail(KV4_EINVAL, "block_size must be in [1, 4096]");
@@ -486,8 +488,8 @@ int attention_impl(int qm, const void* query, int64_t query_token_stride, const 
   std::memset(&a, 0, sizeof(a));
   if (num_blocks < 1) return fail(KV4_EINVAL, "num_blocks must be >= 1 when there are query tokens");
   a.lay = layout ? *layout : kv4::packed_layout(num_kv_heads, (int)code_row_bytes(qm, head_size), block_size);
-  if (int e = check_layout(qm, a.lay)) return e;
-  if (int e = make_plan(qm, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
+  if (kv4_status e = check_layout(qm, a.lay)) return e;
+  if (kv4_status e = make_plan(qm, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
                        max_seq_len, block_size, a.lay, a.plan))
     return e;
   const WsLayout ws = ws_layout(a.plan, num_q_tokens, num_seqs, num_q_heads, head_size);
@@ -538,10 +540,10 @@ int attention_impl(int qm, const void* query, int64_t query_token_stride, const 
   if (a.plan.path == 1) {
     const int64_t max_units =
         a.plan.n_qtiles * a.plan.n_head_tiles * (num_kv_heads / a.plan.hpw) * a.plan.num_splits;
-    if (int e = hip_status(kv4::launch_attn_mfma(a, prefix, max_units, st), "kv4_paged_attention launch"))
+    if (kv4_status e = hip_status(kv4::launch_attn_mfma(a, prefix, max_units, st), "kv4_paged_attention launch"))
       return e;
   } else {
-    if (int e = hip_status(kv4::launch_attn_valu(a, st), "kv4_paged_attention launch")) return e;
+    if (kv4_status e = hip_status(kv4::launch_attn_valu(a, st), "kv4_paged_attention launch")) return e;
   }
   if (a.plan.sk || a.plan.num_splits > 1) {
     // Many rows: one row per lane group (a quarter of the waves at head size
@@ -563,23 +565,33 @@ extern "C" {
 
 const char* kv4_last_error(void) { return g_last_error.c_str(); }
 
-int kv4_rht_write(const void* key, const void* value, int64_t key_token_stride,
+kv4_status kv4_stream_read(const void* buffer, int64_t bytes, uint32_t* sink, int32_t grid, void* stream) {
+  if (bytes < 0 || bytes % 16) return fail(KV4_EINVAL, "bytes must be a non-negative multiple of 16");
+  if (grid < 1 || grid > 65536) return fail(KV4_EINVAL, "grid must be in [1, 65536], got %d", grid);
+  if (bytes == 0) return ok();
+  if (!buffer || !sink) return fail(KV4_EINVAL, "null pointer argument");
+  if (!aligned(buffer, 16) || !aligned(sink, 4)) return fail(KV4_EINVAL, "misaligned pointer");
+  return hip_status(kv4::launch_stream_read(buffer, bytes, sink, grid, static_cast<hipStream_t>(stream)),
+                    "kv4_stream_read");
+}
+
+kv4_status kv4_rht_write(const void* key, const void* value, int64_t key_token_stride,
                   int64_t value_token_stride, void* key_cache, void* value_cache,
                   float* k_scale_cache, float* v_scale_cache, const int64_t* slot_mapping,
                   int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b,
                   int32_t block_size, int64_t num_blocks, uint64_t sign_seed, void* stream) {
-  if (int e = check_head(head_size, b)) return e;
+  if (kv4_status e = check_head(head_size, b)) return e;
   return write_impl(0, "kv4_rht_write", key, value, key_token_stride, value_token_stride, key_cache,
                     value_cache, k_scale_cache, v_scale_cache, slot_mapping, num_tokens, num_kv_heads,
                     head_size, b, block_size, num_blocks, sign_seed, stream);
 }
 
-int kv4_pth_write(int32_t kv_quant_mode, const void* key, const void* value, int64_t key_token_stride,
+kv4_status kv4_pth_write(int32_t kv_quant_mode, const void* key, const void* value, int64_t key_token_stride,
                   int64_t value_token_stride, void* key_cache, void* value_cache, float* k_scale_cache,
                   float* v_scale_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                   int32_t head_size, int32_t block_size, int64_t num_blocks, void* stream) {
-  if (int e = check_mode(kv_quant_mode)) return e;
-  if (int e = check_head_pth(head_size)) return e;
+  if (kv4_status e = check_mode(kv_quant_mode)) return e;
+  if (kv4_status e = check_head_pth(head_size)) return e;
   return write_impl(kv_quant_mode, "kv4_pth_write", key, value, key_token_stride, value_token_stride,
                     key_cache, value_cache, k_scale_cache, v_scale_cache, slot_mapping, num_tokens,
                     num_kv_heads, head_size, 0, block_size, num_blocks, 0, stream);
@@ -602,7 +614,7 @@ size_t kv4_pth_attention_workspace_size(int32_t kv_quant_mode, int64_t num_q_tok
 }
 
 
-int kv4_paged_attention(const void* query, int64_t query_token_stride, const void* key_cache,
+kv4_status kv4_paged_attention(const void* query, int64_t query_token_stride, const void* key_cache,
                         const void* value_cache, const float* k_scale_cache, const float* v_scale_cache,
                         int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
                         const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
@@ -610,22 +622,22 @@ int kv4_paged_attention(const void* query, int64_t query_token_stride, const voi
                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size, int32_t b,
                         int32_t block_size, uint64_t sign_seed, float softmax_scale, void* out,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  if (int e = check_head(head_size, b)) return e;
+  if (kv4_status e = check_head(head_size, b)) return e;
   return attention_impl(0, query, query_token_stride, key_cache, value_cache, k_scale_cache, v_scale_cache,
                         num_blocks, block_table, max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
                         num_q_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_size, b,
                         block_size, sign_seed, softmax_scale, out, workspace, workspace_bytes, stream);
 }
 
-int kv4_pth_attention(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
+kv4_status kv4_pth_attention(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
                       const void* key_cache, const void* value_cache, const float* k_scale_cache,
                       const float* v_scale_cache, int64_t num_blocks, const int32_t* block_table,
                       int32_t max_blocks_per_seq, const int32_t* seq_lens, const int32_t* query_start_loc,
                       int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len, int32_t max_seq_len,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                       float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (int e = check_mode(kv_quant_mode)) return e;
-  if (int e = check_head_pth(head_size)) return e;
+  if (kv4_status e = check_mode(kv_quant_mode)) return e;
+  if (kv4_status e = check_head_pth(head_size)) return e;
   return attention_impl(kv_quant_mode, query, query_token_stride, key_cache, value_cache, k_scale_cache,
                         v_scale_cache, num_blocks, block_table, max_blocks_per_seq, seq_lens, query_start_loc,
                         num_seqs, num_q_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_size,
@@ -633,25 +645,25 @@ int kv4_pth_attention(int32_t kv_quant_mode, const void* query, int64_t query_to
 }
 
 
-int kv4_dequant(const void* cache, const float* scale_cache, int64_t num_blocks, const int64_t* slot_mapping,
+kv4_status kv4_dequant(const void* cache, const float* scale_cache, int64_t num_blocks, const int64_t* slot_mapping,
                 int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size,
                 uint64_t sign_seed, int32_t inverse_rotate, float* out, void* stream) {
-  if (int e = check_head(head_size, b)) return e;
+  if (kv4_status e = check_head(head_size, b)) return e;
   return dequant_impl(0, "kv4_dequant", cache, scale_cache, num_blocks, slot_mapping, num_tokens, num_kv_heads,
                       head_size, b, block_size, sign_seed, inverse_rotate, out, stream);
 }
 
-int kv4_pth_dequant(int32_t kv_quant_mode, const void* cache, const float* scale_cache, int64_t num_blocks,
+kv4_status kv4_pth_dequant(int32_t kv_quant_mode, const void* cache, const float* scale_cache, int64_t num_blocks,
                     const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads, int32_t head_size,
                     int32_t block_size, float* out, void* stream) {
-  if (int e = check_mode(kv_quant_mode)) return e;
-  if (int e = check_head_pth(head_size)) return e;
+  if (kv4_status e = check_mode(kv_quant_mode)) return e;
+  if (kv4_status e = check_head_pth(head_size)) return e;
   return dequant_impl(kv_quant_mode, "kv4_pth_dequant", cache, scale_cache, num_blocks, slot_mapping, num_tokens,
                       num_kv_heads, head_size, 0, block_size, 0, 0, out, stream);
 }
 
 
-int kv4_cache_layout_packed(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+kv4_status kv4_cache_layout_packed(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                             kv4_cache_layout* layout) {
   if (kv_quant_mode < 0 || kv_quant_mode > 2) return fail(KV4_EINVAL, "kv_quant_mode must be 0, 1 or 2");
   if (num_kv_heads < 1 || head_size < 8 || head_size % 8 || block_size < 1 || !layout)
@@ -662,7 +674,7 @@ int kv4_cache_layout_packed(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t
   return ok();
 }
 
-int kv4_cache_layout_inline(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+kv4_status kv4_cache_layout_inline(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                             kv4_cache_layout* layout, int64_t* block_bytes, int64_t* value_offset,
                             int64_t* scale_offset) {
   if (kv_quant_mode < 0 || kv_quant_mode > 2) return fail(KV4_EINVAL, "kv_quant_mode must be 0, 1 or 2");
@@ -680,19 +692,19 @@ int kv4_cache_layout_inline(int32_t kv_quant_mode, int32_t num_kv_heads, int32_t
 }
 
 namespace {
-int check_any_mode(int32_t mode, int32_t head_size, int32_t b) {
+kv4_status check_any_mode(int32_t mode, int32_t head_size, int32_t& b) {
   if (mode == 0) return check_head(head_size, b);
-  if (int e = check_mode(mode)) return e;
+  if (kv4_status e = check_mode(mode)) return e;
   return check_head_pth(head_size);
 }
 }  // namespace
 
-int kv4_write_layout(int32_t kv_quant_mode, const void* key, const void* value, int64_t key_token_stride,
+kv4_status kv4_write_layout(int32_t kv_quant_mode, const void* key, const void* value, int64_t key_token_stride,
                      int64_t value_token_stride, void* key_cache, void* value_cache, float* k_scale_cache,
                      float* v_scale_cache, const kv4_cache_layout* layout, const int64_t* slot_mapping,
                      int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size,
                      int64_t num_blocks, uint64_t sign_seed, void* stream) {
-  if (int e = check_any_mode(kv_quant_mode, head_size, b)) return e;
+  if (kv4_status e = check_any_mode(kv_quant_mode, head_size, b)) return e;
   if (!layout) return fail(KV4_EINVAL, "null layout");
   const kv4::CacheLayout l = to_layout(layout);
   return write_impl(kv_quant_mode, "kv4_write_layout", key, value, key_token_stride, value_token_stride,
@@ -715,7 +727,7 @@ size_t kv4_attention_layout_workspace_size(int32_t kv_quant_mode, const kv4_cach
                         max_seq_len, &l);
 }
 
-int kv4_attention_layout(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
+kv4_status kv4_attention_layout(int32_t kv_quant_mode, const void* query, int64_t query_token_stride,
                          const void* key_cache, const void* value_cache, const float* k_scale_cache,
                          const float* v_scale_cache, const kv4_cache_layout* layout, int64_t num_blocks,
                          const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
@@ -724,7 +736,7 @@ int kv4_attention_layout(int32_t kv_quant_mode, const void* query, int64_t query
                          int32_t head_size, int32_t b, int32_t block_size, uint64_t sign_seed,
                          int32_t sliding_window, float softmax_scale, void* out, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  if (int e = check_any_mode(kv_quant_mode, head_size, b)) return e;
+  if (kv4_status e = check_any_mode(kv_quant_mode, head_size, b)) return e;
   if (!layout) return fail(KV4_EINVAL, "null layout");
   const kv4::CacheLayout l = to_layout(layout);
   return attention_impl(kv_quant_mode, query, query_token_stride, key_cache, value_cache, k_scale_cache,
@@ -734,11 +746,11 @@ int kv4_attention_layout(int32_t kv_quant_mode, const void* query, int64_t query
                         workspace, workspace_bytes, stream, &l, sliding_window);
 }
 
-int kv4_dequant_layout(int32_t kv_quant_mode, const void* cache, const float* scale_cache,
+kv4_status kv4_dequant_layout(int32_t kv_quant_mode, const void* cache, const float* scale_cache,
                        const kv4_cache_layout* layout, int64_t num_blocks, const int64_t* slot_mapping,
                        int64_t num_tokens, int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size,
                        uint64_t sign_seed, int32_t inverse_rotate, float* out, void* stream) {
-  if (int e = check_any_mode(kv_quant_mode, head_size, b)) return e;
+  if (kv4_status e = check_any_mode(kv_quant_mode, head_size, b)) return e;
   if (!layout) return fail(KV4_EINVAL, "null layout");
   const kv4::CacheLayout l = to_layout(layout);
   return dequant_impl(kv_quant_mode, "kv4_dequant_layout", cache, scale_cache, num_blocks, slot_mapping,

@@ -154,6 +154,7 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, unsigned int* sink, int grid, hipStream_t stream);
 // Device plan (work units per sequence, exclusive prefix into `prefix`,
 // num_seqs + 1 ints) followed by the matrix-core attention kernel.
 // In stream-K mode it sets a.plan.sk_grid, which the merge needs.
