@@ -1350,7 +1350,33 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
   }
 }
 
-static int g_num_cus = 0;
+// Attributes of the current device that the launch geometry depends on,
+// read once per device (several GPUs of different kinds may be used from one
+// process, from several threads).
+struct DevAttrs {
+  int dev;
+  int cus;
+  int lds_per_cu;
+};
+
+static DevAttrs device_attrs() {
+  static std::mutex mu;
+  static std::unordered_map<int, DevAttrs> by_dev;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = by_dev.find(dev);
+  if (it != by_dev.end()) return it->second;
+  DevAttrs d{dev, 256, 160 * 1024};
+  int v = 0;
+  if (dev >= 0 && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+    d.cus = v;
+  if (dev >= 0 && hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
+      v > 0)
+    d.lds_per_cu = v;
+  by_dev.emplace(dev, d);
+  return d;
+}
 
 // Sequences whose prefix the attention kernel computes itself (in LDS) when
 // that costs it no occupancy; longer batches run the plan kernel first.
@@ -1362,15 +1388,8 @@ constexpr size_t kFusedPlanLds = (kFusedPlanMaxSeqs + 1 + 16) * sizeof(int32_t);
 // and a kernel whose workgroups fill the CU to within a few hundred bytes
 // (head size 192, int8 / fp8: three of 50.4 KB) was measured to lose a
 // workgroup per CU with the plan LDS although the query said otherwise.
-static bool plan_lds_fits(const void* kernel, int resident) {
-  static int lds_per_cu = 0;
-  if (lds_per_cu == 0) {
-    int dev = 0, v = 0;
-    lds_per_cu = (hipGetDevice(&dev) == hipSuccess &&
-                  hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
-                  v > 0) ? v : 160 * 1024;
-  }
-  // static LDS of each kernel, looked up once
+static bool plan_lds_fits(const void* kernel, int resident, const DevAttrs& da) {
+  // static LDS of each kernel, looked up once (the same code object on every device)
   static std::mutex mu;
   static std::unordered_map<const void*, size_t> static_lds;
   size_t lds = 0;
@@ -1385,36 +1404,43 @@ static bool plan_lds_fits(const void* kernel, int resident) {
     lds = it->second;
   }
   const size_t per_wg = (lds + kFusedPlanLds + 1023) / 1024 * 1024;
-  const int per_cu = resident / (g_num_cus > 0 ? g_num_cus : 1);
-  return (size_t)per_cu * per_wg <= (size_t)lds_per_cu;
+  const int per_cu = resident / (da.cus > 0 ? da.cus : 1);
+  return (size_t)per_cu * per_wg <= (size_t)da.lds_per_cu;
 }
 
 // Workgroups of the kernel the GPU holds at once (fused: with the plan LDS).
+// (per device: the occupancy query is answered for the current device)
 template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB = 1, bool NT = false>
-static int resident_blocks(bool fused) {
-  static int per_cu[2] = {0, 0};
-  int& pc = per_cu[fused ? 1 : 0];
-  if (pc == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb,
-                                                     reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH, WIN, NRB, NT>),
-                                                     64 * mfma_wpb<HS, HPW, QM>(), fused ? kFusedPlanLds : 0) != hipSuccess ||
-        nb < 1)
-      nb = 1;
-    pc = nb;
+static int resident_blocks(bool fused, const DevAttrs& da) {
+  static std::mutex mu;
+  static std::unordered_map<int, int> per_cu;      // key: 2 * device + fused
+  const int key = 2 * da.dev + (fused ? 1 : 0);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = per_cu.find(key);
+    if (it != per_cu.end()) return it->second * da.cus;
   }
-  return pc * g_num_cus;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb,
+                                                   reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH, WIN, NRB, NT>),
+                                                   64 * mfma_wpb<HS, HPW, QM>(), fused ? kFusedPlanLds : 0) != hipSuccess ||
+      nb < 1)
+    nb = 1;
+  std::lock_guard<std::mutex> lock(mu);
+  per_cu.emplace(key, nb);
+  return nb * da.cus;
 }
 
 template <int HS, int QM, bool WIN>
 static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_units, hipStream_t stream) {
   if (a.plan.hpw == 4 && Geo<HS>::NVR != 1) return hipErrorInvalidValue;
   if (QM != 0 && (a.plan.hpw != 1 || a.plan.wpb != mfma_wpb<HS, 1, QM>())) return hipErrorInvalidValue;
-  // resident(fused) -> workgroups the GPU holds at once
+  // resident(fused, device) -> workgroups the GPU holds at once
+  const DevAttrs da = device_attrs();
   auto go = [&](auto kernel, int wpb, auto resident_of) {
-    const int plain = resident_of(false);
-    a.plan.fused_plan = (a.num_seqs <= kFusedPlanMaxSeqs && resident_of(true) == plain &&
-                         plan_lds_fits(reinterpret_cast<const void*>(kernel), plain)) ? 1 : 0;
+    const int plain = resident_of(false, da);
+    a.plan.fused_plan = (a.num_seqs <= kFusedPlanMaxSeqs && resident_of(true, da) == plain &&
+                         plan_lds_fits(reinterpret_cast<const void*>(kernel), plain, da)) ? 1 : 0;
     if (const char* f = std::getenv("KV4_FUSED_PLAN")) a.plan.fused_plan = a.plan.fused_plan && std::atoi(f) != 0;
     const int resident = plain;
     if (!a.plan.fused_plan)
@@ -1428,7 +1454,7 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
       wgs = a.plan.sk_grid;
     } else {
       wgs = (max_units + wpb - 1) / wpb;
-      const int64_t cap = (int64_t)g_num_cus * 8;
+      const int64_t cap = (int64_t)da.cus * 8;
       if (wgs > cap) wgs = cap;
       if (wgs < 1) wgs = 1;
     }
@@ -1439,19 +1465,19 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
     if constexpr (HS == 128) {
       if (a.code_nt) {
         go(attn_mfma_kernel<HS, 1, QM, false, WIN, 1, true>, mfma_wpb<HS, 1, QM>(),
-           [](bool f) { return resident_blocks<HS, 1, QM, false, WIN, 1, true>(f); });
+           [](bool f, const DevAttrs& d) { return resident_blocks<HS, 1, QM, false, WIN, 1, true>(f, d); });
         return hipSuccess;
       }
     }
-    go(attn_mfma_kernel<HS, 1, QM, false, WIN, 1>, mfma_wpb<HS, 1, QM>(), [](bool f) { return resident_blocks<HS, 1, QM, false, WIN>(f); });
+    go(attn_mfma_kernel<HS, 1, QM, false, WIN, 1>, mfma_wpb<HS, 1, QM>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 1, QM, false, WIN>(f, d); });
     return hipSuccess;
   }
   if (a.plan.vjh) {
     if constexpr (HS == 128) {
       if (a.plan.hpw == 2) {
-        go(attn_mfma_kernel<HS, 2, 0, true, WIN, 1>, mfma_wpb<HS, 2, 0>(), [](bool f) { return resident_blocks<HS, 2, 0, true, WIN>(f); });
+        go(attn_mfma_kernel<HS, 2, 0, true, WIN, 1>, mfma_wpb<HS, 2, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 2, 0, true, WIN>(f, d); });
       } else if (a.plan.hpw == 4) {
-        go(attn_mfma_kernel<HS, 4, 0, true, WIN, 1>, mfma_wpb<HS, 4, 0>(), [](bool f) { return resident_blocks<HS, 4, 0, true, WIN>(f); });
+        go(attn_mfma_kernel<HS, 4, 0, true, WIN, 1>, mfma_wpb<HS, 4, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 4, 0, true, WIN>(f, d); });
       } else {
         return hipErrorInvalidValue;
       }
@@ -1461,7 +1487,7 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
   }
   if (a.plan.rb == 2) {
     if constexpr (HS <= 128) {
-      go(attn_mfma_kernel<HS, 1, 0, false, WIN, 2>, mfma_wpb<HS, 1, 0>(), [](bool f) { return resident_blocks<HS, 1, 0, false, WIN, 2>(f); });
+      go(attn_mfma_kernel<HS, 1, 0, false, WIN, 2>, mfma_wpb<HS, 1, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 1, 0, false, WIN, 2>(f, d); });
       return hipSuccess;
     }
     return hipErrorInvalidValue;
@@ -1469,23 +1495,23 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
   if constexpr (HS == 128) {
     if (a.code_nt && a.plan.hpw == 2) {
       go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1, true>, mfma_wpb<HS, 2, 0>(),
-         [](bool f) { return resident_blocks<HS, 2, 0, false, WIN, 1, true>(f); });
+         [](bool f, const DevAttrs& d) { return resident_blocks<HS, 2, 0, false, WIN, 1, true>(f, d); });
       return hipSuccess;
     }
     if (a.code_nt && a.plan.hpw == 4) {
       go(attn_mfma_kernel<HS, 4, 0, false, WIN, 1, true>, mfma_wpb<HS, 4, 0>(),
-         [](bool f) { return resident_blocks<HS, 4, 0, false, WIN, 1, true>(f); });
+         [](bool f, const DevAttrs& d) { return resident_blocks<HS, 4, 0, false, WIN, 1, true>(f, d); });
       return hipSuccess;
     }
   }
   switch (a.plan.hpw) {
-    case 2: go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1>, mfma_wpb<HS, 2, 0>(), [](bool f) { return resident_blocks<HS, 2, 0, false, WIN>(f); }); break;
+    case 2: go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1>, mfma_wpb<HS, 2, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 2, 0, false, WIN>(f, d); }); break;
     case 4:
       // four heads' V loads of a step must fit the 6-bit load counter
       if constexpr (Geo<HS>::NVR == 1)
-        go(attn_mfma_kernel<HS, 4, 0, false, WIN, 1>, mfma_wpb<HS, 4, 0>(), [](bool f) { return resident_blocks<HS, 4, 0, false, WIN>(f); });
+        go(attn_mfma_kernel<HS, 4, 0, false, WIN, 1>, mfma_wpb<HS, 4, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 4, 0, false, WIN>(f, d); });
       break;
-    default: go(attn_mfma_kernel<HS, 1, 0, false, WIN, 1>, mfma_wpb<HS, 1, 0>(), [](bool f) { return resident_blocks<HS, 1, 0, false, WIN>(f); }); break;
+    default: go(attn_mfma_kernel<HS, 1, 0, false, WIN, 1>, mfma_wpb<HS, 1, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 1, 0, false, WIN>(f, d); }); break;
   }
   return hipSuccess;
 }
@@ -1498,14 +1524,6 @@ static hipError_t launch_hs(AttnArgs& a, const int32_t* prefix, int64_t max_unit
 
 hipError_t launch_attn_mfma(AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream) {
   hipError_t e = hipSuccess;
-  if (g_num_cus == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-      g_num_cus = cus;
-    else
-      g_num_cus = 256;
-  }
   if (a.qm == 0) {
     switch (a.hs) {
       case 64: e = launch_hs<64, 0>(a, prefix, max_units, stream); break;
