@@ -190,6 +190,36 @@ kv4_status kv4_paged_attention(const void* query, int64_t query_token_stride,
                                void* stream);
 
 /*
+ * kv4_paged_attention_noalloc -- kv4_paged_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * must not call hipMalloc, harnesses that forbid it). Same arguments, results
+ * and errors, without the workspace: the split partials live in a static
+ * device array of KV4_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held from the library's first use on that GPU until the process ends. The
+ * call allocates and frees nothing. A batch whose plan needs more scratch than
+ * that returns KV4_EWORKSPACE before any launch (the single-token decode
+ * batches of the Phi-3, Llama-3.2-1B and Llama-3-8B shaped workloads need
+ * 5-50 MB; a mixed batch with 512-token prefill chunks or many-token decode
+ * needs more). All calls on one GPU share its array: two calls whose kernels may
+ * run at the same time on one GPU (different streams, or the same stream
+ * from several threads without ordering) race and give wrong results. The
+ * array needs no initialization and keeps the last call's contents.
+ */
+#define KV4_NOALLOC_SCRATCH_BYTES (64u << 20)
+kv4_status kv4_paged_attention_noalloc(const void* query, int64_t query_token_stride,
+                                       const void* key_cache, const void* value_cache,
+                                       const float* k_scale_cache, const float* v_scale_cache,
+                                       int64_t num_blocks,
+                                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, const int32_t* query_start_loc,
+                                       int32_t num_seqs, int64_t num_q_tokens,
+                                       int32_t max_query_len, int32_t max_seq_len,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_size, int32_t b, int32_t block_size,
+                                       uint64_t sign_seed, float softmax_scale,
+                                       void* out, void* stream);
+
+/*
  * kv4_dequant -- gather and dequantize cache slots (for tests and debugging;
  * the round-trip check of [PR62881] Fix).
  *   out[t, h, i] = code * scale  (one float32 product), and with

@@ -50,6 +50,10 @@ _SIGNATURES = {
                                            _vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32, _c_int32,
                                            _c_int32, _c_int32, _c_int32, _c_int32, _c_uint64,
                                            ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
+    "kv4_paged_attention_noalloc": (ctypes.c_int, [_vp, _c_int64, _vp, _vp, _vp, _vp, _c_int64, _vp, _c_int32,
+                                                   _vp, _vp, _c_int32, _c_int64, _c_int32, _c_int32, _c_int32,
+                                                   _c_int32, _c_int32, _c_int32, _c_int32, _c_uint64,
+                                                   ctypes.c_float, _vp, _vp]),
     "kv4_dequant": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _c_int64, _c_int32, _c_int32, _c_int32,
                                    _c_int32, _c_uint64, _c_int32, _vp, _vp]),
     "kv4_last_error": (ctypes.c_char_p, []),
@@ -271,6 +275,52 @@ def kv4_paged_attention(query: torch.Tensor, key_cache: torch.Tensor, value_cach
         int(max_query_len), int(max_seq_len), nq, nkv, hs, _b(b), bs,
         sign_seed & (2 ** 64 - 1), float(softmax_scale), out.data_ptr(), ws_ptr, ws_bytes, _stream(stream))
     _check("kv4_paged_attention", rc)
+    return out
+
+
+KV4_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def kv4_paged_attention_noalloc(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                                k_scale_cache: torch.Tensor, v_scale_cache: torch.Tensor,
+                                block_table: torch.Tensor, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                                max_query_len: int, max_seq_len: int, out: torch.Tensor,
+                                softmax_scale: Optional[float] = None, sign_seed: int = DEFAULT_SIGN_SEED,
+                                b: Optional[int] = None, stream=None) -> torch.Tensor:
+    """kv4_paged_attention without a workspace and without any allocation:
+    the caller passes `out` (bf16 [Tq, nq, hs]); the split partials use the
+    library's static per-GPU scratch (KV4_NOALLOC_SCRATCH_BYTES). Calls whose
+    kernels may overlap on one GPU race on that scratch."""
+    for t, n, dt, nd in ((query, "query", torch.bfloat16, 3), (key_cache, "key_cache", torch.uint8, 4),
+                         (value_cache, "value_cache", torch.uint8, 4), (k_scale_cache, "k_scale_cache", torch.float32, 3),
+                         (v_scale_cache, "v_scale_cache", torch.float32, 3), (block_table, "block_table", torch.int32, 2),
+                         (seq_lens, "seq_lens", torch.int32, 1), (query_start_loc, "query_start_loc", torch.int32, 1),
+                         (out, "out", torch.bfloat16, 3)):
+        _need(t, n, dt, nd)
+        if n != "query":
+            _contig(t, n)
+    Tq, nq, hs = query.shape
+    nb, bs, nkv = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]
+    S = seq_lens.shape[0]
+    if key_cache.shape[3] != hs // 2 or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shapes disagree with query head_size")
+    if k_scale_cache.shape != (nb, bs, nkv) or v_scale_cache.shape != k_scale_cache.shape:
+        raise ValueError("scale cache shapes disagree with the caches")
+    if query_start_loc.shape[0] != S + 1 or block_table.shape[0] != S:
+        raise ValueError("query_start_loc must be [num_seqs + 1] and block_table [num_seqs, *]")
+    if query.stride(2) != 1 or query.stride(1) != hs:
+        raise ValueError("query must have contiguous heads")
+    if out.shape != (Tq, nq, hs):
+        raise ValueError("out must be [num_q_tokens, num_q_heads, head_size]")
+    if softmax_scale is None:
+        softmax_scale = hs ** -0.5
+    rc = lib().kv4_paged_attention_noalloc(
+        query.data_ptr(), query.stride(0), key_cache.data_ptr(), value_cache.data_ptr(),
+        k_scale_cache.data_ptr(), v_scale_cache.data_ptr(), nb, block_table.data_ptr(),
+        block_table.shape[1], seq_lens.data_ptr(), query_start_loc.data_ptr(), S, Tq,
+        int(max_query_len), int(max_seq_len), nq, nkv, hs, _b(b), bs,
+        sign_seed & (2 ** 64 - 1), float(softmax_scale), out.data_ptr(), _stream(stream))
+    _check("kv4_paged_attention_noalloc", rc)
     return out
 
 

@@ -10,11 +10,19 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <unordered_map>
 #include <vector>
 #include <string>
 
 #include "kv4_launch.hpp"
+
+// Device memory of kv4_paged_attention_noalloc: its split partials and
+// sequence prefix, in place of a caller workspace. Every GPU the library runs
+// on holds its own copy from the library's first use there until the process
+// ends. In host code `scratch` names a host-side stand-in: only the address
+// hipGetSymbolAddress returns for the current device may reach a kernel.
+static __device__ __align__(256) unsigned char scratch[KV4_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -559,11 +567,62 @@ kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride,
   return ok();
 }
 
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr with the error set if
+// the lookup fails.
+void* scratch_on_current_device() {
+  static std::mutex mu;
+  static std::unordered_map<int, void*> by_dev;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    fail(KV4_EHIP, "kv4_paged_attention_noalloc: no current HIP device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = by_dev.find(dev);
+  if (it != by_dev.end()) return it->second;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    fail(KV4_EHIP, "kv4_paged_attention_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+         hipGetErrorString(e));
+    return nullptr;
+  }
+  by_dev.emplace(dev, ptr);
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* kv4_last_error(void) { return g_last_error.c_str(); }
+
+kv4_status kv4_paged_attention_noalloc(const void* query, int64_t query_token_stride, const void* key_cache,
+                                       const void* value_cache, const float* k_scale_cache,
+                                       const float* v_scale_cache, int64_t num_blocks, const int32_t* block_table,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                       const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
+                                       int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size,
+                                       uint64_t sign_seed, float softmax_scale, void* out, void* stream) {
+  if (kv4_status e = check_head(head_size, b)) return e;
+  void* ws = scratch_on_current_device();
+  if (!ws) return KV4_EHIP;
+  const kv4_status st =
+      attention_impl(0, query, query_token_stride, key_cache, value_cache, k_scale_cache, v_scale_cache,
+                     num_blocks, block_table, max_blocks_per_seq, seq_lens, query_start_loc, num_seqs, num_q_tokens,
+                     max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_size, b, block_size, sign_seed,
+                     softmax_scale, out, ws, (size_t)KV4_NOALLOC_SCRATCH_BYTES, stream);
+  if (st == KV4_EWORKSPACE) {
+    const std::string why = g_last_error;
+    return fail(KV4_EWORKSPACE,
+                "kv4_paged_attention_noalloc: %s; the static scratch holds %zu bytes -- call "
+                "kv4_paged_attention with a caller workspace for this batch",
+                why.c_str(), (size_t)KV4_NOALLOC_SCRATCH_BYTES);
+  }
+  return st;
+}
 
 kv4_status kv4_stream_read(const void* buffer, int64_t bytes, uint32_t* sink, int32_t grid, void* stream) {
   if (bytes < 0 || bytes % 16) return fail(KV4_EINVAL, "bytes must be a non-negative multiple of 16");

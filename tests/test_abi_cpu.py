@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
         "kv4_pth_write", "kv4_pth_dequant", "kv4_pth_attention", "kv4_pth_attention_workspace_size",
         "kv4_cache_layout_packed", "kv4_cache_layout_inline", "kv4_write_layout",
         "kv4_attention_layout_workspace_size", "kv4_attention_layout", "kv4_dequant_layout",
-        "kv4_stream_read"])
+        "kv4_stream_read", "kv4_paged_attention_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(L):

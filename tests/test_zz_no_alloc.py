@@ -1,0 +1,65 @@
+"""kv4_paged_attention_noalloc (static per-GPU scratch, no allocation)
+against kv4_paged_attention (caller workspace) on the same inputs: two calls
+in a row, the second with a smaller batch, each bit-identical to the
+workspace entry point (same plan, same kernels) and within G2 of the oracle;
+and a batch that needs more than the static scratch is refused before any
+launch."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import DEV, W, allclose_report, host, kv4, oracle_attention_on_gpu_cache, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(w):
+    r = run_gpu(w)                                    # kv4_paged_attention with the binding's workspace
+    lay = r.lay
+    bt, slens, qsl = (torch.from_numpy(x).to(DEV) for x in (lay.block_table, lay.seq_lens, lay.query_start_loc))
+    out = torch.full((w.num_q_tokens, w.num_q_heads, w.head_size), 5.0, dtype=torch.bfloat16, device=DEV)
+    kv4.kv4_paged_attention_noalloc(r.t.query.to(DEV), r.kc, r.vc, r.ks, r.vs, bt, slens, qsl,
+                                    max_query_len=w.max_query_len, max_seq_len=w.max_seq_len, out=out,
+                                    sign_seed=w.sign_seed)
+    torch.cuda.synchronize()
+    return r, out
+
+
+def test_noalloc_matches_workspace_entry_point_twice():
+    cases = [
+        # stream-K decode, GQA 4, several thousand keys: partials in the scratch
+        W.custom("noalloc_big", 32, 8, 128, [1] * 24, [int(x) for x in np.linspace(40, 9000, 24)],
+                 outlier_frac=0.01),
+        # then a smaller batch of another shape (head size 96, split-KV multi-token tiles)
+        W.custom("noalloc_small", 8, 2, 96, [3, 1, 5], [700, 33, 260], seed=3),
+    ]
+    for w in cases:
+        need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, w.num_q_heads,
+                                                      w.num_kv_heads, w.head_size, w.max_query_len,
+                                                      w.max_seq_len)
+        assert 0 < need <= kv4.KV4_NOALLOC_SCRATCH_BYTES
+        r, out = _both(w)
+        got = host(out.float())
+        assert np.array_equal(got, host(r.out.float())), "noalloc differs from the workspace entry point"
+        ref = oracle_attention_on_gpu_cache(r)
+        nbad, mx = allclose_report(got, ref, atol=1e-2, rtol=1e-2)
+        say(f"    {w.name}: workspace {need} B; bit-identical; G2 max abs err {mx:.3e}")
+        assert nbad == 0
+
+
+def test_noalloc_refuses_batches_beyond_the_scratch():
+    w = W.ALL["qwen_mixed"]()
+    need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                                  w.head_size, w.max_query_len, w.max_seq_len)
+    assert need > kv4.KV4_NOALLOC_SCRATCH_BYTES
+    r = run_gpu(w, attention=False)
+    lay = r.lay
+    bt, slens, qsl = (torch.from_numpy(x).to(DEV) for x in (lay.block_table, lay.seq_lens, lay.query_start_loc))
+    out = torch.full((w.num_q_tokens, w.num_q_heads, w.head_size), 5.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(kv4.Kv4Error) as ei:
+        kv4.kv4_paged_attention_noalloc(r.t.query.to(DEV), r.kc, r.vc, r.ks, r.vs, bt, slens, qsl,
+                                        max_query_len=w.max_query_len, max_seq_len=w.max_seq_len, out=out,
+                                        sign_seed=w.sign_seed)
+    assert ei.value.code == kv4.KV4_EWORKSPACE and "static scratch" in str(ei.value)
+    torch.cuda.synchronize()
+    assert host(out.float()).min() == 5.0 and host(out.float()).max() == 5.0   # nothing was launched
