@@ -174,6 +174,11 @@ __device__ __forceinline__ float group_sum_ct(float v) {
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // floor(num / den) for 0 <= num < 2^53, den > 0: a correctly rounded double
 // quotient is within one of the floor, and one integer step fixes it (far

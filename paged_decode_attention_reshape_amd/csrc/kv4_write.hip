@@ -24,6 +24,7 @@
 namespace kv4 {
 
 typedef __bf16 bf16x2_rt __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // rint_half_even(fl(y / scale)) for the IEEE float32 quotient the write rule
 // uses, for all 8 values of a lane. The quotients are first taken as y * rcp
@@ -169,10 +170,36 @@ __device__ __forceinline__ int64_t slot_page(const Args& a, int64_t slot) {
   return a.bs_shift >= 0 ? (slot >> a.bs_shift) : slot / a.bs;
 }
 
+// scale = RN(amax / QMAX) without the division sequence: q0 = RN(amax * c),
+// c = RN(1 / QMAX); r = amax - q0 * QMAX is exact in one fma; RN(q0 + r * c)
+// is the correctly rounded quotient. Checked exhaustively on the host against
+// IEEE float32 division: for QMAX 7 and 127 on every non-negative finite
+// float32, for 448 on every non-negative finite bf16 value (amax is always one:
+// the inputs are bf16 and the rotated values are rounded to bf16 first).
+template <int QMAX>
+__device__ __forceinline__ float div_by_qmax(float amax) {
+  constexpr float c = 1.0f / (float)QMAX;
+  const float q0 = amax * c;
+  const float r = fmaf(-q0, (float)QMAX, amax);
+  return fmaf(r, c, q0);
+}
+
 // At most 96 scalar registers: eight waves per SIMD (101 left it at seven).
-template <int LP, int QM>
+//
+// A wave takes one token per iteration: its K head vectors, then its V head
+// vectors, in slices of VPW = 64 / LP heads of one kind (ceil(nkv / VPW)
+// slices per kind), U slices loaded before any of them is computed. The
+// token, its slot, page and row bases are wave-uniform (scalar registers and
+// scalar ALU); a lane adds a 32-bit offset fixed before the loop (its head
+// within the slice and its 8-element chunk). The input rows are read whatever
+// the slot (a skipped token's row is still a valid row), so no load waits for
+// the slot; lanes past the heads or chunks read a clamped address of the same
+// row and drop the value, so the loads carry no branch and stay in flight
+// together.
+template <int LP, int QM, int U>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96))) void write_kernel(WriteArgs a) {
-  constexpr int VPW = kWave / LP;                      // vectors per wave
+  constexpr int VPW = kWave / LP;                      // heads per slice
+  constexpr int CB = QM == 0 ? 4 : 8;                  // code bytes per lane (8 elements)
   const int lane = threadIdx.x & (kWave - 1);
   const int jj = lane & (LP - 1);                      // chunk index in the vector
   const int grp = lane / LP;
@@ -182,108 +209,113 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96))) void writ
   uint32_t sx[4] = {0u, 0u, 0u, 0u};
   if constexpr (QM == 0) sign_xor_bf16x8(lane_on ? sign_bits8(a.seed, jj) : 0u, sx);
 
-  const int64_t n_items = a.num_tokens * 2 * a.nkv;
-  const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  const int nkv = a.nkv;
+  const int spk = (nkv + VPW - 1) / VPW;               // slices per kind
+  const int spt = 2 * spk;                             // slices per token
+  // lane offset within a slice's input (bytes from the slice's first head),
+  // clamped into the row; and within a slice's cache row
+  const uint32_t in_off = (uint32_t)(grp * a.hs * 2 + 16 * min(jj, nchunk - 1));
+  const int64_t c_off = (int64_t)grp * a.lay.head + CB * jj;
+  const uint32_t in_last = (uint32_t)((nkv - 1) * a.hs * 2 + 16 * min(jj, nchunk - 1));   // last head's chunk
+  const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + uniform((int)(threadIdx.x / kWave));
   const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  // item = token * 2 nkv + kind * nkv + head, advanced by a fixed stride per
-  // iteration: (token, rem) are stepped, not divided, in the loop
-  const int per_tok = 2 * a.nkv;
-  const int64_t stride = n_waves * VPW;
-  const int64_t st_t = stride / per_tok;
-  const int st_r = (int)(stride - st_t * per_tok);
-  int64_t t;
-  int rem;
-  {
-    const int64_t item0 = wave_id * VPW + grp;
-    t = item0 / per_tok;
-    rem = (int)(item0 - t * per_tok);
-  }
 
-  for (int64_t base = wave_id * VPW; base < n_items; base += stride) {
-    if (base != wave_id * VPW) {
-      t += st_t;
-      rem += st_r;
-      if (rem >= per_tok) {
-        rem -= per_tok;
-        ++t;
+  for (int64_t t = wave_id; t < a.num_tokens; t += n_waves) {
+    const char* krow = reinterpret_cast<const char*>(a.key + t * a.key_stride);
+    const char* vrow = reinterpret_cast<const char*>(a.value + t * a.value_stride);
+    int64_t crow = 0, srow = 0;                // code row (bytes) and scale row (floats) of the slot
+    bool ok = false;
+    for (int u0 = 0; u0 < spt; u0 += U) {
+      // the input rows first: they do not depend on the slot
+      u32x4_t w[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int su = min(u0 + u, spt - 1);               // slice (wave-uniform)
+        const int kind = su >= spk ? 1 : 0;
+        const int h0 = (su - kind * spk) * VPW;            // its first head
+        const uint32_t off = min((uint32_t)(h0 * a.hs * 2) + in_off, in_last);
+        w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>((kind ? vrow : krow) + off));
       }
-    }
-    bool ok = t < a.num_tokens;
-    const int kind = rem >= a.nkv ? 1 : 0;
-    const int h = rem - kind * a.nkv;
-    int64_t slot = -1;
-    if (ok) {
-      slot = a.slot_mapping[t];
-      ok = slot >= 0 && slot < a.num_slots;
-    }
-    // load 8 bf16 (16 bytes)
-    uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (ok && lane_on) {
-      const uint16_t* src = kind ? (a.value + t * a.value_stride) : (a.key + t * a.key_stride);
-      w = *reinterpret_cast<const uint4*>(src + (int64_t)h * a.hs + 8 * jj);
-    }
-    const uint32_t wd[4] = {w.x ^ sx[0], w.y ^ sx[1], w.z ^ sx[2], w.w ^ sx[3]};
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[2 * k] = bf16_lo(wd[k]);
-      v[2 * k + 1] = bf16_hi(wd[k]);
-    }
-    // rotation (carried sign sg: the rotated values are sg * v) and one
-    // round-to-nearest-even to bf16 (v_cvt_pk_bf16_f32); rounding, absmax
-    // and the int4 rule are symmetric in the sign, so sg is applied to the
-    // codes only
-    float sg = 1.0f;
-    if constexpr (QM == 0) {
-      sg = fwht_b_lazy<LP>(v, a.b, jj);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t w2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[2 * k], v[2 * k + 1]},
-                                                                                  bf16x2_rt));
-        v[2 * k] = bf16_lo(w2);
-        v[2 * k + 1] = bf16_hi(w2);
+      if (u0 == 0) {                           // then the slot, while they are in flight
+        const int64_t slot = uniform64(a.slot_mapping[t]);
+        ok = slot >= 0 && slot < a.num_slots;
+        const int64_t pg = ok ? slot_page(a, slot) : 0;
+        const int64_t tk = ok ? slot - pg * a.bs : 0;
+        crow = pg * a.lay.blk + tk * a.lay.tok;
+        srow = pg * a.lay.sblk + tk * a.lay.stok;
       }
-    }
-    float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    amax = group_max(amax, LP);
-    if constexpr (QM == 0) {
-      const float scale = amax / 7.0f;
-      const bool fast = scale >= 0x1p-126f && scale <= 0x1p126f;
-      const uint32_t packed = scale > 0.0f ? int4_codes(v, scale, sg, fast) : 0u;
-      if (ok && lane_on) {
-        uint8_t* cache = kind ? a.value_cache : a.key_cache;
-        const int64_t pg = slot_page(a, slot), tk = slot - pg * a.bs;
-        *reinterpret_cast<uint32_t*>(cache + a.lay.code_off(pg, tk, h) + 4 * jj) = packed;
-        if (jj == 0) (kind ? a.v_scale : a.k_scale)[a.lay.scale_off(pg, tk, h)] = scale;
-      }
-    } else {
-      const float scale = amax / (QM == 1 ? 127.0f : 448.0f);
-      const bool fast = scale >= 0x1p-126f && scale <= 0x1p126f;
-      uint32_t lo = 0, hi = 0;
-      if (scale > 0.0f) {
-        if constexpr (QM == 1) {
-          float q[8];
-          rint_quotients<128>(v, scale, fast, q);
+      for (int u = 0; u < U; ++u) {
+        const int su = u0 + u;
+        const int kind = su >= spk ? 1 : 0;
+        const int h0 = (su - kind * spk) * VPW;
+        const int h = h0 + grp;
+        const bool on = su < spt && h < nkv && lane_on;
+        const bool st = ok && on;
+        const u32x4_t wz = on ? w[u] : u32x4_t{0u, 0u, 0u, 0u};
+        const uint32_t wd[4] = {wz.x ^ sx[0], wz.y ^ sx[1], wz.z ^ sx[2], wz.w ^ sx[3]};
+        float v[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lo |= int8_byte(q[e]) << (8 * e);
-            hi |= int8_byte(q[e + 4]) << (8 * e);
-          }
-        } else {
+        for (int k = 0; k < 4; ++k) {
+          v[2 * k] = bf16_lo(wd[k]);
+          v[2 * k + 1] = bf16_hi(wd[k]);
+        }
+        // rotation (carried sign sg: the rotated values are sg * v) and one
+        // round-to-nearest-even to bf16 (v_cvt_pk_bf16_f32); rounding, absmax
+        // and the int4 rule are symmetric in the sign, so sg is applied to the
+        // codes only
+        float sg = 1.0f;
+        if constexpr (QM == 0) {
+          sg = fwht_b_lazy<LP>(v, a.b, jj);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lo |= f32_to_e4m3(v[e] / scale) << (8 * e);
-            hi |= f32_to_e4m3(v[e + 4] / scale) << (8 * e);
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t w2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[2 * k], v[2 * k + 1]},
+                                                                                      bf16x2_rt));
+            v[2 * k] = bf16_lo(w2);
+            v[2 * k + 1] = bf16_hi(w2);
           }
         }
-      }
-      if (ok && lane_on) {
-        uint8_t* cache = kind ? a.value_cache : a.key_cache;
-        const int64_t pg = slot_page(a, slot), tk = slot - pg * a.bs;
-        *reinterpret_cast<uint2*>(cache + a.lay.code_off(pg, tk, h) + 8 * jj) = make_uint2(lo, hi);
-        if (jj == 0) (kind ? a.v_scale : a.k_scale)[a.lay.scale_off(pg, tk, h)] = scale;
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+        amax = group_max(amax, LP);
+        // the slice's first head in the cache row, uniform; the lane's head and chunk on top
+        uint8_t* cache = (kind ? a.value_cache : a.key_cache) + crow + (int64_t)h0 * a.lay.head;
+        float* scl = (kind ? a.v_scale : a.k_scale) + srow + (int64_t)h0 * a.lay.shead;
+        if constexpr (QM == 0) {
+          const float scale = div_by_qmax<7>(amax);
+          const bool fast = scale >= 0x1p-126f && scale <= 0x1p126f;
+          const uint32_t packed = scale > 0.0f ? int4_codes(v, scale, sg, fast) : 0u;
+          if (st) {
+            *reinterpret_cast<uint32_t*>(cache + c_off) = packed;
+            if (jj == 0) scl[grp * a.lay.shead] = scale;
+          }
+        } else {
+          const float scale = div_by_qmax<QM == 1 ? 127 : 448>(amax);
+          const bool fast = scale >= 0x1p-126f && scale <= 0x1p126f;
+          uint32_t lo = 0, hi = 0;
+          if (scale > 0.0f) {
+            if constexpr (QM == 1) {
+              float q[8];
+              rint_quotients<128>(v, scale, fast, q);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                lo |= int8_byte(q[e]) << (8 * e);
+                hi |= int8_byte(q[e + 4]) << (8 * e);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                lo |= f32_to_e4m3(v[e] / scale) << (8 * e);
+                hi |= f32_to_e4m3(v[e + 4] / scale) << (8 * e);
+              }
+            }
+          }
+          if (st) {
+            *reinterpret_cast<uint2*>(cache + c_off) = make_uint2(lo, hi);
+            if (jj == 0) scl[grp * a.lay.shead] = scale;
+          }
+        }
       }
     }
   }
@@ -361,23 +393,36 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 
 static int lanes_per_vector(int hs) { return host_next_pow2(hs / 8); }
 
-template <int QM>
-static void launch_write_qm(const WriteArgs& a, int LP, dim3 grid, dim3 block, hipStream_t stream) {
+template <int QM, int U>
+static void launch_write_qu(const WriteArgs& a, int LP, dim3 grid, dim3 block, hipStream_t stream) {
   switch (LP) {
-    case 1: hipLaunchKernelGGL((write_kernel<1, QM>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((write_kernel<2, QM>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((write_kernel<4, QM>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((write_kernel<8, QM>), grid, block, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((write_kernel<16, QM>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((write_kernel<32, QM>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((write_kernel<1, QM, U>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((write_kernel<2, QM, U>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((write_kernel<4, QM, U>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((write_kernel<8, QM, U>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((write_kernel<16, QM, U>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((write_kernel<32, QM, U>), grid, block, 0, stream, a); break;
   }
 }
 
-hipError_t launch_write(const WriteArgs& a, hipStream_t stream) {
-  const int LP = lanes_per_vector(a.hs);
-  const int64_t items = a.num_tokens * 2 * a.nkv;
-  const int64_t waves = (items + (kWave / LP) - 1) / (kWave / LP);
-  const int64_t blocks = std::min<int64_t>((waves + 3) / 4, 256 * 64);
+template <int QM>
+static void launch_write_qm(const WriteArgs& a, int LP, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (a.slices) {
+    case 1: launch_write_qu<QM, 1>(a, LP, grid, block, stream); break;
+    case 2: launch_write_qu<QM, 2>(a, LP, grid, block, stream); break;
+    case 8: launch_write_qu<QM, 8>(a, LP, grid, block, stream); break;
+    default: launch_write_qu<QM, 4>(a, LP, grid, block, stream); break;
+  }
+}
+
+hipError_t launch_write(const WriteArgs& a0, hipStream_t stream) {
+  const int LP = lanes_per_vector(a0.hs);
+  WriteArgs a = a0;
+  if (a.slices != 1 && a.slices != 2 && a.slices != 4 && a.slices != 8) a.slices = 4;
+  // U: slices in flight, at most the token's slices (one wave per token per iteration)
+  const int64_t spt = 2 * (((int64_t)a.nkv + (kWave / LP) - 1) / (kWave / LP));
+  while (a.slices > 1 && a.slices / 2 >= spt) a.slices /= 2;
+  const int64_t blocks = std::min<int64_t>((a.num_tokens + 3) / 4, 256 * 64);
   dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
   switch (a.qm) {
     case 0: launch_write_qm<0>(a, LP, grid, block, stream); break;
