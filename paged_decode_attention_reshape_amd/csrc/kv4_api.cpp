@@ -401,7 +401,6 @@ kv4_status write_impl(int qm, const char* what, const void* key, const void* val
   a.bs = block_size;
   a.bs_shift = bs_shift_of(block_size);
   a.lay = lay;
-  a.slices = (int)env_long("KV4_WRITE_SLICES", 4);
   return hip_status(kv4::launch_write(a, static_cast<hipStream_t>(stream)), what);
 }
 

@@ -62,7 +62,7 @@ struct WriteArgs {
   int bs;                // block size
   int bs_shift;          // log2(bs) if bs is a power of two, else -1
   CacheLayout lay;
-  int slices;            // head-vector slices a wave loads before computing any (1, 2, 4 or 8)
+  int slices;            // head-vector slices a wave loads before computing any (2 or 4; set by launch_write)
 };
 
 struct DequantArgs {

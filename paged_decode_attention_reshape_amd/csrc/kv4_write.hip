@@ -114,8 +114,10 @@ __device__ __forceinline__ void fwht8_xlane_lazy(float (&v)[8], float sgn) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = fmaf(p[e], sgn, v[e]);
 }
-template <int LPMAX>
-__device__ __forceinline__ float fwht_b_lazy(float (&v)[8], int b, int jj) {
+// XS cross-lane stages (b = 8 * 2^XS), in ascending stride order after the
+// in-lane ones; XS is fixed per kernel, so the stages carry no branch.
+template <int XS>
+__device__ __forceinline__ float fwht_b_lazy(float (&v)[8], int jj) {
   fwht8_inlane(v);
   float sg = 1.0f;
   auto stage = [&](auto dc) {
@@ -124,12 +126,25 @@ __device__ __forceinline__ float fwht_b_lazy(float (&v)[8], int b, int jj) {
     fwht8_xlane_lazy<D>(v, s);
     sg *= s;
   };
-  if constexpr (LPMAX > 1) { if (b > 8) stage(std::integral_constant<int, 1>()); }
-  if constexpr (LPMAX > 2) { if (b > 16) stage(std::integral_constant<int, 2>()); }
-  if constexpr (LPMAX > 4) { if (b > 32) stage(std::integral_constant<int, 4>()); }
-  if constexpr (LPMAX > 8) { if (b > 64) stage(std::integral_constant<int, 8>()); }
-  if constexpr (LPMAX > 16) { if (b > 128) stage(std::integral_constant<int, 16>()); }
+  if constexpr (XS > 0) stage(std::integral_constant<int, 1>());
+  if constexpr (XS > 1) stage(std::integral_constant<int, 2>());
+  if constexpr (XS > 2) stage(std::integral_constant<int, 4>());
+  if constexpr (XS > 3) stage(std::integral_constant<int, 8>());
+  if constexpr (XS > 4) stage(std::integral_constant<int, 16>());
   return sg;
+}
+
+// max over the LP lanes of an aligned lane group of non-negative finite
+// floats, compared as their bit patterns (same order; no NaN quieting)
+template <int LP>
+__device__ __forceinline__ float group_max_nonneg(float v) {
+  uint32_t u = __float_as_uint(v);
+  if constexpr (LP > 1) u = max(u, __float_as_uint(xor_lane<1>(__uint_as_float(u))));
+  if constexpr (LP > 2) u = max(u, __float_as_uint(xor_lane<2>(__uint_as_float(u))));
+  if constexpr (LP > 4) u = max(u, __float_as_uint(xor_lane<4>(__uint_as_float(u))));
+  if constexpr (LP > 8) u = max(u, __float_as_uint(xor_lane<8>(__uint_as_float(u))));
+  if constexpr (LP > 16) u = max(u, __float_as_uint(xor_lane<16>(__uint_as_float(u))));
+  return __uint_as_float(u);
 }
 
 // Per-token-head control modes (no rotation; the pages' int8_per_token_head
@@ -196,7 +211,7 @@ __device__ __forceinline__ float div_by_qmax(float amax) {
 // the slot; lanes past the heads or chunks read a clamped address of the same
 // row and drop the value, so the loads carry no branch and stay in flight
 // together.
-template <int LP, int QM, int U>
+template <int LP, int QM, int U, int XS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96))) void write_kernel(WriteArgs a) {
   constexpr int VPW = kWave / LP;                      // heads per slice
   constexpr int CB = QM == 0 ? 4 : 8;                  // code bytes per lane (8 elements)
@@ -250,9 +265,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96))) void writ
         const int kind = su >= spk ? 1 : 0;
         const int h0 = (su - kind * spk) * VPW;
         const int h = h0 + grp;
-        const bool on = su < spt && h < nkv && lane_on;
-        const bool st = ok && on;
-        const u32x4_t wz = on ? w[u] : u32x4_t{0u, 0u, 0u, 0u};
+        const bool st = ok && su < spt && h < nkv && lane_on;
+        // lanes past the head's chunks take part in the vector's absmax: zero
+        // them (other lanes' values stay inside their own vector and are not
+        // stored)
+        const u32x4_t wz = (nchunk == LP || lane_on) ? w[u] : u32x4_t{0u, 0u, 0u, 0u};
         const uint32_t wd[4] = {wz.x ^ sx[0], wz.y ^ sx[1], wz.z ^ sx[2], wz.w ^ sx[3]};
         float v[8];
 #pragma unroll
@@ -266,7 +283,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96))) void writ
         // codes only
         float sg = 1.0f;
         if constexpr (QM == 0) {
-          sg = fwht_b_lazy<LP>(v, a.b, jj);
+          sg = fwht_b_lazy<XS>(v, jj);
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const uint32_t w2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[2 * k], v[2 * k + 1]},
@@ -278,7 +295,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96))) void writ
         float amax = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
-        amax = group_max(amax, LP);
+        amax = group_max_nonneg<LP>(amax);
         // the slice's first head in the cache row, uniform; the lane's head and chunk on top
         uint8_t* cache = (kind ? a.value_cache : a.key_cache) + crow + (int64_t)h0 * a.lay.head;
         float* scl = (kind ? a.v_scale : a.k_scale) + srow + (int64_t)h0 * a.lay.shead;
@@ -393,35 +410,47 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 
 static int lanes_per_vector(int hs) { return host_next_pow2(hs / 8); }
 
+template <int QM, int LP, int U>
+static void launch_write_xs(const WriteArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  // cross-lane butterfly stages: log2(b / 8) for int4, none for int8 / fp8
+  int xs = 0;
+  if (QM == 0)
+    while ((8 << xs) < a.b) ++xs;
+  switch (xs) {
+    case 0: hipLaunchKernelGGL((write_kernel<LP, QM, U, 0>), grid, block, 0, stream, a); break;
+    case 1: if constexpr (QM == 0 && LP >= 2) hipLaunchKernelGGL((write_kernel<LP, QM, U, 1>), grid, block, 0, stream, a); break;
+    case 2: if constexpr (QM == 0 && LP >= 4) hipLaunchKernelGGL((write_kernel<LP, QM, U, 2>), grid, block, 0, stream, a); break;
+    case 3: if constexpr (QM == 0 && LP >= 8) hipLaunchKernelGGL((write_kernel<LP, QM, U, 3>), grid, block, 0, stream, a); break;
+    case 4: if constexpr (QM == 0 && LP >= 16) hipLaunchKernelGGL((write_kernel<LP, QM, U, 4>), grid, block, 0, stream, a); break;
+    default: if constexpr (QM == 0 && LP >= 32) hipLaunchKernelGGL((write_kernel<LP, QM, U, 5>), grid, block, 0, stream, a); break;
+  }
+}
+
 template <int QM, int U>
 static void launch_write_qu(const WriteArgs& a, int LP, dim3 grid, dim3 block, hipStream_t stream) {
   switch (LP) {
-    case 1: hipLaunchKernelGGL((write_kernel<1, QM, U>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((write_kernel<2, QM, U>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((write_kernel<4, QM, U>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((write_kernel<8, QM, U>), grid, block, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((write_kernel<16, QM, U>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((write_kernel<32, QM, U>), grid, block, 0, stream, a); break;
+    case 1: launch_write_xs<QM, 1, U>(a, grid, block, stream); break;
+    case 2: launch_write_xs<QM, 2, U>(a, grid, block, stream); break;
+    case 4: launch_write_xs<QM, 4, U>(a, grid, block, stream); break;
+    case 8: launch_write_xs<QM, 8, U>(a, grid, block, stream); break;
+    case 16: launch_write_xs<QM, 16, U>(a, grid, block, stream); break;
+    default: launch_write_xs<QM, 32, U>(a, grid, block, stream); break;
   }
 }
 
 template <int QM>
 static void launch_write_qm(const WriteArgs& a, int LP, dim3 grid, dim3 block, hipStream_t stream) {
-  switch (a.slices) {
-    case 1: launch_write_qu<QM, 1>(a, LP, grid, block, stream); break;
-    case 2: launch_write_qu<QM, 2>(a, LP, grid, block, stream); break;
-    case 8: launch_write_qu<QM, 8>(a, LP, grid, block, stream); break;
-    default: launch_write_qu<QM, 4>(a, LP, grid, block, stream); break;
-  }
+  if (a.slices == 2) launch_write_qu<QM, 2>(a, LP, grid, block, stream);
+  else launch_write_qu<QM, 4>(a, LP, grid, block, stream);
 }
 
 hipError_t launch_write(const WriteArgs& a0, hipStream_t stream) {
   const int LP = lanes_per_vector(a0.hs);
   WriteArgs a = a0;
-  if (a.slices != 1 && a.slices != 2 && a.slices != 4 && a.slices != 8) a.slices = 4;
-  // U: slices in flight, at most the token's slices (one wave per token per iteration)
+  // U: slices in flight, 4, or 2 where a token has only 2 (one slice of K
+  // heads, one of V heads)
   const int64_t spt = 2 * (((int64_t)a.nkv + (kWave / LP) - 1) / (kWave / LP));
-  while (a.slices > 1 && a.slices / 2 >= spt) a.slices /= 2;
+  a.slices = spt <= 2 ? 2 : 4;
   const int64_t blocks = std::min<int64_t>((a.num_tokens + 3) / 4, 256 * 64);
   dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
   switch (a.qm) {
