@@ -68,5 +68,42 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizers for the C ABI's validation and planner (kv4_api.cpp):
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (the
+# GPU code objects are built as usual), linked with the other objects of the
+# regular build. Loading it needs the clang ASan runtime preloaded.
+SAN_LIB = os.path.join(BUILD, "asan", "libkv4_asan.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime that matches hipcc (None if absent)."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_sanitized_library(verbose: bool = False) -> str:
+    """libkv4 with kv4_api.cpp built under ASan + UBSan (host code)."""
+    objs = [os.path.join(BUILD, os.path.splitext(f)[0] + ".o") for f in SOURCES]
+    if not all(os.path.exists(o) for o in objs):
+        build_library(verbose)
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    api_obj = os.path.join(os.path.dirname(SAN_LIB), "kv4_api.o")
+    cmd = [HIPCC, "-x", "hip", *COMMON, "-O1", "-g", *SAN_FLAGS, "-c", os.path.join(CSRC, "kv4_api.cpp"),
+           "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the sanitized kv4_api.cpp:\n{r.stdout}\n{r.stderr}")
+    others = [o for o in objs if not o.endswith("kv4_api.o")]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, "-shared-libasan", "-o", SAN_LIB,
+           api_obj, *others]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of the sanitized library failed:\n{r.stdout}\n{r.stderr}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))

@@ -233,3 +233,29 @@ def test_invalid_layouts_are_rejected_on_the_host():
                 (4096, 128, 64, 10, 5, -1)]:       # negative scale stride
         with pytest.raises(kv4.Kv4Error):
             ws(bad)
+
+
+def test_planner_sweep_workspace_sizes(L):
+    """The host planner and workspace layout over a grid of shapes (head
+    sizes, groups, query and sequence lengths, batch sizes, all three cache
+    modes, packed and inline layouts): every valid shape is planned without
+    an error (a single-split plan on the vector kernel needs no workspace at
+    all), a plan on the matrix cores needs some (the sequence prefix), and
+    no query tokens need none."""
+    import itertools
+    for hs, (nq, nkv), mql, msl, S, qm in itertools.product(
+            (8, 64, 96, 128, 192, 256), ((8, 8), (32, 8), (12, 2), (64, 1)), (1, 5, 600), (1, 100, 70000),
+            (1, 7, 1500), (0, 1, 2)):
+        Tq = S * mql
+        if qm == 0:
+            n = L.kv4_paged_attention_workspace_size(Tq, S, nq, nkv, hs, mql, msl)
+        else:
+            n = L.kv4_pth_attention_workspace_size(qm, Tq, S, nq, nkv, hs, mql, msl)
+        assert kv4.kv4_last_error() == "", (hs, nq, nkv, mql, msl, S, qm, kv4.kv4_last_error())
+        assert n % 256 == 0
+        if hs in (64, 96, 128, 192):           # matrix-core plans keep the sequence prefix there
+            assert n > 0, (hs, nq, nkv, mql, msl, S, qm)
+        lay, bb, vo, so = kv4.kv4_cache_layout_inline(qm, nkv, hs, 16)
+        L.kv4_attention_layout_workspace_size(qm, ctypes.byref(lay), Tq, S, nq, nkv, hs, mql, msl)
+        assert kv4.kv4_last_error() == ""
+        assert L.kv4_paged_attention_workspace_size(0, S, nq, nkv, hs, mql, msl) == 0
