@@ -26,72 +26,64 @@ namespace kv4 {
 typedef __bf16 bf16x2_rt __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// rint_half_even(fl(y / scale)) for the IEEE float32 quotient the write rule
-// uses, for all 8 values of a lane. The quotients are first taken as y * rcp
-// (rcp = v_rcp_f32(scale), within 1 ulp; with the product's rounding |t -
-// y/scale| < 2^-22 |t|, below 2^-19 for |t| < 8 and 2^-15 for |t| < 128) and
-// the lane redoes all 8 with the correctly rounded division only if one t lies
-// within `tie` of a half-integer -- the only place where the two can round to
-// different integers (t - rint(t) is exact). `fast` is false for scales
-// outside the normal range.
-template <int QMAX>
-__device__ __forceinline__ void rint_quotients(const float (&y)[8], float scale, bool fast, float (&q)[8]) {
-  constexpr float tie = QMAX <= 8 ? 0.5f - 0x1p-16f : 0.5f - 0x1p-12f;
-  bool redo = !fast;
-  if (fast) {
-    const float rcp = __builtin_amdgcn_rcpf(scale);
+// The IEEE float32 quotient fl(y / scale) that the quantizers round, without a
+// division per element: with r = fl(1 / scale) (one correctly rounded
+// division per vector), q0 = fl(y r), e = y - q0 scale in one fma, and q =
+// fl(q0 + e r) in another (Markstein's correction). For scale in [2^-100,
+// 2^100] and every pair (amax, y) the write path can meet -- amax and y bf16
+// values with |y| <= amax, scale = fl(amax / qmax) -- the codes taken from q
+// equal those taken from the IEEE quotient: checked exhaustively on the host
+// for qmax 7 (rint), 127 (rint) and 448 (e4m3fn, the sign taken from y), where
+// the quotient differs only for subnormal y, whose codes are 0 either way.
+// Scales outside that range take the quotient from the division itself.
+constexpr float kMarksteinLo = 0x1p-100f, kMarksteinHi = 0x1p100f;
+
+__device__ __forceinline__ float quotient(float y, float scale, float r) {
+  const float q0 = y * r;
+  const float e = fmaf(-q0, scale, y);
+  return fmaf(e, r, q0);
+}
+
+// rint_half_even(fl(y / scale)) for all 8 values of a lane (int8 rule).
+__device__ __forceinline__ void rint_quotients(const float (&y)[8], float scale, float (&q)[8]) {
+  if (scale >= kMarksteinLo && scale <= kMarksteinHi) {
+    const float r = 1.0f / scale;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = y[e] * rcp;
-      q[e] = __builtin_rintf(t);
-      redo |= fabsf(t - q[e]) >= tie;
-    }
-  }
-  if (redo) {
+    for (int e = 0; e < 8; ++e) q[e] = __builtin_rintf(quotient(y[e], scale, r));
+  } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = __builtin_rintf(y[e] / scale);
   }
 }
 
 // Packed int4 codes (element e in bits 4e..4e+3) of the quotients sg * v[e] /
-// scale, scale > 0, sg = +1 or -1 (rint is odd, so the sign goes on the
-// quotient). Fast path (normal scales): t = v * (sg * rcp(scale)); the sum t +
-// 1.5 * 2^23 is 1.5 * 2^23 + rint_half_even(t) exactly (|t| < 2^22, unit
-// spacing there), so for |t| <= 8 the low nibble of its bit pattern is the
-// two's-complement code. A normal scale keeps |t| <= 7 up to rounding, so the
-// clamp to [-8, 7] cannot act there. As in rint_quotients, a lane with a t
-// within 2^-16 of a half-integer redoes its 8 codes with the correctly rounded
-// division, clamped (a subnormal scale can give |y / scale| > 7.5).
-__device__ __forceinline__ uint32_t int4_codes(const float (&v)[8], float scale, float sg, bool fast) {
+// scale, scale > 0, sg = +1 or -1 (the quotient of sg * v is sg times that of
+// v exactly: every step rounds symmetrically). The sum q + 1.5 * 2^23 is
+// 1.5 * 2^23 + rint_half_even(q) exactly (|q| < 2^22, unit spacing there), so
+// for |q| <= 8 the low nibble of its bit pattern is the two's-complement code;
+// |q| <= 7 up to rounding for scale = fl(amax / 7), so the clamp to [-8, 7]
+// cannot act. Scales outside the Markstein range (subnormal ones can give
+// |y / scale| > 7.5) take the division and the clamp.
+__device__ __forceinline__ uint32_t int4_codes(const float (&v)[8], float scale, float sg) {
   constexpr float kRound = 12582912.0f;   // 1.5 * 2^23
-  constexpr float tie = 0.5f - 0x1p-16f;
-  uint32_t packed = 0;
-  bool redo = !fast;
-  if (fast) {
-    const float r = __builtin_amdgcn_rcpf(scale) * sg;
+  if (scale >= kMarksteinLo && scale <= kMarksteinHi) {
+    const float r = 1.0f / scale;
     uint32_t u[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = v[e] * r;
-      const float f = t + kRound;
-      redo |= fabsf(t - (f - kRound)) >= tie;
-      u[e] = __float_as_uint(f);
-    }
+    for (int e = 0; e < 8; ++e) u[e] = __float_as_uint(fmaf(quotient(v[e], scale, r), sg, kRound));
     // byte 0 of the even elements' patterns into one word and of the odd
     // ones into another (v_perm_b32: selector 0-3 picks a byte of the second
     // operand, 4-7 of the first, 12 a zero byte), then each byte's low
     // nibble from the even word and high nibble from the odd one
     const uint32_t ev = __builtin_amdgcn_perm(u[2], u[0], 0x0C0C0400u) | __builtin_amdgcn_perm(u[6], u[4], 0x04000C0Cu);
     const uint32_t od = __builtin_amdgcn_perm(u[3], u[1], 0x0C0C0400u) | __builtin_amdgcn_perm(u[7], u[5], 0x04000C0Cu);
-    packed = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+    return (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
   }
-  if (redo) {
-    packed = 0;
+  uint32_t packed = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float q = fminf(fmaxf(__builtin_rintf(v[e] / scale) * sg, -8.0f), 7.0f);
-      packed |= ((uint32_t)(int)q & 0xFu) << (4 * e);
-    }
+  for (int e = 0; e < 8; ++e) {
+    const float q = fminf(fmaxf(__builtin_rintf(v[e] / scale) * sg, -8.0f), 7.0f);
+    packed |= ((uint32_t)(int)q & 0xFu) << (4 * e);
   }
   return packed;
 }
@@ -301,30 +293,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96))) void writ
         float* scl = (kind ? a.v_scale : a.k_scale) + srow + (int64_t)h0 * a.lay.shead;
         if constexpr (QM == 0) {
           const float scale = div_by_qmax<7>(amax);
-          const bool fast = scale >= 0x1p-126f && scale <= 0x1p126f;
-          const uint32_t packed = scale > 0.0f ? int4_codes(v, scale, sg, fast) : 0u;
+          const uint32_t packed = scale > 0.0f ? int4_codes(v, scale, sg) : 0u;
           if (st) {
             *reinterpret_cast<uint32_t*>(cache + c_off) = packed;
             if (jj == 0) scl[grp * a.lay.shead] = scale;
           }
         } else {
           const float scale = div_by_qmax<QM == 1 ? 127 : 448>(amax);
-          const bool fast = scale >= 0x1p-126f && scale <= 0x1p126f;
           uint32_t lo = 0, hi = 0;
           if (scale > 0.0f) {
             if constexpr (QM == 1) {
               float q[8];
-              rint_quotients<128>(v, scale, fast, q);
+              rint_quotients(v, scale, q);
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 lo |= int8_byte(q[e]) << (8 * e);
                 hi |= int8_byte(q[e + 4]) << (8 * e);
               }
             } else {
+              // the quotient of |v| with v's sign bit: -0 keeps its sign
+              float q[8];
+              if (scale >= kMarksteinLo && scale <= kMarksteinHi) {
+                const float r = 1.0f / scale;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                  q[e] = __uint_as_float(__float_as_uint(quotient(fabsf(v[e]), scale, r)) |
+                                         (__float_as_uint(v[e]) & 0x80000000u));
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) q[e] = v[e] / scale;
+              }
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                lo |= f32_to_e4m3(v[e] / scale) << (8 * e);
-                hi |= f32_to_e4m3(v[e + 4] / scale) << (8 * e);
+                lo |= f32_to_e4m3(q[e]) << (8 * e);
+                hi |= f32_to_e4m3(q[e + 4]) << (8 * e);
               }
             }
           }
