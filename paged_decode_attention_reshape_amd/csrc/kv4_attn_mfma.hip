@@ -39,6 +39,7 @@
 //   * k_scale / v_scale of the 32 tokens are loaded once per step (one lane
 //     per token) and redistributed through a 256-byte LDS slot per head.
 // Pages are looked up once per 16-token half tile (block_size % 16 == 0).
+#include <cstdio>
 #include <cstdlib>
 #include <mutex>
 #include <unordered_map>
@@ -1381,14 +1382,19 @@ static DevAttrs device_attrs() {
 // Sequences whose prefix the attention kernel computes itself (in LDS) when
 // that costs it no occupancy; longer batches run the plan kernel first.
 constexpr int kFusedPlanMaxSeqs = 1024;
-constexpr size_t kFusedPlanLds = (kFusedPlanMaxSeqs + 1 + 16) * sizeof(int32_t);
+// LDS of the fused prefix for num_seqs sequences (the prefix, its total and
+// one partial sum per wave), in 1 KB steps: small batches reserve little
+// LDS and keep the kernel's occupancy.
+inline size_t fused_plan_lds(int num_seqs) {
+  return ((size_t)(num_seqs + 1 + 16) * sizeof(int32_t) + 1023) / 1024 * 1024;
+}
 
 // Whether the plan LDS leaves the kernel's resident workgroups per CU as
 // they are, counting LDS in 1 KB units: the occupancy query counts bytes,
 // and a kernel whose workgroups fill the CU to within a few hundred bytes
 // (head size 192, int8 / fp8: three of 50.4 KB) was measured to lose a
 // workgroup per CU with the plan LDS although the query said otherwise.
-static bool plan_lds_fits(const void* kernel, int resident, const DevAttrs& da) {
+static bool plan_lds_fits(const void* kernel, int resident, size_t plan_lds, const DevAttrs& da) {
   // static LDS of each kernel, looked up once (the same code object on every device)
   static std::mutex mu;
   static std::unordered_map<const void*, size_t> static_lds;
@@ -1403,18 +1409,19 @@ static bool plan_lds_fits(const void* kernel, int resident, const DevAttrs& da) 
     }
     lds = it->second;
   }
-  const size_t per_wg = (lds + kFusedPlanLds + 1023) / 1024 * 1024;
+  const size_t per_wg = (lds + plan_lds + 1023) / 1024 * 1024;
   const int per_cu = resident / (da.cus > 0 ? da.cus : 1);
   return (size_t)per_cu * per_wg <= (size_t)da.lds_per_cu;
 }
 
 // Workgroups of the kernel the GPU holds at once (fused: with the plan LDS).
-// (per device: the occupancy query is answered for the current device)
+// (per device: the occupancy query is answered for the current device), with
+// plan_lds bytes of dynamic LDS (the fused prefix; 0 without it)
 template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB = 1, bool NT = false>
-static int resident_blocks(bool fused, const DevAttrs& da) {
+static int resident_blocks(size_t plan_lds, const DevAttrs& da) {
   static std::mutex mu;
-  static std::unordered_map<int, int> per_cu;      // key: 2 * device + fused
-  const int key = 2 * da.dev + (fused ? 1 : 0);
+  static std::unordered_map<int64_t, int> per_cu;      // key: device, LDS
+  const int64_t key = (int64_t)da.dev * (1 << 20) + (int64_t)plan_lds;
   {
     std::lock_guard<std::mutex> lock(mu);
     auto it = per_cu.find(key);
@@ -1423,7 +1430,7 @@ static int resident_blocks(bool fused, const DevAttrs& da) {
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb,
                                                    reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH, WIN, NRB, NT>),
-                                                   64 * mfma_wpb<HS, HPW, QM>(), fused ? kFusedPlanLds : 0) != hipSuccess ||
+                                                   64 * mfma_wpb<HS, HPW, QM>(), plan_lds) != hipSuccess ||
       nb < 1)
     nb = 1;
   std::lock_guard<std::mutex> lock(mu);
@@ -1437,12 +1444,26 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
   if (QM != 0 && (a.plan.hpw != 1 || a.plan.wpb != mfma_wpb<HS, 1, QM>())) return hipErrorInvalidValue;
   // resident(fused, device) -> workgroups the GPU holds at once
   const DevAttrs da = device_attrs();
+  const size_t plan_lds = fused_plan_lds(a.num_seqs);
   auto go = [&](auto kernel, int wpb, auto resident_of) {
-    const int plain = resident_of(false, da);
-    a.plan.fused_plan = (a.num_seqs <= kFusedPlanMaxSeqs && resident_of(true, da) == plain &&
-                         plan_lds_fits(reinterpret_cast<const void*>(kernel), plain, da)) ? 1 : 0;
+    const int plain = resident_of((size_t)0, da);
+    // the workgroups the launch wants at once: stream-K at most its cap; the
+    // prefix is built in-kernel where its LDS leaves room for that many
+    const int want = a.plan.sk ? std::min(plain, a.plan.sk_pcap) : plain;
+    const int with_plan = resident_of(plan_lds, da);
+    a.plan.fused_plan = (a.num_seqs <= kFusedPlanMaxSeqs && with_plan >= want &&
+                         plan_lds_fits(reinterpret_cast<const void*>(kernel), want, plan_lds, da)) ? 1 : 0;
     if (const char* f = std::getenv("KV4_FUSED_PLAN")) a.plan.fused_plan = a.plan.fused_plan && std::atoi(f) != 0;
-    const int resident = plain;
+    if (std::getenv("KV4_DEBUG_PLAN")) {
+      hipFuncAttributes fa{};
+      (void)hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kernel));
+      std::fprintf(stderr,
+                   "[kv4] hs %d hpw %d qm %d rb %d sk %d: resident %d (with %zu B prefix LDS: %d), static LDS %zu, "
+                   "LDS/CU %d, CUs %d, fused prefix %d\n",
+                   HS, a.plan.hpw, QM, a.plan.rb, a.plan.sk, plain, plan_lds, with_plan,
+                   (size_t)fa.sharedSizeBytes, da.lds_per_cu, da.cus, a.plan.fused_plan);
+    }
+    const int resident = a.plan.fused_plan ? std::min(plain, with_plan) : plain;
     if (!a.plan.fused_plan)
       hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a, const_cast<int32_t*>(prefix));
     int64_t wgs;
@@ -1458,26 +1479,26 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
       if (wgs > cap) wgs = cap;
       if (wgs < 1) wgs = 1;
     }
-    hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(64 * wpb), a.plan.fused_plan ? kFusedPlanLds : 0, stream, a,
+    hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(64 * wpb), a.plan.fused_plan ? plan_lds : 0, stream, a,
                        prefix);
   };
   if constexpr (QM != 0) {
     if constexpr (HS == 128) {
       if (a.code_nt) {
         go(attn_mfma_kernel<HS, 1, QM, false, WIN, 1, true>, mfma_wpb<HS, 1, QM>(),
-           [](bool f, const DevAttrs& d) { return resident_blocks<HS, 1, QM, false, WIN, 1, true>(f, d); });
+           [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 1, QM, false, WIN, 1, true>(l, d); });
         return hipSuccess;
       }
     }
-    go(attn_mfma_kernel<HS, 1, QM, false, WIN, 1>, mfma_wpb<HS, 1, QM>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 1, QM, false, WIN>(f, d); });
+    go(attn_mfma_kernel<HS, 1, QM, false, WIN, 1>, mfma_wpb<HS, 1, QM>(), [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 1, QM, false, WIN>(l, d); });
     return hipSuccess;
   }
   if (a.plan.vjh) {
     if constexpr (HS == 128) {
       if (a.plan.hpw == 2) {
-        go(attn_mfma_kernel<HS, 2, 0, true, WIN, 1>, mfma_wpb<HS, 2, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 2, 0, true, WIN>(f, d); });
+        go(attn_mfma_kernel<HS, 2, 0, true, WIN, 1>, mfma_wpb<HS, 2, 0>(), [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 2, 0, true, WIN>(l, d); });
       } else if (a.plan.hpw == 4) {
-        go(attn_mfma_kernel<HS, 4, 0, true, WIN, 1>, mfma_wpb<HS, 4, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 4, 0, true, WIN>(f, d); });
+        go(attn_mfma_kernel<HS, 4, 0, true, WIN, 1>, mfma_wpb<HS, 4, 0>(), [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 4, 0, true, WIN>(l, d); });
       } else {
         return hipErrorInvalidValue;
       }
@@ -1487,7 +1508,7 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
   }
   if (a.plan.rb == 2) {
     if constexpr (HS <= 128) {
-      go(attn_mfma_kernel<HS, 1, 0, false, WIN, 2>, mfma_wpb<HS, 1, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 1, 0, false, WIN, 2>(f, d); });
+      go(attn_mfma_kernel<HS, 1, 0, false, WIN, 2>, mfma_wpb<HS, 1, 0>(), [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 1, 0, false, WIN, 2>(l, d); });
       return hipSuccess;
     }
     return hipErrorInvalidValue;
@@ -1495,23 +1516,23 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
   if constexpr (HS == 128) {
     if (a.code_nt && a.plan.hpw == 2) {
       go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1, true>, mfma_wpb<HS, 2, 0>(),
-         [](bool f, const DevAttrs& d) { return resident_blocks<HS, 2, 0, false, WIN, 1, true>(f, d); });
+         [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 2, 0, false, WIN, 1, true>(l, d); });
       return hipSuccess;
     }
     if (a.code_nt && a.plan.hpw == 4) {
       go(attn_mfma_kernel<HS, 4, 0, false, WIN, 1, true>, mfma_wpb<HS, 4, 0>(),
-         [](bool f, const DevAttrs& d) { return resident_blocks<HS, 4, 0, false, WIN, 1, true>(f, d); });
+         [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 4, 0, false, WIN, 1, true>(l, d); });
       return hipSuccess;
     }
   }
   switch (a.plan.hpw) {
-    case 2: go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1>, mfma_wpb<HS, 2, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 2, 0, false, WIN>(f, d); }); break;
+    case 2: go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1>, mfma_wpb<HS, 2, 0>(), [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 2, 0, false, WIN>(l, d); }); break;
     case 4:
       // four heads' V loads of a step must fit the 6-bit load counter
       if constexpr (Geo<HS>::NVR == 1)
-        go(attn_mfma_kernel<HS, 4, 0, false, WIN, 1>, mfma_wpb<HS, 4, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 4, 0, false, WIN>(f, d); });
+        go(attn_mfma_kernel<HS, 4, 0, false, WIN, 1>, mfma_wpb<HS, 4, 0>(), [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 4, 0, false, WIN>(l, d); });
       break;
-    default: go(attn_mfma_kernel<HS, 1, 0, false, WIN, 1>, mfma_wpb<HS, 1, 0>(), [](bool f, const DevAttrs& d) { return resident_blocks<HS, 1, 0, false, WIN>(f, d); }); break;
+    default: go(attn_mfma_kernel<HS, 1, 0, false, WIN, 1>, mfma_wpb<HS, 1, 0>(), [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 1, 0, false, WIN>(l, d); }); break;
   }
   return hipSuccess;
 }
