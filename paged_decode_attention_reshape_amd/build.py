@@ -35,6 +35,7 @@ SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 # the epilogue touch them with VALU ops; AGPR copies would cost both).
 PER_FILE = {
     "kv4_attn_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "kv4_attn_prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "kv4_attn_valu.hip": ["-fno-honor-nans"],
 }
 

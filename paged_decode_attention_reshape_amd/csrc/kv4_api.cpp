@@ -120,6 +120,31 @@ kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq,
     if (!std::strcmp(f, "mfma")) mfma = mfma_ok;
   }
   p.path = mfma ? 1 : 0;
+  // Chunked prefill (int4, head size 128, GQA group <= 32): sequences with
+  // more queries than one 32-row tile holds go to the prefill kernel, whose
+  // workgroups share each staged K/V step among four tiles and walk every
+  // tile's whole key range; the rest of the plan covers the other sequences
+  // (at most pf_tq queries each, so one tile per sequence).
+  //
+  // KV4_PREFILL: 0 off, 1 on wherever the shape allows, otherwise (default)
+  // on where long chunks carry the batch: at least 8 x pf_tq query tokens
+  // per sequence on average. Measured (Qwen2.5-1.5B shape, hs 128, group
+  // 6): 4 chunks of 512 alone take 117 us with the prefill kernel against
+  // 192 us on the single-kernel plan; the same chunks with 60 decode
+  // sequences take 168 us against 160 us, because the decode rows, which
+  // the single kernel runs in the gaps of its prefill tiles, then cost a
+  // launch of their own.
+  p.pf_qlen = 0;
+  const long pf_mode = env_long("KV4_PREFILL", 2);
+  if (mfma && qm == 0 && hs == 128 && G <= 32 && num_seqs <= kv4::kPfMaxSeqs && pf_mode != 0) {
+    const int pf_tq = 32 / G;
+    const bool dominated = num_q_tokens >= 8LL * pf_tq * num_seqs;
+    if (max_query_len > pf_tq && (pf_mode == 1 || dominated) && (int64_t)num_seqs * pf_tq * nq < INT32_MAX) {
+      p.pf_qlen = pf_tq + 1;
+      p.pf_tq = pf_tq;
+      max_query_len = pf_tq;
+    }
+  }
   // Two 16-row MFMA blocks per wave (int4, one kv head per wave) where a
   // sequence has more than 16 dense rows (query_len x group) to fill: the K
   // and V codes of a step become operands once for 32 rows. Where 16 rows
@@ -237,9 +262,12 @@ WsLayout ws_layout(const kv4::AttnPlan& p, int64_t num_q_tokens, int32_t num_seq
     // split-KV: one row per (split, query token, q head); stream-K: one per
     // (range piece, query token of the tile, q head), at most workgroups +
     // quads * sequences pieces
+    // (beside the prefill kernel: one per (split, sequence, query of the
+    // sequence), at most pf_tq queries per sequence)
+    const size_t qrows = p.pf_qlen > 0 ? (size_t)num_seqs * (size_t)p.pf_tq : (size_t)num_q_tokens;
     const size_t rows = p.sk ? ((size_t)p.sk_pcap + (size_t)p.sk_quads * (size_t)num_seqs) * (size_t)p.tq *
                                    (size_t)nq
-                             : (size_t)p.num_splits * (size_t)num_q_tokens * (size_t)nq;
+                             : (size_t)p.num_splits * qrows * (size_t)nq;
     w.o_off = off;
     w.ml_off = align_up(off + rows * (size_t)hs * sizeof(float), 256);
     off = align_up(w.ml_off + rows * 2 * sizeof(float), 256);
@@ -462,6 +490,37 @@ size_t workspace_impl(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nu
   return need;
 }
 
+// A side stream of the current device (default priority, non-blocking) and
+// the two events of a fork / join, created once per device and kept for the
+// life of the process; mu serializes the fork-launch-join sequences of
+// concurrent calls (an event must not be re-recorded between its record and
+// the wait on it). nullptr if they cannot be created: the call then runs on
+// the caller's stream alone.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+SideStream* side_stream_on_current_device() {
+  static std::mutex mu;
+  static std::unordered_map<int, SideStream*> by_dev;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = by_dev.find(dev);
+  if (it != by_dev.end()) return it->second;
+  SideStream* s = new SideStream();
+  if (hipStreamCreateWithFlags(&s->stream, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&s->fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&s->join, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();   // clear the sticky error: the call goes on without the side stream
+    delete s;                  // (handles created before the failure are left to the process exit)
+    s = nullptr;
+  }
+  by_dev[dev] = s;
+  return s;
+}
+
 kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride, const void* key_cache,
                    const void* value_cache, const float* k_scale_cache, const float* v_scale_cache,
                    int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
@@ -469,7 +528,7 @@ kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride,
                    int64_t num_q_tokens, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size, uint64_t sign_seed,
                    float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                   const kv4::CacheLayout* layout = nullptr, int32_t window = 0) {
+                   const kv4::CacheLayout* layout = nullptr, int32_t window = 0, bool allow_fork = true) {
   if (kv4_status e = check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
                                max_seq_len))
     return e;
@@ -545,15 +604,33 @@ kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride,
   if (const long f = env_long("KV4_NT", -1); f == 0 || f == 1)
     a.code_nt = (f == 1 && nt_kernel_built(qm, head_size, a.plan)) ? 1 : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // With a prefill kernel, the other sequences' kernels (decode kernel and
+  // merge) run on the device's side stream, forked from and joined back into
+  // the caller's stream with events, so they fill the CUs the prefill
+  // workgroups leave free instead of queueing behind them. The caller sees
+  // one stream-ordered call either way.
+  SideStream* side = nullptr;
+  std::unique_lock<std::mutex> fork_lock;
+  hipStream_t dst = st;
+  if (a.plan.pf_qlen > 0 && allow_fork && env_long("KV4_FORK", 1) != 0) {
+    side = side_stream_on_current_device();
+    if (side) {
+      fork_lock = std::unique_lock<std::mutex>(side->mu);
+      if (hipEventRecord(side->fork, st) == hipSuccess && hipStreamWaitEvent(side->stream, side->fork, 0) == hipSuccess)
+        dst = side->stream;
+      else
+        side = nullptr;
+    }
+  }
+  kv4_status rc = KV4_OK;
   if (a.plan.path == 1) {
     const int64_t max_units =
         a.plan.n_qtiles * a.plan.n_head_tiles * (num_kv_heads / a.plan.hpw) * a.plan.num_splits;
-    if (kv4_status e = hip_status(kv4::launch_attn_mfma(a, prefix, max_units, st), "kv4_paged_attention launch"))
-      return e;
+    rc = hip_status(kv4::launch_attn_mfma(a, prefix, max_units, dst), "kv4_paged_attention launch");
   } else {
-    if (kv4_status e = hip_status(kv4::launch_attn_valu(a, st), "kv4_paged_attention launch")) return e;
+    rc = hip_status(kv4::launch_attn_valu(a, dst), "kv4_paged_attention launch");
   }
-  if (a.plan.sk || a.plan.num_splits > 1) {
+  if (rc == KV4_OK && (a.plan.sk || a.plan.num_splits > 1)) {
     // Many rows: one row per lane group (a quarter of the waves at head size
     // 128, each folding its row's partials four loads at a time). Few rows:
     // one row per wave, whose lane groups split the partials, so that more
@@ -562,9 +639,22 @@ kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride,
     const int64_t ng = 64 / kv4::host_next_pow2(head_size / 8);
     a.reduce_rows = (num_q_tokens * num_q_heads / ng >= kReduceRowsMinWaves) ? 1 : 0;
     if (const long f = env_long("KV4_REDUCE_ROWS", -1); f == 0 || f == 1) a.reduce_rows = (int)f;
-    return hip_status(kv4::launch_attn_reduce(a, st), "kv4_paged_attention merge launch");
+    rc = hip_status(kv4::launch_attn_reduce(a, dst), "kv4_paged_attention merge launch");
   }
-  return ok();
+  // The prefill kernel is enqueued after the decode kernel: the short,
+  // memory-bound decode workgroups then spread over every CU first, and each
+  // CU takes its prefill workgroup (which fills its register file) as its
+  // decode work drains, instead of the decode kernel squeezing onto the few
+  // CUs the prefill workgroups leave.
+  if (rc == KV4_OK && a.plan.pf_qlen > 0)
+    rc = hip_status(kv4::launch_attn_prefill(a, st), "kv4_paged_attention prefill launch");
+  if (side) {
+    // join: the caller's stream waits for the side stream's work (also after
+    // a failed launch, so nothing of this call is left unordered)
+    if (hipEventRecord(side->join, side->stream) != hipSuccess || hipStreamWaitEvent(st, side->join, 0) != hipSuccess)
+      if (rc == KV4_OK) rc = fail(KV4_EHIP, "kv4_paged_attention: joining the side stream failed");
+  }
+  return rc == KV4_OK ? ok() : rc;
 }
 
 // The device address of `scratch` on the current device, looked up once per
@@ -613,7 +703,8 @@ kv4_status kv4_paged_attention_noalloc(const void* query, int64_t query_token_st
       attention_impl(0, query, query_token_stride, key_cache, value_cache, k_scale_cache, v_scale_cache,
                      num_blocks, block_table, max_blocks_per_seq, seq_lens, query_start_loc, num_seqs, num_q_tokens,
                      max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_size, b, block_size, sign_seed,
-                     softmax_scale, out, ws, (size_t)KV4_NOALLOC_SCRATCH_BYTES, stream);
+                     softmax_scale, out, ws, (size_t)KV4_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0,
+                     /*allow_fork=*/false);
   if (st == KV4_EWORKSPACE) {
     const std::string why = g_last_error;
     return fail(KV4_EWORKSPACE,

@@ -369,6 +369,59 @@ __device__ __forceinline__ RowSeq row_sequence(const AttnArgs& a, int64_t qtok) 
   return q;
 }
 
+// RowSeq of a known sequence s (the compact row order below).
+__device__ __forceinline__ RowSeq row_sequence_at(const AttnArgs& a, int s) {
+  RowSeq q;
+  q.s = s;
+  q.qb = a.qsl[s];
+  q.qe = a.qsl[s + 1];
+  q.L = a.seq_lens[s];
+  q.pf0 = q.pf1 = q.pftot = 0;
+  if (a.plan.sk) {
+    q.pf0 = a.prefix[s];
+    q.pf1 = a.prefix[s + 1];
+    q.pftot = a.prefix[a.num_seqs];
+  }
+  const int64_t cap = (int64_t)a.max_blocks * a.bs;
+  q.L = q.L < 0 ? 0 : (q.L > cap ? cap : q.L);
+  return q;
+}
+
+// The merge's rows. With a prefill kernel alongside, only the other
+// sequences (at most pf_tq queries each) have partials: their rows are
+// enumerated as (sequence, query of the sequence < pf_tq, head), so no row
+// has to search for its sequence and the prefill rows are never visited;
+// otherwise rows are (query token, head). vrow -> (RowSeq, query token,
+// head); false where the row has nothing to merge here.
+__device__ __forceinline__ int64_t merge_rows(const AttnArgs& a) {
+  return a.plan.pf_qlen > 0 ? (int64_t)a.num_seqs * a.plan.pf_tq * a.nq : a.num_q_tokens * a.nq;
+}
+__device__ __forceinline__ bool prefill_row(const AttnArgs& a, const RowSeq& q, int64_t qtok);
+__device__ __forceinline__ bool merge_row(const AttnArgs& a, int64_t vrow, RowSeq& q, int64_t& qtok, int& h) {
+  if (a.plan.pf_qlen > 0) {
+    const int64_t sq = (uint32_t)vrow / (uint32_t)a.nq;   // rows number fewer than 2^31 (checked on the host)
+    h = (int)(vrow - sq * a.nq);
+    const int s = (int)(sq / a.plan.pf_tq), i = (int)(sq - (int64_t)s * a.plan.pf_tq);
+    q = row_sequence_at(a, s);
+    qtok = q.qb + i;
+    return q.qb >= 0 && qtok < q.qe && qtok < a.num_q_tokens && !prefill_row(a, q, qtok);
+  }
+  qtok = (uint32_t)vrow / (uint32_t)a.nq;
+  h = (int)(vrow - qtok * a.nq);
+  q = row_sequence(a, qtok);
+  return !prefill_row(a, q, qtok);
+}
+
+// Whether query token qtok belongs to a sequence of the prefill kernel (the
+// same clamped test the planner kernels apply).
+__device__ __forceinline__ bool prefill_row(const AttnArgs& a, const RowSeq& q, int64_t qtok) {
+  if (a.plan.pf_qlen <= 0 || qtok < q.qb || qtok >= q.qe) return false;
+  int64_t qb = q.qb, qe = q.qe;
+  qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
+  qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
+  return prefill_seq(a, qb, qe);
+}
+
 // The partials of output row `row` (query token qtok, query head h): nsp of
 // them, partial k at workspace row k * pstride + pbase.
 __device__ __forceinline__ void row_pieces(const AttnArgs& a, const RowSeq& q, int64_t qtok, int h, int64_t row,
@@ -376,6 +429,12 @@ __device__ __forceinline__ void row_pieces(const AttnArgs& a, const RowSeq& q, i
   nsp = 0;
   pbase = row;
   pstride = a.num_q_tokens * a.nq;
+  if (a.plan.pf_qlen > 0 && !a.plan.sk) {
+    // compact split rows (split, sequence, query of the sequence) of the
+    // sequences left to the matrix-core kernel beside the prefill kernel
+    pstride = (int64_t)a.num_seqs * a.plan.pf_tq * a.nq;
+    pbase = ((int64_t)q.s * a.plan.pf_tq + (qtok - q.qb)) * a.nq + h;
+  }
   if (a.plan.sk) {
     // stream-K: the workgroups whose step ranges cover this row's
     // (quad, sequence) steps [xs, xe) each left one piece, numbered
@@ -436,18 +495,20 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   const int jj = lane & (LP - 1);
   const int grp = lane / LP;
   const bool lane_on = jj < (hs >> 3);
-  const int64_t n_rows = a.num_q_tokens * a.nq;
+  const int64_t n_rows = merge_rows(a);
   const uint32_t sbits = (a.qm == 0 && lane_on) ? sign_bits8(a.seed, jj) : 0u;
   const float inv_b = 1.0f / (float)a.b;
   const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  for (int64_t row = wave0; row < n_rows; row += n_waves) {
-    // rows number fewer than 2^31 (checked on the host): 32-bit division
-    const int64_t qtok = (uint32_t)row / (uint32_t)a.nq;
-    const RowSeq q = row_sequence(a, qtok);
+  for (int64_t vrow = wave0; vrow < n_rows; vrow += n_waves) {
+    RowSeq q;
+    int64_t qtok;
+    int h;
+    if (!merge_row(a, vrow, q, qtok, h)) continue;   // the prefill kernel's row, or none
+    const int64_t row = qtok * a.nq + h;
     int nsp;
     int64_t pbase, pstride;
-    row_pieces(a, q, qtok, (int)(row - qtok * a.nq), row, nsp, pbase, pstride);
+    row_pieces(a, q, qtok, h, row, nsp, pbase, pstride);
     float M = -INFINITY, Ls = 0.0f;
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int sp0 = grp; sp0 < nsp; sp0 += 4 * NG) {
@@ -504,17 +565,19 @@ __global__ __launch_bounds__(256) void attn_reduce_rows_kernel(AttnArgs a) {
   const int jj = lane & (LP - 1);
   const int grp = lane / LP;
   const bool lane_on = jj < (hs >> 3);
-  const int64_t n_units = a.num_q_tokens * (a.nq / NG);
+  const int64_t n_units = merge_rows(a) / NG;
   const uint32_t sbits = (a.qm == 0 && lane_on) ? sign_bits8(a.seed, jj) : 0u;
   const float inv_b = 1.0f / (float)a.b;
   const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t n_waves = (int64_t)gridDim.x * (blockDim.x / kWave);
   for (int64_t u = wave0; u < n_units; u += n_waves) {
-    const int64_t row0 = u * NG;                              // the wave's first row
-    const int64_t qtok = (uint32_t)row0 / (uint32_t)a.nq;     // one token for all NG rows
-    const RowSeq q = row_sequence(a, qtok);
-    const int h = (int)(row0 - qtok * a.nq) + grp;
-    const int64_t row = row0 + grp;
+    // the wave's NG rows: consecutive heads of one query token
+    RowSeq q;
+    int64_t qtok;
+    int h0;
+    if (!merge_row(a, u * NG, q, qtok, h0)) continue;   // the prefill kernel's rows, or none
+    const int h = h0 + grp;
+    const int64_t row = qtok * a.nq + h;
     int nsp;
     int64_t pbase, pstride;
     row_pieces(a, q, qtok, h, row, nsp, pbase, pstride);
@@ -577,7 +640,7 @@ hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream) {
   const int LP = host_next_pow2(a.hs / 8);
   const int NG = kWave / LP;
-  const int64_t rows = a.num_q_tokens * a.nq;
+  const int64_t rows = a.plan.pf_qlen > 0 ? (int64_t)a.num_seqs * a.plan.pf_tq * a.nq : a.num_q_tokens * a.nq;
   // one row per lane group where the caller asks for it and a wave's NG rows
   // share one query token
   if (a.reduce_rows && a.nq % NG == 0) {

@@ -91,6 +91,10 @@ constexpr int mfma_waves_per_block(int hpw, int qm, int hs) {
   return (hpw == 4 || (qm != 0 && hs >= 192)) ? 2 : 4;
 }
 
+// Sequences the prefill kernel's in-kernel unit prefix covers (four per
+// thread of its 256); calls with more run without the prefill kernel.
+constexpr int kPfMaxSeqs = 1024;
+
 // Work decomposition of one attention call (chosen on the host from host-known
 // sizes only; no device data is read).
 struct AttnPlan {
@@ -113,6 +117,11 @@ struct AttnPlan {
   int vjh;             // MFMA, head size 128, hpw > 1: V staged per head (heads not adjacent)
   int rb;              // MFMA, int4, hpw 1: 16-row MFMA blocks per wave (1 or 2)
   int fused_plan;      // MFMA: the kernel computes the sequences' prefix itself (set at launch)
+  // Chunked-prefill sequences (int4, query length >= pf_qlen) run on the
+  // prefill kernel; the kernels above and the merge skip them. 0 = none.
+  int pf_qlen;
+  int pf_tq;           // prefill: query tokens per wave tile (32 rows / group)
+  int pf_grid;         // prefill: workgroups launched (a multiple of 8, >= its units)
 };
 
 struct AttnArgs {
@@ -151,6 +160,25 @@ struct AttnArgs {
   AttnPlan plan;
 };
 
+// Query range [qb, qe) and cached length L of sequence s, clamped to what the
+// call's buffers hold (the kernels read nothing outside them whatever the
+// metadata says).
+__device__ __forceinline__ void seq_extent(const AttnArgs& a, int s, int64_t& qb, int64_t& qe, int64_t& L) {
+  qb = a.qsl[s];
+  qe = a.qsl[s + 1];
+  qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
+  qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
+  L = a.seq_lens[s];
+  const int64_t cap = (int64_t)a.max_blocks * a.bs;
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+// Whether a sequence with the (clamped) query range [qb, qe) belongs to the
+// prefill kernel.
+__device__ __forceinline__ bool prefill_seq(const AttnArgs& a, int64_t qb, int64_t qe) {
+  return a.plan.pf_qlen > 0 && qe - qb >= a.plan.pf_qlen;
+}
+
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream);
@@ -160,5 +188,8 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, unsigned int* sink
 // num_seqs + 1 ints) followed by the matrix-core attention kernel.
 // In stream-K mode it sets a.plan.sk_grid, which the merge needs.
 hipError_t launch_attn_mfma(AttnArgs& a, int32_t* prefix, int64_t max_units, hipStream_t stream);
+// The chunked-prefill kernel (a.plan.pf_qlen > 0): every query row of the
+// prefill sequences, written to the output directly.
+hipError_t launch_attn_prefill(AttnArgs& a, hipStream_t stream);
 
 }  // namespace kv4

@@ -166,6 +166,35 @@ def test_workspace_size(L):
     assert "multiple" in kv4.kv4_last_error()
 
 
+def test_prefill_plan_compacts_the_split_rows(L, monkeypatch):
+    # A chunked-prefill batch (Qwen2.5-1.5B shape: 12/2 heads, hs 128, 4 x 512
+    # prefill + 60 decode tokens): the prefill sequences run on the prefill
+    # kernel, so the split partial rows are only those of sequences with at
+    # most 32 // 6 = 5 queries -- (split, sequence, query) rows instead of
+    # (split, query token) rows over all 2108 tokens.
+    monkeypatch.setenv("KV4_PREFILL", "1")
+    args = (2108, 64, 12, 2, 128, 512, 8192)
+    with_pf = L.kv4_paged_attention_workspace_size(*args)
+    monkeypatch.setenv("KV4_PREFILL", "0")
+    without = L.kv4_paged_attention_workspace_size(*args)
+    assert 0 < with_pf < without
+    # the same plan with more sequences than the prefill kernel's prefix holds
+    # (1100 > 1024) falls back to the single-kernel layout
+    monkeypatch.setenv("KV4_PREFILL", "1")
+    many = (1100 + 4 * 512, 1104, 12, 2, 128, 512, 8192)
+    a = L.kv4_paged_attention_workspace_size(*many)
+    monkeypatch.setenv("KV4_PREFILL", "0")
+    assert a == L.kv4_paged_attention_workspace_size(*many)
+    # by default the prefill kernel runs where long chunks carry the batch:
+    # 4 x 512 chunks alone, not the same chunks among 60 decode sequences
+    monkeypatch.delenv("KV4_PREFILL")
+    assert L.kv4_paged_attention_workspace_size(*args) == without
+    only = (2048, 4, 12, 2, 128, 512, 2560)
+    auto = L.kv4_paged_attention_workspace_size(*only)
+    monkeypatch.setenv("KV4_PREFILL", "0")
+    assert auto < L.kv4_paged_attention_workspace_size(*only)
+
+
 def test_dequant_validation(L):
     rc = L.kv4_dequant(16, 16, 4, 16, 3, 2, 96, 64, 16, 42, 1, 16, None)
     assert rc == EINVAL and "largest power of two" in kv4.kv4_last_error()
