@@ -83,13 +83,13 @@ constexpr int kSkMinGrid = 512;         // ... unless that leaves fewer than 2 w
 constexpr bool kPthMfma = true;        // matrix-core kernels for the int8 / fp8 caches
 constexpr int64_t kReduceRowsMinWaves = 2048;   // merge: one row per lane group from this many waves
 
-bool mfma_head_size(int hs) { return hs == 64 || hs == 96 || hs == 128 || hs == 192; }
+bool mfma_head_size(int hs) { return hs == 64 || hs == 96 || hs == 128 || hs == 192 || hs == 256; }
 
 // Kv heads one matrix-core wave serves by default at a head size: each head
 // adds a 2-slot LDS stage (about 8.7 KB at head size 128), and larger stages
 // cut the waves a CU holds below what hides the load latency (measured best:
-// 2 at 64, 96 and 128; 1 at 192).
-int mfma_hpw_max(int hs) { return hs == 192 ? 1 : 2; }
+// 2 at 64, 96 and 128; 1 at 192 and 256).
+int mfma_hpw_max(int hs) { return hs >= 192 ? 1 : 2; }
 
 // Host planner: depends only on host-known sizes (and the KV4_SPLIT_TOKENS /
 // KV4_FORCE_PATH overrides used by tests), so the workspace size and the
@@ -173,7 +173,7 @@ kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq,
   if (mfma && max_query_len <= 1 && qm == 0 && (lay_contig || hs == 128)) {
     long want = env_long("KV4_MFMA_HPW", 0);
     if (want != 1 && want != 2 && want != 4) want = mfma_hpw_max(hs);
-    if (want > 2 && (hs == 96 || hs == 192)) want = 2;   // four heads' V loads would exceed the load counter
+    if (want > 2 && (hs == 96 || hs >= 192)) want = 2;   // four heads' V loads would exceed the load counter
     while (want > 1 && (want * G > kMfmaRows || nkv % want != 0)) want >>= 1;
     p.hpw = (int)want;
   }
@@ -317,6 +317,7 @@ int64_t code_row_bytes(int qm, int32_t head_size) { return qm ? head_size : head
 // The kernels are built with the hint at head size 128 only: int4 with two or
 // four adjacent heads per wave, int8 / fp8 (one head of 128 bytes per wave).
 bool nt_kernel_built(int qm, int32_t head_size, const kv4::AttnPlan& p) {
+  if (p.path == 1 && head_size == 256 && qm == 0) return p.hpw == 1 && !p.vjh && p.rb == 1;   // 128-byte rows
   return p.path == 1 && head_size == 128 && (qm != 0 || (p.hpw >= 2 && !p.vjh && p.rb == 1));
 }
 

@@ -388,6 +388,10 @@ template <int HS, int HPW, int QM>
 constexpr int mfma_wpb() { return mfma_waves_per_block(HPW, QM, HS); }
 template <int HS, int HPW, int QM, int NRB = 1>
 constexpr int mfma_wpe() {
+  // head size 256: the q' pairs and accumulators of one kv head take the
+  // whole register file (one wave per SIMD; its two 8.4 KB stage slots
+  // still keep ~67 KB per CU in flight)
+  if constexpr (HS >= 256) return 1;
   return HPW == 1 && (NRB > 1 || HS >= 192 || (QM != 0 && HS >= 96)) ? 2 : MfmaShape<HPW>::WPE;
 }
 
@@ -417,7 +421,7 @@ constexpr int mfma_wpe() {
 // NT: the K and V code loads carry the non-temporal cache policy. The host
 // asks for it where every 128-byte line a wave loads is loaded by that wave
 // alone; built for head size 128 (int4 with two or four adjacent heads per
-// wave, int8 / fp8).
+// wave, int8 / fp8) and 256 (int4: one head's 128-byte rows).
 //
 // NRB (int4, one kv head per wave): 16-row MFMA blocks per wave. With NRB = 2
 // one wave serves 32 query rows (a prefill tile, or a multi-token decode
@@ -728,8 +732,12 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
     constexpr int NLV = QM ? 2 * StageGeoQ<HS>::VL
                            : (VJH ? 2 * HPW : (VJ ? 2 * (16 / RPI) : (VP ? 2 * VPL : HPW * 8 * NVR)));   // loads per issue_v
     // VJ: half tile hh of a slot (16 * RB bytes) sits in head hh's V region
-    // (2 KB; RB = 128, two or more heads per wave) or at V_OFF + hh KB (RB = 64)
-    auto vj_base = [&](auto* st, int hh) { return st + (RB == 128 ? hh * STH : hh * 1024) + SG::V_OFF; };
+    // (2 KB; RB = 128 of two heads per wave), at V_OFF + 2 hh KB (RB = 128 of
+    // one head, head size 256: its 4 KB V region) or at V_OFF + hh KB (RB = 64)
+    auto vj_base = [&](auto* st, int hh) {
+      return st + (RB == 128 ? (HPW > 1 ? hh * STH : hh * 2048) : hh * 1024) + SG::V_OFF;
+    };
+    static_assert(!(VJ && RB == 128 && HPW == 1) || StageGeo<HS>::VREG >= 4096, "one head's V region holds both half tiles");
     // VP: half tile hh in head hh's V region (two heads) or at V_OFF + hh KB (one)
     auto vp_base = [&](auto* st, int hh) { return st + (HPW == 1 ? hh * 1024 : hh * STH) + SG::V_OFF; };
     static_assert(NLK < 64 && NLV < 64, "vmcnt range");
@@ -893,6 +901,13 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
           if constexpr (NK == 4) {
             const uint4 x = *reinterpret_cast<const uint4*>(kr + 16 * lane);
             kw[h][0] = x.x; kw[h][1] = x.y; kw[h][2] = x.z; kw[h][3] = x.w;
+          } else if constexpr (NK == 8) {
+            // head size 256: two 16-byte loads per half tile (words 4 j .. 4 j + 3)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const uint4 x = *reinterpret_cast<const uint4*>(kr + j * SG::KREG + 16 * lane);
+              kw[h][4 * j] = x.x; kw[h][4 * j + 1] = x.y; kw[h][4 * j + 2] = x.z; kw[h][4 * j + 3] = x.w;
+            }
           } else if constexpr (NK == 3 || NK == 6) {
 #pragma unroll
             for (int j = 0; j < NK / 3; ++j) {
@@ -1047,7 +1062,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
             } else if constexpr (VJH) {
               x[i] = *reinterpret_cast<const uint32_t*>(st + hl * STH + SG::V_OFF + (i >> 2) * 1024 + vj_rd[i & 3]);
             } else if constexpr (VJ) {
-              const unsigned char* src = vj_base(st, i >> 2) + vj_rd[i & 3] + hl * HALF;
+              // region r of a 256-wide head: its columns 128 r .. 128 r + 127 are bytes 64 r .. of the row
+              const unsigned char* src = vj_base(st, i >> 2) + vj_rd[i & 3] + hl * HALF + 64 * r;
               if constexpr (HS >= 128) x[i] = *reinterpret_cast<const uint32_t*>(src);
               else x[i] = *reinterpret_cast<const uint16_t*>(src);
             } else {
@@ -1427,6 +1443,13 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
     }
     return hipErrorInvalidValue;
   }
+  if constexpr (HS == 256) {
+    if (a.code_nt && a.plan.hpw == 1) {
+      go(attn_mfma_kernel<HS, 1, 0, false, WIN, 1, true>, mfma_wpb<HS, 1, 0>(),
+         [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 1, 0, false, WIN, 1, true>(l, d); });
+      return hipSuccess;
+    }
+  }
   if constexpr (HS == 128) {
     if (a.code_nt && a.plan.hpw == 2) {
       go(attn_mfma_kernel<HS, 2, 0, false, WIN, 1, true>, mfma_wpb<HS, 2, 0>(),
@@ -1465,6 +1488,7 @@ hipError_t launch_attn_mfma(AttnArgs& a, int32_t* prefix, int64_t max_units, hip
       case 96: e = launch_hs<96, 0>(a, prefix, max_units, stream); break;
       case 128: e = launch_hs<128, 0>(a, prefix, max_units, stream); break;
       case 192: e = launch_hs<192, 0>(a, prefix, max_units, stream); break;
+      case 256: e = launch_hs<256, 0>(a, prefix, max_units, stream); break;
       default: return hipErrorInvalidValue;
     }
   } else if (a.qm == 1 || a.qm == 2) {
@@ -1477,6 +1501,9 @@ hipError_t launch_attn_mfma(AttnArgs& a, int32_t* prefix, int64_t max_units, hip
         break;
       case 192:
         e = q1 ? launch_hs<192, 1>(a, prefix, max_units, stream) : launch_hs<192, 2>(a, prefix, max_units, stream);
+        break;
+      case 256:
+        e = q1 ? launch_hs<256, 1>(a, prefix, max_units, stream) : launch_hs<256, 2>(a, prefix, max_units, stream);
         break;
       default: return hipErrorInvalidValue;
     }
