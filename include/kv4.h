@@ -424,6 +424,26 @@ kv4_status kv4_stream_read(const void* buffer, int64_t bytes, uint32_t* sink, in
                            void* stream);
 
 /*
+ * kv4_debug_flags -- the inputs the kernels of the current device clamped or
+ * skipped since the last clear, as KV4_DEBUG_* bits (libraries built with
+ * -DKV4_DEBUG; build.build_debug_library()). Every kernel keeps its
+ * accesses inside the caller's buffers whatever the metadata holds: a
+ * negative slot is padding (skipped, by contract); a slot past the cache, a
+ * page id outside [0, num_blocks), a seq_len beyond the page table or a
+ * query_start_loc entry outside [0, num_q_tokens] or decreasing is treated
+ * as "no data" or clamped. Debug builds also record each such event (one
+ * bit per kind, any kernel of the library) instead of only absorbing it.
+ * Synchronizes the current device first, so earlier calls on every stream
+ * are counted; with `clear` nonzero the flags are reset after the read.
+ * `flags` is a host pointer. Release builds: KV4_EUNSUPPORTED, *flags = 0.
+ */
+#define KV4_DEBUG_SLOT 1u     /* a write or dequant slot >= num_blocks * block_size */
+#define KV4_DEBUG_PAGE 2u     /* a block_table entry outside [0, num_blocks) */
+#define KV4_DEBUG_SEQLEN 4u   /* a seq_len < 0 or beyond max_blocks_per_seq * block_size */
+#define KV4_DEBUG_QSL 8u      /* a query_start_loc entry outside [0, num_q_tokens], or decreasing */
+kv4_status kv4_debug_flags(uint32_t* flags, int32_t clear);
+
+/*
  * kv4_last_error -- thread-local description of the last failure of a call
  * made on this thread ("" after a call that succeeded). Never NULL; the
  * string stays valid until the next kv4_* call on the same thread.

@@ -19,7 +19,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkv4.so")
+# KV4_LIBRARY selects another build of the same ABI (e.g. libkv4_debug.so)
+LIB_PATH = os.environ.get("KV4_LIBRARY") or os.path.join(_HERE, "libkv4.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kv4.h")
 
 KV4_OK, KV4_EINVAL, KV4_EUNSUPPORTED, KV4_EHIP, KV4_EWORKSPACE = 0, 1, 2, 3, 4
@@ -58,6 +59,7 @@ _SIGNATURES = {
                                    _c_int32, _c_uint64, _c_int32, _vp, _vp]),
     "kv4_last_error": (ctypes.c_char_p, []),
     "kv4_stream_read": (ctypes.c_int, [_vp, _c_int64, _vp, _c_int32, _vp]),
+    "kv4_debug_flags": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), _c_int32]),
     "kv4_pth_write": (ctypes.c_int, [_c_int32, _vp, _vp, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp,
                                      _c_int64, _c_int32, _c_int32, _c_int32, _c_int64, _vp]),
     "kv4_pth_dequant": (ctypes.c_int, [_c_int32, _vp, _vp, _c_int64, _vp, _c_int64, _c_int32, _c_int32,
@@ -357,6 +359,18 @@ def kv4_stream_read(buffer: torch.Tensor, sink: torch.Tensor, grid: int = 2048, 
     nbytes = buffer.numel() * buffer.element_size()
     _check("kv4_stream_read", lib().kv4_stream_read(buffer.data_ptr(), nbytes - nbytes % 16, sink.data_ptr(),
                                                     int(grid), _stream(stream)))
+
+
+KV4_DEBUG_SLOT, KV4_DEBUG_PAGE, KV4_DEBUG_SEQLEN, KV4_DEBUG_QSL = 1, 2, 4, 8
+
+
+def kv4_debug_flags(clear: bool = False) -> int:
+    """KV4_DEBUG_* bits of the inputs the kernels clamped or skipped (a
+    library built with -DKV4_DEBUG, selected with KV4_LIBRARY; see
+    include/kv4.h). Synchronizes the device."""
+    v = ctypes.c_uint32(0)
+    _check("kv4_debug_flags", lib().kv4_debug_flags(ctypes.byref(v), 1 if clear else 0))
+    return int(v.value)
 
 
 __all__ = ["kv4_rht_write", "kv4_paged_attention", "kv4_paged_attention_workspace_size", "kv4_dequant",

@@ -40,9 +40,9 @@ PER_FILE = {
 }
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -67,6 +67,28 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     return LIB
+
+
+# Debug build: the same sources with -DKV4_DEBUG, whose kernels also record
+# every input they clamp or skip (kv4_debug_flags in include/kv4.h), linked
+# as libkv4_debug.so next to the release library. Load it in place of the
+# release library by setting KV4_LIBRARY to its path before the binding's
+# first call.
+DEBUG_LIB = os.path.join(PKG, "libkv4_debug.so")
+DEBUG_BUILD = os.path.join(BUILD, "debug")
+
+
+def build_debug_library(verbose: bool = False) -> str:
+    os.makedirs(DEBUG_BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose, DEBUG_BUILD, ("-DKV4_DEBUG",)), SOURCES))
+    tmp = DEBUG_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"debug link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, DEBUG_LIB)
+    return DEBUG_LIB
 
 
 # Host-side sanitizers for the C ABI's validation and planner (kv4_api.cpp):

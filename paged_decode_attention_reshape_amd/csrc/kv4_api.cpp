@@ -716,6 +716,21 @@ kv4_status kv4_paged_attention_noalloc(const void* query, int64_t query_token_st
   return st;
 }
 
+kv4_status kv4_debug_flags(uint32_t* flags, int32_t clear) {
+  if (!flags) return fail(KV4_EINVAL, "flags must not be null");
+  *flags = 0;
+#ifdef KV4_DEBUG
+  if (kv4_status e = hip_status(hipDeviceSynchronize(), "kv4_debug_flags: device synchronize")) return e;
+  const bool c = clear != 0;
+  *flags = kv4::debug_flags_write(c) | kv4::debug_flags_mfma(c) | kv4::debug_flags_prefill(c) |
+           kv4::debug_flags_valu(c);
+  return ok();
+#else
+  (void)clear;
+  return fail(KV4_EUNSUPPORTED, "kv4_debug_flags: this library is built without KV4_DEBUG");
+#endif
+}
+
 kv4_status kv4_stream_read(const void* buffer, int64_t bytes, uint32_t* sink, int32_t grid, void* stream) {
   if (bytes < 0 || bytes % 16) return fail(KV4_EINVAL, "bytes must be a non-negative multiple of 16");
   if (grid < 1 || grid > 65536) return fail(KV4_EINVAL, "grid must be in [1, 65536], got %d", grid);

@@ -188,12 +188,8 @@ struct Unit {
 // consecutive kv heads) fastest, then head tile, then split, then query tile.
 __device__ __forceinline__ bool decode_unit(const AttnArgs& a, const int32_t* prefix, int u, Unit& un) {
   const int s = wave_search_le(prefix, a.num_seqs, u);
-  int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
-  qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
-  qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
-  int64_t L = a.seq_lens[s];
-  const int64_t cap = (int64_t)a.max_blocks * a.bs;
-  L = L < 0 ? 0 : (L > cap ? cap : L);
+  int64_t qb, qe, L;
+  seq_extent(a, s, qb, qe, L);
   const int split = a.plan.split_tokens;
   int nsp = (int)((L + split - 1) / split);
   nsp = nsp < 1 ? 1 : (nsp > a.plan.num_splits ? a.plan.num_splits : nsp);
@@ -615,6 +611,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
       int p = -1;
       if (idx < npages) {
         p = bt[idx];
+        KV4_DBG(p < 0 || p >= a.num_blocks, KV4_DEBUG_PAGE);
         p = (p >= 0 && p < a.num_blocks) ? p : -1;
       }
       pg_lane = p;
@@ -1233,12 +1230,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
       const int s_ = wave_search_le(pf, nseq, loc);
       const int64_t t0 = uniform(pf[s_]), t1 = uniform(pf[s_ + 1]);
       const int64_t end = min(x1 - (int64_t)q * S, t1);
-      int64_t qb = a.qsl[s_], qe = a.qsl[s_ + 1];
-      qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
-      qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
-      int64_t L = a.seq_lens[s_];
-      const int64_t cap = (int64_t)a.max_blocks * a.bs;
-      L = L < 0 ? 0 : (L > cap ? cap : L);
+      int64_t qb, qe, L;
+      seq_extent(a, s_, qb, qe, L);
       const int uqb = uniform((int)qb), uql = uniform((int)(qe - qb)), uL = uniform((int)L);
       const int fs = WIN ? sk_first_step(a.window, uL, uql) : 0;
       const int k0 = (int)(32 * (loc - t0 + fs));
@@ -1513,5 +1506,7 @@ hipError_t launch_attn_mfma(AttnArgs& a, int32_t* prefix, int64_t max_units, hip
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }
+
+KV4_DEBUG_ACCESSOR(debug_flags_mfma)
 
 }  // namespace kv4

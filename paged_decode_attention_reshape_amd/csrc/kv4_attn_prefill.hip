@@ -223,6 +223,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
     int p = -1;
     if (idx < npages) {
       p = bt[idx];
+      KV4_DBG(p < 0 || p >= a.num_blocks, KV4_DEBUG_PAGE);
       p = (p >= 0 && p < a.num_blocks) ? p : -1;
     }
     pg_lane = p;
@@ -615,5 +616,7 @@ hipError_t launch_attn_prefill(AttnArgs& a, hipStream_t stream) {
   else hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3((unsigned)grid), blk, 0, stream, a);
   return hipGetLastError();
 }
+
+KV4_DEBUG_ACCESSOR(debug_flags_prefill)
 
 }  // namespace kv4

@@ -58,14 +58,10 @@ __device__ __forceinline__ bool locate_tile(const AttnArgs& a, int64_t qt, Tile&
     lt = qt - (int64_t)s * a.plan.tiles_per_seq;
   }
   if (s < 0 || s >= a.num_seqs) return false;
-  int64_t qb = a.qsl[s], qe = a.qsl[s + 1];
-  qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
-  qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
+  int64_t qb, qe, L;
+  seq_extent(a, s, qb, qe, L);
   const int qlen = (int)(qe - qb);
   if (lt * tq >= qlen) return false;
-  int64_t L = a.seq_lens[s];
-  const int64_t cap = (int64_t)a.max_blocks * a.bs;
-  L = L < 0 ? 0 : (L > cap ? cap : L);
   t.s = s;
   t.i0 = (int)(lt * tq);
   t.qbeg = (int)qb;
@@ -229,6 +225,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
     if (valid) {
       const int page = bt[tok / a.bs];
       valid = page >= 0 && page < a.num_blocks;
+      KV4_DBG(!valid, KV4_DEBUG_PAGE);
       coff = a.lay.code_off(page, tok % a.bs, g);
       soff = a.lay.scale_off(page, tok % a.bs, g);
     }
@@ -671,5 +668,7 @@ hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream) {
   }
   return hipGetLastError();
 }
+
+KV4_DEBUG_ACCESSOR(debug_flags_valu)
 
 }  // namespace kv4

@@ -11,7 +11,40 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kv4.h"
+
 namespace kv4 {
+
+// Debug builds (-DKV4_DEBUG): each kernel records the inputs it clamps or
+// skips as KV4_DEBUG_* bits of a device word of its translation unit (a
+// vector atomic OR; never a trap), read and cleared through
+// kv4_debug_flags(). Release builds compile the checks away.
+#ifdef KV4_DEBUG
+namespace {
+__device__ unsigned int g_debug_flags;
+}
+#define KV4_DBG(cond, bit)                                  \
+  do {                                                      \
+    if (cond) atomicOr(&::kv4::g_debug_flags, (unsigned)(bit)); \
+  } while (0)
+// host accessor of this translation unit's word (defined once per file)
+#define KV4_DEBUG_ACCESSOR(fn)                                                  \
+  uint32_t fn(bool clear) {                                                     \
+    unsigned v = 0;                                                             \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(::kv4::g_debug_flags), sizeof(v)) != hipSuccess) v = 0;       \
+    if (clear) {                                                                \
+      const unsigned z = 0;                                                     \
+      (void)hipMemcpyToSymbol(HIP_SYMBOL(::kv4::g_debug_flags), &z, sizeof(z)); \
+    }                                                                           \
+    return v;                                                                   \
+  }
+#else
+#define KV4_DBG(cond, bit) \
+  do {                     \
+  } while (0)
+#define KV4_DEBUG_ACCESSOR(fn) \
+  uint32_t fn(bool) { return 0; }
+#endif
 
 constexpr int kWave = 64;
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -7,6 +7,8 @@
 
 #include <algorithm>
 
+#include "kv4_device.hpp"
+
 namespace kv4 {
 
 inline int host_next_pow2(int x) {
@@ -166,6 +168,8 @@ struct AttnArgs {
 __device__ __forceinline__ void seq_extent(const AttnArgs& a, int s, int64_t& qb, int64_t& qe, int64_t& L) {
   qb = a.qsl[s];
   qe = a.qsl[s + 1];
+  KV4_DBG(qb < 0 || qe < qb || qe > a.num_q_tokens, KV4_DEBUG_QSL);
+  KV4_DBG(a.seq_lens[s] < 0 || (int64_t)a.seq_lens[s] > (int64_t)a.max_blocks * a.bs, KV4_DEBUG_SEQLEN);
   qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
   qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
   L = a.seq_lens[s];
@@ -178,6 +182,12 @@ __device__ __forceinline__ void seq_extent(const AttnArgs& a, int s, int64_t& qb
 __device__ __forceinline__ bool prefill_seq(const AttnArgs& a, int64_t qb, int64_t qe) {
   return a.plan.pf_qlen > 0 && qe - qb >= a.plan.pf_qlen;
 }
+
+// Debug builds: the KV4_DEBUG_* words of the kernel files (0 in release).
+uint32_t debug_flags_write(bool clear);
+uint32_t debug_flags_mfma(bool clear);
+uint32_t debug_flags_prefill(bool clear);
+uint32_t debug_flags_valu(bool clear);
 
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);

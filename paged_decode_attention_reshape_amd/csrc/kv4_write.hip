@@ -246,6 +246,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96))) void writ
       if (u0 == 0) {                           // then the slot, while they are in flight
         const int64_t slot = uniform64(a.slot_mapping[t]);
         ok = slot >= 0 && slot < a.num_slots;
+        KV4_DBG(slot >= a.num_slots, KV4_DEBUG_SLOT);
         const int64_t pg = ok ? slot_page(a, slot) : 0;
         const int64_t tk = ok ? slot - pg * a.bs : 0;
         crow = pg * a.lay.blk + tk * a.lay.tok;
@@ -365,6 +366,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
       slot = a.slot_mapping[t];
     }
     const bool ok = in && slot >= 0 && slot < a.num_slots;
+    KV4_DBG(in && slot >= a.num_slots, KV4_DEBUG_SLOT);
     uint32_t codes = 0;
     uint2 bytes = make_uint2(0u, 0u);
     float sc = 0.0f;
@@ -490,5 +492,7 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream) {
   }
   return hipGetLastError();
 }
+
+KV4_DEBUG_ACCESSOR(debug_flags_write)
 
 }  // namespace kv4

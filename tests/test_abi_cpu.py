@@ -10,7 +10,7 @@ import pytest
 import paged_decode_attention_reshape_amd as kv4
 from paged_decode_attention_reshape_amd.build import build_library
 
-EINVAL, EWORKSPACE = kv4.KV4_EINVAL, kv4.KV4_EWORKSPACE
+EINVAL, EWORKSPACE, EUNSUPPORTED = kv4.KV4_EINVAL, kv4.KV4_EWORKSPACE, kv4.KV4_EUNSUPPORTED
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
         "kv4_pth_write", "kv4_pth_dequant", "kv4_pth_attention", "kv4_pth_attention_workspace_size",
         "kv4_cache_layout_packed", "kv4_cache_layout_inline", "kv4_write_layout",
         "kv4_attention_layout_workspace_size", "kv4_attention_layout", "kv4_dequant_layout",
-        "kv4_stream_read", "kv4_paged_attention_noalloc"])
+        "kv4_stream_read", "kv4_paged_attention_noalloc", "kv4_debug_flags"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -288,3 +288,26 @@ def test_planner_sweep_workspace_sizes(L):
         L.kv4_attention_layout_workspace_size(qm, ctypes.byref(lay), Tq, S, nq, nkv, hs, mql, msl)
         assert kv4.kv4_last_error() == ""
         assert L.kv4_paged_attention_workspace_size(0, S, nq, nkv, hs, mql, msl) == 0
+
+
+def test_debug_flags_need_a_debug_build(L):
+    import ctypes
+    v = ctypes.c_uint32(7)
+    assert L.kv4_debug_flags(ctypes.byref(v), 0) == EUNSUPPORTED
+    assert v.value == 0 and "KV4_DEBUG" in kv4.kv4_last_error()
+    assert L.kv4_debug_flags(None, 0) == EINVAL
+
+
+def test_debug_library_exports_the_same_abi():
+    """libkv4_debug.so (built with -DKV4_DEBUG) exports every symbol of the
+    header, like the release library."""
+    import os
+    import subprocess
+    from paged_decode_attention_reshape_amd import build as B
+    if not os.path.exists(B.DEBUG_LIB):
+        B.build_debug_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", B.DEBUG_LIB], capture_output=True, text=True,
+                         check=True).stdout
+    names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    missing = [f for f in kv4.header_functions() if f not in names]
+    assert not missing, missing
