@@ -124,6 +124,18 @@ def qwen_mixed(seed: int = 0, n_prefill: int = 4, chunk: int = 512, prefix: int 
         seq_lens=tuple(slens[i] for i in order), shuffle_seqs=True, data_seed=seed)
 
 
+def qwen_prefill(seed: int = 0) -> Workload:
+    """The chunked-prefill part of the Qwen2.5-1.5B mixed batch alone: its 4
+    sequences of 512 new tokens on a 2048-token prefix, no decode sequences."""
+    w = qwen_mixed(seed)
+    keep = [i for i, q in enumerate(w.query_lens) if q > 1]
+    return Workload(
+        name="qwen1p5b_prefill4x512", num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+        head_size=w.head_size, block_size=w.block_size,
+        query_lens=tuple(w.query_lens[i] for i in keep), seq_lens=tuple(w.seq_lens[i] for i in keep),
+        shuffle_seqs=True, data_seed=seed)
+
+
 def llama8b_long(seed: int = 0, batch: int = 128) -> Workload:
     """Llama-3-8B shape: 32/8 heads, head_size 128, ctx log-U[4096, 32768],
     1 % outlier channels x20."""
@@ -154,6 +166,18 @@ def llama8b_hs192(seed: int = 0, batch: int = 32, ctx: int = 16384) -> Workload:
         name="llama8b_hs192_b32x16k", num_q_heads=32, num_kv_heads=8, head_size=192,
         block_size=BLOCK_SIZE, query_lens=(1,) * batch, seq_lens=(ctx,) * batch,
         outlier_frac=0.01, data_seed=seed)
+
+
+def hs256_long(seed: int = 0, batch: int = 128) -> Workload:
+    """Head size 256 at the long-context batch: 16/4 heads (the same cache
+    bytes per token as 32/8 heads of 128), ctx log-U[4096, 32768], 1 % outlier
+    channels x20."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = _loguniform_ints(rng, 4096, 32768, batch)
+    return Workload(
+        name="gqa16x4_hs256_b128_logU4k-32k", num_q_heads=16, num_kv_heads=4,
+        head_size=256, block_size=BLOCK_SIZE, query_lens=(1,) * batch,
+        seq_lens=tuple(int(x) for x in lens), outlier_frac=0.01, data_seed=seed)
 
 
 def custom(name: str, nq: int, nkv: int, hs: int, query_lens: Sequence[int],
@@ -292,8 +316,10 @@ ALL = {
     "phi3": phi3,
     "llama1b": llama1b,
     "qwen_mixed": qwen_mixed,
+    "qwen_prefill": qwen_prefill,
     "llama8b_long": llama8b_long,
     "llama8b_hs192": llama8b_hs192,
+    "hs256_long": hs256_long,
     "llama8b_spec": llama8b_spec,
     "llama8b_spec4": lambda: llama8b_spec(qmin=4, qmax=4),
 }
