@@ -192,12 +192,18 @@ kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq,
     const int64_t quads = p.sk_quads;
     const int64_t max_steps = quads * num_seqs * (((int64_t)(max_seq_len < 1 ? 1 : max_seq_len) + 31) / 32);
     // at least kSkMinSteps steps per workgroup, but two workgroups per CU
-    // where the LDS holds them (measured: Phi-3-shaped decode, 16 steps per
-    // workgroup on 256 workgroups 3 % slower than 8 on 512)
+    // where the LDS holds them
     int64_t cap = std::max<int64_t>(max_steps / kSkMinSteps, std::min<int64_t>(kSkMinGrid, max_steps));
     const long forced = env_long("KV4_SK_GRID", 0);
     if (forced > 0) cap = forced;
     p.sk_pcap = (int)std::max<int64_t>(1, std::min<int64_t>(cap, kSkMaxGrid));
+    // int4 head sizes 64 and 96 (two kv heads per wave): one workgroup per
+    // CU, each with twice the steps, beats two. Measured with the cache read
+    // from HBM (4 rotated copies): Phi-3 shape 32 x 1k 49.9 -> 44.0 us, 64 x
+    // 1k 81.2 -> 70.4, 32 x 4k 144 -> 122; Llama-3.2-1B shape 64 x U[1k, 4k]
+    // 50.4 -> 48.8, 128 x 84.6 -> 80.6. At head size 128 the Llama-3-8B 32k
+    // batch loses 5 % that way and head size 192 22 %, so they keep two.
+    p.sk_per_cu = (qm == 0 && hs < 128 && forced <= 0) ? 1 : 0;
   }
   const int mql = max_query_len < 1 ? 1 : max_query_len;
   p.tiles_per_seq = (mql + p.tq - 1) / p.tq;

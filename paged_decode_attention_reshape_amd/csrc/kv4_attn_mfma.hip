@@ -1394,6 +1394,7 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
       // stream-K: exactly the workgroups the GPU holds at once (at most the
       // planner's cap, which sized the workspace)
       wgs = std::min<int64_t>(resident, a.plan.sk_pcap);
+      if (a.plan.sk_per_cu > 0) wgs = std::min<int64_t>(wgs, (int64_t)da.cus * a.plan.sk_per_cu);
       a.plan.sk_grid = (int)std::max<int64_t>(wgs, 1);
       wgs = a.plan.sk_grid;
     } else {

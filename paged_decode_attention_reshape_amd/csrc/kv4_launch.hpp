@@ -116,6 +116,7 @@ struct AttnPlan {
   int sk_quads;        // stream-K: kv head groups / waves per workgroup
   int sk_pcap;         // stream-K: most workgroups (sizes the workspace)
   int sk_grid;         // stream-K: workgroups launched (set at launch)
+  int sk_per_cu;       // stream-K: at most this many workgroups per CU (0: as many as fit)
   int vjh;             // MFMA, head size 128, hpw > 1: V staged per head (heads not adjacent)
   int rb;              // MFMA, int4, hpw 1: 16-row MFMA blocks per wave (1 or 2)
   int fused_plan;      // MFMA: the kernel computes the sequences' prefix itself (set at launch)
