@@ -21,8 +21,8 @@
 //     (two per SIMD, so one wave's vector work hides the other's matrix
 //     work). Each 32-token K/V step of a half is loaded once into that
 //     half's four-slot LDS ring (direct buffer -> LDS loads, spread over its
-//     four waves, three steps ahead) and read by all four; one workgroup
-//     barrier per step.
+//     four waves, two steps ahead) and read by all four; one workgroup
+//     barrier per two steps.
 //   * The two halves of a tile are merged in LDS at the end (log-sum-exp),
 //     so every row is finished on chip and written once as bf16: no fp32
 //     partials in memory, no merge kernel.
@@ -49,7 +49,8 @@ namespace {
 constexpr int kPfTiles = 4;                     // query tiles per workgroup
 constexpr int kPfHalves = 2;                    // key-range halves per tile
 constexpr int kPfWaves = kPfTiles * kPfHalves;  // waves per workgroup
-constexpr int kPfSlots = 4;                     // ring slots per half: 3 steps in flight, 1 being read
+constexpr int kPfSteps = 2;                     // key steps per workgroup barrier
+constexpr int kPfSlots = 2 * kPfSteps;          // ring slots per half: kPfSteps being read, kPfSteps in flight
 constexpr int kPfSeqsPerThread = (kPfMaxSeqs + 64 * kPfWaves - 1) / (64 * kPfWaves);
 
 // One ring slot: one 32-token step of one kv head (head size 128).
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
   constexpr int LP = 16;             // lanes per row in the q' / output passes (8 elements each)
   constexpr int RPP = kWave / LP;    // rows per pass
   constexpr int HALF = HS / 2;       // code bytes per token row of one kv head
-  constexpr int D = kPfSlots - 1;    // steps of lookahead
+  constexpr int D = kPfSlots - kPfSteps;   // steps of lookahead
   using SL = PfSlot;
   // one K/V ring per key half; per wave one 8 KB buffer: the q' rows of one
   // row block (bf16 hi, then lo) at the start, the second half's partial
@@ -474,8 +475,12 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
     for (int rb = 0; rb < NRB; ++rb) pacc[rb] = mfma_f16(ones, ph4[rb], pacc[rb]);
   };
 
-  // ---- the key walk: one workgroup barrier per step. At the barrier of step
-  // it every wave has finished step it - 1, so its slot takes step it + D.
+  // ---- the key walk: one workgroup barrier per pair of steps. At the
+  // barrier before steps it and it + 1 every wave has finished steps it - 2
+  // and it - 1, so their slots take steps it + D and it + D + 1. (One
+  // barrier per step measured 4 % slower: at each barrier the waves that
+  // finish first idle while their SIMD partner finishes alone; three or
+  // four steps per barrier, with their larger rings, gained less than two.)
   // (Running the two waves of a SIMD out of phase, one on QK while the other
   // is on the softmax, measured slower: the two code paths cost more
   // register moves than the overlap won.)
@@ -484,16 +489,22 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
   // slot pointers are restrict parameters: the compiler then knows that the
   // loads in flight (into other slots) do not feed the reads, and keeps them
   // in flight instead of draining the load counter before each read; the
-  // counts waited for below order them. The first D calls only load (the
+  // counts waited for below order them. The first calls only load (the
   // prologue), through the same instructions.
-  static_assert(kPfSlots == D + 1, "ring: D steps in flight, one being read");
-  auto step = [&](unsigned char* __restrict__ wr, const unsigned char* __restrict__ rc, int it) {
-    issue(wr, it + D);
+  static_assert(kPfSteps == 2 && D % kPfSteps == 0, "two steps per call");
+  auto step = [&](unsigned char* __restrict__ w0, unsigned char* __restrict__ w1,
+                  const unsigned char* __restrict__ r0, const unsigned char* __restrict__ r1, int it) {
+    issue(w0, it + D);
+    issue(w1, it + D + 1);
     if (it < 0) return;
-    const int base = kw0 + 32 * (hs0 + it);
-    if (it < hn && base < k1w && base + 32 > k0w) {   // wave-uniform
-      qk(rc);
-      smpv(rc, it);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = it + j;
+      const int base = kw0 + 32 * (hs0 + i);
+      if (i < hn && base < k1w && base + 32 > k0w) {   // wave-uniform
+        qk(j ? r1 : r0);
+        smpv(j ? r1 : r0, i);
+      }
     }
   };
   // slot of step i; the empty asm keeps the offset an opaque scalar, so the
@@ -504,17 +515,17 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
     asm volatile("" : "+s"(off));
     return myring + off;
   };
-  for (int it = -D; it < n0; ++it) {
+  for (int it = -D; it < n0; it += kPfSteps) {
     if (it >= 0) {
-      // this wave's loads of step it have landed (those of the D - 1 later
-      // steps may still be in flight)
-      if (role == 0) wait_vm<2 * (D - 1)>();
-      else wait_vm<D - 1>();
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // and this wave's LDS reads of step it - 1 have returned
+      // this wave's loads of steps it and it + 1 have landed (those of the
+      // D - 2 later steps may still be in flight)
+      if (role == 0) wait_vm<2 * (D - kPfSteps)>();
+      else wait_vm<D - kPfSteps>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // and this wave's LDS reads of steps it - 2, it - 1 have returned
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
-    step(slot_at(it + D), slot_at(it), it);
+    step(slot_at(it + D), slot_at(it + D + 1), slot_at(it), slot_at(it + 1), it);
   }
   wait_vm<0>();   // no load may land in LDS after this point
   __syncthreads();   // every wave is done with the q' lo rows (wbuf[t + 4] takes the merge partials)
