@@ -120,29 +120,38 @@ kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq,
     if (!std::strcmp(f, "mfma")) mfma = mfma_ok;
   }
   p.path = mfma ? 1 : 0;
-  // Chunked prefill (int4, head size 128, GQA group <= 32): sequences with
-  // more queries than one 32-row tile holds go to the prefill kernel, whose
-  // workgroups share each staged K/V step among four tiles and walk every
-  // tile's whole key range; the rest of the plan covers the other sequences
-  // (at most pf_tq queries each, so one tile per sequence).
+  // Chunked prefill (int4, head size 128, GQA group <= 32): with the prefill
+  // kernel on, every sequence with more than one query goes to it (its
+  // workgroups share each staged K/V step among four tiles of 32 / G tokens
+  // and walk every tile's whole key range); the rest of the plan covers the
+  // single-query sequences as decode (two kv heads per wave, stream-K where
+  // the heads allow), not as 32-row tiles with one query in them.
   //
   // KV4_PREFILL: 0 off, 1 on wherever the shape allows, otherwise (default)
-  // on where long chunks carry the batch: at least 8 x pf_tq query tokens
-  // per sequence on average. Measured (Qwen2.5-1.5B shape, hs 128, group
-  // 6): 4 chunks of 512 alone take 117 us with the prefill kernel against
-  // 192 us on the single-kernel plan; the same chunks with 60 decode
-  // sequences take 168 us against 160 us, because the decode rows, which
-  // the single kernel runs in the gaps of its prefill tiles, then cost a
-  // launch of their own.
+  // on where a long chunk is in the batch (max_query_len >= 8 tiles) and the
+  // tokens beyond one per sequence fill >= 2048 MFMA rows. Measured
+  // (attention call, cache read from HBM; prefill path against the
+  // single-kernel plan): Qwen2.5-1.5B shape (group 6) 4 chunks of 512 + 60
+  // decodes 128 against 160 us, 2 x 2048 + 30 decodes 268 / 332, the 4
+  // chunks alone 112 / 192; Llama-3-8B shape (group 4) 2 x 512 + 128
+  // decodes over 4k-32k contexts 521 / 812, 8 x 256 + 16 decodes 158 / 211.
+  // Left on the single-kernel plan: 1 x 512 + 60 decodes (106 / 98 with
+  // the prefill kernel), 4 x 64 + 60 decodes (94 / 63), 2-16 or 1-12
+  // queries per sequence with no long chunk (2363 / 984, 271 / 64: the
+  // prefill kernel walks each short sequence's whole context in two
+  // halves, far fewer waves than the decode kernel's splits). A batch of
+  // many short multi-query sequences beside one long chunk would also
+  // take the prefill kernel and be slow there; KV4_PREFILL=0 keeps it on
+  // the single-kernel plan.
   p.pf_qlen = 0;
   const long pf_mode = env_long("KV4_PREFILL", 2);
   if (mfma && qm == 0 && hs == 128 && G <= 32 && num_seqs <= kv4::kPfMaxSeqs && pf_mode != 0) {
     const int pf_tq = 32 / G;
-    const bool dominated = num_q_tokens >= 8LL * pf_tq * num_seqs;
-    if (max_query_len > pf_tq && (pf_mode == 1 || dominated) && (int64_t)num_seqs * pf_tq * nq < INT32_MAX) {
-      p.pf_qlen = pf_tq + 1;
+    const bool chunky = max_query_len >= 8 * pf_tq && (num_q_tokens - num_seqs) * G >= 2048;
+    if (max_query_len > pf_tq && (pf_mode == 1 || chunky) && (int64_t)num_seqs * nq < INT32_MAX) {
+      p.pf_qlen = 2;
       p.pf_tq = pf_tq;
-      max_query_len = pf_tq;
+      max_query_len = 1;
     }
   }
   // Two 16-row MFMA blocks per wave (int4, one kv head per wave) where a
@@ -269,8 +278,8 @@ WsLayout ws_layout(const kv4::AttnPlan& p, int64_t num_q_tokens, int32_t num_seq
     // (range piece, query token of the tile, q head), at most workgroups +
     // quads * sequences pieces
     // (beside the prefill kernel: one per (split, sequence, query of the
-    // sequence), at most pf_tq queries per sequence)
-    const size_t qrows = p.pf_qlen > 0 ? (size_t)num_seqs * (size_t)p.pf_tq : (size_t)num_q_tokens;
+    // sequence), at most pf_qlen - 1 queries per sequence)
+    const size_t qrows = p.pf_qlen > 0 ? (size_t)num_seqs * (size_t)(p.pf_qlen - 1) : (size_t)num_q_tokens;
     const size_t rows = p.sk ? ((size_t)p.sk_pcap + (size_t)p.sk_quads * (size_t)num_seqs) * (size_t)p.tq *
                                    (size_t)nq
                              : (size_t)p.num_splits * qrows * (size_t)nq;

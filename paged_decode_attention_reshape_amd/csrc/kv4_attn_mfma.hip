@@ -1265,10 +1265,10 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
     const int k1 = min(usp * split + split, kend);
     if (k0 >= k1 && usp > 0) continue;   // no keys for this tile in this split (the merge skips it)
     // split partial rows: (split, query token) rows, or with a prefill
-    // kernel alongside (sequences of at most pf_tq queries here) the compact
+    // kernel alongside (sequences of at most pf_qlen - 1 queries here) the compact
     // (split, sequence, query of the sequence) rows
     const int64_t ptok0 = a.plan.pf_qlen > 0
-                              ? (int64_t)usp * a.num_seqs * a.plan.pf_tq + (int64_t)us * a.plan.pf_tq - uqbeg
+                              ? ((int64_t)usp * a.num_seqs + us) * (a.plan.pf_qlen - 1) - uqbeg
                               : (int64_t)usp * a.num_q_tokens;
     run_unit(us, ui0, uqbeg, uqlen, uL, ug, uht, k0, k1, ptok0, a.plan.num_splits > 1);
   }

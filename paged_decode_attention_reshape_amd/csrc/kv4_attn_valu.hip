@@ -385,20 +385,21 @@ __device__ __forceinline__ RowSeq row_sequence_at(const AttnArgs& a, int s) {
 }
 
 // The merge's rows. With a prefill kernel alongside, only the other
-// sequences (at most pf_tq queries each) have partials: their rows are
-// enumerated as (sequence, query of the sequence < pf_tq, head), so no row
+// sequences (at most pf_qlen - 1 queries each) have partials: their rows are
+// enumerated as (sequence, query of the sequence < pf_qlen - 1, head), so no row
 // has to search for its sequence and the prefill rows are never visited;
 // otherwise rows are (query token, head). vrow -> (RowSeq, query token,
 // head); false where the row has nothing to merge here.
 __device__ __forceinline__ int64_t merge_rows(const AttnArgs& a) {
-  return a.plan.pf_qlen > 0 ? (int64_t)a.num_seqs * a.plan.pf_tq * a.nq : a.num_q_tokens * a.nq;
+  return a.plan.pf_qlen > 0 ? (int64_t)a.num_seqs * (a.plan.pf_qlen - 1) * a.nq : a.num_q_tokens * a.nq;
 }
 __device__ __forceinline__ bool prefill_row(const AttnArgs& a, const RowSeq& q, int64_t qtok);
 __device__ __forceinline__ bool merge_row(const AttnArgs& a, int64_t vrow, RowSeq& q, int64_t& qtok, int& h) {
   if (a.plan.pf_qlen > 0) {
     const int64_t sq = (uint32_t)vrow / (uint32_t)a.nq;   // rows number fewer than 2^31 (checked on the host)
     h = (int)(vrow - sq * a.nq);
-    const int s = (int)(sq / a.plan.pf_tq), i = (int)(sq - (int64_t)s * a.plan.pf_tq);
+    const int dq = a.plan.pf_qlen - 1;
+    const int s = (int)(sq / dq), i = (int)(sq - (int64_t)s * dq);
     q = row_sequence_at(a, s);
     qtok = q.qb + i;
     return q.qb >= 0 && qtok < q.qe && qtok < a.num_q_tokens && !prefill_row(a, q, qtok);
@@ -429,8 +430,8 @@ __device__ __forceinline__ void row_pieces(const AttnArgs& a, const RowSeq& q, i
   if (a.plan.pf_qlen > 0 && !a.plan.sk) {
     // compact split rows (split, sequence, query of the sequence) of the
     // sequences left to the matrix-core kernel beside the prefill kernel
-    pstride = (int64_t)a.num_seqs * a.plan.pf_tq * a.nq;
-    pbase = ((int64_t)q.s * a.plan.pf_tq + (qtok - q.qb)) * a.nq + h;
+    pstride = (int64_t)a.num_seqs * (a.plan.pf_qlen - 1) * a.nq;
+    pbase = ((int64_t)q.s * (a.plan.pf_qlen - 1) + (qtok - q.qb)) * a.nq + h;
   }
   if (a.plan.sk) {
     // stream-K: the workgroups whose step ranges cover this row's
@@ -637,7 +638,7 @@ hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream) {
   const int LP = host_next_pow2(a.hs / 8);
   const int NG = kWave / LP;
-  const int64_t rows = a.plan.pf_qlen > 0 ? (int64_t)a.num_seqs * a.plan.pf_tq * a.nq : a.num_q_tokens * a.nq;
+  const int64_t rows = a.plan.pf_qlen > 0 ? (int64_t)a.num_seqs * (a.plan.pf_qlen - 1) * a.nq : a.num_q_tokens * a.nq;
   // one row per lane group where the caller asks for it and a wave's NG rows
   // share one query token
   if (a.reduce_rows && a.nq % NG == 0) {

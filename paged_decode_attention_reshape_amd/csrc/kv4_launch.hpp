@@ -122,6 +122,7 @@ struct AttnPlan {
   int fused_plan;      // MFMA: the kernel computes the sequences' prefix itself (set at launch)
   // Chunked-prefill sequences (int4, query length >= pf_qlen) run on the
   // prefill kernel; the kernels above and the merge skip them. 0 = none.
+  // The other sequences have at most pf_qlen - 1 queries each.
   int pf_qlen;
   int pf_tq;           // prefill: query tokens per wave tile (32 rows / group)
   int pf_grid;         // prefill: workgroups launched (a multiple of 8, >= its units)

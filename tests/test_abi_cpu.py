@@ -169,9 +169,9 @@ def test_workspace_size(L):
 def test_prefill_plan_compacts_the_split_rows(L, monkeypatch):
     # A chunked-prefill batch (Qwen2.5-1.5B shape: 12/2 heads, hs 128, 4 x 512
     # prefill + 60 decode tokens): the prefill sequences run on the prefill
-    # kernel, so the split partial rows are only those of sequences with at
-    # most 32 // 6 = 5 queries -- (split, sequence, query) rows instead of
-    # (split, query token) rows over all 2108 tokens.
+    # kernel, so the split partial rows are only those of the single-query
+    # sequences -- (split, sequence) rows instead of (split, query token) rows
+    # over all 2108 tokens.
     monkeypatch.setenv("KV4_PREFILL", "1")
     args = (2108, 64, 12, 2, 128, 512, 8192)
     with_pf = L.kv4_paged_attention_workspace_size(*args)
@@ -185,14 +185,24 @@ def test_prefill_plan_compacts_the_split_rows(L, monkeypatch):
     a = L.kv4_paged_attention_workspace_size(*many)
     monkeypatch.setenv("KV4_PREFILL", "0")
     assert a == L.kv4_paged_attention_workspace_size(*many)
-    # by default the prefill kernel runs where long chunks carry the batch:
-    # 4 x 512 chunks alone, not the same chunks among 60 decode sequences
+    # by default the prefill kernel runs where a long chunk is in the batch
+    # and the tokens beyond one per sequence fill >= 2048 MFMA rows: the 4 x
+    # 512 chunks with or without the 60 decode sequences, not 4 x 64 chunks
+    # among them (1512 rows) nor short multi-query sequences alone
     monkeypatch.delenv("KV4_PREFILL")
-    assert L.kv4_paged_attention_workspace_size(*args) == without
+    assert L.kv4_paged_attention_workspace_size(*args) == with_pf
     only = (2048, 4, 12, 2, 128, 512, 2560)
     auto = L.kv4_paged_attention_workspace_size(*only)
+    small = (4 * 64 + 60, 64, 12, 2, 128, 64, 8192)
+    short = (415, 64, 12, 2, 128, 12, 8192)
+    auto_small = L.kv4_paged_attention_workspace_size(*small)
+    auto_short = L.kv4_paged_attention_workspace_size(*short)
     monkeypatch.setenv("KV4_PREFILL", "0")
     assert auto < L.kv4_paged_attention_workspace_size(*only)
+    assert auto_small == L.kv4_paged_attention_workspace_size(*small)
+    assert auto_short == L.kv4_paged_attention_workspace_size(*short)
+    monkeypatch.setenv("KV4_PREFILL", "1")
+    assert L.kv4_paged_attention_workspace_size(*small) != auto_small
 
 
 def test_dequant_validation(L):

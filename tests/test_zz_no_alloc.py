@@ -47,7 +47,10 @@ def test_noalloc_matches_workspace_entry_point_twice():
         assert nbad == 0
 
 
-def test_noalloc_refuses_batches_beyond_the_scratch():
+def test_noalloc_refuses_batches_beyond_the_scratch(monkeypatch):
+    # the mixed chunked-prefill batch on the single-kernel plan (its split
+    # partials over all 2108 query tokens: ~118 MB)
+    monkeypatch.setenv("KV4_PREFILL", "0")
     w = W.ALL["qwen_mixed"]()
     need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, w.num_q_heads, w.num_kv_heads,
                                                   w.head_size, w.max_query_len, w.max_seq_len)
