@@ -653,7 +653,11 @@ kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride,
     // waves share the latency-bound work (measured: 2048 rows at head size 64
     // 7 % faster per wave; 20k-25k rows 3-9 % faster per group).
     const int64_t ng = 64 / kv4::host_next_pow2(head_size / 8);
-    a.reduce_rows = (num_q_tokens * num_q_heads / ng >= kReduceRowsMinWaves) ? 1 : 0;
+    // the merge's rows: beside the prefill kernel only those of the other
+    // sequences (compact, pf_qlen - 1 queries per sequence)
+    const int64_t mrows =
+        (a.plan.pf_qlen > 0 ? (int64_t)num_seqs * (a.plan.pf_qlen - 1) : num_q_tokens) * num_q_heads;
+    a.reduce_rows = (mrows / ng >= kReduceRowsMinWaves) ? 1 : 0;
     if (const long f = env_long("KV4_REDUCE_ROWS", -1); f == 0 || f == 1) a.reduce_rows = (int)f;
     rc = hip_status(kv4::launch_attn_reduce(a, dst), "kv4_paged_attention merge launch");
   }
