@@ -84,12 +84,15 @@ constexpr bool kPthMfma = true;        // matrix-core kernels for the int8 / fp8
 constexpr int64_t kReduceRowsMinWaves = 2048;   // merge: one row per lane group from this many waves
 
 bool mfma_head_size(int hs) { return hs == 64 || hs == 96 || hs == 128 || hs == 192 || hs == 256; }
+// int4 head sizes 80 and 112 (b = 16) run on the kernels of 96 and 128 with
+// the 16 missing columns zero in q' (one kv head per wave)
+bool mfma_padded_head_size(int hs) { return hs == 80 || hs == 112; }
 
 // Kv heads one matrix-core wave serves by default at a head size: each head
 // adds a 2-slot LDS stage (about 8.7 KB at head size 128), and larger stages
 // cut the waves a CU holds below what hides the load latency (measured best:
 // 2 at 64, 96 and 128; 1 at 192 and 256).
-int mfma_hpw_max(int hs) { return hs >= 192 ? 1 : 2; }
+int mfma_hpw_max(int hs) { return (hs >= 192 || mfma_padded_head_size(hs)) ? 1 : 2; }
 
 // Host planner: depends only on host-known sizes (and the KV4_SPLIT_TOKENS /
 // KV4_FORCE_PATH overrides used by tests), so the workspace size and the
@@ -103,12 +106,14 @@ kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq,
   const int G = nq / nkv;
   const int64_t code_bytes = qm ? hs : hs / 2;
   // the matrix-core kernel moves 16-byte pieces with 32-bit offsets inside a
-  // 16-token half tile; heads of one token row side by side (and their
-  // scales) let one wave serve several kv heads
-  const bool lay_dma = lay.blk % 16 == 0 && lay.tok % 16 == 0 && lay.head % 16 == 0 &&
+  // 16-token half tile (head sizes 80 / 112: 4- and 12-byte pieces, so
+  // 4-byte strides); heads of one token row side by side (and their scales)
+  // let one wave serve several kv heads
+  const int dma_align = (qm == 0 && mfma_padded_head_size(hs)) ? 4 : 16;
+  const bool lay_dma = lay.blk % dma_align == 0 && lay.tok % dma_align == 0 && lay.head % dma_align == 0 &&
                        lay.tok <= (INT32_MAX - 4096) / 16;
   const bool lay_contig = lay.head == code_bytes && lay.shead == 1;
-  const bool hs_ok = mfma_head_size(hs) && (qm == 0 || kPthMfma);
+  const bool hs_ok = (mfma_head_size(hs) && (qm == 0 || kPthMfma)) || (qm == 0 && mfma_padded_head_size(hs));
   const bool mfma_ok = hs_ok && lay_dma && block_size % 16 == 0 && (block_size & (block_size - 1)) == 0;
   // The matrix-core kernel wherever the shape allows it: even single-query
   // decode with one query head per kv head (one busy MFMA row of 16 unless a
@@ -182,6 +187,7 @@ kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq,
   if (mfma && max_query_len <= 1 && qm == 0 && (lay_contig || hs == 128)) {
     long want = env_long("KV4_MFMA_HPW", 0);
     if (want != 1 && want != 2 && want != 4) want = mfma_hpw_max(hs);
+    if (mfma_padded_head_size(hs)) want = 1;   // padded rows: one head per wave
     if (want > 2 && (hs == 96 || hs >= 192)) want = 2;   // four heads' V loads would exceed the load counter
     while (want > 1 && (want * G > kMfmaRows || nkv % want != 0)) want >>= 1;
     p.hpw = (int)want;

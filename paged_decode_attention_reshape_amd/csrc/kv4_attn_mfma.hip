@@ -425,11 +425,22 @@ constexpr int mfma_wpe() {
 // operands once and feed both blocks' products, and each block keeps its own
 // softmax state (the v_scale exponent e is shared: it depends on the keys
 // only).
-template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB, bool NT = false>
+template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB, bool NT = false, bool PAD = false>
 __global__ __launch_bounds__((64 * mfma_wpb<HS, HPW, QM>()))
 __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfma_kernel(AttnArgs a,
                                                                                       const int32_t* prefix) {
   static_assert(NRB == 1 || (HPW == 1 && QM == 0), "two row blocks: int4, one kv head per wave");
+  // PAD: head sizes 80 and 112 (block size b = 16) on the instances of 96 and
+  // 128 (int4, one kv head per wave). The 16 missing columns are zero in q',
+  // so whatever K bytes sit there add nothing to the logits, and their output
+  // columns are neither written nor merged. Heads start 8-byte aligned (40 and
+  // 56 bytes apart), and every code load stays inside the head's hs / 2 bytes:
+  // V rows and the K rows of 112 come as 4-byte pieces (a piece past the row's
+  // end loads the row's first word again, for a column nothing reads); the K
+  // rows of 80 keep their 12-byte pieces, and the last quarter, which would
+  // cross the row's end, loads 8 bytes early and its reader takes word 2.
+  static_assert(!PAD || (QM == 0 && HPW == 1 && !PH && !NT && (HS == 96 || HS == 128)),
+                "padded head sizes: int4, one kv head per wave, 96 / 128 instances");
   using GG = Geo<HS>;
   using SG = typename StageSel<HS, QM>::T;
   using SM = MfmaSmem<HS, HPW, QM, NRB>;
@@ -483,6 +494,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
   // lane constants of the chunk mapping (q setup and epilogue)
   const int cj = lane & (LP - 1);
   const bool c_on = cj < HS / 8;
+  const int hsv = PAD ? a.hs : HS;                         // the head size of the call (PAD: HS - 16)
+  const bool c_live = PAD ? cj < hsv / 8 : c_on;           // a column chunk of the real head
   const uint32_t sbits = (QM == 0 && c_on) ? sign_bits8(a.seed, cj) : 0u;
   uint32_t sx[4];
   sign_xor_bf16x8(sbits, sx);
@@ -497,7 +510,18 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
   const int64_t page_rows = a.lay.sblk;                     // scale floats per page
   const int64_t s_tok = a.lay.stok, s_head = a.lay.shead;   // scale floats per token row / head
   constexpr int CA = NT ? 2 : 0;                            // cache policy of the K/V code loads
-  const uint32_t koff = (uint32_t)n * tok_stride + (uint32_t)q4 * (HALF / 4);
+  const uint32_t koff = (uint32_t)n * tok_stride + (uint32_t)q4 * (HALF / 4) - (PAD && HS == 96 && q4 == 3 ? 8u : 0u);
+  // PAD, head size 112: K word w of this lane's quarter (its 4 bytes, or the
+  // row's first word past the row's end)
+  constexpr bool PADW = PAD && HS == 128;
+  uint32_t kw_src[PADW ? 4 : 1];
+  if constexpr (PADW) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t b = (uint32_t)q4 * 16u + 4u * (uint32_t)w;
+      kw_src[w] = (uint32_t)n * tok_stride + (b < (uint32_t)hsv / 2 ? b : 0u);
+    }
+  }
   uint32_t vo[4];                                           // token 4*q4 + i, 32-bit column chunk n
 #pragma unroll
   for (int i = 0; i < 4; ++i) vo[i] = (uint32_t)(4 * q4 + i) * tok_stride + 4u * (uint32_t)n;
@@ -515,6 +539,18 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
   constexpr int RPI = 1024 / RB;                            // token rows per 1 KB load (VJ)
   const uint32_t vjh_src = (uint32_t)(lane >> 2) * tok_stride + 16u * (uint32_t)(lane & 3);
   const uint32_t vj_src = (uint32_t)((16 * lane) / RB) * tok_stride + (uint32_t)((16 * lane) % RB);
+  // PAD: V as 4-byte pieces, 64 lanes x 4 bytes per load, token-major in LDS
+  // (rows of RB bytes) as the 16-byte loads leave them: load k of a half tile
+  // takes its dwords 64 k .. 64 k + 63, the row's first word past the row's end
+  constexpr int PVL = PAD ? 16 * RB / 256 : 1;            // dword loads per half tile (3 or 4)
+  uint32_t pv_src[PVL];
+  if constexpr (PAD) {
+#pragma unroll
+    for (int k = 0; k < PVL; ++k) {
+      const int d = 64 * k + lane, t = d / (RB / 4), c = d % (RB / 4);
+      pv_src[k] = (uint32_t)t * tok_stride + (4 * c < hsv / 2 ? 4u * (uint32_t)c : 0u);
+    }
+  }
   // ... and lane (n, q4) reads, for token 4 q4 + i of a half tile, its column
   // chunk n of head hl at vj_rd[i] + hl * HALF: 4 bytes (8 columns, head
   // size 128; int8 / fp8: 4 columns of each 64-column region) or 2 bytes (4
@@ -627,9 +663,9 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
       const int ti = rr / gh, hi = rr - (rr / gh) * gh;
       const bool rv = hl < HPW && ti < ntok && hi < nh;
       uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (rv && c_on)
+      if (rv && c_live)
         w = *reinterpret_cast<const uint4*>(a.query + (int64_t)(uqbeg + ui0 + ti) * a.q_stride +
-                                           (int64_t)((kv0 + hl) * G + hq0 + hi) * HS + 8 * cj);
+                                           (int64_t)((kv0 + hl) * G + hq0 + hi) * hsv + 8 * cj);
       const uint32_t wd[4] = {w.x ^ sx[0], w.y ^ sx[1], w.z ^ sx[2], w.w ^ sx[3]};
       float v[8];
 #pragma unroll
@@ -725,9 +761,10 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
     // codes (issue_v, from the bases issue_k left). Steps past the end issue
     // loads with an empty buffer range (they fetch nothing and fill the slot
     // with zeros, which is never read).
-    constexpr int NLK = HPW * (2 * SG::NKL + 1);   // loads per issue_k
-    constexpr int NLV = QM ? 2 * StageGeoQ<HS>::VL
-                           : (VJH ? 2 * HPW : (VJ ? 2 * (16 / RPI) : (VP ? 2 * VPL : HPW * 8 * NVR)));   // loads per issue_v
+    constexpr int NLK = HPW * (2 * (PADW ? 4 : SG::NKL) + 1);   // loads per issue_k
+    constexpr int NLV = PAD ? 2 * PVL
+                            : QM ? 2 * StageGeoQ<HS>::VL
+                            : (VJH ? 2 * HPW : (VJ ? 2 * (16 / RPI) : (VP ? 2 * VPL : HPW * 8 * NVR)));   // loads per issue_v
     // VJ: half tile hh of a slot (16 * RB bytes) sits in head hh's V region
     // (2 KB; RB = 128 of two heads per wave), at V_OFF + 2 hh KB (RB = 128 of
     // one head, head size 256: its 4 KB V region) or at V_OFF + hh KB (RB = 64)
@@ -782,22 +819,35 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
       for (int hl = 0; hl < HPW; ++hl) {
         unsigned char* sth = st + hl * STH;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+          if constexpr (PADW) {
+            // K word w of every lane at K_OFF + h KHALF + 256 w (KHALF = 1 KB)
 #pragma unroll
-          for (int j = 0; j < SG::NKL; ++j) {
-            unsigned char* dst = sth + SG::K_OFF + h * SG::KHALF + j * SG::KREG;
-            const uint32_t o = koff + j * SG::KSZ + hl * head_bytes;
-            if constexpr (SG::KSZ == 16) dma_buf<16, CA>(rk[h], o, dst);
-            else if constexpr (SG::KSZ == 12) dma_buf<12, CA>(rk[h], o, dst);
-            else dma_buf<4, CA>(rk[h], o, dst);
+            for (int w = 0; w < 4; ++w) dma_buf<4, CA>(rk[h], kw_src[w], sth + SG::K_OFF + h * SG::KHALF + w * 256);
+          } else {
+#pragma unroll
+            for (int j = 0; j < SG::NKL; ++j) {
+              unsigned char* dst = sth + SG::K_OFF + h * SG::KHALF + j * SG::KREG;
+              const uint32_t o = koff + j * SG::KSZ + hl * head_bytes;
+              if constexpr (SG::KSZ == 16) dma_buf<16, CA>(rk[h], o, dst);
+              else if constexpr (SG::KSZ == 12) dma_buf<12, CA>(rk[h], o, dst);
+              else dma_buf<4, CA>(rk[h], o, dst);
+            }
           }
+        }
         dma(scp + hl * s_head, sth + SG::S_OFF, 4);
       }
     };
     auto issue_v = [&](unsigned char* __restrict__ st) {
       const __amdgpu_buffer_rsrc_t rv[2] = {rsrc(a.value_cache + v_bya, v_nrec),
                                             rsrc(a.value_cache + v_byb, v_nrec)};
-      if constexpr (QM != 0) {
+      if constexpr (PAD) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int k = 0; k < PVL; ++k)
+            dma_buf<4, CA>(rv[hh], pv_src[k], (VP ? vp_base(st, hh) : vj_base(st, hh)) + k * 256);
+      } else if constexpr (QM != 0) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -895,7 +945,10 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const unsigned char* kr = st + hl * STH + SG::K_OFF + h * SG::KHALF;
-          if constexpr (NK == 4) {
+          if constexpr (PADW) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) kw[h][w] = reinterpret_cast<const uint32_t*>(kr + w * 256)[lane];
+          } else if constexpr (NK == 4) {
             const uint4 x = *reinterpret_cast<const uint4*>(kr + 16 * lane);
             kw[h][0] = x.x; kw[h][1] = x.y; kw[h][2] = x.z; kw[h][3] = x.w;
           } else if constexpr (NK == 8) {
@@ -915,6 +968,12 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
 #pragma unroll
             for (int j = 0; j < NK; ++j) kw[h][j] = reinterpret_cast<const uint32_t*>(kr + j * 256)[lane];
           }
+        }
+        if constexpr (PAD && HS == 96) {
+          // the last quarter's 12 bytes were loaded 8 bytes early: its real
+          // k-step (0) is word 2
+#pragma unroll
+          for (int h = 0; h < 2; ++h) kw[h][0] = q4 == 3 ? kw[h][2] : kw[h][0];
         }
         f32x4_t sa[NRB], sb[NRB];
 #pragma unroll
@@ -1119,7 +1178,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
         // (stream-K: one row per (piece, query token of the tile, q head))
         const int64_t ptok = a.plan.sk ? ptok0 * a.plan.tq + ti_b[rb] : ptok0 + qrow;
         const int64_t prow = ptok * a.nq + h;
-        float* dst = a.ws_o + prow * HS;
+        float* dst = a.ws_o + prow * hsv;
         int ns = 0;
 #pragma unroll
         for (int r = 0; r < NVRV; ++r) {
@@ -1127,7 +1186,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
           vreg(r, w, cb);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            if (VP && 4 * q4 + rr >= HS / 8) continue;   // MFMA rows past the head's columns
+            if ((VP || PAD) && 4 * q4 + rr >= hsv / 8) continue;   // MFMA rows past the head's columns
             float* d = dst + cb + w * (4 * q4 + rr);
             const f32x4_t* A = acc[rb];
             const float pb = pbias[rb];
@@ -1196,13 +1255,13 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = apply_sign(o[e] * inv_b, sbits, e);
       }
-      if (rv && c_on) {
+      if (rv && c_live) {
         uint4 wo;
         wo.x = pack_bf16x2(o[0], o[1]);
         wo.y = pack_bf16x2(o[2], o[3]);
         wo.z = pack_bf16x2(o[4], o[5]);
         wo.w = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<uint4*>(a.out + ((int64_t)(uqbeg + ui0 + ti) * a.nq + (kv0 + hl) * G + hq0 + hi) * HS +
+        *reinterpret_cast<uint4*>(a.out + ((int64_t)(uqbeg + ui0 + ti) * a.nq + (kv0 + hl) * G + hq0 + hi) * hsv +
                                   8 * cj) = wo;
       }
     }
@@ -1340,7 +1399,7 @@ static bool plan_lds_fits(const void* kernel, int resident, size_t plan_lds, con
 // Workgroups of the kernel the GPU holds at once (fused: with the plan LDS).
 // (per device: the occupancy query is answered for the current device), with
 // plan_lds bytes of dynamic LDS (the fused prefix; 0 without it)
-template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB = 1, bool NT = false>
+template <int HS, int HPW, int QM, bool PH, bool WIN, int NRB = 1, bool NT = false, bool PAD = false>
 static int resident_blocks(size_t plan_lds, const DevAttrs& da) {
   static std::mutex mu;
   static std::unordered_map<int64_t, int> per_cu;      // key: device, LDS
@@ -1352,7 +1411,7 @@ static int resident_blocks(size_t plan_lds, const DevAttrs& da) {
   }
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb,
-                                                   reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH, WIN, NRB, NT>),
+                                                   reinterpret_cast<const void*>(&attn_mfma_kernel<HS, HPW, QM, PH, WIN, NRB, NT, PAD>),
                                                    64 * mfma_wpb<HS, HPW, QM>(), plan_lds) != hipSuccess ||
       nb < 1)
     nb = 1;
@@ -1406,6 +1465,20 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
     hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(64 * wpb), a.plan.fused_plan ? plan_lds : 0, stream, a,
                        prefix);
   };
+  if (a.hs != HS) {
+    // head sizes 80 / 112 on the 96 / 128 instances (int4, one kv head per wave)
+    if constexpr (QM == 0 && (HS == 96 || HS == 128)) {
+      if (a.hs != HS - 16 || a.plan.hpw != 1 || a.plan.vjh || a.code_nt) return hipErrorInvalidValue;
+      if (a.plan.rb == 2)
+        go(attn_mfma_kernel<HS, 1, 0, false, WIN, 2, false, true>, mfma_wpb<HS, 1, 0>(),
+           [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 1, 0, false, WIN, 2, false, true>(l, d); });
+      else
+        go(attn_mfma_kernel<HS, 1, 0, false, WIN, 1, false, true>, mfma_wpb<HS, 1, 0>(),
+           [](size_t l, const DevAttrs& d) { return resident_blocks<HS, 1, 0, false, WIN, 1, false, true>(l, d); });
+      return hipSuccess;
+    }
+    return hipErrorInvalidValue;
+  }
   if constexpr (QM != 0) {
     if constexpr (HS == 128) {
       if (a.code_nt) {
@@ -1479,7 +1552,9 @@ hipError_t launch_attn_mfma(AttnArgs& a, int32_t* prefix, int64_t max_units, hip
   if (a.qm == 0) {
     switch (a.hs) {
       case 64: e = launch_hs<64, 0>(a, prefix, max_units, stream); break;
+      case 80:
       case 96: e = launch_hs<96, 0>(a, prefix, max_units, stream); break;
+      case 112:
       case 128: e = launch_hs<128, 0>(a, prefix, max_units, stream); break;
       case 192: e = launch_hs<192, 0>(a, prefix, max_units, stream); break;
       case 256: e = launch_hs<256, 0>(a, prefix, max_units, stream); break;
