@@ -47,6 +47,29 @@ def test_noalloc_matches_workspace_entry_point_twice():
         assert nbad == 0
 
 
+def test_noalloc_with_the_prefill_kernel(monkeypatch):
+    """A mixed chunked-prefill batch on the prefill kernel (its decode rows'
+    partials and both prefixes in the scratch; no side stream), then a smaller
+    decode batch: bit-identical to the workspace entry point, within G2."""
+    monkeypatch.setenv("KV4_PREFILL", "1")
+    cases = [
+        W.custom("noalloc_pf", 12, 2, 128, [150, 1, 1, 40, 1], [2000, 3000, 70, 400, 900], seed=5),
+        W.custom("noalloc_pf_small", 16, 4, 128, [1, 1], [300, 1000], seed=6),
+    ]
+    for w in cases:
+        need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, w.num_q_heads,
+                                                      w.num_kv_heads, w.head_size, w.max_query_len,
+                                                      w.max_seq_len)
+        assert 0 < need <= kv4.KV4_NOALLOC_SCRATCH_BYTES
+        r, out = _both(w)
+        got = host(out.float())
+        assert np.array_equal(got, host(r.out.float())), "noalloc differs from the workspace entry point"
+        ref = oracle_attention_on_gpu_cache(r)
+        nbad, mx = allclose_report(got, ref, atol=1e-2, rtol=1e-2)
+        say(f"    {w.name}: workspace {need} B; bit-identical; G2 max abs err {mx:.3e}")
+        assert nbad == 0
+
+
 def test_noalloc_refuses_batches_beyond_the_scratch(monkeypatch):
     # the mixed chunked-prefill batch on the single-kernel plan (its split
     # partials over all 2108 query tokens: ~118 MB)
