@@ -99,10 +99,19 @@ int mfma_hpw_max(int hs) { return (hs >= 192 || mfma_padded_head_size(hs)) ? 1 :
 // launch agree. Path 1 (matrix cores) is used where the query block is dense
 // (GQA group > 1 or query_len > 1), the head size is a multiple of 32 the
 // kernel is built for, and pages hold a power-of-two number (>= 16) of tokens.
-kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
+// The query lengths one launch of the kernels beside the prefill kernel
+// serves, and the prefill kernel's own threshold and tile.
+struct PfClass {
+  int pf_qlen, pf_tq, q_lo, q_hi;
+};
+
+// single: the plan without the prefill kernel. min_split: the launch of a
+// class beside it splits no finer than this many tokens.
+kv4_status make_plan_for(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
               int32_t max_query_len, int32_t max_seq_len, int32_t block_size, const kv4::CacheLayout& lay,
-              kv4::AttnPlan& p) {
+              kv4::AttnPlan& p, const PfClass* cls, PfClass* pf_out, bool single = false, int min_split = 0) {
   std::memset(&p, 0, sizeof(p));
+  if (pf_out) *pf_out = PfClass{0, 0, 0, 0};
   const int G = nq / nkv;
   const int64_t code_bytes = qm ? hs : hs / 2;
   // the matrix-core kernel moves 16-byte pieces with 32-bit offsets inside a
@@ -126,37 +135,51 @@ kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq,
   }
   p.path = mfma ? 1 : 0;
   // Chunked prefill (int4, head size 128, GQA group <= 32): with the prefill
-  // kernel on, every sequence with more than one query goes to it (its
-  // workgroups share each staged K/V step among four tiles of 32 / G tokens
-  // and walk every tile's whole key range); the rest of the plan covers the
-  // single-query sequences as decode (two kv heads per wave, stream-K where
-  // the heads allow), not as 32-row tiles with one query in them.
+  // kernel on, the sequences with more than Q = 4 tiles of 32 / G queries (at
+  // least one whole prefill workgroup) go to it, whose workgroups share each
+  // staged K/V step among four tiles and walk every tile's whole key range.
+  // The others run on the kernels above in two launches: the single-query
+  // sequences as decode (two kv heads per wave, stream-K where the heads
+  // allow), not as 32-row tiles with one query in them; those with 2 .. Q
+  // queries as tiles (and key splits), where the prefill kernel would walk
+  // their whole context in two halves with far fewer waves.
   //
   // KV4_PREFILL: 0 off, 1 on wherever the shape allows, otherwise (default)
-  // on where a long chunk is in the batch (max_query_len >= 8 tiles) and the
-  // tokens beyond one per sequence fill >= 2048 MFMA rows. Measured
-  // (attention call, cache read from HBM; prefill path against the
-  // single-kernel plan): Qwen2.5-1.5B shape (group 6) 4 chunks of 512 + 60
-  // decodes 128 against 160 us, 2 x 2048 + 30 decodes 268 / 332, the 4
-  // chunks alone 112 / 192; Llama-3-8B shape (group 4) 2 x 512 + 128
+  // on where a sequence may have more than Q queries and the tokens beyond
+  // one per sequence could fill 128 prefill workgroups ((T - S) x kv heads >=
+  // 128 Q). Measured (attention call, cache read from HBM; prefill path
+  // against the single-kernel plan): Qwen2.5-1.5B shape (group 6) 4 chunks of
+  // 512 + 60 decodes 128 against 160 us, 2 x 2048 + 30 decodes 268 / 332, the
+  // 4 chunks alone 112 / 192; Llama-3-8B shape (group 4) 2 x 512 + 128
   // decodes over 4k-32k contexts 521 / 812, 8 x 256 + 16 decodes 158 / 211.
-  // Left on the single-kernel plan: 1 x 512 + 60 decodes (106 / 98 with
-  // the prefill kernel), 4 x 64 + 60 decodes (94 / 63), 2-16 or 1-12
-  // queries per sequence with no long chunk (2363 / 984, 271 / 64: the
-  // prefill kernel walks each short sequence's whole context in two
-  // halves, far fewer waves than the decode kernel's splits). A batch of
-  // many short multi-query sequences beside one long chunk would also
-  // take the prefill kernel and be slow there; KV4_PREFILL=0 keeps it on
-  // the single-kernel plan.
+  // Left on the single-kernel plan: 1 x 512 + 60 decodes (106 / 98 with the
+  // prefill kernel: one chunk's workgroups take a whole walk of its context
+  // however many CUs are free), 4 x 64 + 60 decodes (94 / 63), and batches
+  // of short multi-query sequences.
   p.pf_qlen = 0;
-  const long pf_mode = env_long("KV4_PREFILL", 2);
-  if (mfma && qm == 0 && hs == 128 && G <= 32 && num_seqs <= kv4::kPfMaxSeqs && pf_mode != 0) {
-    const int pf_tq = 32 / G;
-    const bool chunky = max_query_len >= 8 * pf_tq && (num_q_tokens - num_seqs) * G >= 2048;
-    if (max_query_len > pf_tq && (pf_mode == 1 || chunky) && (int64_t)num_seqs * nq < INT32_MAX) {
-      p.pf_qlen = 2;
-      p.pf_tq = pf_tq;
-      max_query_len = 1;
+  if (cls) {
+    // a launch beside the prefill kernel: its class of query lengths
+    p.pf_qlen = cls->pf_qlen;
+    p.pf_tq = cls->pf_tq;
+    p.q_lo = cls->q_lo;
+    p.q_hi = cls->q_hi;
+    // partial rows per split: the fewer of sequences x q_hi and query tokens
+    p.tok_rows = num_q_tokens < (int64_t)num_seqs * cls->q_hi ? 1 : 0;
+    max_query_len = cls->q_hi;
+  } else if (!single) {
+    const long pf_mode = env_long("KV4_PREFILL", 2);
+    if (mfma && qm == 0 && hs == 128 && G <= 32 && num_seqs <= kv4::kPfMaxSeqs && pf_mode != 0) {
+      const int pf_tq = 32 / G;
+      const int Q = kv4::kPfUnitTiles * pf_tq;
+      const bool chunky = (num_q_tokens - num_seqs) * nkv >= 128LL * Q;
+      if (max_query_len > Q && (pf_mode == 1 || chunky) && (int64_t)num_seqs * Q * nq < INT32_MAX) {
+        p.pf_qlen = Q + 1;
+        p.pf_tq = pf_tq;
+        p.q_lo = 0;
+        p.q_hi = 1;
+        if (pf_out) *pf_out = PfClass{Q + 1, pf_tq, 2, Q};
+        max_query_len = 1;
+      }
     }
   }
   // Two 16-row MFMA blocks per wave (int4, one kv head per wave) where a
@@ -256,12 +279,41 @@ kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq,
       if (split < kMinSplit) split = kMinSplit;
     }
   }
+  // the launch of the 2 .. Q-query sequences beside the prefill kernel
+  // counts every query tile as its own, so it would split finer than the
+  // single-kernel plan; at that plan's split size its partials (at most as
+  // many rows per split) take no more workspace than that plan's
+  if (cls && !p.sk && split < min_split) split = min_split;
   if (mfma) split = (split + 31) / 32 * 32;   // the MFMA kernel walks 32-token steps
   if (split >= msl) split = mfma ? (msl + 31) / 32 * 32 : msl;
   p.split_tokens = (int)split;
   p.num_splits = (int)((msl + split - 1) / split);
   if (p.num_splits > 65535) return fail(KV4_EUNSUPPORTED, "too many KV splits (%d)", p.num_splits);
   if (units * p.num_splits > INT32_MAX / 2) return fail(KV4_EUNSUPPORTED, "too many work units");
+  return KV4_OK;
+}
+
+// The plan of a call, and with the prefill kernel on the plan of its second
+// launch beside it (the sequences with 2 .. Q queries; tile->pf_qlen = 0 where
+// there is none).
+kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
+              int32_t max_query_len, int32_t max_seq_len, int32_t block_size, const kv4::CacheLayout& lay,
+              kv4::AttnPlan& p, kv4::AttnPlan* tile = nullptr) {
+  PfClass pf{0, 0, 0, 0};
+  if (kv4_status e = make_plan_for(qm, num_q_tokens, num_seqs, nq, nkv, hs, max_query_len, max_seq_len, block_size,
+                                   lay, p, nullptr, &pf))
+    return e;
+  if (tile) {
+    std::memset(tile, 0, sizeof(*tile));
+    if (pf.pf_qlen > 0 && pf.q_hi >= pf.q_lo) {
+      kv4::AttnPlan one;
+      if (kv4_status e = make_plan_for(qm, num_q_tokens, num_seqs, nq, nkv, hs, max_query_len, max_seq_len,
+                                       block_size, lay, one, nullptr, nullptr, true))
+        return e;
+      return make_plan_for(qm, num_q_tokens, num_seqs, nq, nkv, hs, max_query_len, max_seq_len, block_size, lay,
+                           *tile, &pf, nullptr, false, one.sk ? 0 : one.split_tokens);
+    }
+  }
   return KV4_OK;
 }
 
@@ -283,9 +335,9 @@ WsLayout ws_layout(const kv4::AttnPlan& p, int64_t num_q_tokens, int32_t num_seq
     // split-KV: one row per (split, query token, q head); stream-K: one per
     // (range piece, query token of the tile, q head), at most workgroups +
     // quads * sequences pieces
-    // (beside the prefill kernel: one per (split, sequence, query of the
-    // sequence), at most pf_qlen - 1 queries per sequence)
-    const size_t qrows = p.pf_qlen > 0 ? (size_t)num_seqs * (size_t)(p.pf_qlen - 1) : (size_t)num_q_tokens;
+    // (beside the prefill kernel, compact rows: one per (split, sequence,
+    // query of the sequence), at most q_hi queries per sequence)
+    const size_t qrows = kv4::compact_rows(p) ? (size_t)num_seqs * (size_t)p.q_hi : (size_t)num_q_tokens;
     const size_t rows = p.sk ? ((size_t)p.sk_pcap + (size_t)p.sk_quads * (size_t)num_seqs) * (size_t)p.tq *
                                    (size_t)nq
                              : (size_t)p.num_splits * qrows * (size_t)nq;
@@ -295,6 +347,19 @@ WsLayout ws_layout(const kv4::AttnPlan& p, int64_t num_q_tokens, int32_t num_seq
   }
   w.total = off;
   return w;
+}
+
+// Workspace of a call: its plan's, then (with the prefill kernel) the second
+// launch's at the next 256-byte boundary (*tile_off).
+size_t plans_ws_bytes(const kv4::AttnPlan& p, const kv4::AttnPlan& tile, int64_t num_q_tokens, int32_t num_seqs,
+                      int32_t nq, int32_t hs, size_t* tile_off) {
+  size_t total = ws_layout(p, num_q_tokens, num_seqs, nq, hs).total;
+  if (tile.pf_qlen > 0) {
+    const size_t off = align_up(total, 256);
+    if (tile_off) *tile_off = off;
+    total = off + ws_layout(tile, num_q_tokens, num_seqs, nq, hs).total;
+  }
+  return total;
 }
 
 kv4_status check_attn_sizes(int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
@@ -499,13 +564,13 @@ size_t workspace_impl(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nu
   // block_size is not an argument here: size for the larger of the two paths
   size_t need = 0;
   for (int32_t bs : {16, 1}) {
-    kv4::AttnPlan p;
+    kv4::AttnPlan p, tile;
     const kv4::CacheLayout lay =
         layout ? *layout : kv4::packed_layout(num_kv_heads, (int)code_row_bytes(qm, head_size), 16);
     if (make_plan(qm, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len, max_seq_len,
-                  bs, lay, p))
+                  bs, lay, p, &tile))
       return 0;
-    const size_t n = ws_layout(p, num_q_tokens, num_seqs, num_q_heads, head_size).total;
+    const size_t n = plans_ws_bytes(p, tile, num_q_tokens, num_seqs, num_q_heads, head_size, nullptr);
     need = n > need ? n : need;
   }
   g_last_error.clear();
@@ -578,21 +643,32 @@ kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride,
   if (num_blocks < 1) return fail(KV4_EINVAL, "num_blocks must be >= 1 when there are query tokens");
   a.lay = layout ? *layout : kv4::packed_layout(num_kv_heads, (int)code_row_bytes(qm, head_size), block_size);
   if (kv4_status e = check_layout(qm, a.lay)) return e;
+  kv4::AttnPlan tile_plan;
   if (kv4_status e = make_plan(qm, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
-                       max_seq_len, block_size, a.lay, a.plan))
+                       max_seq_len, block_size, a.lay, a.plan, &tile_plan))
     return e;
-  const WsLayout ws = ws_layout(a.plan, num_q_tokens, num_seqs, num_q_heads, head_size);
+  size_t tile_off = 0;
+  const size_t ws_total =
+      plans_ws_bytes(a.plan, tile_plan, num_q_tokens, num_seqs, num_q_heads, head_size, &tile_off);
+  // the workspace pointers of one launch's plan, from byte `base` on
+  auto place = [&](kv4::AttnArgs& x, size_t base, int32_t*& pfx) {
+    const WsLayout w = ws_layout(x.plan, num_q_tokens, num_seqs, num_q_heads, head_size);
+    char* wsb = static_cast<char*>(workspace) + base;
+    pfx = nullptr;
+    if (w.total == 0) return;
+    if (x.plan.path == 1) pfx = reinterpret_cast<int32_t*>(wsb + w.prefix_off);
+    if (x.plan.sk || x.plan.num_splits > 1) {
+      x.ws_o = reinterpret_cast<float*>(wsb + w.o_off);
+      x.ws_ml = reinterpret_cast<float*>(wsb + w.ml_off);
+    }
+  };
   int32_t* prefix = nullptr;
-  if (ws.total > 0) {
-    if (!workspace || workspace_bytes < ws.total)
-      return fail(KV4_EWORKSPACE, "workspace of %zu bytes required, got %zu", ws.total,
+  if (ws_total > 0) {
+    if (!workspace || workspace_bytes < ws_total)
+      return fail(KV4_EWORKSPACE, "workspace of %zu bytes required, got %zu", ws_total,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(KV4_EINVAL, "workspace must be 16-byte aligned");
-    if (a.plan.path == 1) prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ws.prefix_off);
-    if (a.plan.sk || a.plan.num_splits > 1) {
-      a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.o_off);
-      a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_off);
-    }
+    place(a, 0, prefix);
   }
   a.query = static_cast<const uint16_t*>(query);
   a.q_stride = query_token_stride;
@@ -644,28 +720,46 @@ kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride,
         side = nullptr;
     }
   }
-  kv4_status rc = KV4_OK;
-  if (a.plan.path == 1) {
-    const int64_t max_units =
-        a.plan.n_qtiles * a.plan.n_head_tiles * (num_kv_heads / a.plan.hpw) * a.plan.num_splits;
-    rc = hip_status(kv4::launch_attn_mfma(a, prefix, max_units, dst), "kv4_paged_attention launch");
-  } else {
-    rc = hip_status(kv4::launch_attn_valu(a, dst), "kv4_paged_attention launch");
-  }
-  if (rc == KV4_OK && (a.plan.sk || a.plan.num_splits > 1)) {
-    // Many rows: one row per lane group (a quarter of the waves at head size
-    // 128, each folding its row's partials four loads at a time). Few rows:
-    // one row per wave, whose lane groups split the partials, so that more
-    // waves share the latency-bound work (measured: 2048 rows at head size 64
-    // 7 % faster per wave; 20k-25k rows 3-9 % faster per group).
-    const int64_t ng = 64 / kv4::host_next_pow2(head_size / 8);
-    // the merge's rows: beside the prefill kernel only those of the other
-    // sequences (compact, pf_qlen - 1 queries per sequence)
-    const int64_t mrows =
-        (a.plan.pf_qlen > 0 ? (int64_t)num_seqs * (a.plan.pf_qlen - 1) : num_q_tokens) * num_q_heads;
-    a.reduce_rows = (mrows / ng >= kReduceRowsMinWaves) ? 1 : 0;
-    if (const long f = env_long("KV4_REDUCE_ROWS", -1); f == 0 || f == 1) a.reduce_rows = (int)f;
-    rc = hip_status(kv4::launch_attn_reduce(a, dst), "kv4_paged_attention merge launch");
+  // the kernels of one plan (and their merge), on stream `to`
+  auto run_plan = [&](kv4::AttnArgs& x, int32_t* pfx, hipStream_t to) -> kv4_status {
+    kv4_status r = KV4_OK;
+    x.prefix = pfx;
+    if (x.plan.path == 1) {
+      const int64_t max_units =
+          x.plan.n_qtiles * x.plan.n_head_tiles * (num_kv_heads / x.plan.hpw) * x.plan.num_splits;
+      r = hip_status(kv4::launch_attn_mfma(x, pfx, max_units, to), "kv4_paged_attention launch");
+    } else {
+      r = hip_status(kv4::launch_attn_valu(x, to), "kv4_paged_attention launch");
+    }
+    if (r == KV4_OK && (x.plan.sk || x.plan.num_splits > 1)) {
+      // Many rows: one row per lane group (a quarter of the waves at head size
+      // 128, each folding its row's partials four loads at a time). Few rows:
+      // one row per wave, whose lane groups split the partials, so that more
+      // waves share the latency-bound work (measured: 2048 rows at head size 64
+      // 7 % faster per wave; 20k-25k rows 3-9 % faster per group).
+      const int64_t ng = 64 / kv4::host_next_pow2(head_size / 8);
+      // the merge's rows: beside the prefill kernel (compact rows) only those
+      // of the sequences this launch serves, q_hi queries per sequence
+      const int64_t mrows =
+          (kv4::compact_rows(x.plan) ? (int64_t)num_seqs * x.plan.q_hi : num_q_tokens) * num_q_heads;
+      x.reduce_rows = (mrows / ng >= kReduceRowsMinWaves) ? 1 : 0;
+      if (const long f = env_long("KV4_REDUCE_ROWS", -1); f == 0 || f == 1) x.reduce_rows = (int)f;
+      r = hip_status(kv4::launch_attn_reduce(x, to), "kv4_paged_attention merge launch");
+    }
+    return r;
+  };
+  kv4_status rc = run_plan(a, prefix, dst);
+  if (rc == KV4_OK && tile_plan.pf_qlen > 0) {
+    // the sequences with 2 .. Q queries: their own launch, with its own
+    // workspace region
+    kv4::AttnArgs t = a;
+    t.plan = tile_plan;
+    t.code_nt = code_lines_private(qm, head_size, t.plan, t.lay, key_cache, value_cache) ? 1 : 0;
+    t.ws_o = nullptr;
+    t.ws_ml = nullptr;
+    int32_t* tpfx = nullptr;
+    place(t, tile_off, tpfx);
+    rc = run_plan(t, tpfx, dst);
   }
   // The prefill kernel is enqueued after the decode kernel: the short,
   // memory-bound decode workgroups then spread over every CU first, and each

@@ -224,7 +224,7 @@ __device__ __forceinline__ int sk_first_step(int window, int64_t L, int64_t qlen
 __device__ __forceinline__ int seq_units(const AttnArgs& a, int s) {
   int64_t qb, qe, L;
   seq_extent(a, s, qb, qe, L);
-  if (prefill_seq(a, qb, qe)) return 0;   // the prefill kernel's
+  if (!served_seq(a, qb, qe)) return 0;   // the prefill kernel's, or another launch's
   if (a.plan.sk) return (qe > qb && L > 0) ? (int)((L + 31) / 32) - sk_first_step(a.window, L, qe - qb) : 0;
   const int split = a.plan.split_tokens;
   int nsp = (int)((L + split - 1) / split);
@@ -1323,11 +1323,11 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
     const int k0 = max(usp * split, kwin);
     const int k1 = min(usp * split + split, kend);
     if (k0 >= k1 && usp > 0) continue;   // no keys for this tile in this split (the merge skips it)
-    // split partial rows: (split, query token) rows, or with a prefill
-    // kernel alongside (sequences of at most pf_qlen - 1 queries here) the compact
+    // split partial rows: (split, query token) rows, or beside the prefill
+    // kernel (sequences of at most q_hi queries here) mostly the compact
     // (split, sequence, query of the sequence) rows
-    const int64_t ptok0 = a.plan.pf_qlen > 0
-                              ? ((int64_t)usp * a.num_seqs + us) * (a.plan.pf_qlen - 1) - uqbeg
+    const int64_t ptok0 = compact_rows(a.plan)
+                              ? ((int64_t)usp * a.num_seqs + us) * a.plan.q_hi - uqbeg
                               : (int64_t)usp * a.num_q_tokens;
     run_unit(us, ui0, uqbeg, uqlen, uL, ug, uht, k0, k1, ptok0, a.plan.num_splits > 1);
   }

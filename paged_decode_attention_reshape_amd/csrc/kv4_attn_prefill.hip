@@ -46,7 +46,7 @@ namespace kv4 {
 
 namespace {
 
-constexpr int kPfTiles = 4;                     // query tiles per workgroup
+constexpr int kPfTiles = kPfUnitTiles;          // query tiles per workgroup
 constexpr int kPfHalves = 2;                    // key-range halves per tile
 constexpr int kPfWaves = kPfTiles * kPfHalves;  // waves per workgroup
 constexpr int kPfSteps = 2;                     // key steps per workgroup barrier

@@ -384,40 +384,41 @@ __device__ __forceinline__ RowSeq row_sequence_at(const AttnArgs& a, int s) {
   return q;
 }
 
-// The merge's rows. With a prefill kernel alongside, only the other
-// sequences (at most pf_qlen - 1 queries each) have partials: their rows are
-// enumerated as (sequence, query of the sequence < pf_qlen - 1, head), so no row
-// has to search for its sequence and the prefill rows are never visited;
-// otherwise rows are (query token, head). vrow -> (RowSeq, query token,
-// head); false where the row has nothing to merge here.
-__device__ __forceinline__ int64_t merge_rows(const AttnArgs& a) {
-  return a.plan.pf_qlen > 0 ? (int64_t)a.num_seqs * (a.plan.pf_qlen - 1) * a.nq : a.num_q_tokens * a.nq;
+// The merge's rows. With a prefill kernel alongside, only the sequences this
+// launch serves (at most q_hi queries each) have partials here: with compact
+// rows they are enumerated as (sequence, query of the sequence < q_hi,
+// head), so no row has to search for its sequence and the prefill rows are
+// never visited; otherwise rows are (query token, head), and those of other
+// launches' sequences are skipped. vrow -> (RowSeq, query token, head);
+// false where the row has nothing to merge here.
+__host__ __device__ inline int64_t merge_rows(const AttnArgs& a) {
+  return compact_rows(a.plan) ? (int64_t)a.num_seqs * a.plan.q_hi * a.nq : a.num_q_tokens * a.nq;
 }
-__device__ __forceinline__ bool prefill_row(const AttnArgs& a, const RowSeq& q, int64_t qtok);
+__device__ __forceinline__ bool served_row(const AttnArgs& a, const RowSeq& q);
 __device__ __forceinline__ bool merge_row(const AttnArgs& a, int64_t vrow, RowSeq& q, int64_t& qtok, int& h) {
-  if (a.plan.pf_qlen > 0) {
+  if (compact_rows(a.plan)) {
     const int64_t sq = (uint32_t)vrow / (uint32_t)a.nq;   // rows number fewer than 2^31 (checked on the host)
     h = (int)(vrow - sq * a.nq);
-    const int dq = a.plan.pf_qlen - 1;
+    const int dq = a.plan.q_hi;
     const int s = (int)(sq / dq), i = (int)(sq - (int64_t)s * dq);
     q = row_sequence_at(a, s);
     qtok = q.qb + i;
-    return q.qb >= 0 && qtok < q.qe && qtok < a.num_q_tokens && !prefill_row(a, q, qtok);
+    return q.qb >= 0 && qtok < q.qe && qtok < a.num_q_tokens && served_row(a, q);
   }
   qtok = (uint32_t)vrow / (uint32_t)a.nq;
   h = (int)(vrow - qtok * a.nq);
   q = row_sequence(a, qtok);
-  return !prefill_row(a, q, qtok);
+  return served_row(a, q);
 }
 
-// Whether query token qtok belongs to a sequence of the prefill kernel (the
-// same clamped test the planner kernels apply).
-__device__ __forceinline__ bool prefill_row(const AttnArgs& a, const RowSeq& q, int64_t qtok) {
-  if (a.plan.pf_qlen <= 0 || qtok < q.qb || qtok >= q.qe) return false;
+// Whether this launch serves the row's sequence (the same clamped test the
+// planner kernels apply); every sequence without a prefill kernel.
+__device__ __forceinline__ bool served_row(const AttnArgs& a, const RowSeq& q) {
+  if (a.plan.pf_qlen <= 0) return true;
   int64_t qb = q.qb, qe = q.qe;
   qb = qb < 0 ? 0 : (qb > a.num_q_tokens ? a.num_q_tokens : qb);
   qe = qe < qb ? qb : (qe > a.num_q_tokens ? a.num_q_tokens : qe);
-  return prefill_seq(a, qb, qe);
+  return served_seq(a, qb, qe);
 }
 
 // The partials of output row `row` (query token qtok, query head h): nsp of
@@ -427,11 +428,11 @@ __device__ __forceinline__ void row_pieces(const AttnArgs& a, const RowSeq& q, i
   nsp = 0;
   pbase = row;
   pstride = a.num_q_tokens * a.nq;
-  if (a.plan.pf_qlen > 0 && !a.plan.sk) {
+  if (compact_rows(a.plan) && !a.plan.sk) {
     // compact split rows (split, sequence, query of the sequence) of the
     // sequences left to the matrix-core kernel beside the prefill kernel
-    pstride = (int64_t)a.num_seqs * (a.plan.pf_qlen - 1) * a.nq;
-    pbase = ((int64_t)q.s * (a.plan.pf_qlen - 1) + (qtok - q.qb)) * a.nq + h;
+    pstride = (int64_t)a.num_seqs * a.plan.q_hi * a.nq;
+    pbase = ((int64_t)q.s * a.plan.q_hi + (qtok - q.qb)) * a.nq + h;
   }
   if (a.plan.sk) {
     // stream-K: the workgroups whose step ranges cover this row's
@@ -638,7 +639,7 @@ hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream) {
   const int LP = host_next_pow2(a.hs / 8);
   const int NG = kWave / LP;
-  const int64_t rows = a.plan.pf_qlen > 0 ? (int64_t)a.num_seqs * (a.plan.pf_qlen - 1) * a.nq : a.num_q_tokens * a.nq;
+  const int64_t rows = merge_rows(a);
   // one row per lane group where the caller asks for it and a wave's NG rows
   // share one query token
   if (a.reduce_rows && a.nq % NG == 0) {

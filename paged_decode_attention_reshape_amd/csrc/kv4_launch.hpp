@@ -96,6 +96,9 @@ constexpr int mfma_waves_per_block(int hpw, int qm, int hs) {
 // Sequences the prefill kernel's in-kernel unit prefix covers (four per
 // thread of its 256); calls with more run without the prefill kernel.
 constexpr int kPfMaxSeqs = 1024;
+// Query tiles per prefill workgroup: sequences with more than this many tiles
+// of queries go to the prefill kernel.
+constexpr int kPfUnitTiles = 4;
 
 // Work decomposition of one attention call (chosen on the host from host-known
 // sizes only; no device data is read).
@@ -121,12 +124,22 @@ struct AttnPlan {
   int rb;              // MFMA, int4, hpw 1: 16-row MFMA blocks per wave (1 or 2)
   int fused_plan;      // MFMA: the kernel computes the sequences' prefix itself (set at launch)
   // Chunked-prefill sequences (int4, query length >= pf_qlen) run on the
-  // prefill kernel; the kernels above and the merge skip them. 0 = none.
-  // The other sequences have at most pf_qlen - 1 queries each.
+  // prefill kernel. 0 = none. Beside it the other sequences are split by
+  // query length into launches of the kernels above (and the merge), each
+  // serving q_lo <= query_len <= q_hi (< pf_qlen) and skipping the rest.
   int pf_qlen;
   int pf_tq;           // prefill: query tokens per wave tile (32 rows / group)
   int pf_grid;         // prefill: workgroups launched (a multiple of 8, >= its units)
+  int q_lo, q_hi;      // beside the prefill kernel: the query lengths this launch serves
+  // beside the prefill kernel: split partial and merge rows are (query token,
+  // head) as without it, where the batch has fewer query tokens than
+  // sequences x q_hi; otherwise (sequence, query of the sequence < q_hi, head)
+  int tok_rows;
 };
+
+// Whether a plan's split partial and merge rows are the compact (sequence,
+// query of the sequence, head) rows of a launch beside the prefill kernel.
+__host__ __device__ inline bool compact_rows(const AttnPlan& p) { return p.pf_qlen > 0 && !p.tok_rows; }
 
 struct AttnArgs {
   const uint16_t* query;
@@ -183,6 +196,13 @@ __device__ __forceinline__ void seq_extent(const AttnArgs& a, int s, int64_t& qb
 // prefill kernel.
 __device__ __forceinline__ bool prefill_seq(const AttnArgs& a, int64_t qb, int64_t qe) {
   return a.plan.pf_qlen > 0 && qe - qb >= a.plan.pf_qlen;
+}
+
+// Whether a launch of the kernels beside the prefill kernel serves the
+// sequence with the (clamped) query range [qb, qe): every sequence without
+// a prefill kernel, else those with q_lo <= query_len <= q_hi.
+__device__ __forceinline__ bool served_seq(const AttnArgs& a, int64_t qb, int64_t qe) {
+  return a.plan.pf_qlen <= 0 || (qe - qb >= a.plan.q_lo && qe - qb <= a.plan.q_hi);
 }
 
 // Debug builds: the KV4_DEBUG_* words of the kernel files (0 in release).

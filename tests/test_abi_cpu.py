@@ -185,10 +185,11 @@ def test_prefill_plan_compacts_the_split_rows(L, monkeypatch):
     a = L.kv4_paged_attention_workspace_size(*many)
     monkeypatch.setenv("KV4_PREFILL", "0")
     assert a == L.kv4_paged_attention_workspace_size(*many)
-    # by default the prefill kernel runs where a long chunk is in the batch
-    # and the tokens beyond one per sequence fill >= 2048 MFMA rows: the 4 x
-    # 512 chunks with or without the 60 decode sequences, not 4 x 64 chunks
-    # among them (1512 rows) nor short multi-query sequences alone
+    # by default the prefill kernel runs where a sequence may have more than
+    # Q = 4 tiles of queries (20 at group 6) and the tokens beyond one per
+    # sequence could fill 128 of its workgroups ((T - S) x kv heads >= 128 Q):
+    # the 4 x 512 chunks with or without the 60 decode sequences, not 4 x 64
+    # chunks among them (504 < 2560) nor short multi-query sequences alone
     monkeypatch.delenv("KV4_PREFILL")
     assert L.kv4_paged_attention_workspace_size(*args) == with_pf
     only = (2048, 4, 12, 2, 128, 512, 2560)
