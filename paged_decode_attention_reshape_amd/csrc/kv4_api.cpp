@@ -149,13 +149,13 @@ kv4_status make_plan_for(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t
   // one per sequence could fill 128 prefill workgroups ((T - S) x kv heads >=
   // 128 Q). Measured (attention call, cache read from HBM; prefill path
   // against the single-kernel plan): Qwen2.5-1.5B shape (group 6) 4 chunks of
-  // 512 + 60 decodes 128 against 160 us, 2 x 2048 + 30 decodes 268 / 332, the
-  // 4 chunks alone 112 / 192; Llama-3-8B shape (group 4) 2 x 512 + 128
-  // decodes over 4k-32k contexts 521 / 812, 8 x 256 + 16 decodes 158 / 211.
-  // Left on the single-kernel plan: 1 x 512 + 60 decodes (106 / 98 with the
-  // prefill kernel: one chunk's workgroups take a whole walk of its context
-  // however many CUs are free), 4 x 64 + 60 decodes (94 / 63), and batches
-  // of short multi-query sequences.
+  // 512 + 60 decodes 132 against 160 us, 2 x 2048 + 30 decodes 269 / 334;
+  // Llama-3-8B shape (group 4) 2 x 512 + 128 decodes over 4k-32k contexts
+  // 534 / 809, 8 x 256 + 16 decodes 158 / 209, 1 x 512 + 64 four-query
+  // sequences 503 / 513. Left on the single-kernel plan: Qwen shape 1 x 512 +
+  // 60 decodes (107 / 97 with the prefill kernel: one chunk's workgroups take
+  // a whole walk of its context however many CUs are free), 4 x 64 + 60
+  // decodes (94 / 63), 1 x 512 + 64 four-query sequences (108 / 75).
   p.pf_qlen = 0;
   if (cls) {
     // a launch beside the prefill kernel: its class of query lengths

@@ -349,11 +349,16 @@ struct StageGeoQ {
 template <int HS, int QM> struct StageSel { using T = StageGeoQ<HS>; };
 template <int HS> struct StageSel<HS, 0> { using T = StageGeo<HS>; };
 
-// Stage slots per wave: the loads of step it + 1 run during step it. More
-// slots keep more bytes in flight, but then the L2 evicts 128-byte lines
-// before the wave of the neighbouring kv head (which reads the other half of
-// the line) gets to them; two slots measured best.
-template <int HS>
+// Stage slots per wave: with kStages slots the loads of steps it + 1 ..
+// it + kStages - 1 run during step it. More slots keep more bytes in flight,
+// but two measured best: with the cache read from HBM, a third slot at head
+// size 64 took a Llama-3.2-1B decode batch from 47.3 to 49.2 us (a fourth
+// 52.3), at head size 96 a Phi-3 batch from 43.0 to 44.8, at 128 a Llama-3-8B
+// batch from 393 to 406 (one workgroup per CU instead of two) -- these waves
+// are bound by instruction issue, not by the loads in flight, and at head
+// size 128 the L2 also evicts 128-byte lines before the wave of the
+// neighbouring kv head (which reads the other half of the line) gets to them.
+template <int HS, int HPW, int QM>
 constexpr int stages_for() { return 2; }
 
 // Per wave: kStages stage slots, each holding HPW per-head stages (one per kv
@@ -364,7 +369,7 @@ struct MfmaSmem {
   static constexpr int STAGE_H = StageSel<HS, QM>::T::BYTES;   // one kv head
   static constexpr int STAGE = HPW * STAGE_H;               // one slot
   static constexpr int BUFB = 16 * NRB * HS * 4;            // q' staging / epilogue (fp32 rows)
-  static constexpr int NST = stages_for<HS>();
+  static constexpr int NST = stages_for<HS, HPW, QM>();
   static constexpr int MAINB = NST * STAGE > BUFB ? NST * STAGE : BUFB;
   alignas(16) unsigned char main[MAINB];
   float qsum[16 * NRB];
@@ -452,7 +457,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
   constexpr int RPP = kWave / LP;                                       // rows per pass
   constexpr int HALF = QM ? HS : HS / 2;        // code bytes per token row of one kv head
   static_assert(QM == 0 || HPW == 1, "int8 / fp8: one kv head per wave");
-  constexpr int kStages = stages_for<HS>();
+  constexpr int kStages = stages_for<HS, HPW, QM>();
   constexpr int STH = SM::STAGE_H;
   __shared__ SM smem_all[WPB];
   // fused plan: the sequences' prefix, computed by every workgroup
@@ -774,7 +779,6 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
     static_assert(!(VJ && RB == 128 && HPW == 1) || StageGeo<HS>::VREG >= 4096, "one head's V region holds both half tiles");
     // VP: half tile hh in head hh's V region (two heads) or at V_OFF + hh KB (one)
     auto vp_base = [&](auto* st, int hh) { return st + (HPW == 1 ? hh * 1024 : hh * STH) + SG::V_OFF; };
-    static_assert(NLK < 64 && NLV < 64, "vmcnt range");
     int64_t v_bya = 0, v_byb = 0;
     uint32_t v_nrec = 0;
     auto issue_k = [&](unsigned char* __restrict__ st, int it) {
@@ -890,22 +894,30 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
     };
 
     if (wg_sync) __builtin_amdgcn_s_barrier();
+    // LA = kStages - 1 steps of lookahead: the loads of steps it + 1 ..
+    // it + LA fly while step it is computed
+    constexpr int LA = kStages - 1;
+    constexpr int NLS = NLK + NLV;            // loads per step
+    static_assert(LA >= 1 && LA * NLS < 64, "vmcnt range");
     if (nsteps > 0) {
-      issue_k(sm.main, 0);
-      issue_v(sm.main);
+#pragma unroll
+      for (int j = 0; j < LA; ++j) {
+        issue_k(sm.main + j * SM::STAGE, j);
+        issue_v(sm.main + j * SM::STAGE);
+      }
     }
-    static_assert(kStages == 2, "one step of lookahead");
-    // `st` (read) and `wr` (filled for step it + 1) are distinct slots; the
+    // `st` (read) and `wr` (filled for step it + LA) are distinct slots; the
     // restrict qualifiers let the compiler keep the lookahead loads in flight
     // across the reads of the current step. Outstanding loads at the start of
-    // step it, oldest first: K(it), V(it).
+    // step it, oldest first: K(it), V(it), then K and V of each later step up
+    // to it + LA - 1.
     auto step = [&](const unsigned char* __restrict__ st, unsigned char* __restrict__ wr, int it) {
       const int slot = it % kStages;
       const int base = k0 + 32 * it;
-      wait_vm<NLV>();                         // K and scales of step it landed; V(it) may be in flight
+      wait_vm<NLV + (LA - 1) * NLS>();        // K and scales of step it landed; V(it) may be in flight
       if (wg_sync) __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      issue_k(wr, it + 1);                    // into the slot step it - 1 used
+      issue_k(wr, it + LA);                   // into the slot step it - 1 used
       const bool oka = (okmask >> (2 * slot)) & 1, okb = (okmask >> (2 * slot + 1)) & 1;
 
       // S^T = K . Q'^T per kv head, both half tiles (q' as hi + lo); lane n
@@ -1067,7 +1079,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
       }
       e_run = e_new;
 
-      wait_vm<NLK>();                         // V(it) landed; K(it + 1) may be in flight
+      wait_vm<NLK + (LA - 1) * NLS>();        // V(it) landed; the later steps' loads may be in flight
       __builtin_amdgcn_sched_barrier(0);
       issue_v(wr);
 
@@ -1155,8 +1167,11 @@ __attribute__((amdgpu_waves_per_eu(mfma_wpe<HS, HPW, QM, NRB>()))) void attn_mfm
         for (int rb = 0; rb < NRB; ++rb) pacc[rb] = mfma_f16(ones, ph4[rb], pacc[rb]);
       }
     };
-    for (int it = 0; it < nsteps; ++it)
-      step(sm.main + (it % kStages) * SM::STAGE, sm.main + ((it + 1) % kStages) * SM::STAGE, it);
+    for (int it = 0, rs = 0; it < nsteps; ++it) {
+      const int ws = rs == 0 ? kStages - 1 : rs - 1;   // slot of step it + LA
+      step(sm.main + rs * SM::STAGE, sm.main + ws * SM::STAGE, it);
+      rs = rs + 1 == kStages ? 0 : rs + 1;
+    }
     wait_vm<0>();                             // no load may land in LDS after this point
     __builtin_amdgcn_wave_barrier();
 
