@@ -82,6 +82,12 @@ constexpr int kSkMinSteps = 16;         // stream-K: KV steps per workgroup at l
 constexpr int kSkMinGrid = 512;         // ... unless that leaves fewer than 2 workgroups per CU (256 CUs)
 constexpr bool kPthMfma = true;        // matrix-core kernels for the int8 / fp8 caches
 constexpr int64_t kReduceRowsMinWaves = 2048;   // merge: one row per lane group from this many waves
+// Workgroups of the launch (and of the merge) of the 2 .. Q-query sequences
+// beside the prefill kernel. It is sized for every query tile of the batch,
+// yet often serves few sequences or none (a chunked-prefill batch of long
+// chunks and decodes), and while the prefill kernel holds most CUs a full
+// grid of workgroups that find no unit still queues for the few free CUs.
+constexpr int kTileLaunchWgs = 512;
 
 bool mfma_head_size(int hs) { return hs == 64 || hs == 96 || hs == 128 || hs == 192 || hs == 256; }
 // int4 head sizes 80 and 112 (b = 16) run on the kernels of 96 and 128 with
@@ -754,6 +760,7 @@ kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride,
     // workspace region
     kv4::AttnArgs t = a;
     t.plan = tile_plan;
+    t.plan.wg_cap = kTileLaunchWgs;
     t.code_nt = code_lines_private(qm, head_size, t.plan, t.lay, key_cache, value_cache) ? 1 : 0;
     t.ws_o = nullptr;
     t.ws_ml = nullptr;

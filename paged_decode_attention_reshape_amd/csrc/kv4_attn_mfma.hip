@@ -1473,7 +1473,7 @@ static hipError_t launch_hs_w(AttnArgs& a, const int32_t* prefix, int64_t max_un
       wgs = a.plan.sk_grid;
     } else {
       wgs = (max_units + wpb - 1) / wpb;
-      const int64_t cap = (int64_t)da.cus * 8;
+      const int64_t cap = a.plan.wg_cap > 0 ? std::min<int64_t>(a.plan.wg_cap, (int64_t)da.cus * 8) : (int64_t)da.cus * 8;
       if (wgs > cap) wgs = cap;
       if (wgs < 1) wgs = 1;
     }

@@ -494,6 +494,8 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   const int jj = lane & (LP - 1);
   const int grp = lane / LP;
   const bool lane_on = jj < (hs >> 3);
+  // beside the prefill kernel, a launch that found no unit left no partial
+  if (tile_class(a.plan) && a.prefix[a.num_seqs] == 0) return;
   const int64_t n_rows = merge_rows(a);
   const uint32_t sbits = (a.qm == 0 && lane_on) ? sign_bits8(a.seed, jj) : 0u;
   const float inv_b = 1.0f / (float)a.b;
@@ -564,6 +566,8 @@ __global__ __launch_bounds__(256) void attn_reduce_rows_kernel(AttnArgs a) {
   const int jj = lane & (LP - 1);
   const int grp = lane / LP;
   const bool lane_on = jj < (hs >> 3);
+  // beside the prefill kernel, a launch that found no unit left no partial
+  if (tile_class(a.plan) && a.prefix[a.num_seqs] == 0) return;
   const int64_t n_units = merge_rows(a) / NG;
   const uint32_t sbits = (a.qm == 0 && lane_on) ? sign_bits8(a.seed, jj) : 0u;
   const float inv_b = 1.0f / (float)a.b;
@@ -644,7 +648,7 @@ hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream) {
   // share one query token
   if (a.reduce_rows && a.nq % NG == 0) {
     const int64_t units = rows / NG;                 // waves (grid-stride beyond 2^22)
-    const int64_t blocks = std::min<int64_t>((units + 3) / 4, (int64_t)1 << 20);
+    const int64_t blocks = std::min<int64_t>((units + 3) / 4, a.plan.wg_cap > 0 ? a.plan.wg_cap : (int64_t)1 << 20);
     dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
     switch (LP) {
       case 1: hipLaunchKernelGGL(attn_reduce_rows_kernel<1>, grid, block, 0, stream, a); break;
@@ -657,7 +661,8 @@ hipError_t launch_attn_reduce(const AttnArgs& a, hipStream_t stream) {
     }
     return hipGetLastError();
   }
-  const int64_t blocks = std::min<int64_t>((rows + 3) / 4, (int64_t)1 << 20);   // one wave per row
+  const int64_t blocks =
+      std::min<int64_t>((rows + 3) / 4, a.plan.wg_cap > 0 ? a.plan.wg_cap : (int64_t)1 << 20);   // one wave per row
   dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(256);
   switch (LP) {
     case 1: hipLaunchKernelGGL(attn_reduce_kernel<1>, grid, block, 0, stream, a); break;

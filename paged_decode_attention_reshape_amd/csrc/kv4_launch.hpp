@@ -135,6 +135,9 @@ struct AttnPlan {
   // head) as without it, where the batch has fewer query tokens than
   // sequences x q_hi; otherwise (sequence, query of the sequence < q_hi, head)
   int tok_rows;
+  // most workgroups of this launch and of its merge (0: as many as the work
+  // asks); both loop over their units grid-stride
+  int wg_cap;
 };
 
 // Whether a plan's split partial and merge rows are the compact (sequence,
@@ -204,6 +207,10 @@ __device__ __forceinline__ bool prefill_seq(const AttnArgs& a, int64_t qb, int64
 __device__ __forceinline__ bool served_seq(const AttnArgs& a, int64_t qb, int64_t qe) {
   return a.plan.pf_qlen <= 0 || (qe - qb >= a.plan.q_lo && qe - qb <= a.plan.q_hi);
 }
+
+// Whether a plan is the launch of the 2 .. Q-query sequences beside the
+// prefill kernel.
+__host__ __device__ inline bool tile_class(const AttnPlan& p) { return p.pf_qlen > 0 && p.q_lo > 1; }
 
 // Debug builds: the KV4_DEBUG_* words of the kernel files (0 in release).
 uint32_t debug_flags_write(bool clear);
