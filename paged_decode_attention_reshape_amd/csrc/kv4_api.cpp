@@ -155,11 +155,11 @@ kv4_status make_plan_for(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t
   // one per sequence could fill 128 prefill workgroups ((T - S) x kv heads >=
   // 128 Q). Measured (attention call, cache read from HBM; prefill path
   // against the single-kernel plan): Qwen2.5-1.5B shape (group 6) 4 chunks of
-  // 512 + 60 decodes 132 against 160 us, 2 x 2048 + 30 decodes 269 / 334;
+  // 512 + 60 decodes 121 against 159 us, 2 x 2048 + 30 decodes 267 / 332;
   // Llama-3-8B shape (group 4) 2 x 512 + 128 decodes over 4k-32k contexts
-  // 534 / 809, 8 x 256 + 16 decodes 158 / 209, 1 x 512 + 64 four-query
-  // sequences 503 / 513. Left on the single-kernel plan: Qwen shape 1 x 512 +
-  // 60 decodes (107 / 97 with the prefill kernel: one chunk's workgroups take
+  // 529 / 816, 8 x 256 + 16 decodes 159 / 210, 1 x 512 + 64 four-query
+  // sequences 505 / 522. Left on the single-kernel plan: Qwen shape 1 x 512 +
+  // 60 decodes (106 / 98 with the prefill kernel: one chunk's workgroups take
   // a whole walk of its context however many CUs are free), 4 x 64 + 60
   // decodes (94 / 63), 1 x 512 + 64 four-query sequences (108 / 75).
   p.pf_qlen = 0;
@@ -277,6 +277,13 @@ kv4_status make_plan_for(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t
       } else {
         split = (long)((int64_t)msl * units * p.hpw / target);
         if (split < kMinSplit) split = kMinSplit;
+        // single-query decode beside the prefill kernel (split-KV where its
+        // heads leave no stream-K cut) gets only the CUs the prefill
+        // workgroups leave free: fewer, longer pieces there (measured on the
+        // mixed Qwen2.5-1.5B batch, 60 decodes over 256-8k contexts beside
+        // 4 chunks of 512: splits of 256 tokens 123 us, 512 117, 1024 120,
+        // 2048 145)
+        if (!cls && p.pf_qlen > 0 && !p.sk && split < 2 * kMinSplit) split = 2 * kMinSplit;
       }
     } else {
       int64_t ns = (kTargetUnitsValu + units - 1) / (units > 0 ? units : 1);
