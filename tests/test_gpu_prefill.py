@@ -1,7 +1,10 @@
 """Chunked prefill on the prefill kernel (int4, head size 128): sequences with
-more queries than one 32-row tile holds (query_len > 32 // group) run on the
-workgroup-shared prefill kernel, the others on the decode kernels and the
-merge, in the same call. Every case checks G1 (the written cache, bit-exact)
+more queries than four 32-row tiles hold (query_len > Q = 4 * (32 // group))
+run on the workgroup-shared prefill kernel; beside it, single-query
+sequences run as decode and those with 2 .. Q queries as query tiles in a
+launch of their own (its partial rows per (query token, head) where the
+batch has fewer tokens than sequences x Q, else per (sequence, query)), each
+with its merge, in the same call. Every case checks G1 (the written cache, bit-exact)
 and G2 (atol = rtol = 1e-2 against the fp64 oracle reading the cache the GPU
 wrote) on every output row, with groups 1 to 32 (tiles of 32 // group
 tokens), ragged last tiles, sequences of exactly one tile more than the
@@ -30,6 +33,10 @@ CASES = [
     ("g32", 32, 1, [2, 70, 1], [1000, 100, 65], 16),
     ("long_page_table", 12, 2, [600, 1], [5000, 3000], 16),
     ("only_prefill", 16, 4, [40, 41], [40, 3000], 16),
+    # one chunk beside 127 three-query sequences: the 2 .. Q launch has more
+    # units than its capped grid holds waves (grid-stride), token rows
+    ("many_short_beside_chunk", 32, 8, [200] + [3] * 127,
+     [1500] + [300 + (2700 * i) // 126 for i in range(127)], 16),
 ]
 
 
