@@ -170,8 +170,17 @@ size_t kv4_paged_attention_workspace_size(int64_t num_q_tokens, int32_t num_seqs
  * KV4_SK_GRID=<stream-K workgroups at most>, KV4_MFMA_RB=1 (one 16-row block
  * per wave), KV4_REDUCE_ROWS=0|1 (merge form), KV4_FUSED_PLAN=0 (separate
  * plan kernel), KV4_NT=0|1 (non-temporal K/V code loads, where a kernel is
- * built with them). Results agree within the rounding of the float32
- * accumulation order; KV4_NT and KV4_FUSED_PLAN leave them bit-identical.
+ * built with them), KV4_PREFILL=0|1 (int4, head size 128: the chunked-prefill
+ * kernel never / wherever the shape allows; by default where long chunks
+ * carry the batch), KV4_FORK=0 (see below). Results agree within the rounding
+ * of the float32 accumulation order; KV4_NT, KV4_FUSED_PLAN and KV4_FORK
+ * leave them bit-identical.
+ * With the prefill kernel, the other sequences' launches run on a stream the
+ * library owns (one per device), forked from `stream` with an event before
+ * them and joined back into it with an event after them, so that they fill
+ * the CUs the prefill workgroups leave; the call stays ordered on `stream`
+ * (KV4_FORK=0 runs everything on `stream`). Calls from several threads on
+ * one device take turns on that stream.
  * kv4_paged_attention_workspace_size reads the same variables: query it with
  * the same environment the call will see.
  */
@@ -199,8 +208,11 @@ kv4_status kv4_paged_attention(const void* query, int64_t query_token_stride,
  * call allocates and frees nothing. A batch whose plan needs more scratch than
  * that returns KV4_EWORKSPACE before any launch (the single-token decode
  * batches of the Phi-3, Llama-3.2-1B and Llama-3-8B shaped workloads need
- * 5-50 MB; a mixed batch with 512-token prefill chunks or many-token decode
- * needs more). All calls on one GPU share its array: two calls whose kernels may
+ * 5-50 MB; long many-token decode blocks and mixed batches without the
+ * prefill kernel need more). Beside the prefill kernel, the launch of the
+ * sequences with a few queries takes longer key pieces where that makes the
+ * call fit (results as kv4_paged_attention's up to the float32 accumulation
+ * order). All calls on one GPU share its array: two calls whose kernels may
  * run at the same time on one GPU (different streams, or the same stream
  * from several threads without ordering) race and give wrong results. The
  * array needs no initialization and keeps the last call's contents.

@@ -308,10 +308,10 @@ kv4_status make_plan_for(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t
 
 // The plan of a call, and with the prefill kernel on the plan of its second
 // launch beside it (the sequences with 2 .. Q queries; tile->pf_qlen = 0 where
-// there is none).
+// there is none), whose key pieces are at least tile_min_split tokens long.
 kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq, int32_t nkv, int32_t hs,
               int32_t max_query_len, int32_t max_seq_len, int32_t block_size, const kv4::CacheLayout& lay,
-              kv4::AttnPlan& p, kv4::AttnPlan* tile = nullptr) {
+              kv4::AttnPlan& p, kv4::AttnPlan* tile = nullptr, int tile_min_split = 0) {
   PfClass pf{0, 0, 0, 0};
   if (kv4_status e = make_plan_for(qm, num_q_tokens, num_seqs, nq, nkv, hs, max_query_len, max_seq_len, block_size,
                                    lay, p, nullptr, &pf))
@@ -324,7 +324,7 @@ kv4_status make_plan(int qm, int64_t num_q_tokens, int32_t num_seqs, int32_t nq,
                                        block_size, lay, one, nullptr, nullptr, true))
         return e;
       return make_plan_for(qm, num_q_tokens, num_seqs, nq, nkv, hs, max_query_len, max_seq_len, block_size, lay,
-                           *tile, &pf, nullptr, false, one.sk ? 0 : one.split_tokens);
+                           *tile, &pf, nullptr, false, std::max(one.sk ? 0 : one.split_tokens, tile_min_split));
     }
   }
   return KV4_OK;
@@ -628,7 +628,8 @@ kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride,
                    int64_t num_q_tokens, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_size, int32_t b, int32_t block_size, uint64_t sign_seed,
                    float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                   const kv4::CacheLayout* layout = nullptr, int32_t window = 0, bool allow_fork = true) {
+                   const kv4::CacheLayout* layout = nullptr, int32_t window = 0, bool allow_fork = true,
+                   bool fit_workspace = false) {
   if (kv4_status e = check_attn_sizes(num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
                                max_seq_len))
     return e;
@@ -661,8 +662,18 @@ kv4_status attention_impl(int qm, const void* query, int64_t query_token_stride,
                        max_seq_len, block_size, a.lay, a.plan, &tile_plan))
     return e;
   size_t tile_off = 0;
-  const size_t ws_total =
-      plans_ws_bytes(a.plan, tile_plan, num_q_tokens, num_seqs, num_q_heads, head_size, &tile_off);
+  size_t ws_total = plans_ws_bytes(a.plan, tile_plan, num_q_tokens, num_seqs, num_q_heads, head_size, &tile_off);
+  // a fixed workspace (the static scratch): the launch of the 2 .. Q-query
+  // sequences beside the prefill kernel takes longer key pieces, down to one
+  // per tile, until the call fits
+  for (int ms = tile_plan.split_tokens * 2; fit_workspace && ws_total > workspace_bytes && tile_plan.pf_qlen > 0 &&
+                                            !tile_plan.sk && tile_plan.num_splits > 1 && ms > 0 && ms <= INT32_MAX / 2;
+       ms *= 2) {
+    if (kv4_status e = make_plan(qm, num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, max_query_len,
+                                 max_seq_len, block_size, a.lay, a.plan, &tile_plan, ms))
+      return e;
+    ws_total = plans_ws_bytes(a.plan, tile_plan, num_q_tokens, num_seqs, num_q_heads, head_size, &tile_off);
+  }
   // the workspace pointers of one launch's plan, from byte `base` on
   auto place = [&](kv4::AttnArgs& x, size_t base, int32_t*& pfx) {
     const WsLayout w = ws_layout(x.plan, num_q_tokens, num_seqs, num_q_heads, head_size);
@@ -838,7 +849,7 @@ kv4_status kv4_paged_attention_noalloc(const void* query, int64_t query_token_st
                      num_blocks, block_table, max_blocks_per_seq, seq_lens, query_start_loc, num_seqs, num_q_tokens,
                      max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_size, b, block_size, sign_seed,
                      softmax_scale, out, ws, (size_t)KV4_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0,
-                     /*allow_fork=*/false);
+                     /*allow_fork=*/false, /*fit_workspace=*/true);
   if (st == KV4_EWORKSPACE) {
     const std::string why = g_last_error;
     return fail(KV4_EWORKSPACE,

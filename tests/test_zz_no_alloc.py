@@ -70,6 +70,33 @@ def test_noalloc_with_the_prefill_kernel(monkeypatch):
         assert nbad == 0
 
 
+def test_noalloc_fits_the_tile_launch_to_the_scratch():
+    """A Qwen2.5-1.5B-shaped mixed batch (4 chunks of 512, 60 four-query
+    sequences, 4 decodes) whose workspace, as the caller's workspace entry
+    point plans it, exceeds the static scratch: the launch of the
+    four-query sequences beside the prefill kernel takes longer key pieces
+    until the call fits. Its rows then merge fewer partials, so the output
+    agrees with the workspace entry point to the fp32 accumulation order
+    (within G2) rather than bit for bit; every row is within G2 of the
+    oracle."""
+    rng = np.random.default_rng(11)
+    ql = [512] * 4 + [4] * 60 + [1] * 4
+    sl = [2560] * 4 + [int(x) for x in np.exp(rng.uniform(np.log(256), np.log(8192), 64))]
+    order = rng.permutation(len(ql))
+    w = W.custom("noalloc_fit", 12, 2, 128, [ql[i] for i in order], [sl[i] for i in order], seed=7)
+    need = kv4.kv4_paged_attention_workspace_size(w.num_q_tokens, w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                                  w.head_size, w.max_query_len, w.max_seq_len)
+    assert need > kv4.KV4_NOALLOC_SCRATCH_BYTES
+    r, out = _both(w)
+    got = host(out.float())
+    nbad, mx = allclose_report(got, host(r.out.float()), atol=1e-2, rtol=1e-2)
+    assert nbad == 0, f"noalloc against the workspace entry point: {nbad} elements (max {mx})"
+    ref = oracle_attention_on_gpu_cache(r)
+    nbad, mx = allclose_report(got, ref, atol=1e-2, rtol=1e-2)
+    say(f"    {w.name}: planned workspace {need} B > scratch; G2 max abs err {mx:.3e}")
+    assert nbad == 0
+
+
 def test_noalloc_refuses_batches_beyond_the_scratch(monkeypatch):
     # the mixed chunked-prefill batch on the single-kernel plan (its split
     # partials over all 2108 query tokens: ~118 MB)
