@@ -3,8 +3,9 @@ configuration bench.py times: every KV token written in one write call, one
 attention call over the whole batch (workspace sized by the library).
 
 Workloads: Phi-3 (hs 96), Llama-3.2-1B (GQA 4, hs 64), Qwen2.5-1.5B mixed
-chunked prefill + decode, Llama-3-8B long context (hs 128, x20 outlier
-channels) with its head-size-192 sweep and its multi-token decode, and the
+chunked prefill + decode and its prefill chunks alone, Llama-3-8B long
+context (hs 128, x20 outlier channels) with its head-size-192 sweep, its
+multi-token decode and a head-size-256 GQA variant (16 / 4 heads), and the
 Llama-3-8B shape again with the int8 and fp8 control caches, a 4096-token
 sliding window and the inline-scale padded-slot layout.
 
@@ -46,8 +47,10 @@ CASES = {
     "phi3": ("phi3", "int4", 0, False),
     "llama1b": ("llama1b", "int4", 0, False),
     "qwen_mixed": ("qwen_mixed", "int4", 0, False),
+    "qwen_prefill": ("qwen_prefill", "int4", 0, False),
     "llama8b_long": ("llama8b_long", "int4", 0, False),
     "llama8b_hs192": ("llama8b_hs192", "int4", 0, False),
+    "hs256_long": ("hs256_long", "int4", 0, False),
     "llama8b_spec": ("llama8b_spec", "int4", 0, False),
     "llama8b_long_int8": ("llama8b_long", "int8", 0, False),
     "llama8b_long_fp8": ("llama8b_long", "fp8", 0, False),
