@@ -97,15 +97,46 @@ __device__ __forceinline__ uint32_t int4_codes(const float (&v)[8], float scale,
 // exact negation of partner - own), one v_fmac with the partner as its DPP /
 // swizzle source. Returns the lane's final carried sign (+1 / -1): the true
 // values are sign * v, each element rounded exactly as in fwht_b_ct.
+//
+// Distances 1, 2 and 8 stay inside a DPP row of 16 lanes (quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_ror:8), so the exchange is the fmac's
+// own DPP source: eight v_fmac_f32_dpp in one block, after two wait states
+// for the DPP read of a register a vector instruction just wrote (the
+// compiler does not look inside the block). Each reads its partner's value
+// of a register before any instruction of the block writes that register.
+// Distances 4 and 16 go through ds_swizzle (the LDS pipe, off the vector ALU
+// that bounds the kernel).
+#define KV4_DPP_FMAC8(CTRL)                                                                            \
+  asm volatile("s_nop 1\n\t"                                                                          \
+               "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+               "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+               "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+               "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+               "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+               "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+               "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+               "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1"             \
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),   \
+                 "+v"(v[7])                                                                            \
+               : "v"(sgn))
 template <int D>
 __device__ __forceinline__ void fwht8_xlane_lazy(float (&v)[8], float sgn) {
-  float p[8];   // all 8 exchanges in flight before the first use
+  if constexpr (D == 1) {
+    KV4_DPP_FMAC8("quad_perm:[1,0,3,2]");
+  } else if constexpr (D == 2) {
+    KV4_DPP_FMAC8("quad_perm:[2,3,0,1]");
+  } else if constexpr (D == 8) {
+    KV4_DPP_FMAC8("row_ror:8");
+  } else {
+    float p[8];   // all 8 exchanges in flight before the first use
 #pragma unroll
-  for (int e = 0; e < 8; ++e) p[e] = xor_lane<D>(v[e]);
-  __builtin_amdgcn_sched_barrier(0);
+    for (int e = 0; e < 8; ++e) p[e] = xor_lane<D>(v[e]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = fmaf(p[e], sgn, v[e]);
+    for (int e = 0; e < 8; ++e) v[e] = fmaf(p[e], sgn, v[e]);
+  }
 }
+#undef KV4_DPP_FMAC8
 // XS cross-lane stages (b = 8 * 2^XS), in ascending stride order after the
 // in-lane ones; XS is fixed per kernel, so the stages carry no branch.
 template <int XS>
