@@ -206,6 +206,30 @@ def test_prefill_plan_compacts_the_split_rows(L, monkeypatch):
     assert L.kv4_paged_attention_workspace_size(*small) != auto_small
 
 
+@pytest.mark.parametrize("shape", [
+    # (T, S, nq, nkv, max_query_len, max_seq_len): one chunk beside 64
+    # four-query sequences (Llama-3-8B shape); the mixed Qwen2.5-1.5B batch;
+    # 4 chunks of 512 beside 60 four-query sequences and 4 decodes (Qwen shape)
+    (768, 65, 32, 8, 512, 32768),
+    (2108, 64, 12, 2, 512, 8192),
+    (4 * 512 + 60 * 4 + 4, 68, 12, 2, 512, 8192),
+])
+def test_prefill_plan_multi_query_launch_stays_within_the_single_kernel_plan(L, monkeypatch, shape):
+    # Beside the prefill kernel the launch of the 2 .. Q-query sequences
+    # splits no finer than the single-kernel plan and has at most as many
+    # partial rows per split, so the call's workspace exceeds that plan's by
+    # at most the single-query launch's (its per-sequence prefix and at most
+    # 2048 + S stream-K pieces, or S rows per split of at least 512 tokens)
+    T, S, nq, nkv, mq, msl = shape
+    monkeypatch.setenv("KV4_PREFILL", "0")
+    single = L.kv4_paged_attention_workspace_size(T, S, nq, nkv, 128, mq, msl)
+    monkeypatch.setenv("KV4_PREFILL", "1")
+    with_pf = L.kv4_paged_attention_workspace_size(T, S, nq, nkv, 128, mq, msl)
+    row = nq * (128 + 2) * 4
+    decode = max((2048 + S) * row, S * row * -(-msl // 512)) + 3 * (4 * (S + 1) + 256) + 4 * 256
+    assert 0 < single and 0 < with_pf <= single + decode
+
+
 def test_dequant_validation(L):
     rc = L.kv4_dequant(16, 16, 4, 16, 3, 2, 96, 64, 16, 42, 1, 16, None)
     assert rc == EINVAL and "largest power of two" in kv4.kv4_last_error()
